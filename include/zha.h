@@ -1,0 +1,261 @@
+/*
+ * zha.h -- C ABI of the MI355X (gfx950) library for tree-structured KV search.
+ *
+ * The method is Zyphra Hierarchical Attention (ZHA) as described on the page
+ * "How does a tree of summaries search a context? How ZHA works"
+ * (learn.chabulab.com), cited below as [ZHA lesson] with a section name, and
+ * on the arXiv abstract "Subquadratic Attention with a Hierarchical
+ * Tree-Structured Indexer" (2610.42112), cited as [ZHA abstract].
+ *
+ * Three operations make up the hot path:
+ *   1. build / append the tree of compressed key summaries over a KV cache
+ *      that stays intact ([ZHA lesson] "How is the tree built?",
+ *      "What does a node summarize?");
+ *   2. walk the tree top-down for a batch of queries, one walk per query head,
+ *      opening nodes by top-p or top-K at every step ([ZHA lesson] "How does
+ *      top-p differ from top-K?", "Run a small tree yourself", "Common
+ *      misunderstandings");
+ *   3. softmax attention over exactly the original keys and values the walk
+ *      chose ([ZHA lesson] "How is the tree built?").
+ *
+ * Conventions shared by every call:
+ *   - All device memory is owned by the caller.  The library never
+ *     allocates, frees or synchronises; work is enqueued on the caller's HIP
+ *     stream (hipStream_t passed as void*; NULL = the null stream).
+ *   - Every call validates its arguments on the host first.  A call that
+ *     returns anything but ZHA_OK has enqueued nothing.
+ *   - Device-side conditions (capacity overflow, non-finite scores) set bits
+ *     in a caller-provided uint32 status word (ZHA_FLAG_*), readable after the
+ *     stream is synchronised; the results stay deterministic.
+ *   - Device pointers must be 16-byte aligned (ZHA_ERR_ALIGN otherwise).
+ *   - Layouts (row-major, last index fastest):
+ *       K, V cache   [batch][kv_heads][max_tokens][head_dim]   dtype
+ *       Q, out       [batch][kv_heads*group][q_per_head][head_dim] dtype
+ *       refs         [kv_heads][num_refs][head_dim]            float32
+ *     Query head h uses KV head h / group.  One tree per (sequence, KV head);
+ *     every query head of the group walks it separately.
+ *   - Supported: head_dim 64 or 128; chunk a power of two in [2, 64];
+ *     levels 1..8; num_refs in {1, 2, 4, 8, 16}; dtype float32 or bfloat16.
+ *     Anything else returns ZHA_ERR_UNSUPPORTED.
+ */
+#ifndef ZHA_H
+#define ZHA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZHA_MAX_LEVELS 8
+#define ZHA_MAX_STEPS 8
+
+typedef enum {
+    ZHA_OK = 0,
+    ZHA_ERR_ARG = 1,         /* null pointer or out-of-range scalar           */
+    ZHA_ERR_SHAPE = 2,       /* token counts / sizes inconsistent             */
+    ZHA_ERR_ALIGN = 3,       /* a device pointer is not 16-byte aligned       */
+    ZHA_ERR_CAPACITY = 4,    /* append past max_tokens, tree memory too small */
+    ZHA_ERR_WORKSPACE = 5,   /* workspace smaller than the sizing call says   */
+    ZHA_ERR_UNSUPPORTED = 6, /* geometry outside the supported set            */
+    ZHA_ERR_HIP = 7          /* a HIP launch failed                           */
+} zha_status;
+
+typedef enum { ZHA_F32 = 0, ZHA_BF16 = 1 } zha_dtype;
+
+enum { ZHA_TOPP = 0, ZHA_TOPK = 1 };
+
+/* Device status bits. */
+#define ZHA_FLAG_CAND_OVERFLOW 1u  /* a step had more candidates than max_candidates;
+                                      the excess (in span order) was dropped      */
+#define ZHA_FLAG_SEL_OVERFLOW 2u   /* more level-1 blocks opened than
+                                      max_blocks_per_walk; the excess was dropped */
+#define ZHA_FLAG_NONFINITE 4u      /* a node score was NaN; it ranked last        */
+
+/* Shape of the cache and of the tree over it.
+ * sharpness: the scale s in every score s*<key, query> + bias, which is also
+ * the attention logit scale (usually 1/sqrt(head_dim)).  levels = number of
+ * summary levels above the raw keys ([ZHA lesson] "How is the tree built?":
+ * one level summarises `chunk` keys, two levels chunk^2, ...). */
+typedef struct {
+    int32_t batch;
+    int32_t num_kv_heads;
+    int32_t group_size;      /* query heads per KV head                       */
+    int32_t head_dim;
+    int32_t chunk;           /* children per node                             */
+    int32_t num_refs;        /* reference queries R (tangents per node)       */
+    int32_t levels;
+    int32_t dtype;           /* zha_dtype of K, V, Q and out                  */
+    int64_t max_tokens;      /* cache capacity per (sequence, KV head)        */
+    float sharpness;
+    int32_t reserved;
+} zha_geometry;
+
+/* How a walk opens nodes at each step ([ZHA lesson] "How does top-p differ
+ * from top-K?").
+ *   ZHA_TOPP: open the smallest prefix of the candidates ordered by score
+ *     (descending; equal scores by span start, ascending) whose softmax mass
+ *     reaches p.  p >= 1 opens every candidate, p <= 0 opens one.
+ *   ZHA_TOPK: open min(k[t], candidates) at step t; k[t] = k[num_k-1] for
+ *     t >= num_k.
+ * The softmax runs jointly over the step's whole candidate list.
+ * max_blocks_per_walk bounds the stored level-1 selections of a walk;
+ * max_candidates bounds a step's candidate list (0 = the largest level). */
+typedef struct {
+    int32_t mode;
+    float p;
+    int32_t k[ZHA_MAX_STEPS];
+    int32_t num_k;
+    int32_t max_blocks_per_walk;
+    int32_t max_candidates;
+    int32_t reserved;
+} zha_select;
+
+/* Host handle of one tree set (all sequences and KV heads).  Plain data: the
+ * caller keeps it; zha_build / zha_append update n_tokens.  Fill it with
+ * zha_tree_init only. */
+typedef struct {
+    zha_geometry geom;
+    int64_t n_tokens;                            /* tokens summarised so far  */
+    void *tree_mem;                              /* device, caller-owned      */
+    uint64_t tree_bytes;
+    const float *refs;                           /* device, caller-owned      */
+    int64_t level_cap[ZHA_MAX_LEVELS + 1];       /* nodes per pair, level l   */
+    uint64_t key_off[ZHA_MAX_LEVELS + 1];        /* byte offset of level-l keys   */
+    uint64_t bias_off[ZHA_MAX_LEVELS + 1];       /* byte offset of level-l biases */
+} zha_tree;
+
+/* Per-walk accounting ([ZHA lesson] "Run a small tree yourself": a walk's
+ * work is R per scored node plus one per key read). */
+typedef struct {
+    int32_t scored[ZHA_MAX_STEPS];   /* candidates at step t                  */
+    int32_t opened[ZHA_MAX_STEPS];   /* candidates opened at step t           */
+    int32_t steps;
+    int32_t keys_read;               /* selected keys incl. the raw tail      */
+    int32_t blocks;                  /* level-1 blocks opened (before clamp)  */
+    int32_t unforced_scored;         /* candidates whose scores were computed */
+    int64_t comparisons;             /* R * sum(scored) + keys_read           */
+    uint32_t flags;                  /* ZHA_FLAG_* raised by this walk        */
+    uint32_t reserved;
+} zha_walk_stats;
+
+/* ---- sizing and set-up (host only, no device work) -------------------- */
+
+/* Bytes of tree memory for `g`: for every level l = 1..levels, keys
+ * float32 [batch][kv_heads][floor(max_tokens/chunk^l)][num_refs][head_dim]
+ * then biases float32 [batch][kv_heads][floor(max_tokens/chunk^l)][num_refs],
+ * each array 256-byte aligned.  Returns 0 if `g` is invalid. */
+uint64_t zha_tree_bytes(const zha_geometry *g);
+
+/* Fill `t` for tree memory `tree_mem` (device, >= zha_tree_bytes) and the
+ * reference queries `refs` (device float32 [kv_heads][num_refs][head_dim],
+ * [ZHA lesson] "What does a node summarize?": fixed sample questions).
+ * Sets n_tokens = 0.  No device work. */
+zha_status zha_tree_init(zha_tree *t, const zha_geometry *g, void *tree_mem,
+                         uint64_t tree_bytes, const float *refs);
+
+/* ---- 1. build and append ------------------------------------------------ */
+
+/* Summarise the first n_tokens rows of k_cache into levels 1..levels from
+ * scratch and set t->n_tokens = n_tokens.  Level 1 summarises each whole
+ * chunk of keys (a key is its own tangent for every reference, bias 0);
+ * level l >= 2 summarises each whole chunk of level-(l-1) nodes.  Per
+ * reference r: weights softmax(s*<child key_r, rho_r> + child bias_r), the new
+ * key the weighted sum of child keys, the new bias the log-sum-exp of those
+ * scores minus s*<new key, rho_r> ([ZHA lesson] "What does a node
+ * summarize?").  Partial chunks are not summarised. */
+zha_status zha_build(zha_tree *t, const void *k_cache, int64_t n_tokens, void *stream);
+
+/* The caller has written rows [n, n + n_new) of every (sequence, KV head) of
+ * k_cache, n = t->n_tokens.  Summarise every chunk that these rows complete,
+ * at every level, and set t->n_tokens = n + n_new ([ZHA lesson] "How is the
+ * tree built?": a node is created each time a chunk fills).  The result is
+ * bit-identical to zha_build over n + n_new tokens.  ZHA_ERR_CAPACITY if
+ * n + n_new > max_tokens. */
+zha_status zha_append(zha_tree *t, const void *k_cache, int64_t n_new, void *stream);
+
+/* ---- 2. search ------------------------------------------------------------ */
+
+/* Workspace bytes of zha_search for q_per_head queries per head. */
+uint64_t zha_search_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head);
+
+/* One walk per (sequence, query head, query).  q_per_head = 1 is decode: the
+ * query sees the tree's tokens [0, n_tokens).  Candidates start as the roots:
+ * every top-level node plus every node whose parent chunk has not filled;
+ * per step they are scored (max over r of s*<key_r, q> + bias_r), normalised
+ * with a softmax over the whole step and cut by `sel`; opened level-1 nodes
+ * select their `chunk` keys, other opened nodes give their children as the
+ * next candidates ([ZHA lesson] "Run a small tree yourself").  Raw keys past
+ * the last whole chunk are always selected (not listed).
+ *   sel_blocks  device int32 [walks][max_blocks_per_walk]: level-1 block ids
+ *               j (keys j*chunk .. j*chunk+chunk-1), in the order found
+ *               (steps in order, each step in span order)
+ *   sel_count   device int32 [walks]: blocks stored (<= max_blocks_per_walk)
+ *   stats       device zha_walk_stats [walks], may be NULL
+ *   status      device uint32, OR-ed with ZHA_FLAG_* (not cleared)
+ * walks = batch * kv_heads * group_size * q_per_head, in Q's order.
+ * q_per_head > 1 (prefill blocks) returns ZHA_ERR_UNSUPPORTED. */
+zha_status zha_search(const zha_tree *t, const void *q, int32_t q_per_head,
+                      const zha_select *sel, int32_t *sel_blocks, int32_t *sel_count,
+                      zha_walk_stats *stats, uint32_t *status,
+                      void *ws, uint64_t ws_bytes, void *stream);
+
+/* ---- 3. sparse attention --------------------------------------------------- */
+
+/* Workspace bytes of zha_sparse_attn. */
+uint64_t zha_attn_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head);
+
+/* out = softmax over the selected keys of s*<q, K_i>, applied to V_i, for
+ * every walk: exactly the original keys of the listed level-1 blocks plus
+ * the raw tail [chunk*floor(n_tokens/chunk), n_tokens) ([ZHA lesson] "How is
+ * the tree built?", "Common misunderstandings").  fp32 accumulation; a bf16
+ * output is rounded to nearest-even once.  Block ids must be in
+ * [0, floor(n_tokens/chunk)); entries past sel_count are ignored. */
+zha_status zha_sparse_attn(const zha_tree *t, const void *q, int32_t q_per_head,
+                           const void *k_cache, const void *v_cache,
+                           const zha_select *sel, const int32_t *sel_blocks,
+                           const int32_t *sel_count, void *out,
+                           void *ws, uint64_t ws_bytes, void *stream);
+
+/* ---- one decode step ------------------------------------------------------- */
+
+/* Workspace bytes of zha_forward (search + attention + selection lists). */
+uint64_t zha_forward_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head);
+
+/* zha_append(n_new) (skipped if 0), then zha_search, then zha_sparse_attn,
+ * with the selection lists kept in the workspace. */
+zha_status zha_forward(zha_tree *t, int64_t n_new, const void *q, int32_t q_per_head,
+                       const void *k_cache, const void *v_cache, const zha_select *sel,
+                       void *out, zha_walk_stats *stats, uint32_t *status,
+                       void *ws, uint64_t ws_bytes, void *stream);
+
+/* ---- measurement helpers (same-GPU baselines) ------------------------------ */
+
+/* Workspace bytes of zha_dense_topk_attn. */
+uint64_t zha_dense_workspace_bytes(const zha_tree *t, int32_t q_per_head);
+
+/* Dense full-scan indexer: exact logits s*<q, K_i> for every key i < n_tokens
+ * (one pass over K per (sequence, KV head) serving all its query heads), the
+ * budget[w] highest logits per walk (ties: lower index first), then attention
+ * over exactly those keys into out.  budget: device int32 [walks], each in
+ * [1, n_tokens].  This is the indexer that scores every key, written from
+ * its plain definition; it is the baseline the tree search is measured
+ * against ([ZHA lesson] "How does a tree of summaries search a context?"). */
+zha_status zha_dense_topk_attn(const zha_tree *t, const void *q, const void *k_cache,
+                               const void *v_cache, const int32_t *budget, void *out,
+                               int32_t *sel_tokens, void *ws, uint64_t ws_bytes,
+                               void *stream);
+
+/* Streaming read of `bytes` from device buffer `buf` (sum into *sink, a
+ * device float); gives the achievable HBM read bandwidth on this GPU. */
+zha_status zha_bw_probe(const void *buf, uint64_t bytes, float *sink, void *stream);
+
+/* Static text for a status code. */
+const char *zha_status_string(zha_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZHA_H */

@@ -1,0 +1,155 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects
+bad arguments on the host before any launch (no GPU needed: every call here
+fails validation, so nothing reaches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zha.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(zha_[a-z_0-9]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def Z():
+    from tree_structured_kv_amd import zha
+    return zha
+
+
+def test_every_declared_symbol_is_exported(Z):
+    names = _declared()
+    assert "zha_build" in names and "zha_forward" in names and len(names) >= 10
+    for n in names:
+        assert hasattr(Z.lib, n), n
+    assert sorted(Z.EXPORTS) == names
+
+
+def test_struct_sizes_match_header(Z):
+    # layouts the header fixes: 8 int32 + int64 + float + int32 = 48 bytes
+    assert ctypes.sizeof(Z.Geometry) == 48
+    assert ctypes.sizeof(Z.WalkStats) == 96
+    assert ctypes.sizeof(Z.Select) == 4 * (2 + 8 + 4)
+
+
+def _geom(Z, **kw):
+    base = dict(batch=2, kv_heads=2, group=2, head_dim=128, chunk=8, refs=4, levels=3,
+                dtype="bf16", max_tokens=4096, sharpness=0.088)
+    base.update(kw)
+    return Z.make_geometry(**base)
+
+
+def test_tree_bytes_formula(Z):
+    g = _geom(Z)
+    pairs = 4
+    want = 0
+    for l in (1, 2, 3):
+        cap = 4096 // 8 ** l
+        for nbytes in (pairs * cap * 4 * 128 * 4, pairs * cap * 4 * 4):
+            want += (nbytes + 255) // 256 * 256
+    assert Z.zha_tree_bytes(g) == want
+
+
+@pytest.mark.parametrize("kw", [dict(head_dim=96), dict(chunk=3), dict(chunk=128), dict(refs=3),
+                                dict(levels=0), dict(levels=9), dict(dtype=5),
+                                dict(max_tokens=0), dict(batch=0), dict(sharpness=float("inf"))])
+def test_bad_geometry_rejected(Z, kw):
+    g = _geom(Z, **kw)
+    if kw.get("dtype") == 5:
+        g.dtype = 5
+    assert Z.zha_tree_bytes(g) == 0
+    t = Z.TreeHandle()
+    rc = Z.lib.zha_tree_init(ctypes.byref(t), ctypes.byref(g), 1 << 20, 1 << 40, 1 << 20)
+    assert rc in (1, 6)
+
+
+def _handle(Z, **kw):
+    g = _geom(Z, **kw)
+    t = Z.TreeHandle()
+    rc = Z.lib.zha_tree_init(ctypes.byref(t), ctypes.byref(g), 0x100000, Z.zha_tree_bytes(g), 0x200000)
+    assert rc == 0
+    return t
+
+
+def test_tree_init_checks(Z):
+    g = _geom(Z)
+    t = Z.TreeHandle()
+    need = Z.zha_tree_bytes(g)
+    assert Z.lib.zha_tree_init(ctypes.byref(t), ctypes.byref(g), 0x100008, need, 0x200000) == 3
+    assert Z.lib.zha_tree_init(ctypes.byref(t), ctypes.byref(g), 0x100000, need - 1, 0x200000) == 4
+    assert Z.lib.zha_tree_init(ctypes.byref(t), ctypes.byref(g), None, need, 0x200000) == 1
+    t = _handle(Z)
+    assert t.n_tokens == 0
+    assert list(t.level_cap)[1:4] == [512, 64, 8]
+
+
+def test_build_append_argument_errors(Z):
+    t = _handle(Z)
+    assert Z.lib.zha_build(ctypes.byref(t), None, 16, None) == 1
+    assert Z.lib.zha_build(ctypes.byref(t), 0x300004, 16, None) == 3
+    assert Z.lib.zha_build(ctypes.byref(t), 0x300000, 4097, None) == 4
+    assert Z.lib.zha_build(ctypes.byref(t), 0x300000, -1, None) == 4
+    assert Z.lib.zha_append(ctypes.byref(t), 0x300000, -1, None) == 1
+    assert Z.lib.zha_append(ctypes.byref(t), 0x300000, 4097, None) == 4
+    assert t.n_tokens == 0
+
+
+def test_search_argument_errors(Z):
+    t = _handle(Z)
+    sel = Z.make_select("topp", 0.9, max_blocks=64)
+    ws = Z.zha_search_workspace_bytes(t, sel)
+    assert ws > 0
+    args = lambda **o: [ctypes.byref(t), o.get("q", 0x400000), o.get("qph", 1), ctypes.byref(o.get("sel", sel)),
+                        o.get("blocks", 0x500000), o.get("count", 0x600000), None, o.get("status", 0x700000),
+                        o.get("ws", 0x800000), o.get("wsb", ws), None]
+    assert Z.lib.zha_search(*args(q=None)) == 1
+    assert Z.lib.zha_search(*args(q=0x400002)) == 3
+    assert Z.lib.zha_search(*args(status=None)) == 1
+    assert Z.lib.zha_search(*args(wsb=ws - 1)) == 5
+    assert Z.lib.zha_search(*args(qph=0)) == 1
+    assert Z.lib.zha_search(*args(qph=4)) == 6
+    bad = Z.make_select("topk", k=(0,), max_blocks=64)
+    assert Z.lib.zha_search(*args(sel=bad)) == 1
+    bad = Z.make_select("topp", 0.9, max_blocks=0)
+    assert Z.lib.zha_search(*args(sel=bad)) == 1
+    bad = Z.make_select("topp", float("nan"), max_blocks=8)
+    assert Z.lib.zha_search(*args(sel=bad)) == 1
+
+
+def test_workspace_sizes_grow_with_capacity(Z):
+    t = _handle(Z)
+    s1 = Z.make_select("topp", 0.9, max_blocks=64, max_candidates=100)
+    s2 = Z.make_select("topp", 0.9, max_blocks=64, max_candidates=1000)
+    assert Z.zha_search_workspace_bytes(t, s2) > Z.zha_search_workspace_bytes(t, s1)
+    f = Z.zha_forward_workspace_bytes(t, s1)
+    assert f >= Z.zha_search_workspace_bytes(t, s1) + Z.zha_attn_workspace_bytes(t, s1)
+
+
+def test_attn_forward_argument_errors(Z):
+    t = _handle(Z)
+    sel = Z.make_select("topp", 0.9, max_blocks=64)
+    ws = Z.zha_attn_workspace_bytes(t, sel)
+    base = [ctypes.byref(t), 0x400000, 1, 0x410000, 0x420000, ctypes.byref(sel), 0x430000, 0x440000,
+            0x450000, 0x460000, ws, None]
+    a = list(base); a[3] = None
+    assert Z.lib.zha_sparse_attn(*a) == 1
+    a = list(base); a[8] = 0x450008
+    assert Z.lib.zha_sparse_attn(*a) == 3
+    a = list(base); a[10] = ws - 1
+    assert Z.lib.zha_sparse_attn(*a) == 5
+    fw = Z.zha_forward_workspace_bytes(t, sel)
+    assert Z.lib.zha_forward(ctypes.byref(t), 5000, 0x400000, 1, 0x410000, 0x420000, ctypes.byref(sel),
+                             0x450000, None, 0x470000, 0x460000, fw, None) == 4
+    assert Z.lib.zha_forward(ctypes.byref(t), 0, 0x400000, 1, 0x410000, 0x420000, ctypes.byref(sel),
+                             0x450000, None, 0x470000, 0x460000, fw - 1, None) == 5
+
+
+def test_status_strings(Z):
+    for code in range(8):
+        assert Z.lib.zha_status_string(code)

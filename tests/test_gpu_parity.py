@@ -1,0 +1,245 @@
+"""GPU parity: the HIP path (through the C-ABI) against the fp64 oracle on the
+same seeded inputs, at sizes the oracle finishes in seconds that span several
+workgroups, levels and a ragged tail.  Contract: see tests/parity.py."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from tree_structured_kv_amd import synth as S
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def Z():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from tree_structured_kv_amd import zha
+    return zha
+
+
+def _case(name):
+    W = S.WORKLOADS
+    if name == "demo":          # the fp32 demo geometry, 64 query heads on one tree
+        return replace(W[0], group=64), None
+    if name == "demo-unstructured":
+        return replace(W[0], group=64), "unstructured"
+    if name == "ar1-small":     # ragged: 8192 + 5 tokens, 4 levels
+        return replace(W[1].scaled(n=8197, batch=2), kv_heads=2, levels=4), None
+    if name == "clustered-small":
+        return replace(W[2].scaled(n=32768 + 77, batch=2), kv_heads=2, levels=5), None
+    if name == "mixed-small":
+        return replace(W[4].scaled(n=65536 + 3, batch=2), levels=4), None
+    raise KeyError(name)
+
+
+CASES = ["demo", "demo-unstructured", "ar1-small", "clustered-small", "mixed-small"]
+
+_cache = {}
+
+
+def _setup(Z, name):
+    if name in _cache:
+        return _cache[name]
+    w, variant = _case(name)
+    K, V, Q, R = P.make_inputs(w, unstructured=(variant == "unstructured"))
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda")
+    Kt = torch.from_numpy(K).to(dev).to(dt).contiguous()
+    Vt = torch.from_numpy(V).to(dev).to(dt).contiguous()
+    Qt = torch.from_numpy(Q).to(dev).to(dt).contiguous()
+    geom = Z.make_geometry(w.batch, w.kv_heads, w.group, w.d, w.chunk, w.refs, w.levels, w.dtype,
+                           w.n, w.sharpness)
+    idx = Z.Index(geom, torch.from_numpy(R))
+    idx.build(Kt, w.n)
+    trees = {(b, g): P.oracle_tree(w, K, R, b, g, w.n) for b in range(w.batch) for g in range(w.kv_heads)}
+    _cache[name] = (w, K, V, Q, R, Kt, Vt, Qt, idx, trees)
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_tree_records(Z, name):
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, name)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for l in range(1, w.levels + 1):
+        gk, gb = idx.level(l)
+        gk = gk.cpu().numpy()
+        gb = gb.cpu().numpy()
+        for (b, g), tr in trees.items():
+            ok, ob = tr.level(l)
+            if ok.shape[0] == 0:
+                continue
+            nk = gk[b, g, : ok.shape[0]]
+            nb = gb[b, g, : ok.shape[0]]
+            ek = np.max(np.abs(nk - ok), axis=(1, 2)) / np.maximum(1.0, np.max(np.abs(ok), axis=(1, 2)))
+            eb = np.max(np.abs(nb - ob), axis=1) / np.maximum(1.0, np.max(np.abs(ob), axis=1))
+            worst = max(worst, float(ek.max()), float(eb.max()))
+    assert worst <= P.TOL_TREE, worst
+
+
+@pytest.mark.parametrize("name", ["demo", "ar1-small", "mixed-small"])
+def test_build_equals_appends(Z, name):
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, name)
+    other = Z.Index(idx.geom, torch.from_numpy(R))
+    other.tree_mem.fill_(0x7F)
+    rng = np.random.default_rng(5)
+    done = 0
+    steps = [1, 1, 3, w.chunk - 1, w.chunk, 1000]
+    while done < w.n:
+        m = steps.pop(0) if steps else int(rng.integers(1, 5000))
+        m = min(m, w.n - done)
+        other.append(Kt, m)
+        done += m
+    assert other.n_tokens == w.n
+    torch.cuda.synchronize()
+    for l in range(1, w.levels + 1):
+        a_k, a_b = idx.level(l)
+        b_k, b_b = other.level(l)
+        live = w.n // w.chunk ** l
+        assert torch.equal(a_k[:, :, :live], b_k[:, :, :live]), l
+        assert torch.equal(a_b[:, :, :live], b_b[:, :, :live]), l
+
+
+SELECTS = {
+    "topp90": dict(mode="topp", p=0.9),
+    "topp50": dict(mode="topp", p=0.5),
+    "topk4": dict(mode="topk", k=(4,)),
+    "topk-sched": dict(mode="topk", k=(2, 6, 12)),
+    "greedy": dict(mode="topk", k=(1,)),
+    "p0": dict(mode="topp", p=0.0),
+}
+
+
+def _run(Z, idx, Qt, Kt, Vt, select, max_blocks=None, max_candidates=0):
+    g = idx.geom
+    if max_blocks is None:
+        max_blocks = g.max_tokens // g.chunk
+    sel = P.select_struct(Z, select, max_blocks, max_candidates)
+    bufs = idx.search(Qt, sel)
+    out = idx.sparse_attn(Qt, Kt, Vt, sel, bufs["sel_blocks"], bufs["sel_count"])
+    torch.cuda.synchronize()
+    return sel, bufs, out
+
+
+def _compare(w, K, V, Q, trees, select, bufs, out, min_stable=0.3):
+    blocks = bufs["sel_blocks"].cpu().numpy()
+    count = bufs["sel_count"].cpu().numpy()
+    from tree_structured_kv_amd.zha import stats_to_dicts
+    stats = stats_to_dicts(bufs["stats"].cpu())
+    outs = out.float().cpu().numpy()
+    assert int(bufs["status"].cpu()[0]) == 0
+    stable = 0
+    walks = 0
+    worst = 0.0
+    for b in range(w.batch):
+        for h in range(w.heads):
+            g = h // w.group
+            wi = b * w.heads + h
+            q = Q[b, h]
+            sel_o, st_o = P.oracle_walk(trees[(b, g)], q, select)
+            toks = P.gpu_tokens(blocks[wi], count[wi], w.chunk, w.n)
+            st = stats[wi]
+            walks += 1
+            if st_o["gap"] > P.GAP:
+                stable += 1
+                assert np.array_equal(toks, sel_o), (b, h)
+                assert st["scored"] == st_o["scored"] and st["opened"] == st_o["opened"], (b, h)
+                assert st["comparisons"] == st_o["comparisons"]
+                assert st["keys_read"] == st_o["keys_read"]
+                assert st["unforced_scored"] == st_o["unforced_scored"]
+            ref, _ = O.attend(toks, q.astype(np.float64), K[b, g].astype(np.float64),
+                              V[b, g].astype(np.float64), w.sharpness)
+            ok, e = P.out_ok(outs[b, h], ref, w.dtype)
+            worst = max(worst, e)
+            assert ok, (b, h, e)
+    assert stable >= min_stable * walks, (stable, walks)
+    return stable, walks, worst
+
+
+@pytest.mark.parametrize("sname", list(SELECTS))
+@pytest.mark.parametrize("name", CASES)
+def test_search_and_attention(Z, name, sname):
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, name)
+    select = SELECTS[sname]
+    sel, bufs, out = _run(Z, idx, Qt, Kt, Vt, select)
+    min_stable = 0.15 if name.startswith("demo") and select["mode"] == "topp" else 0.3
+    _compare(w, K, V, Q, trees, select, bufs, out, min_stable=min_stable)
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_open_all_is_dense(Z, name):
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, name)
+    for select in (dict(mode="topp", p=1.0), dict(mode="topk", k=(10 ** 6,))):
+        sel, bufs, out = _run(Z, idx, Qt, Kt, Vt, select)
+        count = bufs["sel_count"].cpu().numpy()
+        assert np.all(count == w.n // w.chunk)
+        outs = out.float().cpu().numpy()
+        for b in range(w.batch):
+            for h in range(w.heads):
+                g = h // w.group
+                ref, _ = O.attend(np.arange(w.n), Q[b, h].astype(np.float64),
+                                  K[b, g].astype(np.float64), V[b, g].astype(np.float64), w.sharpness)
+                assert P.out_ok(outs[b, h], ref, w.dtype)[0], (b, h)
+
+
+def test_widget_accounting_on_gpu(Z):
+    """The page's widget trace (64->4, 16->9, 36->25: 100 keys, 564
+    comparisons) and top-K 6 (24 keys, 472 comparisons), on the GPU."""
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, "demo")
+    from tree_structured_kv_amd.zha import stats_to_dicts
+    for select, want in ((dict(mode="topk", k=(4, 9, 25)), (564, 100, [64, 16, 36], [4, 9, 25])),
+                         (dict(mode="topk", k=(6,)), (472, 24, [64, 24, 24], [6, 6, 6]))):
+        sel, bufs, out = _run(Z, idx, Qt, Kt, Vt, select)
+        for st in stats_to_dicts(bufs["stats"].cpu()):
+            assert (st["comparisons"], st["keys_read"], st["scored"], st["opened"]) == want
+
+
+def test_deterministic(Z):
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, "clustered-small")
+    select = SELECTS["topp90"]
+    _, b1, o1 = _run(Z, idx, Qt, Kt, Vt, select)
+    _, b2, o2 = _run(Z, idx, Qt, Kt, Vt, select)
+    for k in ("sel_blocks", "sel_count", "stats"):
+        c1 = b1["sel_count"]
+        if k == "sel_blocks":
+            for wi in range(c1.numel()):
+                n = int(c1[wi])
+                assert torch.equal(b1[k][wi, :n], b2[k][wi, :n])
+        else:
+            assert torch.equal(b1[k], b2[k])
+    assert torch.equal(o1, o2)
+
+
+def test_overflow_is_flagged_and_deterministic(Z):
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, "mixed-small")
+    select = SELECTS["topp90"]
+    for kw, flag in ((dict(max_blocks=2), Z.FLAG_SEL_OVERFLOW), (dict(max_candidates=20), Z.FLAG_CAND_OVERFLOW)):
+        _, b1, o1 = _run(Z, idx, Qt, Kt, Vt, select, **kw)
+        _, b2, o2 = _run(Z, idx, Qt, Kt, Vt, select, **kw)
+        assert int(b1["status"].cpu()[0]) & flag
+        assert torch.equal(o1, o2)
+        assert torch.equal(b1["sel_count"], b2["sel_count"])
+        assert torch.all(torch.isfinite(o1.float()))
+
+
+def test_forward_equals_parts(Z):
+    """zha_forward(n_new) = zha_append(n_new) + zha_search + zha_sparse_attn."""
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, "ar1-small")
+    select = SELECTS["topp90"]
+    g = idx.geom
+    sel = P.select_struct(Z, select, g.max_tokens // g.chunk)
+    n0 = w.n - 37
+    a = Z.Index(g, torch.from_numpy(R))
+    a.build(Kt, n0)
+    out_f = torch.empty_like(Qt)
+    stats = torch.zeros(a.walks, Z.STATS_WORDS, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    a.forward(37, Qt, Kt, Vt, sel, out_f, stats, status, a.forward_workspace(sel))
+    _, bufs, out_p = _run(Z, idx, Qt, Kt, Vt, select)
+    assert a.n_tokens == w.n
+    assert torch.equal(out_f, out_p)
+    assert torch.equal(stats, bufs["stats"])

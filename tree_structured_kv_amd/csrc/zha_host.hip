@@ -1,0 +1,423 @@
+// zha_host.hip -- the C ABI of libzha: argument checks, sizing, launches.
+//
+// Nothing here allocates, frees or synchronises device memory; every launch
+// goes to the caller's stream.  A call that fails its checks returns before
+// enqueueing anything.
+#include <math.h>
+#include <string.h>
+
+#include "zha_internal.h"
+
+using namespace zha;
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+
+uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_n(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+int ilog2(int v) {
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return l;
+}
+
+int64_t level_count(int64_t n, int c, int l) {
+    for (int i = 0; i < l; ++i) n /= c;
+    return n;
+}
+
+zha_status check_geometry(const zha_geometry *g) {
+    if (!g) return ZHA_ERR_ARG;
+    if (g->batch < 1 || g->num_kv_heads < 1 || g->group_size < 1) return ZHA_ERR_ARG;
+    if (g->head_dim != 64 && g->head_dim != 128) return ZHA_ERR_UNSUPPORTED;
+    if (g->chunk < 2 || g->chunk > 64 || (g->chunk & (g->chunk - 1))) return ZHA_ERR_UNSUPPORTED;
+    if (g->num_refs != 1 && g->num_refs != 2 && g->num_refs != 4 && g->num_refs != 8 &&
+        g->num_refs != 16)
+        return ZHA_ERR_UNSUPPORTED;
+    if (g->levels < 1 || g->levels > ZHA_MAX_LEVELS) return ZHA_ERR_UNSUPPORTED;
+    if (g->dtype != ZHA_F32 && g->dtype != ZHA_BF16) return ZHA_ERR_UNSUPPORTED;
+    if (g->max_tokens < 1 || g->max_tokens >= (int64_t(1) << 31)) return ZHA_ERR_ARG;
+    if (g->max_tokens / g->chunk >= (int64_t(1) << kLevelShift)) return ZHA_ERR_UNSUPPORTED;
+    if (!isfinite(g->sharpness)) return ZHA_ERR_ARG;
+    if (int64_t(g->batch) * g->num_kv_heads > 65535) return ZHA_ERR_UNSUPPORTED;
+    const int64_t walks = int64_t(g->batch) * g->num_kv_heads * g->group_size;
+    if (walks > (int64_t(1) << 24)) return ZHA_ERR_UNSUPPORTED;
+    return ZHA_OK;
+}
+
+zha_status check_tree(const zha_tree *t) {
+    if (!t) return ZHA_ERR_ARG;
+    zha_status s = check_geometry(&t->geom);
+    if (s != ZHA_OK) return s;
+    if (!t->tree_mem || !t->refs) return ZHA_ERR_ARG;
+    if (t->n_tokens < 0 || t->n_tokens > t->geom.max_tokens) return ZHA_ERR_SHAPE;
+    if (t->tree_bytes < zha_tree_bytes(&t->geom)) return ZHA_ERR_CAPACITY;
+    return ZHA_OK;
+}
+
+int64_t total_nodes(const zha_geometry *g) {
+    int64_t tot = 0;
+    for (int l = 1; l <= g->levels; ++l) tot += level_count(g->max_tokens, g->chunk, l);
+    return tot;
+}
+
+int32_t cand_capacity(const zha_tree *t, const zha_select *sel) {
+    int64_t cap = sel->max_candidates > 0 ? sel->max_candidates : total_nodes(&t->geom);
+    if (cap < 1) cap = 1;
+    if (cap > (int64_t(1) << 24)) cap = int64_t(1) << 24;
+    return static_cast<int32_t>(cap);
+}
+
+zha_status check_select(const zha_select *sel) {
+    if (!sel) return ZHA_ERR_ARG;
+    if (sel->mode != ZHA_TOPP && sel->mode != ZHA_TOPK) return ZHA_ERR_ARG;
+    if (!isfinite(sel->p)) return ZHA_ERR_ARG;
+    if (sel->mode == ZHA_TOPK) {
+        if (sel->num_k < 1 || sel->num_k > ZHA_MAX_STEPS) return ZHA_ERR_ARG;
+        for (int i = 0; i < sel->num_k; ++i)
+            if (sel->k[i] < 1) return ZHA_ERR_ARG;
+    }
+    if (sel->max_blocks_per_walk < 1) return ZHA_ERR_ARG;
+    if (sel->max_candidates < 0) return ZHA_ERR_ARG;
+    return ZHA_OK;
+}
+
+int64_t walks_of(const zha_geometry *g, int32_t qph) {
+    return int64_t(g->batch) * g->num_kv_heads * g->group_size * qph;
+}
+
+int attn_splits(const zha_tree *t, const zha_select *sel, int64_t walks) {
+    const int64_t keys = int64_t(sel->max_blocks_per_walk) * t->geom.chunk + t->geom.chunk;
+    int64_t by_grid = (2048 + walks - 1) / walks;
+    int64_t by_keys = (keys + 255) / 256;
+    int64_t s = by_grid < by_keys ? by_grid : by_keys;
+    if (s < 1) s = 1;
+    if (s > 32) s = 32;
+    return static_cast<int>(s);
+}
+
+struct SearchWs {
+    uint64_t cand, score, total;
+};
+SearchWs search_ws_layout(const zha_tree *t, const zha_select *sel, int64_t walks) {
+    const uint64_t cap = static_cast<uint64_t>(cand_capacity(t, sel));
+    SearchWs l;
+    l.cand = 0;
+    l.score = align_up(walks * 2 * cap * sizeof(uint32_t));
+    l.total = l.score + align_up(walks * cap * sizeof(float));
+    return l;
+}
+
+uint64_t attn_ws_bytes(const zha_tree *t, const zha_select *sel, int64_t walks) {
+    const int splits = attn_splits(t, sel, walks);
+    return align_up(uint64_t(walks) * splits * (t->geom.head_dim + 2) * sizeof(float));
+}
+
+struct ForwardWs {
+    uint64_t sel_blocks, sel_count, search, attn, total;
+};
+ForwardWs forward_ws_layout(const zha_tree *t, const zha_select *sel, int64_t walks) {
+    ForwardWs l;
+    l.sel_blocks = 0;
+    l.sel_count = align_up(uint64_t(walks) * sel->max_blocks_per_walk * sizeof(int32_t));
+    l.search = l.sel_count + align_up(uint64_t(walks) * sizeof(int32_t));
+    l.attn = l.search + search_ws_layout(t, sel, walks).total;
+    l.total = l.attn + attn_ws_bytes(t, sel, walks);
+    return l;
+}
+
+zha_status hip_status(hipError_t e) { return e == hipSuccess ? ZHA_OK : ZHA_ERR_HIP; }
+
+zha_status run_levels(zha_tree *t, const void *k_cache, int64_t n_old, int64_t n_new, hipStream_t st) {
+    const zha_geometry &g = t->geom;
+    char *mem = static_cast<char *>(t->tree_mem);
+    for (int l = 1; l <= g.levels; ++l) {
+        const int64_t a = level_count(n_old, g.chunk, l);
+        const int64_t b = level_count(n_new, g.chunk, l);
+        if (b <= a) break;   // nothing new here, hence nothing above either
+        LevelArgs la;
+        memset(&la, 0, sizeof(la));
+        la.keys = k_cache;
+        if (l > 1) {
+            la.child_k = reinterpret_cast<const float *>(mem + t->key_off[l - 1]);
+            la.child_b = reinterpret_cast<const float *>(mem + t->bias_off[l - 1]);
+            la.child_cap = t->level_cap[l - 1];
+        }
+        la.out_k = reinterpret_cast<float *>(mem + t->key_off[l]);
+        la.out_b = reinterpret_cast<float *>(mem + t->bias_off[l]);
+        la.refs = t->refs;
+        la.max_tokens = g.max_tokens;
+        la.out_cap = t->level_cap[l];
+        la.j0 = a;
+        la.count = b - a;
+        la.kv_heads = g.num_kv_heads;
+        la.pairs = g.batch * g.num_kv_heads;
+        la.chunk = g.chunk;
+        la.refs_n = g.num_refs;
+        la.sharpness = g.sharpness;
+        hipError_t e = launch_level(la, g.head_dim, g.dtype, l == 1, st);
+        if (e != hipSuccess) return ZHA_ERR_HIP;
+    }
+    return ZHA_OK;
+}
+
+zha_status do_search(const zha_tree *t, const void *q, const zha_select *sel, int32_t *sel_blocks,
+                     int32_t *sel_count, zha_walk_stats *stats, uint32_t *status, void *ws,
+                     hipStream_t st) {
+    const zha_geometry &g = t->geom;
+    const int64_t walks = walks_of(&g, 1);
+    SearchWs lay = search_ws_layout(t, sel, walks);
+    const char *mem = static_cast<const char *>(t->tree_mem);
+    SearchArgs a;
+    memset(&a, 0, sizeof(a));
+    for (int l = 1; l <= g.levels; ++l) {
+        a.kap[l] = reinterpret_cast<const float *>(mem + t->key_off[l]);
+        a.bet[l] = reinterpret_cast<const float *>(mem + t->bias_off[l]);
+        a.cap[l] = t->level_cap[l];
+        a.nl[l] = level_count(t->n_tokens, g.chunk, l);
+    }
+    a.nl[0] = t->n_tokens;
+    a.nl[g.levels + 1] = 0;
+    a.q = q;
+    a.sel_blocks = sel_blocks;
+    a.sel_count = sel_count;
+    a.stats = stats;
+    a.status = status;
+    a.cand = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.cand);
+    a.score = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.score);
+    a.n_tokens = t->n_tokens;
+    a.walks = static_cast<int32_t>(walks);
+    a.heads = g.num_kv_heads * g.group_size;
+    a.group = g.group_size;
+    a.kv_heads = g.num_kv_heads;
+    a.chunk = g.chunk;
+    a.log2c = ilog2(g.chunk);
+    a.levels = g.levels;
+    a.mode = sel->mode;
+    a.p = sel->p;
+    for (int i = 0; i < ZHA_MAX_STEPS; ++i) {
+        if (sel->mode == ZHA_TOPK)
+            a.k[i] = sel->k[i < sel->num_k ? i : sel->num_k - 1];
+        else
+            a.k[i] = 1;
+    }
+    a.sel_cap = sel->max_blocks_per_walk;
+    a.cand_cap = cand_capacity(t, sel);
+    a.sharpness = g.sharpness;
+    return hip_status(launch_search(a, g.head_dim, g.num_refs, g.dtype, st));
+}
+
+zha_status do_attn(const zha_tree *t, const void *q, const void *k_cache, const void *v_cache,
+                   const zha_select *sel, const int32_t *sel_blocks, const int32_t *sel_count,
+                   void *out, void *ws, hipStream_t st) {
+    const zha_geometry &g = t->geom;
+    const int64_t walks = walks_of(&g, 1);
+    AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.out = out;
+    a.sel_blocks = sel_blocks;
+    a.sel_count = sel_count;
+    a.part = static_cast<float *>(ws);
+    a.max_tokens = g.max_tokens;
+    a.n_tokens = t->n_tokens;
+    a.n1 = level_count(t->n_tokens, g.chunk, 1);
+    a.walks = static_cast<int32_t>(walks);
+    a.heads = g.num_kv_heads * g.group_size;
+    a.group = g.group_size;
+    a.kv_heads = g.num_kv_heads;
+    a.chunk = g.chunk;
+    a.sel_cap = sel->max_blocks_per_walk;
+    a.splits = attn_splits(t, sel, walks);
+    a.sharpness = g.sharpness;
+    return hip_status(launch_attn(a, g.head_dim, g.dtype, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+uint64_t zha_tree_bytes(const zha_geometry *g) {
+    if (check_geometry(g) != ZHA_OK) return 0;
+    const uint64_t pairs = uint64_t(g->batch) * g->num_kv_heads;
+    uint64_t off = 0;
+    for (int l = 1; l <= g->levels; ++l) {
+        const uint64_t cap = static_cast<uint64_t>(level_count(g->max_tokens, g->chunk, l));
+        off += align_up(pairs * cap * g->num_refs * g->head_dim * sizeof(float));
+        off += align_up(pairs * cap * g->num_refs * sizeof(float));
+    }
+    return off;
+}
+
+zha_status zha_tree_init(zha_tree *t, const zha_geometry *g, void *tree_mem, uint64_t tree_bytes,
+                         const float *refs) {
+    if (!t) return ZHA_ERR_ARG;
+    zha_status s = check_geometry(g);
+    if (s != ZHA_OK) return s;
+    if (!tree_mem || !refs) return ZHA_ERR_ARG;
+    if (!aligned16(tree_mem) || !aligned16(refs)) return ZHA_ERR_ALIGN;
+    const uint64_t need = zha_tree_bytes(g);
+    if (tree_bytes < need) return ZHA_ERR_CAPACITY;
+    memset(t, 0, sizeof(*t));
+    t->geom = *g;
+    t->n_tokens = 0;
+    t->tree_mem = tree_mem;
+    t->tree_bytes = tree_bytes;
+    t->refs = refs;
+    const uint64_t pairs = uint64_t(g->batch) * g->num_kv_heads;
+    uint64_t off = 0;
+    for (int l = 1; l <= g->levels; ++l) {
+        const int64_t cap = level_count(g->max_tokens, g->chunk, l);
+        t->level_cap[l] = cap;
+        t->key_off[l] = off;
+        off += align_up(pairs * uint64_t(cap) * g->num_refs * g->head_dim * sizeof(float));
+        t->bias_off[l] = off;
+        off += align_up(pairs * uint64_t(cap) * g->num_refs * sizeof(float));
+    }
+    return ZHA_OK;
+}
+
+zha_status zha_build(zha_tree *t, const void *k_cache, int64_t n_tokens, void *stream) {
+    zha_status s = check_tree(t);
+    if (s != ZHA_OK) return s;
+    if (!k_cache) return ZHA_ERR_ARG;
+    if (!aligned16(k_cache)) return ZHA_ERR_ALIGN;
+    if (n_tokens < 0 || n_tokens > t->geom.max_tokens) return ZHA_ERR_CAPACITY;
+    s = run_levels(t, k_cache, 0, n_tokens, static_cast<hipStream_t>(stream));
+    if (s == ZHA_OK) t->n_tokens = n_tokens;
+    return s;
+}
+
+zha_status zha_append(zha_tree *t, const void *k_cache, int64_t n_new, void *stream) {
+    zha_status s = check_tree(t);
+    if (s != ZHA_OK) return s;
+    if (!k_cache) return ZHA_ERR_ARG;
+    if (!aligned16(k_cache)) return ZHA_ERR_ALIGN;
+    if (n_new < 0) return ZHA_ERR_ARG;
+    if (t->n_tokens + n_new > t->geom.max_tokens) return ZHA_ERR_CAPACITY;
+    s = run_levels(t, k_cache, t->n_tokens, t->n_tokens + n_new, static_cast<hipStream_t>(stream));
+    if (s == ZHA_OK) t->n_tokens += n_new;
+    return s;
+}
+
+uint64_t zha_search_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head) {
+    if (check_tree(t) != ZHA_OK || check_select(sel) != ZHA_OK || q_per_head < 1) return 0;
+    return search_ws_layout(t, sel, walks_of(&t->geom, q_per_head)).total;
+}
+
+zha_status zha_search(const zha_tree *t, const void *q, int32_t q_per_head, const zha_select *sel,
+                      int32_t *sel_blocks, int32_t *sel_count, zha_walk_stats *stats,
+                      uint32_t *status, void *ws, uint64_t ws_bytes, void *stream) {
+    zha_status s = check_tree(t);
+    if (s != ZHA_OK) return s;
+    if ((s = check_select(sel)) != ZHA_OK) return s;
+    if (q_per_head < 1) return ZHA_ERR_ARG;
+    if (q_per_head != 1) return ZHA_ERR_UNSUPPORTED;
+    if (!q || !sel_blocks || !sel_count || !status || !ws) return ZHA_ERR_ARG;
+    if (!aligned16(q) || !aligned16(ws) || !aligned_n(sel_blocks, 4) || !aligned_n(sel_count, 4) ||
+        !aligned_n(status, 4) || (stats && !aligned_n(stats, 8)))
+        return ZHA_ERR_ALIGN;
+    if (ws_bytes < zha_search_workspace_bytes(t, sel, q_per_head)) return ZHA_ERR_WORKSPACE;
+    return do_search(t, q, sel, sel_blocks, sel_count, stats, status, ws, static_cast<hipStream_t>(stream));
+}
+
+uint64_t zha_attn_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head) {
+    if (check_tree(t) != ZHA_OK || check_select(sel) != ZHA_OK || q_per_head < 1) return 0;
+    return attn_ws_bytes(t, sel, walks_of(&t->geom, q_per_head));
+}
+
+zha_status zha_sparse_attn(const zha_tree *t, const void *q, int32_t q_per_head, const void *k_cache,
+                           const void *v_cache, const zha_select *sel, const int32_t *sel_blocks,
+                           const int32_t *sel_count, void *out, void *ws, uint64_t ws_bytes,
+                           void *stream) {
+    zha_status s = check_tree(t);
+    if (s != ZHA_OK) return s;
+    if ((s = check_select(sel)) != ZHA_OK) return s;
+    if (q_per_head < 1) return ZHA_ERR_ARG;
+    if (q_per_head != 1) return ZHA_ERR_UNSUPPORTED;
+    if (!q || !k_cache || !v_cache || !sel_blocks || !sel_count || !out || !ws) return ZHA_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        !aligned16(ws) || !aligned_n(sel_blocks, 4) || !aligned_n(sel_count, 4))
+        return ZHA_ERR_ALIGN;
+    if (ws_bytes < zha_attn_workspace_bytes(t, sel, q_per_head)) return ZHA_ERR_WORKSPACE;
+    return do_attn(t, q, k_cache, v_cache, sel, sel_blocks, sel_count, out, ws,
+                   static_cast<hipStream_t>(stream));
+}
+
+uint64_t zha_forward_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head) {
+    if (check_tree(t) != ZHA_OK || check_select(sel) != ZHA_OK || q_per_head < 1) return 0;
+    return forward_ws_layout(t, sel, walks_of(&t->geom, q_per_head)).total;
+}
+
+zha_status zha_forward(zha_tree *t, int64_t n_new, const void *q, int32_t q_per_head,
+                       const void *k_cache, const void *v_cache, const zha_select *sel, void *out,
+                       zha_walk_stats *stats, uint32_t *status, void *ws, uint64_t ws_bytes,
+                       void *stream) {
+    zha_status s = check_tree(t);
+    if (s != ZHA_OK) return s;
+    if ((s = check_select(sel)) != ZHA_OK) return s;
+    if (q_per_head < 1 || n_new < 0) return ZHA_ERR_ARG;
+    if (q_per_head != 1) return ZHA_ERR_UNSUPPORTED;
+    if (!q || !k_cache || !v_cache || !out || !status || !ws) return ZHA_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        !aligned16(ws) || !aligned_n(status, 4) || (stats && !aligned_n(stats, 8)))
+        return ZHA_ERR_ALIGN;
+    if (t->n_tokens + n_new > t->geom.max_tokens) return ZHA_ERR_CAPACITY;
+    if (ws_bytes < zha_forward_workspace_bytes(t, sel, q_per_head)) return ZHA_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (n_new > 0) {
+        s = run_levels(t, k_cache, t->n_tokens, t->n_tokens + n_new, st);
+        if (s != ZHA_OK) return s;
+        t->n_tokens += n_new;
+    }
+    const int64_t walks = walks_of(&t->geom, 1);
+    ForwardWs lay = forward_ws_layout(t, sel, walks);
+    char *w = static_cast<char *>(ws);
+    int32_t *sb = reinterpret_cast<int32_t *>(w + lay.sel_blocks);
+    int32_t *sc = reinterpret_cast<int32_t *>(w + lay.sel_count);
+    s = do_search(t, q, sel, sb, sc, stats, status, w + lay.search, st);
+    if (s != ZHA_OK) return s;
+    return do_attn(t, q, k_cache, v_cache, sel, sb, sc, out, w + lay.attn, st);
+}
+
+uint64_t zha_dense_workspace_bytes(const zha_tree *t, int32_t q_per_head) {
+    (void)t;
+    (void)q_per_head;
+    return 0;
+}
+
+zha_status zha_dense_topk_attn(const zha_tree *t, const void *q, const void *k_cache,
+                               const void *v_cache, const int32_t *budget, void *out,
+                               int32_t *sel_tokens, void *ws, uint64_t ws_bytes, void *stream) {
+    (void)t; (void)q; (void)k_cache; (void)v_cache; (void)budget; (void)out;
+    (void)sel_tokens; (void)ws; (void)ws_bytes; (void)stream;
+    return ZHA_ERR_UNSUPPORTED;
+}
+
+zha_status zha_bw_probe(const void *buf, uint64_t bytes, float *sink, void *stream) {
+    if (!buf || !sink) return ZHA_ERR_ARG;
+    if (!aligned16(buf) || !aligned_n(sink, 4)) return ZHA_ERR_ALIGN;
+    return hip_status(launch_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
+const char *zha_status_string(zha_status s) {
+    switch (s) {
+        case ZHA_OK: return "ok";
+        case ZHA_ERR_ARG: return "invalid argument";
+        case ZHA_ERR_SHAPE: return "inconsistent shape";
+        case ZHA_ERR_ALIGN: return "device pointer not aligned";
+        case ZHA_ERR_CAPACITY: return "capacity exceeded";
+        case ZHA_ERR_WORKSPACE: return "workspace too small";
+        case ZHA_ERR_UNSUPPORTED: return "unsupported geometry or mode";
+        case ZHA_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

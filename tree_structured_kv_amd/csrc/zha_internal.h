@@ -1,0 +1,113 @@
+// zha_internal.h -- argument blocks shared by the host layer and the HIP
+// kernels of libzha.  Not part of the public ABI (see include/zha.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zha.h"
+
+namespace zha {
+
+// Candidate ids inside a walk: level in the top 4 bits, index in the rest.
+constexpr int kLevelShift = 28;
+constexpr uint32_t kIndexMask = (1u << kLevelShift) - 1u;
+constexpr int kBlock = 256;          // threads per workgroup of every kernel
+
+// One level of summaries for a node range, every (sequence, KV head) pair.
+struct LevelArgs {
+    const void *keys;          // level 1: K cache (pair stride max_tokens * D elements)
+    const float *child_k;      // level >= 2: keys of level l-1   (pair stride child_cap*R*D)
+    const float *child_b;      // level >= 2: biases of level l-1 (pair stride child_cap*R)
+    float *out_k;              // level l keys   (pair stride out_cap*R*D)
+    float *out_b;              // level l biases (pair stride out_cap*R)
+    const float *refs;         // [kv_heads][R][D]
+    int64_t max_tokens;
+    int64_t child_cap;
+    int64_t out_cap;
+    int64_t j0;                // first node to summarise
+    int64_t count;             // nodes to summarise per pair
+    int32_t kv_heads;
+    int32_t pairs;
+    int32_t chunk;
+    int32_t refs_n;
+    float sharpness;
+};
+
+struct SearchArgs {
+    const float *kap[ZHA_MAX_LEVELS + 1];  // level-l keys, pair 0
+    const float *bet[ZHA_MAX_LEVELS + 1];  // level-l biases, pair 0
+    int64_t cap[ZHA_MAX_LEVELS + 1];       // nodes per pair at level l (stride)
+    int64_t nl[ZHA_MAX_LEVELS + 2];        // live nodes at level l; nl[L+1] = 0
+    const void *q;                         // [walks][D]
+    int32_t *sel_blocks;                   // [walks][sel_cap]
+    int32_t *sel_count;                    // [walks]
+    zha_walk_stats *stats;                 // [walks] or null
+    uint32_t *status;
+    uint32_t *cand;                        // ws [walks][2][cand_cap]
+    float *score;                          // ws [walks][cand_cap]
+    int64_t n_tokens;
+    int32_t walks;
+    int32_t heads;                         // query heads per sequence
+    int32_t group;
+    int32_t kv_heads;
+    int32_t chunk;
+    int32_t log2c;
+    int32_t levels;
+    int32_t mode;
+    float p;
+    int32_t k[ZHA_MAX_STEPS];
+    int32_t sel_cap;
+    int32_t cand_cap;
+    float sharpness;
+};
+
+struct AttnArgs {
+    const void *q;                 // [walks][D]
+    const void *k;                 // cache
+    const void *v;                 // cache
+    void *out;                     // [walks][D]
+    const int32_t *sel_blocks;     // [walks][sel_cap]
+    const int32_t *sel_count;      // [walks]
+    float *part;                   // ws [walks][splits][D + 2]
+    int64_t max_tokens;
+    int64_t n_tokens;
+    int64_t n1;                    // whole level-1 chunks
+    int32_t walks;
+    int32_t heads;
+    int32_t group;
+    int32_t kv_heads;
+    int32_t chunk;
+    int32_t sel_cap;
+    int32_t splits;
+    float sharpness;
+};
+
+struct DenseArgs {
+    const void *q;                 // [walks][D]
+    const void *k;
+    const void *v;
+    void *out;
+    const int32_t *budget;         // [walks]
+    float *logits;                 // ws [walks][n_tokens_pad]
+    int32_t *sel;                  // ws [walks][n_tokens_pad]  (selected token ids)
+    int32_t *sel_n;                // ws [walks]
+    float *part;                   // ws [walks][splits][D + 2]
+    int64_t max_tokens;
+    int64_t n_tokens;
+    int64_t row_pad;               // logits/sel row stride
+    int32_t walks;
+    int32_t heads;
+    int32_t group;
+    int32_t kv_heads;
+    int32_t splits;
+    float sharpness;
+};
+
+hipError_t launch_level(const LevelArgs &a, int D, int dtype, bool leaf, hipStream_t st);
+hipError_t launch_search(const SearchArgs &a, int D, int R, int dtype, hipStream_t st);
+hipError_t launch_attn(const AttnArgs &a, int D, int dtype, hipStream_t st);
+hipError_t launch_dense(const DenseArgs &a, int D, int dtype, hipStream_t st);
+hipError_t launch_probe(const void *buf, uint64_t bytes, float *sink, hipStream_t st);
+
+}  // namespace zha
