@@ -66,6 +66,16 @@ typedef enum { ZHA_F32 = 0, ZHA_BF16 = 1 } zha_dtype;
 
 enum { ZHA_TOPP = 0, ZHA_TOPK = 1 };
 
+/* Search engines (zha_select.engine).  Both give identical results.
+ *   ZHA_ENGINE_PERSISTENT: one workgroup per walk runs all steps in one
+ *     launch; best when every walk does the same work (top-K).
+ *   ZHA_ENGINE_LEVEL_SYNC: per step, one launch scores the candidates of all
+ *     walks as one flat list and one launch cuts each walk; balances walks
+ *     of very different sizes (top-p).
+ *   ZHA_ENGINE_AUTO: level-synchronous for top-p with at least 64 walks,
+ *     persistent otherwise. */
+enum { ZHA_ENGINE_AUTO = 0, ZHA_ENGINE_PERSISTENT = 1, ZHA_ENGINE_LEVEL_SYNC = 2 };
+
 /* Device status bits. */
 #define ZHA_FLAG_CAND_OVERFLOW 1u  /* a step had more candidates than max_candidates;
                                       the excess (in span order) was dropped      */
@@ -109,7 +119,7 @@ typedef struct {
     int32_t num_k;
     int32_t max_blocks_per_walk;
     int32_t max_candidates;
-    int32_t reserved;
+    int32_t engine;          /* ZHA_ENGINE_*                                  */
 } zha_select;
 
 /* Host handle of one tree set (all sequences and KV heads).  Plain data: the

@@ -120,6 +120,8 @@ def test_search_argument_errors(Z):
     assert Z.lib.zha_search(*args(sel=bad)) == 1
     bad = Z.make_select("topp", float("nan"), max_blocks=8)
     assert Z.lib.zha_search(*args(sel=bad)) == 1
+    bad = Z.make_select("topp", 0.9, max_blocks=8, engine=7)
+    assert Z.lib.zha_search(*args(sel=bad)) == 1
 
 
 def test_workspace_sizes_grow_with_capacity(Z):

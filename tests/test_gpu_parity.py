@@ -114,11 +114,11 @@ SELECTS = {
 }
 
 
-def _run(Z, idx, Qt, Kt, Vt, select, max_blocks=None, max_candidates=0):
+def _run(Z, idx, Qt, Kt, Vt, select, max_blocks=None, max_candidates=0, engine="auto"):
     g = idx.geom
     if max_blocks is None:
         max_blocks = g.max_tokens // g.chunk
-    sel = P.select_struct(Z, select, max_blocks, max_candidates)
+    sel = P.select_struct(Z, select, max_blocks, max_candidates, engine)
     bufs = idx.search(Qt, sel)
     out = idx.sparse_attn(Qt, Kt, Vt, sel, bufs["sel_blocks"], bufs["sel_count"])
     torch.cuda.synchronize()
@@ -160,12 +160,13 @@ def _compare(w, K, V, Q, trees, select, bufs, out, min_stable=0.3):
     return stable, walks, worst
 
 
+@pytest.mark.parametrize("engine", ["persistent", "level-sync"])
 @pytest.mark.parametrize("sname", list(SELECTS))
 @pytest.mark.parametrize("name", CASES)
-def test_search_and_attention(Z, name, sname):
+def test_search_and_attention(Z, name, sname, engine):
     w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, name)
     select = SELECTS[sname]
-    sel, bufs, out = _run(Z, idx, Qt, Kt, Vt, select)
+    sel, bufs, out = _run(Z, idx, Qt, Kt, Vt, select, engine=engine)
     min_stable = 0.15 if name.startswith("demo") and select["mode"] == "topp" else 0.3
     _compare(w, K, V, Q, trees, select, bufs, out, min_stable=min_stable)
 
@@ -198,11 +199,12 @@ def test_widget_accounting_on_gpu(Z):
             assert (st["comparisons"], st["keys_read"], st["scored"], st["opened"]) == want
 
 
-def test_deterministic(Z):
+@pytest.mark.parametrize("engine", ["persistent", "level-sync"])
+def test_deterministic(Z, engine):
     w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, "clustered-small")
     select = SELECTS["topp90"]
-    _, b1, o1 = _run(Z, idx, Qt, Kt, Vt, select)
-    _, b2, o2 = _run(Z, idx, Qt, Kt, Vt, select)
+    _, b1, o1 = _run(Z, idx, Qt, Kt, Vt, select, engine=engine)
+    _, b2, o2 = _run(Z, idx, Qt, Kt, Vt, select, engine=engine)
     for k in ("sel_blocks", "sel_count", "stats"):
         c1 = b1["sel_count"]
         if k == "sel_blocks":
@@ -214,12 +216,28 @@ def test_deterministic(Z):
     assert torch.equal(o1, o2)
 
 
-def test_overflow_is_flagged_and_deterministic(Z):
+def test_engines_agree(Z):
+    """Both search engines give bit-identical selections, stats and outputs."""
+    for name in ("clustered-small", "mixed-small", "ar1-small"):
+        w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, name)
+        for select in (SELECTS["topp90"], SELECTS["topk4"]):
+            _, b1, o1 = _run(Z, idx, Qt, Kt, Vt, select, engine="persistent")
+            _, b2, o2 = _run(Z, idx, Qt, Kt, Vt, select, engine="level-sync")
+            assert torch.equal(b1["sel_count"], b2["sel_count"])
+            assert torch.equal(b1["stats"], b2["stats"])
+            for wi in range(b1["sel_count"].numel()):
+                n = int(b1["sel_count"][wi])
+                assert torch.equal(b1["sel_blocks"][wi, :n], b2["sel_blocks"][wi, :n])
+            assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("engine", ["persistent", "level-sync"])
+def test_overflow_is_flagged_and_deterministic(Z, engine):
     w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, "mixed-small")
     select = SELECTS["topp90"]
     for kw, flag in ((dict(max_blocks=2), Z.FLAG_SEL_OVERFLOW), (dict(max_candidates=20), Z.FLAG_CAND_OVERFLOW)):
-        _, b1, o1 = _run(Z, idx, Qt, Kt, Vt, select, **kw)
-        _, b2, o2 = _run(Z, idx, Qt, Kt, Vt, select, **kw)
+        _, b1, o1 = _run(Z, idx, Qt, Kt, Vt, select, engine=engine, **kw)
+        _, b2, o2 = _run(Z, idx, Qt, Kt, Vt, select, engine=engine, **kw)
         assert int(b1["status"].cpu()[0]) & flag
         assert torch.equal(o1, o2)
         assert torch.equal(b1["sel_count"], b2["sel_count"])

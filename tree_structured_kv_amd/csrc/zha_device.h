@@ -52,6 +52,31 @@ template <> struct Vec16<bf16_t> {
     }
 };
 
+// DPP cross-lane moves (gfx9 encodings): quad_perm xor 1 / xor 2, and the
+// 8- and 16-lane mirrors, which pair the two halves of a group once the
+// values are uniform inside each half.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+
+// Sum over aligned groups of WIDTH lanes (WIDTH in {16, 32}); every lane of
+// a group gets the group's sum.
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    v += dpp<kDppMirror>(v);
+    if (WIDTH == 32)   // swap the two 16-lane rows of each 32-lane half
+        v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+    return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v, int width) {
     for (int off = 1; off < width; off <<= 1) v += __shfl_xor(v, off, 64);
     return v;

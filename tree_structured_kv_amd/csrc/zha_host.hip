@@ -83,6 +83,7 @@ zha_status check_select(const zha_select *sel) {
     }
     if (sel->max_blocks_per_walk < 1) return ZHA_ERR_ARG;
     if (sel->max_candidates < 0) return ZHA_ERR_ARG;
+    if (sel->engine < ZHA_ENGINE_AUTO || sel->engine > ZHA_ENGINE_LEVEL_SYNC) return ZHA_ERR_ARG;
     return ZHA_OK;
 }
 
@@ -90,31 +91,43 @@ int64_t walks_of(const zha_geometry *g, int32_t qph) {
     return int64_t(g->batch) * g->num_kv_heads * g->group_size * qph;
 }
 
-int attn_splits(const zha_tree *t, const zha_select *sel, int64_t walks) {
-    const int64_t keys = int64_t(sel->max_blocks_per_walk) * t->geom.chunk + t->geom.chunk;
-    int64_t by_grid = (2048 + walks - 1) / walks;
-    int64_t by_keys = (keys + 255) / 256;
-    int64_t s = by_grid < by_keys ? by_grid : by_keys;
-    if (s < 1) s = 1;
-    if (s > 32) s = 32;
-    return static_cast<int>(s);
-}
-
 struct SearchWs {
-    uint64_t cand, score, total;
+    uint64_t cand, score, state, tile_count, tile_map, total;
 };
 SearchWs search_ws_layout(const zha_tree *t, const zha_select *sel, int64_t walks) {
     const uint64_t cap = static_cast<uint64_t>(cand_capacity(t, sel));
     SearchWs l;
     l.cand = 0;
     l.score = align_up(walks * 2 * cap * sizeof(uint32_t));
-    l.total = l.score + align_up(walks * cap * sizeof(float));
+    l.state = l.score + align_up(walks * cap * sizeof(float));
+    l.tile_count = l.state + align_up(walks * sizeof(WalkState));
+    l.tile_map = l.tile_count + align_up((ZHA_MAX_STEPS + 1) * sizeof(int32_t));
+    l.total = l.tile_map + align_up(walks * ((cap + kTile - 1) / kTile) * sizeof(int2));
+    return l;
+}
+
+int64_t attn_max_items(const zha_tree *t, const zha_select *sel, int64_t walks) {
+    const int64_t keys = int64_t(sel->max_blocks_per_walk) * t->geom.chunk + t->geom.chunk - 1;
+    int64_t per = (keys + kChunkKeys - 1) / kChunkKeys;
+    if (per < 1) per = 1;
+    return walks * per;
+}
+
+struct AttnWs {
+    uint64_t part, item_off, item_walk, total;
+};
+AttnWs attn_ws_layout(const zha_tree *t, const zha_select *sel, int64_t walks) {
+    const uint64_t items = static_cast<uint64_t>(attn_max_items(t, sel, walks));
+    AttnWs l;
+    l.part = 0;
+    l.item_off = align_up(items * (t->geom.head_dim + 2) * sizeof(float));
+    l.item_walk = l.item_off + align_up(uint64_t(walks + 1) * sizeof(int32_t));
+    l.total = l.item_walk + align_up(items * sizeof(int32_t));
     return l;
 }
 
 uint64_t attn_ws_bytes(const zha_tree *t, const zha_select *sel, int64_t walks) {
-    const int splits = attn_splits(t, sel, walks);
-    return align_up(uint64_t(walks) * splits * (t->geom.head_dim + 2) * sizeof(float));
+    return attn_ws_layout(t, sel, walks).total;
 }
 
 struct ForwardWs {
@@ -189,6 +202,10 @@ zha_status do_search(const zha_tree *t, const void *q, const zha_select *sel, in
     a.status = status;
     a.cand = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.cand);
     a.score = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.score);
+    a.state = reinterpret_cast<WalkState *>(static_cast<char *>(ws) + lay.state);
+    a.tile_count = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + lay.tile_count);
+    a.tile_map = reinterpret_cast<int2 *>(static_cast<char *>(ws) + lay.tile_map);
+    a.score_grid = 1024;
     a.n_tokens = t->n_tokens;
     a.walks = static_cast<int32_t>(walks);
     a.heads = g.num_kv_heads * g.group_size;
@@ -208,7 +225,14 @@ zha_status do_search(const zha_tree *t, const void *q, const zha_select *sel, in
     a.sel_cap = sel->max_blocks_per_walk;
     a.cand_cap = cand_capacity(t, sel);
     a.sharpness = g.sharpness;
-    return hip_status(launch_search(a, g.head_dim, g.num_refs, g.dtype, st));
+    // roots: all level-L nodes plus the parentless nodes of lower levels
+    int64_t n0 = a.nl[g.levels];
+    for (int l = 1; l < g.levels; ++l) n0 += a.nl[l] - int64_t(g.chunk) * a.nl[l + 1];
+    if (n0 > a.cand_cap) n0 = a.cand_cap;
+    int engine = sel->engine;
+    if (engine == ZHA_ENGINE_AUTO)
+        engine = (sel->mode == ZHA_TOPP && walks >= 64) ? ZHA_ENGINE_LEVEL_SYNC : ZHA_ENGINE_PERSISTENT;
+    return hip_status(launch_search(a, g.head_dim, g.num_refs, g.dtype, engine, static_cast<int>(n0), st));
 }
 
 zha_status do_attn(const zha_tree *t, const void *q, const void *k_cache, const void *v_cache,
@@ -224,7 +248,11 @@ zha_status do_attn(const zha_tree *t, const void *q, const void *k_cache, const 
     a.out = out;
     a.sel_blocks = sel_blocks;
     a.sel_count = sel_count;
-    a.part = static_cast<float *>(ws);
+    AttnWs lay = attn_ws_layout(t, sel, walks);
+    char *wb = static_cast<char *>(ws);
+    a.part = reinterpret_cast<float *>(wb + lay.part);
+    a.item_off = reinterpret_cast<int32_t *>(wb + lay.item_off);
+    a.item_walk = reinterpret_cast<int32_t *>(wb + lay.item_walk);
     a.max_tokens = g.max_tokens;
     a.n_tokens = t->n_tokens;
     a.n1 = level_count(t->n_tokens, g.chunk, 1);
@@ -234,7 +262,8 @@ zha_status do_attn(const zha_tree *t, const void *q, const void *k_cache, const 
     a.kv_heads = g.num_kv_heads;
     a.chunk = g.chunk;
     a.sel_cap = sel->max_blocks_per_walk;
-    a.splits = attn_splits(t, sel, walks);
+    const int64_t items = attn_max_items(t, sel, walks);
+    a.grid = static_cast<int32_t>(items < 2048 ? items : 2048);
     a.sharpness = g.sharpness;
     return hip_status(launch_attn(a, g.head_dim, g.dtype, st));
 }

@@ -12,7 +12,21 @@ namespace zha {
 // Candidate ids inside a walk: level in the top 4 bits, index in the rest.
 constexpr int kLevelShift = 28;
 constexpr uint32_t kIndexMask = (1u << kLevelShift) - 1u;
-constexpr int kBlock = 256;          // threads per workgroup of every kernel
+constexpr int kBlock = 256;          // threads per workgroup of most kernels
+constexpr int kChunkKeys = 1024;     // keys per attention work item
+constexpr int kTile = 32;            // candidates per tile of the level-synchronous scorer
+
+// Per-walk state of the level-synchronous search engine (workspace).
+struct WalkState {
+    int32_t n;                       // candidates of the current step (0 = finished)
+    int32_t buf;                     // current candidate buffer (0 or 1)
+    int32_t sel_n;                   // level-1 blocks found so far (before clamp)
+    int32_t unforced;                // candidates scored so far
+    uint32_t flags;
+    int32_t steps;
+    int32_t scored[ZHA_MAX_STEPS];
+    int32_t opened[ZHA_MAX_STEPS];
+};
 
 // One level of summaries for a node range, every (sequence, KV head) pair.
 struct LevelArgs {
@@ -46,6 +60,9 @@ struct SearchArgs {
     uint32_t *status;
     uint32_t *cand;                        // ws [walks][2][cand_cap]
     float *score;                          // ws [walks][cand_cap]
+    WalkState *state;                      // ws [walks]          (level-synchronous)
+    int32_t *tile_count;                   // ws [ZHA_MAX_STEPS+1] (level-synchronous)
+    int2 *tile_map;                        // ws [walks * ceil(cand_cap / kTile)]
     int64_t n_tokens;
     int32_t walks;
     int32_t heads;                         // query heads per sequence
@@ -59,6 +76,7 @@ struct SearchArgs {
     int32_t k[ZHA_MAX_STEPS];
     int32_t sel_cap;
     int32_t cand_cap;
+    int32_t score_grid;                    // workgroups of the level-synchronous scorer
     float sharpness;
 };
 
@@ -69,7 +87,9 @@ struct AttnArgs {
     void *out;                     // [walks][D]
     const int32_t *sel_blocks;     // [walks][sel_cap]
     const int32_t *sel_count;      // [walks]
-    float *part;                   // ws [walks][splits][D + 2]
+    float *part;                   // ws [max_items][D + 2]
+    int32_t *item_off;             // ws [walks + 1]: first item of each walk
+    int32_t *item_walk;            // ws [max_items]: walk of each item
     int64_t max_tokens;
     int64_t n_tokens;
     int64_t n1;                    // whole level-1 chunks
@@ -79,7 +99,7 @@ struct AttnArgs {
     int32_t kv_heads;
     int32_t chunk;
     int32_t sel_cap;
-    int32_t splits;
+    int32_t grid;                  // workgroups of the item loop
     float sharpness;
 };
 
@@ -105,7 +125,8 @@ struct DenseArgs {
 };
 
 hipError_t launch_level(const LevelArgs &a, int D, int dtype, bool leaf, hipStream_t st);
-hipError_t launch_search(const SearchArgs &a, int D, int R, int dtype, hipStream_t st);
+hipError_t launch_search(const SearchArgs &a, int D, int R, int dtype, int engine, int n0,
+                         hipStream_t st);
 hipError_t launch_attn(const AttnArgs &a, int D, int dtype, hipStream_t st);
 hipError_t launch_dense(const DenseArgs &a, int D, int dtype, hipStream_t st);
 hipError_t launch_probe(const void *buf, uint64_t bytes, float *sink, hipStream_t st);

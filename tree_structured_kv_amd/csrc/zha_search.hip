@@ -1,4 +1,4 @@
-// zha_search.hip -- top-down tree walk for decode queries.
+// zha_search.hip -- top-down tree walks for decode queries.
 //
 // [ZHA lesson] = the page "How does a tree of summaries search a context? How
 // ZHA works".
@@ -14,10 +14,20 @@
 //     exactly K.
 //   "Common misunderstandings": every query head walks on its own.
 //
-// GPU design: one workgroup (4 wavefronts) per walk, the level loop inside
-// the kernel, no host round trip.  A candidate's R keys are one contiguous
-// R*D*4-byte record; a wavefront reads it with 16-byte loads (D/4 lanes per
-// reference), reduces the dot products across lanes and takes the max over
+// Two engines share the scoring, cut and opening code below.
+//
+// * Persistent (k_search_decode): one workgroup (8 wavefronts) per walk, the
+//   step loop inside the kernel, no host round trip.  Best when every walk
+//   does the same work (top-K).
+// * Level-synchronous (k_ls_*): per step, one grid-wide scoring launch over
+//   a flat list of 32-candidate tiles of all walks, then one cut launch with
+//   a workgroup per walk.  Kernel boundaries are the only synchronisation.
+//   Under top-p a few walks can score ten times the median; spreading their
+//   candidates over the whole GPU keeps every CU streaming.
+//
+// Scoring: a candidate's R keys are one contiguous R*D*4-byte record; a
+// wavefront reads it with 16-byte loads (D/4 lanes per reference), sums the
+// dot products with DPP/swizzle cross-lane adds and takes the max over
 // references.  The cut is an exact radix select over 64-bit rank keys
 // (ordered score bits, then the complement of the span start, so equal
 // scores open in span order).  For top-p the softmax masses are integers
@@ -31,7 +41,10 @@ namespace zha {
 
 namespace {
 
-constexpr int kWaves = kBlock / 64;
+constexpr int kThreads = 512;          // workgroup of the persistent and cut kernels
+constexpr int kWaves = kThreads / 64;
+constexpr int kScoreThreads = 256;     // workgroup of the level-synchronous scorer
+constexpr int kU = 4;                  // candidates in flight per wavefront
 constexpr float kMassScale = 2147483648.0f;  // 2^31
 
 __device__ __forceinline__ uint64_t rank_key(float score, uint32_t id, int log2c) {
@@ -47,7 +60,6 @@ struct SelectShared {
     unsigned long long hw[256];
     unsigned long long scan64[kWaves];
     unsigned long long tau;
-    unsigned long long need;
     unsigned long long above;
     uint32_t dig;
     uint32_t cnt;
@@ -55,8 +67,8 @@ struct SelectShared {
     uint32_t flags;
 };
 
-// Block-wide exclusive scan of a uint64 per thread; returns the prefix and
-// writes the total to *total.
+// Block-wide exclusive scan of a uint64 per thread (kThreads threads);
+// returns the prefix and writes the total to *total.
 __device__ __forceinline__ unsigned long long block_exscan64(unsigned long long v,
                                                              unsigned long long *scratch,
                                                              unsigned long long *total) {
@@ -81,308 +93,526 @@ __device__ __forceinline__ unsigned long long block_exscan64(unsigned long long 
     return base + incl - v;
 }
 
-}  // namespace
+template <int D, typename QT>
+__device__ __forceinline__ void load_q(const SearchArgs &a, int w, float (&qv)[4]) {
+    constexpr int LPR = D / 4;
+    const int sub = (threadIdx.x & 63) % LPR;
+    const QT *qp = static_cast<const QT *>(a.q) + static_cast<int64_t>(w) * D + 4 * sub;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qv[e] = Elem<QT>::load(qp, e);
+}
 
-template <int D, int R, typename QT>
-__global__ __launch_bounds__(kBlock) void k_search_decode(SearchArgs a) {
+__device__ __forceinline__ bool step_forced(const SearchArgs &a, int t, int n) {
+    return (n <= 1) || (a.mode == ZHA_TOPK && a.k[t] >= n) || (a.mode == ZHA_TOPP && a.p >= 1.0f);
+}
+
+// One wavefront scores candidates first, first + stride, ... below `end`, kU
+// at a time, and writes sc[i]; returns the largest score it wrote.
+template <int D, int R>
+__device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair, const float (&qv)[4],
+                                            const uint32_t *cur, float *sc, int first, int end,
+                                            int stride, uint32_t &flags) {
     constexpr int LPR = D / 4;            // lanes per reference row (float4 each)
     constexpr int RPL = 64 / LPR;         // references per 64-lane load
     constexpr int NL = (R + RPL - 1) / RPL;
-    constexpr int U = 2;                  // candidates in flight per wavefront
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int w = xcd_remap(blockIdx.x, gridDim.x);
-    if (w >= a.walks) return;
-    const int b = w / a.heads, h = w % a.heads, g = h / a.group;
-    const int64_t pair = static_cast<int64_t>(b) * a.kv_heads + g;
-    const int c = a.chunk, log2c = a.log2c, L = a.levels;
-    const float s = a.sharpness;
-    const int cap = a.cand_cap;
-
-    __shared__ SelectShared sh;
-    __shared__ int32_t s_scored[ZHA_MAX_STEPS], s_opened[ZHA_MAX_STEPS];
-    if (tid == 0) sh.flags = 0;
-
-    // this lane's 4 query elements
+    const int lane = threadIdx.x & 63;
     const int sub = lane % LPR, rsub = lane / LPR;
-    float qv[4];
-    {
-        const QT *qp = static_cast<const QT *>(a.q) + static_cast<int64_t>(w) * D + 4 * sub;
+    const float s = a.sharpness;
+    float wmax = -INFINITY;
+    if (first >= end) return wmax;
+
+    uint32_t ids[kU];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qv[e] = Elem<QT>::load(qp, e);
+    for (int u = 0; u < kU; ++u) {
+        const int i = first + u;
+        ids[u] = cur[i < end ? i : end - 1];
+    }
+    for (int base = first; base < end; base += stride) {
+        float4 kv[kU][NL];
+        float bv[kU][NL];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const uint32_t id = ids[u];
+            const int lvl = static_cast<int>(id >> kLevelShift);
+            const int64_t node = pair * a.cap[lvl] + static_cast<int64_t>(id & kIndexMask);
+            const float *kp = a.kap[lvl] + node * (R * D);
+            const float *bp = a.bet[lvl] + node * R;
+#pragma unroll
+            for (int l = 0; l < NL; ++l) {
+                const int r = l * RPL + rsub;
+                if (r < R) {
+                    kv[u][l] = *reinterpret_cast<const float4 *>(kp + r * D + 4 * sub);
+                    bv[u][l] = bp[r];
+                } else {
+                    kv[u][l] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    bv[u][l] = -INFINITY;
+                }
+            }
+        }
+        // ids of the next round, fetched while this round's records stream in
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int i = base + stride + u;
+            ids[u] = cur[i < end ? i : end - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            float best = -INFINITY;
+#pragma unroll
+            for (int l = 0; l < NL; ++l) {
+                float d = kv[u][l].x * qv[0];
+                d = fmaf(kv[u][l].y, qv[1], d);
+                d = fmaf(kv[u][l].z, qv[2], d);
+                d = fmaf(kv[u][l].w, qv[3], d);
+                d = group_sum<LPR>(d);
+                best = fmaxf(best, fmaf(s, d, bv[u][l]));
+            }
+            // max over the RPL reference groups of the wavefront
+            float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(best), 0));
+#pragma unroll
+            for (int gq = 1; gq < RPL; ++gq)
+                m = fmaxf(m, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(best), gq * LPR)));
+            if (m != m) { m = -INFINITY; flags |= ZHA_FLAG_NONFINITE; }
+            if (m == 0.f) m = 0.f;          // one zero
+            const int i = base + u;
+            if (i < end) {
+                if (lane == 0) sc[i] = m;
+                wmax = fmaxf(wmax, m);
+            }
+        }
+    }
+    return wmax;
+}
+
+// Workgroup (kThreads): the rank key of the candidate at the cut of a step
+// that is not forced; every candidate with a key >= it opens.
+__device__ unsigned long long cut_tau(const SearchArgs &a, int n, const uint32_t *cur,
+                                      const float *sc, float mx, int kt, SelectShared &sh) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int log2c = a.log2c;
+    const bool by_mass = (a.mode == ZHA_TOPP) && (a.p > 0.f);
+    const bool flat = !(mx > -INFINITY);   // every score -inf: equal masses
+    unsigned long long target;
+    if (by_mass) {
+        unsigned long long zpart = 0;
+        for (int i = tid; i < n; i += kThreads) {
+            const float e = flat ? 1.f : expf(sc[i] - mx);
+            zpart += static_cast<unsigned long long>(__float2uint_rn(e * kMassScale));
+        }
+        unsigned long long z;
+        (void)block_exscan64(zpart, sh.scan64, &z);
+        const double tq = ceil(static_cast<double>(a.p) * static_cast<double>(z));
+        target = static_cast<unsigned long long>(tq);
+        if (target < 1) target = 1;
+        if (target > z) target = z;
+    } else {
+        const int m = (a.mode == ZHA_TOPK) ? (kt < n ? kt : n) : 1;
+        target = static_cast<unsigned long long>(m < 1 ? 1 : m);
     }
 
-    uint32_t *cur = a.cand + static_cast<int64_t>(w) * 2 * cap;
-    uint32_t *nxt = cur + cap;
-    float *sc = a.score + static_cast<int64_t>(w) * cap;
-    int32_t *selw = a.sel_blocks + static_cast<int64_t>(w) * a.sel_cap;
+    unsigned long long prefix = 0, need = target, tau = 0;
+    for (int pass = 0; pass < 8; ++pass) {
+        const int shift = 56 - 8 * pass;
+        for (int i = tid; i < 256; i += kThreads) { sh.hcnt[i] = 0; sh.hw[i] = 0; }
+        __syncthreads();
+        for (int i = tid; i < n; i += kThreads) {
+            const float scv = sc[i];
+            const unsigned long long key = rank_key(scv, cur[i], log2c);
+            if (pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8))) {
+                const uint32_t dg = static_cast<uint32_t>(key >> shift) & 255u;
+                unsigned long long wgt = 1;
+                if (by_mass) {
+                    const float e = flat ? 1.f : expf(scv - mx);
+                    wgt = static_cast<unsigned long long>(__float2uint_rn(e * kMassScale));
+                }
+                atomicAdd(&sh.hcnt[dg], 1u);
+                if (wgt) atomicAdd(&sh.hw[dg], wgt);
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane covers digits 255-4*lane .. 252-4*lane (descending)
+            unsigned long long lw[4], lsum = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { lw[e] = sh.hw[255 - 4 * lane - e]; lsum += lw[e]; }
+            unsigned long long incl = lsum;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                unsigned long long o = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += o;
+            }
+            const unsigned long long excl = incl - lsum;
+            const unsigned long long mask = __ballot(incl >= need);
+            const int first = mask ? (__ffsll(static_cast<long long>(mask)) - 1) : 63;
+            if (lane == first) {
+                unsigned long long run = excl;
+                int pick = 3;
+                for (int e = 0; e < 4; ++e) {
+                    if (run + lw[e] >= need) { pick = e; break; }
+                    run += lw[e];
+                }
+                if (!mask) { pick = 3; run = excl + lw[0] + lw[1] + lw[2]; }
+                const uint32_t dg = 255u - 4u * lane - pick;
+                sh.dig = dg;
+                sh.above = run;
+                sh.cnt = sh.hcnt[dg];
+            }
+        }
+        __syncthreads();
+        prefix |= static_cast<unsigned long long>(sh.dig) << shift;
+        need -= sh.above;
+        const uint32_t cnt = sh.cnt;
+        if (pass == 7) {
+            tau = prefix;
+            break;
+        }
+        if (cnt <= 1) {
+            // at most one key carries this prefix: fetch it
+            for (int i = tid; i < n; i += kThreads) {
+                const unsigned long long key = rank_key(sc[i], cur[i], log2c);
+                if ((key >> shift) == (prefix >> shift)) sh.tau = key;
+            }
+            __syncthreads();
+            tau = (cnt == 0) ? 0ull : sh.tau;
+            __syncthreads();
+            break;
+        }
+        __syncthreads();
+    }
+    return tau;
+}
 
-    // Roots: every level-L node, then the nodes of lower levels whose parent
-    // chunk is not full yet, in span order.
-    uint32_t flags = 0;
+// Workgroup (kThreads): open every candidate with a rank key >= tau (all if
+// forced), in candidate order: level-1 nodes append their block id to the
+// selection, others append their c children to nxt.  Returns the number of
+// level-1 and of higher nodes opened.
+__device__ void open_cut(const SearchArgs &a, int n, const uint32_t *cur, const float *sc,
+                         bool forced, unsigned long long tau, uint32_t *nxt, int32_t *selw,
+                         int64_t sel_n, uint32_t &ta, uint32_t &tb, SelectShared &sh) {
+    const int tid = threadIdx.x;
+    const int c = a.chunk, log2c = a.log2c, cap = a.cand_cap;
+    const int per = (n + kThreads - 1) / kThreads;
+    const int i0 = tid * per;
+    const int i1 = min(n, i0 + per);
+    uint32_t ca = 0, cb = 0;
+    for (int i = i0; i < i1; ++i) {
+        const uint32_t id = cur[i];
+        const bool open = forced || rank_key(sc[i], id, log2c) >= tau;
+        if (open) { if ((id >> kLevelShift) == 1u) ++ca; else ++cb; }
+    }
+    unsigned long long tot;
+    const unsigned long long off =
+        block_exscan64((static_cast<unsigned long long>(ca) << 32) | cb, sh.scan64, &tot);
+    uint32_t oa = static_cast<uint32_t>(off >> 32), ob = static_cast<uint32_t>(off);
+    ta = static_cast<uint32_t>(tot >> 32);
+    tb = static_cast<uint32_t>(tot);
+    for (int i = i0; i < i1; ++i) {
+        const uint32_t id = cur[i];
+        const bool open = forced || rank_key(sc[i], id, log2c) >= tau;
+        if (!open) continue;
+        const uint32_t lvl = id >> kLevelShift, j = id & kIndexMask;
+        if (lvl == 1u) {
+            const int64_t pos = sel_n + oa++;
+            if (pos < a.sel_cap) selw[pos] = static_cast<int32_t>(j);
+        } else {
+            const int64_t base = static_cast<int64_t>(ob++) * c;
+            const uint32_t cid = ((lvl - 1u) << kLevelShift);
+            for (int e = 0; e < c; ++e) {
+                if (base + e < cap) nxt[base + e] = cid | (j * static_cast<uint32_t>(c) + e);
+            }
+        }
+    }
+}
+
+// Workgroup: the roots -- every level-L node, then the nodes of lower levels
+// whose parent chunk is not full yet, in span order.  Returns their number
+// (clamped to the candidate capacity).
+__device__ int write_roots(const SearchArgs &a, uint32_t *cur, uint32_t &flags) {
+    const int tid = threadIdx.x, c = a.chunk, L = a.levels, cap = a.cand_cap;
     int64_t n_roots = 0;
     for (int l = L; l >= 1; --l) {
         const int64_t first = (l == L) ? 0 : static_cast<int64_t>(c) * a.nl[l + 1];
         const int64_t cnt = a.nl[l] - first;
-        for (int64_t i = tid; i < cnt; i += kBlock) {
+        for (int64_t i = tid; i < cnt; i += blockDim.x) {
             const int64_t pos = n_roots + i;
             if (pos < cap) cur[pos] = (static_cast<uint32_t>(l) << kLevelShift) | static_cast<uint32_t>(first + i);
         }
         n_roots += cnt;
     }
     if (n_roots > cap) { flags |= ZHA_FLAG_CAND_OVERFLOW; n_roots = cap; }
-    int n = static_cast<int>(n_roots);
+    return static_cast<int>(n_roots);
+}
+
+// One thread: sel_count, status and the per-walk statistics.
+template <int R>
+__device__ void finish_walk(const SearchArgs &a, int w, int steps, const int32_t *scored,
+                            const int32_t *opened, int64_t sel_n, int32_t unforced, uint32_t fl) {
+    if (sel_n > a.sel_cap) fl |= ZHA_FLAG_SEL_OVERFLOW;
+    a.sel_count[w] = static_cast<int32_t>(sel_n < a.sel_cap ? sel_n : a.sel_cap);
+    if (fl) atomicOr(a.status, fl);
+    if (a.stats) {
+        zha_walk_stats st;
+        int64_t tot_scored = 0;
+        for (int i = 0; i < ZHA_MAX_STEPS; ++i) {
+            st.scored[i] = i < steps ? scored[i] : 0;
+            st.opened[i] = i < steps ? opened[i] : 0;
+            if (i < steps) tot_scored += scored[i];
+        }
+        const int64_t tail = a.n_tokens - static_cast<int64_t>(a.chunk) * a.nl[1];
+        st.steps = steps;
+        st.keys_read = static_cast<int32_t>(sel_n * a.chunk + tail);
+        st.blocks = static_cast<int32_t>(sel_n);
+        st.unforced_scored = unforced;
+        st.comparisons = tot_scored * R + st.keys_read;
+        st.flags = fl;
+        st.reserved = 0;
+        a.stats[w] = st;
+    }
+}
+
+__device__ __forceinline__ float block_max(float v, SelectShared &sh) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_max(v, 1, 64);
+    if (lane == 0) sh.red[wave] = v;
+    __syncthreads();
+    float m = sh.red[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) m = fmaxf(m, sh.red[i]);
+    __syncthreads();
+    return m;
+}
+
+}  // namespace
+
+// ---- persistent engine --------------------------------------------------------
+
+template <int D, int R, typename QT>
+__global__ __launch_bounds__(kThreads) void k_search_decode(SearchArgs a) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int w = xcd_remap(blockIdx.x, gridDim.x);
+    if (w >= a.walks) return;
+    const int b = w / a.heads, h = w % a.heads, g = h / a.group;
+    const int64_t pair = static_cast<int64_t>(b) * a.kv_heads + g;
+    const int cap = a.cand_cap;
+
+    __shared__ SelectShared sh;
+    __shared__ int32_t s_scored[ZHA_MAX_STEPS], s_opened[ZHA_MAX_STEPS];
+    if (tid == 0) sh.flags = 0;
+
+    float qv[4];
+    load_q<D, QT>(a, w, qv);
+
+    uint32_t *cur = a.cand + static_cast<int64_t>(w) * 2 * cap;
+    uint32_t *nxt = cur + cap;
+    float *sc = a.score + static_cast<int64_t>(w) * cap;
+    int32_t *selw = a.sel_blocks + static_cast<int64_t>(w) * a.sel_cap;
+
+    uint32_t flags = 0;
+    int n = write_roots(a, cur, flags);
     __syncthreads();
 
     int64_t sel_n = 0;
     int32_t unforced = 0;
     int t = 0;
     for (; t < ZHA_MAX_STEPS && n > 0; ++t) {
-        const int kt = a.k[t];
-        const bool forced = (n == 1) || (a.mode == ZHA_TOPK && kt >= n) ||
-                            (a.mode == ZHA_TOPP && a.p >= 1.0f);
+        const bool forced = step_forced(a, t, n);
         unsigned long long tau = 0;
         if (!forced) {
-            // ---- score every candidate ----------------------------------
-            float wmax = -INFINITY;
-            for (int base = wave * U; base < n; base += kWaves * U) {
-                float4 kv[U][NL];
-                float bv[U][NL];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int i = base + u;
-                    const uint32_t id = (i < n) ? cur[i] : cur[base];
-                    const int lvl = static_cast<int>(id >> kLevelShift);
-                    const int64_t node = pair * a.cap[lvl] + static_cast<int64_t>(id & kIndexMask);
-                    const float *kp = a.kap[lvl] + node * (R * D);
-                    const float *bp = a.bet[lvl] + node * R;
-#pragma unroll
-                    for (int l = 0; l < NL; ++l) {
-                        const int r = l * RPL + rsub;
-                        if (r < R) {
-                            kv[u][l] = *reinterpret_cast<const float4 *>(kp + r * D + 4 * sub);
-                            bv[u][l] = bp[r];
-                        } else {
-                            kv[u][l] = make_float4(0.f, 0.f, 0.f, 0.f);
-                            bv[u][l] = -INFINITY;
-                        }
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    float best = -INFINITY;
-#pragma unroll
-                    for (int l = 0; l < NL; ++l) {
-                        float d = kv[u][l].x * qv[0];
-                        d = fmaf(kv[u][l].y, qv[1], d);
-                        d = fmaf(kv[u][l].z, qv[2], d);
-                        d = fmaf(kv[u][l].w, qv[3], d);
-                        d = wave_sum(d, LPR);
-                        const float v = fmaf(s, d, bv[u][l]);
-                        best = fmaxf(best, v);
-                    }
-                    best = wave_max(best, LPR, 64);
-                    if (best != best) { best = -INFINITY; flags |= ZHA_FLAG_NONFINITE; }
-                    if (best == 0.f) best = 0.f;          // one zero
-                    const int i = base + u;
-                    if (i < n) {
-                        if (lane == 0) sc[i] = best;
-                        wmax = fmaxf(wmax, best);
-                    }
-                }
-            }
+            float wmax = score_wave<D, R>(a, pair, qv, cur, sc, wave * kU, n, kWaves * kU, flags);
             if (lane == 0) sh.red[wave] = wmax;
             __syncthreads();
             float mx = sh.red[0];
 #pragma unroll
             for (int i = 1; i < kWaves; ++i) mx = fmaxf(mx, sh.red[i]);
-
-            // ---- cut target ----------------------------------------------
-            const bool by_mass = (a.mode == ZHA_TOPP) && (a.p > 0.f);
-            const bool flat = !(mx > -INFINITY);   // every score -inf: equal masses
-            unsigned long long target;
-            if (by_mass) {
-                unsigned long long zpart = 0;
-                for (int i = tid; i < n; i += kBlock) {
-                    const float e = flat ? 1.f : expf(sc[i] - mx);
-                    zpart += static_cast<unsigned long long>(__float2uint_rn(e * kMassScale));
-                }
-                unsigned long long z;
-                (void)block_exscan64(zpart, sh.scan64, &z);
-                double tq = ceil(static_cast<double>(a.p) * static_cast<double>(z));
-                target = static_cast<unsigned long long>(tq);
-                if (target < 1) target = 1;
-                if (target > z) target = z;
-            } else {
-                const int m = (a.mode == ZHA_TOPK) ? (kt < n ? kt : n) : 1;
-                target = static_cast<unsigned long long>(m < 1 ? 1 : m);
-            }
-
-            // ---- radix select of the crossing rank key ---------------------
-            unsigned long long prefix = 0, need = target;
-            bool found = false;
-            for (int pass = 0; pass < 8 && !found; ++pass) {
-                const int shift = 56 - 8 * pass;
-                for (int i = tid; i < 256; i += kBlock) { sh.hcnt[i] = 0; sh.hw[i] = 0; }
-                __syncthreads();
-                for (int i = tid; i < n; i += kBlock) {
-                    const float scv = sc[i];
-                    const unsigned long long key = rank_key(scv, cur[i], log2c);
-                    if (pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8))) {
-                        const uint32_t dg = static_cast<uint32_t>(key >> shift) & 255u;
-                        unsigned long long wgt = 1;
-                        if (by_mass) {
-                            const float e = flat ? 1.f : expf(scv - mx);
-                            wgt = static_cast<unsigned long long>(__float2uint_rn(e * kMassScale));
-                        }
-                        atomicAdd(&sh.hcnt[dg], 1u);
-                        if (wgt) atomicAdd(&sh.hw[dg], wgt);
-                    }
-                }
-                __syncthreads();
-                if (wave == 0) {
-                    // lane covers digits 255-4*lane .. 252-4*lane (descending)
-                    unsigned long long lw[4], lsum = 0;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) { lw[e] = sh.hw[255 - 4 * lane - e]; lsum += lw[e]; }
-                    unsigned long long incl = lsum;
-#pragma unroll
-                    for (int off = 1; off < 64; off <<= 1) {
-                        unsigned long long o = __shfl_up(incl, off, 64);
-                        if (lane >= off) incl += o;
-                    }
-                    const unsigned long long excl = incl - lsum;
-                    unsigned long long mask = __ballot(incl >= need);
-                    int first = mask ? (__ffsll(static_cast<long long>(mask)) - 1) : 63;
-                    if (lane == first) {
-                        unsigned long long run = excl;
-                        int pick = 3;
-                        for (int e = 0; e < 4; ++e) {
-                            if (run + lw[e] >= need) { pick = e; break; }
-                            run += lw[e];
-                        }
-                        if (!mask) { pick = 3; run = excl + lw[0] + lw[1] + lw[2]; }
-                        const uint32_t dg = 255u - 4u * lane - pick;
-                        sh.dig = dg;
-                        sh.above = run;
-                        sh.cnt = sh.hcnt[dg];
-                    }
-                }
-                __syncthreads();
-                prefix |= static_cast<unsigned long long>(sh.dig) << shift;
-                need -= sh.above;
-                if (sh.cnt <= 1 || pass == 7) {
-                    if (pass == 7) {
-                        tau = prefix;
-                    } else {
-                        // exactly one key carries this prefix: fetch it
-                        for (int i = tid; i < n; i += kBlock) {
-                            const unsigned long long key = rank_key(sc[i], cur[i], log2c);
-                            if ((key >> shift) == (prefix >> shift)) sh.tau = key;
-                        }
-                        __syncthreads();
-                        tau = (sh.cnt == 0) ? 0ull : sh.tau;
-                    }
-                    found = true;
-                }
-                __syncthreads();
-            }
+            tau = cut_tau(a, n, cur, sc, mx, a.k[t], sh);
             unforced += n;
         }
-
-        // ---- open: compact in candidate (span) order ------------------------
-        const int per = (n + kBlock - 1) / kBlock;
-        const int i0 = tid * per;
-        const int i1 = min(n, i0 + per);
-        uint32_t ca = 0, cb = 0;
-        for (int i = i0; i < i1; ++i) {
-            const uint32_t id = cur[i];
-            const bool open = forced || rank_key(sc[i], id, log2c) >= tau;
-            if (open) { if ((id >> kLevelShift) == 1u) ++ca; else ++cb; }
-        }
-        unsigned long long tot;
-        const unsigned long long off =
-            block_exscan64((static_cast<unsigned long long>(ca) << 32) | cb, sh.scan64, &tot);
-        uint32_t oa = static_cast<uint32_t>(off >> 32), ob = static_cast<uint32_t>(off);
-        const uint32_t ta = static_cast<uint32_t>(tot >> 32), tb = static_cast<uint32_t>(tot);
-        for (int i = i0; i < i1; ++i) {
-            const uint32_t id = cur[i];
-            const bool open = forced || rank_key(sc[i], id, log2c) >= tau;
-            if (!open) continue;
-            const uint32_t lvl = id >> kLevelShift, j = id & kIndexMask;
-            if (lvl == 1u) {
-                const int64_t pos = sel_n + oa++;
-                if (pos < a.sel_cap) selw[pos] = static_cast<int32_t>(j);
-            } else {
-                const int64_t base = static_cast<int64_t>(ob++) * c;
-                const uint32_t cid = ((lvl - 1u) << kLevelShift);
-                for (int e = 0; e < c; ++e) {
-                    if (base + e < cap) nxt[base + e] = cid | (j * static_cast<uint32_t>(c) + e);
-                }
-            }
-        }
+        uint32_t ta, tb;
+        open_cut(a, n, cur, sc, forced, tau, nxt, selw, sel_n, ta, tb, sh);
         if (tid == 0) {
             s_scored[t] = n;
             s_opened[t] = static_cast<int32_t>(ta + tb);
         }
         sel_n += ta;
-        int64_t nn = static_cast<int64_t>(tb) * c;
+        int64_t nn = static_cast<int64_t>(tb) * a.chunk;
         if (nn > cap) { flags |= ZHA_FLAG_CAND_OVERFLOW; nn = cap; }
         uint32_t *tmp = cur; cur = nxt; nxt = tmp;
         n = static_cast<int>(nn);
         __syncthreads();
     }
-    if (sel_n > a.sel_cap) flags |= ZHA_FLAG_SEL_OVERFLOW;
-
-    // ---- outputs ------------------------------------------------------------
     if (flags) atomicOr(&sh.flags, flags);
     __syncthreads();
+    if (tid == 0) finish_walk<R>(a, w, t, s_scored, s_opened, sel_n, unforced, sh.flags);
+}
+
+// ---- level-synchronous engine ---------------------------------------------------
+
+template <int R>
+__global__ __launch_bounds__(kThreads) void k_ls_init(SearchArgs a) {
+    const int tid = threadIdx.x;
+    const int w = blockIdx.x;
+    const int cap = a.cand_cap;
+    if (w == 0 && tid <= ZHA_MAX_STEPS) a.tile_count[tid] = 0;
+    __shared__ uint32_t s_flags;
+    if (tid == 0) s_flags = 0;
+    __syncthreads();
+    uint32_t flags = 0;
+    uint32_t *cur = a.cand + static_cast<int64_t>(w) * 2 * cap;
+    const int n = write_roots(a, cur, flags);
+    if (flags) atomicOr(&s_flags, flags);
+    __syncthreads();
     if (tid == 0) {
-        const uint32_t fl = sh.flags;
-        a.sel_count[w] = static_cast<int32_t>(sel_n < a.sel_cap ? sel_n : a.sel_cap);
-        if (fl) atomicOr(a.status, fl);
-        if (a.stats) {
-            zha_walk_stats st;
-            int64_t tot_scored = 0;
-            for (int i = 0; i < ZHA_MAX_STEPS; ++i) {
-                st.scored[i] = i < t ? s_scored[i] : 0;
-                st.opened[i] = i < t ? s_opened[i] : 0;
-                if (i < t) tot_scored += s_scored[i];
-            }
-            const int64_t tail = a.n_tokens - static_cast<int64_t>(c) * a.nl[1];
-            st.steps = t;
-            st.keys_read = static_cast<int32_t>(sel_n * c + tail);
-            st.blocks = static_cast<int32_t>(sel_n);
-            st.unforced_scored = unforced;
-            st.comparisons = tot_scored * R + st.keys_read;
-            st.flags = fl;
-            st.reserved = 0;
-            a.stats[w] = st;
-        }
+        WalkState st;
+        st.n = n;
+        st.buf = 0;
+        st.sel_n = 0;
+        st.unforced = 0;
+        st.flags = s_flags;
+        st.steps = 0;
+        for (int i = 0; i < ZHA_MAX_STEPS; ++i) { st.scored[i] = 0; st.opened[i] = 0; }
+        a.state[w] = st;
+        if (n == 0) finish_walk<R>(a, w, 0, st.scored, st.opened, 0, 0, st.flags);
     }
+}
+
+// Step t scoring over a flat tile list: at step 0 every walk has the same
+// roots, so its tiles are laid out arithmetically; later steps use the tiles
+// the cut kernel of the step before registered.
+template <int D, int R, typename QT>
+__global__ __launch_bounds__(kScoreThreads) void k_ls_score(SearchArgs a, int t, int tiles0) {
+    constexpr int kSW = kScoreThreads / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_tiles = (t == 0) ? a.walks * tiles0 : a.tile_count[t];
+    for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+        int w, start;
+        if (t == 0) {
+            w = tile / tiles0;
+            start = (tile % tiles0) * kTile;
+        } else {
+            const int2 e = a.tile_map[tile];
+            w = e.x;
+            start = e.y;
+        }
+        const int n = a.state[w].n;
+        const int buf = a.state[w].buf;
+        const int end = min(n, start + kTile);
+        const int b = w / a.heads, h = w % a.heads, g = h / a.group;
+        const int64_t pair = static_cast<int64_t>(b) * a.kv_heads + g;
+        const uint32_t *cur = a.cand + static_cast<int64_t>(w) * 2 * a.cand_cap +
+                              static_cast<int64_t>(buf) * a.cand_cap;
+        float *sc = a.score + static_cast<int64_t>(w) * a.cand_cap;
+        float qv[4];
+        load_q<D, QT>(a, w, qv);
+        uint32_t flags = 0;
+        (void)score_wave<D, R>(a, pair, qv, cur, sc, start + wave * kU, end, kSW * kU, flags);
+        if (flags && lane == 0) atomicOr(a.status, flags);
+    }
+}
+
+// Step t cut: one workgroup per walk.
+template <int R>
+__global__ __launch_bounds__(kThreads) void k_ls_cut(SearchArgs a, int t) {
+    const int tid = threadIdx.x;
+    const int w = blockIdx.x;
+    __shared__ SelectShared sh;
+    __shared__ WalkState st;
+    __shared__ int s_base;
+    if (tid == 0) st = a.state[w];
+    __syncthreads();
+    const int n = st.n;
+    if (n <= 0) return;                    // finished earlier (uniform)
+    const int cap = a.cand_cap;
+    uint32_t *bufs = a.cand + static_cast<int64_t>(w) * 2 * cap;
+    const uint32_t *cur = bufs + static_cast<int64_t>(st.buf) * cap;
+    uint32_t *nxt = bufs + static_cast<int64_t>(st.buf ^ 1) * cap;
+    const float *sc = a.score + static_cast<int64_t>(w) * cap;
+    int32_t *selw = a.sel_blocks + static_cast<int64_t>(w) * a.sel_cap;
+
+    const bool forced = step_forced(a, t, n);
+    unsigned long long tau = 0;
+    if (!forced) {
+        float m = -INFINITY;
+        for (int i = tid; i < n; i += kThreads) m = fmaxf(m, sc[i]);
+        const float mx = block_max(m, sh);
+        tau = cut_tau(a, n, cur, sc, mx, a.k[t], sh);
+    }
+    uint32_t ta, tb;
+    open_cut(a, n, cur, sc, forced, tau, nxt, selw, st.sel_n, ta, tb, sh);
+    __syncthreads();
+    if (tid == 0) {
+        int64_t nn = static_cast<int64_t>(tb) * a.chunk;
+        if (nn > cap) { st.flags |= ZHA_FLAG_CAND_OVERFLOW; nn = cap; }
+        st.scored[t] = n;
+        st.opened[t] = static_cast<int32_t>(ta + tb);
+        if (!forced) st.unforced += n;
+        st.sel_n += static_cast<int32_t>(ta);
+        st.steps = t + 1;
+        st.buf ^= 1;
+        st.n = static_cast<int32_t>(nn);
+        if (st.n == 0 || t + 1 >= a.levels || t + 1 >= ZHA_MAX_STEPS) {
+            st.n = 0;
+            finish_walk<R>(a, w, t + 1, st.scored, st.opened, st.sel_n, st.unforced, st.flags);
+        }
+        a.state[w] = st;
+        s_base = 0;
+        if (st.n > 0 && !step_forced(a, t + 1, st.n))
+            s_base = atomicAdd(&a.tile_count[t + 1], (st.n + kTile - 1) / kTile);
+    }
+    __syncthreads();
+    // register the next step's tiles unless its cut needs no scores
+    if (st.n > 0 && !step_forced(a, t + 1, st.n)) {
+        const int ntile = (st.n + kTile - 1) / kTile;
+        for (int k = tid; k < ntile; k += kThreads) a.tile_map[s_base + k] = make_int2(w, k * kTile);
+    }
+}
+
+// ---- launchers ---------------------------------------------------------------------
+
+template <int D, int R, typename QT>
+static hipError_t launch_t(const SearchArgs &a, int engine, int n0, hipStream_t st) {
+    if (engine != ZHA_ENGINE_LEVEL_SYNC) {
+        hipLaunchKernelGGL((k_search_decode<D, R, QT>), dim3(a.walks), dim3(kThreads), 0, st, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((k_ls_init<R>), dim3(a.walks), dim3(kThreads), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int tiles0 = (n0 + kTile - 1) / kTile;
+    for (int t = 0; t < a.levels && t < ZHA_MAX_STEPS; ++t) {
+        // step 0's forcing is the same for every walk (same roots)
+        const bool skip = (t == 0) && (n0 <= 1 || (a.mode == ZHA_TOPK && a.k[0] >= n0) ||
+                                       (a.mode == ZHA_TOPP && a.p >= 1.0f));
+        if (!skip) {
+            hipLaunchKernelGGL((k_ls_score<D, R, QT>), dim3(a.score_grid), dim3(kScoreThreads), 0, st,
+                               a, t, tiles0 > 0 ? tiles0 : 1);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL((k_ls_cut<R>), dim3(a.walks), dim3(kThreads), 0, st, a, t);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int D, typename QT>
-static hipError_t launch_search_d(const SearchArgs &a, int R, hipStream_t st) {
-    dim3 grid(static_cast<unsigned>(a.walks));
+static hipError_t launch_search_d(const SearchArgs &a, int R, int engine, int n0, hipStream_t st) {
     switch (R) {
-        case 1: hipLaunchKernelGGL((k_search_decode<D, 1, QT>), grid, dim3(kBlock), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((k_search_decode<D, 2, QT>), grid, dim3(kBlock), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((k_search_decode<D, 4, QT>), grid, dim3(kBlock), 0, st, a); break;
-        case 8: hipLaunchKernelGGL((k_search_decode<D, 8, QT>), grid, dim3(kBlock), 0, st, a); break;
-        case 16: hipLaunchKernelGGL((k_search_decode<D, 16, QT>), grid, dim3(kBlock), 0, st, a); break;
+        case 1: return launch_t<D, 1, QT>(a, engine, n0, st);
+        case 2: return launch_t<D, 2, QT>(a, engine, n0, st);
+        case 4: return launch_t<D, 4, QT>(a, engine, n0, st);
+        case 8: return launch_t<D, 8, QT>(a, engine, n0, st);
+        case 16: return launch_t<D, 16, QT>(a, engine, n0, st);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
-hipError_t launch_search(const SearchArgs &a, int D, int R, int dtype, hipStream_t st) {
+hipError_t launch_search(const SearchArgs &a, int D, int R, int dtype, int engine, int n0,
+                         hipStream_t st) {
     if (a.walks <= 0) return hipSuccess;
     if (D == 64)
-        return dtype == ZHA_BF16 ? launch_search_d<64, bf16_t>(a, R, st)
-                                 : launch_search_d<64, float>(a, R, st);
-    return dtype == ZHA_BF16 ? launch_search_d<128, bf16_t>(a, R, st)
-                             : launch_search_d<128, float>(a, R, st);
+        return dtype == ZHA_BF16 ? launch_search_d<64, bf16_t>(a, R, engine, n0, st)
+                                 : launch_search_d<64, float>(a, R, engine, n0, st);
+    return dtype == ZHA_BF16 ? launch_search_d<128, bf16_t>(a, R, engine, n0, st)
+                             : launch_search_d<128, float>(a, R, engine, n0, st);
 }
 
 }  // namespace zha

@@ -21,6 +21,8 @@ MAX_STEPS = 8
 TOPP, TOPK = 0, 1
 F32, BF16 = 0, 1
 FLAG_CAND_OVERFLOW, FLAG_SEL_OVERFLOW, FLAG_NONFINITE = 1, 2, 4
+ENGINE_AUTO, ENGINE_PERSISTENT, ENGINE_LEVEL_SYNC = 0, 1, 2
+ENGINES = {"auto": ENGINE_AUTO, "persistent": ENGINE_PERSISTENT, "level-sync": ENGINE_LEVEL_SYNC}
 
 STATUS = {0: "ZHA_OK", 1: "ZHA_ERR_ARG", 2: "ZHA_ERR_SHAPE", 3: "ZHA_ERR_ALIGN",
           4: "ZHA_ERR_CAPACITY", 5: "ZHA_ERR_WORKSPACE", 6: "ZHA_ERR_UNSUPPORTED",
@@ -40,7 +42,7 @@ class Select(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("p", ctypes.c_float),
                 ("k", ctypes.c_int32 * MAX_STEPS), ("num_k", ctypes.c_int32),
                 ("max_blocks_per_walk", ctypes.c_int32), ("max_candidates", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("engine", ctypes.c_int32)]
 
 
 class TreeHandle(ctypes.Structure):
@@ -136,7 +138,7 @@ def make_geometry(batch, kv_heads, group, head_dim, chunk, refs, levels, dtype, 
                     int(max_tokens), float(sharpness), 0)
 
 
-def make_select(mode="topp", p=0.9, k=(1,), max_blocks=1024, max_candidates=0) -> Select:
+def make_select(mode="topp", p=0.9, k=(1,), max_blocks=1024, max_candidates=0, engine="auto") -> Select:
     s = Select()
     s.mode = TOPK if mode in ("topk", TOPK) else TOPP
     s.p = float(p)
@@ -146,6 +148,7 @@ def make_select(mode="topp", p=0.9, k=(1,), max_blocks=1024, max_candidates=0) -
         s.k[i] = int(ks[min(i, len(ks) - 1)])
     s.max_blocks_per_walk = int(max_blocks)
     s.max_candidates = int(max_candidates)
+    s.engine = ENGINES[engine] if isinstance(engine, str) else int(engine)
     return s
 
 
