@@ -96,18 +96,40 @@ def hbm_probe(Z, gib=4.0, reps=5):
     return best
 
 
-def walk_bytes(w, stats_rows):
-    """Algorithmic bytes of the walks: per unforced-scored candidate one node
-    record R*(4d+4); per walk its query (read) ...; per selected key its K and
-    V rows; per walk one output row."""
+def walk_bytes(w, stats_rows, union_scored=None, union_keys=None):
+    """Algorithmic bytes of one decode step.
+
+    Search: one node record, R*(4d+4) bytes, per node an unforced cut needs
+    scored -- counted once per (sequence, KV head) pair (the union over the
+    group's query heads, from the search's `visited` bitmap) -- plus each
+    walk's query row.  Attention: the K and V rows of every selected key,
+    once per pair (union over the group's heads), plus each walk's query and
+    output rows.  The per-head sums (no union) are reported beside them."""
     e = 2 if w.dtype == "bf16" else 4
     nu = w.refs * (4 * w.d + 4)
+    walks = len(stats_rows)
     scored = sum(s["unforced_scored"] for s in stats_rows)
     keys = sum(s["keys_read"] for s in stats_rows)
-    walks = len(stats_rows)
-    search = nu * scored + walks * w.d * e
-    attn = 2 * w.d * e * keys + walks * w.d * e * 2
-    return search, attn, scored, keys
+    u_sc = scored if union_scored is None else union_scored
+    u_k = keys if union_keys is None else union_keys
+    return dict(
+        search=nu * u_sc + walks * w.d * e,
+        attn=2 * w.d * e * u_k + 2 * walks * w.d * e,
+        search_per_head=nu * scored + walks * w.d * e,
+        attn_per_head=2 * w.d * e * keys + 2 * walks * w.d * e,
+        scored=scored, union_scored=u_sc, keys=keys, union_keys=u_k)
+
+
+def union_keys(w, blocks, count):
+    """Selected keys counted once per (sequence, KV head) pair."""
+    tail = w.n - w.chunk * (w.n // w.chunk)
+    tot = 0
+    for b in range(w.batch):
+        for g in range(w.kv_heads):
+            rows = [b * w.heads + h for h in range(g * w.group, (g + 1) * w.group)]
+            ids = np.concatenate([blocks[r, :count[r]] for r in rows])
+            tot += np.unique(ids).size * w.chunk + tail
+    return tot
 
 
 _PREPARED = {}
@@ -157,13 +179,19 @@ def run_gpu(Z, w, select, steps, warmup, threads):
             evs[2].record()
 
     # accounting pass (untimed): the walks of every query rotation
-    per_rot = []
+    per_rot, acct = [], []
+    vis = idx.visited_bitmap()
     for r in range(ROTATIONS):
-        step(r)
+        vis.zero_()
+        idx.search(Q[r], sel, bufs, visited=vis)
+        idx.sparse_attn(Q[r], K, V, sel, bufs["sel_blocks"], bufs["sel_count"], out, aws)
         torch.cuda.synchronize()
         rows = Zm.stats_to_dicts(bufs["stats"].cpu())
         per_rot.append(rows)
         status = int(bufs["status"].cpu()[0])
+        u_sc = int(np.unpackbits(vis.cpu().numpy().view(np.uint8)).sum())
+        u_k = union_keys(w, bufs["sel_blocks"].cpu().numpy(), bufs["sel_count"].cpu().numpy())
+        acct.append(walk_bytes(w, rows, u_sc, u_k))
     for r in range(warmup):
         step(r)
     torch.cuda.synchronize()
@@ -178,10 +206,8 @@ def run_gpu(Z, w, select, steps, warmup, threads):
     attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
 
     # per-step bytes in the order the steps ran
-    sb, ab, sc_, kr_ = [], [], [], []
-    for i in range(steps):
-        s, a, sc, kr = walk_bytes(w, per_rot[i % ROTATIONS])
-        sb.append(s); ab.append(a); sc_.append(sc); kr_.append(kr)
+    by_step = [acct[i % ROTATIONS] for i in range(steps)]
+    mean = {k: float(np.mean([a[k] for a in by_step])) for k in by_step[0]}
     walks = w.batch * w.heads
     comps = [np.mean([s["comparisons"] for s in rows]) for rows in per_rot]
     keys = [np.mean([s["keys_read"] for s in rows]) for rows in per_rot]
@@ -197,7 +223,7 @@ def run_gpu(Z, w, select, steps, warmup, threads):
         qps=w.batch * steps / wall,
         walks_per_s=walks * steps / wall,
         search_ms=float(np.mean(search_ms)), attn_ms=float(np.mean(attn_ms)),
-        search_bytes=float(np.mean(sb)), attn_bytes=float(np.mean(ab)),
+        search_bytes=mean["search"], attn_bytes=mean["attn"], bytes=mean,
         build_ms=build_ms,
         comparisons_per_walk=float(np.mean(comps)),
         keys_read_per_walk=float(np.mean(keys)),
@@ -256,18 +282,24 @@ def cpu_baseline(w, select, Q_host, seconds_budget=15.0):
 def summary(res, bw_ach):
     w = res["workload"]
     sel = res["select"]
-    s_gbs = res["search_bytes"] / (res["search_ms"] * 1e-3) / 1e9
-    step_bytes = res["search_bytes"] + res["attn_bytes"]
+    by = res["bytes"]
+    s_gbs = by["search"] / (res["search_ms"] * 1e-3) / 1e9
+    a_gbs = by["attn"] / (res["attn_ms"] * 1e-3) / 1e9
+    step_bytes = by["search"] + by["attn"]
     step_gbs = step_bytes / (res["ms_per_step"] * 1e-3) / 1e9
     return dict(
         workload=w.name, select=sel,
         qps=res["qps"], walks_per_s=res["walks_per_s"], ms_per_step=res["ms_per_step"],
         search_ms=res["search_ms"], attn_ms=res["attn_ms"], build_ms=res["build_ms"],
-        search_gbs=s_gbs, step_gbs=step_gbs,
+        search_bytes=by["search"], attn_bytes=by["attn"],
+        search_bytes_per_head=by["search_per_head"], attn_bytes_per_head=by["attn_per_head"],
+        search_gbs=s_gbs, attn_gbs=a_gbs, step_gbs=step_gbs,
         step_frac_of_peak=step_gbs / HBM_PEAK_GBS,
         step_frac_of_achievable=(step_gbs / bw_ach) if bw_ach else None,
         comparisons_per_walk=res["comparisons_per_walk"],
         keys_read_per_walk=res["keys_read_per_walk"], dense_keys=w.n,
+        nodes_scored_per_step=by["scored"], nodes_scored_union_per_step=by["union_scored"],
+        keys_per_step=by["keys"], keys_union_per_step=by["union_keys"],
         status=res["status"], per_walk=res["dist"],
     )
 
@@ -340,14 +372,12 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": ach / HBM_PEAK_GBS, "traffic": None,
-            "kernel": "k_search_decode", "bytes_per_launch": res["search_bytes"],
-            "launch_ms": main_sum["search_ms"], "achievable_gbs": bw_ach,
+            "kernel": "zha_search (level-synchronous: k_ls_score + k_ls_cut launches)",
+            "bytes_per_launch": main_sum["search_bytes"], "launch_ms": main_sum["search_ms"],
+            "achievable_gbs": bw_ach,
         },
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
-        "step": {k: main_sum[k] for k in ("search_ms", "attn_ms", "build_ms", "step_gbs",
-                                          "step_frac_of_peak", "step_frac_of_achievable",
-                                          "comparisons_per_walk", "keys_read_per_walk",
-                                          "dense_keys", "walks_per_s", "status")},
+        "step": {k: v for k, v in main_sum.items() if k not in ("workload", "select", "qps")},
         "also": also,
     }
     print(json.dumps(out), flush=True)

@@ -204,12 +204,23 @@ uint64_t zha_search_workspace_bytes(const zha_tree *t, const zha_select *sel, in
  *   sel_count   device int32 [walks]: blocks stored (<= max_blocks_per_walk)
  *   stats       device zha_walk_stats [walks], may be NULL
  *   status      device uint32, OR-ed with ZHA_FLAG_* (not cleared)
+ *   visited     device uint32 [batch*kv_heads][zha_visited_words/pairs], may be
+ *               NULL (see zha_visited_words)
  * walks = batch * kv_heads * group_size * q_per_head, in Q's order.
  * q_per_head > 1 (prefill blocks) returns ZHA_ERR_UNSUPPORTED. */
 zha_status zha_search(const zha_tree *t, const void *q, int32_t q_per_head,
                       const zha_select *sel, int32_t *sel_blocks, int32_t *sel_count,
-                      zha_walk_stats *stats, uint32_t *status,
+                      zha_walk_stats *stats, uint32_t *status, uint32_t *visited,
                       void *ws, uint64_t ws_bytes, void *stream);
+
+/* 32-bit words of the optional `visited` bitmap of zha_search: per (sequence,
+ * KV head) pair, one bit per node of every level (levels 1..L one after the
+ * other, each max_tokens/chunk^l nodes long), rounded up to whole words.
+ * When `visited` is given, every node whose score an unforced cut needed
+ * sets its bit (OR; the caller clears it).  The set bits are the records a
+ * search has to read at least once per pair, whatever the number of query
+ * heads that scored them. */
+uint64_t zha_visited_words(const zha_tree *t);
 
 /* ---- 3. sparse attention --------------------------------------------------- */
 

@@ -107,10 +107,11 @@ def test_search_argument_errors(Z):
     assert ws > 0
     args = lambda **o: [ctypes.byref(t), o.get("q", 0x400000), o.get("qph", 1), ctypes.byref(o.get("sel", sel)),
                         o.get("blocks", 0x500000), o.get("count", 0x600000), None, o.get("status", 0x700000),
-                        o.get("ws", 0x800000), o.get("wsb", ws), None]
+                        o.get("visited", None), o.get("ws", 0x800000), o.get("wsb", ws), None]
     assert Z.lib.zha_search(*args(q=None)) == 1
     assert Z.lib.zha_search(*args(q=0x400002)) == 3
     assert Z.lib.zha_search(*args(status=None)) == 1
+    assert Z.lib.zha_search(*args(visited=0x900002)) == 3
     assert Z.lib.zha_search(*args(wsb=ws - 1)) == 5
     assert Z.lib.zha_search(*args(qph=0)) == 1
     assert Z.lib.zha_search(*args(qph=4)) == 6
@@ -122,6 +123,11 @@ def test_search_argument_errors(Z):
     assert Z.lib.zha_search(*args(sel=bad)) == 1
     bad = Z.make_select("topp", 0.9, max_blocks=8, engine=7)
     assert Z.lib.zha_search(*args(sel=bad)) == 1
+
+
+def test_visited_words(Z):
+    t = _handle(Z)
+    assert Z.zha_visited_words(t) == 4 * ((512 + 64 + 8 + 31) // 32)
 
 
 def test_workspace_sizes_grow_with_capacity(Z):

@@ -178,9 +178,15 @@ zha_status run_levels(zha_tree *t, const void *k_cache, int64_t n_old, int64_t n
     return ZHA_OK;
 }
 
+int64_t visited_words_per_pair(const zha_tree *t) {
+    int64_t bits = 0;
+    for (int l = 1; l <= t->geom.levels; ++l) bits += t->level_cap[l];
+    return (bits + 31) / 32;
+}
+
 zha_status do_search(const zha_tree *t, const void *q, const zha_select *sel, int32_t *sel_blocks,
-                     int32_t *sel_count, zha_walk_stats *stats, uint32_t *status, void *ws,
-                     hipStream_t st) {
+                     int32_t *sel_count, zha_walk_stats *stats, uint32_t *status, uint32_t *visited,
+                     void *ws, hipStream_t st) {
     const zha_geometry &g = t->geom;
     const int64_t walks = walks_of(&g, 1);
     SearchWs lay = search_ws_layout(t, sel, walks);
@@ -200,6 +206,15 @@ zha_status do_search(const zha_tree *t, const void *q, const zha_select *sel, in
     a.sel_count = sel_count;
     a.stats = stats;
     a.status = status;
+    a.visited = visited;
+    a.vis_words = visited_words_per_pair(t);
+    {
+        int64_t off = 0;
+        for (int l = 1; l <= g.levels; ++l) {
+            a.node_off[l] = off;
+            off += t->level_cap[l];
+        }
+    }
     a.cand = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.cand);
     a.score = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.score);
     a.state = reinterpret_cast<WalkState *>(static_cast<char *>(ws) + lay.state);
@@ -340,9 +355,14 @@ uint64_t zha_search_workspace_bytes(const zha_tree *t, const zha_select *sel, in
     return search_ws_layout(t, sel, walks_of(&t->geom, q_per_head)).total;
 }
 
+uint64_t zha_visited_words(const zha_tree *t) {
+    if (check_tree(t) != ZHA_OK) return 0;
+    return static_cast<uint64_t>(visited_words_per_pair(t)) * t->geom.batch * t->geom.num_kv_heads;
+}
+
 zha_status zha_search(const zha_tree *t, const void *q, int32_t q_per_head, const zha_select *sel,
                       int32_t *sel_blocks, int32_t *sel_count, zha_walk_stats *stats,
-                      uint32_t *status, void *ws, uint64_t ws_bytes, void *stream) {
+                      uint32_t *status, uint32_t *visited, void *ws, uint64_t ws_bytes, void *stream) {
     zha_status s = check_tree(t);
     if (s != ZHA_OK) return s;
     if ((s = check_select(sel)) != ZHA_OK) return s;
@@ -350,10 +370,11 @@ zha_status zha_search(const zha_tree *t, const void *q, int32_t q_per_head, cons
     if (q_per_head != 1) return ZHA_ERR_UNSUPPORTED;
     if (!q || !sel_blocks || !sel_count || !status || !ws) return ZHA_ERR_ARG;
     if (!aligned16(q) || !aligned16(ws) || !aligned_n(sel_blocks, 4) || !aligned_n(sel_count, 4) ||
-        !aligned_n(status, 4) || (stats && !aligned_n(stats, 8)))
+        !aligned_n(status, 4) || (stats && !aligned_n(stats, 8)) || (visited && !aligned_n(visited, 4)))
         return ZHA_ERR_ALIGN;
     if (ws_bytes < zha_search_workspace_bytes(t, sel, q_per_head)) return ZHA_ERR_WORKSPACE;
-    return do_search(t, q, sel, sel_blocks, sel_count, stats, status, ws, static_cast<hipStream_t>(stream));
+    return do_search(t, q, sel, sel_blocks, sel_count, stats, status, visited, ws,
+                     static_cast<hipStream_t>(stream));
 }
 
 uint64_t zha_attn_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head) {
@@ -410,7 +431,7 @@ zha_status zha_forward(zha_tree *t, int64_t n_new, const void *q, int32_t q_per_
     char *w = static_cast<char *>(ws);
     int32_t *sb = reinterpret_cast<int32_t *>(w + lay.sel_blocks);
     int32_t *sc = reinterpret_cast<int32_t *>(w + lay.sel_count);
-    s = do_search(t, q, sel, sb, sc, stats, status, w + lay.search, st);
+    s = do_search(t, q, sel, sb, sc, stats, status, nullptr, w + lay.search, st);
     if (s != ZHA_OK) return s;
     return do_attn(t, q, k_cache, v_cache, sel, sb, sc, out, w + lay.attn, st);
 }

@@ -58,6 +58,9 @@ struct SearchArgs {
     int32_t *sel_count;                    // [walks]
     zha_walk_stats *stats;                 // [walks] or null
     uint32_t *status;
+    uint32_t *visited;                     // [pairs][vis_words] or null
+    int64_t node_off[ZHA_MAX_LEVELS + 1];  // bit of node (l, 0) in a pair's bitmap
+    int64_t vis_words;                     // bitmap words per pair
     uint32_t *cand;                        // ws [walks][2][cand_cap]
     float *score;                          // ws [walks][cand_cap]
     WalkState *state;                      // ws [walks]          (level-synchronous)

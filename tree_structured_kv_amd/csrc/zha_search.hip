@@ -176,7 +176,14 @@ __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair, c
             if (m == 0.f) m = 0.f;          // one zero
             const int i = base + u;
             if (i < end) {
-                if (lane == 0) sc[i] = m;
+                if (lane == 0) {
+                    sc[i] = m;
+                    if (a.visited) {
+                        const uint32_t id = cur[i];
+                        const int64_t bit = a.node_off[id >> kLevelShift] + (id & kIndexMask);
+                        atomicOr(a.visited + pair * a.vis_words + (bit >> 5), 1u << (bit & 31));
+                    }
+                }
                 wmax = fmaxf(wmax, m);
             }
         }

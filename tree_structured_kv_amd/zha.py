@@ -65,7 +65,7 @@ class WalkStats(ctypes.Structure):
 STATS_WORDS = ctypes.sizeof(WalkStats) // 4   # int32 words per stats record
 
 EXPORTS = ["zha_tree_bytes", "zha_tree_init", "zha_build", "zha_append",
-           "zha_search_workspace_bytes", "zha_search", "zha_attn_workspace_bytes",
+           "zha_search_workspace_bytes", "zha_search", "zha_visited_words", "zha_attn_workspace_bytes",
            "zha_sparse_attn", "zha_forward_workspace_bytes", "zha_forward",
            "zha_dense_workspace_bytes", "zha_dense_topk_attn", "zha_bw_probe",
            "zha_status_string"]
@@ -84,7 +84,8 @@ def _load():
         "zha_build": (i32, [tp, vp, i64, vp]),
         "zha_append": (i32, [tp, vp, i64, vp]),
         "zha_search_workspace_bytes": (u64, [tp, sp, i32]),
-        "zha_search": (i32, [tp, vp, i32, sp, vp, vp, vp, vp, vp, u64, vp]),
+        "zha_search": (i32, [tp, vp, i32, sp, vp, vp, vp, vp, vp, vp, u64, vp]),
+        "zha_visited_words": (u64, [tp]),
         "zha_attn_workspace_bytes": (u64, [tp, sp, i32]),
         "zha_sparse_attn": (i32, [tp, vp, i32, vp, vp, sp, vp, vp, vp, vp, u64, vp]),
         "zha_forward_workspace_bytes": (u64, [tp, sp, i32]),
@@ -179,11 +180,16 @@ def zha_search_workspace_bytes(t: TreeHandle, sel: Select, q_per_head: int = 1) 
 
 
 def zha_search(t: TreeHandle, q, sel: Select, sel_blocks, sel_count, stats, status, ws,
-               q_per_head: int = 1, stream=None):
+               q_per_head: int = 1, stream=None, visited=None):
     wsb = ws.numel() * ws.element_size()
     _check(lib.zha_search(ctypes.byref(t), _ptr(q), q_per_head, ctypes.byref(sel), _ptr(sel_blocks),
-                          _ptr(sel_count), _ptr(stats), _ptr(status), _ptr(ws), wsb, _stream(stream)),
+                          _ptr(sel_count), _ptr(stats), _ptr(status), _ptr(visited), _ptr(ws), wsb,
+                          _stream(stream)),
            "zha_search")
+
+
+def zha_visited_words(t: TreeHandle) -> int:
+    return int(lib.zha_visited_words(ctypes.byref(t)))
 
 
 def zha_attn_workspace_bytes(t: TreeHandle, sel: Select, q_per_head: int = 1) -> int:
@@ -300,11 +306,17 @@ class Index:
                            device=self.device),
         )
 
-    def search(self, q, sel: Select, bufs=None, stream=None):
+    def search(self, q, sel: Select, bufs=None, stream=None, visited=None):
         bufs = bufs or self.search_buffers(sel)
         zha_search(self.handle, q, sel, bufs["sel_blocks"], bufs["sel_count"], bufs["stats"],
-                   bufs["status"], bufs["ws"], 1, stream)
+                   bufs["status"], bufs["ws"], 1, stream, visited)
         return bufs
+
+    def visited_bitmap(self):
+        """A zeroed bitmap for zha_search's `visited` output: [pairs][words]."""
+        g = self.geom
+        words = zha_visited_words(self.handle) // (g.batch * g.num_kv_heads)
+        return torch.zeros(g.batch * g.num_kv_heads, words, dtype=torch.int32, device=self.device)
 
     def attn_workspace(self, sel: Select):
         return torch.empty(max(zha_attn_workspace_bytes(self.handle, sel), 16), dtype=torch.uint8,
