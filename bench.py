@@ -157,7 +157,38 @@ def prepare(w, threads):
     return _PREPARED[w.wid]
 
 
-def run_gpu(Z, w, select, steps, warmup, threads):
+def run_dense(idx, w, Q, K, V, per_rot, steps, warmup):
+    """The same-GPU dense full-scan indexer on the same queries, with each
+    walk's key budget equal to the keys the tree walk read."""
+    import torch
+    budgets = [torch.tensor([s["keys_read"] for s in rows], dtype=torch.int32, device="cuda")
+               for rows in per_rot]
+    maxb = int(max(int(b.max()) for b in budgets))
+    ws = idx.dense_workspace(maxb)
+    out = torch.empty(w.batch, w.heads, w.d, dtype=K.dtype, device="cuda")
+    for r in range(warmup):
+        idx.dense_topk_attn(Q[r % ROTATIONS], K, V, budgets[r % ROTATIONS], maxb, out, ws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for i in range(steps):
+        idx.dense_topk_attn(Q[i % ROTATIONS], K, V, budgets[i % ROTATIONS], maxb, out, ws)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    e = 2 if w.dtype == "bf16" else 4
+    walks = w.batch * w.heads
+    k_bytes = w.batch * w.kv_heads * w.n * w.d * e
+    logit_bytes = walks * w.n * 4 * (1 + 4)      # written once, read by 3 histogram passes + 1 compaction
+    keys = float(np.mean([sum(s["keys_read"] for s in rows) for rows in per_rot]))
+    attn_bytes = 2 * w.d * e * keys + 2 * walks * w.d * e
+    return dict(ms_per_step=ms, qps=w.batch / (ms * 1e-3), k_pass_bytes=k_bytes,
+                logit_bytes=logit_bytes, attn_bytes=attn_bytes,
+                gbs=(k_bytes + logit_bytes + attn_bytes) / (ms * 1e-3) / 1e9,
+                max_budget=maxb)
+
+
+def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True):
     import torch
     from tree_structured_kv_amd import zha as Zm
     K, V, Q, R, idx, build_ms = prepare(w, threads)
@@ -217,7 +248,9 @@ def run_gpu(Z, w, select, steps, warmup, threads):
         v = np.array([s[k] for s in allw], dtype=np.float64)
         dist[k] = dict(mean=float(v.mean()), p50=float(np.percentile(v, 50)),
                        p90=float(np.percentile(v, 90)), max=float(v.max()))
+    dense = run_dense(idx, w, Q, K, V, per_rot, steps, warmup) if dense_baseline else None
     res = dict(
+        dense=dense,
         workload=w, select=select, wall_s=wall, steps=steps,
         ms_per_step=wall / steps * 1e3,
         qps=w.batch * steps / wall,
@@ -301,6 +334,8 @@ def summary(res, bw_ach):
         nodes_scored_per_step=by["scored"], nodes_scored_union_per_step=by["union_scored"],
         keys_per_step=by["keys"], keys_union_per_step=by["union_keys"],
         status=res["status"], per_walk=res["dist"],
+        dense=res["dense"],
+        speedup_vs_dense=(res["dense"]["ms_per_step"] / res["ms_per_step"]) if res["dense"] else None,
     )
 
 

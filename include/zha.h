@@ -253,19 +253,24 @@ zha_status zha_forward(zha_tree *t, int64_t n_new, const void *q, int32_t q_per_
 
 /* ---- measurement helpers (same-GPU baselines) ------------------------------ */
 
-/* Workspace bytes of zha_dense_topk_attn. */
-uint64_t zha_dense_workspace_bytes(const zha_tree *t, int32_t q_per_head);
+/* Workspace bytes of zha_dense_topk_attn for budgets up to max_budget. */
+uint64_t zha_dense_workspace_bytes(const zha_tree *t, int32_t max_budget);
 
-/* Dense full-scan indexer: exact logits s*<q, K_i> for every key i < n_tokens
- * (one pass over K per (sequence, KV head) serving all its query heads), the
- * budget[w] highest logits per walk (ties: lower index first), then attention
- * over exactly those keys into out.  budget: device int32 [walks], each in
- * [1, n_tokens].  This is the indexer that scores every key, written from
- * its plain definition; it is the baseline the tree search is measured
- * against ([ZHA lesson] "How does a tree of summaries search a context?"). */
+/* Dense full-scan indexer, the baseline the tree search is measured against:
+ * exact logits s*<q, K_i> for every key i < t->n_tokens (one pass over K per
+ * (sequence, KV head) serving all its query heads), the budget[w] highest
+ * logits of each walk (ties: lower index first), then attention over exactly
+ * those keys into out.  Decode only (one query per head); uses the tree
+ * handle for its shapes and n_tokens only.  This is the indexer that scores
+ * every key before choosing, written from its plain definition ([ZHA lesson]
+ * "How does a tree of summaries search a context?"; news page "Zyphra AI
+ * Introduces ZHA, a Path to True Subquadratic Attention").
+ *   budget      device int32 [walks], clamped to [1, min(n_tokens, max_budget)]
+ *   sel_tokens  device int32 [walks][max_budget] or NULL: the chosen token
+ *               ids of each walk in ascending order (first budget[w] entries) */
 zha_status zha_dense_topk_attn(const zha_tree *t, const void *q, const void *k_cache,
-                               const void *v_cache, const int32_t *budget, void *out,
-                               int32_t *sel_tokens, void *ws, uint64_t ws_bytes,
+                               const void *v_cache, const int32_t *budget, int32_t max_budget,
+                               void *out, int32_t *sel_tokens, void *ws, uint64_t ws_bytes,
                                void *stream);
 
 /* Streaming read of `bytes` from device buffer `buf` (sum into *sink, a

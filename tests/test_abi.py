@@ -158,6 +158,22 @@ def test_attn_forward_argument_errors(Z):
                              0x450000, None, 0x470000, 0x460000, fw - 1, None) == 5
 
 
+def test_dense_argument_errors(Z):
+    t = _handle(Z)
+    ws = Z.zha_dense_workspace_bytes(t, 128)
+    assert ws > Z.zha_dense_workspace_bytes(t, 1) > 0
+    assert Z.zha_dense_workspace_bytes(t, 0) == 0
+    base = [ctypes.byref(t), 0x400000, 0x410000, 0x420000, 0x430000, 128, 0x440000, None, 0x450000, ws, None]
+    a = list(base); a[4] = None
+    assert Z.lib.zha_dense_topk_attn(*a) == 1
+    a = list(base); a[5] = 0
+    assert Z.lib.zha_dense_topk_attn(*a) == 1
+    a = list(base); a[2] = 0x410004
+    assert Z.lib.zha_dense_topk_attn(*a) == 3
+    a = list(base); a[9] = ws - 1
+    assert Z.lib.zha_dense_topk_attn(*a) == 5
+
+
 def test_status_strings(Z):
     for code in range(8):
         assert Z.lib.zha_status_string(code)

@@ -261,3 +261,41 @@ def test_forward_equals_parts(Z):
     assert a.n_tokens == w.n
     assert torch.equal(out_f, out_p)
     assert torch.equal(stats, bufs["stats"])
+
+
+@pytest.mark.parametrize("name", ["demo", "clustered-small", "mixed-small"])
+def test_dense_topk_baseline(Z, name):
+    """The dense full-scan baseline: exact top-budget keys by logit (ties to
+    the lower index) and attention over them, against fp64 logits."""
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, name)
+    rng = np.random.default_rng(3)
+    walks = w.batch * w.heads
+    budget = rng.integers(1, min(w.n, 3000), size=walks).astype(np.int32)
+    budget[0] = w.n          # everything
+    budget[-1] = 1
+    maxb = int(budget.max())
+    bt = torch.from_numpy(budget).cuda()
+    sel_t = torch.full((walks, maxb), -1, dtype=torch.int32, device="cuda")
+    out = idx.dense_topk_attn(Qt, Kt, Vt, bt, maxb, sel_tokens=sel_t)
+    torch.cuda.synchronize()
+    sel_np = sel_t.cpu().numpy()
+    outs = out.float().cpu().numpy()
+    stable = 0
+    for b in range(w.batch):
+        for h in range(w.heads):
+            wi = b * w.heads + h
+            g = h // w.group
+            k = int(budget[wi])
+            got = sel_np[wi, :k].astype(np.int64)
+            assert np.all(np.diff(got) > 0)
+            lg = w.sharpness * (K[b, g].astype(np.float64) @ Q[b, h].astype(np.float64))
+            order = np.lexsort((np.arange(w.n), -lg))
+            want = np.sort(order[:k])
+            gap = np.inf if k >= w.n else lg[order[k - 1]] - lg[order[k]]
+            if gap > P.GAP:
+                stable += 1
+                assert np.array_equal(got, want), (b, h)
+            ref, _ = O.attend(got, Q[b, h].astype(np.float64), K[b, g].astype(np.float64),
+                              V[b, g].astype(np.float64), w.sharpness)
+            assert P.out_ok(outs[b, h], ref, w.dtype)[0], (b, h)
+    assert stable >= 0.5 * walks

@@ -35,10 +35,18 @@ __device__ __forceinline__ void merge_state(float &m, float &l, float *acc, floa
     m = mm;
 }
 
-__device__ __forceinline__ int64_t walk_keys(const AttnArgs &a, int w) {
+__device__ __forceinline__ int64_t walk_entries(const AttnArgs &a, int w) {
     int64_t nb = a.sel_count[w];
     if (nb > a.sel_cap) nb = a.sel_cap;
     if (nb < 0) nb = 0;
+    return nb;
+}
+
+// Keys of a walk: the c keys of every listed block plus the raw tail, or
+// the listed tokens.
+__device__ __forceinline__ int64_t walk_keys(const AttnArgs &a, int w) {
+    const int64_t nb = walk_entries(a, w);
+    if (a.tokens) return nb;
     return nb * a.chunk + (a.n_tokens - static_cast<int64_t>(a.chunk) * a.n1);
 }
 
@@ -100,10 +108,8 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
         const int64_t chunk = item - a.item_off[w];
         const int b = w / a.heads, h = w % a.heads, g = h / a.group;
         const int64_t pair = static_cast<int64_t>(b) * a.kv_heads + g;
-        int64_t nb = a.sel_count[w];
-        if (nb > a.sel_cap) nb = a.sel_cap;
-        if (nb < 0) nb = 0;
-        const int64_t body = nb * c;
+        const int64_t nb = walk_entries(a, w);
+        const int64_t body = a.tokens ? nb : nb * c;
         const int64_t total = walk_keys(a, w);
         const int64_t k0 = chunk * kChunkKeys;
         const int64_t k1 = (k0 + kChunkKeys < total) ? k0 + kChunkKeys : total;
@@ -115,7 +121,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
         }
         const KT *kb = static_cast<const KT *>(a.k) + pair * a.max_tokens * D;
         const KT *vb = static_cast<const KT *>(a.v) + pair * a.max_tokens * D;
-        const int32_t *selw = a.sel_blocks + static_cast<int64_t>(w) * a.sel_cap;
+        const int32_t *selw = (a.tokens ? a.tokens : a.sel_blocks) + static_cast<int64_t>(w) * a.sel_cap;
         const int64_t tail0 = static_cast<int64_t>(c) * a.n1;
 
         float m = -INFINITY, l = 0.f, acc[EPL];
@@ -131,7 +137,11 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
                 ok[u] = ki < k1;
                 int64_t tok = 0;
                 if (ok[u]) {
-                    if (ki < body) {
+                    if (a.tokens) {
+                        const int64_t tk = selw[ki];
+                        ok[u] = tk >= 0 && tk < a.n_tokens;   // ids outside the cache are skipped
+                        tok = ok[u] ? tk : 0;
+                    } else if (ki < body) {
                         const int64_t blk = selw[ki / c];
                         ok[u] = blk >= 0 && blk < a.n1;    // ids outside the live level are skipped
                         tok = ok[u] ? blk * c + (ki % c) : 0;

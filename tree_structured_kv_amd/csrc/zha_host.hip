@@ -106,28 +106,33 @@ SearchWs search_ws_layout(const zha_tree *t, const zha_select *sel, int64_t walk
     return l;
 }
 
-int64_t attn_max_items(const zha_tree *t, const zha_select *sel, int64_t walks) {
-    const int64_t keys = int64_t(sel->max_blocks_per_walk) * t->geom.chunk + t->geom.chunk - 1;
-    int64_t per = (keys + kChunkKeys - 1) / kChunkKeys;
+// Attention work items of a call: each walk's keys (at most keys_bound)
+// cut into chunks of kChunkKeys, at least one item per walk.
+int64_t attn_max_items(int64_t keys_bound, int64_t walks) {
+    int64_t per = (keys_bound + kChunkKeys - 1) / kChunkKeys;
     if (per < 1) per = 1;
     return walks * per;
+}
+
+int64_t tree_keys_bound(const zha_tree *t, const zha_select *sel) {
+    return int64_t(sel->max_blocks_per_walk) * t->geom.chunk + t->geom.chunk - 1;
 }
 
 struct AttnWs {
     uint64_t part, item_off, item_walk, total;
 };
-AttnWs attn_ws_layout(const zha_tree *t, const zha_select *sel, int64_t walks) {
-    const uint64_t items = static_cast<uint64_t>(attn_max_items(t, sel, walks));
+AttnWs attn_ws_layout(int head_dim, int64_t keys_bound, int64_t walks) {
+    const uint64_t items = static_cast<uint64_t>(attn_max_items(keys_bound, walks));
     AttnWs l;
     l.part = 0;
-    l.item_off = align_up(items * (t->geom.head_dim + 2) * sizeof(float));
+    l.item_off = align_up(items * (head_dim + 2) * sizeof(float));
     l.item_walk = l.item_off + align_up(uint64_t(walks + 1) * sizeof(int32_t));
     l.total = l.item_walk + align_up(items * sizeof(int32_t));
     return l;
 }
 
 uint64_t attn_ws_bytes(const zha_tree *t, const zha_select *sel, int64_t walks) {
-    return attn_ws_layout(t, sel, walks).total;
+    return attn_ws_layout(t->geom.head_dim, tree_keys_bound(t, sel), walks).total;
 }
 
 struct ForwardWs {
@@ -250,9 +255,10 @@ zha_status do_search(const zha_tree *t, const void *q, const zha_select *sel, in
     return hip_status(launch_search(a, g.head_dim, g.num_refs, g.dtype, engine, static_cast<int>(n0), st));
 }
 
+// Attention over block lists (tokens == nullptr) or token lists.
 zha_status do_attn(const zha_tree *t, const void *q, const void *k_cache, const void *v_cache,
-                   const zha_select *sel, const int32_t *sel_blocks, const int32_t *sel_count,
-                   void *out, void *ws, hipStream_t st) {
+                   const int32_t *sel_blocks, const int32_t *tokens, const int32_t *sel_count,
+                   int32_t list_cap, int64_t keys_bound, void *out, void *ws, hipStream_t st) {
     const zha_geometry &g = t->geom;
     const int64_t walks = walks_of(&g, 1);
     AttnArgs a;
@@ -262,8 +268,9 @@ zha_status do_attn(const zha_tree *t, const void *q, const void *k_cache, const 
     a.v = v_cache;
     a.out = out;
     a.sel_blocks = sel_blocks;
+    a.tokens = tokens;
     a.sel_count = sel_count;
-    AttnWs lay = attn_ws_layout(t, sel, walks);
+    AttnWs lay = attn_ws_layout(g.head_dim, keys_bound, walks);
     char *wb = static_cast<char *>(ws);
     a.part = reinterpret_cast<float *>(wb + lay.part);
     a.item_off = reinterpret_cast<int32_t *>(wb + lay.item_off);
@@ -276,11 +283,26 @@ zha_status do_attn(const zha_tree *t, const void *q, const void *k_cache, const 
     a.group = g.group_size;
     a.kv_heads = g.num_kv_heads;
     a.chunk = g.chunk;
-    a.sel_cap = sel->max_blocks_per_walk;
-    const int64_t items = attn_max_items(t, sel, walks);
+    a.sel_cap = list_cap;
+    const int64_t items = attn_max_items(keys_bound, walks);
     a.grid = static_cast<int32_t>(items < 2048 ? items : 2048);
     a.sharpness = g.sharpness;
     return hip_status(launch_attn(a, g.head_dim, g.dtype, st));
+}
+
+struct DenseWs {
+    uint64_t logits, sel, sel_n, attn, total;
+};
+DenseWs dense_ws_layout(const zha_tree *t, int32_t max_budget) {
+    const zha_geometry &g = t->geom;
+    const uint64_t walks = static_cast<uint64_t>(walks_of(&g, 1));
+    DenseWs l;
+    l.logits = 0;
+    l.sel = align_up(walks * uint64_t(g.max_tokens) * sizeof(float));
+    l.sel_n = l.sel + align_up(walks * uint64_t(max_budget) * sizeof(int32_t));
+    l.attn = l.sel_n + align_up(walks * sizeof(int32_t));
+    l.total = l.attn + attn_ws_layout(g.head_dim, max_budget, walks).total;
+    return l;
 }
 
 }  // namespace
@@ -396,8 +418,8 @@ zha_status zha_sparse_attn(const zha_tree *t, const void *q, int32_t q_per_head,
         !aligned16(ws) || !aligned_n(sel_blocks, 4) || !aligned_n(sel_count, 4))
         return ZHA_ERR_ALIGN;
     if (ws_bytes < zha_attn_workspace_bytes(t, sel, q_per_head)) return ZHA_ERR_WORKSPACE;
-    return do_attn(t, q, k_cache, v_cache, sel, sel_blocks, sel_count, out, ws,
-                   static_cast<hipStream_t>(stream));
+    return do_attn(t, q, k_cache, v_cache, sel_blocks, nullptr, sel_count, sel->max_blocks_per_walk,
+                   tree_keys_bound(t, sel), out, ws, static_cast<hipStream_t>(stream));
 }
 
 uint64_t zha_forward_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head) {
@@ -433,21 +455,52 @@ zha_status zha_forward(zha_tree *t, int64_t n_new, const void *q, int32_t q_per_
     int32_t *sc = reinterpret_cast<int32_t *>(w + lay.sel_count);
     s = do_search(t, q, sel, sb, sc, stats, status, nullptr, w + lay.search, st);
     if (s != ZHA_OK) return s;
-    return do_attn(t, q, k_cache, v_cache, sel, sb, sc, out, w + lay.attn, st);
+    return do_attn(t, q, k_cache, v_cache, sb, nullptr, sc, sel->max_blocks_per_walk,
+                   tree_keys_bound(t, sel), out, w + lay.attn, st);
 }
 
-uint64_t zha_dense_workspace_bytes(const zha_tree *t, int32_t q_per_head) {
-    (void)t;
-    (void)q_per_head;
-    return 0;
+uint64_t zha_dense_workspace_bytes(const zha_tree *t, int32_t max_budget) {
+    if (check_tree(t) != ZHA_OK || max_budget < 1) return 0;
+    return dense_ws_layout(t, max_budget).total;
 }
 
 zha_status zha_dense_topk_attn(const zha_tree *t, const void *q, const void *k_cache,
-                               const void *v_cache, const int32_t *budget, void *out,
-                               int32_t *sel_tokens, void *ws, uint64_t ws_bytes, void *stream) {
-    (void)t; (void)q; (void)k_cache; (void)v_cache; (void)budget; (void)out;
-    (void)sel_tokens; (void)ws; (void)ws_bytes; (void)stream;
-    return ZHA_ERR_UNSUPPORTED;
+                               const void *v_cache, const int32_t *budget, int32_t max_budget,
+                               void *out, int32_t *sel_tokens, void *ws, uint64_t ws_bytes,
+                               void *stream) {
+    zha_status s = check_tree(t);
+    if (s != ZHA_OK) return s;
+    if (max_budget < 1) return ZHA_ERR_ARG;
+    if (!q || !k_cache || !v_cache || !budget || !out || !ws) return ZHA_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        !aligned16(ws) || !aligned_n(budget, 4) || (sel_tokens && !aligned_n(sel_tokens, 4)))
+        return ZHA_ERR_ALIGN;
+    if (ws_bytes < zha_dense_workspace_bytes(t, max_budget)) return ZHA_ERR_WORKSPACE;
+    const zha_geometry &g = t->geom;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    DenseWs lay = dense_ws_layout(t, max_budget);
+    char *wb = static_cast<char *>(ws);
+    DenseArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k_cache;
+    a.budget = budget;
+    a.logits = reinterpret_cast<float *>(wb + lay.logits);
+    a.sel = sel_tokens ? sel_tokens : reinterpret_cast<int32_t *>(wb + lay.sel);
+    a.sel_n = reinterpret_cast<int32_t *>(wb + lay.sel_n);
+    a.max_tokens = g.max_tokens;
+    a.n_tokens = t->n_tokens;
+    a.row_pad = g.max_tokens;
+    a.walks = static_cast<int32_t>(walks_of(&g, 1));
+    a.heads = g.num_kv_heads * g.group_size;
+    a.group = g.group_size;
+    a.kv_heads = g.num_kv_heads;
+    a.max_budget = max_budget;
+    a.sharpness = g.sharpness;
+    s = hip_status(launch_dense(a, g.head_dim, g.dtype, st));
+    if (s != ZHA_OK) return s;
+    return do_attn(t, q, k_cache, v_cache, nullptr, a.sel, a.sel_n, max_budget, max_budget, out,
+                   wb + lay.attn, st);
 }
 
 zha_status zha_bw_probe(const void *buf, uint64_t bytes, float *sink, void *stream) {

@@ -88,8 +88,9 @@ struct AttnArgs {
     const void *k;                 // cache
     const void *v;                 // cache
     void *out;                     // [walks][D]
-    const int32_t *sel_blocks;     // [walks][sel_cap]
-    const int32_t *sel_count;      // [walks]
+    const int32_t *sel_blocks;     // [walks][sel_cap] level-1 blocks, or
+    const int32_t *tokens;         // [walks][sel_cap] token ids (then no blocks, no tail)
+    const int32_t *sel_count;      // [walks] entries of sel_blocks / tokens
     float *part;                   // ws [max_items][D + 2]
     int32_t *item_off;             // ws [walks + 1]: first item of each walk
     int32_t *item_walk;            // ws [max_items]: walk of each item
@@ -108,22 +109,19 @@ struct AttnArgs {
 
 struct DenseArgs {
     const void *q;                 // [walks][D]
-    const void *k;
-    const void *v;
-    void *out;
+    const void *k;                 // cache
     const int32_t *budget;         // [walks]
-    float *logits;                 // ws [walks][n_tokens_pad]
-    int32_t *sel;                  // ws [walks][n_tokens_pad]  (selected token ids)
-    int32_t *sel_n;                // ws [walks]
-    float *part;                   // ws [walks][splits][D + 2]
+    float *logits;                 // ws [walks][row_pad]
+    int32_t *sel;                  // [walks][max_budget] selected token ids, ascending
+    int32_t *sel_n;                // [walks]
     int64_t max_tokens;
     int64_t n_tokens;
-    int64_t row_pad;               // logits/sel row stride
+    int64_t row_pad;               // logits row stride
     int32_t walks;
     int32_t heads;
     int32_t group;
     int32_t kv_heads;
-    int32_t splits;
+    int32_t max_budget;
     float sharpness;
 };
 

@@ -91,7 +91,7 @@ def _load():
         "zha_forward_workspace_bytes": (u64, [tp, sp, i32]),
         "zha_forward": (i32, [tp, i64, vp, i32, vp, vp, sp, vp, vp, vp, vp, u64, vp]),
         "zha_dense_workspace_bytes": (u64, [tp, i32]),
-        "zha_dense_topk_attn": (i32, [tp, vp, vp, vp, vp, vp, vp, vp, u64, vp]),
+        "zha_dense_topk_attn": (i32, [tp, vp, vp, vp, vp, i32, vp, vp, vp, u64, vp]),
         "zha_bw_probe": (i32, [vp, u64, vp, vp]),
         "zha_status_string": (ctypes.c_char_p, [i32]),
     }
@@ -218,16 +218,16 @@ def zha_forward(t: TreeHandle, n_new: int, q, k_cache, v_cache, sel: Select, out
            "zha_forward")
 
 
-def zha_dense_workspace_bytes(t: TreeHandle, q_per_head: int = 1) -> int:
-    return int(lib.zha_dense_workspace_bytes(ctypes.byref(t), q_per_head))
+def zha_dense_workspace_bytes(t: TreeHandle, max_budget: int) -> int:
+    return int(lib.zha_dense_workspace_bytes(ctypes.byref(t), int(max_budget)))
 
 
-def zha_dense_topk_attn(t: TreeHandle, q, k_cache, v_cache, budget, out, ws, sel_tokens=None,
-                        stream=None):
+def zha_dense_topk_attn(t: TreeHandle, q, k_cache, v_cache, budget, max_budget: int, out, ws,
+                        sel_tokens=None, stream=None):
     wsb = ws.numel() * ws.element_size()
     _check(lib.zha_dense_topk_attn(ctypes.byref(t), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                   _ptr(budget), _ptr(out), _ptr(sel_tokens), _ptr(ws), wsb,
-                                   _stream(stream)),
+                                   _ptr(budget), int(max_budget), _ptr(out), _ptr(sel_tokens),
+                                   _ptr(ws), wsb, _stream(stream)),
            "zha_dense_topk_attn")
 
 
@@ -329,6 +329,20 @@ class Index:
         if ws is None:
             ws = self.attn_workspace(sel)
         zha_sparse_attn(self.handle, q, k_cache, v_cache, sel, sel_blocks, sel_count, out, ws, 1, stream)
+        return out
+
+    def dense_workspace(self, max_budget: int):
+        return torch.empty(max(zha_dense_workspace_bytes(self.handle, max_budget), 16), dtype=torch.uint8,
+                           device=self.device)
+
+    def dense_topk_attn(self, q, k_cache, v_cache, budget, max_budget, out=None, ws=None,
+                        sel_tokens=None, stream=None):
+        if out is None:
+            out = torch.empty_like(q)
+        if ws is None:
+            ws = self.dense_workspace(max_budget)
+        zha_dense_topk_attn(self.handle, q, k_cache, v_cache, budget, max_budget, out, ws,
+                            sel_tokens, stream)
         return out
 
     def forward_workspace(self, sel: Select):
