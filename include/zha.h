@@ -190,14 +190,18 @@ zha_status zha_append(zha_tree *t, const void *k_cache, int64_t n_new, void *str
 /* Workspace bytes of zha_search for q_per_head queries per head. */
 uint64_t zha_search_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head);
 
-/* One walk per (sequence, query head, query).  q_per_head = 1 is decode: the
- * query sees the tree's tokens [0, n_tokens).  Candidates start as the roots:
- * every top-level node plus every node whose parent chunk has not filled;
- * per step they are scored (max over r of s*<key_r, q> + bias_r), normalised
- * with a softmax over the whole step and cut by `sel`; opened level-1 nodes
- * select their `chunk` keys, other opened nodes give their children as the
- * next candidates ([ZHA lesson] "Run a small tree yourself").  Raw keys past
- * the last whole chunk are always selected (not listed).
+/* One walk per (sequence, query head, query).  Candidates start as the
+ * roots: every top-level node plus every node whose parent chunk has not
+ * filled; per step they are scored (max over r of s*<key_r, q> + bias_r),
+ * normalised with a softmax over the whole step and cut by `sel`; opened
+ * level-1 nodes select their `chunk` keys, other opened nodes give their
+ * children as the next candidates ([ZHA lesson] "Run a small tree
+ * yourself", "Common misunderstandings": each head walks on its own).  Raw
+ * keys past the last whole chunk are always selected (not listed).
+ *   q_per_head  1: decode, one query per head seeing the tree's tokens
+ *               [0, n_tokens).  > 1: a prefill block whose queries sit at
+ *               positions n_tokens .. n_tokens + q_per_head - 1; every query
+ *               walks the tree as it stands (the tokens before the block).
  *   sel_blocks  device int32 [walks][max_blocks_per_walk]: level-1 block ids
  *               j (keys j*chunk .. j*chunk+chunk-1), in the order found
  *               (steps in order, each step in span order)
@@ -206,8 +210,7 @@ uint64_t zha_search_workspace_bytes(const zha_tree *t, const zha_select *sel, in
  *   status      device uint32, OR-ed with ZHA_FLAG_* (not cleared)
  *   visited     device uint32 [batch*kv_heads][zha_visited_words/pairs], may be
  *               NULL (see zha_visited_words)
- * walks = batch * kv_heads * group_size * q_per_head, in Q's order.
- * q_per_head > 1 (prefill blocks) returns ZHA_ERR_UNSUPPORTED. */
+ * walks = batch * kv_heads * group_size * q_per_head, in Q's order. */
 zha_status zha_search(const zha_tree *t, const void *q, int32_t q_per_head,
                       const zha_select *sel, int32_t *sel_blocks, int32_t *sel_count,
                       zha_walk_stats *stats, uint32_t *status, uint32_t *visited,
@@ -230,9 +233,12 @@ uint64_t zha_attn_workspace_bytes(const zha_tree *t, const zha_select *sel, int3
 /* out = softmax over the selected keys of s*<q, K_i>, applied to V_i, for
  * every walk: exactly the original keys of the listed level-1 blocks plus
  * the raw tail [chunk*floor(n_tokens/chunk), n_tokens) ([ZHA lesson] "How is
- * the tree built?", "Common misunderstandings").  fp32 accumulation; a bf16
- * output is rounded to nearest-even once.  Block ids must be in
- * [0, floor(n_tokens/chunk)); entries past sel_count are ignored. */
+ * the tree built?", "Common misunderstandings").  For a prefill block
+ * (q_per_head > 1) query t also attends the block's own keys n_tokens ..
+ * n_tokens + t (causal; rows the caller has written, n_tokens + q_per_head <=
+ * max_tokens or ZHA_ERR_CAPACITY).  fp32 accumulation; a bf16 output is
+ * rounded to nearest-even once.  Block ids outside [0, floor(n_tokens/chunk))
+ * are skipped; entries past sel_count are ignored. */
 zha_status zha_sparse_attn(const zha_tree *t, const void *q, int32_t q_per_head,
                            const void *k_cache, const void *v_cache,
                            const zha_select *sel, const int32_t *sel_blocks,
@@ -244,8 +250,12 @@ zha_status zha_sparse_attn(const zha_tree *t, const void *q, int32_t q_per_head,
 /* Workspace bytes of zha_forward (search + attention + selection lists). */
 uint64_t zha_forward_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head);
 
-/* zha_append(n_new) (skipped if 0), then zha_search, then zha_sparse_attn,
- * with the selection lists kept in the workspace. */
+/* One step of a layer with the selection lists kept in the workspace.
+ * Decode (q_per_head = 1): zha_append(n_new) first (the new token's key is
+ * then visible to its own query), then zha_search and zha_sparse_attn.
+ * Prefill block (q_per_head > 1): zha_search and zha_sparse_attn for the
+ * block at positions [n_tokens, n_tokens + q_per_head), then
+ * zha_append(n_new) (normally n_new = q_per_head). */
 zha_status zha_forward(zha_tree *t, int64_t n_new, const void *q, int32_t q_per_head,
                        const void *k_cache, const void *v_cache, const zha_select *sel,
                        void *out, zha_walk_stats *stats, uint32_t *status,

@@ -114,7 +114,7 @@ def test_search_argument_errors(Z):
     assert Z.lib.zha_search(*args(visited=0x900002)) == 3
     assert Z.lib.zha_search(*args(wsb=ws - 1)) == 5
     assert Z.lib.zha_search(*args(qph=0)) == 1
-    assert Z.lib.zha_search(*args(qph=4)) == 6
+    assert Z.lib.zha_search(*args(qph=1 << 22)) == 6   # too many walks
     bad = Z.make_select("topk", k=(0,), max_blocks=64)
     assert Z.lib.zha_search(*args(sel=bad)) == 1
     bad = Z.make_select("topp", 0.9, max_blocks=0)
@@ -151,6 +151,8 @@ def test_attn_forward_argument_errors(Z):
     assert Z.lib.zha_sparse_attn(*a) == 3
     a = list(base); a[10] = ws - 1
     assert Z.lib.zha_sparse_attn(*a) == 5
+    a = list(base); a[2] = 4097    # a prefill block past the cache capacity
+    assert Z.lib.zha_sparse_attn(*a) == 4
     fw = Z.zha_forward_workspace_bytes(t, sel)
     assert Z.lib.zha_forward(ctypes.byref(t), 5000, 0x400000, 1, 0x410000, 0x420000, ctypes.byref(sel),
                              0x450000, None, 0x470000, 0x460000, fw, None) == 4

@@ -299,3 +299,104 @@ def test_dense_topk_baseline(Z, name):
                               V[b, g].astype(np.float64), w.sharpness)
             assert P.out_ok(outs[b, h], ref, w.dtype)[0], (b, h)
     assert stable >= 0.5 * walks
+
+
+# ---- prefill blocks ------------------------------------------------------------
+
+_pcache = {}
+
+
+def _prefill_setup(Z):
+    """A streamed cache (chunk 16, R 8, 3 levels) with a ragged prefix of
+    T0 = 2*4096 + 300 tokens already in the tree and a block of T = 128
+    queries per head at positions T0 .. T0+127 whose K/V rows are written."""
+    if "p" in _pcache:
+        return _pcache["p"]
+    T0, T = 2 * 4096 + 300, 128
+    w = replace(S.WORKLOADS[3].scaled(n=T0 + T, batch=1), kv_heads=2)
+    K, V, _, R = P.make_inputs(w)
+    Q = np.zeros((w.batch, w.heads, T, w.d), np.float32)
+    for g in range(w.kv_heads):
+        q = S.pair_queries(w, 0, g, count=w.group * T, block=T0 // w.block)
+        Q[0, g * w.group:(g + 1) * w.group] = q.reshape(w.group, T, w.d)
+    dev = torch.device("cuda")
+    Kt = torch.from_numpy(K).to(dev).to(torch.bfloat16).contiguous()
+    Vt = torch.from_numpy(V).to(dev).to(torch.bfloat16).contiguous()
+    Qt = torch.from_numpy(Q).to(dev).to(torch.bfloat16).contiguous()
+    geom = Z.make_geometry(w.batch, w.kv_heads, w.group, w.d, w.chunk, w.refs, w.levels, w.dtype,
+                           w.n, w.sharpness)
+    idx = Z.Index(geom, torch.from_numpy(R))
+    idx.build(Kt, T0)
+    trees = {(0, g): P.oracle_tree(w, K, R, 0, g, T0) for g in range(w.kv_heads)}
+    _pcache["p"] = (w, T0, T, K, V, Q, R, Kt, Vt, Qt, idx, trees)
+    return _pcache["p"]
+
+
+@pytest.mark.parametrize("engine", ["persistent", "level-sync"])
+@pytest.mark.parametrize("sname", ["topp90", "topk4", "open-all"])
+def test_prefill_block(Z, sname, engine):
+    """Prefill: every query of the block walks the tree of the tokens before
+    the block, then attends its selection plus the block's keys up to itself."""
+    w, T0, T, K, V, Q, R, Kt, Vt, Qt, idx, trees = _prefill_setup(Z)
+    select = dict(mode="topp", p=1.0) if sname == "open-all" else SELECTS[sname]
+    sel = P.select_struct(Z, select, T0 // w.chunk, engine=engine)
+    bufs = idx.search(Qt, sel, qph=T)
+    out = idx.sparse_attn(Qt, Kt, Vt, sel, bufs["sel_blocks"], bufs["sel_count"], qph=T)
+    torch.cuda.synchronize()
+    from tree_structured_kv_amd.zha import stats_to_dicts
+    blocks = bufs["sel_blocks"].cpu().numpy()
+    count = bufs["sel_count"].cpu().numpy()
+    stats = stats_to_dicts(bufs["stats"].cpu())
+    outs = out.float().cpu().numpy()
+    assert int(bufs["status"].cpu()[0]) == 0
+    stable = walks = 0
+    rng = np.random.default_rng(0)
+    for h in range(w.heads):
+        g = h // w.group
+        for t in rng.choice(T, size=16, replace=False):
+            wi = h * T + t
+            q = Q[0, h, t]
+            sel_o, st_o = P.oracle_walk(trees[(0, g)], q, select)
+            toks = P.gpu_tokens(blocks[wi], count[wi], w.chunk, T0)
+            walks += 1
+            if st_o["gap"] > P.GAP:
+                stable += 1
+                assert np.array_equal(toks, sel_o), (h, t)
+                assert stats[wi]["scored"] == st_o["scored"], (h, t)
+                assert stats[wi]["comparisons"] == st_o["comparisons"]
+            keys = np.concatenate([toks, np.arange(T0, T0 + t + 1)])
+            ref, _ = O.attend(keys, q.astype(np.float64), K[0, g].astype(np.float64),
+                              V[0, g].astype(np.float64), w.sharpness)
+            ok, e = P.out_ok(outs[0, h, t], ref, w.dtype)
+            assert ok, (h, t, e)
+            if sname == "open-all":   # dense causal attention
+                dense, _ = O.attend(np.arange(T0 + t + 1), q.astype(np.float64),
+                                    K[0, g].astype(np.float64), V[0, g].astype(np.float64), w.sharpness)
+                assert P.out_ok(outs[0, h, t], dense, w.dtype)[0]
+    assert stable >= 0.3 * walks
+
+
+def test_prefill_forward_appends_after_search(Z):
+    """zha_forward on a prefill block: search + attention on the tree before
+    the block, then the block is appended (the tree equals a full build)."""
+    w, T0, T, K, V, Q, R, Kt, Vt, Qt, idx, trees = _prefill_setup(Z)
+    select = SELECTS["topp90"]
+    sel = P.select_struct(Z, select, T0 // w.chunk)
+    a = Z.Index(idx.geom, torch.from_numpy(R))
+    a.build(Kt, T0)
+    out_f = torch.empty_like(Qt)
+    stats = torch.zeros(a.walks * T, Z.STATS_WORDS, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    a.forward(T, Qt, Kt, Vt, sel, out_f, stats, status, a.forward_workspace(sel, T), qph=T)
+    bufs = idx.search(Qt, sel, qph=T)
+    out_p = idx.sparse_attn(Qt, Kt, Vt, sel, bufs["sel_blocks"], bufs["sel_count"], qph=T)
+    full = Z.Index(idx.geom, torch.from_numpy(R))
+    full.build(Kt, T0 + T)
+    torch.cuda.synchronize()
+    assert a.n_tokens == T0 + T
+    assert torch.equal(out_f, out_p)
+    assert torch.equal(stats, bufs["stats"])
+    for l in range(1, w.levels + 1):
+        live = (T0 + T) // w.chunk ** l
+        assert torch.equal(a.level(l)[0][:, :, :live], full.level(l)[0][:, :, :live])
+        assert torch.equal(a.level(l)[1][:, :, :live], full.level(l)[1][:, :, :live])

@@ -42,12 +42,14 @@ __device__ __forceinline__ int64_t walk_entries(const AttnArgs &a, int w) {
     return nb;
 }
 
-// Keys of a walk: the c keys of every listed block plus the raw tail, or
-// the listed tokens.
+// Keys of a walk: the c keys of every listed block plus the raw tail (or
+// the listed tokens), then, for query t of a prefill block, the block's own
+// keys n_tokens .. n_tokens + t.
 __device__ __forceinline__ int64_t walk_keys(const AttnArgs &a, int w) {
     const int64_t nb = walk_entries(a, w);
-    if (a.tokens) return nb;
-    return nb * a.chunk + (a.n_tokens - static_cast<int64_t>(a.chunk) * a.n1);
+    const int64_t causal = (a.qph > 1) ? (w % a.qph) + 1 : 0;
+    if (a.tokens) return nb + causal;
+    return nb * a.chunk + (a.n_tokens - static_cast<int64_t>(a.chunk) * a.n1) + causal;
 }
 
 }  // namespace
@@ -106,10 +108,10 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
     for (int32_t item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int w = a.item_walk[item];
         const int64_t chunk = item - a.item_off[w];
-        const int b = w / a.heads, h = w % a.heads, g = h / a.group;
-        const int64_t pair = static_cast<int64_t>(b) * a.kv_heads + g;
+        const int64_t pair = walk_pair(w, a.qph, a.heads, a.group, a.kv_heads);
         const int64_t nb = walk_entries(a, w);
         const int64_t body = a.tokens ? nb : nb * c;
+        const int64_t tree_keys = a.tokens ? nb : body + (a.n_tokens - static_cast<int64_t>(c) * a.n1);
         const int64_t total = walk_keys(a, w);
         const int64_t k0 = chunk * kChunkKeys;
         const int64_t k1 = (k0 + kChunkKeys < total) ? k0 + kChunkKeys : total;
@@ -137,7 +139,9 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
                 ok[u] = ki < k1;
                 int64_t tok = 0;
                 if (ok[u]) {
-                    if (a.tokens) {
+                    if (ki >= tree_keys) {
+                        tok = a.n_tokens + (ki - tree_keys);   // the block's own keys (causal)
+                    } else if (a.tokens) {
                         const int64_t tk = selw[ki];
                         ok[u] = tk >= 0 && tk < a.n_tokens;   // ids outside the cache are skipped
                         tok = ok[u] ? tk : 0;

@@ -93,6 +93,15 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The (sequence, KV head) pair a walk reads: walks are laid out as
+// [batch][query head][query], and query head h uses KV head h / group.
+__device__ __forceinline__ int64_t walk_pair(int64_t w, int qph, int heads, int group, int kv_heads) {
+    const int64_t hq = w / qph;
+    const int64_t b = hq / heads;
+    const int h = static_cast<int>(hq % heads);
+    return b * kv_heads + h / group;
+}
+
 // XCD-aware workgroup order: the hardware hands consecutive workgroup ids to
 // the 8 XCDs in turn; remap so each XCD gets one contiguous range of logical
 // ids (neighbouring walks share tree nodes in that XCD's L2).

@@ -114,8 +114,8 @@ int64_t attn_max_items(int64_t keys_bound, int64_t walks) {
     return walks * per;
 }
 
-int64_t tree_keys_bound(const zha_tree *t, const zha_select *sel) {
-    return int64_t(sel->max_blocks_per_walk) * t->geom.chunk + t->geom.chunk - 1;
+int64_t tree_keys_bound(const zha_tree *t, const zha_select *sel, int32_t qph) {
+    return int64_t(sel->max_blocks_per_walk) * t->geom.chunk + t->geom.chunk - 1 + (qph > 1 ? qph : 0);
 }
 
 struct AttnWs {
@@ -131,20 +131,21 @@ AttnWs attn_ws_layout(int head_dim, int64_t keys_bound, int64_t walks) {
     return l;
 }
 
-uint64_t attn_ws_bytes(const zha_tree *t, const zha_select *sel, int64_t walks) {
-    return attn_ws_layout(t->geom.head_dim, tree_keys_bound(t, sel), walks).total;
+uint64_t attn_ws_bytes(const zha_tree *t, const zha_select *sel, int32_t qph) {
+    return attn_ws_layout(t->geom.head_dim, tree_keys_bound(t, sel, qph), walks_of(&t->geom, qph)).total;
 }
 
 struct ForwardWs {
     uint64_t sel_blocks, sel_count, search, attn, total;
 };
-ForwardWs forward_ws_layout(const zha_tree *t, const zha_select *sel, int64_t walks) {
+ForwardWs forward_ws_layout(const zha_tree *t, const zha_select *sel, int32_t qph) {
+    const int64_t walks = walks_of(&t->geom, qph);
     ForwardWs l;
     l.sel_blocks = 0;
     l.sel_count = align_up(uint64_t(walks) * sel->max_blocks_per_walk * sizeof(int32_t));
     l.search = l.sel_count + align_up(uint64_t(walks) * sizeof(int32_t));
     l.attn = l.search + search_ws_layout(t, sel, walks).total;
-    l.total = l.attn + attn_ws_bytes(t, sel, walks);
+    l.total = l.attn + attn_ws_bytes(t, sel, qph);
     return l;
 }
 
@@ -189,11 +190,11 @@ int64_t visited_words_per_pair(const zha_tree *t) {
     return (bits + 31) / 32;
 }
 
-zha_status do_search(const zha_tree *t, const void *q, const zha_select *sel, int32_t *sel_blocks,
-                     int32_t *sel_count, zha_walk_stats *stats, uint32_t *status, uint32_t *visited,
-                     void *ws, hipStream_t st) {
+zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_select *sel,
+                     int32_t *sel_blocks, int32_t *sel_count, zha_walk_stats *stats, uint32_t *status,
+                     uint32_t *visited, void *ws, hipStream_t st) {
     const zha_geometry &g = t->geom;
-    const int64_t walks = walks_of(&g, 1);
+    const int64_t walks = walks_of(&g, qph);
     SearchWs lay = search_ws_layout(t, sel, walks);
     const char *mem = static_cast<const char *>(t->tree_mem);
     SearchArgs a;
@@ -228,6 +229,7 @@ zha_status do_search(const zha_tree *t, const void *q, const zha_select *sel, in
     a.score_grid = 1024;
     a.n_tokens = t->n_tokens;
     a.walks = static_cast<int32_t>(walks);
+    a.qph = qph;
     a.heads = g.num_kv_heads * g.group_size;
     a.group = g.group_size;
     a.kv_heads = g.num_kv_heads;
@@ -256,11 +258,12 @@ zha_status do_search(const zha_tree *t, const void *q, const zha_select *sel, in
 }
 
 // Attention over block lists (tokens == nullptr) or token lists.
-zha_status do_attn(const zha_tree *t, const void *q, const void *k_cache, const void *v_cache,
-                   const int32_t *sel_blocks, const int32_t *tokens, const int32_t *sel_count,
-                   int32_t list_cap, int64_t keys_bound, void *out, void *ws, hipStream_t st) {
+zha_status do_attn(const zha_tree *t, const void *q, int32_t qph, const void *k_cache,
+                   const void *v_cache, const int32_t *sel_blocks, const int32_t *tokens,
+                   const int32_t *sel_count, int32_t list_cap, int64_t keys_bound, void *out, void *ws,
+                   hipStream_t st) {
     const zha_geometry &g = t->geom;
-    const int64_t walks = walks_of(&g, 1);
+    const int64_t walks = walks_of(&g, qph);
     AttnArgs a;
     memset(&a, 0, sizeof(a));
     a.q = q;
@@ -279,6 +282,7 @@ zha_status do_attn(const zha_tree *t, const void *q, const void *k_cache, const 
     a.n_tokens = t->n_tokens;
     a.n1 = level_count(t->n_tokens, g.chunk, 1);
     a.walks = static_cast<int32_t>(walks);
+    a.qph = qph;
     a.heads = g.num_kv_heads * g.group_size;
     a.group = g.group_size;
     a.kv_heads = g.num_kv_heads;
@@ -389,19 +393,19 @@ zha_status zha_search(const zha_tree *t, const void *q, int32_t q_per_head, cons
     if (s != ZHA_OK) return s;
     if ((s = check_select(sel)) != ZHA_OK) return s;
     if (q_per_head < 1) return ZHA_ERR_ARG;
-    if (q_per_head != 1) return ZHA_ERR_UNSUPPORTED;
+    if (walks_of(&t->geom, q_per_head) > (int64_t(1) << 24)) return ZHA_ERR_UNSUPPORTED;
     if (!q || !sel_blocks || !sel_count || !status || !ws) return ZHA_ERR_ARG;
     if (!aligned16(q) || !aligned16(ws) || !aligned_n(sel_blocks, 4) || !aligned_n(sel_count, 4) ||
         !aligned_n(status, 4) || (stats && !aligned_n(stats, 8)) || (visited && !aligned_n(visited, 4)))
         return ZHA_ERR_ALIGN;
     if (ws_bytes < zha_search_workspace_bytes(t, sel, q_per_head)) return ZHA_ERR_WORKSPACE;
-    return do_search(t, q, sel, sel_blocks, sel_count, stats, status, visited, ws,
+    return do_search(t, q, q_per_head, sel, sel_blocks, sel_count, stats, status, visited, ws,
                      static_cast<hipStream_t>(stream));
 }
 
 uint64_t zha_attn_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head) {
     if (check_tree(t) != ZHA_OK || check_select(sel) != ZHA_OK || q_per_head < 1) return 0;
-    return attn_ws_bytes(t, sel, walks_of(&t->geom, q_per_head));
+    return attn_ws_bytes(t, sel, q_per_head);
 }
 
 zha_status zha_sparse_attn(const zha_tree *t, const void *q, int32_t q_per_head, const void *k_cache,
@@ -412,19 +416,21 @@ zha_status zha_sparse_attn(const zha_tree *t, const void *q, int32_t q_per_head,
     if (s != ZHA_OK) return s;
     if ((s = check_select(sel)) != ZHA_OK) return s;
     if (q_per_head < 1) return ZHA_ERR_ARG;
-    if (q_per_head != 1) return ZHA_ERR_UNSUPPORTED;
+    if (walks_of(&t->geom, q_per_head) > (int64_t(1) << 24)) return ZHA_ERR_UNSUPPORTED;
+    if (q_per_head > 1 && t->n_tokens + q_per_head > t->geom.max_tokens) return ZHA_ERR_CAPACITY;
     if (!q || !k_cache || !v_cache || !sel_blocks || !sel_count || !out || !ws) return ZHA_ERR_ARG;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
         !aligned16(ws) || !aligned_n(sel_blocks, 4) || !aligned_n(sel_count, 4))
         return ZHA_ERR_ALIGN;
     if (ws_bytes < zha_attn_workspace_bytes(t, sel, q_per_head)) return ZHA_ERR_WORKSPACE;
-    return do_attn(t, q, k_cache, v_cache, sel_blocks, nullptr, sel_count, sel->max_blocks_per_walk,
-                   tree_keys_bound(t, sel), out, ws, static_cast<hipStream_t>(stream));
+    return do_attn(t, q, q_per_head, k_cache, v_cache, sel_blocks, nullptr, sel_count,
+                   sel->max_blocks_per_walk, tree_keys_bound(t, sel, q_per_head), out, ws,
+                   static_cast<hipStream_t>(stream));
 }
 
 uint64_t zha_forward_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head) {
     if (check_tree(t) != ZHA_OK || check_select(sel) != ZHA_OK || q_per_head < 1) return 0;
-    return forward_ws_layout(t, sel, walks_of(&t->geom, q_per_head)).total;
+    return forward_ws_layout(t, sel, q_per_head).total;
 }
 
 zha_status zha_forward(zha_tree *t, int64_t n_new, const void *q, int32_t q_per_head,
@@ -435,28 +441,37 @@ zha_status zha_forward(zha_tree *t, int64_t n_new, const void *q, int32_t q_per_
     if (s != ZHA_OK) return s;
     if ((s = check_select(sel)) != ZHA_OK) return s;
     if (q_per_head < 1 || n_new < 0) return ZHA_ERR_ARG;
-    if (q_per_head != 1) return ZHA_ERR_UNSUPPORTED;
+    if (walks_of(&t->geom, q_per_head) > (int64_t(1) << 24)) return ZHA_ERR_UNSUPPORTED;
     if (!q || !k_cache || !v_cache || !out || !status || !ws) return ZHA_ERR_ARG;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
         !aligned16(ws) || !aligned_n(status, 4) || (stats && !aligned_n(stats, 8)))
         return ZHA_ERR_ALIGN;
     if (t->n_tokens + n_new > t->geom.max_tokens) return ZHA_ERR_CAPACITY;
+    if (q_per_head > 1 && t->n_tokens + q_per_head > t->geom.max_tokens) return ZHA_ERR_CAPACITY;
     if (ws_bytes < zha_forward_workspace_bytes(t, sel, q_per_head)) return ZHA_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (n_new > 0) {
+    // decode: the new rows join the tree first, so the query sees them
+    if (q_per_head == 1 && n_new > 0) {
         s = run_levels(t, k_cache, t->n_tokens, t->n_tokens + n_new, st);
         if (s != ZHA_OK) return s;
         t->n_tokens += n_new;
     }
-    const int64_t walks = walks_of(&t->geom, 1);
-    ForwardWs lay = forward_ws_layout(t, sel, walks);
+    ForwardWs lay = forward_ws_layout(t, sel, q_per_head);
     char *w = static_cast<char *>(ws);
     int32_t *sb = reinterpret_cast<int32_t *>(w + lay.sel_blocks);
     int32_t *sc = reinterpret_cast<int32_t *>(w + lay.sel_count);
-    s = do_search(t, q, sel, sb, sc, stats, status, nullptr, w + lay.search, st);
+    s = do_search(t, q, q_per_head, sel, sb, sc, stats, status, nullptr, w + lay.search, st);
     if (s != ZHA_OK) return s;
-    return do_attn(t, q, k_cache, v_cache, sb, nullptr, sc, sel->max_blocks_per_walk,
-                   tree_keys_bound(t, sel), out, w + lay.attn, st);
+    s = do_attn(t, q, q_per_head, k_cache, v_cache, sb, nullptr, sc, sel->max_blocks_per_walk,
+                tree_keys_bound(t, sel, q_per_head), out, w + lay.attn, st);
+    if (s != ZHA_OK) return s;
+    // prefill: the block joins the tree after its own queries have searched it
+    if (q_per_head > 1 && n_new > 0) {
+        s = run_levels(t, k_cache, t->n_tokens, t->n_tokens + n_new, st);
+        if (s != ZHA_OK) return s;
+        t->n_tokens += n_new;
+    }
+    return ZHA_OK;
 }
 
 uint64_t zha_dense_workspace_bytes(const zha_tree *t, int32_t max_budget) {
@@ -499,7 +514,7 @@ zha_status zha_dense_topk_attn(const zha_tree *t, const void *q, const void *k_c
     a.sharpness = g.sharpness;
     s = hip_status(launch_dense(a, g.head_dim, g.dtype, st));
     if (s != ZHA_OK) return s;
-    return do_attn(t, q, k_cache, v_cache, nullptr, a.sel, a.sel_n, max_budget, max_budget, out,
+    return do_attn(t, q, 1, k_cache, v_cache, nullptr, a.sel, a.sel_n, max_budget, max_budget, out,
                    wb + lay.attn, st);
 }
 

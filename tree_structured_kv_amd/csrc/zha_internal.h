@@ -68,6 +68,7 @@ struct SearchArgs {
     int2 *tile_map;                        // ws [walks * ceil(cand_cap / kTile)]
     int64_t n_tokens;
     int32_t walks;
+    int32_t qph;                           // queries per head (1 = decode)
     int32_t heads;                         // query heads per sequence
     int32_t group;
     int32_t kv_heads;
@@ -98,6 +99,8 @@ struct AttnArgs {
     int64_t n_tokens;
     int64_t n1;                    // whole level-1 chunks
     int32_t walks;
+    int32_t qph;                   // queries per head; > 1: a prefill block at
+                                   // positions [n_tokens, n_tokens + qph)
     int32_t heads;
     int32_t group;
     int32_t kv_heads;

@@ -398,8 +398,7 @@ __global__ __launch_bounds__(kThreads) void k_search_decode(SearchArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int w = xcd_remap(blockIdx.x, gridDim.x);
     if (w >= a.walks) return;
-    const int b = w / a.heads, h = w % a.heads, g = h / a.group;
-    const int64_t pair = static_cast<int64_t>(b) * a.kv_heads + g;
+    const int64_t pair = walk_pair(w, a.qph, a.heads, a.group, a.kv_heads);
     const int cap = a.cand_cap;
 
     __shared__ SelectShared sh;
@@ -503,8 +502,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_ls_score(SearchArgs a, int t,
         const int n = a.state[w].n;
         const int buf = a.state[w].buf;
         const int end = min(n, start + kTile);
-        const int b = w / a.heads, h = w % a.heads, g = h / a.group;
-        const int64_t pair = static_cast<int64_t>(b) * a.kv_heads + g;
+        const int64_t pair = walk_pair(w, a.qph, a.heads, a.group, a.kv_heads);
         const uint32_t *cur = a.cand + static_cast<int64_t>(w) * 2 * a.cand_cap +
                               static_cast<int64_t>(buf) * a.cand_cap;
         float *sc = a.score + static_cast<int64_t>(w) * a.cand_cap;

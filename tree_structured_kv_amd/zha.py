@@ -295,21 +295,21 @@ class Index:
         return (k.view(g.batch, g.num_kv_heads, cap, g.num_refs, g.head_dim),
                 b.view(g.batch, g.num_kv_heads, cap, g.num_refs))
 
-    def search_buffers(self, sel: Select):
-        W = self.walks
+    def search_buffers(self, sel: Select, qph: int = 1):
+        W = self.walks * qph
         return dict(
             sel_blocks=torch.empty(W, sel.max_blocks_per_walk, dtype=torch.int32, device=self.device),
             sel_count=torch.empty(W, dtype=torch.int32, device=self.device),
             stats=torch.zeros(W, STATS_WORDS, dtype=torch.int32, device=self.device),
             status=torch.zeros(1, dtype=torch.int32, device=self.device),
-            ws=torch.empty(max(zha_search_workspace_bytes(self.handle, sel), 16), dtype=torch.uint8,
+            ws=torch.empty(max(zha_search_workspace_bytes(self.handle, sel, qph), 16), dtype=torch.uint8,
                            device=self.device),
         )
 
-    def search(self, q, sel: Select, bufs=None, stream=None, visited=None):
-        bufs = bufs or self.search_buffers(sel)
+    def search(self, q, sel: Select, bufs=None, stream=None, visited=None, qph: int = 1):
+        bufs = bufs or self.search_buffers(sel, qph)
         zha_search(self.handle, q, sel, bufs["sel_blocks"], bufs["sel_count"], bufs["stats"],
-                   bufs["status"], bufs["ws"], 1, stream, visited)
+                   bufs["status"], bufs["ws"], qph, stream, visited)
         return bufs
 
     def visited_bitmap(self):
@@ -318,17 +318,17 @@ class Index:
         words = zha_visited_words(self.handle) // (g.batch * g.num_kv_heads)
         return torch.zeros(g.batch * g.num_kv_heads, words, dtype=torch.int32, device=self.device)
 
-    def attn_workspace(self, sel: Select):
-        return torch.empty(max(zha_attn_workspace_bytes(self.handle, sel), 16), dtype=torch.uint8,
+    def attn_workspace(self, sel: Select, qph: int = 1):
+        return torch.empty(max(zha_attn_workspace_bytes(self.handle, sel, qph), 16), dtype=torch.uint8,
                            device=self.device)
 
     def sparse_attn(self, q, k_cache, v_cache, sel: Select, sel_blocks, sel_count, out=None, ws=None,
-                    stream=None):
+                    stream=None, qph: int = 1):
         if out is None:
             out = torch.empty_like(q)
         if ws is None:
-            ws = self.attn_workspace(sel)
-        zha_sparse_attn(self.handle, q, k_cache, v_cache, sel, sel_blocks, sel_count, out, ws, 1, stream)
+            ws = self.attn_workspace(sel, qph)
+        zha_sparse_attn(self.handle, q, k_cache, v_cache, sel, sel_blocks, sel_count, out, ws, qph, stream)
         return out
 
     def dense_workspace(self, max_budget: int):
@@ -345,10 +345,11 @@ class Index:
                             sel_tokens, stream)
         return out
 
-    def forward_workspace(self, sel: Select):
-        return torch.empty(max(zha_forward_workspace_bytes(self.handle, sel), 16), dtype=torch.uint8,
+    def forward_workspace(self, sel: Select, qph: int = 1):
+        return torch.empty(max(zha_forward_workspace_bytes(self.handle, sel, qph), 16), dtype=torch.uint8,
                            device=self.device)
 
-    def forward(self, n_new, q, k_cache, v_cache, sel: Select, out, stats, status, ws, stream=None):
-        zha_forward(self.handle, n_new, q, k_cache, v_cache, sel, out, stats, status, ws, 1, stream)
+    def forward(self, n_new, q, k_cache, v_cache, sel: Select, out, stats, status, ws, stream=None,
+                qph: int = 1):
+        zha_forward(self.handle, n_new, q, k_cache, v_cache, sel, out, stats, status, ws, qph, stream)
         return out
