@@ -33,6 +33,8 @@ METRIC = "decode queries/sec (search+sparse attn) at 256K/1M keys; % HBM rooflin
 HBM_PEAK_GBS = 8000.0
 ROTATIONS = 8
 
+STREAM = "prefill-256K-stream"      # streaming build + prefill blocks (reported under `also`)
+
 WORKLOADS = {
     # name: (workload id, selection)
     "decode-256K-topp": (2, dict(mode="topp", p=0.9)),
@@ -266,6 +268,80 @@ def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True):
     return res
 
 
+def run_stream(w, select, threads, max_blocks=8192, max_candidates=0):
+    """Streaming build + prefill: the cache grows by blocks of w.block tokens;
+    each block's queries (every head) search the tree of the tokens before
+    the block, attend their selection plus the block's own keys (causal),
+    then the block is appended to the tree."""
+    import torch
+    from tree_structured_kv_amd import synth as S
+    from tree_structured_kv_amd import zha as Zm
+    T = w.block
+    nblk = w.n // T
+    K, V, _, R = gen_inputs(w, threads)
+    t0 = time.time()
+    Q = torch.empty(nblk, w.batch, w.heads, T, w.d, dtype=K.dtype, device="cuda")
+
+    def one(args):
+        b, g = args
+        ps = S.structure(w, b, g)
+        qs = [S.pair_queries(w, b, g, count=w.group * T, ps=ps, block=k).reshape(w.group, T, w.d)
+              for k in range(nblk)]
+        return b, g, torch.from_numpy(np.stack(qs)).to(K.dtype)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for b, g, qt in ex.map(one, [(b, g) for b in range(w.batch) for g in range(w.kv_heads)]):
+            Q[:, b, g * w.group:(g + 1) * w.group].copy_(qt)
+    torch.cuda.synchronize()
+    log(f"{w.name}: block queries generated in {time.time() - t0:.1f}s")
+    geom = Zm.make_geometry(w.batch, w.kv_heads, w.group, w.d, w.chunk, w.refs, w.levels, w.dtype,
+                            w.n, w.sharpness)
+    sel = Zm.make_select(select["mode"], select.get("p", 0.9), select.get("k", (1,)),
+                         max_blocks=max_blocks, max_candidates=max_candidates)
+
+    def stream(record):
+        idx = Zm.Index(geom, R)
+        bufs = idx.search_buffers(sel, T)
+        aws = idx.attn_workspace(sel, T)
+        out = torch.empty(w.batch, w.heads, T, w.d, dtype=K.dtype, device="cuda")
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nblk)]
+        stats = []
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for k in range(nblk):
+            e = evs[k]
+            e[0].record()
+            idx.search(Q[k], sel, bufs, qph=T)
+            e[1].record()
+            idx.sparse_attn(Q[k], K, V, sel, bufs["sel_blocks"], bufs["sel_count"], out, aws, qph=T)
+            e[2].record()
+            idx.append(K, T)
+            e[3].record()
+            if record and k % 8 == 7:
+                torch.cuda.synchronize()
+                stats.append(Zm.stats_to_dicts(bufs["stats"][:: 97].cpu()))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        ms = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                       for e in evs])
+        return wall, ms, stats, int(bufs["status"].cpu()[0])
+
+    stream(False)                    # warm-up pass (kernel loading, allocator)
+    wall, ms, stats, status = stream(True)
+    rows = [s for st in stats for s in st]
+    tot = ms.sum(axis=0)
+    return dict(
+        workload=w.name, select=select, tokens=w.n, block=T, blocks=nblk,
+        tokens_per_s=w.n / wall, wall_ms=wall * 1e3,
+        search_ms=float(tot[0]), attn_ms=float(tot[1]), append_ms=float(tot[2]),
+        append_fraction=float(tot[2] / tot.sum()),
+        last_block_ms=[float(x) for x in ms[-1]],
+        comparisons_per_query_head=float(np.mean([r["comparisons"] for r in rows])) if rows else None,
+        tree_keys_per_query_head=float(np.mean([r["keys_read"] for r in rows])) if rows else None,
+        max_blocks_per_walk=max_blocks, max_candidates=max_candidates, status=status,
+    )
+
+
 def cpu_baseline(w, select, Q_host, seconds_budget=15.0):
     """The fp64 oracle (walk + attention) over the query heads of sampled
     sequences, threads over walks (ctypes drops the GIL)."""
@@ -348,6 +424,8 @@ def main():
     ap.add_argument("--also", default="decode-1M-topp,decode-256K-topk64",
                     help="comma-separated extra workloads reported under 'also'")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--stream", type=int, default=1,
+                    help="also run the streaming build + prefill workload (1/0)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense full-scan baseline")
     ap.add_argument("--calibrate", action="store_true",
                     help="also copy 1 GiB three times (the known-size kernel that scales HBM counters)")
@@ -382,6 +460,10 @@ def main():
     Q0 = res["Q"][0, 0].float().cpu().numpy()
 
     also = []
+    if args.stream:
+        st = run_stream(S.WORKLOADS[3], dict(mode="topp", p=0.9), args.threads)
+        log(json.dumps(st))
+        also.append(st)
     for name in [x for x in args.also.split(",") if x]:
         wid2, sel2 = WORKLOADS[name]
         r2 = run_gpu(Zm, S.WORKLOADS[wid2], sel2, max(5, args.steps // 3), 2, args.threads,

@@ -216,21 +216,20 @@ def pair_queries(w: Workload, b: int, g: int, rot: int = 0, count: int | None = 
             out[i] = acc / math.sqrt(m)
         return _cast(w, out)
     nseg = ps.centroids.shape[0]
+    if w.structure != "mixed":
+        if block is not None:
+            lim = max(1, int(np.searchsorted(ps.seg_start, w.block * block, side="left")))
+        else:
+            lim = nseg
+        j = rq.integers(0, lim, size=count)
+        out = w.amp * ps.centroids[j] + w.noise * rq.standard_normal((count, w.d))
+        return _cast(w, out)
     out = np.zeros((count, w.d))
     for i in range(count):
-        if w.structure == "mixed":
-            h = g * w.group + i
-            m = (1, 8, 64)[(w.heads * b + h) % 3]
-            m = min(m, nseg)
-            tg = rq.choice(nseg, size=m, replace=False)
-            direction = ps.centroids[tg].sum(axis=0) / math.sqrt(m)
-        else:
-            if block is not None:
-                lim = max(1, int(np.searchsorted(ps.seg_start, w.block * block, side="left")))
-                j = int(rq.integers(0, lim))
-            else:
-                j = int(rq.integers(0, nseg))
-            direction = ps.centroids[j]
+        h = g * w.group + i
+        m = min((1, 8, 64)[(w.heads * b + h) % 3], nseg)
+        tg = rq.choice(nseg, size=m, replace=False)
+        direction = ps.centroids[tg].sum(axis=0) / math.sqrt(m)
         out[i] = w.amp * direction + w.noise * rq.standard_normal(w.d)
     return _cast(w, out)
 
