@@ -190,12 +190,15 @@ def run_dense(idx, w, Q, K, V, per_rot, steps, warmup):
                 max_budget=maxb)
 
 
+ENGINE = "auto"
+
+
 def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True):
     import torch
     from tree_structured_kv_amd import zha as Zm
     K, V, Q, R, idx, build_ms = prepare(w, threads)
     sel = Zm.make_select(select["mode"], select.get("p", 0.9), select.get("k", (1,)),
-                         max_blocks=w.n // w.chunk)
+                         max_blocks=w.n // w.chunk, engine=ENGINE)
     bufs = idx.search_buffers(sel)
     out = torch.empty(w.batch, w.heads, w.d, dtype=K.dtype, device="cuda")
     aws = idx.attn_workspace(sel)
@@ -423,6 +426,7 @@ def main():
     ap.add_argument("--workload", default="decode-256K-topp", choices=sorted(WORKLOADS))
     ap.add_argument("--also", default="decode-1M-topp,decode-256K-topk64",
                     help="comma-separated extra workloads reported under 'also'")
+    ap.add_argument("--engine", default="auto", choices=["auto", "persistent", "level-sync", "union"])
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--stream", type=int, default=1,
                     help="also run the streaming build + prefill workload (1/0)")
@@ -441,6 +445,8 @@ def main():
     from tree_structured_kv_amd import synth as S
     from tree_structured_kv_amd import zha as Zm
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    global ENGINE
+    ENGINE = args.engine
 
     bw_ach = hbm_probe(Zm)
     log(f"achievable HBM read bandwidth {bw_ach:.0f} GB/s")

@@ -66,15 +66,24 @@ typedef enum { ZHA_F32 = 0, ZHA_BF16 = 1 } zha_dtype;
 
 enum { ZHA_TOPP = 0, ZHA_TOPK = 1 };
 
-/* Search engines (zha_select.engine).  Both give identical results.
+/* Search engines (zha_select.engine).  All give the same selections (the
+ * persistent and level-synchronous engines bit-identical results; the union
+ * engine sums dot products in another order, so a score may differ in the
+ * last fp32 bits, which matters only at cuts closer than that).
  *   ZHA_ENGINE_PERSISTENT: one workgroup per walk runs all steps in one
- *     launch; best when every walk does the same work (top-K).
+ *     launch; best when every walk does the same work.
  *   ZHA_ENGINE_LEVEL_SYNC: per step, one launch scores the candidates of all
  *     walks as one flat list and one launch cuts each walk; balances walks
- *     of very different sizes (top-p).
- *   ZHA_ENGINE_AUTO: level-synchronous for top-p with at least 64 walks,
- *     persistent otherwise. */
-enum { ZHA_ENGINE_AUTO = 0, ZHA_ENGINE_PERSISTENT = 1, ZHA_ENGINE_LEVEL_SYNC = 2 };
+ *     of very different sizes.
+ *   ZHA_ENGINE_UNION: per step, each (sequence, KV head) pair keeps one list,
+ *     the union of its query heads' candidates with a head mask per node;
+ *     every node record is read once and scored for all heads of the group
+ *     (fp32 matrix-core tiles), then each head cuts its own candidates.
+ *     Decode only (q_per_head = 1), group_size <= 16.
+ *   ZHA_ENGINE_AUTO: union for decode with 16 query heads per KV head and at
+ *     least 64 walks, else level-synchronous for top-p with at least 64
+ *     walks, else persistent. */
+enum { ZHA_ENGINE_AUTO = 0, ZHA_ENGINE_PERSISTENT = 1, ZHA_ENGINE_LEVEL_SYNC = 2, ZHA_ENGINE_UNION = 3 };
 
 /* Device status bits. */
 #define ZHA_FLAG_CAND_OVERFLOW 1u  /* a step had more candidates than max_candidates;

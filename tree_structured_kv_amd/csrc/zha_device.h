@@ -77,6 +77,17 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Max over aligned groups of WIDTH consecutive lanes (WIDTH in {1, 2, 4, 8,
+// 16}); every lane of a group gets the group's max.
+template <int WIDTH>
+__device__ __forceinline__ float group_max(float v) {
+    if (WIDTH >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
+    if (WIDTH >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
+    if (WIDTH >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    if (WIDTH >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+    return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v, int width) {
     for (int off = 1; off < width; off <<= 1) v += __shfl_xor(v, off, 64);
     return v;

@@ -83,7 +83,7 @@ zha_status check_select(const zha_select *sel) {
     }
     if (sel->max_blocks_per_walk < 1) return ZHA_ERR_ARG;
     if (sel->max_candidates < 0) return ZHA_ERR_ARG;
-    if (sel->engine < ZHA_ENGINE_AUTO || sel->engine > ZHA_ENGINE_LEVEL_SYNC) return ZHA_ERR_ARG;
+    if (sel->engine < ZHA_ENGINE_AUTO || sel->engine > ZHA_ENGINE_UNION) return ZHA_ERR_ARG;
     return ZHA_OK;
 }
 
@@ -92,7 +92,8 @@ int64_t walks_of(const zha_geometry *g, int32_t qph) {
 }
 
 struct SearchWs {
-    uint64_t cand, score, state, tile_count, tile_map, total;
+    uint64_t cand, score, state, tile_count, tile_map, u_ids, u_mask, u_omask, u_n, u_next, h_score,
+        total;
 };
 SearchWs search_ws_layout(const zha_tree *t, const zha_select *sel, int64_t walks) {
     const uint64_t cap = static_cast<uint64_t>(cand_capacity(t, sel));
@@ -102,7 +103,14 @@ SearchWs search_ws_layout(const zha_tree *t, const zha_select *sel, int64_t walk
     l.state = l.score + align_up(walks * cap * sizeof(float));
     l.tile_count = l.state + align_up(walks * sizeof(WalkState));
     l.tile_map = l.tile_count + align_up((ZHA_MAX_STEPS + 1) * sizeof(int32_t));
-    l.total = l.tile_map + align_up(walks * ((cap + kTile - 1) / kTile) * sizeof(int2));
+    l.u_ids = l.tile_map + align_up(walks * ((cap + kTile - 1) / kTile) * sizeof(int2));
+    const uint64_t pairs = uint64_t(t->geom.batch) * t->geom.num_kv_heads;
+    l.u_mask = l.u_ids + align_up(pairs * 2 * cap * sizeof(uint32_t));
+    l.u_omask = l.u_mask + align_up(pairs * 2 * cap * sizeof(uint32_t));
+    l.u_n = l.u_omask + align_up(pairs * cap * sizeof(uint32_t));
+    l.u_next = l.u_n + align_up(pairs * 2 * sizeof(int32_t));
+    l.h_score = l.u_next + align_up(walks * sizeof(int32_t));
+    l.total = l.h_score + align_up(walks * cap * sizeof(float));
     return l;
 }
 
@@ -226,6 +234,14 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
     a.state = reinterpret_cast<WalkState *>(static_cast<char *>(ws) + lay.state);
     a.tile_count = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + lay.tile_count);
     a.tile_map = reinterpret_cast<int2 *>(static_cast<char *>(ws) + lay.tile_map);
+    a.u_ids = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.u_ids);
+    a.u_mask = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.u_mask);
+    a.u_omask = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.u_omask);
+    a.u_n = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + lay.u_n);
+    a.u_next = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + lay.u_next);
+    a.h_score = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.h_score);
+    a.u_score = a.score;
+    a.pairs = g.batch * g.num_kv_heads;
     a.score_grid = 1024;
     a.n_tokens = t->n_tokens;
     a.walks = static_cast<int32_t>(walks);
@@ -252,8 +268,16 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
     for (int l = 1; l < g.levels; ++l) n0 += a.nl[l] - int64_t(g.chunk) * a.nl[l + 1];
     if (n0 > a.cand_cap) n0 = a.cand_cap;
     int engine = sel->engine;
-    if (engine == ZHA_ENGINE_AUTO)
-        engine = (sel->mode == ZHA_TOPP && walks >= 64) ? ZHA_ENGINE_LEVEL_SYNC : ZHA_ENGINE_PERSISTENT;
+    if (engine == ZHA_ENGINE_AUTO) {
+        if (qph == 1 && t->geom.group_size == 16 && walks >= 64)
+            engine = ZHA_ENGINE_UNION;
+        else if (sel->mode == ZHA_TOPP && walks >= 64)
+            engine = ZHA_ENGINE_LEVEL_SYNC;
+        else
+            engine = ZHA_ENGINE_PERSISTENT;
+    }
+    if (engine == ZHA_ENGINE_UNION)
+        return hip_status(launch_union(a, g.head_dim, g.num_refs, g.dtype, static_cast<int>(n0), st));
     return hip_status(launch_search(a, g.head_dim, g.num_refs, g.dtype, engine, static_cast<int>(n0), st));
 }
 
@@ -398,6 +422,8 @@ zha_status zha_search(const zha_tree *t, const void *q, int32_t q_per_head, cons
     if (!aligned16(q) || !aligned16(ws) || !aligned_n(sel_blocks, 4) || !aligned_n(sel_count, 4) ||
         !aligned_n(status, 4) || (stats && !aligned_n(stats, 8)) || (visited && !aligned_n(visited, 4)))
         return ZHA_ERR_ALIGN;
+    if (sel->engine == ZHA_ENGINE_UNION && (q_per_head != 1 || t->geom.group_size > 16))
+        return ZHA_ERR_UNSUPPORTED;
     if (ws_bytes < zha_search_workspace_bytes(t, sel, q_per_head)) return ZHA_ERR_WORKSPACE;
     return do_search(t, q, q_per_head, sel, sel_blocks, sel_count, stats, status, visited, ws,
                      static_cast<hipStream_t>(stream));
@@ -448,6 +474,8 @@ zha_status zha_forward(zha_tree *t, int64_t n_new, const void *q, int32_t q_per_
         return ZHA_ERR_ALIGN;
     if (t->n_tokens + n_new > t->geom.max_tokens) return ZHA_ERR_CAPACITY;
     if (q_per_head > 1 && t->n_tokens + q_per_head > t->geom.max_tokens) return ZHA_ERR_CAPACITY;
+    if (sel->engine == ZHA_ENGINE_UNION && (q_per_head != 1 || t->geom.group_size > 16))
+        return ZHA_ERR_UNSUPPORTED;
     if (ws_bytes < zha_forward_workspace_bytes(t, sel, q_per_head)) return ZHA_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     // decode: the new rows join the tree first, so the query sees them

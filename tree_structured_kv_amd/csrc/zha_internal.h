@@ -66,6 +66,16 @@ struct SearchArgs {
     WalkState *state;                      // ws [walks]          (level-synchronous)
     int32_t *tile_count;                   // ws [ZHA_MAX_STEPS+1] (level-synchronous)
     int2 *tile_map;                        // ws [walks * ceil(cand_cap / kTile)]
+    // union engine: one candidate list per (sequence, KV head) pair, the
+    // union over its query heads, with a head mask per node
+    uint32_t *u_ids;                       // ws [pairs][2][cand_cap]
+    uint32_t *u_mask;                      // ws [pairs][2][cand_cap]
+    uint32_t *u_omask;                     // ws [pairs][cand_cap]  heads that opened the node
+    int32_t *u_n;                          // ws [pairs][2]  {list size, current buffer}
+    int32_t *u_next;                       // ws [walks]  next step's candidates per head
+    float *u_score;                        // ws [pairs][group][cand_cap] (aliases `score`)
+    float *h_score;                        // ws [walks][cand_cap]  a head's compacted scores
+    int32_t pairs;
     int64_t n_tokens;
     int32_t walks;
     int32_t qph;                           // queries per head (1 = decode)
@@ -131,6 +141,7 @@ struct DenseArgs {
 hipError_t launch_level(const LevelArgs &a, int D, int dtype, bool leaf, hipStream_t st);
 hipError_t launch_search(const SearchArgs &a, int D, int R, int dtype, int engine, int n0,
                          hipStream_t st);
+hipError_t launch_union(const SearchArgs &a, int D, int R, int dtype, int n0, hipStream_t st);
 hipError_t launch_attn(const AttnArgs &a, int D, int dtype, hipStream_t st);
 hipError_t launch_dense(const DenseArgs &a, int D, int dtype, hipStream_t st);
 hipError_t launch_probe(const void *buf, uint64_t bytes, float *sink, hipStream_t st);

@@ -36,62 +36,14 @@
 // order, which keeps every candidate list in span order without a sort.
 #include "zha_device.h"
 #include "zha_internal.h"
+#include "zha_walk.h"
 
 namespace zha {
 
 namespace {
 
-constexpr int kThreads = 512;          // workgroup of the persistent and cut kernels
-constexpr int kWaves = kThreads / 64;
 constexpr int kScoreThreads = 256;     // workgroup of the level-synchronous scorer
 constexpr int kU = 4;                  // candidates in flight per wavefront
-constexpr float kMassScale = 2147483648.0f;  // 2^31
-
-__device__ __forceinline__ uint64_t rank_key(float score, uint32_t id, int log2c) {
-    const uint32_t lvl = id >> kLevelShift;
-    const uint32_t j = id & kIndexMask;
-    const uint32_t start = j << (log2c * lvl);
-    return (static_cast<uint64_t>(ordered_bits(score)) << 32) |
-           static_cast<uint64_t>(0xffffffffu - start);
-}
-
-struct SelectShared {
-    uint32_t hcnt[256];
-    unsigned long long hw[256];
-    unsigned long long scan64[kWaves];
-    unsigned long long tau;
-    unsigned long long above;
-    uint32_t dig;
-    uint32_t cnt;
-    float red[kWaves];
-    uint32_t flags;
-};
-
-// Block-wide exclusive scan of a uint64 per thread (kThreads threads);
-// returns the prefix and writes the total to *total.
-__device__ __forceinline__ unsigned long long block_exscan64(unsigned long long v,
-                                                             unsigned long long *scratch,
-                                                             unsigned long long *total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    unsigned long long incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        unsigned long long o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-    }
-    if (lane == 63) scratch[wave] = incl;
-    __syncthreads();
-    unsigned long long base = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        unsigned long long x = scratch[w];
-        if (w < wave) base += x;
-        tot += x;
-    }
-    __syncthreads();
-    *total = tot;
-    return base + incl - v;
-}
 
 template <int D, typename QT>
 __device__ __forceinline__ void load_q(const SearchArgs &a, int w, float (&qv)[4]) {
@@ -100,10 +52,6 @@ __device__ __forceinline__ void load_q(const SearchArgs &a, int w, float (&qv)[4
     const QT *qp = static_cast<const QT *>(a.q) + static_cast<int64_t>(w) * D + 4 * sub;
 #pragma unroll
     for (int e = 0; e < 4; ++e) qv[e] = Elem<QT>::load(qp, e);
-}
-
-__device__ __forceinline__ bool step_forced(const SearchArgs &a, int t, int n) {
-    return (n <= 1) || (a.mode == ZHA_TOPK && a.k[t] >= n) || (a.mode == ZHA_TOPP && a.p >= 1.0f);
 }
 
 // One wavefront scores candidates first, first + stride, ... below `end`, kU
@@ -191,104 +139,6 @@ __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair, c
     return wmax;
 }
 
-// Workgroup (kThreads): the rank key of the candidate at the cut of a step
-// that is not forced; every candidate with a key >= it opens.
-__device__ unsigned long long cut_tau(const SearchArgs &a, int n, const uint32_t *cur,
-                                      const float *sc, float mx, int kt, SelectShared &sh) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int log2c = a.log2c;
-    const bool by_mass = (a.mode == ZHA_TOPP) && (a.p > 0.f);
-    const bool flat = !(mx > -INFINITY);   // every score -inf: equal masses
-    unsigned long long target;
-    if (by_mass) {
-        unsigned long long zpart = 0;
-        for (int i = tid; i < n; i += kThreads) {
-            const float e = flat ? 1.f : expf(sc[i] - mx);
-            zpart += static_cast<unsigned long long>(__float2uint_rn(e * kMassScale));
-        }
-        unsigned long long z;
-        (void)block_exscan64(zpart, sh.scan64, &z);
-        const double tq = ceil(static_cast<double>(a.p) * static_cast<double>(z));
-        target = static_cast<unsigned long long>(tq);
-        if (target < 1) target = 1;
-        if (target > z) target = z;
-    } else {
-        const int m = (a.mode == ZHA_TOPK) ? (kt < n ? kt : n) : 1;
-        target = static_cast<unsigned long long>(m < 1 ? 1 : m);
-    }
-
-    unsigned long long prefix = 0, need = target, tau = 0;
-    for (int pass = 0; pass < 8; ++pass) {
-        const int shift = 56 - 8 * pass;
-        for (int i = tid; i < 256; i += kThreads) { sh.hcnt[i] = 0; sh.hw[i] = 0; }
-        __syncthreads();
-        for (int i = tid; i < n; i += kThreads) {
-            const float scv = sc[i];
-            const unsigned long long key = rank_key(scv, cur[i], log2c);
-            if (pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8))) {
-                const uint32_t dg = static_cast<uint32_t>(key >> shift) & 255u;
-                unsigned long long wgt = 1;
-                if (by_mass) {
-                    const float e = flat ? 1.f : expf(scv - mx);
-                    wgt = static_cast<unsigned long long>(__float2uint_rn(e * kMassScale));
-                }
-                atomicAdd(&sh.hcnt[dg], 1u);
-                if (wgt) atomicAdd(&sh.hw[dg], wgt);
-            }
-        }
-        __syncthreads();
-        if (wave == 0) {
-            // lane covers digits 255-4*lane .. 252-4*lane (descending)
-            unsigned long long lw[4], lsum = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { lw[e] = sh.hw[255 - 4 * lane - e]; lsum += lw[e]; }
-            unsigned long long incl = lsum;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                unsigned long long o = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += o;
-            }
-            const unsigned long long excl = incl - lsum;
-            const unsigned long long mask = __ballot(incl >= need);
-            const int first = mask ? (__ffsll(static_cast<long long>(mask)) - 1) : 63;
-            if (lane == first) {
-                unsigned long long run = excl;
-                int pick = 3;
-                for (int e = 0; e < 4; ++e) {
-                    if (run + lw[e] >= need) { pick = e; break; }
-                    run += lw[e];
-                }
-                if (!mask) { pick = 3; run = excl + lw[0] + lw[1] + lw[2]; }
-                const uint32_t dg = 255u - 4u * lane - pick;
-                sh.dig = dg;
-                sh.above = run;
-                sh.cnt = sh.hcnt[dg];
-            }
-        }
-        __syncthreads();
-        prefix |= static_cast<unsigned long long>(sh.dig) << shift;
-        need -= sh.above;
-        const uint32_t cnt = sh.cnt;
-        if (pass == 7) {
-            tau = prefix;
-            break;
-        }
-        if (cnt <= 1) {
-            // at most one key carries this prefix: fetch it
-            for (int i = tid; i < n; i += kThreads) {
-                const unsigned long long key = rank_key(sc[i], cur[i], log2c);
-                if ((key >> shift) == (prefix >> shift)) sh.tau = key;
-            }
-            __syncthreads();
-            tau = (cnt == 0) ? 0ull : sh.tau;
-            __syncthreads();
-            break;
-        }
-        __syncthreads();
-    }
-    return tau;
-}
-
 // Workgroup (kThreads): open every candidate with a rank key >= tau (all if
 // forced), in candidate order: level-1 nodes append their block id to the
 // selection, others append their c children to nxt.  Returns the number of
@@ -329,64 +179,6 @@ __device__ void open_cut(const SearchArgs &a, int n, const uint32_t *cur, const 
             }
         }
     }
-}
-
-// Workgroup: the roots -- every level-L node, then the nodes of lower levels
-// whose parent chunk is not full yet, in span order.  Returns their number
-// (clamped to the candidate capacity).
-__device__ int write_roots(const SearchArgs &a, uint32_t *cur, uint32_t &flags) {
-    const int tid = threadIdx.x, c = a.chunk, L = a.levels, cap = a.cand_cap;
-    int64_t n_roots = 0;
-    for (int l = L; l >= 1; --l) {
-        const int64_t first = (l == L) ? 0 : static_cast<int64_t>(c) * a.nl[l + 1];
-        const int64_t cnt = a.nl[l] - first;
-        for (int64_t i = tid; i < cnt; i += blockDim.x) {
-            const int64_t pos = n_roots + i;
-            if (pos < cap) cur[pos] = (static_cast<uint32_t>(l) << kLevelShift) | static_cast<uint32_t>(first + i);
-        }
-        n_roots += cnt;
-    }
-    if (n_roots > cap) { flags |= ZHA_FLAG_CAND_OVERFLOW; n_roots = cap; }
-    return static_cast<int>(n_roots);
-}
-
-// One thread: sel_count, status and the per-walk statistics.
-template <int R>
-__device__ void finish_walk(const SearchArgs &a, int w, int steps, const int32_t *scored,
-                            const int32_t *opened, int64_t sel_n, int32_t unforced, uint32_t fl) {
-    if (sel_n > a.sel_cap) fl |= ZHA_FLAG_SEL_OVERFLOW;
-    a.sel_count[w] = static_cast<int32_t>(sel_n < a.sel_cap ? sel_n : a.sel_cap);
-    if (fl) atomicOr(a.status, fl);
-    if (a.stats) {
-        zha_walk_stats st;
-        int64_t tot_scored = 0;
-        for (int i = 0; i < ZHA_MAX_STEPS; ++i) {
-            st.scored[i] = i < steps ? scored[i] : 0;
-            st.opened[i] = i < steps ? opened[i] : 0;
-            if (i < steps) tot_scored += scored[i];
-        }
-        const int64_t tail = a.n_tokens - static_cast<int64_t>(a.chunk) * a.nl[1];
-        st.steps = steps;
-        st.keys_read = static_cast<int32_t>(sel_n * a.chunk + tail);
-        st.blocks = static_cast<int32_t>(sel_n);
-        st.unforced_scored = unforced;
-        st.comparisons = tot_scored * R + st.keys_read;
-        st.flags = fl;
-        st.reserved = 0;
-        a.stats[w] = st;
-    }
-}
-
-__device__ __forceinline__ float block_max(float v, SelectShared &sh) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = wave_max(v, 1, 64);
-    if (lane == 0) sh.red[wave] = v;
-    __syncthreads();
-    float m = sh.red[0];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) m = fmaxf(m, sh.red[i]);
-    __syncthreads();
-    return m;
 }
 
 }  // namespace
