@@ -17,6 +17,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import math
 import os
@@ -32,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode queries/sec (search+sparse attn) at 256K/1M keys; % HBM roofline"
 HBM_PEAK_GBS = 8000.0
 ROTATIONS = 8
+FLUSH_BYTES = 1 << 30               # written between timed steps: evicts L2 and the 256 MB MALL
 
 STREAM = "prefill-256K-stream"      # streaming build + prefill blocks (reported under `also`)
 
@@ -171,13 +174,16 @@ def run_dense(idx, w, Q, K, V, per_rot, steps, warmup):
     for r in range(warmup):
         idx.dense_topk_attn(Q[r % ROTATIONS], K, V, budgets[r % ROTATIONS], maxb, out, ws)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record()
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for i in range(steps):
+        flush.fill_(i & 0xFF)
+        evs[i][0].record()
         idx.dense_topk_attn(Q[i % ROTATIONS], K, V, budgets[i % ROTATIONS], maxb, out, ws)
-    ev[1].record()
+        evs[i][1].record()
     torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1]) / steps
+    del flush
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     e = 2 if w.dtype == "bf16" else 4
     walks = w.batch * w.heads
     k_bytes = w.batch * w.kv_heads * w.n * w.d * e
@@ -231,15 +237,28 @@ def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True):
     for r in range(warmup):
         step(r)
     torch.cuda.synchronize()
+    # timed steps: each step's search and attention bracketed by HIP events
+    # on the launch stream, with 1 GiB written between steps so that every
+    # step reads its tree records and keys from HBM, not from L2 or the MALL
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(steps):
+        flush.fill_(i & 0xFF)
         step(i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    del flush
     search_ms = [e[0].elapsed_time(e[1]) for e in evs]
     attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    # the same steps back to back (caches warm from the previous step)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    b2b_ms = (time.perf_counter() - t0) / steps * 1e3
 
     # per-step bytes in the order the steps ran
     by_step = [acct[i % ROTATIONS] for i in range(steps)]
@@ -256,10 +275,13 @@ def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True):
     dense = run_dense(idx, w, Q, K, V, per_rot, steps, warmup) if dense_baseline else None
     res = dict(
         dense=dense,
-        workload=w, select=select, wall_s=wall, steps=steps,
-        ms_per_step=wall / steps * 1e3,
-        qps=w.batch * steps / wall,
-        walks_per_s=walks * steps / wall,
+        workload=w, select=select, wall_s=wall, steps=steps, engine=idx.engine(sel),
+        ms_per_step=float(step_ms.mean()),
+        ms_p10=float(np.percentile(step_ms, 10)), ms_p50=float(np.percentile(step_ms, 50)),
+        ms_p90=float(np.percentile(step_ms, 90)),
+        qps=w.batch / (float(step_ms.mean()) * 1e-3),
+        walks_per_s=walks / (float(step_ms.mean()) * 1e-3),
+        back_to_back_ms=b2b_ms, back_to_back_qps=w.batch / (b2b_ms * 1e-3),
         search_ms=float(np.mean(search_ms)), attn_ms=float(np.mean(attn_ms)),
         search_bytes=mean["search"], attn_bytes=mean["attn"], bytes=mean,
         build_ms=build_ms,
@@ -391,6 +413,42 @@ def cpu_baseline(w, select, Q_host, seconds_budget=15.0):
                 seconds=dt)
 
 
+ENGINE_KERNELS = {
+    "union": "k_un_init, then per level k_un_score + k_un_cut + k_un_expand",
+    "level-sync": "k_ls_init, then per level k_ls_score + k_ls_cut",
+    "persistent": "one k_search_decode launch",
+}
+
+
+def kernel_digest():
+    """Digest of the kernel sources: HBM counters taken on other sources are stale."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "tree_structured_kv_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, engine):
+    """HBM bytes per zha_search call from the committed rocprofv3 counter
+    summaries (a `bench-traffic:` JSON line in profiles/*.md), if they were
+    taken on the current kernel sources; else None."""
+    digest = kernel_digest()
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(f) as fh:
+            for line in fh:
+                if not line.startswith("bench-traffic: "):
+                    continue
+                d = json.loads(line[len("bench-traffic: "):])
+                if d.get("workload") == workload and d.get("engine") == engine and d.get("source") == digest:
+                    d["profile"] = os.path.relpath(f, ROOT)
+                    return d
+    return None
+
+
 def summary(res, bw_ach):
     w = res["workload"]
     sel = res["select"]
@@ -400,8 +458,10 @@ def summary(res, bw_ach):
     step_bytes = by["search"] + by["attn"]
     step_gbs = step_bytes / (res["ms_per_step"] * 1e-3) / 1e9
     return dict(
-        workload=w.name, select=sel,
+        workload=w.name, select=sel, engine=res["engine"],
         qps=res["qps"], walks_per_s=res["walks_per_s"], ms_per_step=res["ms_per_step"],
+        ms_p10=res["ms_p10"], ms_p50=res["ms_p50"], ms_p90=res["ms_p90"],
+        back_to_back_qps=res["back_to_back_qps"], back_to_back_ms=res["back_to_back_ms"],
         search_ms=res["search_ms"], attn_ms=res["attn_ms"], build_ms=res["build_ms"],
         search_bytes=by["search"], attn_bytes=by["attn"],
         search_bytes_per_head=by["search_per_head"], attn_bytes_per_head=by["attn_per_head"],
@@ -484,6 +544,7 @@ def main():
         log(f"cpu baseline {cpu}")
 
     ach = main_sum["search_gbs"]
+    traffic = measured_traffic(args.workload, main_sum["engine"])
     out = {
         "metric": METRIC,
         "value": main_sum["qps"],
@@ -505,10 +566,12 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": ach / HBM_PEAK_GBS, "traffic": None,
-            "kernel": "zha_search (level-synchronous: k_ls_score + k_ls_cut launches)",
+            "frac": ach / HBM_PEAK_GBS,
+            "traffic": None if traffic is None else traffic["bytes_per_call"],
+            "kernel": f"zha_search ({main_sum['engine']} engine: {ENGINE_KERNELS[main_sum['engine']]})",
             "bytes_per_launch": main_sum["search_bytes"], "launch_ms": main_sum["search_ms"],
-            "achievable_gbs": bw_ach,
+            "achievable_gbs": bw_ach, "frac_of_achievable": ach / bw_ach,
+            "traffic_source": None if traffic is None else traffic["profile"],
         },
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
         "step": {k: v for k, v in main_sum.items() if k not in ("workload", "select", "qps")},

@@ -199,6 +199,13 @@ zha_status zha_append(zha_tree *t, const void *k_cache, int64_t n_new, void *str
 /* Workspace bytes of zha_search for q_per_head queries per head. */
 uint64_t zha_search_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head);
 
+/* The engine (ZHA_ENGINE_PERSISTENT, _LEVEL_SYNC or _UNION) zha_search runs
+ * for these arguments: sel->engine itself, or what ZHA_ENGINE_AUTO resolves
+ * to.  Host only, enqueues nothing.  -1 if the tree or selection is invalid
+ * or the engine does not support the shape.  All engines give identical
+ * selections wherever the cut's score gap exceeds rounding. */
+int32_t zha_search_engine(const zha_tree *t, const zha_select *sel, int32_t q_per_head);
+
 /* One walk per (sequence, query head, query).  Candidates start as the
  * roots: every top-level node plus every node whose parent chunk has not
  * filled; per step they are scored (max over r of s*<key_r, q> + bias_r),

@@ -198,6 +198,17 @@ int64_t visited_words_per_pair(const zha_tree *t) {
     return (bits + 31) / 32;
 }
 
+// The engine a search runs on: the caller's choice, or for AUTO the one
+// that measured fastest for the shape (union when 16 query heads share a KV
+// head in decode, level-synchronous for wide top-p batches, else persistent).
+int resolve_engine(const zha_tree *t, const zha_select *sel, int32_t qph) {
+    if (sel->engine != ZHA_ENGINE_AUTO) return sel->engine;
+    const int64_t walks = walks_of(&t->geom, qph);
+    if (qph == 1 && t->geom.group_size == 16 && walks >= 64) return ZHA_ENGINE_UNION;
+    if (sel->mode == ZHA_TOPP && walks >= 64) return ZHA_ENGINE_LEVEL_SYNC;
+    return ZHA_ENGINE_PERSISTENT;
+}
+
 zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_select *sel,
                      int32_t *sel_blocks, int32_t *sel_count, zha_walk_stats *stats, uint32_t *status,
                      uint32_t *visited, void *ws, hipStream_t st) {
@@ -267,15 +278,7 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
     int64_t n0 = a.nl[g.levels];
     for (int l = 1; l < g.levels; ++l) n0 += a.nl[l] - int64_t(g.chunk) * a.nl[l + 1];
     if (n0 > a.cand_cap) n0 = a.cand_cap;
-    int engine = sel->engine;
-    if (engine == ZHA_ENGINE_AUTO) {
-        if (qph == 1 && t->geom.group_size == 16 && walks >= 64)
-            engine = ZHA_ENGINE_UNION;
-        else if (sel->mode == ZHA_TOPP && walks >= 64)
-            engine = ZHA_ENGINE_LEVEL_SYNC;
-        else
-            engine = ZHA_ENGINE_PERSISTENT;
-    }
+    const int engine = resolve_engine(t, sel, qph);
     if (engine == ZHA_ENGINE_UNION)
         return hip_status(launch_union(a, g.head_dim, g.num_refs, g.dtype, static_cast<int>(n0), st));
     return hip_status(launch_search(a, g.head_dim, g.num_refs, g.dtype, engine, static_cast<int>(n0), st));
@@ -403,6 +406,13 @@ zha_status zha_append(zha_tree *t, const void *k_cache, int64_t n_new, void *str
 uint64_t zha_search_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head) {
     if (check_tree(t) != ZHA_OK || check_select(sel) != ZHA_OK || q_per_head < 1) return 0;
     return search_ws_layout(t, sel, walks_of(&t->geom, q_per_head)).total;
+}
+
+int32_t zha_search_engine(const zha_tree *t, const zha_select *sel, int32_t q_per_head) {
+    if (check_tree(t) != ZHA_OK || check_select(sel) != ZHA_OK || q_per_head < 1) return -1;
+    const int e = resolve_engine(t, sel, q_per_head);
+    if (e == ZHA_ENGINE_UNION && (q_per_head != 1 || t->geom.group_size > 16)) return -1;
+    return e;
 }
 
 uint64_t zha_visited_words(const zha_tree *t) {
