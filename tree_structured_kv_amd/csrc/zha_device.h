@@ -30,6 +30,22 @@ template <> struct Elem<bf16_t> {
     static __device__ __forceinline__ void store(bf16_t *p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
+// Four consecutive elements as floats (one 16- or 8-byte load).
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+    static __device__ __forceinline__ void load(const float *p, float *o) {
+        const float4 v = *reinterpret_cast<const float4 *>(p);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+};
+template <> struct Vec4<bf16_t> {
+    static __device__ __forceinline__ void load(const bf16_t *p, float *o) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(p);
+        o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+        o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+};
+
 // 16 bytes of a row as floats: 4 fp32 or 8 bf16 elements.
 template <typename T> struct Vec16;
 template <> struct Vec16<float> {

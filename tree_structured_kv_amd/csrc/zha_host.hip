@@ -92,11 +92,17 @@ int64_t walks_of(const zha_geometry *g, int32_t qph) {
 }
 
 struct SearchWs {
-    uint64_t cand, score, state, tile_count, tile_map, u_ids, u_mask, u_omask, u_n, u_next, h_score,
-        total;
+    uint64_t cand, score, state, tile_count, tile_map, u_ids, u_omask, u_n, u_next, h_score, u_rank,
+        u_par, u_open, u_flat, u_score, flat_cap, total;
 };
-SearchWs search_ws_layout(const zha_tree *t, const zha_select *sel, int64_t walks) {
+// Workspace of zha_search; the union engine's arrays only where it can run
+// (decode, at most 16 query heads per KV head).
+SearchWs search_ws_layout(const zha_tree *t, const zha_select *sel, int32_t qph) {
     const uint64_t cap = static_cast<uint64_t>(cand_capacity(t, sel));
+    const uint64_t walks = static_cast<uint64_t>(walks_of(&t->geom, qph));
+    const bool uni = qph == 1 && t->geom.group_size <= 16;
+    const uint64_t pairs = uni ? uint64_t(t->geom.batch) * t->geom.num_kv_heads : 0;
+    const uint64_t uw = uni ? walks : 0;
     SearchWs l;
     l.cand = 0;
     l.score = align_up(walks * 2 * cap * sizeof(uint32_t));
@@ -104,13 +110,18 @@ SearchWs search_ws_layout(const zha_tree *t, const zha_select *sel, int64_t walk
     l.tile_count = l.state + align_up(walks * sizeof(WalkState));
     l.tile_map = l.tile_count + align_up((ZHA_MAX_STEPS + 1) * sizeof(int32_t));
     l.u_ids = l.tile_map + align_up(walks * ((cap + kTile - 1) / kTile) * sizeof(int2));
-    const uint64_t pairs = uint64_t(t->geom.batch) * t->geom.num_kv_heads;
-    l.u_mask = l.u_ids + align_up(pairs * 2 * cap * sizeof(uint32_t));
-    l.u_omask = l.u_mask + align_up(pairs * 2 * cap * sizeof(uint32_t));
+    l.u_omask = l.u_ids + align_up(pairs * 2 * cap * sizeof(uint32_t));
     l.u_n = l.u_omask + align_up(pairs * cap * sizeof(uint32_t));
     l.u_next = l.u_n + align_up(pairs * 2 * sizeof(int32_t));
-    l.h_score = l.u_next + align_up(walks * sizeof(int32_t));
-    l.total = l.h_score + align_up(walks * cap * sizeof(float));
+    l.h_score = l.u_next + align_up(uw * sizeof(int32_t));
+    l.u_rank = l.h_score + align_up(uw * cap * sizeof(float));
+    l.u_par = l.u_rank + align_up(pairs * cap * sizeof(int32_t));
+    l.u_open = l.u_par + align_up(pairs * cap * sizeof(uint32_t));
+    l.u_flat = l.u_open + align_up(uw * cap * sizeof(int32_t));
+    l.flat_cap = pairs * (cap + kFlatPad);
+    l.u_score = l.u_flat + align_up(2 * l.flat_cap * 16);
+    const uint64_t gp = (uint64_t(t->geom.group_size) + 3) / 4 * 4;
+    l.total = l.u_score + align_up(pairs * cap * gp * sizeof(float));
     return l;
 }
 
@@ -152,7 +163,7 @@ ForwardWs forward_ws_layout(const zha_tree *t, const zha_select *sel, int32_t qp
     l.sel_blocks = 0;
     l.sel_count = align_up(uint64_t(walks) * sel->max_blocks_per_walk * sizeof(int32_t));
     l.search = l.sel_count + align_up(uint64_t(walks) * sizeof(int32_t));
-    l.attn = l.search + search_ws_layout(t, sel, walks).total;
+    l.attn = l.search + search_ws_layout(t, sel, qph).total;
     l.total = l.attn + attn_ws_bytes(t, sel, qph);
     return l;
 }
@@ -214,7 +225,7 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
                      uint32_t *visited, void *ws, hipStream_t st) {
     const zha_geometry &g = t->geom;
     const int64_t walks = walks_of(&g, qph);
-    SearchWs lay = search_ws_layout(t, sel, walks);
+    SearchWs lay = search_ws_layout(t, sel, qph);
     const char *mem = static_cast<const char *>(t->tree_mem);
     SearchArgs a;
     memset(&a, 0, sizeof(a));
@@ -246,12 +257,16 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
     a.tile_count = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + lay.tile_count);
     a.tile_map = reinterpret_cast<int2 *>(static_cast<char *>(ws) + lay.tile_map);
     a.u_ids = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.u_ids);
-    a.u_mask = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.u_mask);
     a.u_omask = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.u_omask);
     a.u_n = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + lay.u_n);
     a.u_next = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + lay.u_next);
     a.h_score = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.h_score);
-    a.u_score = a.score;
+    a.u_rank = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + lay.u_rank);
+    a.u_par = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.u_par);
+    a.u_open = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + lay.u_open);
+    a.u_flat = reinterpret_cast<int4 *>(static_cast<char *>(ws) + lay.u_flat);
+    a.flat_cap = static_cast<int64_t>(lay.flat_cap);
+    a.u_score = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.u_score);
     a.pairs = g.batch * g.num_kv_heads;
     a.score_grid = 1024;
     a.n_tokens = t->n_tokens;
@@ -405,7 +420,7 @@ zha_status zha_append(zha_tree *t, const void *k_cache, int64_t n_new, void *str
 
 uint64_t zha_search_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head) {
     if (check_tree(t) != ZHA_OK || check_select(sel) != ZHA_OK || q_per_head < 1) return 0;
-    return search_ws_layout(t, sel, walks_of(&t->geom, q_per_head)).total;
+    return search_ws_layout(t, sel, q_per_head).total;
 }
 
 int32_t zha_search_engine(const zha_tree *t, const zha_select *sel, int32_t q_per_head) {

@@ -15,6 +15,7 @@ constexpr uint32_t kIndexMask = (1u << kLevelShift) - 1u;
 constexpr int kBlock = 256;          // threads per workgroup of most kernels
 constexpr int kChunkKeys = 1024;     // keys per attention work item
 constexpr int kTile = 32;            // candidates per tile of the level-synchronous scorer
+constexpr int kFlatPad = 32;         // union engine: each pair's run of scoring entries is padded to this
 
 // Per-walk state of the level-synchronous search engine (workspace).
 struct WalkState {
@@ -64,17 +65,22 @@ struct SearchArgs {
     uint32_t *cand;                        // ws [walks][2][cand_cap]
     float *score;                          // ws [walks][cand_cap]
     WalkState *state;                      // ws [walks]          (level-synchronous)
-    int32_t *tile_count;                   // ws [ZHA_MAX_STEPS+1] (level-synchronous)
+    int32_t *tile_count;                   // ws [ZHA_MAX_STEPS+1] tiles (level-synchronous) or
+                                           // flat entries (union) per step
     int2 *tile_map;                        // ws [walks * ceil(cand_cap / kTile)]
     // union engine: one candidate list per (sequence, KV head) pair, the
     // union over its query heads, with a head mask per node
     uint32_t *u_ids;                       // ws [pairs][2][cand_cap]
-    uint32_t *u_mask;                      // ws [pairs][2][cand_cap]
     uint32_t *u_omask;                     // ws [pairs][cand_cap]  heads that opened the node
     int32_t *u_n;                          // ws [pairs][2]  {list size, current buffer}
-    int32_t *u_next;                       // ws [walks]  next step's candidates per head
-    float *u_score;                        // ws [pairs][group][cand_cap] (aliases `score`)
-    float *h_score;                        // ws [walks][cand_cap]  a head's compacted scores
+    int32_t *u_next;                       // ws [walks]  entries a head opened (levels > 1)
+    float *u_score;                        // ws [pairs][cand_cap][round_up(group, 4)]
+    float *h_score;                        // ws [walks][cand_cap]  a head's gathered scores
+    int32_t *u_rank;                       // ws [pairs][cand_cap]  rank of an opened entry
+    uint32_t *u_par;                       // ws [pairs][cand_cap]  opened entry of each rank
+    int32_t *u_open;                       // ws [walks][cand_cap]  list positions a head opened
+    int4 *u_flat;                          // ws [2][flat_cap]  {pair, position, node id, 0}
+    int64_t flat_cap;                      // entries per flat buffer
     int32_t pairs;
     int64_t n_tokens;
     int32_t walks;

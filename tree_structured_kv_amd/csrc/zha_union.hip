@@ -7,21 +7,26 @@
 // ("How does top-p differ from top-K?") over exactly its own candidates
 // ("Run a small tree yourself").  What the heads of a group share is the
 // tree, so they share the reads: at step t the pair's list holds the union
-// of the heads' candidate sets, each node tagged with the mask of heads it
-// is a candidate for.  Children of an opened node inherit the mask of the
-// heads that opened it, which is exactly the set of heads whose next
-// candidates they are.
+// of the heads' candidate sets (the children of every node any head opened,
+// in list order), and every node of it is scored for all heads at once.
 //
 // Per step:
-//   k_un_score  grid-wide over 32-node tiles of every pair's list: a node
-//               record is read once and scored for all heads of the group
-//               with fp32 16x16x4 matrix-core tiles (heads x (node, ref)),
-//               then s * dot + bias and the max over references;
-//   k_un_cut    one workgroup per walk: the head's exact radix-select cut
-//               over the list entries carrying its bit, its level-1
-//               selections in span order, its bit on the higher nodes it opens;
-//   k_un_expand one workgroup per pair: the next union list (children of the
-//               nodes any head opened, tagged with those heads).
+//   k_un_score  grid-wide over a flat list of (pair, list position, node)
+//               entries: a node record is read once and scored for all
+//               heads of the group with fp32 16x16x4 matrix-core tiles
+//               (heads x (node, ref)), then s * dot + bias and the max over
+//               references;
+//   k_un_cut    one workgroup per walk (head h of pair p): its candidates are
+//               the children of the nodes it opened at the previous step,
+//               found through the parents' ranks in the union list; the
+//               head's exact radix-select cut, its level-1 selections in
+//               span order, the higher nodes it opens (list positions, in
+//               order) and head bit h on them;
+//   k_un_expand one workgroup per pair: ranks of the opened nodes (in list
+//               order), the next union list (their children, written
+//               coalesced) and its flat scoring entries.
+// A head's candidates keep the list order, so selections, statistics and
+// the cut are those of a walk of that head alone.
 #include "zha_device.h"
 #include "zha_internal.h"
 #include "zha_walk.h"
@@ -32,19 +37,22 @@ namespace {
 
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kCutThreads = 1024;     // workgroup of the expand kernel
-constexpr int kCutWaves = kCutThreads / 64;
 constexpr int kScoreThreads = 256;
-constexpr int kUG = 2;                // node groups in flight per wavefront
+constexpr int kUG = 2;                // matrix tiles in flight per wavefront
+constexpr int kLdsCand = 14336;       // candidate scores a cut stages in LDS (56 KB)
+constexpr int kLdsPar = 2048;         // parent ranks a cut stages in LDS (8 KB)
 
 __device__ __forceinline__ int head_walk(const SearchArgs &a, int pair, int h) {
     const int b = pair / a.kv_heads, g = pair % a.kv_heads;
     return b * a.heads + g * a.group + h;
 }
 
+__device__ __forceinline__ int round_flat(int n) { return (n + kFlatPad - 1) / kFlatPad * kFlatPad; }
+
 struct ExpandShared {
-    uint32_t seg_cnt[kCutWaves];
-    int32_t tile_base, tile_n;
+    uint32_t seg_cnt[kWaves];
+    int32_t flat_base;
+    int32_t need;
 };
 
 // Block-wide sum of a uint32 per thread (kThreads threads).
@@ -67,14 +75,9 @@ __global__ __launch_bounds__(512) void k_un_init(SearchArgs a) {
     __syncthreads();
     uint32_t flags = 0;
     uint32_t *ids = a.u_ids + static_cast<int64_t>(p) * 2 * cap;
-    uint32_t *mask = a.u_mask + static_cast<int64_t>(p) * 2 * cap;
     const int n = write_roots(a, ids, flags);
-    const uint32_t all = (a.group >= 32) ? 0xffffffffu : ((1u << a.group) - 1u);
     uint32_t *om = a.u_omask + static_cast<int64_t>(p) * cap;
-    for (int i = tid; i < n; i += blockDim.x) {
-        mask[i] = all;
-        om[i] = 0;
-    }
+    for (int i = tid; i < n; i += blockDim.x) om[i] = 0;
     if (flags) atomicOr(&s_flags, flags);
     __syncthreads();
     if (tid == 0) {
@@ -91,231 +94,337 @@ __global__ __launch_bounds__(512) void k_un_init(SearchArgs a) {
         st->flags = s_flags;
         st->steps = 0;
         for (int i = 0; i < ZHA_MAX_STEPS; ++i) { st->scored[i] = 0; st->opened[i] = 0; }
+        a.u_next[w] = 0;
         if (n == 0) finish_walk<R>(a, w, 0, st->scored, st->opened, 0, 0, s_flags);
     }
 }
 
-// Step t scoring of every pair's union list: a wavefront takes NPG = 16/R
-// nodes at a time (the 16 columns of a matrix-core tile are (node, ref)),
-// the rows are the group's heads.  Matrix step k of lane group q = lane/16
-// multiplies element d = 16*(k/4) + 4*q + k%4 of the query and of the
-// reference row (one permutation of D for both operands), so one 16-byte
-// load of the four lanes of a column reads 64 contiguous bytes of its row.
+// Step t scoring.  The flat list holds, pair after pair, one entry per node
+// of the pair's union list, each pair's run padded to a multiple of
+// kFlatPad (pad entries repeat a real node and store nothing); at t = 0 the
+// entries are the roots, the same count n0 for every pair, and are computed.
+// A wavefront takes NPG = 16/R nodes per matrix tile (the 16 columns are
+// (node, ref), the rows the group's heads), kUG tiles per block, and walks
+// one contiguous run of blocks, fetching the next block's entries while the
+// current block's records load; a block never straddles two pairs.  Matrix
+// step k of lane group q = lane/16 multiplies element d = 16*(k/4) + 4*q +
+// k%4 of the query and of the reference row (one permutation of D for both
+// operands), so one 16-byte load of the four lanes of a column reads 64
+// contiguous bytes of its row.
 template <int D, int R, typename QT>
-__global__ __launch_bounds__(kScoreThreads) void k_un_score(SearchArgs a, int t, int tiles0) {
-    constexpr int NPG = 16 / R;           // nodes per tile
+__global__ __launch_bounds__(kScoreThreads) void k_un_score(SearchArgs a, int t, int n0) {
+    constexpr int NPG = 16 / R;           // nodes per matrix tile
     constexpr int KS = D / 4;             // 16x16x4 steps
     constexpr int kSW = kScoreThreads / 64;
+    constexpr int WB = NPG * kUG;         // nodes per block
+    static_assert(kFlatPad % WB == 0, "a block must not straddle two pairs");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const int n_tiles = (t == 0) ? a.pairs * tiles0 : a.tile_count[t];
+    // per-level bases, looked up per lane (a block may mix levels)
+    __shared__ const float *s_kap[ZHA_MAX_LEVELS + 1];
+    __shared__ const float *s_bet[ZHA_MAX_LEVELS + 1];
+    __shared__ int64_t s_cap[ZHA_MAX_LEVELS + 1];
+    if (threadIdx.x <= ZHA_MAX_LEVELS) {
+        s_kap[threadIdx.x] = a.kap[threadIdx.x];
+        s_bet[threadIdx.x] = a.bet[threadIdx.x];
+        s_cap[threadIdx.x] = a.cap[threadIdx.x];
+    }
+    __syncthreads();
+    const int n0p = round_flat(n0);
+    const int n_flat = (t == 0) ? a.pairs * n0p : a.tile_count[t];
+    const int nb = n_flat / WB;
+    const int nw = gridDim.x * kSW;
+    const int per = (nb + nw - 1) / nw;
+    const int b0 = (blockIdx.x * kSW + wave) * per;
+    const int b1 = min(nb, b0 + per);
+    if (b0 >= b1) return;
     const float s = a.sharpness;
-    // each workgroup takes one contiguous run of tiles, so consecutive tiles
-    // mostly belong to the same pair and keep the query operand
-    const int per = (n_tiles + gridDim.x - 1) / gridDim.x;
-    const int tile0 = blockIdx.x * per;
-    const int tile1 = min(n_tiles, tile0 + per);
-    int cur_pair = -1;
-    float qa[KS];
-    for (int tile = tile0; tile < tile1; ++tile) {
-        int p, start;
+    const int gp = (a.group + 3) & ~3;    // heads per score row (padded)
+    const int4 *flat = a.u_flat + (t & 1) * a.flat_cap;
+
+    // entry of flat position e: {pair, list position (-1: pad), node id}
+    auto entry = [&](int e) -> int4 {
         if (t == 0) {
-            p = tile / tiles0;
-            start = (tile % tiles0) * kTile;
-        } else {
-            const int2 e = a.tile_map[tile];
-            p = e.x;
-            start = e.y;
+            const int p = e / n0p, pos = e - p * n0p;
+            const uint32_t *ids = a.u_ids + static_cast<int64_t>(p) * 2 * a.cand_cap;
+            const uint32_t id = ids[pos < n0 ? pos : n0 - 1];
+            return make_int4(p, pos < n0 ? pos : -1, static_cast<int>(id), 0);
         }
-        const int n_u = a.u_n[2 * p];
-        const int buf = a.u_n[2 * p + 1];
-        const int end = min(n_u, start + kTile);
-        const uint32_t *ids = a.u_ids + (static_cast<int64_t>(p) * 2 + buf) * a.cand_cap;
+        return flat[e];
+    };
+
+    int4 nxt[kUG];
+#pragma unroll
+    for (int u = 0; u < kUG; ++u) nxt[u] = entry(b0 * WB + u * NPG + col / R);
+    int cur_pair = -1;
+    // query operand: fp32 values, or for bf16 queries the raw 16-bit pairs
+    // (half the registers; widened per matrix step)
+    constexpr bool kPacked = sizeof(QT) == 2;
+    float qa[kPacked ? 1 : KS];
+    uint32_t qpk[kPacked ? KS / 2 : 1];
+    auto qval = [&](int k) -> float {
+        if constexpr (kPacked)
+            return __uint_as_float((k & 1) ? (qpk[k >> 1] & 0xffff0000u) : (qpk[k >> 1] << 16));
+        else
+            return qa[k];
+    };
+    for (int b = b0; b < b1; ++b) {
+        int4 ent[kUG];
+#pragma unroll
+        for (int u = 0; u < kUG; ++u) ent[u] = nxt[u];
+        if (b + 1 < b1) {
+#pragma unroll
+            for (int u = 0; u < kUG; ++u) nxt[u] = entry((b + 1) * WB + u * NPG + col / R);
+        }
+        const int p = __builtin_amdgcn_readfirstlane(ent[0].x);
+        float kb[kUG][KS];
+        float bias[kUG];
+#pragma unroll
+        for (int u = 0; u < kUG; ++u) {
+            const uint32_t id = static_cast<uint32_t>(ent[u].z);
+            const int lvl = static_cast<int>(id >> kLevelShift);
+            const int64_t node = static_cast<int64_t>(p) * s_cap[lvl] + (id & kIndexMask);
+            const float *kp = s_kap[lvl] + node * (R * D) + (col % R) * D + 4 * grp;
+#pragma unroll
+            for (int k = 0; k < KS; k += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(kp + 4 * k);
+                kb[u][k] = v.x; kb[u][k + 1] = v.y; kb[u][k + 2] = v.z; kb[u][k + 3] = v.w;
+            }
+            bias[u] = s_bet[lvl][node * R + (col % R)];
+        }
         // query operand: row = head `col` of the pair's group (zero past G)
         if (p != cur_pair) {
             cur_pair = p;
             const bool ok = col < a.group;
             const int w = head_walk(a, p, ok ? col : 0);
             const QT *qp = static_cast<const QT *>(a.q) + static_cast<int64_t>(w) * D + 4 * grp;
+            if constexpr (kPacked) {
 #pragma unroll
-            for (int k = 0; k < KS; ++k) qa[k] = ok ? Elem<QT>::load(qp, 16 * (k / 4) + (k % 4)) : 0.f;
-        }
-        for (int g0 = start + wave * NPG; g0 < end; g0 += kSW * NPG * kUG) {
-            float kb[kUG][KS];
-            float bias[kUG];
-            int node_i[kUG];
-#pragma unroll
-            for (int u = 0; u < kUG; ++u) {
-                const int i = g0 + u * kSW * NPG + col / R;
-                node_i[u] = i;
-                const int ic = i < end ? i : end - 1;
-                const uint32_t id = ids[ic];
-                const int lvl = static_cast<int>(id >> kLevelShift);
-                const int64_t node = static_cast<int64_t>(p) * a.cap[lvl] + (id & kIndexMask);
-                const float *kp = a.kap[lvl] + node * (R * D) + (col % R) * D + 4 * grp;
-#pragma unroll
-                for (int k = 0; k < KS; k += 4) {
-                    const float4 v = *reinterpret_cast<const float4 *>(kp + 4 * k);
-                    kb[u][k] = v.x; kb[u][k + 1] = v.y; kb[u][k + 2] = v.z; kb[u][k + 3] = v.w;
+                for (int j = 0; j < KS / 4; ++j) {
+                    const uint2 v = *reinterpret_cast<const uint2 *>(qp + 16 * j);
+                    qpk[2 * j] = ok ? v.x : 0u;
+                    qpk[2 * j + 1] = ok ? v.y : 0u;
                 }
-                bias[u] = a.bet[lvl][node * R + (col % R)];
+            } else {
+#pragma unroll
+                for (int j = 0; j < KS / 4; ++j) Vec4<QT>::load(qp + 16 * j, qa + 4 * j);
+#pragma unroll
+                for (int k = 0; k < KS; ++k) qa[k] = ok ? qa[k] : 0.f;
             }
+        }
+        // the kUG products interleaved, so consecutive matrix ops are independent
+        float4_t acc[kUG];
 #pragma unroll
-            for (int u = 0; u < kUG; ++u) {
-                float4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < kUG; ++u) acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int k = 0; k < KS; ++k)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[k], kb[u][k], acc, 0, 0, 0);
-                const int i = node_i[u];
+        for (int k = 0; k < KS; ++k)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float v = fmaf(s, acc[e], bias[u]);
-                    v = group_max<R>(v);
-                    if (v != v) v = -INFINITY;
-                    if (v == 0.f) v = 0.f;
-                    const int h = 4 * grp + e;
-                    if ((col % R) == 0 && i < end && h < a.group)
-                        a.u_score[(static_cast<int64_t>(p) * a.group + h) * a.cand_cap + i] = v;
-                }
-                if (a.visited && (col % R) == 0 && grp == 0 && i < end) {
-                    const uint32_t id = ids[i];
-                    const int64_t bitn = a.node_off[id >> kLevelShift] + (id & kIndexMask);
-                    atomicOr(a.visited + p * a.vis_words + (bitn >> 5), 1u << (bitn & 31));
-                }
+            for (int u = 0; u < kUG; ++u)
+                acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(qval(k), kb[u][k], acc[u], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < kUG; ++u) {
+            const int pos = ent[u].y;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float x = fmaf(s, acc[u][e], bias[u]);
+                x = group_max<R>(x);
+                if (x != x) x = -INFINITY;
+                v[e] = (x == 0.f) ? 0.f : x;
+            }
+            // heads 4*grp .. 4*grp+3 of node `pos`: one 16-byte store
+            if ((col % R) == 0 && pos >= 0 && 4 * grp < a.group)
+                *reinterpret_cast<float4 *>(a.u_score + (static_cast<int64_t>(p) * a.cand_cap + pos) * gp + 4 * grp) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            if (a.visited && (col % R) == 0 && grp == 0 && pos >= 0) {
+                const uint32_t id = static_cast<uint32_t>(ent[u].z);
+                const int64_t bitn = a.node_off[id >> kLevelShift] + (id & kIndexMask);
+                atomicOr(a.visited + p * a.vis_words + (bitn >> 5), 1u << (bitn & 31));
             }
         }
     }
 }
 
-// Step t, one workgroup per walk (head h of pair p): the entries of the
-// pair's list that carry bit h are compacted (in list order) into the
-// walk's own (id, score, list index) arrays; the head's exact cut then runs
-// over those alone, its level-1 selections go out in span order, and bit h
-// is set on every higher node it opens.
+// Step t, one workgroup per walk (head h of pair p).  The head's candidates
+// are, in order, the children of the list entries it opened at step t-1 (at
+// t = 0: every root); child e of the entry of rank k among all opened
+// entries sits at list position k*c + e, and those positions increase with
+// the candidate index, so the ones inside a truncated list form a prefix.
+// The parents' ranks are staged in LDS, the candidates' scores too when they
+// fit (every pass of the cut then reads LDS), their ids in the walk's global
+// array.  After the exact cut, level-1 nodes go to the selection in span
+// order, higher nodes are recorded (list positions, in order) for the next
+// step and get head bit h in the pair's open masks.
 template <int R>
-__global__ __launch_bounds__(kThreads) void k_un_cut(SearchArgs a, int t) {
+__device__ __forceinline__ void cut_head(const SearchArgs &a, int t, int w, SelectShared &sh, uint32_t *s_one,
+                                         uint32_t *s_high, float *lds_sc, int32_t *lds_par) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int w = blockIdx.x;
     const int p = w / a.group, h = w % a.group;
     const uint32_t bit = 1u << h;
-    const int cap = a.cand_cap, log2c = a.log2c;
-    __shared__ SelectShared sh;
-    __shared__ uint32_t s_seg[kWaves];
+    const int cap = a.cand_cap, log2c = a.log2c, c = a.chunk;
     const int n_u = a.u_n[2 * p];
     const int buf = a.u_n[2 * p + 1];
-    if (n_u <= 0) return;                          // the pair has finished (uniform)
+    const int n_open_prev = (t == 0) ? 0 : a.u_next[w];
+    if (t > 0 && n_open_prev == 0) return;         // this head opened nothing more
+    WalkState *st = a.state + w;
     const uint32_t *ids = a.u_ids + (static_cast<int64_t>(p) * 2 + buf) * cap;
-    const uint32_t *mask = a.u_mask + (static_cast<int64_t>(p) * 2 + buf) * cap;
-    const float *sc = a.u_score + (static_cast<int64_t>(p) * a.group + h) * cap;
+    const int gp = (a.group + 3) & ~3;
+    const float *sc = a.u_score + static_cast<int64_t>(p) * cap * gp + h;   // score of position i: sc[i * gp]
+    const int32_t *rank = a.u_rank + static_cast<int64_t>(p) * cap;
     uint32_t *om = a.u_omask + static_cast<int64_t>(p) * cap;
-    uint32_t *cid = a.cand + static_cast<int64_t>(w) * 2 * cap;     // this head's candidates
-    uint32_t *cux = cid + cap;                                       // their list positions
-    float *csc = a.h_score + static_cast<int64_t>(w) * cap;         // their scores
+    int32_t *opened_pos = a.u_open + static_cast<int64_t>(w) * cap;
+    uint32_t *cid = a.cand + static_cast<int64_t>(w) * 2 * cap;     // this head's candidate ids
+    uint32_t *cux = cid + cap;                                       // their list positions (fallback)
+    float *csc = a.h_score + static_cast<int64_t>(w) * cap;         // their scores (fallback)
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-    // compaction: wavefront v owns list segment v, 64*kScanU entries a round
-    const int seg = ((n_u + kWaves - 1) / kWaves + 63) / 64 * 64;
-    const int s0 = wave * seg, s1 = min(n_u, s0 + seg);
-    uint32_t mine = 0;
-    for (int b0 = s0; b0 < s1; b0 += 64 * kScanU) {
-        uint32_t mv[kScanU];
+    const int64_t raw64 = (t == 0) ? n_u : static_cast<int64_t>(n_open_prev) * c;
+    const int raw = static_cast<int>(raw64 < cap ? raw64 : cap);
+    const bool par_lds = n_open_prev <= kLdsPar;
+    if (t > 0) {
+        if (par_lds) {
+            for (int j0 = tid; j0 < n_open_prev; j0 += kScanU * kThreads) {
+                int i[kScanU];
 #pragma unroll
-        for (int u = 0; u < kScanU; ++u) {
-            const int i = b0 + 64 * u + lane;
-            mv[u] = i < s1 ? mask[i] : 0u;
-        }
+                for (int u = 0; u < kScanU; ++u) {
+                    const int j = j0 + u * kThreads;
+                    i[u] = j < n_open_prev ? opened_pos[j] : 0;
+                }
 #pragma unroll
-        for (int u = 0; u < kScanU; ++u) mine += __popcll(__ballot((mv[u] & bit) != 0u));
-    }
-    if (lane == 0) s_seg[wave] = mine;
-    __syncthreads();
-    uint32_t before = 0, cnt_u = 0;
-    for (int v = 0; v < kWaves; ++v) {
-        if (v < wave) before += s_seg[v];
-        cnt_u += s_seg[v];
-    }
-    const int cnt = static_cast<int>(cnt_u);
-    const bool forced = step_forced(a, t, cnt);
-    float m = -INFINITY;
-    for (int b0 = s0; b0 < s1; b0 += 64 * kScanU) {
-        uint32_t mv[kScanU];
-#pragma unroll
-        for (int u = 0; u < kScanU; ++u) {
-            const int i = b0 + 64 * u + lane;
-            mv[u] = i < s1 ? mask[i] : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < kScanU; ++u) {
-            const int i = b0 + 64 * u + lane;
-            const bool in = (mv[u] & bit) != 0u;
-            const unsigned long long bal = __ballot(in);
-            if (in) {
-                const uint32_t k = before + __popcll(bal & below);
-                cid[k] = ids[i];
-                cux[k] = static_cast<uint32_t>(i);
-                if (!forced) {
-                    const float v = sc[i];
-                    csc[k] = v;
-                    m = fmaxf(m, v);
+                for (int u = 0; u < kScanU; ++u) {
+                    const int j = j0 + u * kThreads;
+                    if (j < n_open_prev) lds_par[j] = rank[i[u]];
                 }
             }
-            before += __popcll(bal);
+        } else {
+            for (int x0 = tid; x0 < raw; x0 += kScanU * kThreads) {
+                int i[kScanU];
+#pragma unroll
+                for (int u = 0; u < kScanU; ++u) {
+                    const int x = x0 + u * kThreads;
+                    i[u] = x < raw ? opened_pos[x >> log2c] : 0;
+                }
+#pragma unroll
+                for (int u = 0; u < kScanU; ++u) {
+                    const int x = x0 + u * kThreads;
+                    if (x < raw) cux[x] = static_cast<uint32_t>(rank[i[u]] * c + (x & (c - 1)));
+                }
+            }
         }
     }
     __syncthreads();
+    auto position = [&](int x) -> int {
+        if (t == 0) return x;
+        if (par_lds) return lds_par[x >> log2c] * c + (x & (c - 1));
+        return static_cast<int>(cux[x]);
+    };
+    // the candidates inside the list: a prefix of length cnt
+    uint32_t valid = 0;
+    for (int x = tid; x < raw; x += kThreads) valid += position(x) < n_u;
+    const int cnt = static_cast<int>(block_sum_u32(valid, sh));   // also a barrier
     if (cnt == 0) {
         if (tid == 0) a.u_next[w] = 0;
         return;
     }
+    const bool forced = step_forced(a, t, cnt);
+    const bool sc_lds = cnt <= kLdsCand;
+    float *vs = sc_lds ? lds_sc : csc;
+    float m = -INFINITY;
+    for (int x0 = tid; x0 < cnt; x0 += kScanU * kThreads) {
+        uint32_t id[kScanU];
+        float v[kScanU];
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+            const int x = x0 + u * kThreads;
+            const int pos = x < cnt ? position(x) : 0;
+            id[u] = x < cnt ? ids[pos] : 0u;
+            v[u] = (x < cnt && !forced) ? sc[static_cast<int64_t>(pos) * gp] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+            const int x = x0 + u * kThreads;
+            if (x < cnt) {
+                cid[x] = id[u];
+                if (!forced) {
+                    vs[x] = v[u];
+                    m = fmaxf(m, v[u]);
+                }
+            }
+        }
+    }
+    __syncthreads();
     unsigned long long tau = 0;
     if (!forced) {
         const float mx = block_max(m, sh);
-        tau = cut_tau(a, cnt, cid, csc, mx, a.k[t], sh);
+        tau = sc_lds ? cut_tau_win(a, cnt, cid, lds_sc, mx, a.k[t], sh)
+                     : cut_tau_win(a, cnt, cid, csc, mx, a.k[t], sh);
     }
 
-    // open, in list order over the compact arrays
-    const int seg2 = ((cnt + kWaves - 1) / kWaves + 63) / 64 * 64;
-    const int c0 = wave * seg2, c1 = min(cnt, c0 + seg2);
+    // open, in candidate order: wavefront v owns segment v (64*kScanU a round)
+    const int seg = ((cnt + kWaves - 1) / kWaves + 63) / 64 * 64;
+    const int c0 = wave * seg, c1 = min(cnt, c0 + seg);
+    auto opens = [&](int k, uint32_t &id) -> bool {
+        id = cid[k];
+        return forced || rank_key(vs[k], id, log2c) >= tau;
+    };
     uint32_t n1 = 0, nopen = 0, nhigh = 0;
-    for (int base = c0; base < c1; base += 64) {
-        const int k = base + lane;
-        bool open = false;
-        uint32_t id = 0;
-        if (k < c1) {
-            id = cid[k];
-            open = forced || rank_key(csc[k], id, log2c) >= tau;
+    for (int b0 = c0; b0 < c1; b0 += 64 * kScanU) {
+        bool op[kScanU];
+        uint32_t id[kScanU];
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+            const int k = b0 + 64 * u + lane;
+            id[u] = 0;
+            op[u] = k < c1 && opens(k, id[u]);
         }
-        n1 += __popcll(__ballot(open && (id >> kLevelShift) == 1u));
-        nopen += __popcll(__ballot(open));
-        nhigh += __popcll(__ballot(open && (id >> kLevelShift) > 1u));
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+            n1 += __popcll(__ballot(op[u] && (id[u] >> kLevelShift) == 1u));
+            nopen += __popcll(__ballot(op[u]));
+            nhigh += __popcll(__ballot(op[u] && (id[u] >> kLevelShift) > 1u));
+        }
     }
-    if (lane == 0) s_seg[wave] = n1;
-    const uint32_t tot_open = block_sum_u32(lane == 0 ? nopen : 0u, sh);
-    const uint32_t tot_high = block_sum_u32(lane == 0 ? nhigh : 0u, sh);
-    WalkState *st = a.state + w;
+    if (lane == 0) {
+        s_one[wave] = n1;
+        s_high[wave] = nhigh;
+    }
+    const uint32_t tot_open = block_sum_u32(lane == 0 ? nopen : 0u, sh);   // also a barrier
     const int64_t sel0 = st->sel_n;
-    uint32_t pre = 0, tot1 = 0;
+    uint32_t pre1 = 0, tot1 = 0, preh = 0, toth = 0;
     for (int v = 0; v < kWaves; ++v) {
-        if (v < wave) pre += s_seg[v];
-        tot1 += s_seg[v];
+        if (v < wave) { pre1 += s_one[v]; preh += s_high[v]; }
+        tot1 += s_one[v];
+        toth += s_high[v];
     }
     int32_t *selw = a.sel_blocks + static_cast<int64_t>(w) * a.sel_cap;
-    for (int base = c0; base < c1; base += 64) {
-        const int k = base + lane;
-        bool open = false;
-        uint32_t id = 0;
-        if (k < c1) {
-            id = cid[k];
-            open = forced || rank_key(csc[k], id, log2c) >= tau;
+    for (int b0 = c0; b0 < c1; b0 += 64 * kScanU) {
+        bool op[kScanU];
+        uint32_t id[kScanU];
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+            const int k = b0 + 64 * u + lane;
+            id[u] = 0;
+            op[u] = k < c1 && opens(k, id[u]);
         }
-        const bool l1 = open && (id >> kLevelShift) == 1u;
-        const unsigned long long m1 = __ballot(l1);
-        if (l1) {
-            const int64_t pos = sel0 + pre + __popcll(m1 & below);
-            if (pos < a.sel_cap) selw[pos] = static_cast<int32_t>(id & kIndexMask);
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+            const int k = b0 + 64 * u + lane;
+            const bool l1 = op[u] && (id[u] >> kLevelShift) == 1u;
+            const bool hi = op[u] && (id[u] >> kLevelShift) > 1u;
+            const unsigned long long m1 = __ballot(l1);
+            const unsigned long long mh = __ballot(hi);
+            if (l1) {
+                const int64_t pos = sel0 + pre1 + __popcll(m1 & below);
+                if (pos < a.sel_cap) selw[pos] = static_cast<int32_t>(id[u] & kIndexMask);
+            }
+            if (hi) {
+                const int i = position(k);
+                opened_pos[preh + __popcll(mh & below)] = i;
+                atomicOr(&om[i], bit);
+            }
+            pre1 += __popcll(m1);
+            preh += __popcll(mh);
         }
-        if (open && (id >> kLevelShift) > 1u) atomicOr(&om[cux[k]], bit);
-        pre += __popcll(m1);
     }
     if (tid == 0) {
         st->scored[t] = cnt;
@@ -323,86 +432,99 @@ __global__ __launch_bounds__(kThreads) void k_un_cut(SearchArgs a, int t) {
         if (!forced) st->unforced += cnt;
         st->sel_n = static_cast<int32_t>(sel0 + tot1);
         st->steps = t + 1;
-        a.u_next[w] = static_cast<int32_t>(tot_high) * a.chunk;
+        a.u_next[w] = static_cast<int32_t>(toth);
     }
 }
 
-// Step t, one workgroup per pair: the next list holds the children of every
-// node some head opened, in span order, each child tagged with the heads
-// that opened its parent.
+// Step t for pair p, after every head's cut: the list entries any head
+// opened get their rank (in list order) and the next list is their
+// children, rank by rank; when some head's next cut needs scores, the
+// children also go to the flat scoring list of step t+1.  Clears the open
+// masks, and finishes the walks after the last step.
 template <int R>
-__global__ __launch_bounds__(kCutThreads) void k_un_expand(SearchArgs a, int t) {
+__device__ __forceinline__ void expand_pair(const SearchArgs &a, int t, int p, ExpandShared &sh) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int p = blockIdx.x;
-    const int cap = a.cand_cap, c = a.chunk;
-    __shared__ ExpandShared sh;
+    const int cap = a.cand_cap, c = a.chunk, log2c = a.log2c;
     const int n_u = a.u_n[2 * p];
     const int buf = a.u_n[2 * p + 1];
     if (n_u <= 0) return;
     const uint32_t *ids = a.u_ids + (static_cast<int64_t>(p) * 2 + buf) * cap;
     uint32_t *nids = a.u_ids + (static_cast<int64_t>(p) * 2 + (buf ^ 1)) * cap;
-    uint32_t *nmask = a.u_mask + (static_cast<int64_t>(p) * 2 + (buf ^ 1)) * cap;
     uint32_t *om = a.u_omask + static_cast<int64_t>(p) * cap;
+    int32_t *rank = a.u_rank + static_cast<int64_t>(p) * cap;
+    uint32_t *par = a.u_par + static_cast<int64_t>(p) * cap;
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-    const int seg = ((n_u + kCutWaves - 1) / kCutWaves + 63) / 64 * 64;
-    const int s0 = wave * seg, s1 = min(n_u, s0 + seg);
+    // at the last level every candidate is a level-1 node, so nothing was
+    // marked for opening and the open masks are still clear
+    const bool final_step = (t + 1 >= a.levels) || (t + 1 >= ZHA_MAX_STEPS);
+    const int seg = ((n_u + kWaves - 1) / kWaves + 63) / 64 * 64;
+    const int s0 = wave * seg, s1 = final_step ? s0 : min(n_u, s0 + seg);
     uint32_t mine = 0;
-    for (int base = s0; base < s1; base += 64) {
-        const int i = base + lane;
-        mine += __popcll(__ballot(i < s1 && om[i] != 0u));
+    for (int base = s0; base < s1; base += 64 * kScanU) {
+        uint32_t mv[kScanU];
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+            const int i = base + 64 * u + lane;
+            mv[u] = i < s1 ? om[i] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) mine += __popcll(__ballot(mv[u] != 0u));
     }
     if (lane == 0) sh.seg_cnt[wave] = mine;
     __syncthreads();
     uint32_t before = 0, total = 0;
-    for (int v = 0; v < kCutWaves; ++v) {
+    for (int v = 0; v < kWaves; ++v) {
         if (v < wave) before += sh.seg_cnt[v];
         total += sh.seg_cnt[v];
     }
     for (int base = s0; base < s1; base += 64) {
         const int i = base + lane;
-        const uint32_t m = (i < s1) ? om[i] : 0u;
-        const bool emit = m != 0u;
+        const bool emit = i < s1 && om[i] != 0u;
         const unsigned long long bal = __ballot(emit);
         if (emit) {
-            const int64_t k = before + __popcll(bal & below);
-            const uint32_t id = ids[i];
-            const uint32_t lvl = id >> kLevelShift, j = id & kIndexMask;
-            const uint32_t cid = (lvl - 1u) << kLevelShift;
-            for (int e = 0; e < c; ++e) {
-                const int64_t pos = k * c + e;
-                if (pos < cap) {
-                    nids[pos] = cid | (j * static_cast<uint32_t>(c) + e);
-                    nmask[pos] = m;
-                }
-            }
+            const uint32_t k = before + __popcll(bal & below);
+            rank[i] = static_cast<int32_t>(k);
+            par[k] = ids[i];
         }
         before += __popcll(bal);
     }
     int64_t n_next = static_cast<int64_t>(total) * c;
     const bool overflow = n_next > cap;
     if (overflow) n_next = cap;
-    const bool last = (n_next == 0) || (t + 1 >= a.levels) || (t + 1 >= ZHA_MAX_STEPS);
-    __syncthreads();
-    // clear the open masks for the next step
-    const int64_t clear = (n_next > n_u) ? n_next : n_u;
-    for (int64_t i = tid; i < clear; i += kCutThreads) om[i] = 0;
+    const bool last = (n_next == 0) || final_step;
+    if (tid == 0) {
+        bool need = false;
+        for (int hh = 0; hh < a.group && !last; ++hh) {
+            const int64_t nh = static_cast<int64_t>(a.u_next[head_walk(a, p, hh)]) * c;
+            if (nh > 0 && !step_forced(a, t + 1, static_cast<int>(nh < cap ? nh : cap))) need = true;
+        }
+        sh.need = need ? 1 : 0;
+        sh.flat_base = need ? atomicAdd(&a.tile_count[t + 1], round_flat(static_cast<int>(n_next))) : 0;
+    }
+    __syncthreads();                               // par[] and the flat base are ready
+    if (!last) {
+        const bool need = sh.need != 0;
+        const int fbase = sh.flat_base;
+        int4 *flat = a.u_flat + ((t + 1) & 1) * a.flat_cap;
+        const int nn = static_cast<int>(n_next);
+        const int padded = need ? round_flat(nn) : nn;
+        for (int x = tid; x < padded; x += kThreads) {
+            const int xr = x < nn ? x : 0;
+            const uint32_t pid = par[xr >> log2c];
+            const uint32_t lvl = pid >> kLevelShift, j = pid & kIndexMask;
+            const uint32_t child = ((lvl - 1u) << kLevelShift) | (j * static_cast<uint32_t>(c) + (xr & (c - 1)));
+            if (x < nn) nids[x] = child;
+            if (need) flat[fbase + x] = make_int4(p, x < nn ? x : -1, static_cast<int>(child), 0);
+        }
+        // clear the open masks for the next step
+        const int clear = nn > n_u ? nn : n_u;
+        for (int i = tid; i < clear; i += kThreads) om[i] = 0;
+    }
     if (tid == 0) {
         a.u_n[2 * p] = last ? 0 : static_cast<int32_t>(n_next);
         a.u_n[2 * p + 1] = buf ^ 1;
-        bool need_scores = false;
-        for (int hh = 0; hh < a.group && !last; ++hh) {
-            const int nh = a.u_next[p * a.group + hh];
-            if (nh > 0 && !step_forced(a, t + 1, nh)) need_scores = true;
-        }
-        sh.tile_n = 0;
-        if (need_scores) {
-            sh.tile_n = static_cast<int>((n_next + kTile - 1) / kTile);
-            sh.tile_base = atomicAdd(&a.tile_count[t + 1], sh.tile_n);
-        }
     }
-    __syncthreads();
-    for (int k = tid; k < sh.tile_n; k += kCutThreads) a.tile_map[sh.tile_base + k] = make_int2(p, k * kTile);
     if (tid < a.group) {
         const int w = head_walk(a, p, tid);
         WalkState *st = a.state + w;
@@ -411,23 +533,63 @@ __global__ __launch_bounds__(kCutThreads) void k_un_expand(SearchArgs a, int t) 
     }
 }
 
+// Step t, one workgroup per walk: the head's cut (cut_head).
+template <int R>
+__global__ __launch_bounds__(kThreads) void k_un_cut(SearchArgs a, int t) {
+    __shared__ SelectShared sh;
+    __shared__ uint32_t s_one[kWaves], s_high[kWaves];
+    __shared__ float s_sc[kLdsCand];
+    __shared__ int32_t s_par[kLdsPar];
+    const int w = blockIdx.x;
+    if (a.u_n[2 * (w / a.group)] <= 0) return;     // the pair has finished (all its heads)
+    cut_head<R>(a, t, w, sh, s_one, s_high, s_sc, s_par);
+}
+
+// Step t, one workgroup per pair, after every head's cut (a kernel boundary:
+// a device-wide fence inside one kernel costs far more on this GPU, whose
+// L2 caches are per XCD): the pair's next list (expand_pair).
+template <int R>
+__global__ __launch_bounds__(kThreads) void k_un_expand(SearchArgs a, int t) {
+    __shared__ ExpandShared sh;
+    expand_pair<R>(a, t, blockIdx.x, sh);
+}
+
+// Workgroups of the scorer that fit on the device at once (its wavefronts
+// take equal runs of blocks, so all of them should be resident), per device.
+template <typename K>
+static int resident_grid(K kernel, int threads) {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cache[dev] == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+            per_cu <= 0)
+            per_cu = 1;
+        cache[dev] = cus * per_cu;
+    }
+    return cache[dev];
+}
+
 template <int D, int R, typename QT>
 static hipError_t launch_union_t(const SearchArgs &a, int n0, hipStream_t st) {
     hipLaunchKernelGGL((k_un_init<R>), dim3(a.pairs), dim3(512), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int tiles0 = (n0 + kTile - 1) / kTile;
+    const int score_grid = resident_grid(k_un_score<D, R, QT>, kScoreThreads);
     for (int t = 0; t < a.levels && t < ZHA_MAX_STEPS; ++t) {
         const bool skip = (t == 0) && (n0 <= 1 || (a.mode == ZHA_TOPK && a.k[0] >= n0) ||
                                        (a.mode == ZHA_TOPP && a.p >= 1.0f));
         if (!skip) {
-            hipLaunchKernelGGL((k_un_score<D, R, QT>), dim3(a.score_grid), dim3(kScoreThreads), 0, st, a,
-                               t, tiles0 > 0 ? tiles0 : 1);
+            hipLaunchKernelGGL((k_un_score<D, R, QT>), dim3(score_grid), dim3(kScoreThreads), 0, st, a, t,
+                               n0);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         hipLaunchKernelGGL((k_un_cut<R>), dim3(a.pairs * a.group), dim3(kThreads), 0, st, a, t);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((k_un_expand<R>), dim3(a.pairs), dim3(kCutThreads), 0, st, a, t);
+        hipLaunchKernelGGL((k_un_expand<R>), dim3(a.pairs), dim3(kThreads), 0, st, a, t);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

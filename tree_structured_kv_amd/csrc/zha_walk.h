@@ -78,6 +78,9 @@ constexpr int kThreads = 512;          // workgroup of the cut kernels
 constexpr int kWaves = kThreads / 64;
 constexpr int kScanU = 4;              // list entries in flight per thread in a scan
 
+constexpr int kWinPasses = 4;          // value-window passes of the fast cut
+constexpr int kWinFinal = 64;          // candidates ranked one by one at its end
+
 struct SelectShared {
     uint32_t hcnt[256];
     unsigned long long hw[256];
@@ -88,6 +91,12 @@ struct SelectShared {
     uint32_t cnt;
     float red[kWaves];
     uint32_t flags;
+    // fast cut: the last window's candidates (key, weight), then in key order
+    unsigned long long fkey[kWinFinal];
+    unsigned long long fw[kWinFinal];
+    unsigned long long skey[kWinFinal];
+    unsigned long long sw[kWinFinal];
+    uint32_t nf;
 };
 
 // Block-wide exclusive scan of a uint64 per thread (kThreads threads);
@@ -248,6 +257,181 @@ __device__ __forceinline__ unsigned long long cut_tau(const SearchArgs &a, int n
         }
         __syncthreads();
     }
+    return tau;
+}
+
+// Bin of score v in a window of 256 bins counted down from `top` (bin 0
+// holds the highest scores; values below the window fall in bin 255).
+// Monotone: a higher score never lands in a higher bin.
+__device__ __forceinline__ int win_bin(float v, float top, float scale) {
+    float d = (top - v) * scale;
+    d = fminf(fmaxf(d, 0.f), 255.f);
+    return static_cast<int>(d);
+}
+
+// Workgroup (kThreads): the same key as cut_tau, found by narrowing a
+// window of score values instead of key digits.  Each pass bins the
+// candidates still in the window (bin membership of every earlier pass is
+// re-tested exactly, so no float boundary is ever recomputed), takes the
+// bin where the running weight from the top crosses what is still needed,
+// and stops once that bin holds at most kWinFinal candidates; those are then
+// ranked by their full keys.  Weights are the integer masses of cut_tau (or
+// counts), so the crossing is the same candidate.  Scores spread over the
+// bins, so the shared-memory histogram sees little contention.  Falls back
+// to cut_tau when every score is -inf or a window cannot be split (ties).
+__device__ __forceinline__ unsigned long long cut_tau_win(const SearchArgs &a, int n, const uint32_t *cur,
+                                                          const float *sc, float mx, int kt, SelectShared &sh) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int log2c = a.log2c;
+    if (!(mx > -INFINITY)) return cut_tau(a, n, cur, sc, mx, kt, sh);
+    const bool by_mass = (a.mode == ZHA_TOPP) && (a.p > 0.f);
+    // total weight and the lowest finite score
+    unsigned long long zpart = 0;
+    float mn = mx;
+    for (int i0 = tid; i0 < n; i0 += kScanU * kThreads) {
+        float v[kScanU];
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+            const int i = i0 + u * kThreads;
+            v[u] = i < n ? sc[i] : mx;
+        }
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+            if (v[u] > -INFINITY) mn = fminf(mn, v[u]);
+            if (by_mass && i0 + u * kThreads < n)
+                zpart += static_cast<unsigned long long>(__float2uint_rn(expf(v[u] - mx) * kMassScale));
+        }
+    }
+    mn = -wave_max(-mn, 1, 64);
+    if (lane == 0) sh.red[wave] = mn;
+    unsigned long long z;
+    (void)block_exscan64(zpart, sh.scan64, &z);    // barriers: sh.red is complete
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) mn = fminf(mn, sh.red[i]);
+    __syncthreads();
+    unsigned long long need;
+    if (by_mass) {
+        const double tq = ceil(static_cast<double>(a.p) * static_cast<double>(z));
+        need = static_cast<unsigned long long>(tq);
+        if (need < 1) need = 1;
+        if (need > z) need = z;
+    } else {
+        const int m = (a.mode == ZHA_TOPK) ? (kt < n ? kt : n) : 1;
+        need = static_cast<unsigned long long>(m < 1 ? 1 : m);
+    }
+    // scores more than 23 below the top carry integer mass 0 and can never
+    // be the crossing candidate of a mass cut
+    float top = mx, bot = by_mass ? fmaxf(mn, mx - 23.f) : mn;
+    float w_top[kWinPasses], w_scale[kWinPasses];
+    int w_bin[kWinPasses];
+    int depth = 0;
+    bool done = false;
+    for (; depth < kWinPasses; ++depth) {
+        if (!(top > bot)) break;                   // the window is a single value: ties
+        const float scale = 256.f / (top - bot);
+        w_top[depth] = top;
+        w_scale[depth] = scale;
+        for (int i = tid; i < 256; i += kThreads) { sh.hcnt[i] = 0; sh.hw[i] = 0; }
+        __syncthreads();
+        for (int i0 = tid; i0 < n; i0 += kScanU * kThreads) {
+            float v[kScanU];
+#pragma unroll
+            for (int u = 0; u < kScanU; ++u) {
+                const int i = i0 + u * kThreads;
+                v[u] = i < n ? sc[i] : -INFINITY;
+            }
+#pragma unroll
+            for (int u = 0; u < kScanU; ++u) {
+                if (i0 + u * kThreads >= n) continue;
+                bool in = true;
+                for (int q = 0; q < depth; ++q) in = in && win_bin(v[u], w_top[q], w_scale[q]) == w_bin[q];
+                if (!in) continue;
+                const int b = win_bin(v[u], top, scale);
+                unsigned long long wgt = 1;
+                if (by_mass) wgt = static_cast<unsigned long long>(__float2uint_rn(expf(v[u] - mx) * kMassScale));
+                atomicAdd(&sh.hcnt[b], 1u);
+                if (wgt) atomicAdd(&sh.hw[b], wgt);
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane covers bins 4*lane .. 4*lane+3 (ascending = scores descending)
+            unsigned long long lw[4], lsum = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { lw[e] = by_mass ? sh.hw[4 * lane + e] : sh.hcnt[4 * lane + e]; lsum += lw[e]; }
+            unsigned long long incl = lsum;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                unsigned long long o = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += o;
+            }
+            const unsigned long long excl = incl - lsum;
+            const unsigned long long mask = __ballot(incl >= need);
+            const int first = mask ? (__ffsll(static_cast<long long>(mask)) - 1) : 63;
+            if (lane == first) {
+                unsigned long long run = excl;
+                int pick = 3;
+                for (int e = 0; e < 4; ++e) {
+                    if (run + lw[e] >= need) { pick = e; break; }
+                    run += lw[e];
+                }
+                if (!mask) { pick = 3; run = excl + lw[0] + lw[1] + lw[2]; }
+                sh.dig = 4u * lane + pick;
+                sh.above = run;
+                sh.cnt = sh.hcnt[4 * lane + pick];
+            }
+        }
+        __syncthreads();
+        const int b = static_cast<int>(sh.dig);
+        need -= sh.above;
+        w_bin[depth] = b;
+        const uint32_t cb = sh.cnt;
+        __syncthreads();
+        if (cb <= static_cast<uint32_t>(kWinFinal)) { ++depth; done = true; break; }
+        // the next window spans bin b (membership is still decided by the
+        // exact bin tests above; these bounds only spread the next pass)
+        const float nt = top - static_cast<float>(b) / scale;
+        const float nb = top - static_cast<float>(b + 1) / scale;
+        top = fminf(nt, top);
+        bot = fmaxf(nb, bot);
+    }
+    if (!done) return cut_tau(a, n, cur, sc, mx, kt, sh);
+
+    // the final bin's candidates, ranked by key
+    if (tid == 0) sh.nf = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kThreads) {
+        const float v = sc[i];
+        bool in = true;
+        for (int q = 0; q < depth; ++q) in = in && win_bin(v, w_top[q], w_scale[q]) == w_bin[q];
+        if (!in) continue;
+        const uint32_t slot = atomicAdd(&sh.nf, 1u);
+        if (slot < static_cast<uint32_t>(kWinFinal)) {
+            sh.fkey[slot] = rank_key(v, cur[i], log2c);
+            sh.fw[slot] = by_mass ? static_cast<unsigned long long>(__float2uint_rn(expf(v - mx) * kMassScale)) : 1ull;
+        }
+    }
+    __syncthreads();
+    const int nf = static_cast<int>(sh.nf < static_cast<uint32_t>(kWinFinal) ? sh.nf : kWinFinal);
+    if (tid < nf) {
+        const unsigned long long k = sh.fkey[tid];
+        int r = 0;
+        for (int j = 0; j < nf; ++j) r += sh.fkey[j] > k;
+        sh.skey[r] = k;
+        sh.sw[r] = sh.fw[tid];
+    }
+    __syncthreads();
+    if (tid == 0) {
+        unsigned long long run = 0, tau = nf > 0 ? sh.skey[nf - 1] : 0ull;
+        for (int r = 0; r < nf; ++r) {
+            run += sh.sw[r];
+            if (run >= need) { tau = sh.skey[r]; break; }
+        }
+        sh.tau = tau;
+    }
+    __syncthreads();
+    const unsigned long long tau = sh.tau;
+    __syncthreads();
     return tau;
 }
 
