@@ -80,10 +80,21 @@ enum { ZHA_TOPP = 0, ZHA_TOPK = 1 };
  *     every node record is read once and scored for all heads of the group
  *     (fp32 matrix-core tiles), then each head cuts its own candidates.
  *     Decode only (q_per_head = 1), group_size <= 16.
- *   ZHA_ENGINE_AUTO: union for decode with 16 query heads per KV head and at
- *     least 64 walks, else level-synchronous for top-p with at least 64
- *     walks, else persistent. */
-enum { ZHA_ENGINE_AUTO = 0, ZHA_ENGINE_PERSISTENT = 1, ZHA_ENGINE_LEVEL_SYNC = 2, ZHA_ENGINE_UNION = 3 };
+ *   ZHA_ENGINE_BLOCK: for prefill blocks (any q_per_head): the walks are
+ *     grouped by the parent node they opened and each parent's children are
+ *     scored for all of its walks at once (fp32 matrix-core tiles); the root
+ *     list is scored against every walk the same way.  One wavefront cuts
+ *     each walk.
+ *   ZHA_ENGINE_AUTO: block for prefill (q_per_head > 1), else union for
+ *     decode with 16 query heads per KV head and at least 64 walks, else
+ *     level-synchronous for top-p with at least 64 walks, else persistent. */
+enum {
+    ZHA_ENGINE_AUTO = 0,
+    ZHA_ENGINE_PERSISTENT = 1,
+    ZHA_ENGINE_LEVEL_SYNC = 2,
+    ZHA_ENGINE_UNION = 3,
+    ZHA_ENGINE_BLOCK = 4
+};
 
 /* Device status bits. */
 #define ZHA_FLAG_CAND_OVERFLOW 1u  /* a step had more candidates than max_candidates;
@@ -199,7 +210,7 @@ zha_status zha_append(zha_tree *t, const void *k_cache, int64_t n_new, void *str
 /* Workspace bytes of zha_search for q_per_head queries per head. */
 uint64_t zha_search_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head);
 
-/* The engine (ZHA_ENGINE_PERSISTENT, _LEVEL_SYNC or _UNION) zha_search runs
+/* The engine (ZHA_ENGINE_PERSISTENT, _LEVEL_SYNC, _UNION or _BLOCK) zha_search runs
  * for these arguments: sel->engine itself, or what ZHA_ENGINE_AUTO resolves
  * to.  Host only, enqueues nothing.  -1 if the tree or selection is invalid
  * or the engine does not support the shape.  All engines give identical

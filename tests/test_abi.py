@@ -187,15 +187,15 @@ def test_search_engine_resolution(Z):
     topp = Z.make_select("topp", 0.9, max_blocks=64)
     topk = Z.make_select("topk", k=(4,), max_blocks=64)
     assert Z.zha_search_engine(small, topp) == "persistent"
-    assert Z.zha_search_engine(small, topp, 16) == "level-sync"      # 128 walks of a prefill block
-    assert Z.zha_search_engine(small, topk, 16) == "persistent"
-    for e in ("persistent", "level-sync", "union"):
+    assert Z.zha_search_engine(small, topp, 16) == "block"           # 128 walks of a prefill block
+    assert Z.zha_search_engine(small, topk, 16) == "block"
+    for e in ("persistent", "level-sync", "union", "block"):
         s = Z.make_select("topp", 0.9, max_blocks=64, engine=e)
         assert Z.zha_search_engine(small, s) == e
     assert Z.zha_search_engine(small, Z.make_select("topp", 0.9, max_blocks=64, engine="union"), 4) is None
     wide = _handle(Z, batch=4, kv_heads=1, group=16)     # 64 decode walks, 16 heads per KV head
     assert Z.zha_search_engine(wide, topp) == "union"
     assert Z.zha_search_engine(wide, topk) == "union"
-    assert Z.zha_search_engine(wide, topp, 2) == "level-sync"
+    assert Z.zha_search_engine(wide, topp, 2) == "block"
     big = _handle(Z, batch=4, kv_heads=1, group=32)
     assert Z.zha_search_engine(big, Z.make_select("topp", 0.9, max_blocks=64, engine="union")) is None

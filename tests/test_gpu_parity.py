@@ -160,7 +160,7 @@ def _compare(w, K, V, Q, trees, select, bufs, out, min_stable=0.3):
     return stable, walks, worst
 
 
-@pytest.mark.parametrize("engine", ["persistent", "level-sync", "union"])
+@pytest.mark.parametrize("engine", ["persistent", "level-sync", "union", "block"])
 @pytest.mark.parametrize("sname", list(SELECTS))
 @pytest.mark.parametrize("name", CASES)
 def test_search_and_attention(Z, name, sname, engine):
@@ -201,7 +201,7 @@ def test_widget_accounting_on_gpu(Z):
             assert (st["comparisons"], st["keys_read"], st["scored"], st["opened"]) == want
 
 
-@pytest.mark.parametrize("engine", ["persistent", "level-sync", "union"])
+@pytest.mark.parametrize("engine", ["persistent", "level-sync", "union", "block"])
 def test_deterministic(Z, engine):
     w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, "clustered-small")
     select = SELECTS["topp90"]
@@ -218,14 +218,15 @@ def test_deterministic(Z, engine):
     assert torch.equal(o1, o2)
 
 
-def test_union_agrees_on_stable_walks(Z):
-    """The union engine scores with matrix-core tiles (another summation order):
-    its selections equal the persistent engine's wherever the cut gap is not
-    tiny, and its stats count each head's own candidates."""
+@pytest.mark.parametrize("engine", ["union", "block"])
+def test_matrix_engines_agree_on_stable_walks(Z, engine):
+    """The union and block engines score with matrix-core tiles (another
+    summation order): their selections equal the persistent engine's wherever
+    the cut gap is not tiny, and their stats count each walk's own candidates."""
     w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, "mixed-small")
     for select in (SELECTS["topp90"], SELECTS["topk4"]):
         _, b1, o1 = _run(Z, idx, Qt, Kt, Vt, select, engine="persistent")
-        _, b2, o2 = _run(Z, idx, Qt, Kt, Vt, select, engine="union")
+        _, b2, o2 = _run(Z, idx, Qt, Kt, Vt, select, engine=engine)
         c1, c2 = b1["sel_count"].cpu(), b2["sel_count"].cpu()
         same = 0
         for wi in range(c1.numel()):
@@ -257,7 +258,7 @@ def test_engines_agree(Z):
             assert torch.equal(o1, o2)
 
 
-@pytest.mark.parametrize("engine", ["persistent", "level-sync", "union"])
+@pytest.mark.parametrize("engine", ["persistent", "level-sync", "union", "block"])
 def test_overflow_is_flagged_and_deterministic(Z, engine):
     w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, "mixed-small")
     select = SELECTS["topp90"]
@@ -358,7 +359,7 @@ def _prefill_setup(Z):
     return _pcache["p"]
 
 
-@pytest.mark.parametrize("engine", ["persistent", "level-sync"])
+@pytest.mark.parametrize("engine", ["persistent", "level-sync", "block"])
 @pytest.mark.parametrize("sname", ["topp90", "topk4", "open-all"])
 def test_prefill_block(Z, sname, engine):
     """Prefill: every query of the block walks the tree of the tokens before

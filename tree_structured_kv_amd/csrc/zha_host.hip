@@ -83,7 +83,7 @@ zha_status check_select(const zha_select *sel) {
     }
     if (sel->max_blocks_per_walk < 1) return ZHA_ERR_ARG;
     if (sel->max_candidates < 0) return ZHA_ERR_ARG;
-    if (sel->engine < ZHA_ENGINE_AUTO || sel->engine > ZHA_ENGINE_UNION) return ZHA_ERR_ARG;
+    if (sel->engine < ZHA_ENGINE_AUTO || sel->engine > ZHA_ENGINE_BLOCK) return ZHA_ERR_ARG;
     return ZHA_OK;
 }
 
@@ -93,7 +93,8 @@ int64_t walks_of(const zha_geometry *g, int32_t qph) {
 
 struct SearchWs {
     uint64_t cand, score, state, tile_count, tile_map, u_ids, u_omask, u_n, u_next, h_score, u_rank,
-        u_par, u_open, u_flat, u_score, flat_cap, total;
+        u_par, u_open, u_flat, u_score, b_roots, b_cnt, b_fill, b_first, b_inv, b_units, flat_cap, nbins,
+        pcap, total;
 };
 // Workspace of zha_search; the union engine's arrays only where it can run
 // (decode, at most 16 query heads per KV head).
@@ -121,7 +122,19 @@ SearchWs search_ws_layout(const zha_tree *t, const zha_select *sel, int32_t qph)
     l.flat_cap = pairs * (cap + kFlatPad);
     l.u_score = l.u_flat + align_up(2 * l.flat_cap * 16);
     const uint64_t gp = (uint64_t(t->geom.group_size) + 3) / 4 * 4;
-    l.total = l.u_score + align_up(pairs * cap * gp * sizeof(float));
+    // block engine: parents are the nodes of levels >= 2; a walk keeps at
+    // most cap/c + 1 of them per step
+    const uint64_t all_pairs = uint64_t(t->geom.batch) * t->geom.num_kv_heads;
+    l.nbins = 0;
+    for (int lv = 2; lv <= t->geom.levels; ++lv) l.nbins += static_cast<uint64_t>(t->level_cap[lv]);
+    l.pcap = cap / static_cast<uint64_t>(t->geom.chunk) + 1;
+    l.b_roots = l.u_score + align_up(pairs * cap * gp * sizeof(float));
+    l.b_cnt = l.b_roots + align_up(cap * sizeof(uint32_t));
+    l.b_fill = l.b_cnt + align_up(all_pairs * l.nbins * sizeof(int32_t));
+    l.b_first = l.b_fill + align_up(all_pairs * l.nbins * sizeof(int32_t));
+    l.b_inv = l.b_first + align_up(all_pairs * l.nbins * sizeof(int32_t));
+    l.b_units = l.b_inv + align_up(walks * l.pcap * sizeof(int2));
+    l.total = l.b_units + align_up(walks * l.pcap * sizeof(int4));
     return l;
 }
 
@@ -210,11 +223,13 @@ int64_t visited_words_per_pair(const zha_tree *t) {
 }
 
 // The engine a search runs on: the caller's choice, or for AUTO the one
-// that measured fastest for the shape (union when 16 query heads share a KV
-// head in decode, level-synchronous for wide top-p batches, else persistent).
+// that measured fastest for the shape (block for prefill blocks, union when
+// 16 query heads share a KV head in decode, level-synchronous for wide top-p
+// batches, else persistent).
 int resolve_engine(const zha_tree *t, const zha_select *sel, int32_t qph) {
     if (sel->engine != ZHA_ENGINE_AUTO) return sel->engine;
     const int64_t walks = walks_of(&t->geom, qph);
+    if (qph > 1) return ZHA_ENGINE_BLOCK;
     if (qph == 1 && t->geom.group_size == 16 && walks >= 64) return ZHA_ENGINE_UNION;
     if (sel->mode == ZHA_TOPP && walks >= 64) return ZHA_ENGINE_LEVEL_SYNC;
     return ZHA_ENGINE_PERSISTENT;
@@ -267,6 +282,23 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
     a.u_flat = reinterpret_cast<int4 *>(static_cast<char *>(ws) + lay.u_flat);
     a.flat_cap = static_cast<int64_t>(lay.flat_cap);
     a.u_score = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.u_score);
+    a.b_roots = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + lay.b_roots);
+    a.b_cnt = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + lay.b_cnt);
+    a.b_fill = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + lay.b_fill);
+    a.b_first = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + lay.b_first);
+    a.b_inv = reinterpret_cast<int2 *>(static_cast<char *>(ws) + lay.b_inv);
+    a.b_units = reinterpret_cast<int4 *>(static_cast<char *>(ws) + lay.b_units);
+    a.nbins = static_cast<int64_t>(lay.nbins);
+    a.pcap = static_cast<int32_t>(lay.pcap);
+    {
+        int64_t off = 0;
+        for (int l = 0; l <= ZHA_MAX_LEVELS + 1; ++l) a.bin_lvl[l] = 0;
+        for (int l = 2; l <= g.levels; ++l) {
+            a.bin_lvl[l] = off;
+            off += t->level_cap[l];
+        }
+        a.bin_lvl[g.levels + 1] = off;
+    }
     a.pairs = g.batch * g.num_kv_heads;
     a.score_grid = 1024;
     a.n_tokens = t->n_tokens;
@@ -292,8 +324,11 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
     // roots: all level-L nodes plus the parentless nodes of lower levels
     int64_t n0 = a.nl[g.levels];
     for (int l = 1; l < g.levels; ++l) n0 += a.nl[l] - int64_t(g.chunk) * a.nl[l + 1];
+    a.n_roots = n0;
     if (n0 > a.cand_cap) n0 = a.cand_cap;
     const int engine = resolve_engine(t, sel, qph);
+    if (engine == ZHA_ENGINE_BLOCK)
+        return hip_status(launch_block(a, g.head_dim, g.num_refs, g.dtype, static_cast<int>(n0), st));
     if (engine == ZHA_ENGINE_UNION)
         return hip_status(launch_union(a, g.head_dim, g.num_refs, g.dtype, static_cast<int>(n0), st));
     return hip_status(launch_search(a, g.head_dim, g.num_refs, g.dtype, engine, static_cast<int>(n0), st));

@@ -81,6 +81,17 @@ struct SearchArgs {
     int32_t *u_open;                       // ws [walks][cand_cap]  list positions a head opened
     int4 *u_flat;                          // ws [2][flat_cap]  {pair, position, node id, 0}
     int64_t flat_cap;                      // entries per flat buffer
+    // block engine (prefill query blocks): walks grouped by the parent they opened
+    uint32_t *b_roots;                     // ws [cand_cap]  the roots (the same for every pair)
+    int32_t *b_cnt;                        // ws [pairs][nbins]  walks that opened each parent
+    int32_t *b_fill;                       // ws [pairs][nbins]
+    int32_t *b_first;                      // ws [pairs][nbins]  first entry of each parent
+    int2 *b_inv;                           // ws [walks * pcap]  {walk, slot of the parent}
+    int4 *b_units;                         // ws [walks * pcap]  {pair, parent id, first entry, rows}
+    int64_t nbins;                         // parents (nodes of levels >= 2) per pair
+    int64_t bin_lvl[ZHA_MAX_LEVELS + 2];   // first bin of level l within a pair
+    int32_t pcap;                          // parents a walk keeps per step
+    int64_t n_roots;                       // roots before clamping to cand_cap
     int32_t pairs;
     int64_t n_tokens;
     int32_t walks;
@@ -148,6 +159,7 @@ hipError_t launch_level(const LevelArgs &a, int D, int dtype, bool leaf, hipStre
 hipError_t launch_search(const SearchArgs &a, int D, int R, int dtype, int engine, int n0,
                          hipStream_t st);
 hipError_t launch_union(const SearchArgs &a, int D, int R, int dtype, int n0, hipStream_t st);
+hipError_t launch_block(const SearchArgs &a, int D, int R, int dtype, int n0, hipStream_t st);
 hipError_t launch_attn(const AttnArgs &a, int D, int dtype, hipStream_t st);
 hipError_t launch_dense(const DenseArgs &a, int D, int dtype, hipStream_t st);
 hipError_t launch_probe(const void *buf, uint64_t bytes, float *sink, hipStream_t st);

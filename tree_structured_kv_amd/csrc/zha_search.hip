@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void k_search_decode(SearchArgs a) {
             float mx = sh.red[0];
 #pragma unroll
             for (int i = 1; i < kWaves; ++i) mx = fmaxf(mx, sh.red[i]);
-            tau = cut_tau(a, n, cur, sc, mx, a.k[t], sh);
+            tau = cut_tau_win(a, n, cur, sc, mx, a.k[t], sh);
             unforced += n;
         }
         uint32_t ta, tb;
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void k_ls_cut(SearchArgs a, int t) {
         float m = -INFINITY;
         for (int i = tid; i < n; i += kThreads) m = fmaxf(m, sc[i]);
         const float mx = block_max(m, sh);
-        tau = cut_tau(a, n, cur, sc, mx, a.k[t], sh);
+        tau = cut_tau_win(a, n, cur, sc, mx, a.k[t], sh);
     }
     uint32_t ta, tb;
     open_cut(a, n, cur, sc, forced, tau, nxt, selw, st.sel_n, ta, tb, sh);

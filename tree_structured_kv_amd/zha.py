@@ -21,9 +21,9 @@ MAX_STEPS = 8
 TOPP, TOPK = 0, 1
 F32, BF16 = 0, 1
 FLAG_CAND_OVERFLOW, FLAG_SEL_OVERFLOW, FLAG_NONFINITE = 1, 2, 4
-ENGINE_AUTO, ENGINE_PERSISTENT, ENGINE_LEVEL_SYNC, ENGINE_UNION = 0, 1, 2, 3
+ENGINE_AUTO, ENGINE_PERSISTENT, ENGINE_LEVEL_SYNC, ENGINE_UNION, ENGINE_BLOCK = 0, 1, 2, 3, 4
 ENGINES = {"auto": ENGINE_AUTO, "persistent": ENGINE_PERSISTENT, "level-sync": ENGINE_LEVEL_SYNC,
-           "union": ENGINE_UNION}
+           "union": ENGINE_UNION, "block": ENGINE_BLOCK}
 
 STATUS = {0: "ZHA_OK", 1: "ZHA_ERR_ARG", 2: "ZHA_ERR_SHAPE", 3: "ZHA_ERR_ALIGN",
           4: "ZHA_ERR_CAPACITY", 5: "ZHA_ERR_WORKSPACE", 6: "ZHA_ERR_UNSUPPORTED",
