@@ -22,6 +22,9 @@ namespace zha {
 
 namespace {
 
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
 constexpr int kWaves = kBlock / 64;
 
 __device__ __forceinline__ void merge_state(float &m, float &l, float *acc, float m2, float l2,
@@ -44,10 +47,10 @@ __device__ __forceinline__ int64_t walk_entries(const AttnArgs &a, int w) {
 
 // Keys of a walk: the c keys of every listed block plus the raw tail (or
 // the listed tokens), then, for query t of a prefill block, the block's own
-// keys n_tokens .. n_tokens + t.
+// keys n_tokens .. n_tokens + t (unless k_attn_block takes those).
 __device__ __forceinline__ int64_t walk_keys(const AttnArgs &a, int w) {
     const int64_t nb = walk_entries(a, w);
-    const int64_t causal = (a.qph > 1) ? (w % a.qph) + 1 : 0;
+    const int64_t causal = (a.qph > 1 && !a.block_mfma) ? (w % a.qph) + 1 : 0;
     if (a.tokens) return nb + causal;
     return nb * a.chunk + (a.n_tokens - static_cast<int64_t>(a.chunk) * a.n1) + causal;
 }
@@ -68,6 +71,7 @@ __global__ __launch_bounds__(1024) void k_attn_plan(AttnArgs a) {
         if (w < a.walks) {
             const int64_t keys = walk_keys(a, w);
             cnt = static_cast<int32_t>((keys + kChunkKeys - 1) / kChunkKeys);
+            if (a.block_mfma) ++cnt;                 // the last item: the block's own keys
             if (cnt < 1) cnt = 1;
         }
         int32_t incl = cnt;
@@ -108,6 +112,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
     for (int32_t item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int w = a.item_walk[item];
         const int64_t chunk = item - a.item_off[w];
+        if (a.block_mfma && item == a.item_off[w + 1] - 1) continue;   // k_attn_block's item
         const int64_t pair = walk_pair(w, a.qph, a.heads, a.group, a.kv_heads);
         const int64_t nb = walk_entries(a, w);
         const int64_t body = a.tokens ? nb : nb * c;
@@ -196,6 +201,142 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
     }
 }
 
+// Prefill: attention of every query of the block over the block's own keys
+// (query t sees keys 0..t of the block, at positions n_tokens + 0..t), as a
+// partial state in the walk's last work item; k_attn_combine merges it with
+// the tree keys' items.  One workgroup per (pair, head, 64-query tile), one
+// wavefront per 16 queries; key tiles of 64 go through LDS (K row-major, V
+// transposed).  Logits come from bf16 16x16x16 matrix products computed as
+// S^T = K Q^T (rows = keys, columns = queries), so the probabilities already
+// sit in the B-operand layout of the fp32 16x16x4 products O^T += V^T P^T:
+// at step e, lane group g of both operands takes key 4g + e of a 16-key
+// slice.  Online softmax in fp32; P and V enter the second product in fp32.
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
+    constexpr int KT = 64;                 // keys per tile
+    constexpr int KP = D + 8;              // sK row pitch (elements)
+    constexpr int VP = KT + 8;             // sVt row pitch (elements)
+    constexpr int DS = D / 16;             // bf16 product steps (16 elements each)
+    constexpr int DT = D / 16;             // output row tiles of O^T
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int T = a.qph;
+    const int qtiles = (T + 63) / 64;
+    // longest query tiles first (causal work grows with the tile)
+    const int qt = qtiles - 1 - static_cast<int>(blockIdx.x % qtiles);
+    const int hq = static_cast<int>(blockIdx.x / qtiles);      // query head over all pairs
+    const int pair = hq / a.group;
+    __shared__ bf16_t sK[KT * KP];
+    __shared__ bf16_t sVt[D * VP];
+    const bf16_t *kbase = static_cast<const bf16_t *>(a.k) + (static_cast<int64_t>(pair) * a.max_tokens + a.n_tokens) * D;
+    const bf16_t *vbase = static_cast<const bf16_t *>(a.v) + (static_cast<int64_t>(pair) * a.max_tokens + a.n_tokens) * D;
+    const int q0 = qt * 64 + wave * 16;                    // this wavefront's first query
+    const int myq = q0 + col;                              // this lane's query (column)
+    const int64_t walk = static_cast<int64_t>(hq) * T + (myq < T ? myq : T - 1);
+    // B operand of S^T: Q^T, lane (query col, group grp) holds d = 16*k + 4*grp .. +3
+    short4_t qb[DS];
+    {
+        const bf16_t *qp = static_cast<const bf16_t *>(a.q) + walk * D + 4 * grp;
+#pragma unroll
+        for (int k = 0; k < DS; ++k) qb[k] = *reinterpret_cast<const short4_t *>(qp + 16 * k);
+    }
+    const float s = a.sharpness;
+    float m = -INFINITY, l = 0.f;
+    float4_t acc[DT];
+#pragma unroll
+    for (int i = 0; i < DT; ++i) acc[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+    const int last_key = min(T, qt * 64 + 64);             // keys this tile of queries can see
+    for (int k0 = 0; k0 < last_key; k0 += KT) {
+        __syncthreads();
+        // stage keys k0 .. k0+63 (rows past the block are zero)
+        for (int idx = tid; idx < KT * (D / 8); idx += 256) {
+            const int key = idx / (D / 8), d8 = (idx % (D / 8)) * 8;
+            uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = make_uint4(0u, 0u, 0u, 0u);
+            if (k0 + key < T) {
+                kv = *reinterpret_cast<const uint4 *>(kbase + static_cast<int64_t>(k0 + key) * D + d8);
+                vv = *reinterpret_cast<const uint4 *>(vbase + static_cast<int64_t>(k0 + key) * D + d8);
+            }
+            *reinterpret_cast<uint4 *>(sK + key * KP + d8) = kv;
+            const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sVt[(d8 + 2 * i) * VP + key] = static_cast<bf16_t>(vw[i] & 0xffffu);
+                sVt[(d8 + 2 * i + 1) * VP + key] = static_cast<bf16_t>(vw[i] >> 16);
+            }
+        }
+        __syncthreads();
+        if (k0 > q0 + 15) continue;                        // every key of the tile is in this wave's future
+        // S^T for 4 slices of 16 keys: lane holds keys 16*sub + 4*grp + e, query col
+        float p[4][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+            float4_t st = {0.f, 0.f, 0.f, 0.f};
+            const bf16_t *kr = sK + (16 * sub + col) * KP + 4 * grp;
+#pragma unroll
+            for (int k = 0; k < DS; ++k) {
+                const short4_t ka = *reinterpret_cast<const short4_t *>(kr + 16 * k);
+                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, qb[k], st, 0, 0, 0);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int key = k0 + 16 * sub + 4 * grp + e;
+                const float lg = (key <= myq && key < T) ? s * st[e] : -INFINITY;
+                p[sub][e] = lg;
+                tmax = fmaxf(tmax, lg);
+            }
+        }
+        // row (query) max over the 4 lane groups holding this column
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float mn = fmaxf(m, tmax);
+        const float corr = (m > -INFINITY) ? expf(m - mn) : 0.f;
+        float psum = 0.f;
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float pe = (p[sub][e] > -INFINITY) ? expf(p[sub][e] - mn) : 0.f;
+                p[sub][e] = pe;
+                psum += pe;
+            }
+        psum += __shfl_xor(psum, 16, 64);
+        psum += __shfl_xor(psum, 32, 64);
+        l = l * corr + psum;
+        m = mn;
+#pragma unroll
+        for (int i = 0; i < DT; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][e] *= corr;
+        // O^T += V^T P^T
+#pragma unroll
+        for (int i = 0; i < DT; ++i) {
+            const bf16_t *vr = sVt + (16 * i + col) * VP + 4 * grp;
+#pragma unroll
+            for (int sub = 0; sub < 4; ++sub) {
+                const uint2 vw = *reinterpret_cast<const uint2 *>(vr + 16 * sub);
+                const float v0 = __uint_as_float(vw.x << 16), v1 = __uint_as_float(vw.x & 0xffff0000u);
+                const float v2 = __uint_as_float(vw.y << 16), v3 = __uint_as_float(vw.y & 0xffff0000u);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(v0, p[sub][0], acc[i], 0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(v1, p[sub][1], acc[i], 0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(v2, p[sub][2], acc[i], 0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(v3, p[sub][3], acc[i], 0, 0, 0);
+            }
+        }
+    }
+    if (myq >= T) return;
+    // the walk's last item: {m, l, unnormalised sum of p * v}
+    float *part = a.part + static_cast<int64_t>(a.item_off[walk + 1] - 1) * (D + 2);
+#pragma unroll
+    for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part[2 + 16 * i + 4 * grp + e] = acc[i][e];
+    if (grp == 0) {
+        part[0] = m;
+        part[1] = l;
+    }
+}
+
 template <int D, typename KT>
 __global__ __launch_bounds__(D) void k_attn_combine(AttnArgs a) {
     const int w = blockIdx.x, e = threadIdx.x;
@@ -224,6 +365,15 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((k_attn_partial<D, KT>), dim3(static_cast<unsigned>(a.grid)), dim3(kBlock), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if constexpr (sizeof(KT) == 2) {
+        if (a.block_mfma) {
+            const int qtiles = (a.qph + 63) / 64;
+            hipLaunchKernelGGL((k_attn_block<D>), dim3(static_cast<unsigned>(a.walks / a.qph * qtiles)), dim3(256),
+                               0, st, a);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
     hipLaunchKernelGGL((k_attn_combine<D, KT>), dim3(a.walks), dim3(D), 0, st, a);
     return hipGetLastError();
 }

@@ -143,7 +143,7 @@ SearchWs search_ws_layout(const zha_tree *t, const zha_select *sel, int32_t qph)
 int64_t attn_max_items(int64_t keys_bound, int64_t walks) {
     int64_t per = (keys_bound + kChunkKeys - 1) / kChunkKeys;
     if (per < 1) per = 1;
-    return walks * per;
+    return walks * (per + 1);     // + the block-keys item of a prefill walk
 }
 
 int64_t tree_keys_bound(const zha_tree *t, const zha_select *sel, int32_t qph) {
@@ -367,6 +367,7 @@ zha_status do_attn(const zha_tree *t, const void *q, int32_t qph, const void *k_
     a.sel_cap = list_cap;
     const int64_t items = attn_max_items(keys_bound, walks);
     a.grid = static_cast<int32_t>(items < 2048 ? items : 2048);
+    a.block_mfma = (qph > 1 && tokens == nullptr && g.dtype == ZHA_BF16) ? 1 : 0;
     a.sharpness = g.sharpness;
     return hip_status(launch_attn(a, g.head_dim, g.dtype, st));
 }

@@ -134,6 +134,8 @@ struct AttnArgs {
     int32_t chunk;
     int32_t sel_cap;
     int32_t grid;                  // workgroups of the item loop
+    int32_t block_mfma;            // prefill: the block's own keys go to k_attn_block
+                                   // (one extra item per walk, the last one)
     float sharpness;
 };
 
