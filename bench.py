@@ -221,7 +221,7 @@ def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True):
             evs[2].record()
 
     # accounting pass (untimed): the walks of every query rotation
-    per_rot, acct = [], []
+    per_rot, acct, per_level = [], [], []
     vis = idx.visited_bitmap()
     for r in range(ROTATIONS):
         vis.zero_()
@@ -231,9 +231,17 @@ def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True):
         rows = Zm.stats_to_dicts(bufs["stats"].cpu())
         per_rot.append(rows)
         status = int(bufs["status"].cpu()[0])
-        u_sc = int(np.unpackbits(vis.cpu().numpy().view(np.uint8)).sum())
+        vbits = np.unpackbits(vis.cpu().numpy().view(np.uint8), axis=1, bitorder="little")
+        u_sc = int(vbits.sum())
+        lvl_counts = []
+        off = 0
+        for lv in range(1, w.levels + 1):
+            capl = w.n // w.chunk ** lv
+            lvl_counts.append(int(vbits[:, off:off + capl].sum()))
+            off += capl
         u_k = union_keys(w, bufs["sel_blocks"].cpu().numpy(), bufs["sel_count"].cpu().numpy())
         acct.append(walk_bytes(w, rows, u_sc, u_k))
+        per_level.append(lvl_counts)
     for r in range(warmup):
         step(r)
     torch.cuda.synchronize()
@@ -288,6 +296,7 @@ def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True):
         comparisons_per_walk=float(np.mean(comps)),
         keys_read_per_walk=float(np.mean(keys)),
         status=status, dist=dist,
+        union_scored_per_level=[float(x) for x in np.mean(np.array(per_level), axis=0)],
         idx=idx, K=K, V=V, Q=Q, R=R, per_rot=per_rot,
     )
     return res
@@ -473,6 +482,7 @@ def summary(res, bw_ach):
         nodes_scored_per_step=by["scored"], nodes_scored_union_per_step=by["union_scored"],
         keys_per_step=by["keys"], keys_union_per_step=by["union_keys"],
         status=res["status"], per_walk=res["dist"],
+        nodes_scored_union_per_level=res["union_scored_per_level"],
         dense=res["dense"],
         speedup_vs_dense=(res["dense"]["ms_per_step"] / res["ms_per_step"]) if res["dense"] else None,
     )
