@@ -96,14 +96,146 @@ __global__ __launch_bounds__(kBlock) void k_summarize(LevelArgs a) {
     }
 }
 
+// Level 1, one wavefront per node, the chunk's c keys staged once in LDS
+// (fp32) next to the group's R references (one copy per workgroup):
+//   1. lane pair p = r*c + i: sigma = s <K_i, rho_r>; max and sum of
+//      exp(sigma - max) over the c lanes of reference r; w = softmax;
+//   2. lane item (r, 16 elements): key_r = sum_i w_i K_i, written as
+//      coalesced 16-float runs; bias_r = max + log(sum) - s <key_r, rho_r>
+//      summed over the D/16 lanes of r.
+// Every key is read from HBM once; the passes over it run from LDS.
+template <int D, typename KT>
+__global__ __launch_bounds__(kBlock) void k_leaf(LevelArgs a, int waves) {
+    constexpr int P = D + 4;                    // LDS row pitch (floats)
+    constexpr int NS = D / 16;                  // 16-element slices of a row
+    extern __shared__ float lds[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int R = a.refs_n, c = a.chunk;
+    const int pair = blockIdx.y;
+    const int g = pair % a.kv_heads;
+    const float s = a.sharpness;
+    float *rho = lds;                                          // [R][P]
+    const int per_wave = (c * P + c * R + 2 * R + 3) & ~3;     // 16-byte aligned regions
+    float *kk = lds + R * P + wave * per_wave;                 // [c][P]
+    float *wt = kk + c * P;                                    // [R][c]
+    float *mx_s = wt + c * R;                                  // [R]
+    float *z_s = mx_s + R;                                     // [R]
+    const float *refs = a.refs + static_cast<int64_t>(g) * R * D;
+    for (int idx = threadIdx.x; idx < R * (D / 4); idx += blockDim.x) {
+        const int r = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
+        *reinterpret_cast<float4 *>(rho + r * P + d4) = *reinterpret_cast<const float4 *>(refs + r * D + d4);
+    }
+    __syncthreads();
+    const int64_t jn = static_cast<int64_t>(blockIdx.x) * waves + wave;
+    if (wave >= waves || jn >= a.count) return;  // no workgroup barrier below
+    const int64_t j = a.j0 + jn;
+    const KT *keys = static_cast<const KT *>(a.keys) + (static_cast<int64_t>(pair) * a.max_tokens + j * c) * D;
+    float *ok = a.out_k + (static_cast<int64_t>(pair) * a.out_cap + j) * R * D;
+    float *ob = a.out_b + (static_cast<int64_t>(pair) * a.out_cap + j) * R;
+
+    // the chunk's keys, 16 bytes per lane per round
+    constexpr int EV = 16 / static_cast<int>(sizeof(KT));       // elements per 16 bytes
+    for (int idx = lane; idx < c * (D / EV); idx += 64) {
+        const int i = idx / (D / EV), d0 = (idx % (D / EV)) * EV;
+        float v[EV];
+        if constexpr (sizeof(KT) == 2) {
+            Vec16<KT>::load(keys + i * D + d0, v);
+        } else {
+            const float4 x = *reinterpret_cast<const float4 *>(keys + i * D + d0);
+            v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        }
+#pragma unroll
+        for (int e = 0; e < EV; e += 4)
+            *reinterpret_cast<float4 *>(kk + i * P + d0 + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // 1. scores and softmax weights, one (r, i) pair per lane and round
+    for (int p0 = 0; p0 < c * R; p0 += 64) {
+        const int pi = p0 + lane;
+        const bool live = pi < c * R;
+        const int r = live ? pi / c : 0, i = live ? pi % c : 0;
+        const float *kr = kk + i * P;
+        const float *qr = rho + r * P;
+        float d = 0.f;
+#pragma unroll 8
+        for (int e = 0; e < D; e += 4) {
+            const float4 x = *reinterpret_cast<const float4 *>(kr + e);
+            const float4 y = *reinterpret_cast<const float4 *>(qr + e);
+            d = fmaf(x.x, y.x, d);
+            d = fmaf(x.y, y.y, d);
+            d = fmaf(x.z, y.z, d);
+            d = fmaf(x.w, y.w, d);
+        }
+        const float sg = live ? s * d : -INFINITY;
+        float m = sg;
+        for (int off = 1; off < c; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        const float ex = live ? expf(sg - m) : 0.f;
+        float z = ex;
+        for (int off = 1; off < c; off <<= 1) z += __shfl_xor(z, off, 64);
+        if (live) {
+            wt[r * c + i] = ex / z;
+            if (i == 0) { mx_s[r] = m; z_s[r] = z; }
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // 2. keys and biases, one (r, 16-element slice) per lane and round
+    for (int t0 = 0; t0 < R * NS; t0 += 64) {
+        const int ti = t0 + lane;
+        const bool live = ti < R * NS;
+        const int r = live ? ti / NS : 0, d0 = live ? (ti % NS) * 16 : 0;
+        float acc[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+        for (int i = 0; i < c; ++i) {
+            const float w = wt[r * c + i];
+            const float *kr = kk + i * P + d0;
+#pragma unroll
+            for (int e = 0; e < 16; e += 4) {
+                const float4 x = *reinterpret_cast<const float4 *>(kr + e);
+                acc[e] = fmaf(w, x.x, acc[e]);
+                acc[e + 1] = fmaf(w, x.y, acc[e + 1]);
+                acc[e + 2] = fmaf(w, x.z, acc[e + 2]);
+                acc[e + 3] = fmaf(w, x.w, acc[e + 3]);
+            }
+        }
+        float part = 0.f;
+        const float *qr = rho + r * P + d0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) part = fmaf(acc[e], qr[e], part);
+        for (int off = 1; off < NS; off <<= 1) part += __shfl_xor(part, off, 64);
+        if (live) {
+#pragma unroll
+            for (int e = 0; e < 16; e += 4)
+                *reinterpret_cast<float4 *>(ok + r * D + d0 + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+            if (d0 == 0) ob[r] = (mx_s[r] + logf(z_s[r])) - s * part;
+        }
+    }
+}
+
+// Workgroup shape of k_leaf: as many node wavefronts as fit in 64 KB of LDS.
+static int leaf_waves(const LevelArgs &a, int D, size_t &lds_bytes) {
+    const int P = D + 4;
+    const size_t per_wave = (static_cast<size_t>(a.chunk) * P + static_cast<size_t>(a.chunk) * a.refs_n +
+                             2 * static_cast<size_t>(a.refs_n) + 3) / 4 * 4;
+    const size_t fixed = static_cast<size_t>(a.refs_n) * P;
+    int waves = kBlock / 64;
+    while (waves > 1 && (fixed + waves * per_wave) * sizeof(float) > 65536) --waves;
+    lds_bytes = (fixed + waves * per_wave) * sizeof(float);
+    return waves;
+}
+
 template <int D, typename KT>
 static hipError_t launch_level_t(const LevelArgs &a, bool leaf, hipStream_t st) {
+    if (leaf) {
+        size_t lds = 0;
+        const int waves = leaf_waves(a, D, lds);
+        dim3 grid(static_cast<unsigned>((a.count + waves - 1) / waves), static_cast<unsigned>(a.pairs));
+        hipLaunchKernelGGL((k_leaf<D, KT>), grid, dim3(kBlock), lds, st, a, waves);
+        return hipGetLastError();
+    }
     dim3 grid(static_cast<unsigned>((a.count + (kBlock / 64) - 1) / (kBlock / 64)),
               static_cast<unsigned>(a.pairs));
-    if (leaf)
-        hipLaunchKernelGGL((k_summarize<D, KT, true>), grid, dim3(kBlock), 0, st, a);
-    else
-        hipLaunchKernelGGL((k_summarize<D, KT, false>), grid, dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL((k_summarize<D, KT, false>), grid, dim3(kBlock), 0, st, a);
     return hipGetLastError();
 }
 
