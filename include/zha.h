@@ -119,7 +119,13 @@ typedef struct {
     int32_t dtype;           /* zha_dtype of K, V, Q and out                  */
     int64_t max_tokens;      /* cache capacity per (sequence, KV head)        */
     float sharpness;
-    int32_t reserved;
+    int32_t summary_dtype;   /* zha_dtype of the stored node keys: ZHA_F32
+                                (default), or ZHA_BF16 -- each key rounded to
+                                bf16 (nearest, ties to even) after it is
+                                computed in fp32, and its bias computed from
+                                the rounded key, so a node's score at its own
+                                reference query is still the subtree's
+                                log-sum-exp.  Biases are always fp32.        */
 } zha_geometry;
 
 /* How a walk opens nodes at each step ([ZHA lesson] "How does top-p differ
@@ -173,7 +179,8 @@ typedef struct {
 /* ---- sizing and set-up (host only, no device work) -------------------- */
 
 /* Bytes of tree memory for `g`: for every level l = 1..levels, keys
- * float32 [batch][kv_heads][floor(max_tokens/chunk^l)][num_refs][head_dim]
+ * (summary_dtype: float32 or bf16)
+ * [batch][kv_heads][floor(max_tokens/chunk^l)][num_refs][head_dim]
  * then biases float32 [batch][kv_heads][floor(max_tokens/chunk^l)][num_refs],
  * each array 256-byte aligned.  Returns 0 if `g` is invalid. */
 uint64_t zha_tree_bytes(const zha_geometry *g);

@@ -62,14 +62,16 @@ def lib():
         i32p = ctypes.POINTER(ctypes.c_int32)
         L.ora_level_nodes.restype = ctypes.c_int64
         L.ora_level_nodes.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+        L.ora_round_bf16.restype = ctypes.c_double
+        L.ora_round_bf16.argtypes = [ctypes.c_double]
         L.ora_summarize.restype = None
         L.ora_summarize.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
-                                    dp, dp, dp, dp, dp]
+                                    dp, dp, dp, dp, dp, ctypes.c_int]
         L.ora_node_score.restype = ctypes.c_double
         L.ora_node_score.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, dp, dp, dp]
         L.ora_build.restype = None
         L.ora_build.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                ctypes.c_int, ctypes.c_double, dp, dp, dp, dp]
+                                ctypes.c_int, ctypes.c_double, dp, dp, dp, dp, ctypes.c_int]
         L.ora_walk.restype = ctypes.c_int
         L.ora_walk.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                ctypes.c_int, ctypes.c_double, dp, dp, dp, ctypes.c_int,
@@ -119,13 +121,18 @@ class Tree:
         return self.offsets[l + 1] - self.offsets[l]
 
 
-def summarize(child_k, child_b, refs, s: float):
+def round_bf16(x: float) -> float:
+    """x rounded to the nearest bfloat16 value, ties to even (``ora_round_bf16``)."""
+    return float(lib().ora_round_bf16(float(x)))
+
+
+def summarize(child_k, child_b, refs, s: float, key_bf16: bool = False):
     """One node from children [c][R][d] / [c][R] (see ``ora_summarize``)."""
     ck, cb, rf = _f64(child_k), _f64(child_b), _f64(refs)
     c, R, d = ck.shape
     nk = np.zeros((R, d))
     nb = np.zeros(R)
-    lib().ora_summarize(c, R, d, float(s), _dp(ck), _dp(cb), _dp(rf), _dp(nk), _dp(nb))
+    lib().ora_summarize(c, R, d, float(s), _dp(ck), _dp(cb), _dp(rf), _dp(nk), _dp(nb), int(key_bf16))
     return nk, nb
 
 
@@ -135,7 +142,7 @@ def node_score(node_k, node_b, q, s: float) -> float:
     return float(lib().ora_node_score(R, d, float(s), _dp(nk), _dp(nb), _dp(qq)))
 
 
-def build(keys, refs, c: int, L: int, s: float) -> Tree:
+def build(keys, refs, c: int, L: int, s: float, key_bf16: bool = False) -> Tree:
     keys, refs = _f64(keys), _f64(refs)
     n, d = keys.shape
     R = refs.shape[0]
@@ -145,7 +152,7 @@ def build(keys, refs, c: int, L: int, s: float) -> Tree:
     total = offs[L + 1]
     tk = np.zeros((max(total, 1), R, d))
     tb = np.zeros((max(total, 1), R))
-    lib().ora_build(n, d, c, R, L, float(s), _dp(keys), _dp(refs), _dp(tk), _dp(tb))
+    lib().ora_build(n, d, c, R, L, float(s), _dp(keys), _dp(refs), _dp(tk), _dp(tb), int(key_bf16))
     return Tree(n, d, c, R, L, float(s), tk[:total], tb[:total], offs)
 
 

@@ -35,15 +35,30 @@ static double dot(int d, const double *a, const double *b)
     return acc;
 }
 
+double ora_round_bf16(double x)
+{
+    /* bfloat16 keeps 8 significant bits: scale the significand to [128, 256),
+     * round to the nearest integer (ties to even: the default rounding mode
+     * of nearbyint) and scale back. */
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    double m = frexp(x, &e);            /* x = m * 2^e, 0.5 <= |m| < 1 */
+    return ldexp(nearbyint(ldexp(m, 8)), e - 8);
+}
+
 void ora_summarize(int c, int R, int d, double s,
                    const double *child_k, const double *child_b,
-                   const double *refs, double *node_k, double *node_b)
+                   const double *refs, double *node_k, double *node_b,
+                   int key_bf16)
 {
     /* [ZHA lesson] "What does a node summarize?": for each reference query
      * rho_r, score every child tangent as s<key, rho_r> + bias, take the
      * softmax of those scores as weights, the new key is the weighted sum of
      * the child keys, and the new bias is the log-sum-exp of the scores minus
-     * s<new key, rho_r>.  The softmax and log-sum-exp are max-shifted. */
+     * s<new key, rho_r>.  The softmax and log-sum-exp are max-shifted.
+     * With key_bf16 the key is stored rounded to bfloat16 and the bias is
+     * taken against the stored key, so the score at rho_r stays the
+     * log-sum-exp. */
     double *sig = (double *)malloc(sizeof(double) * (size_t)c);
     for (int r = 0; r < R; ++r) {
         const double *rho = refs + (size_t)r * d;
@@ -62,6 +77,8 @@ void ora_summarize(int c, int R, int d, double s,
             const double *k = child_k + ((size_t)i * R + r) * d;
             for (int e = 0; e < d; ++e) out[e] += w * k[e];
         }
+        if (key_bf16)
+            for (int e = 0; e < d; ++e) out[e] = ora_round_bf16(out[e]);
         double lse = mx + log(z);
         node_b[r] = lse - s * dot(d, out, rho);
     }
@@ -83,7 +100,7 @@ double ora_node_score(int R, int d, double s, const double *node_k,
 
 void ora_build(int64_t n, int d, int c, int R, int L, double s,
                const double *keys, const double *refs,
-               double *tree_k, double *tree_b)
+               double *tree_k, double *tree_b, int key_bf16)
 {
     /* [ZHA lesson] "How is the tree built?" and "Run a small tree yourself":
      * level 1 summarises each whole chunk of c neighbouring keys, a leaf
@@ -112,7 +129,7 @@ void ora_build(int64_t n, int d, int c, int R, int L, double s,
             }
             ora_summarize(c, R, d, s, ck, cb, refs,
                           tree_k + (size_t)(off + j) * R * d,
-                          tree_b + (size_t)(off + j) * R);
+                          tree_b + (size_t)(off + j) * R, key_bf16);
         }
         off_prev = off;
         off += nl;

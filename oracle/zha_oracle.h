@@ -42,13 +42,20 @@ typedef struct {
 /* Number of nodes at level l (1..L) for n tokens: floor(n / c^l). */
 int64_t ora_level_nodes(int64_t n, int c, int l);
 
-/* One node from its c children, each holding R (key, bias) tangents. */
+/* x rounded to the nearest bfloat16 value (8 significant bits), ties to
+ * even. */
+double ora_round_bf16(double x);
+
+/* One node from its c children, each holding R (key, bias) tangents.  With
+ * key_bf16 != 0 the node's keys are stored rounded to bfloat16 and its
+ * biases are computed from the rounded keys. */
 void ora_summarize(int c, int R, int d, double s,
                    const double *child_k,   /* [c][R][d] */
                    const double *child_b,   /* [c][R]    */
                    const double *refs,      /* [R][d]    */
                    double *node_k,          /* [R][d]    */
-                   double *node_b);         /* [R]       */
+                   double *node_b,          /* [R]       */
+                   int key_bf16);
 
 /* Node score for a query: max over r of s<key_r, q> + bias_r. */
 double ora_node_score(int R, int d, double s, const double *node_k,
@@ -60,7 +67,8 @@ double ora_node_score(int R, int d, double s, const double *node_k,
 void ora_build(int64_t n, int d, int c, int R, int L, double s,
                const double *keys,   /* [n][d] */
                const double *refs,   /* [R][d] */
-               double *tree_k, double *tree_b);
+               double *tree_k, double *tree_b,
+               int key_bf16);        /* node keys stored as bfloat16 */
 
 /* One walk for one query.  sel receives the selected token indices in
  * ascending order (capacity n).  Returns 0 on success, -1 on bad input. */

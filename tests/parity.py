@@ -53,9 +53,15 @@ def make_inputs(w: S.Workload, pairs=None, unstructured=False):
     return K, V, Q, R
 
 
-def oracle_tree(w: S.Workload, K, R, b, g, n):
+def oracle_tree(w: S.Workload, K, R, b, g, n, key_bf16=False):
     return O.build(K[b, g, :n].astype(np.float64), R[g].astype(np.float64), w.chunk, w.levels,
-                   w.sharpness)
+                   w.sharpness, key_bf16=key_bf16)
+
+
+def bf16_ulp(x):
+    """Spacing of bfloat16 values at |x| (8 significant bits)."""
+    ax = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)
+    return np.ldexp(1.0, np.floor(np.log2(ax)).astype(np.int64) - 7)
 
 
 def oracle_walk(tree, q, select):

@@ -41,9 +41,9 @@ CASES = ["demo", "demo-unstructured", "ar1-small", "clustered-small", "mixed-sma
 _cache = {}
 
 
-def _setup(Z, name):
-    if name in _cache:
-        return _cache[name]
+def _setup(Z, name, summary="f32"):
+    if (name, summary) in _cache:
+        return _cache[(name, summary)]
     w, variant = _case(name)
     K, V, Q, R = P.make_inputs(w, unstructured=(variant == "unstructured"))
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -52,12 +52,13 @@ def _setup(Z, name):
     Vt = torch.from_numpy(V).to(dev).to(dt).contiguous()
     Qt = torch.from_numpy(Q).to(dev).to(dt).contiguous()
     geom = Z.make_geometry(w.batch, w.kv_heads, w.group, w.d, w.chunk, w.refs, w.levels, w.dtype,
-                           w.n, w.sharpness)
+                           w.n, w.sharpness, summary=summary)
     idx = Z.Index(geom, torch.from_numpy(R))
     idx.build(Kt, w.n)
-    trees = {(b, g): P.oracle_tree(w, K, R, b, g, w.n) for b in range(w.batch) for g in range(w.kv_heads)}
-    _cache[name] = (w, K, V, Q, R, Kt, Vt, Qt, idx, trees)
-    return _cache[name]
+    trees = {(b, g): P.oracle_tree(w, K, R, b, g, w.n, key_bf16=(summary == "bf16"))
+             for b in range(w.batch) for g in range(w.kv_heads)}
+    _cache[(name, summary)] = (w, K, V, Q, R, Kt, Vt, Qt, idx, trees)
+    return _cache[(name, summary)]
 
 
 @pytest.mark.parametrize("name", CASES)
@@ -79,6 +80,55 @@ def test_tree_records(Z, name):
             eb = np.max(np.abs(nb - ob), axis=1) / np.maximum(1.0, np.max(np.abs(ob), axis=1))
             worst = max(worst, float(ek.max()), float(eb.max()))
     assert worst <= P.TOL_TREE, worst
+
+
+@pytest.mark.parametrize("name", ["demo", "ar1-small", "clustered-small", "mixed-small"])
+def test_tree_records_bf16_summaries(Z, name):
+    """bf16 node keys: each stored key is the bf16 rounding of its summary, so
+    it equals the oracle's (fp64 summary, rounded) or differs by one bf16
+    step where the fp32 and fp64 summaries straddle a rounding boundary, or
+    by the fp32 bar (2e-5 of the row's largest key) where the summary
+    cancels to a tiny value.  Above level 1 a parent also inherits its
+    children's one-step differences (a convex combination of them: at most
+    one bf16 step of the row's largest key).  The bias follows the stored
+    key (tolerance: the key differences' share of s<key, rho> plus the fp32
+    bar).  Nearly every key must match exactly."""
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, name, "bf16")
+    torch.cuda.synchronize()
+    n_keys = n_exact = 0
+    for l in range(1, w.levels + 1):
+        gk, gb = idx.level(l)
+        assert gk.dtype == torch.bfloat16
+        gk = gk.float().cpu().numpy().astype(np.float64)
+        gb = gb.cpu().numpy().astype(np.float64)
+        for (b, g), tr in trees.items():
+            ok, ob = tr.level(l)
+            if ok.shape[0] == 0:
+                continue
+            nk = gk[b, g, : ok.shape[0]]
+            nb = gb[b, g, : ok.shape[0]]
+            rowmax = np.max(np.abs(ok), axis=2, keepdims=True)
+            ulp = P.bf16_ulp(ok) + P.TOL_TREE * np.maximum(1.0, rowmax)
+            if l > 1:
+                ulp = ulp + P.bf16_ulp(rowmax)
+            assert np.all(np.abs(nk - ok) <= ulp), l
+            n_keys += nk.size
+            n_exact += int(np.sum(nk == ok))
+            rho = R[g].astype(np.float64)                               # [R][d]
+            slack = w.sharpness * np.sum(ulp * np.abs(rho)[None], axis=2)  # [nodes][R]
+            tol = P.TOL_TREE * np.maximum(1.0, np.abs(ob)) + slack
+            assert np.all(np.abs(nb - ob) <= tol), l
+    assert n_exact >= 0.999 * n_keys, (n_exact, n_keys)
+
+
+@pytest.mark.parametrize("engine", ["level-sync", "union", "block"])
+@pytest.mark.parametrize("sname", ["topp90", "topk4"])
+@pytest.mark.parametrize("name", ["clustered-small", "mixed-small"])
+def test_search_and_attention_bf16_summaries(Z, name, sname, engine):
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, name, "bf16")
+    select = SELECTS[sname]
+    sel, bufs, out = _run(Z, idx, Qt, Kt, Vt, select, engine=engine)
+    _compare(w, K, V, Q, trees, select, bufs, out, min_stable=0.3)
 
 
 @pytest.mark.parametrize("name", ["demo", "ar1-small", "mixed-small"])

@@ -371,3 +371,44 @@ def test_prefix_property(oracle_mod):
         a, b = part.level(l)
         A, B = full.level(l)
         assert np.array_equal(a, A[: a.shape[0]]) and np.array_equal(b, B[: b.shape[0]])
+
+
+# P-bf16 -- bf16 node keys (a storage variant of "What does a node
+# summarize?"): the rounding is round-to-nearest-even to 8 significant bits,
+# checked on hand-computed ties and against torch's float32 -> bfloat16
+# conversion; every stored key is a bf16 value within half a bf16 step of the
+# fp64 summary; and because each bias is taken against the stored key, the
+# node's tangent for rho_r is still exact at rho_r.
+def test_round_bf16_definition(oracle_mod):
+    O = oracle_mod
+    cases = {1.0: 1.0, 1 + 2 ** -8: 1.0, 1 + 3 * 2 ** -8: 1 + 2 ** -6, 1 + 2 ** -8 + 2 ** -20: 1 + 2 ** -7,
+             -2.5: -2.5, 3.14159: 3.140625, 0.0: 0.0, 255.5: 256.0, 2 ** -100 * 1.00390625: 2 ** -100}
+    for x, want in cases.items():
+        assert O.round_bf16(x) == want, (x, O.round_bf16(x), want)
+    import torch
+    rng = np.random.default_rng(7)
+    xs = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    ref = torch.from_numpy(xs).to(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([O.round_bf16(float(x)) for x in xs])
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_keys_tangent_exact_at_reference(oracle_mod):
+    O = oracle_mod
+    rng = np.random.default_rng(3)
+    n, d, c, R, L, s = 256, 16, 4, 3, 3, 0.7
+    K = rng.standard_normal((n, d))
+    refs = rng.standard_normal((R, d))
+    tr = O.build(K, refs, c, L, s, key_bf16=True)
+    exact = O.build(K, refs, c, L, s)
+    for l in range(1, L + 1):
+        kl, bl = tr.level(l)
+        for j, (a, z) in enumerate(_spans(tr, l)):
+            for r in range(R):
+                assert all(O.round_bf16(x) == x for x in kl[j, r])
+                tangent = s * kl[j, r] @ refs[r] + bl[j, r]
+                true = logsumexp(s * K[a:z] @ refs[r])
+                assert abs(tangent - true) <= 1e-12 * max(1.0, abs(true))
+    k1, _ = tr.level(1)
+    e1, _ = exact.level(1)
+    assert np.all(np.abs(k1 - e1) <= np.ldexp(1.0, np.floor(np.log2(np.abs(e1) + 1e-300)).astype(int) - 8))

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kBkThreads) void k_bk_init(SearchArgs a, int n0) {
 // once and runs every row tile of the unit against them.  Matrix step k of
 // lane group q = lane/16 multiplies element d = 16*(k/4) + 4*q + k%4 of the
 // query and of the reference row.
-template <int D, int R, typename QT>
+template <int D, int R, typename QT, typename ST>
 __global__ __launch_bounds__(kBkThreads) void k_bk_score(SearchArgs a, int t, int n0) {
     constexpr int NPG = 16 / R;
     constexpr int KS = D / 4;
@@ -176,12 +176,11 @@ __global__ __launch_bounds__(kBkThreads) void k_bk_score(SearchArgs a, int t, in
             const uint32_t id = (t == 0) ? a.b_roots[ci] : child_id(parent, ci, c);
             const int lvl = static_cast<int>(id >> kLevelShift);
             const int64_t node = static_cast<int64_t>(pair) * s_cap[lvl] + (id & kIndexMask);
-            const float *kp = s_kap[lvl] + node * (R * D) + (col % R) * D + 4 * grp;
+            const ST *kp = reinterpret_cast<const ST *>(s_kap[lvl]) + node * (R * D) + (col % R) * D + 4 * grp;
             float kb[KS];
 #pragma unroll
             for (int k = 0; k < KS; k += 4) {
-                const float4 v = *reinterpret_cast<const float4 *>(kp + 4 * k);
-                kb[k] = v.x; kb[k + 1] = v.y; kb[k + 2] = v.z; kb[k + 3] = v.w;
+                Vec4<ST>::load(kp + 4 * k, &kb[k]);
             }
             const float bias = s_bet[lvl][node * R + (col % R)];
             if (mark && (col % R) == 0 && grp == 0 && ct * NPG + col / R < nchild) {
@@ -555,7 +554,7 @@ __global__ __launch_bounds__(64) void k_bk_fill(SearchArgs a) {
     }
 }
 
-template <int D, int R, typename QT>
+template <int D, int R, typename QT, typename ST>
 static hipError_t launch_block_t(const SearchArgs &a, int n0, hipStream_t st) {
     const int init_grid = (a.walks + kBkThreads - 1) / kBkThreads;
     hipLaunchKernelGGL((k_bk_init<R>), dim3(init_grid > 0 ? init_grid : 1), dim3(kBkThreads), 0, st, a, n0);
@@ -565,7 +564,7 @@ static hipError_t launch_block_t(const SearchArgs &a, int n0, hipStream_t st) {
     const bool skip0 = n0 <= 1 || (a.mode == ZHA_TOPK && a.k[0] >= n0) || (a.mode == ZHA_TOPP && a.p >= 1.0f);
     for (int t = 0; t < a.levels && t < ZHA_MAX_STEPS; ++t) {
         if (t > 0 || !skip0) {
-            hipLaunchKernelGGL((k_bk_score<D, R, QT>), dim3(score_grid), dim3(kBkThreads), 0, st, a, t, n0);
+            hipLaunchKernelGGL((k_bk_score<D, R, QT, ST>), dim3(score_grid), dim3(kBkThreads), 0, st, a, t, n0);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         hipLaunchKernelGGL((k_bk_cut<R>), dim3(a.walks), dim3(64), 0, st, a, t);
@@ -580,25 +579,30 @@ static hipError_t launch_block_t(const SearchArgs &a, int n0, hipStream_t st) {
     return hipSuccess;
 }
 
-template <int D, typename QT>
+template <int D, typename QT, typename ST>
 static hipError_t launch_block_d(const SearchArgs &a, int R, int n0, hipStream_t st) {
     switch (R) {
-        case 1: return launch_block_t<D, 1, QT>(a, n0, st);
-        case 2: return launch_block_t<D, 2, QT>(a, n0, st);
-        case 4: return launch_block_t<D, 4, QT>(a, n0, st);
-        case 8: return launch_block_t<D, 8, QT>(a, n0, st);
-        case 16: return launch_block_t<D, 16, QT>(a, n0, st);
+        case 1: return launch_block_t<D, 1, QT, ST>(a, n0, st);
+        case 2: return launch_block_t<D, 2, QT, ST>(a, n0, st);
+        case 4: return launch_block_t<D, 4, QT, ST>(a, n0, st);
+        case 8: return launch_block_t<D, 8, QT, ST>(a, n0, st);
+        case 16: return launch_block_t<D, 16, QT, ST>(a, n0, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_block(const SearchArgs &a, int D, int R, int dtype, int n0, hipStream_t st) {
+template <int D, typename QT>
+static hipError_t launch_block_s(const SearchArgs &a, int R, int sdtype, int n0, hipStream_t st) {
+    return sdtype == ZHA_BF16 ? launch_block_d<D, QT, bf16_t>(a, R, n0, st) : launch_block_d<D, QT, float>(a, R, n0, st);
+}
+
+hipError_t launch_block(const SearchArgs &a, int D, int R, int dtype, int sdtype, int n0, hipStream_t st) {
     if (a.walks <= 0) return hipSuccess;
     if (D == 64)
-        return dtype == ZHA_BF16 ? launch_block_d<64, bf16_t>(a, R, n0, st)
-                                 : launch_block_d<64, float>(a, R, n0, st);
-    return dtype == ZHA_BF16 ? launch_block_d<128, bf16_t>(a, R, n0, st)
-                             : launch_block_d<128, float>(a, R, n0, st);
+        return dtype == ZHA_BF16 ? launch_block_s<64, bf16_t>(a, R, sdtype, n0, st)
+                                 : launch_block_s<64, float>(a, R, sdtype, n0, st);
+    return dtype == ZHA_BF16 ? launch_block_s<128, bf16_t>(a, R, sdtype, n0, st)
+                             : launch_block_s<128, float>(a, R, sdtype, n0, st);
 }
 
 }  // namespace zha

@@ -20,7 +20,7 @@
 
 namespace zha {
 
-template <int D, typename KT, bool LEAF>
+template <int D, typename KT, bool LEAF, typename ST>
 __global__ __launch_bounds__(kBlock) void k_summarize(LevelArgs a) {
     constexpr int EPL = D / 64;                 // elements per lane
     const int lane = threadIdx.x & 63;
@@ -38,9 +38,9 @@ __global__ __launch_bounds__(kBlock) void k_summarize(LevelArgs a) {
     float *sig = sig_lds[wave];
 
     const KT *keys = static_cast<const KT *>(a.keys) + static_cast<int64_t>(pair) * a.max_tokens * D;
-    const float *ck = a.child_k + static_cast<int64_t>(pair) * a.child_cap * R * D;
+    const ST *ck = static_cast<const ST *>(a.child_k) + static_cast<int64_t>(pair) * a.child_cap * R * D;
     const float *cb = a.child_b + static_cast<int64_t>(pair) * a.child_cap * R;
-    float *ok = a.out_k + (static_cast<int64_t>(pair) * a.out_cap + j) * R * D;
+    ST *ok = static_cast<ST *>(a.out_k) + (static_cast<int64_t>(pair) * a.out_cap + j) * R * D;
     float *ob = a.out_b + (static_cast<int64_t>(pair) * a.out_cap + j) * R;
     const float *refs = a.refs + static_cast<int64_t>(g) * R * D;
 
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kBlock) void k_summarize(LevelArgs a) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
                 float x = LEAF ? Elem<KT>::load(keys, child * D + lane * EPL + e)
-                               : ck[(child * R + r) * D + lane * EPL + e];
+                               : Elem<ST>::load(ck, (child * R + r) * D + lane * EPL + e);
                 part = fmaf(x, rho[e], part);
             }
             float dotv = wave_sum(part, 64);
@@ -80,15 +80,17 @@ __global__ __launch_bounds__(kBlock) void k_summarize(LevelArgs a) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
                 float x = LEAF ? Elem<KT>::load(keys, child * D + lane * EPL + e)
-                               : ck[(child * R + r) * D + lane * EPL + e];
+                               : Elem<ST>::load(ck, (child * R + r) * D + lane * EPL + e);
                 acc[e] = fmaf(w, x, acc[e]);
             }
         }
         float part = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-            ok[r * D + lane * EPL + e] = acc[e];
-            part = fmaf(acc[e], rho[e], part);
+            Elem<ST>::store(ok, r * D + lane * EPL + e, acc[e]);
+            // the bias uses the key as stored (bf16: rounded)
+            const float kept = (sizeof(ST) == 2) ? bf16_to_f32(f32_to_bf16(acc[e])) : acc[e];
+            part = fmaf(kept, rho[e], part);
         }
         const float kr = wave_sum(part, 64);
         if (lane == 0) ob[r] = (mx + logf(z)) - s * kr;
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(kBlock) void k_summarize(LevelArgs a) {
 //      coalesced 16-float runs; bias_r = max + log(sum) - s <key_r, rho_r>
 //      summed over the D/16 lanes of r.
 // Every key is read from HBM once; the passes over it run from LDS.
-template <int D, typename KT>
+template <int D, typename KT, typename ST>
 __global__ __launch_bounds__(kBlock) void k_leaf(LevelArgs a, int waves) {
     constexpr int P = D + 4;                    // LDS row pitch (floats)
     constexpr int NS = D / 16;                  // 16-element slices of a row
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(kBlock) void k_leaf(LevelArgs a, int waves) {
     if (wave >= waves || jn >= a.count) return;  // no workgroup barrier below
     const int64_t j = a.j0 + jn;
     const KT *keys = static_cast<const KT *>(a.keys) + (static_cast<int64_t>(pair) * a.max_tokens + j * c) * D;
-    float *ok = a.out_k + (static_cast<int64_t>(pair) * a.out_cap + j) * R * D;
+    ST *ok = static_cast<ST *>(a.out_k) + (static_cast<int64_t>(pair) * a.out_cap + j) * R * D;
     float *ob = a.out_b + (static_cast<int64_t>(pair) * a.out_cap + j) * R;
 
     // the chunk's keys, 16 bytes per lane per round
@@ -198,15 +200,31 @@ __global__ __launch_bounds__(kBlock) void k_leaf(LevelArgs a, int waves) {
                 acc[e + 3] = fmaf(w, x.w, acc[e + 3]);
             }
         }
+        if constexpr (sizeof(ST) == 2) {
+            // the stored key is the bf16 rounding; the bias uses it
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[e] = bf16_to_f32(f32_to_bf16(acc[e]));
+        }
         float part = 0.f;
         const float *qr = rho + r * P + d0;
 #pragma unroll
         for (int e = 0; e < 16; ++e) part = fmaf(acc[e], qr[e], part);
         for (int off = 1; off < NS; off <<= 1) part += __shfl_xor(part, off, 64);
         if (live) {
+            if constexpr (sizeof(ST) == 2) {
+                uint32_t wv[8];
 #pragma unroll
-            for (int e = 0; e < 16; e += 4)
-                *reinterpret_cast<float4 *>(ok + r * D + d0 + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+                for (int e = 0; e < 8; ++e)
+                    wv[e] = static_cast<uint32_t>(f32_to_bf16(acc[2 * e])) |
+                            (static_cast<uint32_t>(f32_to_bf16(acc[2 * e + 1])) << 16);
+                *reinterpret_cast<uint4 *>(ok + r * D + d0) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                *reinterpret_cast<uint4 *>(ok + r * D + d0 + 8) = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; e += 4)
+                    *reinterpret_cast<float4 *>(ok + r * D + d0 + e) =
+                        make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+            }
             if (d0 == 0) ob[r] = (mx_s[r] + logf(z_s[r])) - s * part;
         }
     }
@@ -224,28 +242,33 @@ static int leaf_waves(const LevelArgs &a, int D, size_t &lds_bytes) {
     return waves;
 }
 
-template <int D, typename KT>
+template <int D, typename KT, typename ST>
 static hipError_t launch_level_t(const LevelArgs &a, bool leaf, hipStream_t st) {
     if (leaf) {
         size_t lds = 0;
         const int waves = leaf_waves(a, D, lds);
         dim3 grid(static_cast<unsigned>((a.count + waves - 1) / waves), static_cast<unsigned>(a.pairs));
-        hipLaunchKernelGGL((k_leaf<D, KT>), grid, dim3(kBlock), lds, st, a, waves);
+        hipLaunchKernelGGL((k_leaf<D, KT, ST>), grid, dim3(kBlock), lds, st, a, waves);
         return hipGetLastError();
     }
     dim3 grid(static_cast<unsigned>((a.count + (kBlock / 64) - 1) / (kBlock / 64)),
               static_cast<unsigned>(a.pairs));
-    hipLaunchKernelGGL((k_summarize<D, KT, false>), grid, dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL((k_summarize<D, KT, false, ST>), grid, dim3(kBlock), 0, st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_level(const LevelArgs &a, int D, int dtype, bool leaf, hipStream_t st) {
+template <int D, typename KT>
+static hipError_t launch_level_s(const LevelArgs &a, int sdtype, bool leaf, hipStream_t st) {
+    return sdtype == ZHA_BF16 ? launch_level_t<D, KT, bf16_t>(a, leaf, st) : launch_level_t<D, KT, float>(a, leaf, st);
+}
+
+hipError_t launch_level(const LevelArgs &a, int D, int dtype, int sdtype, bool leaf, hipStream_t st) {
     if (a.count <= 0) return hipSuccess;
     if (D == 64)
-        return dtype == ZHA_BF16 ? launch_level_t<64, bf16_t>(a, leaf, st)
-                                 : launch_level_t<64, float>(a, leaf, st);
-    return dtype == ZHA_BF16 ? launch_level_t<128, bf16_t>(a, leaf, st)
-                             : launch_level_t<128, float>(a, leaf, st);
+        return dtype == ZHA_BF16 ? launch_level_s<64, bf16_t>(a, sdtype, leaf, st)
+                                 : launch_level_s<64, float>(a, sdtype, leaf, st);
+    return dtype == ZHA_BF16 ? launch_level_s<128, bf16_t>(a, sdtype, leaf, st)
+                             : launch_level_s<128, float>(a, sdtype, leaf, st);
 }
 
 }  // namespace zha

@@ -30,6 +30,9 @@ int64_t level_count(int64_t n, int c, int l) {
     return n;
 }
 
+// Bytes of one stored node-key element.
+uint64_t summary_bytes(const zha_geometry *g) { return g->summary_dtype == ZHA_BF16 ? 2 : 4; }
+
 zha_status check_geometry(const zha_geometry *g) {
     if (!g) return ZHA_ERR_ARG;
     if (g->batch < 1 || g->num_kv_heads < 1 || g->group_size < 1) return ZHA_ERR_ARG;
@@ -40,6 +43,7 @@ zha_status check_geometry(const zha_geometry *g) {
         return ZHA_ERR_UNSUPPORTED;
     if (g->levels < 1 || g->levels > ZHA_MAX_LEVELS) return ZHA_ERR_UNSUPPORTED;
     if (g->dtype != ZHA_F32 && g->dtype != ZHA_BF16) return ZHA_ERR_UNSUPPORTED;
+    if (g->summary_dtype != ZHA_F32 && g->summary_dtype != ZHA_BF16) return ZHA_ERR_UNSUPPORTED;
     if (g->max_tokens < 1 || g->max_tokens >= (int64_t(1) << 31)) return ZHA_ERR_ARG;
     if (g->max_tokens / g->chunk >= (int64_t(1) << kLevelShift)) return ZHA_ERR_UNSUPPORTED;
     if (!isfinite(g->sharpness)) return ZHA_ERR_ARG;
@@ -194,11 +198,11 @@ zha_status run_levels(zha_tree *t, const void *k_cache, int64_t n_old, int64_t n
         memset(&la, 0, sizeof(la));
         la.keys = k_cache;
         if (l > 1) {
-            la.child_k = reinterpret_cast<const float *>(mem + t->key_off[l - 1]);
+            la.child_k = mem + t->key_off[l - 1];
             la.child_b = reinterpret_cast<const float *>(mem + t->bias_off[l - 1]);
             la.child_cap = t->level_cap[l - 1];
         }
-        la.out_k = reinterpret_cast<float *>(mem + t->key_off[l]);
+        la.out_k = mem + t->key_off[l];
         la.out_b = reinterpret_cast<float *>(mem + t->bias_off[l]);
         la.refs = t->refs;
         la.max_tokens = g.max_tokens;
@@ -210,7 +214,7 @@ zha_status run_levels(zha_tree *t, const void *k_cache, int64_t n_old, int64_t n
         la.chunk = g.chunk;
         la.refs_n = g.num_refs;
         la.sharpness = g.sharpness;
-        hipError_t e = launch_level(la, g.head_dim, g.dtype, l == 1, st);
+        hipError_t e = launch_level(la, g.head_dim, g.dtype, g.summary_dtype, l == 1, st);
         if (e != hipSuccess) return ZHA_ERR_HIP;
     }
     return ZHA_OK;
@@ -328,10 +332,10 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
     if (n0 > a.cand_cap) n0 = a.cand_cap;
     const int engine = resolve_engine(t, sel, qph);
     if (engine == ZHA_ENGINE_BLOCK)
-        return hip_status(launch_block(a, g.head_dim, g.num_refs, g.dtype, static_cast<int>(n0), st));
+        return hip_status(launch_block(a, g.head_dim, g.num_refs, g.dtype, g.summary_dtype, static_cast<int>(n0), st));
     if (engine == ZHA_ENGINE_UNION)
-        return hip_status(launch_union(a, g.head_dim, g.num_refs, g.dtype, static_cast<int>(n0), st));
-    return hip_status(launch_search(a, g.head_dim, g.num_refs, g.dtype, engine, static_cast<int>(n0), st));
+        return hip_status(launch_union(a, g.head_dim, g.num_refs, g.dtype, g.summary_dtype, static_cast<int>(n0), st));
+    return hip_status(launch_search(a, g.head_dim, g.num_refs, g.dtype, g.summary_dtype, engine, static_cast<int>(n0), st));
 }
 
 // Attention over block lists (tokens == nullptr) or token lists.
@@ -397,7 +401,7 @@ uint64_t zha_tree_bytes(const zha_geometry *g) {
     uint64_t off = 0;
     for (int l = 1; l <= g->levels; ++l) {
         const uint64_t cap = static_cast<uint64_t>(level_count(g->max_tokens, g->chunk, l));
-        off += align_up(pairs * cap * g->num_refs * g->head_dim * sizeof(float));
+        off += align_up(pairs * cap * g->num_refs * g->head_dim * summary_bytes(g));
         off += align_up(pairs * cap * g->num_refs * sizeof(float));
     }
     return off;
@@ -424,7 +428,7 @@ zha_status zha_tree_init(zha_tree *t, const zha_geometry *g, void *tree_mem, uin
         const int64_t cap = level_count(g->max_tokens, g->chunk, l);
         t->level_cap[l] = cap;
         t->key_off[l] = off;
-        off += align_up(pairs * uint64_t(cap) * g->num_refs * g->head_dim * sizeof(float));
+        off += align_up(pairs * uint64_t(cap) * g->num_refs * g->head_dim * summary_bytes(g));
         t->bias_off[l] = off;
         off += align_up(pairs * uint64_t(cap) * g->num_refs * sizeof(float));
     }

@@ -32,9 +32,9 @@ struct WalkState {
 // One level of summaries for a node range, every (sequence, KV head) pair.
 struct LevelArgs {
     const void *keys;          // level 1: K cache (pair stride max_tokens * D elements)
-    const float *child_k;      // level >= 2: keys of level l-1   (pair stride child_cap*R*D)
+    const void *child_k;       // level >= 2: keys of level l-1   (pair stride child_cap*R*D)
     const float *child_b;      // level >= 2: biases of level l-1 (pair stride child_cap*R)
-    float *out_k;              // level l keys   (pair stride out_cap*R*D)
+    void *out_k;               // level l keys   (pair stride out_cap*R*D; fp32 or bf16)
     float *out_b;              // level l biases (pair stride out_cap*R)
     const float *refs;         // [kv_heads][R][D]
     int64_t max_tokens;
@@ -50,7 +50,7 @@ struct LevelArgs {
 };
 
 struct SearchArgs {
-    const float *kap[ZHA_MAX_LEVELS + 1];  // level-l keys, pair 0
+    const float *kap[ZHA_MAX_LEVELS + 1];  // level-l keys, pair 0 (bf16 data when the summaries are bf16)
     const float *bet[ZHA_MAX_LEVELS + 1];  // level-l biases, pair 0
     int64_t cap[ZHA_MAX_LEVELS + 1];       // nodes per pair at level l (stride)
     int64_t nl[ZHA_MAX_LEVELS + 2];        // live nodes at level l; nl[L+1] = 0
@@ -157,11 +157,11 @@ struct DenseArgs {
     float sharpness;
 };
 
-hipError_t launch_level(const LevelArgs &a, int D, int dtype, bool leaf, hipStream_t st);
-hipError_t launch_search(const SearchArgs &a, int D, int R, int dtype, int engine, int n0,
+hipError_t launch_level(const LevelArgs &a, int D, int dtype, int sdtype, bool leaf, hipStream_t st);
+hipError_t launch_search(const SearchArgs &a, int D, int R, int dtype, int sdtype, int engine, int n0,
                          hipStream_t st);
-hipError_t launch_union(const SearchArgs &a, int D, int R, int dtype, int n0, hipStream_t st);
-hipError_t launch_block(const SearchArgs &a, int D, int R, int dtype, int n0, hipStream_t st);
+hipError_t launch_union(const SearchArgs &a, int D, int R, int dtype, int sdtype, int n0, hipStream_t st);
+hipError_t launch_block(const SearchArgs &a, int D, int R, int dtype, int sdtype, int n0, hipStream_t st);
 hipError_t launch_attn(const AttnArgs &a, int D, int dtype, hipStream_t st);
 hipError_t launch_dense(const DenseArgs &a, int D, int dtype, hipStream_t st);
 hipError_t launch_probe(const void *buf, uint64_t bytes, float *sink, hipStream_t st);

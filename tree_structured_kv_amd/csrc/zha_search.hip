@@ -56,7 +56,7 @@ __device__ __forceinline__ void load_q(const SearchArgs &a, int w, float (&qv)[4
 
 // One wavefront scores candidates first, first + stride, ... below `end`, kU
 // at a time, and writes sc[i]; returns the largest score it wrote.
-template <int D, int R>
+template <int D, int R, typename ST>
 __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair, const float (&qv)[4],
                                             const uint32_t *cur, float *sc, int first, int end,
                                             int stride, uint32_t &flags) {
@@ -83,13 +83,15 @@ __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair, c
             const uint32_t id = ids[u];
             const int lvl = static_cast<int>(id >> kLevelShift);
             const int64_t node = pair * a.cap[lvl] + static_cast<int64_t>(id & kIndexMask);
-            const float *kp = a.kap[lvl] + node * (R * D);
+            const ST *kp = reinterpret_cast<const ST *>(a.kap[lvl]) + node * (R * D);
             const float *bp = a.bet[lvl] + node * R;
 #pragma unroll
             for (int l = 0; l < NL; ++l) {
                 const int r = l * RPL + rsub;
                 if (r < R) {
-                    kv[u][l] = *reinterpret_cast<const float4 *>(kp + r * D + 4 * sub);
+                    float t4[4];
+                    Vec4<ST>::load(kp + r * D + 4 * sub, t4);
+                    kv[u][l] = make_float4(t4[0], t4[1], t4[2], t4[3]);
                     bv[u][l] = bp[r];
                 } else {
                     kv[u][l] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -185,7 +187,7 @@ __device__ void open_cut(const SearchArgs &a, int n, const uint32_t *cur, const 
 
 // ---- persistent engine --------------------------------------------------------
 
-template <int D, int R, typename QT>
+template <int D, int R, typename QT, typename ST>
 __global__ __launch_bounds__(kThreads) void k_search_decode(SearchArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int w = xcd_remap(blockIdx.x, gridDim.x);
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void k_search_decode(SearchArgs a) {
         const bool forced = step_forced(a, t, n);
         unsigned long long tau = 0;
         if (!forced) {
-            float wmax = score_wave<D, R>(a, pair, qv, cur, sc, wave * kU, n, kWaves * kU, flags);
+            float wmax = score_wave<D, R, ST>(a, pair, qv, cur, sc, wave * kU, n, kWaves * kU, flags);
             if (lane == 0) sh.red[wave] = wmax;
             __syncthreads();
             float mx = sh.red[0];
@@ -276,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void k_ls_init(SearchArgs a) {
 // Step t scoring over a flat tile list: at step 0 every walk has the same
 // roots, so its tiles are laid out arithmetically; later steps use the tiles
 // the cut kernel of the step before registered.
-template <int D, int R, typename QT>
+template <int D, int R, typename QT, typename ST>
 __global__ __launch_bounds__(kScoreThreads) void k_ls_score(SearchArgs a, int t, int tiles0) {
     constexpr int kSW = kScoreThreads / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -301,7 +303,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_ls_score(SearchArgs a, int t,
         float qv[4];
         load_q<D, QT>(a, w, qv);
         uint32_t flags = 0;
-        (void)score_wave<D, R>(a, pair, qv, cur, sc, start + wave * kU, end, kSW * kU, flags);
+        (void)score_wave<D, R, ST>(a, pair, qv, cur, sc, start + wave * kU, end, kSW * kU, flags);
         if (flags && lane == 0) atomicOr(a.status, flags);
     }
 }
@@ -365,10 +367,10 @@ __global__ __launch_bounds__(kThreads) void k_ls_cut(SearchArgs a, int t) {
 
 // ---- launchers ---------------------------------------------------------------------
 
-template <int D, int R, typename QT>
+template <int D, int R, typename QT, typename ST>
 static hipError_t launch_t(const SearchArgs &a, int engine, int n0, hipStream_t st) {
     if (engine != ZHA_ENGINE_LEVEL_SYNC) {
-        hipLaunchKernelGGL((k_search_decode<D, R, QT>), dim3(a.walks), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((k_search_decode<D, R, QT, ST>), dim3(a.walks), dim3(kThreads), 0, st, a);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((k_ls_init<R>), dim3(a.walks), dim3(kThreads), 0, st, a);
@@ -380,7 +382,7 @@ static hipError_t launch_t(const SearchArgs &a, int engine, int n0, hipStream_t 
         const bool skip = (t == 0) && (n0 <= 1 || (a.mode == ZHA_TOPK && a.k[0] >= n0) ||
                                        (a.mode == ZHA_TOPP && a.p >= 1.0f));
         if (!skip) {
-            hipLaunchKernelGGL((k_ls_score<D, R, QT>), dim3(a.score_grid), dim3(kScoreThreads), 0, st,
+            hipLaunchKernelGGL((k_ls_score<D, R, QT, ST>), dim3(a.score_grid), dim3(kScoreThreads), 0, st,
                                a, t, tiles0 > 0 ? tiles0 : 1);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
@@ -390,26 +392,32 @@ static hipError_t launch_t(const SearchArgs &a, int engine, int n0, hipStream_t 
     return hipSuccess;
 }
 
-template <int D, typename QT>
+template <int D, typename QT, typename ST>
 static hipError_t launch_search_d(const SearchArgs &a, int R, int engine, int n0, hipStream_t st) {
     switch (R) {
-        case 1: return launch_t<D, 1, QT>(a, engine, n0, st);
-        case 2: return launch_t<D, 2, QT>(a, engine, n0, st);
-        case 4: return launch_t<D, 4, QT>(a, engine, n0, st);
-        case 8: return launch_t<D, 8, QT>(a, engine, n0, st);
-        case 16: return launch_t<D, 16, QT>(a, engine, n0, st);
+        case 1: return launch_t<D, 1, QT, ST>(a, engine, n0, st);
+        case 2: return launch_t<D, 2, QT, ST>(a, engine, n0, st);
+        case 4: return launch_t<D, 4, QT, ST>(a, engine, n0, st);
+        case 8: return launch_t<D, 8, QT, ST>(a, engine, n0, st);
+        case 16: return launch_t<D, 16, QT, ST>(a, engine, n0, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_search(const SearchArgs &a, int D, int R, int dtype, int engine, int n0,
+template <int D, typename QT>
+static hipError_t launch_search_s(const SearchArgs &a, int R, int sdtype, int engine, int n0, hipStream_t st) {
+    return sdtype == ZHA_BF16 ? launch_search_d<D, QT, bf16_t>(a, R, engine, n0, st)
+                              : launch_search_d<D, QT, float>(a, R, engine, n0, st);
+}
+
+hipError_t launch_search(const SearchArgs &a, int D, int R, int dtype, int sdtype, int engine, int n0,
                          hipStream_t st) {
     if (a.walks <= 0) return hipSuccess;
     if (D == 64)
-        return dtype == ZHA_BF16 ? launch_search_d<64, bf16_t>(a, R, engine, n0, st)
-                                 : launch_search_d<64, float>(a, R, engine, n0, st);
-    return dtype == ZHA_BF16 ? launch_search_d<128, bf16_t>(a, R, engine, n0, st)
-                             : launch_search_d<128, float>(a, R, engine, n0, st);
+        return dtype == ZHA_BF16 ? launch_search_s<64, bf16_t>(a, R, sdtype, engine, n0, st)
+                                 : launch_search_s<64, float>(a, R, sdtype, engine, n0, st);
+    return dtype == ZHA_BF16 ? launch_search_s<128, bf16_t>(a, R, sdtype, engine, n0, st)
+                             : launch_search_s<128, float>(a, R, sdtype, engine, n0, st);
 }
 
 }  // namespace zha

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(512) void k_un_init(SearchArgs a) {
 // k%4 of the query and of the reference row (one permutation of D for both
 // operands), so one 16-byte load of the four lanes of a column reads 64
 // contiguous bytes of its row.
-template <int D, int R, typename QT>
+template <int D, int R, typename QT, typename ST>
 __global__ __launch_bounds__(kScoreThreads) void k_un_score(SearchArgs a, int t, int n0) {
     constexpr int NPG = 16 / R;           // nodes per matrix tile
     constexpr int KS = D / 4;             // 16x16x4 steps
@@ -184,11 +184,10 @@ __global__ __launch_bounds__(kScoreThreads) void k_un_score(SearchArgs a, int t,
             const uint32_t id = static_cast<uint32_t>(ent[u].z);
             const int lvl = static_cast<int>(id >> kLevelShift);
             const int64_t node = static_cast<int64_t>(p) * s_cap[lvl] + (id & kIndexMask);
-            const float *kp = s_kap[lvl] + node * (R * D) + (col % R) * D + 4 * grp;
+            const ST *kp = reinterpret_cast<const ST *>(s_kap[lvl]) + node * (R * D) + (col % R) * D + 4 * grp;
 #pragma unroll
             for (int k = 0; k < KS; k += 4) {
-                const float4 v = *reinterpret_cast<const float4 *>(kp + 4 * k);
-                kb[u][k] = v.x; kb[u][k + 1] = v.y; kb[u][k + 2] = v.z; kb[u][k + 3] = v.w;
+                Vec4<ST>::load(kp + 4 * k, &kb[u][k]);
             }
             bias[u] = s_bet[lvl][node * R + (col % R)];
         }
@@ -573,17 +572,17 @@ static int resident_grid(K kernel, int threads) {
     return cache[dev];
 }
 
-template <int D, int R, typename QT>
+template <int D, int R, typename QT, typename ST>
 static hipError_t launch_union_t(const SearchArgs &a, int n0, hipStream_t st) {
     hipLaunchKernelGGL((k_un_init<R>), dim3(a.pairs), dim3(512), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int score_grid = resident_grid(k_un_score<D, R, QT>, kScoreThreads);
+    const int score_grid = resident_grid(k_un_score<D, R, QT, ST>, kScoreThreads);
     for (int t = 0; t < a.levels && t < ZHA_MAX_STEPS; ++t) {
         const bool skip = (t == 0) && (n0 <= 1 || (a.mode == ZHA_TOPK && a.k[0] >= n0) ||
                                        (a.mode == ZHA_TOPP && a.p >= 1.0f));
         if (!skip) {
-            hipLaunchKernelGGL((k_un_score<D, R, QT>), dim3(score_grid), dim3(kScoreThreads), 0, st, a, t,
+            hipLaunchKernelGGL((k_un_score<D, R, QT, ST>), dim3(score_grid), dim3(kScoreThreads), 0, st, a, t,
                                n0);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
@@ -595,25 +594,30 @@ static hipError_t launch_union_t(const SearchArgs &a, int n0, hipStream_t st) {
     return hipSuccess;
 }
 
-template <int D, typename QT>
+template <int D, typename QT, typename ST>
 static hipError_t launch_union_d(const SearchArgs &a, int R, int n0, hipStream_t st) {
     switch (R) {
-        case 1: return launch_union_t<D, 1, QT>(a, n0, st);
-        case 2: return launch_union_t<D, 2, QT>(a, n0, st);
-        case 4: return launch_union_t<D, 4, QT>(a, n0, st);
-        case 8: return launch_union_t<D, 8, QT>(a, n0, st);
-        case 16: return launch_union_t<D, 16, QT>(a, n0, st);
+        case 1: return launch_union_t<D, 1, QT, ST>(a, n0, st);
+        case 2: return launch_union_t<D, 2, QT, ST>(a, n0, st);
+        case 4: return launch_union_t<D, 4, QT, ST>(a, n0, st);
+        case 8: return launch_union_t<D, 8, QT, ST>(a, n0, st);
+        case 16: return launch_union_t<D, 16, QT, ST>(a, n0, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_union(const SearchArgs &a, int D, int R, int dtype, int n0, hipStream_t st) {
+template <int D, typename QT>
+static hipError_t launch_union_s(const SearchArgs &a, int R, int sdtype, int n0, hipStream_t st) {
+    return sdtype == ZHA_BF16 ? launch_union_d<D, QT, bf16_t>(a, R, n0, st) : launch_union_d<D, QT, float>(a, R, n0, st);
+}
+
+hipError_t launch_union(const SearchArgs &a, int D, int R, int dtype, int sdtype, int n0, hipStream_t st) {
     if (a.pairs <= 0) return hipSuccess;
     if (D == 64)
-        return dtype == ZHA_BF16 ? launch_union_d<64, bf16_t>(a, R, n0, st)
-                                 : launch_union_d<64, float>(a, R, n0, st);
-    return dtype == ZHA_BF16 ? launch_union_d<128, bf16_t>(a, R, n0, st)
-                             : launch_union_d<128, float>(a, R, n0, st);
+        return dtype == ZHA_BF16 ? launch_union_s<64, bf16_t>(a, R, sdtype, n0, st)
+                                 : launch_union_s<64, float>(a, R, sdtype, n0, st);
+    return dtype == ZHA_BF16 ? launch_union_s<128, bf16_t>(a, R, sdtype, n0, st)
+                             : launch_union_s<128, float>(a, R, sdtype, n0, st);
 }
 
 }  // namespace zha

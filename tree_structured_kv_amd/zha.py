@@ -36,7 +36,7 @@ class Geometry(ctypes.Structure):
                 ("chunk", ctypes.c_int32), ("num_refs", ctypes.c_int32),
                 ("levels", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int64), ("sharpness", ctypes.c_float),
-                ("reserved", ctypes.c_int32)]
+                ("summary_dtype", ctypes.c_int32)]
 
 
 class Select(ctypes.Structure):
@@ -135,10 +135,11 @@ def _stream(stream) -> int | None:
 
 
 def make_geometry(batch, kv_heads, group, head_dim, chunk, refs, levels, dtype, max_tokens,
-                  sharpness) -> Geometry:
+                  sharpness, summary="f32") -> Geometry:
     return Geometry(batch, kv_heads, group, head_dim, chunk, refs, levels,
                     BF16 if dtype in ("bf16", BF16, torch.bfloat16) else F32,
-                    int(max_tokens), float(sharpness), 0)
+                    int(max_tokens), float(sharpness),
+                    BF16 if summary in ("bf16", BF16, torch.bfloat16) else F32)
 
 
 def make_select(mode="topp", p=0.9, k=(1,), max_blocks=1024, max_candidates=0, engine="auto") -> Select:
@@ -298,7 +299,10 @@ class Index:
         cap = h.level_cap[l]
         nk = g.batch * g.num_kv_heads * cap * g.num_refs * g.head_dim
         nb = g.batch * g.num_kv_heads * cap * g.num_refs
-        k = self.tree_mem[h.key_off[l]: h.key_off[l] + 4 * nk].view(torch.float32)
+        if g.summary_dtype == BF16:
+            k = self.tree_mem[h.key_off[l]: h.key_off[l] + 2 * nk].view(torch.bfloat16)
+        else:
+            k = self.tree_mem[h.key_off[l]: h.key_off[l] + 4 * nk].view(torch.float32)
         b = self.tree_mem[h.bias_off[l]: h.bias_off[l] + 4 * nb].view(torch.float32)
         return (k.view(g.batch, g.num_kv_heads, cap, g.num_refs, g.head_dim),
                 b.view(g.batch, g.num_kv_heads, cap, g.num_refs))
