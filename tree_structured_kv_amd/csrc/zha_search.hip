@@ -45,22 +45,30 @@ namespace {
 constexpr int kScoreThreads = 256;     // workgroup of the level-synchronous scorer
 constexpr int kU = 4;                  // candidates in flight per wavefront
 
-template <int D, typename QT>
-__device__ __forceinline__ void load_q(const SearchArgs &a, int w, float (&qv)[4]) {
-    constexpr int LPR = D / 4;
+// Elements of a node-key row per lane: 16 bytes of keys (4 fp32, or 8 bf16
+// while that still leaves at least 16 lanes per row).
+template <int D, typename ST>
+constexpr int row_epl() { return (sizeof(ST) == 2 && D >= 128) ? 8 : 4; }
+
+template <int D, typename QT, typename ST>
+__device__ __forceinline__ void load_q(const SearchArgs &a, int w, float (&qv)[row_epl<D, ST>()]) {
+    constexpr int EPL = row_epl<D, ST>();
+    constexpr int LPR = D / EPL;
     const int sub = (threadIdx.x & 63) % LPR;
-    const QT *qp = static_cast<const QT *>(a.q) + static_cast<int64_t>(w) * D + 4 * sub;
+    const QT *qp = static_cast<const QT *>(a.q) + static_cast<int64_t>(w) * D + EPL * sub;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) qv[e] = Elem<QT>::load(qp, e);
+    for (int e = 0; e < EPL; ++e) qv[e] = Elem<QT>::load(qp, e);
 }
 
 // One wavefront scores candidates first, first + stride, ... below `end`, kU
 // at a time, and writes sc[i]; returns the largest score it wrote.
 template <int D, int R, typename ST>
-__device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair, const float (&qv)[4],
+__device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair,
+                                            const float (&qv)[row_epl<D, ST>()],
                                             const uint32_t *cur, float *sc, int first, int end,
                                             int stride, uint32_t &flags) {
-    constexpr int LPR = D / 4;            // lanes per reference row (float4 each)
+    constexpr int EPL = row_epl<D, ST>();  // key elements per lane (one 16-byte load)
+    constexpr int LPR = D / EPL;          // lanes per reference row
     constexpr int RPL = 64 / LPR;         // references per 64-lane load
     constexpr int NL = (R + RPL - 1) / RPL;
     const int lane = threadIdx.x & 63;
@@ -76,7 +84,7 @@ __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair, c
         ids[u] = cur[i < end ? i : end - 1];
     }
     for (int base = first; base < end; base += stride) {
-        float4 kv[kU][NL];
+        float kv[kU][NL][EPL];
         float bv[kU][NL];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
@@ -89,12 +97,14 @@ __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair, c
             for (int l = 0; l < NL; ++l) {
                 const int r = l * RPL + rsub;
                 if (r < R) {
-                    float t4[4];
-                    Vec4<ST>::load(kp + r * D + 4 * sub, t4);
-                    kv[u][l] = make_float4(t4[0], t4[1], t4[2], t4[3]);
+                    if constexpr (EPL == 8)
+                        Vec16<ST>::load(kp + r * D + EPL * sub, kv[u][l]);
+                    else
+                        Vec4<ST>::load(kp + r * D + EPL * sub, kv[u][l]);
                     bv[u][l] = bp[r];
                 } else {
-                    kv[u][l] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) kv[u][l][e] = 0.f;
                     bv[u][l] = -INFINITY;
                 }
             }
@@ -110,10 +120,9 @@ __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair, c
             float best = -INFINITY;
 #pragma unroll
             for (int l = 0; l < NL; ++l) {
-                float d = kv[u][l].x * qv[0];
-                d = fmaf(kv[u][l].y, qv[1], d);
-                d = fmaf(kv[u][l].z, qv[2], d);
-                d = fmaf(kv[u][l].w, qv[3], d);
+                float d = kv[u][l][0] * qv[0];
+#pragma unroll
+                for (int e = 1; e < EPL; ++e) d = fmaf(kv[u][l][e], qv[e], d);
                 d = group_sum<LPR>(d);
                 best = fmaxf(best, fmaf(s, d, bv[u][l]));
             }
@@ -199,8 +208,8 @@ __global__ __launch_bounds__(kThreads) void k_search_decode(SearchArgs a) {
     __shared__ int32_t s_scored[ZHA_MAX_STEPS], s_opened[ZHA_MAX_STEPS];
     if (tid == 0) sh.flags = 0;
 
-    float qv[4];
-    load_q<D, QT>(a, w, qv);
+    float qv[row_epl<D, ST>()];
+    load_q<D, QT, ST>(a, w, qv);
 
     uint32_t *cur = a.cand + static_cast<int64_t>(w) * 2 * cap;
     uint32_t *nxt = cur + cap;
@@ -300,8 +309,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_ls_score(SearchArgs a, int t,
         const uint32_t *cur = a.cand + static_cast<int64_t>(w) * 2 * a.cand_cap +
                               static_cast<int64_t>(buf) * a.cand_cap;
         float *sc = a.score + static_cast<int64_t>(w) * a.cand_cap;
-        float qv[4];
-        load_q<D, QT>(a, w, qv);
+        float qv[row_epl<D, ST>()];
+        load_q<D, QT, ST>(a, w, qv);
         uint32_t flags = 0;
         (void)score_wave<D, R, ST>(a, pair, qv, cur, sc, start + wave * kU, end, kSW * kU, flags);
         if (flags && lane == 0) atomicOr(a.status, flags);

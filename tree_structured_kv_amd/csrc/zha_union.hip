@@ -36,6 +36,17 @@ namespace zha {
 namespace {
 
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+// Four bf16 values (two packed 32-bit words) as a matrix-core operand.
+__device__ __forceinline__ short4_t pack4(uint32_t lo, uint32_t hi) {
+    short4_t r;
+    r[0] = static_cast<short>(lo & 0xffffu);
+    r[1] = static_cast<short>(lo >> 16);
+    r[2] = static_cast<short>(hi & 0xffffu);
+    r[3] = static_cast<short>(hi >> 16);
+    return r;
+}
 
 constexpr int kScoreThreads = 256;
 constexpr int kUG = 2;                // matrix tiles in flight per wavefront
@@ -168,6 +179,41 @@ __global__ __launch_bounds__(kScoreThreads) void k_un_score(SearchArgs a, int t,
         else
             return qa[k];
     };
+    // bf16 keys and queries go to bf16 matrix products instead
+    constexpr bool kBf16Mma = sizeof(ST) == 2 && sizeof(QT) == 2;
+    constexpr int KS2 = D / 16;           // 16x16x16 steps
+    short4_t qh[kBf16Mma ? KS2 : 1];
+    // query operand: row = head `col` of the pair's group (zero past G)
+    auto load_query = [&](int p) {
+        if (p == cur_pair) return;
+        cur_pair = p;
+        const bool ok = col < a.group;
+        const int w = head_walk(a, p, ok ? col : 0);
+        const QT *qrow = static_cast<const QT *>(a.q) + static_cast<int64_t>(w) * D;
+        if constexpr (kBf16Mma) {
+#pragma unroll
+            for (int m = 0; m < KS2 / 2; ++m) {
+                uint4 v = *reinterpret_cast<const uint4 *>(qrow + 32 * m + 8 * grp);
+                if (!ok) v = make_uint4(0u, 0u, 0u, 0u);
+                qh[2 * m] = pack4(v.x, v.y);
+                qh[2 * m + 1] = pack4(v.z, v.w);
+            }
+        } else if constexpr (kPacked) {
+            const QT *qp = qrow + 4 * grp;
+#pragma unroll
+            for (int j = 0; j < KS / 4; ++j) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(qp + 16 * j);
+                qpk[2 * j] = ok ? v.x : 0u;
+                qpk[2 * j + 1] = ok ? v.y : 0u;
+            }
+        } else {
+            const QT *qp = qrow + 4 * grp;
+#pragma unroll
+            for (int j = 0; j < KS / 4; ++j) Vec4<QT>::load(qp + 16 * j, qa + 4 * j);
+#pragma unroll
+            for (int k = 0; k < KS; ++k) qa[k] = ok ? qa[k] : 0.f;
+        }
+    };
     for (int b = b0; b < b1; ++b) {
         int4 ent[kUG];
 #pragma unroll
@@ -177,8 +223,38 @@ __global__ __launch_bounds__(kScoreThreads) void k_un_score(SearchArgs a, int t,
             for (int u = 0; u < kUG; ++u) nxt[u] = entry((b + 1) * WB + u * NPG + col / R);
         }
         const int p = __builtin_amdgcn_readfirstlane(ent[0].x);
-        float kb[kUG][KS];
         float bias[kUG];
+        float4_t acc[kUG];
+#pragma unroll
+        for (int u = 0; u < kUG; ++u) acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (kBf16Mma) {
+            // bf16 keys and queries: 16x16x16 bf16 products, exact products
+            // summed in fp32.  Step k of lane group q takes elements
+            // 32*(k/2) + 8*q + 4*(k%2) .. +3 of both rows, so one 16-byte
+            // load serves two steps.
+            short4_t kh[kUG][KS2];
+#pragma unroll
+            for (int u = 0; u < kUG; ++u) {
+                const uint32_t id = static_cast<uint32_t>(ent[u].z);
+                const int lvl = static_cast<int>(id >> kLevelShift);
+                const int64_t node = static_cast<int64_t>(p) * s_cap[lvl] + (id & kIndexMask);
+                const bf16_t *kp = reinterpret_cast<const bf16_t *>(s_kap[lvl]) + node * (R * D) + (col % R) * D + 8 * grp;
+#pragma unroll
+                for (int m = 0; m < KS2 / 2; ++m) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(kp + 32 * m);
+                    kh[u][2 * m] = pack4(v.x, v.y);
+                    kh[u][2 * m + 1] = pack4(v.z, v.w);
+                }
+                bias[u] = s_bet[lvl][node * R + (col % R)];
+            }
+            load_query(p);
+#pragma unroll
+            for (int k = 0; k < KS2; ++k)
+#pragma unroll
+                for (int u = 0; u < kUG; ++u)
+                    acc[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qh[k], kh[u][k], acc[u], 0, 0, 0);
+        } else {
+        float kb[kUG][KS];
 #pragma unroll
         for (int u = 0; u < kUG; ++u) {
             const uint32_t id = static_cast<uint32_t>(ent[u].z);
@@ -191,35 +267,14 @@ __global__ __launch_bounds__(kScoreThreads) void k_un_score(SearchArgs a, int t,
             }
             bias[u] = s_bet[lvl][node * R + (col % R)];
         }
-        // query operand: row = head `col` of the pair's group (zero past G)
-        if (p != cur_pair) {
-            cur_pair = p;
-            const bool ok = col < a.group;
-            const int w = head_walk(a, p, ok ? col : 0);
-            const QT *qp = static_cast<const QT *>(a.q) + static_cast<int64_t>(w) * D + 4 * grp;
-            if constexpr (kPacked) {
-#pragma unroll
-                for (int j = 0; j < KS / 4; ++j) {
-                    const uint2 v = *reinterpret_cast<const uint2 *>(qp + 16 * j);
-                    qpk[2 * j] = ok ? v.x : 0u;
-                    qpk[2 * j + 1] = ok ? v.y : 0u;
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < KS / 4; ++j) Vec4<QT>::load(qp + 16 * j, qa + 4 * j);
-#pragma unroll
-                for (int k = 0; k < KS; ++k) qa[k] = ok ? qa[k] : 0.f;
-            }
-        }
+        load_query(p);
         // the kUG products interleaved, so consecutive matrix ops are independent
-        float4_t acc[kUG];
-#pragma unroll
-        for (int u = 0; u < kUG; ++u) acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < KS; ++k)
 #pragma unroll
             for (int u = 0; u < kUG; ++u)
                 acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(qval(k), kb[u][k], acc[u], 0, 0, 0);
+        }
 #pragma unroll
         for (int u = 0; u < kUG; ++u) {
             const int pos = ent[u].y;
