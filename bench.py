@@ -470,6 +470,77 @@ def measured_traffic(workload, engine):
     return None
 
 
+SWEEP_NS = [4096, 16384, 65536, 262144, 1 << 20, 1 << 22, 1 << 24]
+
+
+def sweep_levels(n, c=4, top=64):
+    """Depth policy of the length sweep: the fewest levels that leave at
+    most `top` nodes at the top level."""
+    L = 1
+    while n // c ** L > top:
+        L += 1
+    return L
+
+
+def run_sweep(Zm, ns=SWEEP_NS, queries=64, sample=16, reps=10):
+    """Length sweep on nested keys (synth.nested_*): for each context length,
+    one tree (chunk 4, 4 references, depth by sweep_levels) and `queries`
+    one-place queries walked with top-p 0.9; reports comparisons and keys
+    read per walk, the dense attention mass the selection keeps (fp64 on the
+    host, `sample` walks) and the search time."""
+    import torch
+    from tree_structured_kv_amd import synth as S
+    d, c, R, s = 64, 4, 4, 20.0
+    out = []
+    for n in ns:
+        L = sweep_levels(n, c)
+        t0 = time.time()
+        K = S.nested_keys(n, d)
+        Q = S.nested_queries(n, d, queries)
+        refs = S.nested_refs(R, d)
+        Kt = torch.from_numpy(K).cuda().view(1, 1, n, d)
+        Qt = torch.from_numpy(Q).cuda().view(1, queries, d)
+        geom = Zm.make_geometry(1, 1, queries, d, c, R, L, "f32", n, s)
+        idx = Zm.Index(geom, torch.from_numpy(refs).view(1, R, d))
+        idx.build(Kt, n)
+        sel = Zm.make_select("topp", 0.9, max_blocks=n // c, max_candidates=0)
+        bufs = idx.search_buffers(sel)
+        idx.search(Qt, sel, bufs)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            idx.search(Qt, sel, bufs)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        stats = Zm.stats_to_dicts(bufs["stats"].cpu())
+        blocks = bufs["sel_blocks"].cpu().numpy()
+        count = bufs["sel_count"].cpu().numpy()
+        status = int(bufs["status"].cpu()[0])
+        kept = []
+        for wi in range(min(sample, queries)):
+            lg = np.empty(n, np.float64)
+            for a in range(0, n, 1 << 20):
+                lg[a:a + (1 << 20)] = s * (K[a:a + (1 << 20)] @ Q[wi]).astype(np.float64)
+            p = np.exp(lg - lg.max())
+            toks = (blocks[wi, :count[wi]].astype(np.int64)[:, None] * c + np.arange(c)[None, :]).reshape(-1)
+            tail = np.arange(c * (n // c), n)
+            kept.append(float((p[toks].sum() + p[tail].sum()) / p.sum()))
+        row = dict(tokens=n, levels=L, top_nodes=n // c ** L, engine=idx.engine(sel),
+                   comparisons_per_walk=float(np.mean([r["comparisons"] for r in stats])),
+                   keys_read_per_walk=float(np.mean([r["keys_read"] for r in stats])),
+                   nodes_scored_per_walk=float(np.mean([sum(r["scored"]) for r in stats])),
+                   mass_kept=float(np.mean(kept)), mass_kept_min=float(np.min(kept)),
+                   search_ms=ms, search_us_per_walk=ms * 1e3 / queries, status=status,
+                   seconds=time.time() - t0)
+        log(json.dumps(row))
+        out.append(row)
+        del Kt, idx, bufs
+        torch.cuda.empty_cache()
+    return out
+
+
 def summary(res, bw_ach):
     w = res["workload"]
     sel = res["select"]
@@ -517,6 +588,8 @@ def main():
     ap.add_argument("--calibrate", action="store_true",
                     help="also copy 1 GiB three times (the known-size kernel that scales HBM counters)")
     ap.add_argument("--threads", type=int, default=min(16, len(os.sched_getaffinity(0))))
+    ap.add_argument("--sweep", action="store_true",
+                    help="only the length sweep on nested keys (4K .. 16M tokens); prints one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -530,6 +603,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     global ENGINE
     ENGINE = args.engine
+
+    if args.sweep:
+        rows = run_sweep(Zm)
+        print(json.dumps({"sweep": "nested keys, chunk 4, R 4, d 64, s 20, top-p 0.9, 64 one-place queries",
+                          "rows": rows}), flush=True)
+        return
 
     bw_ach = hbm_probe(Zm)
     log(f"achievable HBM read bandwidth {bw_ach:.0f} GB/s")

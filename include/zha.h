@@ -48,8 +48,8 @@
 extern "C" {
 #endif
 
-#define ZHA_MAX_LEVELS 8
-#define ZHA_MAX_STEPS 8
+#define ZHA_MAX_LEVELS 12
+#define ZHA_MAX_STEPS 12
 
 typedef enum {
     ZHA_OK = 0,

@@ -22,7 +22,7 @@ _LIB = os.path.join(_HERE, "libzha_oracle.so")
 
 TOPP = 0
 TOPK = 1
-MAX_LEVELS = 8
+MAX_LEVELS = 12
 
 
 class WalkStats(ctypes.Structure):

@@ -23,7 +23,7 @@
 #define ZHA_ORACLE_H
 #include <stdint.h>
 
-#define ORA_MAX_LEVELS 8
+#define ORA_MAX_LEVELS 12
 
 #define ORA_TOPP 0
 #define ORA_TOPK 1

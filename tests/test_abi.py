@@ -34,8 +34,8 @@ def test_every_declared_symbol_is_exported(Z):
 def test_struct_sizes_match_header(Z):
     # layouts the header fixes: 8 int32 + int64 + float + int32 = 48 bytes
     assert ctypes.sizeof(Z.Geometry) == 48
-    assert ctypes.sizeof(Z.WalkStats) == 96
-    assert ctypes.sizeof(Z.Select) == 4 * (2 + 8 + 4)
+    assert ctypes.sizeof(Z.WalkStats) == 4 * (2 * 12 + 8)
+    assert ctypes.sizeof(Z.Select) == 4 * (2 + 12 + 4)
 
 
 def _geom(Z, **kw):
@@ -57,7 +57,7 @@ def test_tree_bytes_formula(Z):
 
 
 @pytest.mark.parametrize("kw", [dict(head_dim=96), dict(chunk=3), dict(chunk=128), dict(refs=3),
-                                dict(levels=0), dict(levels=9), dict(dtype=5),
+                                dict(levels=0), dict(levels=13), dict(dtype=5),
                                 dict(max_tokens=0), dict(batch=0), dict(sharpness=float("inf"))])
 def test_bad_geometry_rejected(Z, kw):
     g = _geom(Z, **kw)
@@ -199,3 +199,22 @@ def test_search_engine_resolution(Z):
     assert Z.zha_search_engine(wide, topp, 2) == "block"
     big = _handle(Z, batch=4, kv_heads=1, group=32)
     assert Z.zha_search_engine(big, Z.make_select("topp", 0.9, max_blocks=64, engine="union")) is None
+
+
+def test_sweep_depth_policy_and_nested_inputs():
+    # the length sweep's depth rule: fewest levels leaving <= 64 top nodes (chunk 4)
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    import numpy as np
+    from tree_structured_kv_amd import synth as S
+    assert [bench.sweep_levels(n) for n in bench.SWEEP_NS] == [3, 4, 5, 6, 7, 8, 9]
+    assert all(n // 4 ** bench.sweep_levels(n) <= 64 < n // 4 ** (bench.sweep_levels(n) - 1)
+               for n in bench.SWEEP_NS)
+    k1 = S.nested_keys(5000, 64)
+    k2 = S.nested_keys(5000, 64)
+    assert k1.dtype == np.float32 and k1.shape == (5000, 64) and np.array_equal(k1, k2)
+    # keys of one 64-key segment are close, neighbouring segments less so
+    seg = k1[:64]
+    assert np.min(seg @ seg.mean(0)) > 0.9 * np.max(k1[64:128] @ seg.mean(0)) - 1.0
+    assert S.nested_queries(5000, 64, 8).shape == (8, 64)

@@ -262,3 +262,60 @@ def batch_inputs(w: Workload, rot: int = 0, threads: int = 8, unstructured: bool
             one(bg)
     R = np.stack([refs(w, g) for g in range(H)])
     return K, V, Q, R
+
+
+# ---- length sweep: nested keys -------------------------------------------------
+#
+# A self-similar structure, for measuring how a walk's cost grows with the
+# context: segments of `seg` keys share a unit centroid, and the centroids
+# nest in tiers of 4 at every scale -- one direction at the top, and each
+# tier's 4 children of a direction drawn around it (direction + 0.6 * a
+# random unit vector, renormalised), until there is a centroid per segment.
+# key = amp * segment centroid + noise * N(0, I/d); a query targets one
+# segment ("asks about one place"): amp * centroid + noise * N(0, I/d).
+# Stream ids 10.. keep these draws apart from the five workloads above.
+
+S_NEST_KEYS, S_NEST_QUERIES, S_NEST_REFS = 10, 11, 12
+
+
+def _unit(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def _nested_centroids(n, d, seed, seg):
+    rng = np.random.default_rng(np.random.SeedSequence([ROOT_SEED, 100, seed, S_NEST_KEYS]))
+    nseg = (n + seg - 1) // seg
+    cent = _unit(rng.standard_normal((1, d)))
+    while cent.shape[0] < nseg:
+        kids = np.repeat(cent, 4, axis=0)
+        cent = _unit(kids + 0.6 * _unit(rng.standard_normal(kids.shape)))
+    return cent[:nseg], rng
+
+
+def nested_keys(n, d, seed=0, seg=64, amp=1.0, noise=0.1):
+    """float32 [n][d] keys of the length sweep (see above), drawn in float32
+    in fixed 1M-row slices (so memory stays bounded at 16M keys)."""
+    cent, rng = _nested_centroids(n, d, seed, seg)
+    cent = (amp * cent).astype(np.float32)
+    out = np.empty((n, d), np.float32)
+    sl = 1 << 20
+    scale = np.float32(noise / math.sqrt(d))
+    for a in range(0, n, sl):
+        b = min(n, a + sl)
+        out[a:b] = cent[np.arange(a, b) // seg] + scale * rng.standard_normal((b - a, d), dtype=np.float32)
+    return out
+
+
+def nested_queries(n, d, count, seed=0, seg=64, amp=1.0, noise=0.1):
+    """float32 [count][d] one-place queries for nested_keys(n, d, seed)."""
+    cent, _ = _nested_centroids(n, d, seed, seg)
+    rng = np.random.default_rng(np.random.SeedSequence([ROOT_SEED, 100, seed, S_NEST_QUERIES]))
+    j = rng.integers(0, cent.shape[0], size=count)
+    q = amp * cent[j] + noise * rng.standard_normal((count, d)) / math.sqrt(d)
+    return q.astype(np.float32)
+
+
+def nested_refs(r, d, seed=0):
+    """float32 [r][d] reference queries N(0, 1)/sqrt(d) of the length sweep."""
+    rng = np.random.default_rng(np.random.SeedSequence([ROOT_SEED, 100, seed, S_NEST_REFS]))
+    return (rng.standard_normal((r, d)) / math.sqrt(d)).astype(np.float32)

@@ -16,8 +16,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libzha.so")
 
-MAX_LEVELS = 8
-MAX_STEPS = 8
+MAX_LEVELS = 12
+MAX_STEPS = 12
 TOPP, TOPK = 0, 1
 F32, BF16 = 0, 1
 FLAG_CAND_OVERFLOW, FLAG_SEL_OVERFLOW, FLAG_NONFINITE = 1, 2, 4
