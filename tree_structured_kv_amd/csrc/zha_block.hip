@@ -180,9 +180,9 @@ __global__ __launch_bounds__(kBkThreads) void k_bk_score(SearchArgs a, int t, in
             float kb[KS];
 #pragma unroll
             for (int k = 0; k < KS; k += 4) {
-                Vec4<ST>::load(kp + 4 * k, &kb[k]);
+                GVec4<ST>::load(kp + 4 * k, &kb[k]);
             }
-            const float bias = s_bet[lvl][node * R + (col % R)];
+            const float bias = gload_f(s_bet[lvl] + node * R + (col % R));
             if (mark && (col % R) == 0 && grp == 0 && ct * NPG + col / R < nchild) {
                 const int64_t bitn = a.node_off[lvl] + (id & kIndexMask);
                 atomicOr(a.visited + static_cast<int64_t>(pair) * a.vis_words + (bitn >> 5), 1u << (bitn & 31));

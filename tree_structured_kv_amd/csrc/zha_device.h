@@ -46,6 +46,35 @@ template <> struct Vec4<bf16_t> {
     }
 };
 
+// Loads through pointers known to address device (global) memory.  When a
+// pointer is read from a table in LDS the compiler cannot tell its address
+// space and emits flat loads, which also count on the LDS counter: a later
+// wait for an LDS read then waits for every flat load still in flight.
+typedef float gf4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t gu4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t gu2_t __attribute__((ext_vector_type(2)));
+#define ZHA_GLOBAL(T) const __attribute__((address_space(1))) T *
+__device__ __forceinline__ gf4_t gload_f4(const void *p) { return *(ZHA_GLOBAL(gf4_t))p; }
+__device__ __forceinline__ gu4_t gload_u4(const void *p) { return *(ZHA_GLOBAL(gu4_t))p; }
+__device__ __forceinline__ gu2_t gload_u2(const void *p) { return *(ZHA_GLOBAL(gu2_t))p; }
+__device__ __forceinline__ float gload_f(const float *p) { return *(ZHA_GLOBAL(float))p; }
+
+// Vec4 through a global pointer.
+template <typename T> struct GVec4;
+template <> struct GVec4<float> {
+    static __device__ __forceinline__ void load(const float *p, float *o) {
+        const gf4_t v = gload_f4(p);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+};
+template <> struct GVec4<bf16_t> {
+    static __device__ __forceinline__ void load(const bf16_t *p, float *o) {
+        const gu2_t v = gload_u2(p);
+        o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+        o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+};
+
 // 16 bytes of a row as floats: 4 fp32 or 8 bf16 elements.
 template <typename T> struct Vec16;
 template <> struct Vec16<float> {

@@ -116,22 +116,22 @@ SearchWs search_ws_layout(const zha_tree *t, const zha_select *sel, int32_t qph)
     l.tile_map = l.tile_count + align_up((ZHA_MAX_STEPS + 1) * sizeof(int32_t));
     l.u_ids = l.tile_map + align_up(walks * ((cap + kTile - 1) / kTile) * sizeof(int2));
     l.u_omask = l.u_ids + align_up(pairs * 2 * cap * sizeof(uint32_t));
-    l.u_n = l.u_omask + align_up(pairs * cap * sizeof(uint32_t));
+    l.u_n = l.u_omask + align_up(pairs * 2 * cap * sizeof(uint32_t));
     l.u_next = l.u_n + align_up(pairs * 2 * sizeof(int32_t));
     l.h_score = l.u_next + align_up(uw * sizeof(int32_t));
     l.u_rank = l.h_score + align_up(uw * cap * sizeof(float));
     l.u_par = l.u_rank + align_up(pairs * cap * sizeof(int32_t));
     l.u_open = l.u_par + align_up(pairs * cap * sizeof(uint32_t));
     l.u_flat = l.u_open + align_up(uw * cap * sizeof(int32_t));
-    l.flat_cap = pairs * (cap + kFlatPad);
+    l.flat_cap = pairs * (cap + kExpSlices * kFlatPad);
     l.u_score = l.u_flat + align_up(2 * l.flat_cap * 16);
-    const uint64_t gp = (uint64_t(t->geom.group_size) + 3) / 4 * 4;
     // block engine: parents are the nodes of levels >= 2; a walk keeps at
     // most cap/c + 1 of them per step
     const uint64_t all_pairs = uint64_t(t->geom.batch) * t->geom.num_kv_heads;
     l.nbins = 0;
     for (int lv = 2; lv <= t->geom.levels; ++lv) l.nbins += static_cast<uint64_t>(t->level_cap[lv]);
     l.pcap = cap / static_cast<uint64_t>(t->geom.chunk) + 1;
+    const uint64_t gp = (uint64_t(t->geom.group_size) + 3) / 4 * 4;
     l.b_roots = l.u_score + align_up(pairs * cap * gp * sizeof(float));
     l.b_cnt = l.b_roots + align_up(cap * sizeof(uint32_t));
     l.b_fill = l.b_cnt + align_up(all_pairs * l.nbins * sizeof(int32_t));

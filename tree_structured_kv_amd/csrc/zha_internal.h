@@ -15,7 +15,8 @@ constexpr uint32_t kIndexMask = (1u << kLevelShift) - 1u;
 constexpr int kBlock = 256;          // threads per workgroup of most kernels
 constexpr int kChunkKeys = 1024;     // keys per attention work item
 constexpr int kTile = 32;            // candidates per tile of the level-synchronous scorer
-constexpr int kFlatPad = 32;         // union engine: each pair's run of scoring entries is padded to this
+constexpr int kFlatPad = 32;         // union engine: each run of scoring entries is padded to this
+constexpr int kExpSlices = 8;        // union engine: workgroups (runs) per pair building the next list
 
 // Per-walk state of the level-synchronous search engine (workspace).
 struct WalkState {
@@ -71,8 +72,8 @@ struct SearchArgs {
     // union engine: one candidate list per (sequence, KV head) pair, the
     // union over its query heads, with a head mask per node
     uint32_t *u_ids;                       // ws [pairs][2][cand_cap]
-    uint32_t *u_omask;                     // ws [pairs][cand_cap]  heads that opened the node
-    int32_t *u_n;                          // ws [pairs][2]  {list size, current buffer}
+    uint32_t *u_omask;                     // ws [pairs][2][cand_cap]  heads that opened the node (by step parity)
+    int32_t *u_n;                          // ws [pairs][2]  list size (by step parity)
     int32_t *u_next;                       // ws [walks]  entries a head opened (levels > 1)
     float *u_score;                        // ws [pairs][cand_cap][round_up(group, 4)]
     float *h_score;                        // ws [walks][cand_cap]  a head's gathered scores

@@ -22,9 +22,10 @@
 //               head's exact radix-select cut, its level-1 selections in
 //               span order, the higher nodes it opens (list positions, in
 //               order) and head bit h on them;
-//   k_un_expand one workgroup per pair: ranks of the opened nodes (in list
-//               order), the next union list (their children, written
-//               coalesced) and its flat scoring entries.
+//   k_un_expand up to kExpSlices workgroups per pair, each over a slice of
+//               its list: ranks of the opened nodes (in list order), the
+//               next union list (their children, written coalesced) and
+//               its flat scoring entries.
 // A head's candidates keep the list order, so selections, statistics and
 // the cut are those of a walk of that head alone.
 #include "zha_device.h"
@@ -52,6 +53,7 @@ constexpr int kScoreThreads = 256;
 constexpr int kUG = 2;                // matrix tiles in flight per wavefront
 constexpr int kLdsCand = 14336;       // candidate scores a cut stages in LDS (56 KB)
 constexpr int kLdsPar = 2048;         // parent ranks a cut stages in LDS (8 KB)
+constexpr int kExpMin = 256;          // list entries per expand workgroup (at least)
 
 __device__ __forceinline__ int head_walk(const SearchArgs &a, int pair, int h) {
     const int b = pair / a.kv_heads, g = pair % a.kv_heads;
@@ -62,6 +64,7 @@ __device__ __forceinline__ int round_flat(int n) { return (n + kFlatPad - 1) / k
 
 struct ExpandShared {
     uint32_t seg_cnt[kWaves];
+    uint32_t pre_cnt[kWaves];
     int32_t flat_base;
     int32_t need;
 };
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(512) void k_un_init(SearchArgs a) {
     uint32_t flags = 0;
     uint32_t *ids = a.u_ids + static_cast<int64_t>(p) * 2 * cap;
     const int n = write_roots(a, ids, flags);
-    uint32_t *om = a.u_omask + static_cast<int64_t>(p) * cap;
+    uint32_t *om = a.u_omask + static_cast<int64_t>(p) * 2 * cap;     // step 0's masks
     for (int i = tid; i < n; i += blockDim.x) om[i] = 0;
     if (flags) atomicOr(&s_flags, flags);
     __syncthreads();
@@ -241,11 +244,11 @@ __global__ __launch_bounds__(kScoreThreads) void k_un_score(SearchArgs a, int t,
                 const bf16_t *kp = reinterpret_cast<const bf16_t *>(s_kap[lvl]) + node * (R * D) + (col % R) * D + 8 * grp;
 #pragma unroll
                 for (int m = 0; m < KS2 / 2; ++m) {
-                    const uint4 v = *reinterpret_cast<const uint4 *>(kp + 32 * m);
+                    const gu4_t v = gload_u4(kp + 32 * m);
                     kh[u][2 * m] = pack4(v.x, v.y);
                     kh[u][2 * m + 1] = pack4(v.z, v.w);
                 }
-                bias[u] = s_bet[lvl][node * R + (col % R)];
+                bias[u] = gload_f(s_bet[lvl] + node * R + (col % R));
             }
             load_query(p);
 #pragma unroll
@@ -263,9 +266,9 @@ __global__ __launch_bounds__(kScoreThreads) void k_un_score(SearchArgs a, int t,
             const ST *kp = reinterpret_cast<const ST *>(s_kap[lvl]) + node * (R * D) + (col % R) * D + 4 * grp;
 #pragma unroll
             for (int k = 0; k < KS; k += 4) {
-                Vec4<ST>::load(kp + 4 * k, &kb[u][k]);
+                GVec4<ST>::load(kp + 4 * k, &kb[u][k]);
             }
-            bias[u] = s_bet[lvl][node * R + (col % R)];
+            bias[u] = gload_f(s_bet[lvl] + node * R + (col % R));
         }
         load_query(p);
         // the kUG products interleaved, so consecutive matrix ops are independent
@@ -316,8 +319,8 @@ __device__ __forceinline__ void cut_head(const SearchArgs &a, int t, int w, Sele
     const int p = w / a.group, h = w % a.group;
     const uint32_t bit = 1u << h;
     const int cap = a.cand_cap, log2c = a.log2c, c = a.chunk;
-    const int n_u = a.u_n[2 * p];
-    const int buf = a.u_n[2 * p + 1];
+    const int buf = t & 1;                         // list, masks and lengths alternate by step
+    const int n_u = a.u_n[2 * p + buf];
     const int n_open_prev = (t == 0) ? 0 : a.u_next[w];
     if (t > 0 && n_open_prev == 0) return;         // this head opened nothing more
     WalkState *st = a.state + w;
@@ -325,7 +328,7 @@ __device__ __forceinline__ void cut_head(const SearchArgs &a, int t, int w, Sele
     const int gp = (a.group + 3) & ~3;
     const float *sc = a.u_score + static_cast<int64_t>(p) * cap * gp + h;   // score of position i: sc[i * gp]
     const int32_t *rank = a.u_rank + static_cast<int64_t>(p) * cap;
-    uint32_t *om = a.u_omask + static_cast<int64_t>(p) * cap;
+    uint32_t *om = a.u_omask + (static_cast<int64_t>(p) * 2 + buf) * cap;
     int32_t *opened_pos = a.u_open + static_cast<int64_t>(w) * cap;
     uint32_t *cid = a.cand + static_cast<int64_t>(w) * 2 * cap;     // this head's candidate ids
     uint32_t *cux = cid + cap;                                       // their list positions (fallback)
@@ -490,30 +493,65 @@ __device__ __forceinline__ void cut_head(const SearchArgs &a, int t, int w, Sele
     }
 }
 
-// Step t for pair p, after every head's cut: the list entries any head
-// opened get their rank (in list order) and the next list is their
-// children, rank by rank; when some head's next cut needs scores, the
-// children also go to the flat scoring list of step t+1.  Clears the open
-// masks, and finishes the walks after the last step.
+// Workgroups that build one pair's next list: one per kExpMin entries of
+// its current list, at most kExpSlices.
+__device__ __forceinline__ int expand_slices(int n_u) {
+    const int ns = n_u / kExpMin;
+    return ns < 1 ? 1 : (ns > kExpSlices ? kExpSlices : ns);
+}
+
+// Step t, workgroup s of pair p, after every head's cut: the list entries
+// any head opened get their rank (in list order) and the next list is their
+// children, rank by rank.  Workgroup s takes one slice of the list: it
+// counts the opened entries before its slice (its first rank), ranks its
+// own, writes their children and, when some head's next cut needs scores,
+// appends them to the flat scoring list of step t+1; it also clears the
+// next step's open masks at those positions (the masks alternate between
+// two buffers, as the list lengths do, so no slice reads what another
+// clears).  The last slice sees the whole list: it records the next length
+// and finishes the walks after the last step.
 template <int R>
-__device__ __forceinline__ void expand_pair(const SearchArgs &a, int t, int p, ExpandShared &sh) {
+__device__ __forceinline__ void expand_slice(const SearchArgs &a, int t, int p, int s, ExpandShared &sh) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cap = a.cand_cap, c = a.chunk, log2c = a.log2c;
-    const int n_u = a.u_n[2 * p];
-    const int buf = a.u_n[2 * p + 1];
-    if (n_u <= 0) return;
-    const uint32_t *ids = a.u_ids + (static_cast<int64_t>(p) * 2 + buf) * cap;
-    uint32_t *nids = a.u_ids + (static_cast<int64_t>(p) * 2 + (buf ^ 1)) * cap;
-    uint32_t *om = a.u_omask + static_cast<int64_t>(p) * cap;
+    const int cur = t & 1, nxt = cur ^ 1;
+    const int n_u = a.u_n[2 * p + cur];
+    // at the last level every candidate is a level-1 node: nothing was
+    // marked for opening, only the walks are finished
+    const bool final_step = (t + 1 >= a.levels) || (t + 1 >= ZHA_MAX_STEPS);
+    const int ns = final_step ? 1 : expand_slices(n_u);
+    if (s >= ns) return;
+    const bool keeper = s == ns - 1;
+    if (n_u <= 0) {                                // finished at an earlier step
+        if (keeper && tid == 0) a.u_n[2 * p + nxt] = 0;
+        return;
+    }
+    const uint32_t *ids = a.u_ids + (static_cast<int64_t>(p) * 2 + cur) * cap;
+    uint32_t *nids = a.u_ids + (static_cast<int64_t>(p) * 2 + nxt) * cap;
+    const uint32_t *om = a.u_omask + (static_cast<int64_t>(p) * 2 + cur) * cap;
+    uint32_t *om_next = a.u_omask + (static_cast<int64_t>(p) * 2 + nxt) * cap;
     int32_t *rank = a.u_rank + static_cast<int64_t>(p) * cap;
     uint32_t *par = a.u_par + static_cast<int64_t>(p) * cap;
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-    // at the last level every candidate is a level-1 node, so nothing was
-    // marked for opening and the open masks are still clear
-    const bool final_step = (t + 1 >= a.levels) || (t + 1 >= ZHA_MAX_STEPS);
-    const int seg = ((n_u + kWaves - 1) / kWaves + 63) / 64 * 64;
-    const int s0 = wave * seg, s1 = final_step ? s0 : min(n_u, s0 + seg);
+    const int per = ((n_u + ns - 1) / ns + 63) / 64 * 64;
+    const int i0 = final_step ? 0 : min(n_u, s * per);
+    const int i1 = final_step ? 0 : min(n_u, i0 + per);
+    // opened entries before the slice
+    uint32_t cb = 0;
+    for (int j0 = tid; j0 < i0; j0 += kScanU * kThreads) {
+        uint32_t mv[kScanU];
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+            const int i = j0 + u * kThreads;
+            mv[u] = i < i0 ? om[i] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) cb += mv[u] != 0u;
+    }
+    // ... and in each wavefront's segment of it
+    const int seg = ((i1 - i0 + kWaves - 1) / kWaves + 63) / 64 * 64;
+    const int s0 = min(i1, i0 + wave * seg), s1 = min(i1, s0 + seg);
     uint32_t mine = 0;
     for (int base = s0; base < s1; base += 64 * kScanU) {
         uint32_t mv[kScanU];
@@ -525,13 +563,20 @@ __device__ __forceinline__ void expand_pair(const SearchArgs &a, int t, int p, E
 #pragma unroll
         for (int u = 0; u < kScanU; ++u) mine += __popcll(__ballot(mv[u] != 0u));
     }
-    if (lane == 0) sh.seg_cnt[wave] = mine;
-    __syncthreads();
-    uint32_t before = 0, total = 0;
-    for (int v = 0; v < kWaves; ++v) {
-        if (v < wave) before += sh.seg_cnt[v];
-        total += sh.seg_cnt[v];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cb += __shfl_xor(cb, off, 64);
+    if (lane == 0) {
+        sh.seg_cnt[wave] = mine;
+        sh.pre_cnt[wave] = cb;
     }
+    __syncthreads();
+    uint32_t k0 = 0, before = 0, km = 0;
+    for (int v = 0; v < kWaves; ++v) {
+        k0 += sh.pre_cnt[v];
+        if (v < wave) before += sh.seg_cnt[v];
+        km += sh.seg_cnt[v];
+    }
+    before += k0;
     for (int base = s0; base < s1; base += 64) {
         const int i = base + lane;
         const bool emit = i < s1 && om[i] != 0u;
@@ -543,42 +588,44 @@ __device__ __forceinline__ void expand_pair(const SearchArgs &a, int t, int p, E
         }
         before += __popcll(bal);
     }
-    int64_t n_next = static_cast<int64_t>(total) * c;
-    const bool overflow = n_next > cap;
-    if (overflow) n_next = cap;
-    const bool last = (n_next == 0) || final_step;
+    // this slice's children: ranks k0 .. k0+km-1, positions (k0 + r) * c + e
+    const int64_t total = static_cast<int64_t>(k0) + km;   // the whole list's (last slice only)
+    const int64_t x0 = static_cast<int64_t>(k0) * c;
+    const int64_t x1 = min(static_cast<int64_t>(k0 + km) * c, static_cast<int64_t>(cap));
+    const int cnt = x1 > x0 ? static_cast<int>(x1 - x0) : 0;
     if (tid == 0) {
         bool need = false;
-        for (int hh = 0; hh < a.group && !last; ++hh) {
+        for (int hh = 0; hh < a.group && !final_step && cnt > 0; ++hh) {
             const int64_t nh = static_cast<int64_t>(a.u_next[head_walk(a, p, hh)]) * c;
             if (nh > 0 && !step_forced(a, t + 1, static_cast<int>(nh < cap ? nh : cap))) need = true;
         }
         sh.need = need ? 1 : 0;
-        sh.flat_base = need ? atomicAdd(&a.tile_count[t + 1], round_flat(static_cast<int>(n_next))) : 0;
+        sh.flat_base = need ? atomicAdd(&a.tile_count[t + 1], round_flat(cnt)) : 0;
     }
     __syncthreads();                               // par[] and the flat base are ready
-    if (!last) {
+    if (!final_step && cnt > 0) {
         const bool need = sh.need != 0;
         const int fbase = sh.flat_base;
         int4 *flat = a.u_flat + ((t + 1) & 1) * a.flat_cap;
-        const int nn = static_cast<int>(n_next);
-        const int padded = need ? round_flat(nn) : nn;
+        const int padded = need ? round_flat(cnt) : cnt;
         for (int x = tid; x < padded; x += kThreads) {
-            const int xr = x < nn ? x : 0;
+            const int64_t xr = x0 + (x < cnt ? x : 0);
             const uint32_t pid = par[xr >> log2c];
             const uint32_t lvl = pid >> kLevelShift, j = pid & kIndexMask;
             const uint32_t child = ((lvl - 1u) << kLevelShift) | (j * static_cast<uint32_t>(c) + (xr & (c - 1)));
-            if (x < nn) nids[x] = child;
-            if (need) flat[fbase + x] = make_int4(p, x < nn ? x : -1, static_cast<int>(child), 0);
+            if (x < cnt) {
+                nids[xr] = child;
+                om_next[xr] = 0u;
+            }
+            if (need) flat[fbase + x] = make_int4(p, x < cnt ? static_cast<int>(xr) : -1, static_cast<int>(child), 0);
         }
-        // clear the open masks for the next step
-        const int clear = nn > n_u ? nn : n_u;
-        for (int i = tid; i < clear; i += kThreads) om[i] = 0;
     }
-    if (tid == 0) {
-        a.u_n[2 * p] = last ? 0 : static_cast<int32_t>(n_next);
-        a.u_n[2 * p + 1] = buf ^ 1;
-    }
+    if (!keeper) return;
+    int64_t n_next = total * c;
+    const bool overflow = n_next > cap;
+    if (overflow) n_next = cap;
+    const bool last = (n_next == 0) || final_step;
+    if (tid == 0) a.u_n[2 * p + nxt] = last ? 0 : static_cast<int32_t>(n_next);
     if (tid < a.group) {
         const int w = head_walk(a, p, tid);
         WalkState *st = a.state + w;
@@ -595,17 +642,17 @@ __global__ __launch_bounds__(kThreads) void k_un_cut(SearchArgs a, int t) {
     __shared__ float s_sc[kLdsCand];
     __shared__ int32_t s_par[kLdsPar];
     const int w = blockIdx.x;
-    if (a.u_n[2 * (w / a.group)] <= 0) return;     // the pair has finished (all its heads)
+    if (a.u_n[2 * (w / a.group) + (t & 1)] <= 0) return;   // the pair has finished (all its heads)
     cut_head<R>(a, t, w, sh, s_one, s_high, s_sc, s_par);
 }
 
-// Step t, one workgroup per pair, after every head's cut (a kernel boundary:
-// a device-wide fence inside one kernel costs far more on this GPU, whose
-// L2 caches are per XCD): the pair's next list (expand_pair).
+// Step t, kExpSlices workgroups per pair, after every head's cut (a kernel
+// boundary: a device-wide fence inside one kernel costs far more on this
+// GPU, whose L2 caches are per XCD): the pair's next list (expand_slice).
 template <int R>
 __global__ __launch_bounds__(kThreads) void k_un_expand(SearchArgs a, int t) {
     __shared__ ExpandShared sh;
-    expand_pair<R>(a, t, blockIdx.x, sh);
+    expand_slice<R>(a, t, blockIdx.x / kExpSlices, blockIdx.x % kExpSlices, sh);
 }
 
 // Workgroups of the scorer that fit on the device at once (its wavefronts
@@ -643,7 +690,7 @@ static hipError_t launch_union_t(const SearchArgs &a, int n0, hipStream_t st) {
         }
         hipLaunchKernelGGL((k_un_cut<R>), dim3(a.pairs * a.group), dim3(kThreads), 0, st, a, t);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((k_un_expand<R>), dim3(a.pairs), dim3(kThreads), 0, st, a, t);
+        hipLaunchKernelGGL((k_un_expand<R>), dim3(a.pairs * kExpSlices), dim3(kThreads), 0, st, a, t);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
