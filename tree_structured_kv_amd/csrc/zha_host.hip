@@ -331,6 +331,22 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
     a.n_roots = n0;
     if (n0 > a.cand_cap) n0 = a.cand_cap;
     const int engine = resolve_engine(t, sel, qph);
+    // union engine: the first steps whose pair lists cannot exceed
+    // kSmallList nodes run in one launch; a root at level l adds at most
+    // c^s nodes to the list of step s < l
+    a.small_steps = 0;
+    if (engine == ZHA_ENGINE_UNION) {
+        for (int s = 0; s < g.levels && s < ZHA_MAX_STEPS; ++s) {
+            double bound = 0.0, cs = 1.0;
+            for (int i = 0; i < s; ++i) cs *= g.chunk;
+            for (int l = s + 1; l <= g.levels; ++l) {
+                const int64_t roots = (l == g.levels) ? a.nl[l] : a.nl[l] - int64_t(g.chunk) * a.nl[l + 1];
+                bound += static_cast<double>(roots) * cs;
+            }
+            if (bound > kSmallList) break;
+            a.small_steps = s + 1;
+        }
+    }
     if (engine == ZHA_ENGINE_BLOCK)
         return hip_status(launch_block(a, g.head_dim, g.num_refs, g.dtype, g.summary_dtype, static_cast<int>(n0), st));
     if (engine == ZHA_ENGINE_UNION)

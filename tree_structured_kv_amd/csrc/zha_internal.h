@@ -17,6 +17,7 @@ constexpr int kChunkKeys = 1024;     // keys per attention work item
 constexpr int kTile = 32;            // candidates per tile of the level-synchronous scorer
 constexpr int kFlatPad = 32;         // union engine: each run of scoring entries is padded to this
 constexpr int kExpSlices = 8;        // union engine: workgroups (runs) per pair building the next list
+constexpr int kSmallList = 64;       // union engine: list bound of the steps fused into one launch
 
 // Per-walk state of the level-synchronous search engine (workspace).
 struct WalkState {
@@ -93,6 +94,7 @@ struct SearchArgs {
     int64_t bin_lvl[ZHA_MAX_LEVELS + 2];   // first bin of level l within a pair
     int32_t pcap;                          // parents a walk keeps per step
     int64_t n_roots;                       // roots before clamping to cand_cap
+    int32_t small_steps;                   // union engine: first steps done by one workgroup per pair
     int32_t pairs;
     int64_t n_tokens;
     int32_t walks;

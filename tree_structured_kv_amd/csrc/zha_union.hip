@@ -54,6 +54,8 @@ constexpr int kUG = 2;                // matrix tiles in flight per wavefront
 constexpr int kLdsCand = 14336;       // candidate scores a cut stages in LDS (56 KB)
 constexpr int kLdsPar = 2048;         // parent ranks a cut stages in LDS (8 KB)
 constexpr int kExpMin = 256;          // list entries per expand workgroup (at least)
+constexpr int kWaveCand = 480;        // candidates a wavefront cut stages in LDS
+static_assert(kSmallList <= kWaveCand, "a fused step's candidates fit in LDS");
 
 __device__ __forceinline__ int head_walk(const SearchArgs &a, int pair, int h) {
     const int b = pair / a.kv_heads, g = pair % a.kv_heads;
@@ -113,6 +115,21 @@ __global__ __launch_bounds__(512) void k_un_init(SearchArgs a) {
     }
 }
 
+// Level bases of the node records, staged in LDS: a block may mix levels.
+struct LevelTables {
+    const float *kap[ZHA_MAX_LEVELS + 1];
+    const float *bet[ZHA_MAX_LEVELS + 1];
+    int64_t cap[ZHA_MAX_LEVELS + 1];
+};
+
+__device__ __forceinline__ void load_tables(const SearchArgs &a, LevelTables &tb) {
+    if (threadIdx.x <= ZHA_MAX_LEVELS) {
+        tb.kap[threadIdx.x] = a.kap[threadIdx.x];
+        tb.bet[threadIdx.x] = a.bet[threadIdx.x];
+        tb.cap[threadIdx.x] = a.cap[threadIdx.x];
+    }
+}
+
 // Step t scoring.  The flat list holds, pair after pair, one entry per node
 // of the pair's union list, each pair's run padded to a multiple of
 // kFlatPad (pad entries repeat a real node and store nothing); at t = 0 the
@@ -125,47 +142,23 @@ __global__ __launch_bounds__(512) void k_un_init(SearchArgs a) {
 // k%4 of the query and of the reference row (one permutation of D for both
 // operands), so one 16-byte load of the four lanes of a column reads 64
 // contiguous bytes of its row.
-template <int D, int R, typename QT, typename ST>
-__global__ __launch_bounds__(kScoreThreads) void k_un_score(SearchArgs a, int t, int n0) {
+//
+// score_run: one wavefront scores blocks b0 .. b1-1 (WB = NPG*kUG entries
+// each) of a list whose entry e is entry(e) = {pair, list position (-1:
+// pad), node id}; scores go to u_score.
+template <int D, int R, typename QT, typename ST, typename Entry>
+__device__ __forceinline__ void score_run(const SearchArgs &a, const LevelTables &tb, Entry entry, int b0, int b1) {
     constexpr int NPG = 16 / R;           // nodes per matrix tile
     constexpr int KS = D / 4;             // 16x16x4 steps
-    constexpr int kSW = kScoreThreads / 64;
     constexpr int WB = NPG * kUG;         // nodes per block
-    static_assert(kFlatPad % WB == 0, "a block must not straddle two pairs");
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int col = lane & 15, grp = lane >> 4;
-    // per-level bases, looked up per lane (a block may mix levels)
-    __shared__ const float *s_kap[ZHA_MAX_LEVELS + 1];
-    __shared__ const float *s_bet[ZHA_MAX_LEVELS + 1];
-    __shared__ int64_t s_cap[ZHA_MAX_LEVELS + 1];
-    if (threadIdx.x <= ZHA_MAX_LEVELS) {
-        s_kap[threadIdx.x] = a.kap[threadIdx.x];
-        s_bet[threadIdx.x] = a.bet[threadIdx.x];
-        s_cap[threadIdx.x] = a.cap[threadIdx.x];
-    }
-    __syncthreads();
-    const int n0p = round_flat(n0);
-    const int n_flat = (t == 0) ? a.pairs * n0p : a.tile_count[t];
-    const int nb = n_flat / WB;
-    const int nw = gridDim.x * kSW;
-    const int per = (nb + nw - 1) / nw;
-    const int b0 = (blockIdx.x * kSW + wave) * per;
-    const int b1 = min(nb, b0 + per);
+    const float *const *s_kap = tb.kap;
+    const float *const *s_bet = tb.bet;
+    const int64_t *s_cap = tb.cap;
     if (b0 >= b1) return;
     const float s = a.sharpness;
     const int gp = (a.group + 3) & ~3;    // heads per score row (padded)
-    const int4 *flat = a.u_flat + (t & 1) * a.flat_cap;
-
-    // entry of flat position e: {pair, list position (-1: pad), node id}
-    auto entry = [&](int e) -> int4 {
-        if (t == 0) {
-            const int p = e / n0p, pos = e - p * n0p;
-            const uint32_t *ids = a.u_ids + static_cast<int64_t>(p) * 2 * a.cand_cap;
-            const uint32_t id = ids[pos < n0 ? pos : n0 - 1];
-            return make_int4(p, pos < n0 ? pos : -1, static_cast<int>(id), 0);
-        }
-        return flat[e];
-    };
 
     int4 nxt[kUG];
 #pragma unroll
@@ -300,6 +293,37 @@ __global__ __launch_bounds__(kScoreThreads) void k_un_score(SearchArgs a, int t,
             }
         }
     }
+}
+
+template <int D, int R, typename QT, typename ST>
+__global__ __launch_bounds__(kScoreThreads) void k_un_score(SearchArgs a, int t, int n0) {
+    constexpr int WB = (16 / R) * kUG;    // nodes per block
+    constexpr int kSW = kScoreThreads / 64;
+    static_assert(kFlatPad % WB == 0, "a block must not straddle two pairs");
+    const int wave = threadIdx.x >> 6;
+    __shared__ LevelTables tb;
+    load_tables(a, tb);
+    __syncthreads();
+    const int n0p = round_flat(n0);
+    const int n_flat = (t == 0) ? a.pairs * n0p : a.tile_count[t];
+    const int nb = n_flat / WB;
+    const int nw = gridDim.x * kSW;
+    const int per = (nb + nw - 1) / nw;
+    const int b0 = (blockIdx.x * kSW + wave) * per;
+    const int b1 = min(nb, b0 + per);
+    const int4 *flat = a.u_flat + (t & 1) * a.flat_cap;
+    // entry of flat position e: at t = 0 the roots of every pair, each
+    // pair's run padded to a multiple of kFlatPad
+    auto entry = [&](int e) -> int4 {
+        if (t == 0) {
+            const int p = e / n0p, pos = e - p * n0p;
+            const uint32_t *ids = a.u_ids + static_cast<int64_t>(p) * 2 * a.cand_cap;
+            const uint32_t id = ids[pos < n0 ? pos : n0 - 1];
+            return make_int4(p, pos < n0 ? pos : -1, static_cast<int>(id), 0);
+        }
+        return flat[e];
+    };
+    score_run<D, R, QT, ST>(a, tb, entry, b0, b1);
 }
 
 // Step t, one workgroup per walk (head h of pair p).  The head's candidates
@@ -493,6 +517,230 @@ __device__ __forceinline__ void cut_head(const SearchArgs &a, int t, int w, Sele
     }
 }
 
+// Per-wavefront LDS of the fused first steps (k_un_small): a histogram of
+// 8-bit key digits, each bin holding (count << 48) + weight, and the head's
+// candidates (score, id, list position) when they fit.
+struct WaveCutShared {
+    unsigned long long hist[256];
+    float sc[kWaveCand];
+    uint32_t id[kWaveCand];
+    int32_t pos[kWaveCand];
+};
+
+constexpr int kCountShift = 48;       // weights of a list stay below 2^48 (at most 2^17 x 2^31)
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long o = __shfl_xor(v, off, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Wavefront: the cut key of cut_tau -- the rank key of the candidate at
+// which the weight summed in decreasing key order first reaches what the
+// step needs (weights and need exactly as there) -- by an 8-bit radix
+// select over the 64-bit keys with the histogram in the wavefront's LDS.
+// Candidates i < n have scores vs[i] and ids is[i].
+__device__ unsigned long long wave_tau(const SearchArgs &a, int n, const uint32_t *is, const float *vs, float mx,
+                                       int kt, WaveCutShared &L) {
+    const int lane = threadIdx.x & 63;
+    const int log2c = a.log2c;
+    const bool by_mass = (a.mode == ZHA_TOPP) && (a.p > 0.f);
+    const bool flat = !(mx > -INFINITY);   // every score -inf: equal masses
+    auto weight = [&](float v) -> unsigned long long {
+        if (!by_mass) return 1ull;
+        const float e = flat ? 1.f : expf(v - mx);
+        return static_cast<unsigned long long>(__float2uint_rn(e * kMassScale));
+    };
+    unsigned long long need;
+    if (by_mass) {
+        unsigned long long zp = 0;
+        for (int i = lane; i < n; i += 64) zp += weight(vs[i]);
+        const unsigned long long z = wave_sum_u64(zp);
+        const double tq = ceil(static_cast<double>(a.p) * static_cast<double>(z));
+        need = static_cast<unsigned long long>(tq);
+        if (need < 1) need = 1;
+        if (need > z) need = z;
+    } else {
+        const int m = (a.mode == ZHA_TOPK) ? (kt < n ? kt : n) : 1;
+        need = static_cast<unsigned long long>(m < 1 ? 1 : m);
+    }
+    const unsigned long long wmask = (1ull << kCountShift) - 1ull;
+    unsigned long long prefix = 0, tau = 0;
+    for (int pass = 0; pass < 8; ++pass) {
+        const int shift = 56 - 8 * pass;
+        for (int b = lane; b < 256; b += 64) L.hist[b] = 0;
+        __builtin_amdgcn_wave_barrier();
+        for (int i = lane; i < n; i += 64) {
+            const float v = vs[i];
+            const unsigned long long key = rank_key(v, is[i], log2c);
+            if (pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8)))
+                atomicAdd(&L.hist[static_cast<uint32_t>(key >> shift) & 255u], (1ull << kCountShift) + weight(v));
+        }
+        __builtin_amdgcn_wave_barrier();
+        // lane covers digits 255-4*lane .. 252-4*lane (descending)
+        unsigned long long lw[4], lsum = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { lw[e] = L.hist[255 - 4 * lane - e] & wmask; lsum += lw[e]; }
+        unsigned long long incl = lsum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const unsigned long long o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
+        }
+        const unsigned long long excl = incl - lsum;
+        const unsigned long long reach = __ballot(incl >= need);
+        const int first = reach ? (__ffsll(static_cast<long long>(reach)) - 1) : 63;
+        unsigned long long run = excl;
+        int pick = 3;
+        for (int e = 0; e < 4; ++e) {
+            if (run + lw[e] >= need) { pick = e; break; }
+            run += lw[e];
+        }
+        if (!reach) { pick = 3; run = excl + lw[0] + lw[1] + lw[2]; }
+        const uint32_t dig = static_cast<uint32_t>(__shfl(static_cast<int>(255 - 4 * lane - pick), first, 64));
+        const unsigned long long above = __shfl(run, first, 64);
+        const unsigned long long cnt = L.hist[dig] >> kCountShift;
+        __builtin_amdgcn_wave_barrier();
+        prefix |= static_cast<unsigned long long>(dig) << shift;
+        need -= above;
+        if (pass == 7) {
+            tau = prefix;
+            break;
+        }
+        if (cnt <= 1) {
+            // at most one key carries this prefix: fetch it
+            unsigned long long found = 0;
+            for (int i = lane; i < n; i += 64) {
+                const unsigned long long key = rank_key(vs[i], is[i], log2c);
+                if ((key >> shift) == (prefix >> shift)) found = key;
+            }
+            found = wave_max_u64(found);
+            tau = (cnt == 0) ? 0ull : found;
+            break;
+        }
+    }
+    return tau;
+}
+
+// Step t for walk w (head h of pair p), on one wavefront: the same result as
+// cut_head -- candidates, exact cut, level-1 selections in span order,
+// opened higher nodes (list positions, in order) with head bit h on them,
+// and the walk's statistics.
+template <int R>
+__device__ void cut_wave(const SearchArgs &a, int t, int w, WaveCutShared &L) {
+    const int lane = threadIdx.x & 63;
+    const int p = w / a.group, h = w % a.group;
+    const uint32_t bit = 1u << h;
+    const int cap = a.cand_cap, log2c = a.log2c, c = a.chunk;
+    const int buf = t & 1;
+    const int n_u = a.u_n[2 * p + buf];
+    if (n_u <= 0) return;                          // the pair has finished
+    const int n_open_prev = (t == 0) ? 0 : a.u_next[w];
+    if (t > 0 && n_open_prev == 0) return;         // this head opened nothing more
+    WalkState *st = a.state + w;
+    const uint32_t *ids = a.u_ids + (static_cast<int64_t>(p) * 2 + buf) * cap;
+    const int gp = (a.group + 3) & ~3;
+    const float *sc = a.u_score + static_cast<int64_t>(p) * cap * gp + h;   // score of position i: sc[i * gp]
+    const int32_t *rank = a.u_rank + static_cast<int64_t>(p) * cap;
+    uint32_t *om = a.u_omask + (static_cast<int64_t>(p) * 2 + buf) * cap;
+    int32_t *opened_pos = a.u_open + static_cast<int64_t>(w) * cap;
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    const int64_t raw64 = (t == 0) ? n_u : static_cast<int64_t>(n_open_prev) * c;
+    const int raw = static_cast<int>(raw64 < cap ? raw64 : cap);
+    auto position = [&](int x) -> int {
+        if (t == 0) return x;
+        return rank[opened_pos[x >> log2c]] * c + (x & (c - 1));
+    };
+    // the candidates inside the list: a prefix of length cnt
+    int valid = 0;
+    for (int x = lane; x < raw; x += 64) valid += position(x) < n_u;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) valid += __shfl_xor(valid, off, 64);
+    if (valid == 0) {
+        if (lane == 0) a.u_next[w] = 0;
+        return;
+    }
+    // the lists of the fused steps are at most kSmallList long (a bound the
+    // host derives from the tree); a longer one marks the walk
+    int cnt = valid;
+    if (cnt > kWaveCand) {
+        if (lane == 0) atomicOr(&st->flags, ZHA_FLAG_CAND_OVERFLOW);
+        cnt = kWaveCand;
+    }
+    const bool forced = step_forced(a, t, cnt);
+    // stage (score, id, position) in LDS
+    float *vs = L.sc;
+    uint32_t *is = L.id;
+    int32_t *ps = L.pos;
+    float m = -INFINITY;
+    for (int x = lane; x < cnt; x += 64) {
+        const int pos = position(x);
+        ps[x] = pos;
+        is[x] = ids[pos];
+        if (!forced) {
+            // another wavefront of this workgroup wrote it: read past L1
+            const float v = __hip_atomic_load(sc + static_cast<int64_t>(pos) * gp, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+            vs[x] = v;
+            m = fmaxf(m, v);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    unsigned long long tau = 0;
+    if (!forced) tau = wave_tau(a, cnt, is, vs, wave_max(m, 1, 64), a.k[t], L);
+
+    // open, in candidate order
+    const int64_t sel0 = st->sel_n;
+    int32_t *selw = a.sel_blocks + static_cast<int64_t>(w) * a.sel_cap;
+    uint32_t pre1 = 0, preh = 0, nopen = 0;
+    for (int base = 0; base < cnt; base += 64) {
+        const int x = base + lane;
+        const bool in = x < cnt;
+        const uint32_t id = in ? is[x] : 0u;
+        const bool op = in && (forced || rank_key(vs[x], id, log2c) >= tau);
+        const bool l1 = op && (id >> kLevelShift) == 1u;
+        const bool hi = op && (id >> kLevelShift) > 1u;
+        const unsigned long long m1 = __ballot(l1);
+        const unsigned long long mh = __ballot(hi);
+        if (l1) {
+            const int64_t pos = sel0 + pre1 + __popcll(m1 & below);
+            if (pos < a.sel_cap) selw[pos] = static_cast<int32_t>(id & kIndexMask);
+        }
+        if (hi) {
+            const int i = ps[x];
+            opened_pos[preh + __popcll(mh & below)] = i;
+            atomicOr(&om[i], bit);
+        }
+        pre1 += __popcll(m1);
+        preh += __popcll(mh);
+        nopen += __popcll(__ballot(op));
+    }
+    if (lane == 0) {
+        st->scored[t] = cnt;
+        st->opened[t] = static_cast<int32_t>(nopen);
+        if (!forced) st->unforced += cnt;
+        st->sel_n = static_cast<int32_t>(sel0 + pre1);
+        st->steps = t + 1;
+        a.u_next[w] = static_cast<int32_t>(preh);
+    }
+}
+
+// An open mask: set by atomics, so read past L1 (a kernel that cuts and
+// expands in one workgroup may hold a stale line of it there).
+__device__ __forceinline__ uint32_t load_mask(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Workgroups that build one pair's next list: one per kExpMin entries of
 // its current list, at most kExpSlices.
 __device__ __forceinline__ int expand_slices(int n_u) {
@@ -509,9 +757,11 @@ __device__ __forceinline__ int expand_slices(int n_u) {
 // next step's open masks at those positions (the masks alternate between
 // two buffers, as the list lengths do, so no slice reads what another
 // clears).  The last slice sees the whole list: it records the next length
-// and finishes the walks after the last step.
+// and finishes the walks after the last step.  Without emit_flat no flat
+// entries are written (the next step is not scored from the flat list).
 template <int R>
-__device__ __forceinline__ void expand_slice(const SearchArgs &a, int t, int p, int s, ExpandShared &sh) {
+__device__ __forceinline__ void expand_slice(const SearchArgs &a, int t, int p, int s, ExpandShared &sh,
+                                             bool emit_flat = true) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cap = a.cand_cap, c = a.chunk, log2c = a.log2c;
     const int cur = t & 1, nxt = cur ^ 1;
@@ -544,7 +794,7 @@ __device__ __forceinline__ void expand_slice(const SearchArgs &a, int t, int p, 
 #pragma unroll
         for (int u = 0; u < kScanU; ++u) {
             const int i = j0 + u * kThreads;
-            mv[u] = i < i0 ? om[i] : 0u;
+            mv[u] = i < i0 ? load_mask(om + i) : 0u;
         }
 #pragma unroll
         for (int u = 0; u < kScanU; ++u) cb += mv[u] != 0u;
@@ -558,7 +808,7 @@ __device__ __forceinline__ void expand_slice(const SearchArgs &a, int t, int p, 
 #pragma unroll
         for (int u = 0; u < kScanU; ++u) {
             const int i = base + 64 * u + lane;
-            mv[u] = i < s1 ? om[i] : 0u;
+            mv[u] = i < s1 ? load_mask(om + i) : 0u;
         }
 #pragma unroll
         for (int u = 0; u < kScanU; ++u) mine += __popcll(__ballot(mv[u] != 0u));
@@ -579,7 +829,7 @@ __device__ __forceinline__ void expand_slice(const SearchArgs &a, int t, int p, 
     before += k0;
     for (int base = s0; base < s1; base += 64) {
         const int i = base + lane;
-        const bool emit = i < s1 && om[i] != 0u;
+        const bool emit = i < s1 && load_mask(om + i) != 0u;
         const unsigned long long bal = __ballot(emit);
         if (emit) {
             const uint32_t k = before + __popcll(bal & below);
@@ -595,7 +845,7 @@ __device__ __forceinline__ void expand_slice(const SearchArgs &a, int t, int p, 
     const int cnt = x1 > x0 ? static_cast<int>(x1 - x0) : 0;
     if (tid == 0) {
         bool need = false;
-        for (int hh = 0; hh < a.group && !final_step && cnt > 0; ++hh) {
+        for (int hh = 0; hh < a.group && emit_flat && !final_step && cnt > 0; ++hh) {
             const int64_t nh = static_cast<int64_t>(a.u_next[head_walk(a, p, hh)]) * c;
             if (nh > 0 && !step_forced(a, t + 1, static_cast<int>(nh < cap ? nh : cap))) need = true;
         }
@@ -655,6 +905,64 @@ __global__ __launch_bounds__(kThreads) void k_un_expand(SearchArgs a, int t) {
     expand_slice<R>(a, t, blockIdx.x / kExpSlices, blockIdx.x % kExpSlices, sh);
 }
 
+// The first `steps` steps of every pair in one launch, one workgroup per
+// pair (while the lists are short, a launch per kernel and step costs more
+// than the work): per step the pair's whole list is scored (when some head
+// needs scores), each head's cut runs on one wavefront (cut_wave), and the
+// workgroup builds the next list (expand_slice, every slice in turn),
+// including the flat scoring list of the first step the grid-wide kernels
+// take over.
+template <int D, int R, typename QT, typename ST>
+__global__ __launch_bounds__(kThreads) void k_un_small(SearchArgs a, int steps) {
+    constexpr int WB = (16 / R) * kUG;    // nodes per scoring block
+    const int p = blockIdx.x, wave = threadIdx.x >> 6;
+    const int cap = a.cand_cap, c = a.chunk;
+    __shared__ LevelTables tb;
+    __shared__ WaveCutShared wc[kWaves];
+    __shared__ ExpandShared esh;
+    __shared__ int s_need;
+    load_tables(a, tb);
+    for (int t = 0; t < steps; ++t) {
+        const int buf = t & 1;
+        // does some head's cut need scores?  (one thread per head)
+        if (threadIdx.x == 0) s_need = 0;
+        const int n_u = a.u_n[2 * p + buf];
+        __syncthreads();
+        if (n_u > 0 && threadIdx.x < a.group) {
+            bool need;
+            if (t == 0) {
+                need = !step_forced(a, 0, n_u);
+            } else {
+                const int64_t nh = static_cast<int64_t>(a.u_next[head_walk(a, p, threadIdx.x)]) * c;
+                need = nh > 0 && !step_forced(a, t, static_cast<int>(nh < cap ? nh : cap));
+            }
+            if (need) s_need = 1;
+        }
+        __syncthreads();
+        if (s_need) {
+            const uint32_t *ids = a.u_ids + (static_cast<int64_t>(p) * 2 + buf) * cap;
+            const int nb = (n_u + WB - 1) / WB;
+            const int per = (nb + kWaves - 1) / kWaves;
+            const int b0 = wave * per, b1 = min(nb, b0 + per);
+            auto entry = [&](int e) -> int4 {
+                const int pos = e < n_u ? e : n_u - 1;
+                return make_int4(p, e < n_u ? e : -1, static_cast<int>(ids[pos]), 0);
+            };
+            score_run<D, R, QT, ST>(a, tb, entry, b0, b1);
+        }
+        __syncthreads();
+        for (int h = wave; h < a.group; h += kWaves) cut_wave<R>(a, t, head_walk(a, p, h), wc[wave]);
+        __syncthreads();
+        // only the hand-over step is scored from the flat list: pairs run
+        // at their own pace, so an earlier step's entries (same buffer
+        // parity) could overwrite another pair's
+        for (int sl = 0; sl < kExpSlices; ++sl) {
+            expand_slice<R>(a, t, p, sl, esh, t + 1 == steps);
+            __syncthreads();
+        }
+    }
+}
+
 // Workgroups of the scorer that fit on the device at once (its wavefronts
 // take equal runs of blocks, so all of them should be resident), per device.
 template <typename K>
@@ -680,7 +988,12 @@ static hipError_t launch_union_t(const SearchArgs &a, int n0, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int score_grid = resident_grid(k_un_score<D, R, QT, ST>, kScoreThreads);
-    for (int t = 0; t < a.levels && t < ZHA_MAX_STEPS; ++t) {
+    const int t0 = a.small_steps;
+    if (t0 > 0) {
+        hipLaunchKernelGGL((k_un_small<D, R, QT, ST>), dim3(a.pairs), dim3(kThreads), 0, st, a, t0);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    for (int t = t0; t < a.levels && t < ZHA_MAX_STEPS; ++t) {
         const bool skip = (t == 0) && (n0 <= 1 || (a.mode == ZHA_TOPK && a.k[0] >= n0) ||
                                        (a.mode == ZHA_TOPP && a.p >= 1.0f));
         if (!skip) {
