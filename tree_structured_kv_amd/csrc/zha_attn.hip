@@ -9,7 +9,10 @@
 //
 // GPU design.  Walks select very different numbers of keys under top-p, so
 // the work is planned on the device: k_attn_plan cuts every walk's key list
-// into chunks of kChunkKeys and lays the (walk, chunk) items out flat;
+// into chunks and lays the (walk, chunk) items out flat (512 keys per item
+// when the call reads under 2M keys in all, so that long walks spread over
+// more workgroups, 2048 from 8M on, where fewer, longer items stream
+// better, else 1024);
 // k_attn_partial is a grid-stride loop over the items, so every workgroup
 // streams about the same number of bytes whatever the spread between walks.
 // A key row is D*e bytes read as 16-byte pieces by D*e/16 lanes.  The online
@@ -57,20 +60,36 @@ __device__ __forceinline__ int64_t walk_keys(const AttnArgs &a, int w) {
 
 }  // namespace
 
-// One workgroup: item offsets = exclusive scan of max(1, ceil(keys / chunk))
-// over walks, and the walk id of every item.
+// One workgroup: the keys per item (from the call's total), item offsets =
+// exclusive scan of max(1, ceil(keys / item keys)) over walks, and the walk
+// id of every item.
 __global__ __launch_bounds__(1024) void k_attn_plan(AttnArgs a) {
     __shared__ int32_t wsum[16];
     __shared__ int32_t carry;
+    __shared__ unsigned long long ksum[16];
+    __shared__ int32_t s_ck;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    unsigned long long mine = 0;
+    for (int w = tid; w < a.walks; w += 1024) mine += static_cast<unsigned long long>(walk_keys(a, w));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mine += __shfl_xor(mine, off, 64);
+    if (lane == 0) ksum[wave] = mine;
     if (tid == 0) carry = 0;
     __syncthreads();
+    if (tid == 0) {
+        unsigned long long tot = 0;
+        for (int i = 0; i < 16; ++i) tot += ksum[i];
+        s_ck = tot < (2ull << 20) ? kChunkMin : (tot < (8ull << 20) ? 1024 : kChunkMax);
+        a.item_off[a.walks + 1] = s_ck;
+    }
+    __syncthreads();
+    const int ck = s_ck;
     for (int base = 0; base < a.walks; base += 1024) {
         const int w = base + tid;
         int32_t cnt = 0;
         if (w < a.walks) {
             const int64_t keys = walk_keys(a, w);
-            cnt = static_cast<int32_t>((keys + kChunkKeys - 1) / kChunkKeys);
+            cnt = static_cast<int32_t>((keys + ck - 1) / ck);
             if (a.block_mfma) ++cnt;                 // the last item: the block's own keys
             if (cnt < 1) cnt = 1;
         }
@@ -107,7 +126,9 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
     const int c = a.chunk;
     const float s = a.sharpness;
     const int32_t n_items = a.item_off[a.walks];
+    const int ck = a.item_off[a.walks + 1];     // keys per item (at most kChunkMax)
     __shared__ float sm[kWaves], sl[kWaves], sacc[kWaves][D];
+    __shared__ int32_t s_ids[kChunkMax + 1];    // the item's block (or token) ids
 
     for (int32_t item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int w = a.item_walk[item];
@@ -118,8 +139,8 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
         const int64_t body = a.tokens ? nb : nb * c;
         const int64_t tree_keys = a.tokens ? nb : body + (a.n_tokens - static_cast<int64_t>(c) * a.n1);
         const int64_t total = walk_keys(a, w);
-        const int64_t k0 = chunk * kChunkKeys;
-        const int64_t k1 = (k0 + kChunkKeys < total) ? k0 + kChunkKeys : total;
+        const int64_t k0 = chunk * ck;
+        const int64_t k1 = (k0 + ck < total) ? k0 + ck : total;
 
         float qv[EPL];
         {
@@ -130,6 +151,13 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
         const KT *vb = static_cast<const KT *>(a.v) + pair * a.max_tokens * D;
         const int32_t *selw = (a.tokens ? a.tokens : a.sel_blocks) + static_cast<int64_t>(w) * a.sel_cap;
         const int64_t tail0 = static_cast<int64_t>(c) * a.n1;
+        // the ids this item reads, staged once (the key loop then needs no
+        // dependent global load): entries e0 .. e1-1 of the walk's list
+        const int64_t kb1 = (k1 < body) ? k1 : body;
+        const int64_t e0 = a.tokens ? k0 : k0 / c;
+        const int64_t e1 = (kb1 <= k0) ? e0 : (a.tokens ? kb1 : (kb1 + c - 1) / c);
+        for (int64_t i = tid; i < e1 - e0; i += kBlock) s_ids[i] = selw[e0 + i];
+        __syncthreads();
 
         float m = -INFINITY, l = 0.f, acc[EPL];
         for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
@@ -147,11 +175,11 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
                     if (ki >= tree_keys) {
                         tok = a.n_tokens + (ki - tree_keys);   // the block's own keys (causal)
                     } else if (a.tokens) {
-                        const int64_t tk = selw[ki];
+                        const int64_t tk = s_ids[ki - e0];
                         ok[u] = tk >= 0 && tk < a.n_tokens;   // ids outside the cache are skipped
                         tok = ok[u] ? tk : 0;
                     } else if (ki < body) {
-                        const int64_t blk = selw[ki / c];
+                        const int64_t blk = s_ids[ki / c - e0];
                         ok[u] = blk >= 0 && blk < a.n1;    // ids outside the live level are skipped
                         tok = ok[u] ? blk * c + (ki % c) : 0;
                     } else {

@@ -143,9 +143,9 @@ SearchWs search_ws_layout(const zha_tree *t, const zha_select *sel, int32_t qph)
 }
 
 // Attention work items of a call: each walk's keys (at most keys_bound)
-// cut into chunks of kChunkKeys, at least one item per walk.
+// cut into chunks of at least kChunkMin keys, at least one item per walk.
 int64_t attn_max_items(int64_t keys_bound, int64_t walks) {
-    int64_t per = (keys_bound + kChunkKeys - 1) / kChunkKeys;
+    int64_t per = (keys_bound + kChunkMin - 1) / kChunkMin;
     if (per < 1) per = 1;
     return walks * (per + 1);     // + the block-keys item of a prefill walk
 }
@@ -162,7 +162,7 @@ AttnWs attn_ws_layout(int head_dim, int64_t keys_bound, int64_t walks) {
     AttnWs l;
     l.part = 0;
     l.item_off = align_up(items * (head_dim + 2) * sizeof(float));
-    l.item_walk = l.item_off + align_up(uint64_t(walks + 1) * sizeof(int32_t));
+    l.item_walk = l.item_off + align_up(uint64_t(walks + 2) * sizeof(int32_t));
     l.total = l.item_walk + align_up(items * sizeof(int32_t));
     return l;
 }

@@ -13,7 +13,8 @@ namespace zha {
 constexpr int kLevelShift = 28;
 constexpr uint32_t kIndexMask = (1u << kLevelShift) - 1u;
 constexpr int kBlock = 256;          // threads per workgroup of most kernels
-constexpr int kChunkKeys = 1024;     // keys per attention work item
+constexpr int kChunkMin = 512;       // keys per attention work item: the planner picks 512 .. 2048
+constexpr int kChunkMax = 2048;      // (more, smaller items when a call reads few keys)
 constexpr int kTile = 32;            // candidates per tile of the level-synchronous scorer
 constexpr int kFlatPad = 32;         // union engine: each run of scoring entries is padded to this
 constexpr int kExpSlices = 8;        // union engine: workgroups (runs) per pair building the next list
@@ -123,7 +124,7 @@ struct AttnArgs {
     const int32_t *tokens;         // [walks][sel_cap] token ids (then no blocks, no tail)
     const int32_t *sel_count;      // [walks] entries of sel_blocks / tokens
     float *part;                   // ws [max_items][D + 2]
-    int32_t *item_off;             // ws [walks + 1]: first item of each walk
+    int32_t *item_off;             // ws [walks + 2]: first item of each walk; [walks + 1]: keys per item
     int32_t *item_walk;            // ws [max_items]: walk of each item
     int64_t max_tokens;
     int64_t n_tokens;

@@ -54,7 +54,7 @@ constexpr int kUG = 2;                // matrix tiles in flight per wavefront
 constexpr int kLdsCand = 14336;       // candidate scores a cut stages in LDS (56 KB)
 constexpr int kLdsPar = 2048;         // parent ranks a cut stages in LDS (8 KB)
 constexpr int kExpMin = 256;          // list entries per expand workgroup (at least)
-constexpr int kWaveCand = 480;        // candidates a wavefront cut stages in LDS
+constexpr int kWaveCand = 128;        // candidates a wavefront cut stages in LDS
 static_assert(kSmallList <= kWaveCand, "a fused step's candidates fit in LDS");
 
 __device__ __forceinline__ int head_walk(const SearchArgs &a, int pair, int h) {
