@@ -96,6 +96,20 @@ enum {
     ZHA_ENGINE_BLOCK = 4
 };
 
+/* Attention paths (zha_select.attn_engine).  Both attend exactly the keys
+ * each walk selected and give the same result up to the order of fp32 sums.
+ *   ZHA_ATTN_PER_WALK: every walk reads its own selected blocks (split-K
+ *     work items per walk).
+ *   ZHA_ATTN_UNION: per (sequence, KV head) pair, every block any of its
+ *     query heads selected is read once and attended by each head that
+ *     selected it (bf16 matrix-core logits for all heads of the group, a
+ *     head mask per block).  Decode (q_per_head = 1), bf16 caches,
+ *     group_size <= 16.  A walk's list is taken as a set: a block listed
+ *     twice counts once (zha_search never lists a block twice).
+ *   ZHA_ATTN_AUTO: union for bf16 decode with 16 query heads per KV head,
+ *     else per-walk. */
+enum { ZHA_ATTN_AUTO = 0, ZHA_ATTN_PER_WALK = 1, ZHA_ATTN_UNION = 2 };
+
 /* Device status bits. */
 #define ZHA_FLAG_CAND_OVERFLOW 1u  /* a step had more candidates than max_candidates;
                                       the excess (in span order) was dropped      */
@@ -145,7 +159,8 @@ typedef struct {
     int32_t num_k;
     int32_t max_blocks_per_walk;
     int32_t max_candidates;
-    int32_t engine;          /* ZHA_ENGINE_*                                  */
+    int32_t engine;          /* ZHA_ENGINE_* (search)                         */
+    int32_t attn_engine;     /* ZHA_ATTN_* (sparse attention)                 */
 } zha_select;
 
 /* Host handle of one tree set (all sequences and KV heads).  Plain data: the

@@ -103,6 +103,6 @@ def row_rel_err(a, b):
     return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30))
 
 
-def select_struct(Z, select, max_blocks, max_candidates=0, engine="auto"):
+def select_struct(Z, select, max_blocks, max_candidates=0, engine="auto", attn="auto"):
     return Z.make_select(select["mode"], select.get("p", 0.9), select.get("k", (1,)),
-                         max_blocks=max_blocks, max_candidates=max_candidates, engine=engine)
+                         max_blocks=max_blocks, max_candidates=max_candidates, engine=engine, attn=attn)

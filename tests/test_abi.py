@@ -35,7 +35,37 @@ def test_struct_sizes_match_header(Z):
     # layouts the header fixes: 8 int32 + int64 + float + int32 = 48 bytes
     assert ctypes.sizeof(Z.Geometry) == 48
     assert ctypes.sizeof(Z.WalkStats) == 4 * (2 * 12 + 8)
-    assert ctypes.sizeof(Z.Select) == 4 * (2 + 12 + 4)
+    assert ctypes.sizeof(Z.Select) == 4 * (2 + 12 + 5)
+
+
+def test_attention_workspace_and_engine_choice(Z):
+    """The union attention arrays exist only where that path can run (bf16
+    decode, at most 16 query heads per KV head); an unknown attention engine
+    is rejected (workspace size 0)."""
+    g = _geom(Z, group=16, max_tokens=8192)
+    t = Z.TreeHandle()
+    t.geom = g
+    t.n_tokens = 0
+    t.tree_mem = t.refs = 256          # never dereferenced by the sizing calls
+    t.tree_bytes = Z.zha_tree_bytes(g)
+    for lv in range(1, 4):
+        t.level_cap[lv] = 8192 // 8 ** lv
+    sel = Z.make_select("topp", 0.9, max_blocks=1024)
+    dec = Z.lib.zha_attn_workspace_bytes(ctypes.byref(t), ctypes.byref(sel), 1)
+    pre = Z.lib.zha_attn_workspace_bytes(ctypes.byref(t), ctypes.byref(sel), 4)
+    assert dec > 0 and pre > 0
+    # union arrays: masks [pairs][n1cap] + item flags + partials [pairs][items][G][D+2]
+    pairs, n1cap = 4, 8192 // 8
+    ipp = (n1cap + 127) // 128 + 1
+    union = pairs * n1cap * 4 + pairs * ipp * 4 + pairs * ipp * 16 * 130 * 4
+    g32 = _geom(Z, group=16, max_tokens=8192, dtype="f32")
+    t.geom = g32
+    t.tree_bytes = Z.zha_tree_bytes(g32)
+    dec32 = Z.lib.zha_attn_workspace_bytes(ctypes.byref(t), ctypes.byref(sel), 1)
+    assert dec - dec32 >= union
+    bad = Z.make_select("topp", 0.9, max_blocks=1024)
+    bad.attn_engine = 7
+    assert Z.lib.zha_attn_workspace_bytes(ctypes.byref(t), ctypes.byref(bad), 1) == 0
 
 
 def _geom(Z, **kw):

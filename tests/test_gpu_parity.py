@@ -225,6 +225,86 @@ def test_search_and_attention(Z, name, sname, engine):
     _compare(w, K, V, Q, trees, select, bufs, out, min_stable=min_stable)
 
 
+@pytest.mark.parametrize("sname", ["topp90", "topk4", "p0"])
+@pytest.mark.parametrize("name", ["ar1-small", "clustered-small", "mixed-small", "mha-small"])
+def test_union_attention(Z, name, sname):
+    """The union attention path (each pair's selected blocks read once, all
+    heads at once) against the fp64 oracle on the same selections, and
+    against the per-walk path."""
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, name)
+    select = SELECTS[sname]
+    g = idx.geom
+    sel_u = P.select_struct(Z, select, g.max_tokens // g.chunk, attn="union")
+    sel_p = P.select_struct(Z, select, g.max_tokens // g.chunk, attn="per-walk")
+    bufs = idx.search(Qt, sel_u)
+    out_u = idx.sparse_attn(Qt, Kt, Vt, sel_u, bufs["sel_blocks"], bufs["sel_count"])
+    out_p = idx.sparse_attn(Qt, Kt, Vt, sel_p, bufs["sel_blocks"], bufs["sel_count"])
+    torch.cuda.synchronize()
+    blocks = bufs["sel_blocks"].cpu().numpy()
+    count = bufs["sel_count"].cpu().numpy()
+    ou, op = out_u.float().cpu().numpy(), out_p.float().cpu().numpy()
+    for b in range(w.batch):
+        for h in range(w.heads):
+            gi = h // w.group
+            wi = b * w.heads + h
+            toks = P.gpu_tokens(blocks[wi], count[wi], w.chunk, w.n)
+            ref, _ = O.attend(toks, Q[b, h].astype(np.float64), K[b, gi].astype(np.float64),
+                              V[b, gi].astype(np.float64), w.sharpness)
+            for o in (ou[b, h], op[b, h]):
+                ok, e = P.out_ok(o, ref, w.dtype)
+                assert ok, (b, h, e)
+
+
+def test_union_attention_given_lists(Z):
+    """Hand-made block lists: random sets, ids outside the live level (skipped),
+    entries past sel_count (ignored), empty lists (then only the 3-key raw
+    tail, which every walk attends)."""
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, "mixed-small")
+    g = idx.geom
+    n1 = w.n // w.chunk
+    assert w.n % w.chunk == 3          # a 3-key raw tail every walk attends
+    cap = 64
+    rng = np.random.default_rng(5)
+    walks = w.batch * w.heads
+    blocks = np.full((walks, cap), -1, np.int32)
+    count = np.zeros(walks, np.int32)
+    for wi in range(walks):
+        k = int(rng.integers(0, cap + 1))
+        ids = np.sort(rng.choice(n1 + 40, size=k, replace=False)).astype(np.int32)   # some past n1
+        blocks[wi, :k] = ids
+        count[wi] = k if wi % 7 else 0
+    tb = torch.from_numpy(blocks).cuda()
+    tc = torch.from_numpy(count).cuda()
+    outs = {}
+    for attn in ("union", "per-walk"):
+        sel = P.select_struct(Z, SELECTS["topp90"], cap, attn=attn)
+        outs[attn] = idx.sparse_attn(Qt, Kt, Vt, sel, tb, tc).float().cpu().numpy()
+    torch.cuda.synchronize()
+    for wi in range(walks):
+        b, h = divmod(wi, w.heads)
+        gi = h // w.group
+        ids = blocks[wi, : count[wi]]
+        ids = ids[(ids >= 0) & (ids < n1)]
+        toks = np.sort(np.concatenate([(ids[:, None] * w.chunk + np.arange(w.chunk)).reshape(-1),
+                                       np.arange(n1 * w.chunk, w.n)])).astype(np.int64)
+        ref, _ = O.attend(toks, Q[b, h].astype(np.float64), K[b, gi].astype(np.float64),
+                          V[b, gi].astype(np.float64), w.sharpness)
+        for attn, o in outs.items():
+            ok, e = P.out_ok(o.reshape(walks, -1)[wi], ref, w.dtype)
+            assert ok, (attn, wi, e)
+
+
+def test_union_attention_rejects_unsupported(Z):
+    """fp32 caches, more than 16 heads per KV head and prefill blocks take the
+    per-walk path only: an explicit union request is an error."""
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, "demo")       # fp32, 64 heads per KV head
+    sel = P.select_struct(Z, SELECTS["topp90"], idx.geom.max_tokens // idx.geom.chunk, attn="union")
+    bufs = idx.search(Qt, P.select_struct(Z, SELECTS["topp90"], idx.geom.max_tokens // idx.geom.chunk))
+    with pytest.raises(Z.ZhaError) as ei:
+        idx.sparse_attn(Qt, Kt, Vt, sel, bufs["sel_blocks"], bufs["sel_count"])
+    assert ei.value.code == 6
+
+
 @pytest.mark.parametrize("name", CASES)
 def test_open_all_is_dense(Z, name):
     w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, name)

@@ -1,0 +1,362 @@
+// zha_attn_union.hip -- decode attention over each (sequence, KV head)
+// pair's union of selected blocks.
+//
+// [ZHA lesson] = the page "How does a tree of summaries search a context? How
+// ZHA works".  "Common misunderstandings": every query head walks on its own
+// and attends exactly the original keys it selected; the heads of a group
+// share the K/V cache, so a block several heads selected is read once here
+// and used for each of them, with a head mask per block.
+//
+//   k_ua_fill    clears the pair's block masks (one bit per head of the group);
+//   k_ua_mark    one workgroup per walk sets its head bit on every block it
+//                selected;
+//   k_ua_attn    workgroup r of pair p takes a range of chunks: chunk j is the
+//                selected blocks among level-1 blocks [j*kUaBlocks,
+//                (j+1)*kUaBlocks); the pair's last workgroup also takes the
+//                raw tail, which every head attends.  A chunk's blocks are
+//                compacted in LDS; each wavefront takes 16-key tiles, computes the
+//                logits of all heads at once with bf16 16x16x16 matrix
+//                products S^T = K Q^T (rows = keys, columns = heads), masks
+//                the heads that did not select a key's block, keeps an online
+//                softmax per head in fp32 and accumulates O^T += V^T P^T with
+//                bf16 16x16x16 products (V exact, P as the sum of two bf16
+//                parts, fp32 sums), its state carried across the chunks;
+//                the wavefronts' states are merged in LDS into one partial
+//                per (workgroup, head);
+//   k_ua_combine one workgroup per walk merges its pair's partials.
+// The per-head result is the same softmax over the same key set as the
+// per-walk kernels of zha_attn.hip, summed in another order.
+#include "zha_device.h"
+#include "zha_internal.h"
+
+namespace zha {
+
+namespace {
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kUaWaves = 4;
+
+__device__ __forceinline__ short4_t pk4(uint32_t lo, uint32_t hi) {
+    short4_t r;
+    r[0] = static_cast<short>(lo & 0xffffu);
+    r[1] = static_cast<short>(lo >> 16);
+    r[2] = static_cast<short>(hi & 0xffffu);
+    r[3] = static_cast<short>(hi >> 16);
+    return r;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void k_ua_fill(AttnArgs a) {
+    const int64_t n = static_cast<int64_t>(a.pairs) * a.n1;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t p = i / a.n1, b = i - p * a.n1;
+        a.umask[p * a.n1cap + b] = 0u;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_ua_mark(AttnArgs a) {
+    const int w = blockIdx.x;
+    const int64_t pair = walk_pair(w, 1, a.heads, a.group, a.kv_heads);
+    const uint32_t bit = 1u << (w % a.group);
+    int64_t nb = a.sel_count[w];
+    if (nb > a.sel_cap) nb = a.sel_cap;
+    const int32_t *sel = a.sel_blocks + static_cast<int64_t>(w) * a.sel_cap;
+    for (int64_t i = threadIdx.x; i < nb; i += 256) {
+        const int32_t blk = sel[i];
+        if (blk >= 0 && blk < a.n1) atomicOr(a.umask + pair * a.n1cap + blk, bit);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
+    constexpr int DS = D / 16;            // bf16 16x16x16 steps of a logit
+    constexpr int DT = D / 16;            // row tiles of O^T: row i of tile r is d = DT*i + r
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int c = a.chunk, log2c = a.log2c, G = a.group, wpp = a.items_pp;
+    const int p = blockIdx.x / wpp, r = blockIdx.x - p * wpp;
+    const int nchunks = static_cast<int>((a.n1 + kUaBlocks - 1) / kUaBlocks);
+    const int j0 = r * a.ua_cpw, j1 = min(nchunks, j0 + a.ua_cpw);
+    const int jend = j1 + (r == wpp - 1 ? 1 : 0);   // the last workgroup also takes the tail
+    const float s = a.sharpness;
+    const int64_t tail0 = static_cast<int64_t>(c) * a.n1;
+    const int tail_keys = static_cast<int>(a.n_tokens - tail0);
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    __shared__ int32_t s_blk[kUaBlocks];
+    __shared__ uint32_t s_msk[kUaBlocks];
+    __shared__ int32_t s_cnt[2];
+    __shared__ float s_m[kUaWaves][16], s_l[kUaWaves][16];
+    __shared__ float s_o[kUaWaves][D * 16];
+    const bf16_t *kc = static_cast<const bf16_t *>(a.k) + static_cast<int64_t>(p) * a.max_tokens * D;
+    const bf16_t *vc = static_cast<const bf16_t *>(a.v) + static_cast<int64_t>(p) * a.max_tokens * D;
+    // B operand of S^T: lane (head col, group grp) holds the query of head
+    // col at elements 32*(st/2) + 8*grp + 4*(st%2) .. +3 (zero past G)
+    const bool hv = col < G;
+    short4_t qb[DS];
+    {
+        const int64_t qw = static_cast<int64_t>(p) * G + (hv ? col : 0);   // walk of head col
+        const bf16_t *qr = static_cast<const bf16_t *>(a.q) + qw * D + 8 * grp;
+#pragma unroll
+        for (int m = 0; m < DS / 2; ++m) {
+            gu4_t v = gload_u4(qr + 32 * m);
+            if (!hv) v = gu4_t{0u, 0u, 0u, 0u};
+            qb[2 * m] = pk4(v.x, v.y);
+            qb[2 * m + 1] = pk4(v.z, v.w);
+        }
+    }
+    // online softmax state of head col, kept across the workgroup's chunks
+    float m_run = -INFINITY, l_run = 0.f;
+    float4_t acc[DT];
+#pragma unroll
+    for (int q = 0; q < DT; ++q) acc[q] = float4_t{0.f, 0.f, 0.f, 0.f};
+    bool any = false;
+
+    for (int j = j0; j < jend; ++j) {
+        const bool tail_item = j >= j1;
+        // the chunk's selected blocks, in order (two wavefronts of 64 entries)
+        uint32_t mk = 0u;
+        unsigned long long bal = 0ull;
+        const int b = j * kUaBlocks + (wave & 1) * 64 + lane;
+        if (!tail_item && wave < 2) {
+            mk = (b < a.n1) ? a.umask[static_cast<int64_t>(p) * a.n1cap + b] : 0u;
+            bal = __ballot(mk != 0u);
+            if (lane == 0) s_cnt[wave] = __popcll(bal);
+        }
+        __syncthreads();
+        if (!tail_item && wave < 2 && mk != 0u) {
+            const int at = (wave ? s_cnt[0] : 0) + __popcll(bal & below);
+            s_blk[at] = b;
+            s_msk[at] = mk;
+        }
+        const int nkeys = tail_item ? tail_keys : (s_cnt[0] + s_cnt[1]) * c;
+        __syncthreads();
+        if (nkeys <= 0) continue;
+        any = true;
+        auto token_of = [&](int kk) -> int64_t {
+            if (tail_item) return tail0 + kk;
+            return (static_cast<int64_t>(s_blk[kk >> log2c]) << log2c) + (kk & (c - 1));
+        };
+        const int ntiles = (nkeys + 15) / 16;
+        struct Tile {
+            short4_t kb[DS];                  // A operand of S^T
+            uint32_t vw[4][DT / 2];           // V rows for O^T += V^T P^T
+        };
+        // key rows of tile t: for S^T, key kbase + col (same element order
+        // as qb); for the second product at step e, key kbase + 4*grp + e,
+        // elements DT*col .. DT*col + DT - 1
+        auto load_tile = [&](int t, Tile &T) {
+            const int kbase = t * 16;
+            const int ka = kbase + col;
+            const bf16_t *kr = kc + token_of(ka < nkeys ? ka : kbase) * D + 8 * grp;
+#pragma unroll
+            for (int m = 0; m < DS / 2; ++m) {
+                const gu4_t v = gload_u4(kr + 32 * m);
+                T.kb[2 * m] = pk4(v.x, v.y);
+                T.kb[2 * m + 1] = pk4(v.z, v.w);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int kk = kbase + 4 * grp + e;
+                const bf16_t *vr = vc + token_of(kk < nkeys ? kk : kbase) * D + DT * col;
+                if constexpr (DT == 8) {
+                    const gu4_t v = gload_u4(vr);
+                    T.vw[e][0] = v.x; T.vw[e][1] = v.y; T.vw[e][2] = v.z; T.vw[e][3] = v.w;
+                } else {
+                    const gu2_t v = gload_u2(vr);
+                    T.vw[e][0] = v.x; T.vw[e][1] = v.y;
+                }
+            }
+        };
+        auto run_tile = [&](int t, const Tile &T) {
+            const int kbase = t * 16;
+            float4_t sa = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < DS; ++st) sa = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(T.kb[st], qb[st], sa, 0, 0, 0);
+            // logits of head col for keys kbase + 4*grp + e; masked: -inf
+            float x[4], tmax = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int kk = kbase + 4 * grp + e;
+                bool ok = hv && kk < nkeys;
+                if (ok && !tail_item) ok = (s_msk[kk >> log2c] >> col) & 1u;
+                x[e] = ok ? s * sa[e] : -INFINITY;
+                tmax = fmaxf(tmax, x[e]);
+            }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            const float mn = fmaxf(m_run, tmax);
+            const float corr = (m_run > -INFINITY) ? expf(m_run - mn) : 0.f;
+            float pe[4], psum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pe[e] = (x[e] > -INFINITY) ? expf(x[e] - mn) : 0.f;
+                psum += pe[e];
+            }
+            psum += __shfl_xor(psum, 16, 64);
+            psum += __shfl_xor(psum, 32, 64);
+            l_run = l_run * corr + psum;
+            m_run = mn;
+#pragma unroll
+            for (int q = 0; q < DT; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[q][e] *= corr;
+            // O^T += V^T P^T as bf16 16x16x16 products: the probabilities of
+            // keys 4*grp .. 4*grp+3 are already this lane's B operand; each is
+            // split into two bf16 parts (hi + lo, within 2^-17 of p relative),
+            // so the fp32 sums keep fp32 accuracy while V stays exact
+            short4_t ph, pl;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bf16_t hb = f32_to_bf16(pe[e]);
+                ph[e] = static_cast<short>(hb);
+                pl[e] = static_cast<short>(f32_to_bf16(pe[e] - bf16_to_f32(hb)));
+            }
+#pragma unroll
+            for (int q = 0; q < DT; ++q) {
+                // A operand: element DT*col + q of keys 4*grp + e
+                short4_t va;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t wd = T.vw[e][q >> 1];
+                    va[e] = static_cast<short>((q & 1) ? (wd >> 16) : (wd & 0xffffu));
+                }
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, acc[q], 0, 0, 0);
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc[q], 0, 0, 0);
+            }
+        };
+        // one tile in flight per wavefront (two cost occupancy and were slower)
+        for (int t = wave; t < ntiles; t += kUaWaves) {
+            Tile T;
+            load_tile(t, T);
+            run_tile(t, T);
+        }
+        __syncthreads();                           // the tiles read s_blk / s_msk
+    }
+    if (!any) {                                    // uniform: no keys in this workgroup's range
+        if (tid == 0) a.ic[blockIdx.x] = 0;
+        return;
+    }
+    // merge the wavefronts' states per head
+    if (grp == 0) {
+        s_m[wave][col] = m_run;
+        s_l[wave][col] = l_run;
+    }
+#pragma unroll
+    for (int q = 0; q < DT; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_o[wave][(DT * (4 * grp + e) + q) * 16 + col] = acc[q][e];
+    __syncthreads();
+    for (int i = tid; i < D * 16; i += 256) {
+        const int d = i >> 4, h = i & 15;
+        if (h >= G) continue;
+        float mm = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < kUaWaves; ++v) mm = fmaxf(mm, s_m[v][h]);
+        float ll = 0.f, oo = 0.f;
+        if (mm > -INFINITY) {
+#pragma unroll
+            for (int v = 0; v < kUaWaves; ++v) {
+                if (!(s_m[v][h] > -INFINITY)) continue;
+                const float f = expf(s_m[v][h] - mm);
+                ll = fmaf(s_l[v][h], f, ll);
+                oo = fmaf(s_o[v][d * 16 + h], f, oo);
+            }
+        }
+        float *part = a.part + (static_cast<int64_t>(blockIdx.x) * G + h) * (D + 2);
+        part[2 + d] = oo;
+        if (d == 0) {
+            part[0] = mm;
+            part[1] = ll;
+        }
+    }
+    if (tid == 0) a.ic[blockIdx.x] = 1;
+}
+
+// One workgroup per walk: its pair's item flags staged in LDS, then each
+// wavefront merges every fourth item (online, one pass), then the four
+// states are merged.
+template <int D>
+__global__ __launch_bounds__(256) void k_ua_combine(AttnArgs a) {
+    constexpr int EPL = D / 64;           // output elements per lane
+    const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t p = walk_pair(w, 1, a.heads, a.group, a.kv_heads);
+    const int h = w % a.group, ipp = a.items_pp;
+    const int64_t i0 = p * ipp;
+    __shared__ int32_t s_items[kUaMaxItems];
+    __shared__ int32_t s_n;
+    __shared__ float s_m[kUaWaves], s_l[kUaWaves], s_acc[kUaWaves][D];
+    // the items that wrote partials, in order
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    for (int j = tid; j < ipp; j += 256)
+        if (a.ic[i0 + j] != 0) s_items[atomicAdd(&s_n, 1)] = j;
+    __syncthreads();
+    const int n = s_n;
+    float m = -INFINITY, l = 0.f, acc[EPL];
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) acc[k] = 0.f;
+    for (int x = wave; x < n; x += kUaWaves) {
+        const float *pp = a.part + ((i0 + s_items[x]) * a.group + h) * (D + 2);
+        const float pm = pp[0], pls = pp[1];
+        float v[EPL];
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) v[k] = pp[2 + lane * EPL + k];
+        if (!(pm > -INFINITY)) continue;
+        const float mn = fmaxf(m, pm);
+        const float c1 = (m > -INFINITY) ? expf(m - mn) : 0.f, c2 = expf(pm - mn);
+        l = l * c1 + pls * c2;
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) acc[k] = acc[k] * c1 + v[k] * c2;
+        m = mn;
+    }
+    if (lane == 0) {
+        s_m[wave] = m;
+        s_l[wave] = l;
+    }
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) s_acc[wave][lane * EPL + k] = acc[k];
+    __syncthreads();
+    if (tid < D) {
+        float mm = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < kUaWaves; ++v) mm = fmaxf(mm, s_m[v]);
+        float ll = 0.f, av = 0.f;
+        if (mm > -INFINITY) {
+#pragma unroll
+            for (int v = 0; v < kUaWaves; ++v) {
+                if (!(s_m[v] > -INFINITY)) continue;
+                const float f = expf(s_m[v] - mm);
+                ll = fmaf(s_l[v], f, ll);
+                av = fmaf(s_acc[v][tid], f, av);
+            }
+        }
+        const float o = (ll > 0.f) ? av / ll : 0.f;
+        Elem<bf16_t>::store(static_cast<bf16_t *>(a.out), static_cast<int64_t>(w) * D + tid, o);
+    }
+}
+
+template <int D>
+static hipError_t launch_ua_t(const AttnArgs &a, hipStream_t st) {
+    const int64_t fill = static_cast<int64_t>(a.pairs) * a.n1;
+    const int fill_grid = static_cast<int>(fill / 256 + 1 < 2048 ? fill / 256 + 1 : 2048);
+    hipLaunchKernelGGL(k_ua_fill, dim3(fill_grid), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_ua_mark, dim3(a.walks), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_ua_attn<D>), dim3(static_cast<unsigned>(a.pairs * a.items_pp)), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_ua_combine<D>), dim3(a.walks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_union(const AttnArgs &a, int D, hipStream_t st) {
+    if (a.walks <= 0) return hipSuccess;
+    return D == 64 ? launch_ua_t<64>(a, st) : launch_ua_t<128>(a, st);
+}
+
+}  // namespace zha

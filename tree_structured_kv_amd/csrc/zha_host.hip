@@ -8,6 +8,8 @@
 
 #include "zha_internal.h"
 
+#include <algorithm>
+
 using namespace zha;
 
 namespace {
@@ -88,6 +90,7 @@ zha_status check_select(const zha_select *sel) {
     if (sel->max_blocks_per_walk < 1) return ZHA_ERR_ARG;
     if (sel->max_candidates < 0) return ZHA_ERR_ARG;
     if (sel->engine < ZHA_ENGINE_AUTO || sel->engine > ZHA_ENGINE_BLOCK) return ZHA_ERR_ARG;
+    if (sel->attn_engine < ZHA_ATTN_AUTO || sel->attn_engine > ZHA_ATTN_UNION) return ZHA_ERR_ARG;
     return ZHA_OK;
 }
 
@@ -154,21 +157,51 @@ int64_t tree_keys_bound(const zha_tree *t, const zha_select *sel, int32_t qph) {
     return int64_t(sel->max_blocks_per_walk) * t->geom.chunk + t->geom.chunk - 1 + (qph > 1 ? qph : 0);
 }
 
+// The union attention path: decode over bf16 caches, at most 16 query heads
+// per KV head (one matrix-core column per head), at most kUaMaxItems work
+// items per pair.
+bool union_attn_ok(const zha_tree *t, int32_t qph) {
+    const int64_t items = (t->geom.max_tokens / t->geom.chunk + kUaBlocks - 1) / kUaBlocks + 1;
+    return qph == 1 && t->geom.dtype == ZHA_BF16 && t->geom.group_size <= 16 && items <= kUaMaxItems;
+}
+
+// ZHA_ATTN_* a call runs (ZHA_ATTN_UNION only where union_attn_ok).
+int resolve_attn(const zha_tree *t, const zha_select *sel, int32_t qph) {
+    if (sel->attn_engine != ZHA_ATTN_AUTO) return sel->attn_engine;
+    return (union_attn_ok(t, qph) && t->geom.group_size == 16) ? ZHA_ATTN_UNION : ZHA_ATTN_PER_WALK;
+}
+
 struct AttnWs {
-    uint64_t part, item_off, item_walk, total;
+    uint64_t part, item_off, item_walk, umask, ic, upart, total;
+    int64_t n1cap, ipp;
 };
-AttnWs attn_ws_layout(int head_dim, int64_t keys_bound, int64_t walks) {
+// Per-walk items; with `t` (a decode call that may take the union path) also
+// the union arrays.
+AttnWs attn_ws_layout(int head_dim, int64_t keys_bound, int64_t walks, const zha_tree *t = nullptr) {
     const uint64_t items = static_cast<uint64_t>(attn_max_items(keys_bound, walks));
     AttnWs l;
     l.part = 0;
     l.item_off = align_up(items * (head_dim + 2) * sizeof(float));
     l.item_walk = l.item_off + align_up(uint64_t(walks + 2) * sizeof(int32_t));
-    l.total = l.item_walk + align_up(items * sizeof(int32_t));
+    l.umask = l.item_walk + align_up(items * sizeof(int32_t));
+    l.n1cap = 0;
+    l.ipp = 0;
+    uint64_t pairs = 0;
+    if (t && union_attn_ok(t, 1)) {
+        pairs = uint64_t(t->geom.batch) * t->geom.num_kv_heads;
+        l.n1cap = t->geom.max_tokens / t->geom.chunk;
+        l.ipp = (l.n1cap + kUaBlocks - 1) / kUaBlocks + 1;
+    }
+    l.ic = l.umask + align_up(pairs * uint64_t(l.n1cap) * sizeof(uint32_t));
+    l.upart = l.ic + align_up(pairs * uint64_t(l.ipp) * sizeof(int32_t));
+    const uint64_t g = t ? uint64_t(t->geom.group_size) : 0;
+    l.total = l.upart + align_up(pairs * uint64_t(l.ipp) * g * (head_dim + 2) * sizeof(float));
     return l;
 }
 
 uint64_t attn_ws_bytes(const zha_tree *t, const zha_select *sel, int32_t qph) {
-    return attn_ws_layout(t->geom.head_dim, tree_keys_bound(t, sel, qph), walks_of(&t->geom, qph)).total;
+    return attn_ws_layout(t->geom.head_dim, tree_keys_bound(t, sel, qph), walks_of(&t->geom, qph),
+                          qph == 1 ? t : nullptr).total;
 }
 
 struct ForwardWs {
@@ -358,7 +391,7 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
 zha_status do_attn(const zha_tree *t, const void *q, int32_t qph, const void *k_cache,
                    const void *v_cache, const int32_t *sel_blocks, const int32_t *tokens,
                    const int32_t *sel_count, int32_t list_cap, int64_t keys_bound, void *out, void *ws,
-                   hipStream_t st) {
+                   hipStream_t st, int attn_engine = ZHA_ATTN_PER_WALK) {
     const zha_geometry &g = t->geom;
     const int64_t walks = walks_of(&g, qph);
     AttnArgs a;
@@ -370,7 +403,8 @@ zha_status do_attn(const zha_tree *t, const void *q, int32_t qph, const void *k_
     a.sel_blocks = sel_blocks;
     a.tokens = tokens;
     a.sel_count = sel_count;
-    AttnWs lay = attn_ws_layout(g.head_dim, keys_bound, walks);
+    const bool uni = attn_engine == ZHA_ATTN_UNION && tokens == nullptr;
+    AttnWs lay = attn_ws_layout(g.head_dim, keys_bound, walks, uni ? t : nullptr);
     char *wb = static_cast<char *>(ws);
     a.part = reinterpret_cast<float *>(wb + lay.part);
     a.item_off = reinterpret_cast<int32_t *>(wb + lay.item_off);
@@ -389,6 +423,23 @@ zha_status do_attn(const zha_tree *t, const void *q, int32_t qph, const void *k_
     a.grid = static_cast<int32_t>(items < 2048 ? items : 2048);
     a.block_mfma = (qph > 1 && tokens == nullptr && g.dtype == ZHA_BF16) ? 1 : 0;
     a.sharpness = g.sharpness;
+    a.pairs = g.batch * g.num_kv_heads;
+    a.log2c = ilog2(g.chunk);
+    if (uni) {
+        a.umask = reinterpret_cast<uint32_t *>(wb + lay.umask);
+        a.ic = reinterpret_cast<int32_t *>(wb + lay.ic);
+        a.part = reinterpret_cast<float *>(wb + lay.upart);
+        a.n1cap = lay.n1cap;
+        // about 4096 workgroups in all, each over a contiguous range of chunks
+        const int64_t nchunks = (a.n1 + kUaBlocks - 1) / kUaBlocks;
+        int64_t wpp = std::max<int64_t>(1, 4096 / a.pairs);
+        if (wpp > nchunks) wpp = std::max<int64_t>(1, nchunks);
+        const int64_t cpw = nchunks > 0 ? (nchunks + wpp - 1) / wpp : 0;
+        if (cpw > 0) wpp = (nchunks + cpw - 1) / cpw;
+        a.items_pp = static_cast<int32_t>(wpp);
+        a.ua_cpw = static_cast<int32_t>(cpw);
+        return hip_status(launch_attn_union(a, g.head_dim, st));
+    }
     return hip_status(launch_attn(a, g.head_dim, g.dtype, st));
 }
 
@@ -530,9 +581,11 @@ zha_status zha_sparse_attn(const zha_tree *t, const void *q, int32_t q_per_head,
         !aligned16(ws) || !aligned_n(sel_blocks, 4) || !aligned_n(sel_count, 4))
         return ZHA_ERR_ALIGN;
     if (ws_bytes < zha_attn_workspace_bytes(t, sel, q_per_head)) return ZHA_ERR_WORKSPACE;
+    const int ae = resolve_attn(t, sel, q_per_head);
+    if (ae == ZHA_ATTN_UNION && !union_attn_ok(t, q_per_head)) return ZHA_ERR_UNSUPPORTED;
     return do_attn(t, q, q_per_head, k_cache, v_cache, sel_blocks, nullptr, sel_count,
                    sel->max_blocks_per_walk, tree_keys_bound(t, sel, q_per_head), out, ws,
-                   static_cast<hipStream_t>(stream));
+                   static_cast<hipStream_t>(stream), ae);
 }
 
 uint64_t zha_forward_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head) {
@@ -557,6 +610,8 @@ zha_status zha_forward(zha_tree *t, int64_t n_new, const void *q, int32_t q_per_
     if (q_per_head > 1 && t->n_tokens + q_per_head > t->geom.max_tokens) return ZHA_ERR_CAPACITY;
     if (sel->engine == ZHA_ENGINE_UNION && (q_per_head != 1 || t->geom.group_size > 16))
         return ZHA_ERR_UNSUPPORTED;
+    const int ae = resolve_attn(t, sel, q_per_head);
+    if (ae == ZHA_ATTN_UNION && !union_attn_ok(t, q_per_head)) return ZHA_ERR_UNSUPPORTED;
     if (ws_bytes < zha_forward_workspace_bytes(t, sel, q_per_head)) return ZHA_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     // decode: the new rows join the tree first, so the query sees them
@@ -572,7 +627,7 @@ zha_status zha_forward(zha_tree *t, int64_t n_new, const void *q, int32_t q_per_
     s = do_search(t, q, q_per_head, sel, sb, sc, stats, status, nullptr, w + lay.search, st);
     if (s != ZHA_OK) return s;
     s = do_attn(t, q, q_per_head, k_cache, v_cache, sb, nullptr, sc, sel->max_blocks_per_walk,
-                tree_keys_bound(t, sel, q_per_head), out, w + lay.attn, st);
+                tree_keys_bound(t, sel, q_per_head), out, w + lay.attn, st, ae);
     if (s != ZHA_OK) return s;
     // prefill: the block joins the tree after its own queries have searched it
     if (q_per_head > 1 && n_new > 0) {

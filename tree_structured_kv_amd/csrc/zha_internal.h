@@ -19,6 +19,8 @@ constexpr int kTile = 32;            // candidates per tile of the level-synchro
 constexpr int kFlatPad = 32;         // union engine: each run of scoring entries is padded to this
 constexpr int kExpSlices = 8;        // union engine: workgroups (runs) per pair building the next list
 constexpr int kSmallList = 64;       // union engine: list bound of the steps fused into one launch
+constexpr int kUaBlocks = 128;       // union attention: level-1 blocks per work item
+constexpr int kUaMaxItems = 4096;    // union attention: work items per pair (at most)
 
 // Per-walk state of the level-synchronous search engine (workspace).
 struct WalkState {
@@ -141,6 +143,14 @@ struct AttnArgs {
     int32_t block_mfma;            // prefill: the block's own keys go to k_attn_block
                                    // (one extra item per walk, the last one)
     float sharpness;
+    // union path (decode): per pair, the union of its heads' selected blocks
+    uint32_t *umask;               // ws [pairs][n1cap]  heads that selected each level-1 block
+    int32_t *ic;                   // ws [pairs][items_pp]  1: the item wrote partials
+    int64_t n1cap;                 // level-1 blocks per pair (stride of umask)
+    int32_t items_pp;              // workgroups (partials) per pair
+    int32_t ua_cpw;                // kUaBlocks-block chunks per workgroup
+    int32_t pairs;
+    int32_t log2c;
 };
 
 struct DenseArgs {
@@ -167,6 +177,7 @@ hipError_t launch_search(const SearchArgs &a, int D, int R, int dtype, int sdtyp
 hipError_t launch_union(const SearchArgs &a, int D, int R, int dtype, int sdtype, int n0, hipStream_t st);
 hipError_t launch_block(const SearchArgs &a, int D, int R, int dtype, int sdtype, int n0, hipStream_t st);
 hipError_t launch_attn(const AttnArgs &a, int D, int dtype, hipStream_t st);
+hipError_t launch_attn_union(const AttnArgs &a, int D, hipStream_t st);
 hipError_t launch_dense(const DenseArgs &a, int D, int dtype, hipStream_t st);
 hipError_t launch_probe(const void *buf, uint64_t bytes, float *sink, hipStream_t st);
 

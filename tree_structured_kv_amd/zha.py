@@ -24,6 +24,8 @@ FLAG_CAND_OVERFLOW, FLAG_SEL_OVERFLOW, FLAG_NONFINITE = 1, 2, 4
 ENGINE_AUTO, ENGINE_PERSISTENT, ENGINE_LEVEL_SYNC, ENGINE_UNION, ENGINE_BLOCK = 0, 1, 2, 3, 4
 ENGINES = {"auto": ENGINE_AUTO, "persistent": ENGINE_PERSISTENT, "level-sync": ENGINE_LEVEL_SYNC,
            "union": ENGINE_UNION, "block": ENGINE_BLOCK}
+ATTN_AUTO, ATTN_PER_WALK, ATTN_UNION = 0, 1, 2
+ATTN_ENGINES = {"auto": ATTN_AUTO, "per-walk": ATTN_PER_WALK, "union": ATTN_UNION}
 
 STATUS = {0: "ZHA_OK", 1: "ZHA_ERR_ARG", 2: "ZHA_ERR_SHAPE", 3: "ZHA_ERR_ALIGN",
           4: "ZHA_ERR_CAPACITY", 5: "ZHA_ERR_WORKSPACE", 6: "ZHA_ERR_UNSUPPORTED",
@@ -43,7 +45,7 @@ class Select(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("p", ctypes.c_float),
                 ("k", ctypes.c_int32 * MAX_STEPS), ("num_k", ctypes.c_int32),
                 ("max_blocks_per_walk", ctypes.c_int32), ("max_candidates", ctypes.c_int32),
-                ("engine", ctypes.c_int32)]
+                ("engine", ctypes.c_int32), ("attn_engine", ctypes.c_int32)]
 
 
 class TreeHandle(ctypes.Structure):
@@ -142,7 +144,8 @@ def make_geometry(batch, kv_heads, group, head_dim, chunk, refs, levels, dtype, 
                     BF16 if summary in ("bf16", BF16, torch.bfloat16) else F32)
 
 
-def make_select(mode="topp", p=0.9, k=(1,), max_blocks=1024, max_candidates=0, engine="auto") -> Select:
+def make_select(mode="topp", p=0.9, k=(1,), max_blocks=1024, max_candidates=0, engine="auto",
+                attn="auto") -> Select:
     s = Select()
     s.mode = TOPK if mode in ("topk", TOPK) else TOPP
     s.p = float(p)
@@ -153,6 +156,7 @@ def make_select(mode="topp", p=0.9, k=(1,), max_blocks=1024, max_candidates=0, e
     s.max_blocks_per_walk = int(max_blocks)
     s.max_candidates = int(max_candidates)
     s.engine = ENGINES[engine] if isinstance(engine, str) else int(engine)
+    s.attn_engine = ATTN_ENGINES[attn] if isinstance(attn, str) else int(attn)
     return s
 
 
