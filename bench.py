@@ -295,7 +295,8 @@ def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True, summary="
     dense = run_dense(idx, w, Q, K, V, per_rot, steps, warmup) if dense_baseline else None
     res = dict(
         dense=dense,
-        workload=w, select=select, wall_s=wall, steps=steps, engine=idx.engine(sel), node_keys=summary,
+        workload=w, select=select, wall_s=wall, steps=steps, engine=idx.engine(sel),
+        attn_engine=idx.attn_engine(sel), node_keys=summary,
         ms_per_step=float(step_ms.mean()),
         ms_p10=float(np.percentile(step_ms, 10)), ms_p50=float(np.percentile(step_ms, 50)),
         ms_p90=float(np.percentile(step_ms, 90)),
@@ -550,7 +551,8 @@ def summary(res, bw_ach):
     step_bytes = by["search"] + by["attn"]
     step_gbs = step_bytes / (res["ms_per_step"] * 1e-3) / 1e9
     return dict(
-        workload=w.name, select=sel, engine=res["engine"], node_keys=res["node_keys"],
+        workload=w.name, select=sel, engine=res["engine"], attn_engine=res["attn_engine"],
+        node_keys=res["node_keys"],
         qps=res["qps"], walks_per_s=res["walks_per_s"], ms_per_step=res["ms_per_step"],
         ms_p10=res["ms_p10"], ms_p50=res["ms_p50"], ms_p90=res["ms_p90"],
         back_to_back_qps=res["back_to_back_qps"], back_to_back_ms=res["back_to_back_ms"],

@@ -279,6 +279,12 @@ uint64_t zha_visited_words(const zha_tree *t);
 /* Workspace bytes of zha_sparse_attn. */
 uint64_t zha_attn_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head);
 
+/* The attention path (ZHA_ATTN_PER_WALK or ZHA_ATTN_UNION) zha_sparse_attn
+ * runs for these arguments: sel->attn_engine itself, or what ZHA_ATTN_AUTO
+ * resolves to.  Host only, enqueues nothing.  -1 if the tree or selection is
+ * invalid or the path does not support the shape. */
+int32_t zha_attn_engine(const zha_tree *t, const zha_select *sel, int32_t q_per_head);
+
 /* out = softmax over the selected keys of s*<q, K_i>, applied to V_i, for
  * every walk: exactly the original keys of the listed level-1 blocks plus
  * the raw tail [chunk*floor(n_tokens/chunk), n_tokens) ([ZHA lesson] "How is

@@ -66,6 +66,22 @@ def test_attention_workspace_and_engine_choice(Z):
     bad = Z.make_select("topp", 0.9, max_blocks=1024)
     bad.attn_engine = 7
     assert Z.lib.zha_attn_workspace_bytes(ctypes.byref(t), ctypes.byref(bad), 1) == 0
+    assert Z.zha_attn_engine(t, bad, 1) is None
+    # AUTO: union for bf16 decode with 16 heads per KV head, else per-walk
+    t.geom = g
+    t.tree_bytes = Z.zha_tree_bytes(g)
+    assert Z.zha_attn_engine(t, sel, 1) == "union"
+    assert Z.zha_attn_engine(t, sel, 4) == "per-walk"
+    assert Z.zha_attn_engine(t, Z.make_select("topp", 0.9, max_blocks=1024, attn="per-walk"), 1) == "per-walk"
+    assert Z.zha_attn_engine(t, Z.make_select("topp", 0.9, max_blocks=1024, attn="union"), 4) is None
+    g8 = _geom(Z, group=8, max_tokens=8192)
+    t.geom = g8
+    t.tree_bytes = Z.zha_tree_bytes(g8)
+    assert Z.zha_attn_engine(t, sel, 1) == "per-walk"
+    assert Z.zha_attn_engine(t, Z.make_select("topp", 0.9, max_blocks=1024, attn="union"), 1) == "union"
+    t.geom = g32
+    t.tree_bytes = Z.zha_tree_bytes(g32)
+    assert Z.zha_attn_engine(t, Z.make_select("topp", 0.9, max_blocks=1024, attn="union"), 1) is None
 
 
 def _geom(Z, **kw):

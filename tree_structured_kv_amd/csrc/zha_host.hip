@@ -537,6 +537,13 @@ int32_t zha_search_engine(const zha_tree *t, const zha_select *sel, int32_t q_pe
     return e;
 }
 
+int32_t zha_attn_engine(const zha_tree *t, const zha_select *sel, int32_t q_per_head) {
+    if (check_tree(t) != ZHA_OK || check_select(sel) != ZHA_OK || q_per_head < 1) return -1;
+    const int e = resolve_attn(t, sel, q_per_head);
+    if (e == ZHA_ATTN_UNION && !union_attn_ok(t, q_per_head)) return -1;
+    return e;
+}
+
 uint64_t zha_visited_words(const zha_tree *t) {
     if (check_tree(t) != ZHA_OK) return 0;
     return static_cast<uint64_t>(visited_words_per_pair(t)) * t->geom.batch * t->geom.num_kv_heads;

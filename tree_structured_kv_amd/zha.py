@@ -68,7 +68,7 @@ class WalkStats(ctypes.Structure):
 STATS_WORDS = ctypes.sizeof(WalkStats) // 4   # int32 words per stats record
 
 EXPORTS = ["zha_tree_bytes", "zha_tree_init", "zha_build", "zha_append",
-           "zha_search_workspace_bytes", "zha_search_engine", "zha_search", "zha_visited_words", "zha_attn_workspace_bytes",
+           "zha_search_workspace_bytes", "zha_search_engine", "zha_search", "zha_visited_words", "zha_attn_workspace_bytes", "zha_attn_engine",
            "zha_sparse_attn", "zha_forward_workspace_bytes", "zha_forward",
            "zha_dense_workspace_bytes", "zha_dense_topk_attn", "zha_bw_probe",
            "zha_status_string"]
@@ -88,6 +88,7 @@ def _load():
         "zha_append": (i32, [tp, vp, i64, vp]),
         "zha_search_workspace_bytes": (u64, [tp, sp, i32]),
         "zha_search_engine": (i32, [tp, sp, i32]),
+        "zha_attn_engine": (i32, [tp, sp, i32]),
         "zha_search": (i32, [tp, vp, i32, sp, vp, vp, vp, vp, vp, vp, u64, vp]),
         "zha_visited_words": (u64, [tp]),
         "zha_attn_workspace_bytes": (u64, [tp, sp, i32]),
@@ -190,6 +191,12 @@ def zha_search_engine(t: TreeHandle, sel: Select, q_per_head: int = 1) -> str | 
     """Name of the engine zha_search runs for these arguments (None: invalid)."""
     e = int(lib.zha_search_engine(ctypes.byref(t), ctypes.byref(sel), q_per_head))
     return {v: k for k, v in ENGINES.items()}.get(e) if e > 0 else None
+
+
+def zha_attn_engine(t: TreeHandle, sel: Select, q_per_head: int = 1) -> str | None:
+    """Name of the attention path zha_sparse_attn runs (None: invalid)."""
+    e = int(lib.zha_attn_engine(ctypes.byref(t), ctypes.byref(sel), q_per_head))
+    return {v: k for k, v in ATTN_ENGINES.items()}.get(e) if e > 0 else None
 
 
 def zha_search(t: TreeHandle, q, sel: Select, sel_blocks, sel_count, stats, status, ws,
@@ -330,6 +337,9 @@ class Index:
 
     def engine(self, sel: Select, qph: int = 1):
         return zha_search_engine(self.handle, sel, qph)
+
+    def attn_engine(self, sel: Select, qph: int = 1):
+        return zha_attn_engine(self.handle, sel, qph)
 
     def visited_bitmap(self):
         """A zeroed bitmap for zha_search's `visited` output: [pairs][words]."""
