@@ -54,10 +54,12 @@ def test_attention_workspace_and_engine_choice(Z):
     dec = Z.lib.zha_attn_workspace_bytes(ctypes.byref(t), ctypes.byref(sel), 1)
     pre = Z.lib.zha_attn_workspace_bytes(ctypes.byref(t), ctypes.byref(sel), 4)
     assert dec > 0 and pre > 0
-    # union arrays: masks [pairs][n1cap] + item flags + partials [pairs][items][G][D+2]
+    # union arrays: 16-bit masks [pairs][n1cap], chunk bits, workgroup flags
+    # and partials [pairs][workgroups][16][D+2]
     pairs, n1cap = 4, 8192 // 8
-    ipp = (n1cap + 127) // 128 + 1
-    union = pairs * n1cap * 4 + pairs * ipp * 4 + pairs * ipp * 16 * 130 * 4
+    nchunks = n1cap // 128
+    wpg = min(4096 // pairs, nchunks)
+    union = pairs * n1cap * 2 + pairs * 4 + pairs * wpg * 4 + pairs * wpg * 16 * 130 * 4
     g32 = _geom(Z, group=16, max_tokens=8192, dtype="f32")
     t.geom = g32
     t.tree_bytes = Z.zha_tree_bytes(g32)
@@ -71,9 +73,8 @@ def test_attention_workspace_and_engine_choice(Z):
     t.geom = g
     t.tree_bytes = Z.zha_tree_bytes(g)
     assert Z.zha_attn_engine(t, sel, 1) == "union"
-    assert Z.zha_attn_engine(t, sel, 4) == "per-walk"
+    assert Z.zha_attn_engine(t, sel, 4) == "union"          # bf16 prefill blocks: 16 queries per group
     assert Z.zha_attn_engine(t, Z.make_select("topp", 0.9, max_blocks=1024, attn="per-walk"), 1) == "per-walk"
-    assert Z.zha_attn_engine(t, Z.make_select("topp", 0.9, max_blocks=1024, attn="union"), 4) is None
     g8 = _geom(Z, group=8, max_tokens=8192)
     t.geom = g8
     t.tree_bytes = Z.zha_tree_bytes(g8)
@@ -82,6 +83,7 @@ def test_attention_workspace_and_engine_choice(Z):
     t.geom = g32
     t.tree_bytes = Z.zha_tree_bytes(g32)
     assert Z.zha_attn_engine(t, Z.make_select("topp", 0.9, max_blocks=1024, attn="union"), 1) is None
+    assert Z.zha_attn_engine(t, sel, 4) == "per-walk"       # fp32 prefill
 
 
 def _geom(Z, **kw):

@@ -295,8 +295,8 @@ def test_union_attention_given_lists(Z):
 
 
 def test_union_attention_rejects_unsupported(Z):
-    """fp32 caches, more than 16 heads per KV head and prefill blocks take the
-    per-walk path only: an explicit union request is an error."""
+    """fp32 caches and more than 16 query heads per KV head take the per-walk
+    path only: an explicit union request is an error."""
     w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, "demo")       # fp32, 64 heads per KV head
     sel = P.select_struct(Z, SELECTS["topp90"], idx.geom.max_tokens // idx.geom.chunk, attn="union")
     bufs = idx.search(Qt, P.select_struct(Z, SELECTS["topp90"], idx.geom.max_tokens // idx.geom.chunk))
@@ -533,6 +533,43 @@ def test_prefill_block(Z, sname, engine):
                                     K[0, g].astype(np.float64), V[0, g].astype(np.float64), w.sharpness)
                 assert P.out_ok(outs[0, h, t], dense, w.dtype)[0]
     assert stable >= 0.3 * walks
+
+
+@pytest.mark.parametrize("sname", ["topp90", "topk4", "open-all"])
+@pytest.mark.parametrize("T", [128, 100])
+def test_prefill_attention_paths(Z, sname, T):
+    """Prefill blocks: the union attention path (groups of 16 consecutive
+    queries of a head; with T = 100 the last group of each head is ragged)
+    and the per-walk path, each against oracle attention over the same
+    selection plus the block's keys up to the query on sampled queries, and
+    against each other on every query."""
+    w, T0, _, K, V, Q, R, Kt, Vt, Qt, idx, trees = _prefill_setup(Z)
+    Qb = Qt[:, :, :T].contiguous()
+    select = dict(mode="topp", p=1.0) if sname == "open-all" else SELECTS[sname]
+    sel_u = P.select_struct(Z, select, T0 // w.chunk, attn="union")
+    sel_p = P.select_struct(Z, select, T0 // w.chunk, attn="per-walk")
+    assert idx.attn_engine(sel_u, T) == "union"
+    bufs = idx.search(Qb, sel_u, qph=T)
+    out_u = idx.sparse_attn(Qb, Kt, Vt, sel_u, bufs["sel_blocks"], bufs["sel_count"], qph=T)
+    out_p = idx.sparse_attn(Qb, Kt, Vt, sel_p, bufs["sel_blocks"], bufs["sel_count"], qph=T)
+    torch.cuda.synchronize()
+    blocks = bufs["sel_blocks"].cpu().numpy()
+    count = bufs["sel_count"].cpu().numpy()
+    ou, op = out_u.float().cpu().numpy(), out_p.float().cpu().numpy()
+    assert np.all(np.abs(ou - op) <= 1e-2 * np.maximum(1.0, np.abs(op)))
+    rng = np.random.default_rng(1)
+    for h in range(w.heads):
+        g = h // w.group
+        for t in list(rng.choice(T, size=8, replace=False)) + [T - 1]:
+            wi = h * T + t
+            q = Q[0, h, t]
+            toks = P.gpu_tokens(blocks[wi], count[wi], w.chunk, T0)
+            keys = np.concatenate([toks, np.arange(T0, T0 + t + 1)])
+            ref, _ = O.attend(keys, q.astype(np.float64), K[0, g].astype(np.float64),
+                              V[0, g].astype(np.float64), w.sharpness)
+            for o in (ou[0, h, t], op[0, h, t]):
+                ok, e = P.out_ok(o, ref, w.dtype)
+                assert ok, (h, t, e)
 
 
 def test_prefill_forward_appends_after_search(Z):

@@ -354,7 +354,8 @@ __global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
     }
     if (myq >= T) return;
     // the walk's last item: {m, l, unnormalised sum of p * v}
-    float *part = a.part + static_cast<int64_t>(a.item_off[walk + 1] - 1) * (D + 2);
+    float *part = a.bpart ? a.bpart + walk * (D + 2)
+                          : a.part + static_cast<int64_t>(a.item_off[walk + 1] - 1) * (D + 2);
 #pragma unroll
     for (int i = 0; i < DT; ++i)
 #pragma unroll
@@ -403,6 +404,18 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
         }
     }
     hipLaunchKernelGGL((k_attn_combine<D, KT>), dim3(a.walks), dim3(D), 0, st, a);
+    return hipGetLastError();
+}
+
+// The block's own keys of a bf16 prefill block alone (the union path
+// merges them itself).
+hipError_t launch_attn_block(const AttnArgs &a, int D, hipStream_t st) {
+    const int qtiles = (a.qph + 63) / 64;
+    const dim3 grid(static_cast<unsigned>(a.walks / a.qph * qtiles));
+    if (D == 64)
+        hipLaunchKernelGGL((k_attn_block<64>), grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_attn_block<128>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

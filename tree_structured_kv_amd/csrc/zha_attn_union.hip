@@ -1,31 +1,35 @@
-// zha_attn_union.hip -- decode attention over each (sequence, KV head)
-// pair's union of selected blocks.
+// zha_attn_union.hip -- attention over the union of the selected blocks of a
+// group of walks that share a KV cache, one matrix-core column per walk.
 //
 // [ZHA lesson] = the page "How does a tree of summaries search a context? How
 // ZHA works".  "Common misunderstandings": every query head walks on its own
-// and attends exactly the original keys it selected; the heads of a group
-// share the K/V cache, so a block several heads selected is read once here
-// and used for each of them, with a head mask per block.
+// and attends exactly the original keys it selected.  Walks that share a KV
+// cache often select the same blocks; here such a block is read once and
+// used for every walk of the group that selected it, with a walk mask per
+// block.  A group is
+//   decode (q_per_head = 1): the G query heads of a (sequence, KV head) pair;
+//   prefill blocks: 16 consecutive queries of one query head.
 //
-//   k_ua_fill    clears the pair's block masks (one bit per head of the group);
-//   k_ua_mark    one workgroup per walk sets its head bit on every block it
-//                selected;
-//   k_ua_attn    workgroup r of pair p takes a range of chunks: chunk j is the
-//                selected blocks among level-1 blocks [j*kUaBlocks,
-//                (j+1)*kUaBlocks); the pair's last workgroup also takes the
-//                raw tail, which every head attends.  A chunk's blocks are
-//                compacted in LDS; each wavefront takes 16-key tiles, computes the
-//                logits of all heads at once with bf16 16x16x16 matrix
-//                products S^T = K Q^T (rows = keys, columns = heads), masks
-//                the heads that did not select a key's block, keeps an online
-//                softmax per head in fp32 and accumulates O^T += V^T P^T with
-//                bf16 16x16x16 products (V exact, P as the sum of two bf16
-//                parts, fp32 sums), its state carried across the chunks;
-//                the wavefronts' states are merged in LDS into one partial
-//                per (workgroup, head);
-//   k_ua_combine one workgroup per walk merges its pair's partials.
-// The per-head result is the same softmax over the same key set as the
-// per-walk kernels of zha_attn.hip, summed in another order.
+//   k_ua_fill    clears the groups' block masks (16 bits per level-1 block,
+//                one per column) and chunk bits (one per kUaBlocks blocks);
+//   k_ua_mark    one wavefront per walk sets its column bit on every block it
+//                selected, and the bit of each chunk holding one;
+//   k_ua_attn    workgroup r of group g takes a range of chunks (the group's
+//                last workgroup also the raw tail, which every walk attends);
+//                a marked chunk's blocks are compacted in LDS; each wavefront
+//                takes 16-key tiles, computes the logits of all columns at
+//                once with bf16 16x16x16 matrix products S^T = K Q^T (rows =
+//                keys, columns = walks), masks the columns that did not
+//                select a key's block, keeps an online softmax per column in
+//                fp32 and accumulates O^T += V^T P^T with bf16 products (V
+//                exact, P as the sum of two bf16 parts, fp32 sums), its state
+//                carried across the chunks; the wavefronts' states are merged
+//                in LDS into one partial per (workgroup, column);
+//   k_ua_combine one workgroup per decode walk merges its group's partials;
+//   k_ua_combine_pf one wavefront per prefill walk merges its group's
+//                partials with the block's own keys (k_attn_block).
+// A walk's result is the same softmax over the same key set as the per-walk
+// kernels of zha_attn.hip, summed in another order.
 #include "zha_device.h"
 #include "zha_internal.h"
 
@@ -47,59 +51,110 @@ __device__ __forceinline__ short4_t pk4(uint32_t lo, uint32_t hi) {
     return r;
 }
 
+// The KV pair of group g.
+__device__ __forceinline__ int64_t ua_pair(const AttnArgs &a, int64_t g) {
+    if (a.qph == 1) return g;
+    const int64_t hq = g / a.qtiles;             // sequence * heads + query head
+    return (hq / a.heads) * a.kv_heads + (hq % a.heads) / a.group;
+}
+
+// The walk of column col of group g, or -1 past the group's walks.
+__device__ __forceinline__ int64_t ua_walk(const AttnArgs &a, int64_t g, int col) {
+    if (a.qph == 1) return col < a.group ? g * a.group + col : -1;
+    const int64_t hq = g / a.qtiles;
+    const int t = static_cast<int>(g - hq * a.qtiles) * 16 + col;
+    return t < a.qph ? hq * a.qph + t : -1;
+}
+
+// Group and column of walk w.
+__device__ __forceinline__ void ua_slot(const AttnArgs &a, int64_t w, int64_t &g, int &col) {
+    if (a.qph == 1) {
+        g = w / a.group;
+        col = static_cast<int>(w - g * a.group);
+        return;
+    }
+    const int64_t hq = w / a.qph;
+    const int t = static_cast<int>(w - hq * a.qph);
+    g = hq * a.qtiles + t / 16;
+    col = t % 16;
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(256) void k_ua_fill(AttnArgs a) {
-    const int64_t n = static_cast<int64_t>(a.pairs) * a.n1;
+    const int64_t mw = (a.n1 + 1) / 2;           // mask words in use per group
+    const int64_t fw = mw + a.cwords;
+    const int64_t n = a.ugroups * fw;
+    uint32_t *mask = reinterpret_cast<uint32_t *>(a.umask);
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
          i += static_cast<int64_t>(gridDim.x) * 256) {
-        const int64_t p = i / a.n1, b = i - p * a.n1;
-        a.umask[p * a.n1cap + b] = 0u;
+        const int64_t g = i / fw, k = i - g * fw;
+        if (k < mw)
+            mask[g * (a.n1cap / 2) + k] = 0u;
+        else
+            a.uchunk[g * a.cwords + (k - mw)] = 0u;
     }
 }
 
 __global__ __launch_bounds__(256) void k_ua_mark(AttnArgs a) {
-    const int w = blockIdx.x;
-    const int64_t pair = walk_pair(w, 1, a.heads, a.group, a.kv_heads);
-    const uint32_t bit = 1u << (w % a.group);
+    const int lane = threadIdx.x & 63;
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (w >= a.walks) return;
+    int64_t g;
+    int col;
+    ua_slot(a, w, g, col);
     int64_t nb = a.sel_count[w];
     if (nb > a.sel_cap) nb = a.sel_cap;
-    const int32_t *sel = a.sel_blocks + static_cast<int64_t>(w) * a.sel_cap;
-    for (int64_t i = threadIdx.x; i < nb; i += 256) {
+    const int32_t *sel = a.sel_blocks + w * a.sel_cap;
+    uint32_t *mask = reinterpret_cast<uint32_t *>(a.umask) + g * (a.n1cap / 2);
+    uint32_t *chunks = a.uchunk + g * a.cwords;
+    int last = -1;                                 // this lane's last chunk marked
+    for (int64_t i = lane; i < nb; i += 64) {
         const int32_t blk = sel[i];
-        if (blk >= 0 && blk < a.n1) atomicOr(a.umask + pair * a.n1cap + blk, bit);
+        if (blk < 0 || blk >= a.n1) continue;
+        atomicOr(mask + (blk >> 1), (1u << col) << (16 * (blk & 1)));
+        const int ch = blk / kUaBlocks;
+        if (ch != last) {
+            atomicOr(chunks + (ch >> 5), 1u << (ch & 31));
+            last = ch;
+        }
     }
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
     constexpr int DS = D / 16;            // bf16 16x16x16 steps of a logit
-    constexpr int DT = D / 16;            // row tiles of O^T: row i of tile r is d = DT*i + r
+    constexpr int DT = D / 16;            // row tiles of O^T: row i of tile q is d = DT*i + q
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const int c = a.chunk, log2c = a.log2c, G = a.group, wpp = a.items_pp;
-    const int p = blockIdx.x / wpp, r = blockIdx.x - p * wpp;
+    const int c = a.chunk, log2c = a.log2c, wpg = a.items_pp;
+    const int64_t g = blockIdx.x / wpg;
+    const int r = static_cast<int>(blockIdx.x - g * wpg);
+    const int64_t p = ua_pair(a, g);
     const int nchunks = static_cast<int>((a.n1 + kUaBlocks - 1) / kUaBlocks);
     const int j0 = r * a.ua_cpw, j1 = min(nchunks, j0 + a.ua_cpw);
-    const int jend = j1 + (r == wpp - 1 ? 1 : 0);   // the last workgroup also takes the tail
+    const int jend = j1 + (r == wpg - 1 ? 1 : 0);   // the last workgroup also takes the tail
     const float s = a.sharpness;
     const int64_t tail0 = static_cast<int64_t>(c) * a.n1;
     const int tail_keys = static_cast<int>(a.n_tokens - tail0);
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const uint16_t *gmask = a.umask + g * a.n1cap;
+    const uint32_t *gchunks = a.uchunk + g * a.cwords;
     __shared__ int32_t s_blk[kUaBlocks];
     __shared__ uint32_t s_msk[kUaBlocks];
     __shared__ int32_t s_cnt[2];
     __shared__ float s_m[kUaWaves][16], s_l[kUaWaves][16];
     __shared__ float s_o[kUaWaves][D * 16];
-    const bf16_t *kc = static_cast<const bf16_t *>(a.k) + static_cast<int64_t>(p) * a.max_tokens * D;
-    const bf16_t *vc = static_cast<const bf16_t *>(a.v) + static_cast<int64_t>(p) * a.max_tokens * D;
-    // B operand of S^T: lane (head col, group grp) holds the query of head
-    // col at elements 32*(st/2) + 8*grp + 4*(st%2) .. +3 (zero past G)
-    const bool hv = col < G;
+    const bf16_t *kc = static_cast<const bf16_t *>(a.k) + p * a.max_tokens * D;
+    const bf16_t *vc = static_cast<const bf16_t *>(a.v) + p * a.max_tokens * D;
+    // B operand of S^T: lane (column col, group grp) holds the query of
+    // column col at elements 32*(st/2) + 8*grp + 4*(st%2) .. +3 (zero past
+    // the group's walks)
+    const int64_t qw = ua_walk(a, g, col);
+    const bool hv = qw >= 0;
     short4_t qb[DS];
     {
-        const int64_t qw = static_cast<int64_t>(p) * G + (hv ? col : 0);   // walk of head col
-        const bf16_t *qr = static_cast<const bf16_t *>(a.q) + qw * D + 8 * grp;
+        const bf16_t *qr = static_cast<const bf16_t *>(a.q) + (hv ? qw : 0) * D + 8 * grp;
 #pragma unroll
         for (int m = 0; m < DS / 2; ++m) {
             gu4_t v = gload_u4(qr + 32 * m);
@@ -108,7 +163,7 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
             qb[2 * m + 1] = pk4(v.z, v.w);
         }
     }
-    // online softmax state of head col, kept across the workgroup's chunks
+    // online softmax state of column col, kept across the workgroup's chunks
     float m_run = -INFINITY, l_run = 0.f;
     float4_t acc[DT];
 #pragma unroll
@@ -117,12 +172,13 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
 
     for (int j = j0; j < jend; ++j) {
         const bool tail_item = j >= j1;
+        if (!tail_item && !((gchunks[j >> 5] >> (j & 31)) & 1u)) continue;   // no block selected here
         // the chunk's selected blocks, in order (two wavefronts of 64 entries)
         uint32_t mk = 0u;
         unsigned long long bal = 0ull;
         const int b = j * kUaBlocks + (wave & 1) * 64 + lane;
         if (!tail_item && wave < 2) {
-            mk = (b < a.n1) ? a.umask[static_cast<int64_t>(p) * a.n1cap + b] : 0u;
+            mk = (b < a.n1) ? gmask[b] : 0u;
             bal = __ballot(mk != 0u);
             if (lane == 0) s_cnt[wave] = __popcll(bal);
         }
@@ -176,7 +232,7 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
             float4_t sa = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < DS; ++st) sa = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(T.kb[st], qb[st], sa, 0, 0, 0);
-            // logits of head col for keys kbase + 4*grp + e; masked: -inf
+            // logits of column col for keys kbase + 4*grp + e; masked: -inf
             float x[4], tmax = -INFINITY;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -240,7 +296,7 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
         if (tid == 0) a.ic[blockIdx.x] = 0;
         return;
     }
-    // merge the wavefronts' states per head
+    // merge the wavefronts' states per column
     if (grp == 0) {
         s_m[wave][col] = m_run;
         s_l[wave][col] = l_run;
@@ -252,7 +308,6 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
     __syncthreads();
     for (int i = tid; i < D * 16; i += 256) {
         const int d = i >> 4, h = i & 15;
-        if (h >= G) continue;
         float mm = -INFINITY;
 #pragma unroll
         for (int v = 0; v < kUaWaves; ++v) mm = fmaxf(mm, s_m[v][h]);
@@ -266,7 +321,7 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
                 oo = fmaf(s_o[v][d * 16 + h], f, oo);
             }
         }
-        float *part = a.part + (static_cast<int64_t>(blockIdx.x) * G + h) * (D + 2);
+        float *part = a.part + (static_cast<int64_t>(blockIdx.x) * 16 + h) * (D + 2);
         part[2 + d] = oo;
         if (d == 0) {
             part[0] = mm;
@@ -276,23 +331,24 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
     if (tid == 0) a.ic[blockIdx.x] = 1;
 }
 
-// One workgroup per walk: its pair's item flags staged in LDS, then each
-// wavefront merges every fourth item (online, one pass), then the four
-// states are merged.
+// Decode: one workgroup per walk: its group's workgroup flags staged in LDS,
+// then each wavefront merges every fourth partial (online, one pass), then
+// the four states are merged.
 template <int D>
 __global__ __launch_bounds__(256) void k_ua_combine(AttnArgs a) {
     constexpr int EPL = D / 64;           // output elements per lane
     const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t p = walk_pair(w, 1, a.heads, a.group, a.kv_heads);
-    const int h = w % a.group, ipp = a.items_pp;
-    const int64_t i0 = p * ipp;
+    int64_t g;
+    int col;
+    ua_slot(a, w, g, col);
+    const int wpg = a.items_pp;
+    const int64_t i0 = g * wpg;
     __shared__ int32_t s_items[kUaMaxItems];
     __shared__ int32_t s_n;
     __shared__ float s_m[kUaWaves], s_l[kUaWaves], s_acc[kUaWaves][D];
-    // the items that wrote partials, in order
     if (tid == 0) s_n = 0;
     __syncthreads();
-    for (int j = tid; j < ipp; j += 256)
+    for (int j = tid; j < wpg; j += 256)
         if (a.ic[i0 + j] != 0) s_items[atomicAdd(&s_n, 1)] = j;
     __syncthreads();
     const int n = s_n;
@@ -300,7 +356,7 @@ __global__ __launch_bounds__(256) void k_ua_combine(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < EPL; ++k) acc[k] = 0.f;
     for (int x = wave; x < n; x += kUaWaves) {
-        const float *pp = a.part + ((i0 + s_items[x]) * a.group + h) * (D + 2);
+        const float *pp = a.part + ((i0 + s_items[x]) * 16 + col) * (D + 2);
         const float pm = pp[0], pls = pp[1];
         float v[EPL];
 #pragma unroll
@@ -339,18 +395,62 @@ __global__ __launch_bounds__(256) void k_ua_combine(AttnArgs a) {
     }
 }
 
+// Prefill: one wavefront per walk merges its group's partials (in order)
+// and the partial of the block's own keys (bpart, from k_attn_block).
+template <int D>
+__global__ __launch_bounds__(256) void k_ua_combine_pf(AttnArgs a) {
+    constexpr int EPL = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (w >= a.walks) return;
+    int64_t g;
+    int col;
+    ua_slot(a, w, g, col);
+    const int wpg = a.items_pp;
+    float m = -INFINITY, l = 0.f, acc[EPL];
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) acc[k] = 0.f;
+    auto merge = [&](const float *pp) {
+        const float pm = pp[0], pls = pp[1];
+        float v[EPL];
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) v[k] = pp[2 + lane * EPL + k];
+        if (!(pm > -INFINITY)) return;
+        const float mn = fmaxf(m, pm);
+        const float c1 = (m > -INFINITY) ? expf(m - mn) : 0.f, c2 = expf(pm - mn);
+        l = l * c1 + pls * c2;
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) acc[k] = acc[k] * c1 + v[k] * c2;
+        m = mn;
+    };
+    for (int r = 0; r < wpg; ++r)
+        if (a.ic[g * wpg + r] != 0) merge(a.part + ((g * wpg + r) * 16 + col) * (D + 2));
+    merge(a.bpart + w * (D + 2));
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) {
+        const float o = (l > 0.f) ? acc[k] / l : 0.f;
+        Elem<bf16_t>::store(static_cast<bf16_t *>(a.out), w * D + lane * EPL + k, o);
+    }
+}
+
 template <int D>
 static hipError_t launch_ua_t(const AttnArgs &a, hipStream_t st) {
-    const int64_t fill = static_cast<int64_t>(a.pairs) * a.n1;
-    const int fill_grid = static_cast<int>(fill / 256 + 1 < 2048 ? fill / 256 + 1 : 2048);
-    hipLaunchKernelGGL(k_ua_fill, dim3(fill_grid), dim3(256), 0, st, a);
+    const int64_t fill = a.ugroups * ((a.n1 + 1) / 2 + a.cwords);
+    const int64_t fg = fill / 256 + 1;
+    hipLaunchKernelGGL(k_ua_fill, dim3(static_cast<unsigned>(fg < 4096 ? fg : 4096)), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_ua_mark, dim3(a.walks), dim3(256), 0, st, a);
+    const int64_t wg4 = (a.walks + 3) / 4;
+    hipLaunchKernelGGL(k_ua_mark, dim3(static_cast<unsigned>(wg4)), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_ua_attn<D>), dim3(static_cast<unsigned>(a.pairs * a.items_pp)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_ua_attn<D>), dim3(static_cast<unsigned>(a.ugroups * a.items_pp)), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_ua_combine<D>), dim3(a.walks), dim3(256), 0, st, a);
+    if (a.qph == 1) {
+        hipLaunchKernelGGL((k_ua_combine<D>), dim3(a.walks), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
+    if ((e = launch_attn_block(a, D, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_ua_combine_pf<D>), dim3(static_cast<unsigned>(wg4)), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -157,51 +157,66 @@ int64_t tree_keys_bound(const zha_tree *t, const zha_select *sel, int32_t qph) {
     return int64_t(sel->max_blocks_per_walk) * t->geom.chunk + t->geom.chunk - 1 + (qph > 1 ? qph : 0);
 }
 
-// The union attention path: decode over bf16 caches, at most 16 query heads
-// per KV head (one matrix-core column per head), at most kUaMaxItems work
-// items per pair.
+// The union attention path: bf16 caches; decode with at most 16 query heads
+// per KV head (one matrix-core column per head), or a prefill block (16
+// consecutive queries of a head per group).
+struct UnionGeom {
+    int64_t ugroups, n1cap, nchunks, cwords, wpg_max, qtiles;
+};
+UnionGeom union_geom(const zha_tree *t, int32_t qph) {
+    const zha_geometry &g = t->geom;
+    UnionGeom u;
+    const int64_t pairs = int64_t(g.batch) * g.num_kv_heads;
+    u.qtiles = qph > 1 ? (qph + 15) / 16 : 1;
+    u.ugroups = qph > 1 ? int64_t(g.batch) * g.num_kv_heads * g.group_size * u.qtiles : pairs;
+    u.n1cap = (g.max_tokens / g.chunk + 1) / 2 * 2;
+    u.nchunks = (u.n1cap + kUaBlocks - 1) / kUaBlocks;
+    u.cwords = (u.nchunks + 31) / 32;
+    u.wpg_max = qph > 1 ? 1 : std::max<int64_t>(1, std::min<int64_t>(4096 / pairs, u.nchunks));
+    return u;
+}
+
 bool union_attn_ok(const zha_tree *t, int32_t qph) {
-    const int64_t items = (t->geom.max_tokens / t->geom.chunk + kUaBlocks - 1) / kUaBlocks + 1;
-    return qph == 1 && t->geom.dtype == ZHA_BF16 && t->geom.group_size <= 16 && items <= kUaMaxItems;
+    if (t->geom.dtype != ZHA_BF16) return false;
+    if (qph == 1 && t->geom.group_size > 16) return false;
+    const UnionGeom u = union_geom(t, qph);
+    return u.wpg_max <= kUaMaxItems && u.ugroups * u.wpg_max < (int64_t(1) << 31);
 }
 
 // ZHA_ATTN_* a call runs (ZHA_ATTN_UNION only where union_attn_ok).
 int resolve_attn(const zha_tree *t, const zha_select *sel, int32_t qph) {
     if (sel->attn_engine != ZHA_ATTN_AUTO) return sel->attn_engine;
-    return (union_attn_ok(t, qph) && t->geom.group_size == 16) ? ZHA_ATTN_UNION : ZHA_ATTN_PER_WALK;
+    if (!union_attn_ok(t, qph)) return ZHA_ATTN_PER_WALK;
+    return (qph > 1 || t->geom.group_size == 16) ? ZHA_ATTN_UNION : ZHA_ATTN_PER_WALK;
 }
 
 struct AttnWs {
-    uint64_t part, item_off, item_walk, umask, ic, upart, total;
-    int64_t n1cap, ipp;
+    uint64_t part, item_off, item_walk, umask, uchunk, ic, upart, bpart, total;
+    UnionGeom u;
 };
-// Per-walk items; with `t` (a decode call that may take the union path) also
-// the union arrays.
-AttnWs attn_ws_layout(int head_dim, int64_t keys_bound, int64_t walks, const zha_tree *t = nullptr) {
+// Per-walk items; with `t` (a call that may take the union path) also the
+// union arrays.
+AttnWs attn_ws_layout(int head_dim, int64_t keys_bound, int64_t walks, const zha_tree *t = nullptr,
+                      int32_t qph = 1) {
     const uint64_t items = static_cast<uint64_t>(attn_max_items(keys_bound, walks));
     AttnWs l;
     l.part = 0;
     l.item_off = align_up(items * (head_dim + 2) * sizeof(float));
     l.item_walk = l.item_off + align_up(uint64_t(walks + 2) * sizeof(int32_t));
     l.umask = l.item_walk + align_up(items * sizeof(int32_t));
-    l.n1cap = 0;
-    l.ipp = 0;
-    uint64_t pairs = 0;
-    if (t && union_attn_ok(t, 1)) {
-        pairs = uint64_t(t->geom.batch) * t->geom.num_kv_heads;
-        l.n1cap = t->geom.max_tokens / t->geom.chunk;
-        l.ipp = (l.n1cap + kUaBlocks - 1) / kUaBlocks + 1;
-    }
-    l.ic = l.umask + align_up(pairs * uint64_t(l.n1cap) * sizeof(uint32_t));
-    l.upart = l.ic + align_up(pairs * uint64_t(l.ipp) * sizeof(int32_t));
-    const uint64_t g = t ? uint64_t(t->geom.group_size) : 0;
-    l.total = l.upart + align_up(pairs * uint64_t(l.ipp) * g * (head_dim + 2) * sizeof(float));
+    const bool uni = t && union_attn_ok(t, qph);
+    l.u = uni ? union_geom(t, qph) : UnionGeom{0, 0, 0, 0, 0, 1};
+    const uint64_t ng = uint64_t(l.u.ugroups);
+    l.uchunk = l.umask + align_up(ng * uint64_t(l.u.n1cap) * sizeof(uint16_t));
+    l.ic = l.uchunk + align_up(ng * uint64_t(l.u.cwords) * sizeof(uint32_t));
+    l.upart = l.ic + align_up(ng * uint64_t(l.u.wpg_max) * sizeof(int32_t));
+    l.bpart = l.upart + align_up(ng * uint64_t(l.u.wpg_max) * 16 * (head_dim + 2) * sizeof(float));
+    l.total = l.bpart + align_up((uni && qph > 1 ? uint64_t(walks) : 0) * (head_dim + 2) * sizeof(float));
     return l;
 }
 
 uint64_t attn_ws_bytes(const zha_tree *t, const zha_select *sel, int32_t qph) {
-    return attn_ws_layout(t->geom.head_dim, tree_keys_bound(t, sel, qph), walks_of(&t->geom, qph),
-                          qph == 1 ? t : nullptr).total;
+    return attn_ws_layout(t->geom.head_dim, tree_keys_bound(t, sel, qph), walks_of(&t->geom, qph), t, qph).total;
 }
 
 struct ForwardWs {
@@ -404,7 +419,7 @@ zha_status do_attn(const zha_tree *t, const void *q, int32_t qph, const void *k_
     a.tokens = tokens;
     a.sel_count = sel_count;
     const bool uni = attn_engine == ZHA_ATTN_UNION && tokens == nullptr;
-    AttnWs lay = attn_ws_layout(g.head_dim, keys_bound, walks, uni ? t : nullptr);
+    AttnWs lay = attn_ws_layout(g.head_dim, keys_bound, walks, uni ? t : nullptr, qph);
     char *wb = static_cast<char *>(ws);
     a.part = reinterpret_cast<float *>(wb + lay.part);
     a.item_off = reinterpret_cast<int32_t *>(wb + lay.item_off);
@@ -426,17 +441,22 @@ zha_status do_attn(const zha_tree *t, const void *q, int32_t qph, const void *k_
     a.pairs = g.batch * g.num_kv_heads;
     a.log2c = ilog2(g.chunk);
     if (uni) {
-        a.umask = reinterpret_cast<uint32_t *>(wb + lay.umask);
+        a.umask = reinterpret_cast<uint16_t *>(wb + lay.umask);
+        a.uchunk = reinterpret_cast<uint32_t *>(wb + lay.uchunk);
         a.ic = reinterpret_cast<int32_t *>(wb + lay.ic);
         a.part = reinterpret_cast<float *>(wb + lay.upart);
-        a.n1cap = lay.n1cap;
-        // about 4096 workgroups in all, each over a contiguous range of chunks
+        a.bpart = qph > 1 ? reinterpret_cast<float *>(wb + lay.bpart) : nullptr;
+        a.n1cap = lay.u.n1cap;
+        a.ugroups = lay.u.ugroups;
+        a.cwords = static_cast<int32_t>(lay.u.cwords);
+        a.qtiles = static_cast<int32_t>(lay.u.qtiles);
+        // decode: about 4096 workgroups in all, each over a contiguous range
+        // of chunks; prefill: one workgroup per group, over all chunks
         const int64_t nchunks = (a.n1 + kUaBlocks - 1) / kUaBlocks;
-        int64_t wpp = std::max<int64_t>(1, 4096 / a.pairs);
-        if (wpp > nchunks) wpp = std::max<int64_t>(1, nchunks);
-        const int64_t cpw = nchunks > 0 ? (nchunks + wpp - 1) / wpp : 0;
-        if (cpw > 0) wpp = (nchunks + cpw - 1) / cpw;
-        a.items_pp = static_cast<int32_t>(wpp);
+        int64_t wpg = std::min<int64_t>(lay.u.wpg_max, std::max<int64_t>(1, nchunks));
+        const int64_t cpw = nchunks > 0 ? (nchunks + wpg - 1) / wpg : 0;
+        if (cpw > 0) wpg = (nchunks + cpw - 1) / cpw;
+        a.items_pp = static_cast<int32_t>(wpg);
         a.ua_cpw = static_cast<int32_t>(cpw);
         return hip_status(launch_attn_union(a, g.head_dim, st));
     }

@@ -143,11 +143,18 @@ struct AttnArgs {
     int32_t block_mfma;            // prefill: the block's own keys go to k_attn_block
                                    // (one extra item per walk, the last one)
     float sharpness;
-    // union path (decode): per pair, the union of its heads' selected blocks
-    uint32_t *umask;               // ws [pairs][n1cap]  heads that selected each level-1 block
-    int32_t *ic;                   // ws [pairs][items_pp]  1: the item wrote partials
-    int64_t n1cap;                 // level-1 blocks per pair (stride of umask)
-    int32_t items_pp;              // workgroups (partials) per pair
+    // union path: per group of walks sharing a KV cache (decode: a pair's
+    // heads; prefill: 16 consecutive queries of a head), the union of their
+    // selected blocks, one column per walk
+    uint16_t *umask;               // ws [ugroups][n1cap]  columns that selected each level-1 block
+    uint32_t *uchunk;              // ws [ugroups][cwords]  chunks of kUaBlocks blocks holding one
+    int32_t *ic;                   // ws [ugroups][items_pp]  1: the workgroup wrote partials
+    float *bpart;                  // ws [walks][D + 2]  prefill: the block's own keys (k_attn_block)
+    int64_t n1cap;                 // level-1 blocks per group (stride of umask, even)
+    int64_t ugroups;
+    int32_t cwords;
+    int32_t qtiles;                // prefill: groups per (sequence, query head)
+    int32_t items_pp;              // workgroups (partials) per group
     int32_t ua_cpw;                // kUaBlocks-block chunks per workgroup
     int32_t pairs;
     int32_t log2c;
@@ -178,6 +185,7 @@ hipError_t launch_union(const SearchArgs &a, int D, int R, int dtype, int sdtype
 hipError_t launch_block(const SearchArgs &a, int D, int R, int dtype, int sdtype, int n0, hipStream_t st);
 hipError_t launch_attn(const AttnArgs &a, int D, int dtype, hipStream_t st);
 hipError_t launch_attn_union(const AttnArgs &a, int D, hipStream_t st);
+hipError_t launch_attn_block(const AttnArgs &a, int D, hipStream_t st);
 hipError_t launch_dense(const DenseArgs &a, int D, int dtype, hipStream_t st);
 hipError_t launch_probe(const void *buf, uint64_t bytes, float *sink, hipStream_t st);
 
