@@ -79,6 +79,8 @@ enum { ZHA_TOPP = 0, ZHA_TOPK = 1 };
  *     the union of its query heads' candidates with a head mask per node;
  *     every node record is read once and scored for all heads of the group
  *     (fp32 matrix-core tiles), then each head cuts its own candidates.
+ *     With fewer than 16 heads per KV head the last two steps (the widest,
+ *     where the heads' lists overlap least) run level-synchronously.
  *     Decode only (q_per_head = 1), group_size <= 16.
  *   ZHA_ENGINE_BLOCK: for prefill blocks (any q_per_head): the walks are
  *     grouped by the parent node they opened and each parent's children are
@@ -86,8 +88,9 @@ enum { ZHA_TOPP = 0, ZHA_TOPK = 1 };
  *     list is scored against every walk the same way.  One wavefront cuts
  *     each walk.
  *   ZHA_ENGINE_AUTO: block for prefill (q_per_head > 1), else union for
- *     decode with 16 query heads per KV head and at least 64 walks, else
- *     level-synchronous for top-p with at least 64 walks, else persistent. */
+ *     decode with at least 64 walks and 16 query heads per KV head, or 8 to
+ *     16 under top-p, else level-synchronous for top-p with at least 64
+ *     walks, else persistent. */
 enum {
     ZHA_ENGINE_AUTO = 0,
     ZHA_ENGINE_PERSISTENT = 1,

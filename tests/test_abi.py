@@ -247,6 +247,11 @@ def test_search_engine_resolution(Z):
     assert Z.zha_search_engine(wide, topp, 2) == "block"
     big = _handle(Z, batch=4, kv_heads=1, group=32)
     assert Z.zha_search_engine(big, Z.make_select("topp", 0.9, max_blocks=64, engine="union")) is None
+    eight = _handle(Z, batch=4, kv_heads=2, group=8)     # 64 decode walks, 8 heads per KV head
+    assert Z.zha_search_engine(eight, topp) == "union"
+    assert Z.zha_search_engine(eight, topk) == "persistent"
+    four = _handle(Z, batch=8, kv_heads=2, group=4)      # 64 walks, 4 heads per KV head
+    assert Z.zha_search_engine(four, topp) == "level-sync"
 
 
 def test_sweep_depth_policy_and_nested_inputs():

@@ -12,8 +12,8 @@
 //
 //   k_ua_fill    clears the groups' block masks (16 bits per level-1 block,
 //                one per column) and chunk bits (one per kUaBlocks blocks);
-//   k_ua_mark    one wavefront per walk sets its column bit on every block it
-//                selected, and the bit of each chunk holding one;
+//   k_ua_mark    each walk sets its column bit on every block it selected,
+//                and the bit of each chunk holding one;
 //   k_ua_attn    workgroup r of group g takes a range of chunks (the group's
 //                last workgroup also the raw tail, which every walk attends);
 //                a marked chunk's blocks are compacted in LDS; each wavefront
@@ -96,9 +96,15 @@ __global__ __launch_bounds__(256) void k_ua_fill(AttnArgs a) {
     }
 }
 
+// A workgroup marks one decode walk (256 lanes) or four prefill walks (64
+// lanes each).  A walk's list is in ascending order, so the lanes of a
+// wavefront see consecutive entries: only the first lane of each run of
+// equal chunks sets the chunk bit (a handful of words per group take them).
 __global__ __launch_bounds__(256) void k_ua_mark(AttnArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int per = a.qph == 1 ? 256 : 64;        // lanes per walk
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * (256 / per) + tid / per;
+    const int sub = tid % per;
     if (w >= a.walks) return;
     int64_t g;
     int col;
@@ -108,15 +114,15 @@ __global__ __launch_bounds__(256) void k_ua_mark(AttnArgs a) {
     const int32_t *sel = a.sel_blocks + w * a.sel_cap;
     uint32_t *mask = reinterpret_cast<uint32_t *>(a.umask) + g * (a.n1cap / 2);
     uint32_t *chunks = a.uchunk + g * a.cwords;
-    int last = -1;                                 // this lane's last chunk marked
-    for (int64_t i = lane; i < nb; i += 64) {
-        const int32_t blk = sel[i];
-        if (blk < 0 || blk >= a.n1) continue;
-        atomicOr(mask + (blk >> 1), (1u << col) << (16 * (blk & 1)));
-        const int ch = blk / kUaBlocks;
-        if (ch != last) {
-            atomicOr(chunks + (ch >> 5), 1u << (ch & 31));
-            last = ch;
+    for (int64_t i0 = 0; i0 < nb; i0 += per) {
+        const int64_t i = i0 + sub;
+        const int32_t blk = i < nb ? sel[i] : -1;
+        const bool ok = blk >= 0 && blk < a.n1;
+        const int ch = ok ? blk / kUaBlocks : -1;
+        const int prev = __shfl_up(ch, 1, 64);
+        if (ok) {
+            atomicOr(mask + (blk >> 1), (1u << col) << (16 * (blk & 1)));
+            if (lane == 0 || prev != ch) atomicOr(chunks + (ch >> 5), 1u << (ch & 31));
         }
     }
 }
@@ -441,7 +447,7 @@ static hipError_t launch_ua_t(const AttnArgs &a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t wg4 = (a.walks + 3) / 4;
-    hipLaunchKernelGGL(k_ua_mark, dim3(static_cast<unsigned>(wg4)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_ua_mark, dim3(static_cast<unsigned>(a.qph == 1 ? a.walks : wg4)), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((k_ua_attn<D>), dim3(static_cast<unsigned>(a.ugroups * a.items_pp)), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

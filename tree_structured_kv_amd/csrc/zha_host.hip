@@ -283,6 +283,8 @@ int resolve_engine(const zha_tree *t, const zha_select *sel, int32_t qph) {
     const int64_t walks = walks_of(&t->geom, qph);
     if (qph > 1) return ZHA_ENGINE_BLOCK;
     if (qph == 1 && t->geom.group_size == 16 && walks >= 64) return ZHA_ENGINE_UNION;
+    if (qph == 1 && t->geom.group_size >= 8 && t->geom.group_size <= 16 && sel->mode == ZHA_TOPP && walks >= 64)
+        return ZHA_ENGINE_UNION;
     if (sel->mode == ZHA_TOPP && walks >= 64) return ZHA_ENGINE_LEVEL_SYNC;
     return ZHA_ENGINE_PERSISTENT;
 }
@@ -394,6 +396,14 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
             if (bound > kSmallList) break;
             a.small_steps = s + 1;
         }
+    }
+    // union engine with fewer than 16 heads per KV head: the heads' lists
+    // overlap less, and on the last two steps (the widest) the
+    // level-synchronous engine's per-walk scoring is faster; hand over there
+    a.ls_from = 0;
+    if (engine == ZHA_ENGINE_UNION && g.group_size < 16) {
+        const int from = std::max(a.small_steps + 1, g.levels - 2);
+        if (from < g.levels && from < ZHA_MAX_STEPS) a.ls_from = from;
     }
     if (engine == ZHA_ENGINE_BLOCK)
         return hip_status(launch_block(a, g.head_dim, g.num_refs, g.dtype, g.summary_dtype, static_cast<int>(n0), st));

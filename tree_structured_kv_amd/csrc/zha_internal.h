@@ -98,6 +98,7 @@ struct SearchArgs {
     int32_t pcap;                          // parents a walk keeps per step
     int64_t n_roots;                       // roots before clamping to cand_cap
     int32_t small_steps;                   // union engine: first steps done by one workgroup per pair
+    int32_t ls_from;                       // union engine: steps from here run level-synchronously (0: none)
     int32_t pairs;
     int64_t n_tokens;
     int32_t walks;
@@ -182,6 +183,7 @@ hipError_t launch_level(const LevelArgs &a, int D, int dtype, int sdtype, bool l
 hipError_t launch_search(const SearchArgs &a, int D, int R, int dtype, int sdtype, int engine, int n0,
                          hipStream_t st);
 hipError_t launch_union(const SearchArgs &a, int D, int R, int dtype, int sdtype, int n0, hipStream_t st);
+hipError_t launch_ls_from(const SearchArgs &a, int D, int R, int dtype, int sdtype, int t0, hipStream_t st);
 hipError_t launch_block(const SearchArgs &a, int D, int R, int dtype, int sdtype, int n0, hipStream_t st);
 hipError_t launch_attn(const AttnArgs &a, int D, int dtype, hipStream_t st);
 hipError_t launch_attn_union(const AttnArgs &a, int D, hipStream_t st);

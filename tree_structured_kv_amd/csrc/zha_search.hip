@@ -401,6 +401,47 @@ static hipError_t launch_t(const SearchArgs &a, int engine, int n0, hipStream_t 
     return hipSuccess;
 }
 
+// Steps t0 .. of the level-synchronous engine, after another engine wrote
+// the walks' state, candidate lists and scoring tiles of step t0.
+template <int D, int R, typename QT, typename ST>
+static hipError_t launch_ls_from_t(const SearchArgs &a, int t0, hipStream_t st) {
+    hipError_t e;
+    for (int t = t0; t < a.levels && t < ZHA_MAX_STEPS; ++t) {
+        hipLaunchKernelGGL((k_ls_score<D, R, QT, ST>), dim3(a.score_grid), dim3(kScoreThreads), 0, st, a, t, 1);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((k_ls_cut<R>), dim3(a.walks), dim3(kThreads), 0, st, a, t);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int D, typename QT, typename ST>
+static hipError_t launch_ls_from_d(const SearchArgs &a, int R, int t0, hipStream_t st) {
+    switch (R) {
+        case 1: return launch_ls_from_t<D, 1, QT, ST>(a, t0, st);
+        case 2: return launch_ls_from_t<D, 2, QT, ST>(a, t0, st);
+        case 4: return launch_ls_from_t<D, 4, QT, ST>(a, t0, st);
+        case 8: return launch_ls_from_t<D, 8, QT, ST>(a, t0, st);
+        case 16: return launch_ls_from_t<D, 16, QT, ST>(a, t0, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_ls_from(const SearchArgs &a, int D, int R, int dtype, int sdtype, int t0, hipStream_t st) {
+    if (D == 64) {
+        if (dtype == ZHA_BF16)
+            return sdtype == ZHA_BF16 ? launch_ls_from_d<64, bf16_t, bf16_t>(a, R, t0, st)
+                                      : launch_ls_from_d<64, bf16_t, float>(a, R, t0, st);
+        return sdtype == ZHA_BF16 ? launch_ls_from_d<64, float, bf16_t>(a, R, t0, st)
+                                  : launch_ls_from_d<64, float, float>(a, R, t0, st);
+    }
+    if (dtype == ZHA_BF16)
+        return sdtype == ZHA_BF16 ? launch_ls_from_d<128, bf16_t, bf16_t>(a, R, t0, st)
+                                  : launch_ls_from_d<128, bf16_t, float>(a, R, t0, st);
+    return sdtype == ZHA_BF16 ? launch_ls_from_d<128, float, bf16_t>(a, R, t0, st)
+                              : launch_ls_from_d<128, float, float>(a, R, t0, st);
+}
+
 template <int D, typename QT, typename ST>
 static hipError_t launch_search_d(const SearchArgs &a, int R, int engine, int n0, hipStream_t st) {
     switch (R) {

@@ -963,6 +963,54 @@ __global__ __launch_bounds__(kThreads) void k_un_small(SearchArgs a, int steps) 
     }
 }
 
+// Hand-over to the level-synchronous engine after the union cut of step t:
+// one workgroup per walk writes its candidates of step t+1 -- the children
+// of the list entries it opened, in order, exactly the list that engine's
+// own cut would have written -- as that engine's candidate list, sets its
+// walk state, finishes it if nothing remains, and registers its scoring
+// tiles.
+template <int R>
+__global__ __launch_bounds__(kThreads) void k_un_to_ls(SearchArgs a, int t) {
+    const int tid = threadIdx.x;
+    const int w = blockIdx.x;
+    const int p = w / a.group;
+    const int cap = a.cand_cap, c = a.chunk, log2c = a.log2c;
+    if (a.u_n[2 * p + (t & 1)] <= 0) return;      // the pair finished earlier; so did its walks
+    __shared__ WalkState st;
+    __shared__ int s_base;
+    if (tid == 0) st = a.state[w];
+    const uint32_t *ids = a.u_ids + (static_cast<int64_t>(p) * 2 + (t & 1)) * cap;
+    const int32_t *opened_pos = a.u_open + static_cast<int64_t>(w) * cap;
+    int64_t nn = static_cast<int64_t>(a.u_next[w]) * c;
+    const bool overflow = nn > cap;
+    if (overflow) nn = cap;
+    uint32_t *cur = a.cand + static_cast<int64_t>(w) * 2 * cap;     // buffer 0
+    for (int64_t x = tid; x < nn; x += kThreads) {
+        const uint32_t pid = ids[opened_pos[x >> log2c]];
+        const uint32_t lvl = pid >> kLevelShift, j = pid & kIndexMask;
+        cur[x] = ((lvl - 1u) << kLevelShift) | (j * static_cast<uint32_t>(c) + static_cast<uint32_t>(x & (c - 1)));
+    }
+    __syncthreads();
+    if (tid == 0) {
+        if (overflow) st.flags |= ZHA_FLAG_CAND_OVERFLOW;
+        st.buf = 0;
+        st.n = static_cast<int32_t>(nn);
+        if (st.n == 0 || t + 1 >= a.levels || t + 1 >= ZHA_MAX_STEPS) {
+            st.n = 0;
+            finish_walk<R>(a, w, st.steps, st.scored, st.opened, st.sel_n, st.unforced, st.flags);
+        }
+        a.state[w] = st;
+        s_base = 0;
+        if (st.n > 0 && !step_forced(a, t + 1, st.n))
+            s_base = atomicAdd(&a.tile_count[t + 1], (st.n + kTile - 1) / kTile);
+    }
+    __syncthreads();
+    if (st.n > 0 && !step_forced(a, t + 1, st.n)) {
+        const int ntile = (st.n + kTile - 1) / kTile;
+        for (int k = tid; k < ntile; k += kThreads) a.tile_map[s_base + k] = make_int2(w, k * kTile);
+    }
+}
+
 // Workgroups of the scorer that fit on the device at once (its wavefronts
 // take equal runs of blocks, so all of them should be resident), per device.
 template <typename K>
@@ -993,7 +1041,8 @@ static hipError_t launch_union_t(const SearchArgs &a, int n0, hipStream_t st) {
         hipLaunchKernelGGL((k_un_small<D, R, QT, ST>), dim3(a.pairs), dim3(kThreads), 0, st, a, t0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    for (int t = t0; t < a.levels && t < ZHA_MAX_STEPS; ++t) {
+    const int t1 = a.ls_from > 0 ? a.ls_from : a.levels;   // union steps: t0 .. t1-1
+    for (int t = t0; t < t1 && t < ZHA_MAX_STEPS; ++t) {
         const bool skip = (t == 0) && (n0 <= 1 || (a.mode == ZHA_TOPK && a.k[0] >= n0) ||
                                        (a.mode == ZHA_TOPP && a.p >= 1.0f));
         if (!skip) {
@@ -1003,9 +1052,16 @@ static hipError_t launch_union_t(const SearchArgs &a, int n0, hipStream_t st) {
         }
         hipLaunchKernelGGL((k_un_cut<R>), dim3(a.pairs * a.group), dim3(kThreads), 0, st, a, t);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((k_un_expand<R>), dim3(a.pairs * kExpSlices), dim3(kThreads), 0, st, a, t);
+        if (t + 1 == a.ls_from) {
+            hipLaunchKernelGGL((k_un_to_ls<R>), dim3(a.walks), dim3(kThreads), 0, st, a, t);
+        } else {
+            hipLaunchKernelGGL((k_un_expand<R>), dim3(a.pairs * kExpSlices), dim3(kThreads), 0, st, a, t);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    if (a.ls_from > 0)
+        return launch_ls_from(a, D, R, sizeof(QT) == 2 ? ZHA_BF16 : ZHA_F32, sizeof(ST) == 2 ? ZHA_BF16 : ZHA_F32,
+                              a.ls_from, st);
     return hipSuccess;
 }
 
