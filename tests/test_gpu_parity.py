@@ -256,7 +256,8 @@ def test_union_attention(Z, name, sname):
 
 
 def test_union_attention_given_lists(Z):
-    """Hand-made block lists: random sets, ids outside the live level (skipped),
+    """Hand-made block lists: random sorted sets (some with a repeated id,
+    which the union path takes once), ids outside the live level (skipped),
     entries past sel_count (ignored), empty lists (then only the 3-key raw
     tail, which every walk attends)."""
     w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, "mixed-small")
@@ -271,6 +272,9 @@ def test_union_attention_given_lists(Z):
     for wi in range(walks):
         k = int(rng.integers(0, cap + 1))
         ids = np.sort(rng.choice(n1 + 40, size=k, replace=False)).astype(np.int32)   # some past n1
+        if wi % 5 == 1 and k > 4:                     # repeat an id (runs of three on one mask word)
+            ids[2] = ids[1] = ids[3] if ids[3] % 2 == 1 else ids[1]
+            ids = np.sort(ids)
         blocks[wi, :k] = ids
         count[wi] = k if wi % 7 else 0
     tb = torch.from_numpy(blocks).cuda()
@@ -285,11 +289,15 @@ def test_union_attention_given_lists(Z):
         gi = h // w.group
         ids = blocks[wi, : count[wi]]
         ids = ids[(ids >= 0) & (ids < n1)]
+        repeated = len(np.unique(ids)) < len(ids)
+        ids = np.unique(ids)
         toks = np.sort(np.concatenate([(ids[:, None] * w.chunk + np.arange(w.chunk)).reshape(-1),
                                        np.arange(n1 * w.chunk, w.n)])).astype(np.int64)
         ref, _ = O.attend(toks, Q[b, h].astype(np.float64), K[b, gi].astype(np.float64),
                           V[b, gi].astype(np.float64), w.sharpness)
         for attn, o in outs.items():
+            if repeated and attn == "per-walk":
+                continue                      # the per-walk path attends a repeated block twice
             ok, e = P.out_ok(o.reshape(walks, -1)[wi], ref, w.dtype)
             assert ok, (attn, wi, e)
 

@@ -10,10 +10,9 @@
 //   decode (q_per_head = 1): the G query heads of a (sequence, KV head) pair;
 //   prefill blocks: 16 consecutive queries of one query head.
 //
-//   k_ua_fill    clears the groups' block masks (16 bits per level-1 block,
-//                one per column) and chunk bits (one per kUaBlocks blocks);
-//   k_ua_mark    each walk sets its column bit on every block it selected,
-//                and the bit of each chunk holding one;
+//   k_ua_build   the groups' block masks (16 bits per level-1 block, one per
+//                column: the walks that selected it) and chunk bits (one per
+//                kUaBlocks blocks), built in LDS one slice of blocks at a time;
 //   k_ua_attn    workgroup r of group g takes a range of chunks (the group's
 //                last workgroup also the raw tail, which every walk attends);
 //                a marked chunk's blocks are compacted in LDS; each wavefront
@@ -32,6 +31,8 @@
 // kernels of zha_attn.hip, summed in another order.
 #include "zha_device.h"
 #include "zha_internal.h"
+
+#include <algorithm>
 
 namespace zha {
 
@@ -81,49 +82,85 @@ __device__ __forceinline__ void ua_slot(const AttnArgs &a, int64_t w, int64_t &g
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void k_ua_fill(AttnArgs a) {
-    const int64_t mw = (a.n1 + 1) / 2;           // mask words in use per group
-    const int64_t fw = mw + a.cwords;
-    const int64_t n = a.ugroups * fw;
-    uint32_t *mask = reinterpret_cast<uint32_t *>(a.umask);
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * 256) {
-        const int64_t g = i / fw, k = i - g * fw;
-        if (k < mw)
-            mask[g * (a.n1cap / 2) + k] = 0u;
-        else
-            a.uchunk[g * a.cwords + (k - mw)] = 0u;
-    }
-}
+// One workgroup (T lanes: 1,024 for decode pairs, whose lists are long; 256
+// for prefill groups, which are many and short) per (group, slice of
+// kUaSlice level-1 blocks):
+// the group's walks' lists, taken as one run of entries, set each walk's
+// column bit on the blocks it selected in the slice, in LDS (eight list loads
+// in flight per lane); then the slice's masks (zeros included, so nothing
+// needs clearing first) and chunk bits go out with plain coalesced stores.
+constexpr int kUbLoads = 8;
 
-// A workgroup marks one decode walk (256 lanes) or four prefill walks (64
-// lanes each).  A walk's list is in ascending order, so the lanes of a
-// wavefront see consecutive entries: only the first lane of each run of
-// equal chunks sets the chunk bit (a handful of words per group take them).
-__global__ __launch_bounds__(256) void k_ua_mark(AttnArgs a) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int per = a.qph == 1 ? 256 : 64;        // lanes per walk
-    const int64_t w = static_cast<int64_t>(blockIdx.x) * (256 / per) + tid / per;
-    const int sub = tid % per;
-    if (w >= a.walks) return;
-    int64_t g;
-    int col;
-    ua_slot(a, w, g, col);
-    int64_t nb = a.sel_count[w];
-    if (nb > a.sel_cap) nb = a.sel_cap;
-    const int32_t *sel = a.sel_blocks + w * a.sel_cap;
-    uint32_t *mask = reinterpret_cast<uint32_t *>(a.umask) + g * (a.n1cap / 2);
-    uint32_t *chunks = a.uchunk + g * a.cwords;
-    for (int64_t i0 = 0; i0 < nb; i0 += per) {
-        const int64_t i = i0 + sub;
-        const int32_t blk = i < nb ? sel[i] : -1;
-        const bool ok = blk >= 0 && blk < a.n1;
-        const int ch = ok ? blk / kUaBlocks : -1;
-        const int prev = __shfl_up(ch, 1, 64);
-        if (ok) {
-            atomicOr(mask + (blk >> 1), (1u << col) << (16 * (blk & 1)));
-            if (lane == 0 || prev != ch) atomicOr(chunks + (ch >> 5), 1u << (ch & 31));
+template <int T>
+__global__ __launch_bounds__(T) void k_ua_build(AttnArgs a) {
+    static_assert(kUaBlocks == 128 && kUaSlice == 128 * kUaBlocks, "chunk-bit layout");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nsl = static_cast<int>((a.n1 + kUaSlice - 1) / kUaSlice);
+    const int64_t g = blockIdx.x / nsl;
+    const int sl = static_cast<int>(blockIdx.x - g * nsl);
+    const int64_t b0 = static_cast<int64_t>(sl) * kUaSlice;
+    const int64_t b1 = min(a.n1, b0 + kUaSlice);
+    const int nw = static_cast<int>((b1 - b0 + 1) / 2);      // mask words of the slice
+    __shared__ uint32_t sm[kUaSlice / 2];
+    __shared__ int64_t s_off[17], s_row[16];      // entry prefix per column; list row start
+    __shared__ int32_t s_cbit[kUaSlice / kUaBlocks];
+    for (int k = tid; k < kUaSlice / 2; k += T) sm[k] = 0u;
+    if (tid == 0) {
+        const int ncols = a.qph == 1 ? a.group : 16;
+        int64_t off = 0;
+        int c = 0;
+        for (; c < ncols; ++c) {
+            const int64_t w = ua_walk(a, g, c);
+            if (w < 0) break;                      // past the group's walks
+            int64_t nb = a.sel_count[w];
+            nb = nb < 0 ? 0 : (nb > a.sel_cap ? a.sel_cap : nb);
+            s_off[c] = off;
+            s_row[c] = w * a.sel_cap;
+            off += nb;
         }
+        for (; c <= 16; ++c) s_off[c] = off;       // empty columns past the walks
+    }
+    __syncthreads();
+    const int64_t total = s_off[16];
+    int c = 0;                                     // column of this lane's next entry
+    for (int64_t base = 0; base < total; base += T * kUbLoads) {
+        int32_t blk[kUbLoads];
+        int col[kUbLoads];
+#pragma unroll
+        for (int u = 0; u < kUbLoads; ++u) {
+            const int64_t i = base + u * T + tid;
+            blk[u] = -1;
+            col[u] = 0;
+            if (i < total) {
+                while (i >= s_off[c + 1]) ++c;     // entries rise with u, so c only moves up
+                col[u] = c;
+                blk[u] = a.sel_blocks[s_row[c] + (i - s_off[c])];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUbLoads; ++u)
+            if (blk[u] >= b0 && blk[u] < b1)
+                atomicOr(&sm[(blk[u] - b0) >> 1], (1u << col[u]) << (16 * (blk[u] & 1)));
+    }
+    __syncthreads();
+    uint32_t *mask = reinterpret_cast<uint32_t *>(a.umask) + g * (a.n1cap / 2) + (b0 >> 1);
+    for (int k = tid; k < nw; k += T) mask[k] = sm[k];
+    // chunk bits: a chunk of kUaBlocks blocks is 64 mask words, one per lane;
+    // each wavefront tests CW chunks, then four lanes pack 32 chunks a word
+    constexpr int CW = (kUaSlice / kUaBlocks) / (T / 64);
+    for (int j = 0; j < CW; ++j) {
+        const int ch = wave * CW + j;
+        const int k = ch * 64 + lane;
+        const uint32_t v = k < nw ? sm[k] : 0u;
+        const bool any = __ballot(v != 0u) != 0ull;
+        if (lane == 0) s_cbit[ch] = any ? 1 : 0;
+    }
+    __syncthreads();
+    if (tid < 4) {
+        uint32_t bits = 0u;
+        for (int j = 0; j < 32; ++j) bits |= static_cast<uint32_t>(s_cbit[tid * 32 + j]) << j;
+        const int64_t word = b0 / (32 * kUaBlocks) + tid;
+        if (word < a.cwords) a.uchunk[g * a.cwords + word] = bits;
     }
 }
 
@@ -441,14 +478,16 @@ __global__ __launch_bounds__(256) void k_ua_combine_pf(AttnArgs a) {
 
 template <int D>
 static hipError_t launch_ua_t(const AttnArgs &a, hipStream_t st) {
-    const int64_t fill = a.ugroups * ((a.n1 + 1) / 2 + a.cwords);
-    const int64_t fg = fill / 256 + 1;
-    hipLaunchKernelGGL(k_ua_fill, dim3(static_cast<unsigned>(fg < 4096 ? fg : 4096)), dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    const int64_t nsl = std::max<int64_t>(1, (a.n1 + kUaSlice - 1) / kUaSlice);
     const int64_t wg4 = (a.walks + 3) / 4;
-    hipLaunchKernelGGL(k_ua_mark, dim3(static_cast<unsigned>(a.qph == 1 ? a.walks : wg4)), dim3(256), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipError_t e;
+    if (a.n1 > 0) {
+        if (a.qph == 1)
+            hipLaunchKernelGGL(k_ua_build<1024>, dim3(static_cast<unsigned>(a.ugroups * nsl)), dim3(1024), 0, st, a);
+        else
+            hipLaunchKernelGGL(k_ua_build<256>, dim3(static_cast<unsigned>(a.ugroups * nsl)), dim3(256), 0, st, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((k_ua_attn<D>), dim3(static_cast<unsigned>(a.ugroups * a.items_pp)), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.qph == 1) {

@@ -21,6 +21,7 @@ constexpr int kExpSlices = 8;        // union engine: workgroups (runs) per pair
 constexpr int kSmallList = 64;       // union engine: list bound of the steps fused into one launch
 constexpr int kUaBlocks = 128;       // union attention: level-1 blocks per work item
 constexpr int kUaMaxItems = 4096;    // union attention: work items per pair (at most)
+constexpr int kUaSlice = 16384;      // union attention: level-1 blocks per mask-building workgroup
 
 // Per-walk state of the level-synchronous search engine (workspace).
 struct WalkState {
