@@ -366,20 +366,45 @@ __global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
     }
 }
 
+// One workgroup per walk, lane e = output element e: the items' maxima are
+// read spread over the lanes, then the items are merged in order, U at a
+// time with their loads issued together.
 template <int D, typename KT>
 __global__ __launch_bounds__(D) void k_attn_combine(AttnArgs a) {
+    constexpr int U = 4;
     const int w = blockIdx.x, e = threadIdx.x;
-    const int32_t i0 = a.item_off[w], i1 = a.item_off[w + 1];
+    const int32_t i0 = a.item_off[w], n = a.item_off[w + 1] - i0;
+    const float *part = a.part + static_cast<int64_t>(i0) * (D + 2);
+    __shared__ float s_max[D / 64];
     float mm = -INFINITY;
-    for (int32_t i = i0; i < i1; ++i) mm = fmaxf(mm, a.part[static_cast<int64_t>(i) * (D + 2)]);
+    for (int j = e; j < n; j += D) mm = fmaxf(mm, part[static_cast<int64_t>(j) * (D + 2)]);
+    mm = wave_max(mm, 1, 64);
+    if ((e & 63) == 0) s_max[e >> 6] = mm;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) mm = fmaxf(mm, s_max[i]);
     float ll = 0.f, av = 0.f;
     if (mm > -INFINITY) {
-        for (int32_t i = i0; i < i1; ++i) {
-            const float *p = a.part + static_cast<int64_t>(i) * (D + 2);
-            if (!(p[0] > -INFINITY)) continue;
-            const float cf = expf(p[0] - mm);
-            ll = fmaf(p[1], cf, ll);
-            av = fmaf(p[2 + e], cf, av);
+        for (int j0 = 0; j0 < n; j0 += U) {
+            float pm[U], pl[U], pv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                pm[u] = -INFINITY;
+                pl[u] = pv[u] = 0.f;
+                if (j0 + u < n) {
+                    const float *p = part + static_cast<int64_t>(j0 + u) * (D + 2);
+                    pm[u] = p[0];
+                    pl[u] = p[1];
+                    pv[u] = p[2 + e];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (!(pm[u] > -INFINITY)) continue;
+                const float cf = expf(pm[u] - mm);
+                ll = fmaf(pl[u], cf, ll);
+                av = fmaf(pv[u], cf, av);
+            }
         }
     }
     const float o = (ll > 0.f) ? av / ll : 0.f;
