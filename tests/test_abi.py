@@ -65,6 +65,14 @@ def test_attention_workspace_and_engine_choice(Z):
     t.tree_bytes = Z.zha_tree_bytes(g32)
     dec32 = Z.lib.zha_attn_workspace_bytes(ctypes.byref(t), ctypes.byref(sel), 1)
     assert dec - dec32 >= union
+    # prefill (4 query rows per head): groups of 16 of a pair's 16 x 4 walks,
+    # one workgroup each, plus per walk the block's own partial, the sort key,
+    # the sorted order and its inverse
+    walks, ug = pairs * 16 * 4, pairs * (16 * 4 // 16)
+    union_pf = (ug * n1cap * 2 + ug * 4 + ug * 4 + ug * 16 * 130 * 4
+                + walks * 130 * 4 + walks * 8 + walks * 4 + walks * 4)
+    pre32 = Z.lib.zha_attn_workspace_bytes(ctypes.byref(t), ctypes.byref(sel), 4)
+    assert pre - pre32 >= union_pf
     bad = Z.make_select("topp", 0.9, max_blocks=1024)
     bad.attn_engine = 7
     assert Z.lib.zha_attn_workspace_bytes(ctypes.byref(t), ctypes.byref(bad), 1) == 0
@@ -73,7 +81,7 @@ def test_attention_workspace_and_engine_choice(Z):
     t.geom = g
     t.tree_bytes = Z.zha_tree_bytes(g)
     assert Z.zha_attn_engine(t, sel, 1) == "union"
-    assert Z.zha_attn_engine(t, sel, 4) == "union"          # bf16 prefill blocks: 16 queries per group
+    assert Z.zha_attn_engine(t, sel, 4) == "union"          # bf16 prefill blocks: groups of 16 walks
     assert Z.zha_attn_engine(t, Z.make_select("topp", 0.9, max_blocks=1024, attn="per-walk"), 1) == "per-walk"
     g8 = _geom(Z, group=8, max_tokens=8192)
     t.geom = g8

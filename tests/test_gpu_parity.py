@@ -544,13 +544,14 @@ def test_prefill_block(Z, sname, engine):
 
 
 @pytest.mark.parametrize("sname", ["topp90", "topk4", "open-all"])
-@pytest.mark.parametrize("T", [128, 100])
+@pytest.mark.parametrize("T", [128, 99])
 def test_prefill_attention_paths(Z, sname, T):
-    """Prefill blocks: the union attention path (groups of 16 consecutive
-    queries of a head; with T = 100 the last group of each head is ragged)
-    and the per-walk path, each against oracle attention over the same
-    selection plus the block's keys up to the query on sampled queries, and
-    against each other on every query."""
+    """Prefill blocks: the union attention path (groups of 16 walks of a
+    pair in the order of their selection sketches; with T = 99 the pair's
+    4 x 99 walks leave a ragged last group) and the per-walk path, each
+    against oracle attention over the same selection plus the block's keys
+    up to the query on sampled queries, and against each other on every
+    query."""
     w, T0, _, K, V, Q, R, Kt, Vt, Qt, idx, trees = _prefill_setup(Z)
     Qb = Qt[:, :, :T].contiguous()
     select = dict(mode="topp", p=1.0) if sname == "open-all" else SELECTS[sname]
@@ -578,6 +579,52 @@ def test_prefill_attention_paths(Z, sname, T):
             for o in (ou[0, h, t], op[0, h, t]):
                 ok, e = P.out_ok(o, ref, w.dtype)
                 assert ok, (h, t, e)
+
+
+def test_prefill_union_sort_segments(Z):
+    """A prefill block whose pair holds more walks than one sort segment
+    (4 heads x 4,100 queries = 16,400 > 16,384): the union path (sorted
+    groups, two segments) against the per-walk path on every query and
+    against the oracle on sampled queries of both segments, the ragged
+    last group included."""
+    T0, T = 1024 + 40, 4100
+    w = replace(S.WORKLOADS[3].scaled(n=T0 + T, batch=1), kv_heads=1)
+    K, V, _, R = P.make_inputs(w)
+    q = S.pair_queries(w, 0, 0, count=w.group * T)
+    Q = q.reshape(1, w.group, T, w.d).astype(np.float32)
+    dev = torch.device("cuda")
+    Kt = torch.from_numpy(K).to(dev).to(torch.bfloat16).contiguous()
+    Vt = torch.from_numpy(V).to(dev).to(torch.bfloat16).contiguous()
+    Qt = torch.from_numpy(Q).to(dev).to(torch.bfloat16).contiguous()
+    geom = Z.make_geometry(w.batch, w.kv_heads, w.group, w.d, w.chunk, w.refs, w.levels, w.dtype,
+                           w.n, w.sharpness)
+    idx = Z.Index(geom, torch.from_numpy(R))
+    idx.build(Kt, T0)
+    select = SELECTS["topp90"]
+    sel_u = P.select_struct(Z, select, T0 // w.chunk, attn="union")
+    sel_p = P.select_struct(Z, select, T0 // w.chunk, attn="per-walk")
+    assert idx.attn_engine(sel_u, T) == "union"
+    bufs = idx.search(Qt, sel_u, qph=T)
+    out_u = idx.sparse_attn(Qt, Kt, Vt, sel_u, bufs["sel_blocks"], bufs["sel_count"], qph=T)
+    out_p = idx.sparse_attn(Qt, Kt, Vt, sel_p, bufs["sel_blocks"], bufs["sel_count"], qph=T)
+    torch.cuda.synchronize()
+    blocks = bufs["sel_blocks"].cpu().numpy()
+    count = bufs["sel_count"].cpu().numpy()
+    ou, op = out_u.float().cpu().numpy(), out_p.float().cpu().numpy()
+    assert np.all(np.isfinite(ou))
+    assert np.all(np.abs(ou - op) <= 1e-2 * np.maximum(1.0, np.abs(op)))
+    rng = np.random.default_rng(3)
+    # walks 16,384 .. 16,399 (head 3, queries 4,084 ..) form the second segment
+    picks = [(3, T - 1), (3, T - 16), (3, 4084), (0, 0), (1, 2049)]
+    picks += [(int(h), int(t)) for h, t in zip(rng.integers(0, w.group, 6), rng.integers(0, T, 6))]
+    for h, t in picks:
+        wi = h * T + t
+        toks = P.gpu_tokens(blocks[wi], count[wi], w.chunk, T0)
+        keys = np.concatenate([toks, np.arange(T0, T0 + t + 1)])
+        ref, _ = O.attend(keys, Q[0, h, t].astype(np.float64), K[0, 0].astype(np.float64),
+                          V[0, 0].astype(np.float64), w.sharpness)
+        ok, e = P.out_ok(ou[0, h, t], ref, w.dtype)
+        assert ok, (h, t, e)
 
 
 def test_prefill_forward_appends_after_search(Z):

@@ -8,8 +8,17 @@
 // used for every walk of the group that selected it, with a walk mask per
 // block.  A group is
 //   decode (q_per_head = 1): the G query heads of a (sequence, KV head) pair;
-//   prefill blocks: 16 consecutive queries of one query head.
+//   prefill blocks: 16 walks of one pair (any of its G x q_per_head query
+//                rows), consecutive in the order of a sketch of their
+//                selections, so that the walks of a group select alike.
 //
+//   k_ua_sig     prefill: each walk's sketch, two minhashes of the blocks it
+//                selected (for each of two fixed hash functions, the
+//                smallest hash over its blocks): walks whose block sets
+//                overlap much agree on them often;
+//   k_ua_order   prefill: per pair (up to kUaSortMax walks at a time), a
+//                bitonic sort in LDS of the (sketch, index) keys; the sorted
+//                order, and its inverse, define the groups;
 //   k_ua_build   the groups' block masks (16 bits per level-1 block, one per
 //                column: the walks that selected it) and chunk bits (one per
 //                kUaBlocks blocks), built in LDS one slice of blocks at a time;
@@ -52,19 +61,23 @@ __device__ __forceinline__ short4_t pk4(uint32_t lo, uint32_t hi) {
     return r;
 }
 
+// The walks of a pair are consecutive: its G query heads, each with its
+// q_per_head query rows.
+__device__ __forceinline__ int64_t ua_wpp(const AttnArgs &a) {
+    return static_cast<int64_t>(a.group) * a.qph;
+}
+
 // The KV pair of group g.
 __device__ __forceinline__ int64_t ua_pair(const AttnArgs &a, int64_t g) {
-    if (a.qph == 1) return g;
-    const int64_t hq = g / a.qtiles;             // sequence * heads + query head
-    return (hq / a.heads) * a.kv_heads + (hq % a.heads) / a.group;
+    return a.qph == 1 ? g : g / a.gpp;
 }
 
 // The walk of column col of group g, or -1 past the group's walks.
 __device__ __forceinline__ int64_t ua_walk(const AttnArgs &a, int64_t g, int col) {
     if (a.qph == 1) return col < a.group ? g * a.group + col : -1;
-    const int64_t hq = g / a.qtiles;
-    const int t = static_cast<int>(g - hq * a.qtiles) * 16 + col;
-    return t < a.qph ? hq * a.qph + t : -1;
+    const int64_t p = g / a.gpp, wpp = ua_wpp(a);
+    const int64_t s = (g - p * a.gpp) * 16 + col;   // sorted position within the pair
+    return s < wpp ? p * wpp + a.uperm[p * wpp + s] : -1;
 }
 
 // Group and column of walk w.
@@ -74,13 +87,102 @@ __device__ __forceinline__ void ua_slot(const AttnArgs &a, int64_t w, int64_t &g
         col = static_cast<int>(w - g * a.group);
         return;
     }
-    const int64_t hq = w / a.qph;
-    const int t = static_cast<int>(w - hq * a.qph);
-    g = hq * a.qtiles + t / 16;
-    col = t % 16;
+    const int64_t wpp = ua_wpp(a);
+    const int64_t s = a.uinv[w];
+    g = (w / wpp) * a.gpp + s / 16;
+    col = static_cast<int>(s % 16);
+}
+
+// MurmurHash3's 32-bit finalizer (an invertible mix), over x and a seed.
+__device__ __forceinline__ uint32_t ua_mix(uint32_t x, uint32_t seed) {
+    x ^= seed;
+    x ^= x >> 16;
+    x *= 0x85ebca6bu;
+    x ^= x >> 13;
+    x *= 0xc2b2ae35u;
+    x ^= x >> 16;
+    return x;
 }
 
 }  // namespace
+
+// Prefill: the sort key of every walk, 16 lanes a walk: the smallest value of
+// each of two hash functions over the blocks it selected (ids outside the
+// level are ignored; a walk without blocks gets the largest values), then its
+// index within its pair's sort segment.  Low bits of the second minhash are
+// dropped to make room for the index, which makes every key distinct.
+__global__ __launch_bounds__(256) void k_ua_sig(AttnArgs a) {
+    constexpr int U = 4;
+    const int tid = threadIdx.x, sub = tid & 15;
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * 16 + (tid >> 4);
+    uint32_t m1 = 0xffffffffu, m2 = 0xffffffffu;
+    if (w < a.walks) {
+        int64_t nb = a.sel_count[w];
+        nb = nb < 0 ? 0 : (nb > a.sel_cap ? a.sel_cap : nb);
+        const int32_t *sel = a.sel_blocks + w * a.sel_cap;
+        for (int64_t i0 = sub; i0 < nb; i0 += 16 * U) {
+            int32_t b[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) b[u] = i0 + 16 * u < nb ? sel[i0 + 16 * u] : -1;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (b[u] < 0 || b[u] >= a.n1) continue;
+                m1 = min(m1, ua_mix(static_cast<uint32_t>(b[u]), 0x9e3779b9u));
+                m2 = min(m2, ua_mix(static_cast<uint32_t>(b[u]), 0x7f4a7c15u));
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+        m1 = min(m1, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m1), off, 64)));
+        m2 = min(m2, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m2), off, 64)));
+    }
+    if (w < a.walks && sub == 0) {
+        const uint64_t loc = static_cast<uint64_t>((w % ua_wpp(a)) % kUaSortMax);
+        a.ukey[w] = (static_cast<uint64_t>(m1) << 32) | (static_cast<uint64_t>(m2 >> 15) << 14) | loc;
+    }
+}
+
+// Prefill: one workgroup per (pair, segment of kUaSortMax walks) sorts the
+// segment's keys ascending in LDS (a bitonic network over the next power of
+// two, padded with keys above every real one) and writes the pair-local walk
+// at each sorted position (uperm) and the sorted position of each walk
+// (uinv).  Keys are distinct, so the order is the same on every run.
+__global__ __launch_bounds__(1024) void k_ua_order(AttnArgs a) {
+    static_assert(kUaSortMax == 16384, "the key keeps 14 bits of segment index");
+    __shared__ unsigned long long s[kUaSortMax];
+    const int tid = threadIdx.x;
+    const int64_t wpp = ua_wpp(a);
+    const int nseg = static_cast<int>((wpp + kUaSortMax - 1) / kUaSortMax);
+    const int64_t p = blockIdx.x / nseg;
+    const int64_t l0 = static_cast<int64_t>(blockIdx.x - p * nseg) * kUaSortMax;
+    const int n = static_cast<int>(min<int64_t>(kUaSortMax, wpp - l0));
+    int N = 1;
+    while (N < n) N <<= 1;
+    const int64_t base = p * wpp + l0;             // first walk of the segment
+    for (int i = tid; i < N; i += 1024) s[i] = i < n ? a.ukey[base + i] : ~0ull;
+    __syncthreads();
+    for (int k = 2; k <= N; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < N; i += 1024) {
+                const int ij = i ^ j;
+                if (ij > i) {
+                    const unsigned long long x = s[i], y = s[ij];
+                    if (((i & k) == 0) ? (x > y) : (x < y)) {
+                        s[i] = y;
+                        s[ij] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int i = tid; i < n; i += 1024) {
+        const int loc = static_cast<int>(s[i] & (kUaSortMax - 1));
+        a.uperm[base + i] = static_cast<int32_t>(l0 + loc);
+        a.uinv[base + loc] = static_cast<int32_t>(l0 + i);
+    }
+}
 
 // One workgroup (T lanes: 1,024 for decode pairs, whose lists are long; 256
 // for prefill groups, which are many and short) per (group, slice of
@@ -481,6 +583,14 @@ static hipError_t launch_ua_t(const AttnArgs &a, hipStream_t st) {
     const int64_t nsl = std::max<int64_t>(1, (a.n1 + kUaSlice - 1) / kUaSlice);
     const int64_t wg4 = (a.walks + 3) / 4;
     hipError_t e;
+    if (a.qph > 1) {
+        hipLaunchKernelGGL(k_ua_sig, dim3(static_cast<unsigned>((a.walks + 15) / 16)), dim3(256), 0, st, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int64_t wpp = static_cast<int64_t>(a.group) * a.qph;
+        const int64_t nseg = (wpp + kUaSortMax - 1) / kUaSortMax;
+        hipLaunchKernelGGL(k_ua_order, dim3(static_cast<unsigned>(a.pairs * nseg)), dim3(1024), 0, st, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (a.n1 > 0) {
         if (a.qph == 1)
             hipLaunchKernelGGL(k_ua_build<1024>, dim3(static_cast<unsigned>(a.ugroups * nsl)), dim3(1024), 0, st, a);

@@ -158,17 +158,18 @@ int64_t tree_keys_bound(const zha_tree *t, const zha_select *sel, int32_t qph) {
 }
 
 // The union attention path: bf16 caches; decode with at most 16 query heads
-// per KV head (one matrix-core column per head), or a prefill block (16
-// consecutive queries of a head per group).
+// per KV head (one matrix-core column per head), or a prefill block (groups
+// of 16 walks of a (sequence, KV head) pair, taken in the order of their
+// selection sketches).
 struct UnionGeom {
-    int64_t ugroups, n1cap, nchunks, cwords, wpg_max, qtiles;
+    int64_t ugroups, n1cap, nchunks, cwords, wpg_max, gpp;
 };
 UnionGeom union_geom(const zha_tree *t, int32_t qph) {
     const zha_geometry &g = t->geom;
     UnionGeom u;
     const int64_t pairs = int64_t(g.batch) * g.num_kv_heads;
-    u.qtiles = qph > 1 ? (qph + 15) / 16 : 1;
-    u.ugroups = qph > 1 ? int64_t(g.batch) * g.num_kv_heads * g.group_size * u.qtiles : pairs;
+    u.gpp = qph > 1 ? (int64_t(g.group_size) * qph + 15) / 16 : 1;
+    u.ugroups = pairs * u.gpp;
     u.n1cap = (g.max_tokens / g.chunk + 1) / 2 * 2;
     u.nchunks = (u.n1cap + kUaBlocks - 1) / kUaBlocks;
     u.cwords = (u.nchunks + 31) / 32;
@@ -191,7 +192,7 @@ int resolve_attn(const zha_tree *t, const zha_select *sel, int32_t qph) {
 }
 
 struct AttnWs {
-    uint64_t part, item_off, item_walk, umask, uchunk, ic, upart, bpart, total;
+    uint64_t part, item_off, item_walk, umask, uchunk, ic, upart, bpart, ukey, uperm, uinv, total;
     UnionGeom u;
 };
 // Per-walk items; with `t` (a call that may take the union path) also the
@@ -211,7 +212,11 @@ AttnWs attn_ws_layout(int head_dim, int64_t keys_bound, int64_t walks, const zha
     l.ic = l.uchunk + align_up(ng * uint64_t(l.u.cwords) * sizeof(uint32_t));
     l.upart = l.ic + align_up(ng * uint64_t(l.u.wpg_max) * sizeof(int32_t));
     l.bpart = l.upart + align_up(ng * uint64_t(l.u.wpg_max) * 16 * (head_dim + 2) * sizeof(float));
-    l.total = l.bpart + align_up((uni && qph > 1 ? uint64_t(walks) : 0) * (head_dim + 2) * sizeof(float));
+    const uint64_t pw = uni && qph > 1 ? uint64_t(walks) : 0;   // prefill-only arrays
+    l.ukey = l.bpart + align_up(pw * (head_dim + 2) * sizeof(float));
+    l.uperm = l.ukey + align_up(pw * sizeof(unsigned long long));
+    l.uinv = l.uperm + align_up(pw * sizeof(int32_t));
+    l.total = l.uinv + align_up(pw * sizeof(int32_t));
     return l;
 }
 
@@ -456,10 +461,13 @@ zha_status do_attn(const zha_tree *t, const void *q, int32_t qph, const void *k_
         a.ic = reinterpret_cast<int32_t *>(wb + lay.ic);
         a.part = reinterpret_cast<float *>(wb + lay.upart);
         a.bpart = qph > 1 ? reinterpret_cast<float *>(wb + lay.bpart) : nullptr;
+        a.ukey = qph > 1 ? reinterpret_cast<unsigned long long *>(wb + lay.ukey) : nullptr;
+        a.uperm = qph > 1 ? reinterpret_cast<int32_t *>(wb + lay.uperm) : nullptr;
+        a.uinv = qph > 1 ? reinterpret_cast<int32_t *>(wb + lay.uinv) : nullptr;
         a.n1cap = lay.u.n1cap;
         a.ugroups = lay.u.ugroups;
         a.cwords = static_cast<int32_t>(lay.u.cwords);
-        a.qtiles = static_cast<int32_t>(lay.u.qtiles);
+        a.gpp = static_cast<int32_t>(lay.u.gpp);
         // decode: about 4096 workgroups in all, each over a contiguous range
         // of chunks; prefill: one workgroup per group, over all chunks
         const int64_t nchunks = (a.n1 + kUaBlocks - 1) / kUaBlocks;

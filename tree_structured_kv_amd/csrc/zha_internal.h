@@ -22,6 +22,7 @@ constexpr int kSmallList = 64;       // union engine: list bound of the steps fu
 constexpr int kUaBlocks = 128;       // union attention: level-1 blocks per work item
 constexpr int kUaMaxItems = 4096;    // union attention: work items per pair (at most)
 constexpr int kUaSlice = 16384;      // union attention: level-1 blocks per mask-building workgroup
+constexpr int kUaSortMax = 16384;    // union attention, prefill: walks sorted together (one workgroup)
 
 // Per-walk state of the level-synchronous search engine (workspace).
 struct WalkState {
@@ -146,16 +147,20 @@ struct AttnArgs {
                                    // (one extra item per walk, the last one)
     float sharpness;
     // union path: per group of walks sharing a KV cache (decode: a pair's
-    // heads; prefill: 16 consecutive queries of a head), the union of their
-    // selected blocks, one column per walk
+    // heads; prefill: 16 walks of a pair, consecutive in the order of their
+    // selection sketches), the union of their selected blocks, one column
+    // per walk
     uint16_t *umask;               // ws [ugroups][n1cap]  columns that selected each level-1 block
     uint32_t *uchunk;              // ws [ugroups][cwords]  chunks of kUaBlocks blocks holding one
     int32_t *ic;                   // ws [ugroups][items_pp]  1: the workgroup wrote partials
     float *bpart;                  // ws [walks][D + 2]  prefill: the block's own keys (k_attn_block)
+    unsigned long long *ukey;      // ws [walks]  prefill: sketch key of each walk (sort key)
+    int32_t *uperm;                // ws [walks]  prefill: pair-local walk at each sorted position
+    int32_t *uinv;                 // ws [walks]  prefill: sorted position of each walk within its pair
     int64_t n1cap;                 // level-1 blocks per group (stride of umask, even)
     int64_t ugroups;
     int32_t cwords;
-    int32_t qtiles;                // prefill: groups per (sequence, query head)
+    int32_t gpp;                   // prefill: groups per pair (16 sorted walks each)
     int32_t items_pp;              // workgroups (partials) per group
     int32_t ua_cpw;                // kUaBlocks-block chunks per workgroup
     int32_t pairs;
