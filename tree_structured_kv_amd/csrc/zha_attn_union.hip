@@ -273,8 +273,12 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int c = a.chunk, log2c = a.log2c, wpg = a.items_pp;
-    const int64_t g = blockIdx.x / wpg;
-    const int r = static_cast<int>(blockIdx.x - g * wpg);
+    // prefill: neighbouring groups (sorted by sketch) select alike, so runs
+    // of them go to one XCD, whose L2 then serves their shared blocks
+    const int64_t item = a.qph == 1 ? static_cast<int64_t>(blockIdx.x) : xcd_item(blockIdx.x, a.ugroups * wpg);
+    if (item < 0) return;
+    const int64_t g = item / wpg;
+    const int r = static_cast<int>(item - g * wpg);
     const int64_t p = ua_pair(a, g);
     const int nchunks = static_cast<int>((a.n1 + kUaBlocks - 1) / kUaBlocks);
     const int j0 = r * a.ua_cpw, j1 = min(nchunks, j0 + a.ua_cpw);
@@ -438,7 +442,7 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
         __syncthreads();                           // the tiles read s_blk / s_msk
     }
     if (!any) {                                    // uniform: no keys in this workgroup's range
-        if (tid == 0) a.ic[blockIdx.x] = 0;
+        if (tid == 0) a.ic[item] = 0;
         return;
     }
     // merge the wavefronts' states per column
@@ -466,14 +470,14 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
                 oo = fmaf(s_o[v][d * 16 + h], f, oo);
             }
         }
-        float *part = a.part + (static_cast<int64_t>(blockIdx.x) * 16 + h) * (D + 2);
+        float *part = a.part + (item * 16 + h) * (D + 2);
         part[2 + d] = oo;
         if (d == 0) {
             part[0] = mm;
             part[1] = ll;
         }
     }
-    if (tid == 0) a.ic[blockIdx.x] = 1;
+    if (tid == 0) a.ic[item] = 1;
 }
 
 // Decode: one workgroup per walk: its group's workgroup flags staged in LDS,
@@ -598,7 +602,9 @@ static hipError_t launch_ua_t(const AttnArgs &a, hipStream_t st) {
             hipLaunchKernelGGL(k_ua_build<256>, dim3(static_cast<unsigned>(a.ugroups * nsl)), dim3(256), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_ua_attn<D>), dim3(static_cast<unsigned>(a.ugroups * a.items_pp)), dim3(256), 0, st, a);
+    const int64_t items = a.ugroups * a.items_pp;
+    hipLaunchKernelGGL((k_ua_attn<D>), dim3(static_cast<unsigned>(a.qph == 1 ? items : xcd_grid(items))), dim3(256), 0,
+                       st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.qph == 1) {
         hipLaunchKernelGGL((k_ua_combine<D>), dim3(a.walks), dim3(256), 0, st, a);

@@ -23,6 +23,17 @@ constexpr int kUaBlocks = 128;       // union attention: level-1 blocks per work
 constexpr int kUaMaxItems = 4096;    // union attention: work items per pair (at most)
 constexpr int kUaSlice = 16384;      // union attention: level-1 blocks per mask-building workgroup
 constexpr int kUaSortMax = 16384;    // union attention, prefill: walks sorted together (one workgroup)
+constexpr int kXcds = 8;             // MI355X: accelerator dies (XCDs), each with its own L2
+
+// Workgroups go to the XCDs in turn (workgroup i to XCD i mod kXcds).  With
+// a grid of xcd_grid(n) workgroups, workgroup i takes item xcd_item(i, n)
+// (nothing when that is -1): runs of consecutive items share one XCD and its
+// L2.
+__host__ __device__ constexpr int64_t xcd_grid(int64_t n) { return (n + kXcds - 1) / kXcds * kXcds; }
+__device__ __forceinline__ int64_t xcd_item(int64_t i, int64_t n) {
+    const int64_t v = (i % kXcds) * ((n + kXcds - 1) / kXcds) + i / kXcds;
+    return v < n ? v : -1;
+}
 
 // Per-walk state of the level-synchronous search engine (workspace).
 struct WalkState {
