@@ -20,12 +20,14 @@
 //               record loaded once per unit and reused by every row tile;
 //   k_bk_cut    one wavefront per walk: the exact value-window cut over its
 //               candidates (children of the parents it opened, in order),
-//               level-1 selections in span order, the higher nodes it opens
-//               (its next parents) and a count per opened parent;
+//               level-1 selections in span order and the higher nodes it
+//               opens (its next parents);
+//   k_bk_bins   per run of 64 walks of a pair: the walks opening each
+//               parent, counted in LDS, then added to the parent's count;
 //   k_bk_group  one workgroup: offsets of every parent's walk list (a scan
 //               over the counts) and the unit list;
-//   k_bk_fill   one wavefront per walk: its (walk, slot) entries into the
-//               lists of the parents it opened.
+//   k_bk_bins   (fill) per run again: each run reserves its range of every
+//               parent's list, then writes its (walk, slot) entries.
 // A walk's candidate x is child x % c of its parent x / c (at t = 0: root
 // x), so candidate ids are never stored, only each walk's parent list.
 #include "zha_device.h"
@@ -41,6 +43,8 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 constexpr int kBkThreads = 256;        // scorer workgroup
 constexpr int kBkRows = 64;            // walks per unit (four row tiles of 16)
 constexpr int kGroupThreads = 1024;    // k_bk_group workgroup
+constexpr int kBkRun = 64;             // walks per counting / list-filling workgroup
+constexpr int kBkHist = 8192;          // parents per pair counted in LDS (32 KB)
 
 __device__ __forceinline__ int64_t pair_of(const SearchArgs &a, int w) {
     return walk_pair(w, a.qph, a.heads, a.group, a.kv_heads);
@@ -471,12 +475,6 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
         st.n = 0;
         if (lane == 0) finish_walk<R>(a, w, t + 1, st.scored, st.opened, st.sel_n, st.unforced, st.flags);
     }
-    // count this walk under every parent whose children the next cut scores
-    if (st.n > 0 && !step_forced(a, t + 1, st.n)) {
-        const int np = static_cast<int>((st.n + c - 1) / c);
-        for (int j = lane; j < np; j += 64)
-            atomicAdd(&a.b_cnt[pair * a.nbins + parent_bin(a, par_nxt[j])], 1);
-    }
     if (lane == 0) a.state[w] = st;
 }
 
@@ -534,23 +532,78 @@ __global__ __launch_bounds__(kGroupThreads) void k_bk_group(SearchArgs a, int t)
     if (tid == 0) a.tile_count[t] = static_cast<int32_t>(carry >> 40);
 }
 
-// One wavefront per walk whose next cut needs scores: its (walk, slot)
-// entries into the lists of the parents it opened.
-__global__ __launch_bounds__(64) void k_bk_fill(SearchArgs a) {
-    const int lane = threadIdx.x;
-    const int w = blockIdx.x;
+// The parents walk w's next cut scores the children of (its current parent
+// list, after its cut), or 0 when that cut needs no scores.
+__device__ __forceinline__ int bk_parents(const SearchArgs &a, int w, const uint32_t *&par) {
     const int n = a.state[w].n;
     const int t1 = a.state[w].steps;                      // the step about to be cut
-    if (n <= 0 || step_forced(a, t1, n)) return;
-    const int c = a.chunk, cap = a.cand_cap;
-    const int buf = a.state[w].buf;
-    const uint32_t *par = a.cand + static_cast<int64_t>(w) * 2 * cap + static_cast<int64_t>(buf) * cap;
-    const int64_t pair = pair_of(a, w);
-    const int np = (n + c - 1) / c;
-    for (int j = lane; j < np; j += 64) {
-        const int64_t b = pair * a.nbins + parent_bin(a, par[j]);
-        const int pos = a.b_first[b] + atomicAdd(&a.b_fill[b], 1);
-        a.b_inv[pos] = make_int2(w, j);
+    if (n <= 0 || step_forced(a, t1, n)) return 0;
+    par = a.cand + static_cast<int64_t>(w) * 2 * a.cand_cap + static_cast<int64_t>(a.state[w].buf) * a.cand_cap;
+    return (n + a.chunk - 1) / a.chunk;
+}
+
+// One workgroup per run of kBkRun walks of one pair (four wavefronts, a walk
+// each at a time).  !FILL: every walk counts under each parent it opened
+// (b_cnt, before k_bk_group); FILL: its (walk, slot) entries go into those
+// parents' lists (b_inv, after k_bk_group).  Thousands of walks open the
+// same upper parents, so the run first counts in LDS and then touches each
+// parent's global counter once: one atomic per (run, parent) instead of one
+// per (walk, parent).  The order of a parent's entries is whatever the
+// atomics give; a score does not depend on its row in a tile, so results do
+// not.  With more than kBkHist parents per pair the entries take one global
+// atomic each.
+template <bool FILL>
+__global__ __launch_bounds__(kBkThreads) void k_bk_bins(SearchArgs a) {
+    __shared__ int32_t h[kBkHist];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t wpp = static_cast<int64_t>(a.group) * a.qph;
+    const int64_t runs = (wpp + kBkRun - 1) / kBkRun;
+    const int64_t p = blockIdx.x / runs;
+    const int64_t w0 = p * wpp + (blockIdx.x - p * runs) * kBkRun;
+    const int64_t w1 = min(w0 + kBkRun, (p + 1) * wpp);
+    const int64_t nb = a.nbins;
+    const bool lds = nb <= kBkHist;
+    int32_t *cnt = a.b_cnt + p * nb;
+    int32_t *fill = a.b_fill + p * nb;
+    const int32_t *first = a.b_first + p * nb;
+    if (lds) {
+        for (int k = tid; k < nb; k += kBkThreads) h[k] = 0;
+        __syncthreads();
+    }
+    for (int64_t w = w0 + wave; w < w1; w += kBkThreads / 64) {
+        const uint32_t *par = nullptr;
+        const int np = bk_parents(a, static_cast<int>(w), par);
+        for (int j = lane; j < np; j += 64) {
+            const int64_t b = parent_bin(a, par[j]);
+            if (lds) {
+                atomicAdd(&h[b], 1);
+            } else if (!FILL) {
+                atomicAdd(&cnt[b], 1);
+            } else {
+                const int pos = first[b] + atomicAdd(&fill[b], 1);
+                a.b_inv[pos] = make_int2(static_cast<int>(w), j);
+            }
+        }
+    }
+    if (!lds) return;                              // uniform
+    __syncthreads();
+    for (int k = tid; k < nb; k += kBkThreads) {
+        const int v = h[k];
+        if (v == 0) continue;
+        if (FILL)
+            h[k] = first[k] + atomicAdd(&fill[k], v);   // this run's first entry of parent k
+        else
+            atomicAdd(&cnt[k], v);
+    }
+    if (!FILL) return;
+    __syncthreads();
+    for (int64_t w = w0 + wave; w < w1; w += kBkThreads / 64) {
+        const uint32_t *par = nullptr;
+        const int np = bk_parents(a, static_cast<int>(w), par);
+        for (int j = lane; j < np; j += 64) {
+            const int pos = atomicAdd(&h[parent_bin(a, par[j])], 1);
+            a.b_inv[pos] = make_int2(static_cast<int>(w), j);
+        }
     }
 }
 
@@ -561,6 +614,8 @@ static hipError_t launch_block_t(const SearchArgs &a, int n0, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int score_grid = 2048;
+    const int64_t wpp = static_cast<int64_t>(a.group) * a.qph;
+    const unsigned runs_grid = static_cast<unsigned>(a.pairs * ((wpp + kBkRun - 1) / kBkRun));
     const bool skip0 = n0 <= 1 || (a.mode == ZHA_TOPK && a.k[0] >= n0) || (a.mode == ZHA_TOPP && a.p >= 1.0f);
     for (int t = 0; t < a.levels && t < ZHA_MAX_STEPS; ++t) {
         if (t > 0 || !skip0) {
@@ -570,9 +625,11 @@ static hipError_t launch_block_t(const SearchArgs &a, int n0, hipStream_t st) {
         hipLaunchKernelGGL((k_bk_cut<R>), dim3(a.walks), dim3(64), 0, st, a, t);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (t + 1 < a.levels && t + 1 < ZHA_MAX_STEPS) {
+            hipLaunchKernelGGL(k_bk_bins<false>, dim3(runs_grid), dim3(kBkThreads), 0, st, a);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
             hipLaunchKernelGGL(k_bk_group, dim3(1), dim3(kGroupThreads), 0, st, a, t + 1);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            hipLaunchKernelGGL(k_bk_fill, dim3(a.walks), dim3(64), 0, st, a);
+            hipLaunchKernelGGL(k_bk_bins<true>, dim3(runs_grid), dim3(kBkThreads), 0, st, a);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }
