@@ -45,6 +45,7 @@ constexpr int kBkRows = 64;            // walks per unit (four row tiles of 16)
 constexpr int kGroupThreads = 1024;    // k_bk_group workgroup
 constexpr int kBkRun = 64;             // walks per counting / list-filling workgroup
 constexpr int kBkHist = 8192;          // parents per pair counted in LDS (32 KB)
+constexpr int kBkCutRegs = 16;         // candidates per lane a cut keeps in registers
 
 __device__ __forceinline__ int64_t pair_of(const SearchArgs &a, int w) {
     return walk_pair(w, a.qph, a.heads, a.group, a.kv_heads);
@@ -241,9 +242,13 @@ __global__ __launch_bounds__(kBkThreads) void k_bk_score(SearchArgs a, int t, in
     }
 }
 
-// Step t cut, one wavefront (workgroup) per walk.
+// Step t cut, one wavefront (workgroup) per walk.  Its scores and candidate
+// ids are loaded into registers once, all loads in flight, when there are at
+// most 64 * kBkCutRegs candidates (the passes then read no memory); longer
+// lists are read kBkCutRegs a lane at a time in every pass.
 template <int R>
 __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
+    constexpr int KR = kBkCutRegs;
     const int lane = threadIdx.x;
     const int w = blockIdx.x;
     __shared__ WaveCut sh;
@@ -251,7 +256,6 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
     const int n = st.n;
     if (n <= 0) return;                                   // finished earlier
     const int cap = a.cand_cap, c = a.chunk, log2c = a.log2c;
-    const int64_t pair = pair_of(a, w);
     uint32_t *parents = a.cand + static_cast<int64_t>(w) * 2 * cap;
     const uint32_t *par_cur = parents + static_cast<int64_t>(st.buf) * cap;
     uint32_t *par_nxt = parents + static_cast<int64_t>(st.buf ^ 1) * cap;
@@ -262,23 +266,78 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
         if (t == 0) return a.b_roots[x];
         return child_id(par_cur[x >> log2c], x & (c - 1), c);
     };
+    const bool staged = n <= 64 * KR;
+    float vr[KR];
+    uint32_t ir[KR];
+    if (staged) {
+#pragma unroll
+        for (int i = 0; i < KR; ++i) {
+            const int x = lane + 64 * i;
+            vr[i] = x < n ? sc[x] : -INFINITY;
+        }
+#pragma unroll
+        for (int i = 0; i < KR; ++i) {
+            const int x = lane + 64 * i;
+            ir[i] = x < n ? cand_id(x) : 0u;
+        }
+    }
+    // f(score, x, id, x < n) for x = lane, lane + 64, ... (every lane takes
+    // part in every round of 64 candidates; rounds in increasing x); ids are
+    // read only when asked for
+    auto rounds = [&](bool want_id, auto &&f) {
+        if (staged) {
+            const int nr = (n + 63) >> 6;
+#pragma unroll
+            for (int i = 0; i < KR; ++i) {
+                if (i >= nr) break;
+                const int x = lane + 64 * i;
+                f(vr[i], x, ir[i], x < n);
+            }
+            return;
+        }
+        for (int x0 = 0; x0 < n; x0 += 64 * KR) {
+            float v[KR];
+            uint32_t id[KR];
+#pragma unroll
+            for (int i = 0; i < KR; ++i) {
+                const int x = x0 + lane + 64 * i;
+                v[i] = x < n ? sc[x] : -INFINITY;
+                id[i] = 0u;
+            }
+            if (want_id) {
+#pragma unroll
+                for (int i = 0; i < KR; ++i) {
+                    const int x = x0 + lane + 64 * i;
+                    id[i] = x < n ? cand_id(x) : 0u;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < KR; ++i) {
+                if (x0 + 64 * i >= n) break;
+                const int x = x0 + lane + 64 * i;
+                f(v[i], x, id[i], x < n);
+            }
+        }
+    };
 
     const bool forced = step_forced(a, t, n);
     unsigned long long tau = 0;
     if (!forced) {
         const bool by_mass = (a.mode == ZHA_TOPP) && (a.p > 0.f);
         float mx = -INFINITY;
-        for (int x = lane; x < n; x += 64) mx = fmaxf(mx, sc[x]);
+        rounds(false, [&](float v, int, uint32_t, bool in) {
+            if (in) mx = fmaxf(mx, v);
+        });
         mx = wave_max(mx, 1, 64);
         bool exact_done = false;
         if (mx > -INFINITY) {
             float mn = mx;
             unsigned long long z = 0;
-            for (int x = lane; x < n; x += 64) {
-                const float v = sc[x];
+            rounds(false, [&](float v, int, uint32_t, bool in) {
+                if (!in) return;
                 if (v > -INFINITY) mn = fminf(mn, v);
                 if (by_mass) z += static_cast<unsigned long long>(__float2uint_rn(expf(v - mx) * kMassScale));
-            }
+            });
             mn = -wave_max(-mn, 1, 64);
             z = wave_sum_u64(z);
             unsigned long long need;
@@ -304,17 +363,17 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
                 w_scale[depth] = scale;
                 for (int i = lane; i < 256; i += 64) { sh.hcnt[i] = 0; sh.hw[i] = 0; }
                 __syncthreads();
-                for (int x = lane; x < n; x += 64) {
-                    const float v = sc[x];
-                    bool in = true;
-                    for (int q = 0; q < depth; ++q) in = in && win_bin(v, w_top[q], w_scale[q]) == w_bin[q];
-                    if (!in) continue;
+                rounds(false, [&](float v, int, uint32_t, bool in) {
+                    if (!in) return;
+                    bool inw = true;
+                    for (int q = 0; q < depth; ++q) inw = inw && win_bin(v, w_top[q], w_scale[q]) == w_bin[q];
+                    if (!inw) return;
                     const int b = win_bin(v, top, scale);
                     unsigned long long wgt = 1;
                     if (by_mass) wgt = static_cast<unsigned long long>(__float2uint_rn(expf(v - mx) * kMassScale));
                     atomicAdd(&sh.hcnt[b], 1u);
                     if (wgt) atomicAdd(&sh.hw[b], wgt);
-                }
+                });
                 __syncthreads();
                 {
                     unsigned long long lw[4], lsum = 0;
@@ -360,19 +419,19 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
             if (found) {
                 if (lane == 0) sh.nf = 0;
                 __syncthreads();
-                for (int x = lane; x < n; x += 64) {
-                    const float v = sc[x];
-                    bool in = true;
-                    for (int q = 0; q < depth; ++q) in = in && win_bin(v, w_top[q], w_scale[q]) == w_bin[q];
-                    if (!in) continue;
+                rounds(true, [&](float v, int, uint32_t id, bool in) {
+                    if (!in) return;
+                    bool inw = true;
+                    for (int q = 0; q < depth; ++q) inw = inw && win_bin(v, w_top[q], w_scale[q]) == w_bin[q];
+                    if (!inw) return;
                     const uint32_t slot = atomicAdd(&sh.nf, 1u);
                     if (slot < static_cast<uint32_t>(kWinFinal)) {
-                        sh.fkey[slot] = rank_key(v, cand_id(x), log2c);
+                        sh.fkey[slot] = rank_key(v, id, log2c);
                         sh.fw[slot] = by_mass ? static_cast<unsigned long long>(
                                                     __float2uint_rn(expf(v - mx) * kMassScale))
                                               : 1ull;
                     }
-                }
+                });
                 __syncthreads();
                 const int nf = static_cast<int>(sh.nf < static_cast<uint32_t>(kWinFinal) ? sh.nf : kWinFinal);
                 if (lane < nf) {
@@ -439,13 +498,12 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
     // open, in candidate order
     const int pcap = a.pcap;
     uint32_t n1 = 0, nh = 0, nopen = 0;
-    for (int x0 = 0; x0 < n; x0 += 64) {
-        const int x = x0 + lane;
+    rounds(true, [&](float v, int, uint32_t idx, bool in) {
         bool open = false;
         uint32_t id = 0;
-        if (x < n) {
-            id = cand_id(x);
-            open = forced || rank_key(sc[x], id, log2c) >= tau;
+        if (in) {
+            id = idx;
+            open = forced || rank_key(v, id, log2c) >= tau;
         }
         const bool l1 = open && (id >> kLevelShift) == 1u;
         const bool hi = open && (id >> kLevelShift) > 1u;
@@ -461,7 +519,7 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
         n1 += __popcll(m1);
         nh += __popcll(mh);
         nopen += __popcll(__ballot(open));
-    }
+    });
     int64_t nn = static_cast<int64_t>(nh) * c;
     if (nn > cap) { st.flags |= ZHA_FLAG_CAND_OVERFLOW; nn = cap; }
     st.scored[t] = n;
