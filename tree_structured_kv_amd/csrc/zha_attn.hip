@@ -233,19 +233,24 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
 // (query t sees keys 0..t of the block, at positions n_tokens + 0..t), as a
 // partial state in the walk's last work item; k_attn_combine merges it with
 // the tree keys' items.  One workgroup per (pair, head, 64-query tile), one
-// wavefront per 16 queries; key tiles of 64 go through LDS (K row-major, V
-// transposed).  Logits come from bf16 16x16x16 matrix products computed as
+// wavefront per 16 queries; key tiles of 64 go through LDS (K and V
+// row-major).  Logits come from bf16 16x16x16 matrix products computed as
 // S^T = K Q^T (rows = keys, columns = queries), so the probabilities already
-// sit in the B-operand layout of the fp32 16x16x4 products O^T += V^T P^T:
-// at step e, lane group g of both operands takes key 4g + e of a 16-key
-// slice.  Online softmax in fp32; P and V enter the second product in fp32.
+// sit in the B-operand layout of the products O^T += V^T P^T: lane group g
+// holds keys 4g .. 4g+3 of a 16-key slice.  Those are bf16 16x16x16 products
+// too, with each probability split into two bf16 parts (hi + lo, within
+// 2^-17 relative), so the fp32 sums keep fp32 accuracy while V stays exact
+// (fp32 16x16x4 products would take 16 times the matrix-core time).  Row i of
+// output tile q is element d = DT*i + q, so a lane reads the DT consecutive
+// elements DT*col .. of each of its keys' V rows once for all tiles.
+// Online softmax in fp32.
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
     constexpr int KT = 64;                 // keys per tile
-    constexpr int KP = D + 8;              // sK row pitch (elements)
-    constexpr int VP = KT + 8;             // sVt row pitch (elements)
+    constexpr int KP = D + 8;              // sK / sV row pitch (elements)
     constexpr int DS = D / 16;             // bf16 product steps (16 elements each)
     constexpr int DT = D / 16;             // output row tiles of O^T
+    constexpr int VW = DT / 2;             // 32-bit words of a lane's V slice
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int T = a.qph;
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
     const int hq = static_cast<int>(blockIdx.x / qtiles);      // query head over all pairs
     const int pair = hq / a.group;
     __shared__ bf16_t sK[KT * KP];
-    __shared__ bf16_t sVt[D * VP];
+    __shared__ bf16_t sV[KT * KP];
     const bf16_t *kbase = static_cast<const bf16_t *>(a.k) + (static_cast<int64_t>(pair) * a.max_tokens + a.n_tokens) * D;
     const bf16_t *vbase = static_cast<const bf16_t *>(a.v) + (static_cast<int64_t>(pair) * a.max_tokens + a.n_tokens) * D;
     const int q0 = qt * 64 + wave * 16;                    // this wavefront's first query
@@ -285,12 +290,7 @@ __global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
                 vv = *reinterpret_cast<const uint4 *>(vbase + static_cast<int64_t>(k0 + key) * D + d8);
             }
             *reinterpret_cast<uint4 *>(sK + key * KP + d8) = kv;
-            const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sVt[(d8 + 2 * i) * VP + key] = static_cast<bf16_t>(vw[i] & 0xffffu);
-                sVt[(d8 + 2 * i + 1) * VP + key] = static_cast<bf16_t>(vw[i] >> 16);
-            }
+            *reinterpret_cast<uint4 *>(sV + key * KP + d8) = vv;
         }
         __syncthreads();
         if (k0 > q0 + 15) continue;                        // every key of the tile is in this wave's future
@@ -338,17 +338,29 @@ __global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
             for (int e = 0; e < 4; ++e) acc[i][e] *= corr;
         // O^T += V^T P^T
 #pragma unroll
-        for (int i = 0; i < DT; ++i) {
-            const bf16_t *vr = sVt + (16 * i + col) * VP + 4 * grp;
+        for (int sub = 0; sub < 4; ++sub) {
+            short4_t ph, pl;
 #pragma unroll
-            for (int sub = 0; sub < 4; ++sub) {
-                const uint2 vw = *reinterpret_cast<const uint2 *>(vr + 16 * sub);
-                const float v0 = __uint_as_float(vw.x << 16), v1 = __uint_as_float(vw.x & 0xffff0000u);
-                const float v2 = __uint_as_float(vw.y << 16), v3 = __uint_as_float(vw.y & 0xffff0000u);
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(v0, p[sub][0], acc[i], 0, 0, 0);
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(v1, p[sub][1], acc[i], 0, 0, 0);
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(v2, p[sub][2], acc[i], 0, 0, 0);
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(v3, p[sub][3], acc[i], 0, 0, 0);
+            for (int e = 0; e < 4; ++e) {
+                const bf16_t hb = f32_to_bf16(p[sub][e]);
+                ph[e] = static_cast<short>(hb);
+                pl[e] = static_cast<short>(f32_to_bf16(p[sub][e] - bf16_to_f32(hb)));
+            }
+            uint32_t vw[4][VW];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t *vr = reinterpret_cast<const uint32_t *>(sV + (16 * sub + 4 * grp + e) * KP + DT * col);
+#pragma unroll
+                for (int j = 0; j < VW; ++j) vw[e][j] = vr[j];
+            }
+#pragma unroll
+            for (int q = 0; q < DT; ++q) {
+                short4_t va;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    va[e] = static_cast<short>((q & 1) ? (vw[e][q >> 1] >> 16) : (vw[e][q >> 1] & 0xffffu));
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, acc[q], 0, 0, 0);
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc[q], 0, 0, 0);
             }
         }
     }
@@ -357,9 +369,9 @@ __global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
     float *part = a.bpart ? a.bpart + walk * (D + 2)
                           : a.part + static_cast<int64_t>(a.item_off[walk + 1] - 1) * (D + 2);
 #pragma unroll
-    for (int i = 0; i < DT; ++i)
+    for (int q = 0; q < DT; ++q)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) part[2 + 16 * i + 4 * grp + e] = acc[i][e];
+        for (int e = 0; e < 4; ++e) part[2 + DT * (4 * grp + e) + q] = acc[q][e];
     if (grp == 0) {
         part[0] = m;
         part[1] = l;
