@@ -39,6 +39,22 @@ namespace zha {
 namespace {
 
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+// An fp32 value as the exact sum of three bf16 values: hi and mid keep the
+// top 8 significant bits of x and of x - hi (truncation leaves an exact
+// remainder), and the remaining at most 8 bits fit lo exactly.
+__device__ __forceinline__ void split3(float x, short &hi, short &mid, short &lo) {
+    const uint32_t u = __float_as_uint(x);
+    const float h = __uint_as_float(u & 0xffff0000u);
+    const float r = x - h;
+    const uint32_t ur = __float_as_uint(r);
+    const float m = __uint_as_float(ur & 0xffff0000u);
+    const float l = r - m;
+    hi = static_cast<short>(u >> 16);
+    mid = static_cast<short>(ur >> 16);
+    lo = static_cast<short>(__float_as_uint(l) >> 16);
+}
 
 constexpr int kBkThreads = 256;        // scorer workgroup
 constexpr int kBkRows = 64;            // walks per unit (four row tiles of 16)
@@ -116,8 +132,13 @@ __global__ __launch_bounds__(kBkThreads) void k_bk_init(SearchArgs a, int n0) {
 // rows are the walks (and their slots) of one opened parent, whose c
 // children are the columns.  A wavefront owns column tiles wave, wave+4, ..
 // (NPG = 16/R nodes x R references each); it loads a column tile's records
-// once and runs every row tile of the unit against them.  Matrix step k of
-// lane group q = lane/16 multiplies element d = 16*(k/4) + 4*q + k%4 of the
+// once and runs every row tile of the unit against them.  bf16 queries: each
+// fp32 key element is split into three bf16 parts whose sum is exact
+// (split3; one part when the keys are stored in bf16) and every 16-element
+// slice of the dot product is three bf16 16x16x16 products (exact bf16
+// products summed in fp32, as with fp32 products, at a fifth of their
+// matrix-core time); fp32 queries take fp32 16x16x4 products.  Lane group q
+// = lane/16 holds elements 16*j + 4*q .. 16*j + 4*q + 3 of slice j of the
 // query and of the reference row.
 template <int D, int R, typename QT, typename ST>
 __global__ __launch_bounds__(kBkThreads) void k_bk_score(SearchArgs a, int t, int n0) {
@@ -144,6 +165,12 @@ __global__ __launch_bounds__(kBkThreads) void k_bk_score(SearchArgs a, int t, in
     const float s = a.sharpness;
     const int cap = a.cand_cap;
     const bool mark = a.visited != nullptr;
+    // the unit's rows: walk, candidate slot base and query, staged in LDS
+    // once per unit (the row loop then has no dependent global load)
+    constexpr int QP = D + 16 / static_cast<int>(sizeof(QT));   // s_q row pitch (elements)
+    constexpr int PPR = D * static_cast<int>(sizeof(QT)) / 16;  // 16-byte pieces per query row
+    __shared__ int32_t s_walk[kBkRows], s_slot[kBkRows];
+    __shared__ __align__(16) QT s_q[kBkRows * QP];
 
     for (int unit = u0; unit < u1; ++unit) {
         int pair, rows, first;
@@ -175,6 +202,23 @@ __global__ __launch_bounds__(kBkThreads) void k_bk_score(SearchArgs a, int t, in
                 slot0 = e.y * c;
             }
         };
+        __syncthreads();                                  // the previous unit is done with s_*
+        for (int idx = threadIdx.x; idx < kBkRows * PPR; idx += kBkThreads) {
+            const int r = idx / PPR, pc = idx - r * PPR;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (r < rows) {
+                int walk, slot0;
+                row_of(r, walk, slot0);
+                v = *reinterpret_cast<const uint4 *>(static_cast<const QT *>(a.q) + static_cast<int64_t>(walk) * D +
+                                                     pc * (16 / static_cast<int>(sizeof(QT))));
+                if (pc == 0) {
+                    s_walk[r] = walk;
+                    s_slot[r] = slot0;
+                }
+            }
+            *reinterpret_cast<uint4 *>(s_q + r * QP + pc * (16 / static_cast<int>(sizeof(QT)))) = v;
+        }
+        __syncthreads();
         for (int ct = wave; ct < n_ct; ct += kSW) {
             // this lane's column: node ct*NPG + col/R, reference col%R
             const int ci = min(ct * NPG + col / R, nchild - 1);
@@ -188,39 +232,50 @@ __global__ __launch_bounds__(kBkThreads) void k_bk_score(SearchArgs a, int t, in
                 GVec4<ST>::load(kp + 4 * k, &kb[k]);
             }
             const float bias = gload_f(s_bet[lvl] + node * R + (col % R));
+            // bf16 queries: the key slices as three bf16 operands (B: rows =
+            // elements 4*grp .. of slice j, column col)
+            constexpr int NS = D / 16;
+            constexpr int NP = (sizeof(ST) == 2) ? 1 : 3;     // bf16 keys are their own hi part
+            short4_t kbf[NP][NS];
+            if constexpr (sizeof(QT) == 2) {
+#pragma unroll
+                for (int j = 0; j < NS; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        short hi, mid, lo;
+                        split3(kb[4 * j + i], hi, mid, lo);
+                        kbf[0][j][i] = hi;
+                        if constexpr (NP == 3) {
+                            kbf[1][j][i] = mid;
+                            kbf[2][j][i] = lo;
+                        }
+                    }
+            }
             if (mark && (col % R) == 0 && grp == 0 && ct * NPG + col / R < nchild) {
                 const int64_t bitn = a.node_off[lvl] + (id & kIndexMask);
                 atomicOr(a.visited + static_cast<int64_t>(pair) * a.vis_words + (bitn >> 5), 1u << (bitn & 31));
             }
             for (int rt = 0; rt < n_rt; ++rt) {
-                // query operand: row = walk of row `col` of this tile (zero past the unit)
-                int qw, qslot;
-                const int qr = rt * 16 + col;
-                row_of(min(qr, rows - 1), qw, qslot);
-                (void)qslot;
-                const bool ok = qr < rows;
-                const QT *qp = static_cast<const QT *>(a.q) + static_cast<int64_t>(qw) * D + 4 * grp;
+                // query operand: row `col` of this tile (zero past the unit)
+                const QT *qr = s_q + (rt * 16 + col) * QP + 4 * grp;
                 float4_t acc = {0.f, 0.f, 0.f, 0.f};
                 if constexpr (sizeof(QT) == 2) {
-                    uint32_t qpk[KS / 2];
+                    short4_t qa[NS];
+#pragma unroll
+                    for (int j = 0; j < NS; ++j) qa[j] = *reinterpret_cast<const short4_t *>(qr + 16 * j);
+#pragma unroll
+                    for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+                        for (int j = 0; j < NS; ++j)
+                            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qa[j], kbf[pp][j], acc, 0, 0, 0);
+                } else {
 #pragma unroll
                     for (int j = 0; j < KS / 4; ++j) {
-                        const uint2 v = *reinterpret_cast<const uint2 *>(qp + 16 * j);
-                        qpk[2 * j] = ok ? v.x : 0u;
-                        qpk[2 * j + 1] = ok ? v.y : 0u;
+                        const float4_t qv = *reinterpret_cast<const float4_t *>(qr + 16 * j);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[i], kb[4 * j + i], acc, 0, 0, 0);
                     }
-#pragma unroll
-                    for (int k = 0; k < KS; ++k) {
-                        const float qv = __uint_as_float((k & 1) ? (qpk[k >> 1] & 0xffff0000u) : (qpk[k >> 1] << 16));
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv, kb[k], acc, 0, 0, 0);
-                    }
-                } else {
-                    float qa[KS];
-#pragma unroll
-                    for (int j = 0; j < KS / 4; ++j) Vec4<QT>::load(qp + 16 * j, qa + 4 * j);
-#pragma unroll
-                    for (int k = 0; k < KS; ++k)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ok ? qa[k] : 0.f, kb[k], acc, 0, 0, 0);
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -231,10 +286,8 @@ __global__ __launch_bounds__(kBkThreads) void k_bk_score(SearchArgs a, int t, in
                     const int r = rt * 16 + 4 * grp + e;
                     const int child = ct * NPG + col / R;
                     if ((col % R) == 0 && r < rows && child < nchild) {
-                        int walk, slot0;
-                        row_of(r, walk, slot0);
-                        const int slot = slot0 + child;
-                        if (slot < cap) a.score[static_cast<int64_t>(walk) * cap + slot] = v;
+                        const int slot = s_slot[r] + child;
+                        if (slot < cap) a.score[static_cast<int64_t>(s_walk[r]) * cap + slot] = v;
                     }
                 }
             }
