@@ -51,6 +51,7 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kUaWaves = 4;
+constexpr int kUaBatch = 1024;         // selected blocks gathered in LDS before their tiles run
 
 __device__ __forceinline__ short4_t pk4(uint32_t lo, uint32_t hi) {
     short4_t r;
@@ -282,16 +283,15 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
     const int64_t p = ua_pair(a, g);
     const int nchunks = static_cast<int>((a.n1 + kUaBlocks - 1) / kUaBlocks);
     const int j0 = r * a.ua_cpw, j1 = min(nchunks, j0 + a.ua_cpw);
-    const int jend = j1 + (r == wpg - 1 ? 1 : 0);   // the last workgroup also takes the tail
     const float s = a.sharpness;
     const int64_t tail0 = static_cast<int64_t>(c) * a.n1;
     const int tail_keys = static_cast<int>(a.n_tokens - tail0);
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const uint16_t *gmask = a.umask + g * a.n1cap;
     const uint32_t *gchunks = a.uchunk + g * a.cwords;
-    __shared__ int32_t s_blk[kUaBlocks];
-    __shared__ uint32_t s_msk[kUaBlocks];
-    __shared__ int32_t s_cnt[2];
+    __shared__ int32_t s_blk[kUaBatch];
+    __shared__ uint32_t s_msk[kUaBatch];
+    __shared__ int32_t s_cnt[kUaWaves];
     __shared__ float s_m[kUaWaves][16], s_l[kUaWaves][16];
     __shared__ float s_o[kUaWaves][D * 16];
     const bf16_t *kc = static_cast<const bf16_t *>(a.k) + p * a.max_tokens * D;
@@ -319,28 +319,12 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
     for (int q = 0; q < DT; ++q) acc[q] = float4_t{0.f, 0.f, 0.f, 0.f};
     bool any = false;
 
-    for (int j = j0; j < jend; ++j) {
-        const bool tail_item = j >= j1;
-        if (!tail_item && !((gchunks[j >> 5] >> (j & 31)) & 1u)) continue;   // no block selected here
-        // the chunk's selected blocks, in order (two wavefronts of 64 entries)
-        uint32_t mk = 0u;
-        unsigned long long bal = 0ull;
-        const int b = j * kUaBlocks + (wave & 1) * 64 + lane;
-        if (!tail_item && wave < 2) {
-            mk = (b < a.n1) ? gmask[b] : 0u;
-            bal = __ballot(mk != 0u);
-            if (lane == 0) s_cnt[wave] = __popcll(bal);
-        }
-        __syncthreads();
-        if (!tail_item && wave < 2 && mk != 0u) {
-            const int at = (wave ? s_cnt[0] : 0) + __popcll(bal & below);
-            s_blk[at] = b;
-            s_msk[at] = mk;
-        }
-        const int nkeys = tail_item ? tail_keys : (s_cnt[0] + s_cnt[1]) * c;
-        __syncthreads();
-        if (nkeys <= 0) continue;
-        any = true;
+    // The workgroup's selected blocks are gathered into an LDS batch (two
+    // chunks per round, one wavefront per half chunk) and the batch's keys
+    // run as one stream of 16-key tiles, so the tile loop is long and the
+    // barriers few even when each chunk holds only a handful of blocks; the
+    // raw tail (last workgroup of the group) runs as a pass of its own.
+    auto process = [&](const int nkeys, const bool tail_item) {
         auto token_of = [&](int kk) -> int64_t {
             if (tail_item) return tail0 + kk;
             return (static_cast<int64_t>(s_blk[kk >> log2c]) << log2c) + (kk & (c - 1));
@@ -439,7 +423,50 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
             load_tile(t, T);
             run_tile(t, T);
         }
-        __syncthreads();                           // the tiles read s_blk / s_msk
+    };
+    // the next chunk at or after x in [j0, j1) holding a selected block (j1: none)
+    auto next_set = [&](int x) -> int {
+        while (x < j1) {
+            const uint32_t wd = gchunks[x >> 5] >> (x & 31);
+            if (wd != 0u) return x + __ffs(wd) - 1;
+            x = (x | 31) + 1;
+        }
+        return j1;
+    };
+    int nb = 0;                                    // blocks in the batch
+    int ja = next_set(j0);
+    while (ja < j1) {
+        const int jb = next_set(ja + 1);
+        const int jm = (wave < 2) ? ja : jb;
+        const int blk = jm * kUaBlocks + (wave & 1) * 64 + lane;
+        const uint32_t mk = (jm < j1 && blk < a.n1) ? gmask[blk] : 0u;
+        const unsigned long long bal = __ballot(mk != 0u);
+        if (lane == 0) s_cnt[wave] = __popcll(bal);
+        __syncthreads();
+        int before = nb, total = nb;
+#pragma unroll
+        for (int v = 0; v < kUaWaves; ++v) {
+            if (v < wave) before += s_cnt[v];
+            total += s_cnt[v];
+        }
+        if (mk != 0u) {
+            const int at = before + __popcll(bal & below);
+            s_blk[at] = blk;
+            s_msk[at] = mk;
+        }
+        nb = total;
+        ja = (jb < j1) ? next_set(jb + 1) : j1;
+        __syncthreads();                           // s_cnt is read; the batch entries are written
+        if (nb > 0 && (ja >= j1 || nb + 2 * kUaBlocks > kUaBatch)) {
+            any = true;
+            process(nb * c, false);
+            __syncthreads();                       // the tiles read s_blk / s_msk
+            nb = 0;
+        }
+    }
+    if (r == wpg - 1 && tail_keys > 0) {
+        any = true;
+        process(tail_keys, true);
     }
     if (!any) {                                    // uniform: no keys in this workgroup's range
         if (tid == 0) a.ic[item] = 0;
