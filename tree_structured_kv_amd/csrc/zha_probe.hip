@@ -4,16 +4,28 @@
 
 namespace zha {
 
+// Eight 16-byte nontemporal loads in flight per lane, 64 workgroups per CU
+// over the grid: the best of the read streams tried on MI355X (ordinary
+// loads, 4 or 8 in flight, strided or contiguous per workgroup, 8 to 64
+// workgroups per CU: 5.3-5.9 TB/s; nontemporal: 6.3-6.9 TB/s).  Nontemporal
+// loads are not used by the search or attention kernels: there they slowed
+// the kernels that ran after them more than they sped up their own reads.
 __global__ __launch_bounds__(kBlock) void k_read_probe(const uint4 *buf, uint64_t n16, float *sink) {
+    constexpr int U = 8;
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
     uint32_t acc = 0;
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kBlock;
     uint64_t i = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        uint4 a = buf[i], b = buf[i + stride], c = buf[i + 2 * stride], d = buf[i + 3 * stride];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        u4v v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u4v *)(buf + i + u * stride));
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
     for (; i < n16; i += stride) {
-        uint4 a = buf[i];
+        const uint4 a = buf[i];
         acc ^= a.x ^ a.y ^ a.z ^ a.w;
     }
     // keep the loads alive: a write that practically never happens
@@ -23,7 +35,7 @@ __global__ __launch_bounds__(kBlock) void k_read_probe(const uint4 *buf, uint64_
 hipError_t launch_probe(const void *buf, uint64_t bytes, float *sink, hipStream_t st) {
     const uint64_t n16 = bytes / 16;
     if (n16 == 0) return hipSuccess;
-    const unsigned grid = 256 * 16;   // 16 workgroups per CU
+    const unsigned grid = 256 * 64;   // 64 workgroups per CU
     hipLaunchKernelGGL(k_read_probe, dim3(grid), dim3(kBlock), 0, st,
                        static_cast<const uint4 *>(buf), n16, sink);
     return hipGetLastError();
