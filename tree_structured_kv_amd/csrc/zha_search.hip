@@ -318,11 +318,16 @@ __global__ __launch_bounds__(kScoreThreads) void k_ls_score(SearchArgs a, int t,
 }
 
 // Step t cut: one workgroup per walk.
+constexpr int kLsStage = 6144;         // candidates a level-synchronous cut stages in LDS (48 KB)
+constexpr int kStageU = 12;            // staging loads in flight per thread
+
 template <int R>
 __global__ __launch_bounds__(kThreads) void k_ls_cut(SearchArgs a, int t) {
     const int tid = threadIdx.x;
     const int w = blockIdx.x;
     __shared__ SelectShared sh;
+    __shared__ uint32_t s_id[kLsStage];
+    __shared__ float s_sc[kLsStage];
     __shared__ WalkState st;
     __shared__ int s_base;
     if (tid == 0) st = a.state[w];
@@ -337,15 +342,45 @@ __global__ __launch_bounds__(kThreads) void k_ls_cut(SearchArgs a, int t) {
     int32_t *selw = a.sel_blocks + static_cast<int64_t>(w) * a.sel_cap;
 
     const bool forced = step_forced(a, t, n);
+    // the walk's candidate ids and scores, staged in LDS once (kLsStage
+    // entries at most; all loads of a lane in flight together), so that the
+    // cut's passes and the opening read no global memory
+    const bool staged = n <= kLsStage;
+    float m = -INFINITY;
+    if (staged) {
+        for (int i0 = tid; i0 < n; i0 += kStageU * kThreads) {
+            uint32_t id[kStageU];
+            float v[kStageU];
+#pragma unroll
+            for (int u = 0; u < kStageU; ++u) {
+                const int i = i0 + u * kThreads;
+                id[u] = i < n ? cur[i] : 0u;
+                v[u] = (i < n && !forced) ? sc[i] : -INFINITY;
+            }
+#pragma unroll
+            for (int u = 0; u < kStageU; ++u) {
+                const int i = i0 + u * kThreads;
+                if (i < n) {
+                    s_id[i] = id[u];
+                    s_sc[i] = v[u];
+                    m = fmaxf(m, v[u]);
+                }
+            }
+        }
+    } else if (!forced) {
+        for (int i = tid; i < n; i += kThreads) m = fmaxf(m, sc[i]);
+    }
+    const uint32_t *cid = staged ? s_id : cur;
+    const float *csc = staged ? s_sc : sc;
     unsigned long long tau = 0;
     if (!forced) {
-        float m = -INFINITY;
-        for (int i = tid; i < n; i += kThreads) m = fmaxf(m, sc[i]);
-        const float mx = block_max(m, sh);
-        tau = cut_tau_win(a, n, cur, sc, mx, a.k[t], sh);
+        const float mx = block_max(m, sh);        // also a barrier: the staged entries are complete
+        tau = cut_tau_win(a, n, cid, csc, mx, a.k[t], sh);
+    } else {
+        __syncthreads();
     }
     uint32_t ta, tb;
-    open_cut(a, n, cur, sc, forced, tau, nxt, selw, st.sel_n, ta, tb, sh);
+    open_cut(a, n, cid, csc, forced, tau, nxt, selw, st.sel_n, ta, tb, sh);
     __syncthreads();
     if (tid == 0) {
         int64_t nn = static_cast<int64_t>(tb) * a.chunk;
