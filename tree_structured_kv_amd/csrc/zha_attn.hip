@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
     constexpr int EPL = Vec16<KT>::N;     // elements per lane per row
     constexpr int LPK = D / EPL;          // lanes per key row
     constexpr int KPW = 64 / LPK;         // keys per 64-lane load
-    constexpr int U = 8;                  // key rows in flight per lane group
+    constexpr int U = 4;                  // key rows in flight per lane group (2, 6, 8, 16: slower)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int slot = lane / LPK, sub = lane % LPK;
