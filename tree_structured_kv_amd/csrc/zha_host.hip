@@ -391,6 +391,7 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
     // c^s nodes to the list of step s < l
     a.small_steps = 0;
     if (engine == ZHA_ENGINE_UNION) {
+        double all = 0.0;                          // nodes of the fused steps together
         for (int s = 0; s < g.levels && s < ZHA_MAX_STEPS; ++s) {
             double bound = 0.0, cs = 1.0;
             for (int i = 0; i < s; ++i) cs *= g.chunk;
@@ -398,7 +399,8 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
                 const int64_t roots = (l == g.levels) ? a.nl[l] : a.nl[l] - int64_t(g.chunk) * a.nl[l + 1];
                 bound += static_cast<double>(roots) * cs;
             }
-            if (bound > kSmallList) break;
+            all += bound;
+            if (bound > kSmallList || all > kTopNodes) break;
             a.small_steps = s + 1;
         }
     }

@@ -19,6 +19,7 @@ constexpr int kTile = 32;            // candidates per tile of the level-synchro
 constexpr int kFlatPad = 32;         // union engine: each run of scoring entries is padded to this
 constexpr int kExpSlices = 8;        // union engine: workgroups (runs) per pair building the next list
 constexpr int kSmallList = 64;       // union engine: list bound of the steps fused into one launch
+constexpr int kTopNodes = 256;       // union engine: nodes the fused first steps may meet, all steps
 constexpr int kUaBlocks = 128;       // union attention: level-1 blocks per work item
 constexpr int kUaMaxItems = 4096;    // union attention: work items per pair (at most)
 constexpr int kUaSlice = 16384;      // union attention: level-1 blocks per mask-building workgroup

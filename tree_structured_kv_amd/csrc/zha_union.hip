@@ -145,9 +145,12 @@ __device__ __forceinline__ void load_tables(const SearchArgs &a, LevelTables &tb
 //
 // score_run: one wavefront scores blocks b0 .. b1-1 (WB = NPG*kUG entries
 // each) of a list whose entry e is entry(e) = {pair, list position (-1:
-// pad), node id}; scores go to u_score.
-template <int D, int R, typename QT, typename ST, typename Entry>
-__device__ __forceinline__ void score_run(const SearchArgs &a, const LevelTables &tb, Entry entry, int b0, int b1) {
+// pad), node id}; out(pair, position, id, grp, v) takes the scores v[0..3]
+// of heads 4*grp .. 4*grp+3 of each real entry (one lane per entry and
+// grp).
+template <int D, int R, typename QT, typename ST, typename Entry, typename Out>
+__device__ __forceinline__ void score_run(const SearchArgs &a, const LevelTables &tb, Entry entry, int b0, int b1,
+                                          Out out) {
     constexpr int NPG = 16 / R;           // nodes per matrix tile
     constexpr int KS = D / 4;             // 16x16x4 steps
     constexpr int WB = NPG * kUG;         // nodes per block
@@ -158,7 +161,6 @@ __device__ __forceinline__ void score_run(const SearchArgs &a, const LevelTables
     const int64_t *s_cap = tb.cap;
     if (b0 >= b1) return;
     const float s = a.sharpness;
-    const int gp = (a.group + 3) & ~3;    // heads per score row (padded)
 
     int4 nxt[kUG];
 #pragma unroll
@@ -282,18 +284,26 @@ __device__ __forceinline__ void score_run(const SearchArgs &a, const LevelTables
                 if (x != x) x = -INFINITY;
                 v[e] = (x == 0.f) ? 0.f : x;
             }
-            // heads 4*grp .. 4*grp+3 of node `pos`: one 16-byte store
-            if ((col % R) == 0 && pos >= 0 && 4 * grp < a.group)
-                *reinterpret_cast<float4 *>(a.u_score + (static_cast<int64_t>(p) * a.cand_cap + pos) * gp + 4 * grp) =
-                    make_float4(v[0], v[1], v[2], v[3]);
-            if (a.visited && (col % R) == 0 && grp == 0 && pos >= 0) {
-                const uint32_t id = static_cast<uint32_t>(ent[u].z);
-                const int64_t bitn = a.node_off[id >> kLevelShift] + (id & kIndexMask);
-                atomicOr(a.visited + p * a.vis_words + (bitn >> 5), 1u << (bitn & 31));
-            }
+            if ((col % R) == 0 && pos >= 0) out(p, pos, static_cast<uint32_t>(ent[u].z), grp, v);
         }
     }
 }
+
+// Scores of heads 4*grp .. 4*grp+3 of list entry `pos` of pair p to
+// u_score (one 16-byte store), and the node marked in the visited bitmap.
+struct UScoreOut {
+    const SearchArgs &a;
+    __device__ __forceinline__ void operator()(int p, int pos, uint32_t id, int grp, const float (&v)[4]) const {
+        const int gp = (a.group + 3) & ~3;
+        if (4 * grp < a.group)
+            *reinterpret_cast<float4 *>(a.u_score + (static_cast<int64_t>(p) * a.cand_cap + pos) * gp + 4 * grp) =
+                make_float4(v[0], v[1], v[2], v[3]);
+        if (a.visited && grp == 0) {
+            const int64_t bitn = a.node_off[id >> kLevelShift] + (id & kIndexMask);
+            atomicOr(a.visited + p * a.vis_words + (bitn >> 5), 1u << (bitn & 31));
+        }
+    }
+};
 
 template <int D, int R, typename QT, typename ST>
 __global__ __launch_bounds__(kScoreThreads) void k_un_score(SearchArgs a, int t, int n0) {
@@ -323,7 +333,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_un_score(SearchArgs a, int t,
         }
         return flat[e];
     };
-    score_run<D, R, QT, ST>(a, tb, entry, b0, b1);
+    score_run<D, R, QT, ST>(a, tb, entry, b0, b1, UScoreOut{a});
 }
 
 // Step t, one workgroup per walk (head h of pair p).  The head's candidates
@@ -906,60 +916,252 @@ __global__ __launch_bounds__(kThreads) void k_un_expand(SearchArgs a, int t) {
 }
 
 // The first `steps` steps of every pair in one launch, one workgroup per
-// pair (while the lists are short, a launch per kernel and step costs more
-// than the work): per step the pair's whole list is scored (when some head
-// needs scores), each head's cut runs on one wavefront (cut_wave), and the
-// workgroup builds the next list (expand_slice, every slice in turn),
-// including the flat scoring list of the first step the grid-wide kernels
-// take over.
+// pair, in LDS.  The host bounds the candidates of each of these steps to
+// kSmallList per pair: every node a walk of the pair could meet at step s is
+// a depth-s descendant of a root (D_s), and D_0 .. D_{steps-1} are few.  The
+// workgroup enumerates them, scores them all for every head in one pass of
+// record loads (matrix tiles, as the grid-wide scorer), then runs each step's
+// cut per head on one wavefront (cut_wave's rules: the candidates are the
+// children of the entries the head opened, in order; wave_tau's cut key)
+// from LDS, and builds no list in memory until the last step: there it
+// writes what the grid-wide kernels take over -- the next union list (the
+// children of the entries any head opened, in order), its cleared open masks
+// and flat scoring entries, the ranks of the opened entries, each head's
+// opened positions and count, and the walk states.  Entries of D_s that no
+// head reaches are scored but never read.
+struct TopShared {
+    uint32_t id[kTopNodes];               // D_0, D_1, .. concatenated
+    int16_t cbase[kTopNodes];             // index in D_{s+1} of an entry's first child (-1: level 1)
+    float sc[kTopNodes][16];              // scores, [entry][head]
+    int32_t doff[ZHA_MAX_STEPS + 2];      // D_s = entries doff[s] .. doff[s+1]-1
+    uint8_t open[2][16][kSmallList];      // a head's opened entries (index in D_s), by step parity
+    int32_t nopen[16];
+    uint32_t mask[kSmallList];            // heads that opened each entry of D_s
+    uint8_t ord[kSmallList];              // the entry of each rank among the opened ones
+    int32_t scored[16][ZHA_MAX_STEPS], opened[16][ZHA_MAX_STEPS];
+    int32_t unforced[16], sel_n[16], steps[16];
+    uint32_t flags[16];
+    int32_t active[16];
+    int32_t need;
+};
+
 template <int D, int R, typename QT, typename ST>
 __global__ __launch_bounds__(kThreads) void k_un_small(SearchArgs a, int steps) {
     constexpr int WB = (16 / R) * kUG;    // nodes per scoring block
-    const int p = blockIdx.x, wave = threadIdx.x >> 6;
-    const int cap = a.cand_cap, c = a.chunk;
+    const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cap = a.cand_cap, c = a.chunk, log2c = a.log2c, G = a.group;
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     __shared__ LevelTables tb;
+    __shared__ TopShared T;
     __shared__ WaveCutShared wc[kWaves];
-    __shared__ ExpandShared esh;
-    __shared__ int s_need;
     load_tables(a, tb);
-    for (int t = 0; t < steps; ++t) {
-        const int buf = t & 1;
-        // does some head's cut need scores?  (one thread per head)
-        if (threadIdx.x == 0) s_need = 0;
-        const int n_u = a.u_n[2 * p + buf];
-        __syncthreads();
-        if (n_u > 0 && threadIdx.x < a.group) {
-            bool need;
-            if (t == 0) {
-                need = !step_forced(a, 0, n_u);
-            } else {
-                const int64_t nh = static_cast<int64_t>(a.u_next[head_walk(a, p, threadIdx.x)]) * c;
-                need = nh > 0 && !step_forced(a, t, static_cast<int>(nh < cap ? nh : cap));
+    const int n0 = a.u_n[2 * p];                   // the roots (k_un_init)
+    if (n0 <= 0) return;                           // empty tree: k_un_init finished the walks (uniform)
+    const uint32_t *ids0 = a.u_ids + static_cast<int64_t>(p) * 2 * cap;
+    for (int i = tid; i < n0; i += kThreads) T.id[i] = ids0[i];
+    if (tid == 0) {
+        T.doff[0] = 0;
+        T.doff[1] = n0;
+    }
+    if (tid < G) {
+        const WalkState &st = a.state[head_walk(a, p, tid)];
+        for (int i = 0; i < ZHA_MAX_STEPS; ++i) {
+            T.scored[tid][i] = st.scored[i];
+            T.opened[tid][i] = st.opened[i];
+        }
+        T.unforced[tid] = st.unforced;
+        T.sel_n[tid] = st.sel_n;
+        T.steps[tid] = st.steps;
+        T.flags[tid] = st.flags;
+        T.active[tid] = 1;
+        T.nopen[tid] = 0;
+    }
+    __syncthreads();
+    // D_{s+1}: the children of D_s's entries above level 1, in order (one
+    // wavefront; D_s holds at most 64 entries, one per lane)
+    for (int s = 0; s + 1 < steps; ++s) {
+        if (wave == 0) {
+            const int b = T.doff[s], e = T.doff[s + 1];
+            const int i = b + lane;
+            uint32_t id = 0;
+            bool par = false;
+            if (i < e) {
+                id = T.id[i];
+                par = (id >> kLevelShift) > 1u;
             }
-            if (need) s_need = 1;
+            const unsigned long long bal = __ballot(par);
+            const int k = __popcll(bal & below);
+            if (i < e) T.cbase[i] = static_cast<int16_t>(par ? k * c : -1);
+            if (par) {
+                const uint32_t lvl = id >> kLevelShift, j = id & kIndexMask;
+                for (int ch = 0; ch < c; ++ch)
+                    T.id[e + k * c + ch] = ((lvl - 1u) << kLevelShift) | (j * static_cast<uint32_t>(c) + ch);
+            }
+            if (lane == 0) T.doff[s + 2] = e + __popcll(bal) * c;
         }
         __syncthreads();
-        if (s_need) {
-            const uint32_t *ids = a.u_ids + (static_cast<int64_t>(p) * 2 + buf) * cap;
-            const int nb = (n_u + WB - 1) / WB;
-            const int per = (nb + kWaves - 1) / kWaves;
-            const int b0 = wave * per, b1 = min(nb, b0 + per);
-            auto entry = [&](int e) -> int4 {
-                const int pos = e < n_u ? e : n_u - 1;
-                return make_int4(p, e < n_u ? e : -1, static_cast<int>(ids[pos]), 0);
-            };
-            score_run<D, R, QT, ST>(a, tb, entry, b0, b1);
+    }
+    // every entry of D_0 .. D_{steps-1}, scored for every head
+    {
+        const int ntot = T.doff[steps];
+        const int nb = (ntot + WB - 1) / WB;
+        const int per = (nb + kWaves - 1) / kWaves;
+        const int b0 = wave * per, b1 = min(nb, b0 + per);
+        auto entry = [&](int e) -> int4 {
+            const int pos = e < ntot ? e : ntot - 1;
+            return make_int4(p, e < ntot ? e : -1, static_cast<int>(T.id[pos]), 0);
+        };
+        auto out = [&](int, int pos, uint32_t, int grp, const float (&v)[4]) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * grp + e < G) T.sc[pos][4 * grp + e] = v[e];
+        };
+        score_run<D, R, QT, ST>(a, tb, entry, b0, b1, out);
+    }
+    __syncthreads();
+    for (int s = 0; s < steps; ++s) {
+        const int b = T.doff[s], cur = s & 1;
+        // some head's cut needs scores (the nodes of the step are then
+        // marked visited, as the grid-wide scorer marks its lists)
+        if (tid == 0) T.need = 0;
+        for (int i = tid; i < kSmallList; i += kThreads) T.mask[i] = 0u;
+        __syncthreads();
+        if (tid < G && T.active[tid]) {
+            const int cnt = (s == 0) ? n0 : T.nopen[tid] * c;
+            if (!step_forced(a, s, cnt)) T.need = 1;
         }
         __syncthreads();
-        for (int h = wave; h < a.group; h += kWaves) cut_wave<R>(a, t, head_walk(a, p, h), wc[wave]);
+        for (int h = wave; h < G; h += kWaves) {
+            if (!T.active[h]) continue;            // opened nothing at an earlier step
+            WaveCutShared &L = wc[wave];
+            const int w = head_walk(a, p, h);
+            const int cnt = (s == 0) ? n0 : T.nopen[h] * c;
+            // candidate x: entry `pos` of D_s
+            int pos = 0;
+            if (lane < cnt)
+                pos = (s == 0) ? lane : T.cbase[T.doff[s - 1] + T.open[cur ^ 1][h][lane >> log2c]] + (lane & (c - 1));
+            const bool in = lane < cnt;
+            const uint32_t id = in ? T.id[b + pos] : 0u;
+            const float v = in ? T.sc[b + pos][h] : -INFINITY;
+            if (in) {
+                L.sc[lane] = v;
+                L.id[lane] = id;
+                L.pos[lane] = pos;
+            }
+            if (a.visited && T.need && in) {
+                const int64_t bitn = a.node_off[id >> kLevelShift] + (id & kIndexMask);
+                atomicOr(a.visited + static_cast<int64_t>(p) * a.vis_words + (bitn >> 5), 1u << (bitn & 31));
+            }
+            __builtin_amdgcn_wave_barrier();
+            const bool forced = step_forced(a, s, cnt);
+            unsigned long long tau = 0;
+            if (!forced) tau = wave_tau(a, cnt, L.id, L.sc, wave_max(in ? v : -INFINITY, 1, 64), a.k[s], L);
+            // open, in candidate order
+            const bool op = in && (forced || rank_key(v, id, log2c) >= tau);
+            const bool l1 = op && (id >> kLevelShift) == 1u;
+            const bool hi = op && (id >> kLevelShift) > 1u;
+            const unsigned long long m1 = __ballot(l1), mh = __ballot(hi);
+            const int sel0 = T.sel_n[h];
+            if (l1) {
+                const int64_t at = static_cast<int64_t>(sel0) + __popcll(m1 & below);
+                if (at < a.sel_cap) a.sel_blocks[static_cast<int64_t>(w) * a.sel_cap + at] = static_cast<int32_t>(id & kIndexMask);
+            }
+            if (hi) {
+                T.open[cur][h][__popcll(mh & below)] = static_cast<uint8_t>(pos);
+                atomicOr(&T.mask[pos], 1u << h);
+            }
+            const int nopen = __popcll(__ballot(op));
+            __builtin_amdgcn_wave_barrier();
+            if (lane == 0) {
+                T.scored[h][s] = cnt;
+                T.opened[h][s] = nopen;
+                if (!forced) T.unforced[h] += cnt;
+                T.sel_n[h] = sel0 + __popcll(m1);
+                T.steps[h] = s + 1;
+                T.nopen[h] = __popcll(mh);
+                T.active[h] = __popcll(mh) > 0;
+            }
+        }
         __syncthreads();
-        // only the hand-over step is scored from the flat list: pairs run
-        // at their own pace, so an earlier step's entries (same buffer
-        // parity) could overwrite another pair's
-        for (int sl = 0; sl < kExpSlices; ++sl) {
-            expand_slice<R>(a, t, p, sl, esh, t + 1 == steps);
+        // the union of the opened entries, ranked in order (one wavefront)
+        const int nd = T.doff[s + 1] - b;
+        __shared__ int32_t s_total;
+        if (wave == 0) {
+            const bool o = lane < nd && T.mask[lane] != 0u;
+            const unsigned long long bal = __ballot(o);
+            if (s + 1 == steps && o) {
+                const int k = __popcll(bal & below);
+                a.u_rank[static_cast<int64_t>(p) * cap + lane] = k;
+                a.u_par[static_cast<int64_t>(p) * cap + k] = T.id[b + lane];
+                T.ord[k] = static_cast<uint8_t>(lane);
+            }
+            if (lane == 0) s_total = __popcll(bal);
+        }
+        __syncthreads();
+        const int total = s_total;
+        int64_t n_next = static_cast<int64_t>(total) * c;
+        const bool overflow = n_next > cap;
+        if (overflow) n_next = cap;
+        const bool last = (n_next == 0) || (s + 1 >= a.levels) || (s + 1 >= ZHA_MAX_STEPS);
+        if (!last && s + 1 < steps) continue;      // uniform: the next step runs from LDS
+        // hand-over (or the end of the pair's walks)
+        const int nxt = (s + 1) & 1;
+        if (!last) {
+            uint32_t *nids = a.u_ids + (static_cast<int64_t>(p) * 2 + nxt) * cap;
+            uint32_t *om_next = a.u_omask + (static_cast<int64_t>(p) * 2 + nxt) * cap;
+            __shared__ int32_t s_need, s_base;
+            if (tid == 0) {
+                bool need = false;
+                for (int h = 0; h < G; ++h) {
+                    const int64_t nh = static_cast<int64_t>(T.nopen[h]) * c;
+                    if (nh > 0 && !step_forced(a, s + 1, static_cast<int>(nh < cap ? nh : cap))) need = true;
+                }
+                s_need = need ? 1 : 0;
+                s_base = need ? atomicAdd(&a.tile_count[s + 1], round_flat(static_cast<int>(n_next))) : 0;
+            }
             __syncthreads();
+            const int cnt = static_cast<int>(n_next);
+            const int padded = s_need ? round_flat(cnt) : cnt;
+            int4 *flat = a.u_flat + static_cast<int64_t>((s + 1) & 1) * a.flat_cap;
+            // ranked entry k is the k-th set entry of the mask
+            for (int x = tid; x < padded; x += kThreads) {
+                const int xr = x < cnt ? x : 0;
+                const uint32_t pid = T.id[b + T.ord[xr >> log2c]];   // the opened entry of rank xr / c
+                const uint32_t lvl = pid >> kLevelShift, j = pid & kIndexMask;
+                const uint32_t child = ((lvl - 1u) << kLevelShift) | (j * static_cast<uint32_t>(c) + (xr & (c - 1)));
+                if (x < cnt) {
+                    nids[x] = child;
+                    om_next[x] = 0u;
+                }
+                if (s_need) flat[s_base + x] = make_int4(p, x < cnt ? x : -1, static_cast<int>(child), 0);
+            }
         }
+        if (tid == 0) {
+            a.u_n[2 * p + nxt] = last ? 0 : static_cast<int32_t>(n_next);
+            a.u_n[2 * p + (nxt ^ 1)] = last ? 0 : nd;
+        }
+        if (tid < G) {
+            const int h = tid, w = head_walk(a, p, h);
+            WalkState *st = a.state + w;
+            for (int i = 0; i < ZHA_MAX_STEPS; ++i) {
+                st->scored[i] = T.scored[h][i];
+                st->opened[i] = T.opened[h][i];
+            }
+            const uint32_t fl = T.flags[h] | (overflow ? ZHA_FLAG_CAND_OVERFLOW : 0u);
+            st->unforced = T.unforced[h];
+            st->sel_n = T.sel_n[h];
+            st->steps = T.steps[h];
+            st->flags = fl;
+            a.u_next[w] = T.nopen[h];
+            if (last) finish_walk<R>(a, w, T.steps[h], T.scored[h], T.opened[h], T.sel_n[h], T.unforced[h], fl);
+        }
+        // each head's opened entries of D_s, as list positions for the next cut
+        for (int i = tid; i < G * kSmallList; i += kThreads) {
+            const int h = i / kSmallList, k = i - h * kSmallList;
+            if (!last && k < T.nopen[h])
+                a.u_open[static_cast<int64_t>(head_walk(a, p, h)) * cap + k] = T.open[s & 1][h][k];
+        }
+        return;
     }
 }
 
