@@ -54,8 +54,7 @@ constexpr int kUG = 2;                // matrix tiles in flight per wavefront
 constexpr int kLdsCand = 14336;       // candidate scores a cut stages in LDS (56 KB)
 constexpr int kLdsPar = 2048;         // parent ranks a cut stages in LDS (8 KB)
 constexpr int kExpMin = 256;          // list entries per expand workgroup (at least)
-constexpr int kWaveCand = 128;        // candidates a wavefront cut stages in LDS
-static_assert(kSmallList <= kWaveCand, "a fused step's candidates fit in LDS");
+static_assert(kSmallList <= 64, "a fused step's candidates fit one wavefront, one per lane");
 
 __device__ __forceinline__ int head_walk(const SearchArgs &a, int pair, int h) {
     const int b = pair / a.kv_heads, g = pair % a.kv_heads;
@@ -527,54 +526,24 @@ __device__ __forceinline__ void cut_head(const SearchArgs &a, int t, int w, Sele
     }
 }
 
-// Per-wavefront LDS of the fused first steps (k_un_small): a histogram of
-// 8-bit key digits, each bin holding (count << 48) + weight, and the head's
-// candidates (score, id, list position) when they fit.
-struct WaveCutShared {
-    unsigned long long hist[256];
-    float sc[kWaveCand];
-    uint32_t id[kWaveCand];
-    int32_t pos[kWaveCand];
-};
-
-constexpr int kCountShift = 48;       // weights of a list stay below 2^48 (at most 2^17 x 2^31)
-
-__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const unsigned long long o = __shfl_xor(v, off, 64);
-        v = o > v ? o : v;
-    }
-    return v;
-}
-
-// Wavefront: the cut key of cut_tau -- the rank key of the candidate at
+// Wavefront, at most 64 candidates, one per lane (key 0 and weight 0 on the
+// other lanes): the cut key of cut_tau -- the rank key of the candidate at
 // which the weight summed in decreasing key order first reaches what the
-// step needs (weights and need exactly as there) -- by an 8-bit radix
-// select over the 64-bit keys with the histogram in the wavefront's LDS.
-// Candidates i < n have scores vs[i] and ids is[i].
-__device__ unsigned long long wave_tau(const SearchArgs &a, int n, const uint32_t *is, const float *vs, float mx,
-                                       int kt, WaveCutShared &L) {
+// step needs (weights and need exactly as there) -- by a bitonic sort of the
+// (key, weight) pairs across the lanes (keys are distinct: they hold the
+// span start), an inclusive scan of the weights and a ballot.
+__device__ unsigned long long lane_tau(const SearchArgs &a, bool in, float v, uint32_t id, float mx, int n, int kt) {
     const int lane = threadIdx.x & 63;
-    const int log2c = a.log2c;
     const bool by_mass = (a.mode == ZHA_TOPP) && (a.p > 0.f);
     const bool flat = !(mx > -INFINITY);   // every score -inf: equal masses
-    auto weight = [&](float v) -> unsigned long long {
-        if (!by_mass) return 1ull;
-        const float e = flat ? 1.f : expf(v - mx);
-        return static_cast<unsigned long long>(__float2uint_rn(e * kMassScale));
-    };
+    uint32_t wt = 0u;
+    if (in) wt = by_mass ? __float2uint_rn((flat ? 1.f : expf(v - mx)) * kMassScale) : 1u;
+    unsigned long long key = in ? rank_key(v, id, a.log2c) : 0ull;
     unsigned long long need;
     if (by_mass) {
-        unsigned long long zp = 0;
-        for (int i = lane; i < n; i += 64) zp += weight(vs[i]);
-        const unsigned long long z = wave_sum_u64(zp);
+        unsigned long long z = wt;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
         const double tq = ceil(static_cast<double>(a.p) * static_cast<double>(z));
         need = static_cast<unsigned long long>(tq);
         if (need < 1) need = 1;
@@ -583,166 +552,30 @@ __device__ unsigned long long wave_tau(const SearchArgs &a, int n, const uint32_
         const int m = (a.mode == ZHA_TOPK) ? (kt < n ? kt : n) : 1;
         need = static_cast<unsigned long long>(m < 1 ? 1 : m);
     }
-    const unsigned long long wmask = (1ull << kCountShift) - 1ull;
-    unsigned long long prefix = 0, tau = 0;
-    for (int pass = 0; pass < 8; ++pass) {
-        const int shift = 56 - 8 * pass;
-        for (int b = lane; b < 256; b += 64) L.hist[b] = 0;
-        __builtin_amdgcn_wave_barrier();
-        for (int i = lane; i < n; i += 64) {
-            const float v = vs[i];
-            const unsigned long long key = rank_key(v, is[i], log2c);
-            if (pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8)))
-                atomicAdd(&L.hist[static_cast<uint32_t>(key >> shift) & 255u], (1ull << kCountShift) + weight(v));
-        }
-        __builtin_amdgcn_wave_barrier();
-        // lane covers digits 255-4*lane .. 252-4*lane (descending)
-        unsigned long long lw[4], lsum = 0;
+    // descending bitonic sort over the 64 lanes
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { lw[e] = L.hist[255 - 4 * lane - e] & wmask; lsum += lw[e]; }
-        unsigned long long incl = lsum;
+    for (int k = 2; k <= 64; k <<= 1) {
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const unsigned long long o = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += o;
-        }
-        const unsigned long long excl = incl - lsum;
-        const unsigned long long reach = __ballot(incl >= need);
-        const int first = reach ? (__ffsll(static_cast<long long>(reach)) - 1) : 63;
-        unsigned long long run = excl;
-        int pick = 3;
-        for (int e = 0; e < 4; ++e) {
-            if (run + lw[e] >= need) { pick = e; break; }
-            run += lw[e];
-        }
-        if (!reach) { pick = 3; run = excl + lw[0] + lw[1] + lw[2]; }
-        const uint32_t dig = static_cast<uint32_t>(__shfl(static_cast<int>(255 - 4 * lane - pick), first, 64));
-        const unsigned long long above = __shfl(run, first, 64);
-        const unsigned long long cnt = L.hist[dig] >> kCountShift;
-        __builtin_amdgcn_wave_barrier();
-        prefix |= static_cast<unsigned long long>(dig) << shift;
-        need -= above;
-        if (pass == 7) {
-            tau = prefix;
-            break;
-        }
-        if (cnt <= 1) {
-            // at most one key carries this prefix: fetch it
-            unsigned long long found = 0;
-            for (int i = lane; i < n; i += 64) {
-                const unsigned long long key = rank_key(vs[i], is[i], log2c);
-                if ((key >> shift) == (prefix >> shift)) found = key;
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const unsigned long long ok = __shfl_xor(key, j, 64);
+            const uint32_t ow = static_cast<uint32_t>(__shfl_xor(static_cast<int>(wt), j, 64));
+            const bool lower = (lane & j) == 0, desc = (lane & k) == 0;
+            const bool take = (lower == desc) ? (ok > key) : (ok < key);
+            if (take) {
+                key = ok;
+                wt = ow;
             }
-            found = wave_max_u64(found);
-            tau = (cnt == 0) ? 0ull : found;
-            break;
         }
     }
-    return tau;
-}
-
-// Step t for walk w (head h of pair p), on one wavefront: the same result as
-// cut_head -- candidates, exact cut, level-1 selections in span order,
-// opened higher nodes (list positions, in order) with head bit h on them,
-// and the walk's statistics.
-template <int R>
-__device__ void cut_wave(const SearchArgs &a, int t, int w, WaveCutShared &L) {
-    const int lane = threadIdx.x & 63;
-    const int p = w / a.group, h = w % a.group;
-    const uint32_t bit = 1u << h;
-    const int cap = a.cand_cap, log2c = a.log2c, c = a.chunk;
-    const int buf = t & 1;
-    const int n_u = a.u_n[2 * p + buf];
-    if (n_u <= 0) return;                          // the pair has finished
-    const int n_open_prev = (t == 0) ? 0 : a.u_next[w];
-    if (t > 0 && n_open_prev == 0) return;         // this head opened nothing more
-    WalkState *st = a.state + w;
-    const uint32_t *ids = a.u_ids + (static_cast<int64_t>(p) * 2 + buf) * cap;
-    const int gp = (a.group + 3) & ~3;
-    const float *sc = a.u_score + static_cast<int64_t>(p) * cap * gp + h;   // score of position i: sc[i * gp]
-    const int32_t *rank = a.u_rank + static_cast<int64_t>(p) * cap;
-    uint32_t *om = a.u_omask + (static_cast<int64_t>(p) * 2 + buf) * cap;
-    int32_t *opened_pos = a.u_open + static_cast<int64_t>(w) * cap;
-    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-
-    const int64_t raw64 = (t == 0) ? n_u : static_cast<int64_t>(n_open_prev) * c;
-    const int raw = static_cast<int>(raw64 < cap ? raw64 : cap);
-    auto position = [&](int x) -> int {
-        if (t == 0) return x;
-        return rank[opened_pos[x >> log2c]] * c + (x & (c - 1));
-    };
-    // the candidates inside the list: a prefix of length cnt
-    int valid = 0;
-    for (int x = lane; x < raw; x += 64) valid += position(x) < n_u;
+    unsigned long long incl = wt;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) valid += __shfl_xor(valid, off, 64);
-    if (valid == 0) {
-        if (lane == 0) a.u_next[w] = 0;
-        return;
+    for (int off = 1; off < 64; off <<= 1) {
+        const unsigned long long o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
     }
-    // the lists of the fused steps are at most kSmallList long (a bound the
-    // host derives from the tree); a longer one marks the walk
-    int cnt = valid;
-    if (cnt > kWaveCand) {
-        if (lane == 0) atomicOr(&st->flags, ZHA_FLAG_CAND_OVERFLOW);
-        cnt = kWaveCand;
-    }
-    const bool forced = step_forced(a, t, cnt);
-    // stage (score, id, position) in LDS
-    float *vs = L.sc;
-    uint32_t *is = L.id;
-    int32_t *ps = L.pos;
-    float m = -INFINITY;
-    for (int x = lane; x < cnt; x += 64) {
-        const int pos = position(x);
-        ps[x] = pos;
-        is[x] = ids[pos];
-        if (!forced) {
-            // another wavefront of this workgroup wrote it: read past L1
-            const float v = __hip_atomic_load(sc + static_cast<int64_t>(pos) * gp, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-            vs[x] = v;
-            m = fmaxf(m, v);
-        }
-    }
-    __builtin_amdgcn_wave_barrier();
-    unsigned long long tau = 0;
-    if (!forced) tau = wave_tau(a, cnt, is, vs, wave_max(m, 1, 64), a.k[t], L);
-
-    // open, in candidate order
-    const int64_t sel0 = st->sel_n;
-    int32_t *selw = a.sel_blocks + static_cast<int64_t>(w) * a.sel_cap;
-    uint32_t pre1 = 0, preh = 0, nopen = 0;
-    for (int base = 0; base < cnt; base += 64) {
-        const int x = base + lane;
-        const bool in = x < cnt;
-        const uint32_t id = in ? is[x] : 0u;
-        const bool op = in && (forced || rank_key(vs[x], id, log2c) >= tau);
-        const bool l1 = op && (id >> kLevelShift) == 1u;
-        const bool hi = op && (id >> kLevelShift) > 1u;
-        const unsigned long long m1 = __ballot(l1);
-        const unsigned long long mh = __ballot(hi);
-        if (l1) {
-            const int64_t pos = sel0 + pre1 + __popcll(m1 & below);
-            if (pos < a.sel_cap) selw[pos] = static_cast<int32_t>(id & kIndexMask);
-        }
-        if (hi) {
-            const int i = ps[x];
-            opened_pos[preh + __popcll(mh & below)] = i;
-            atomicOr(&om[i], bit);
-        }
-        pre1 += __popcll(m1);
-        preh += __popcll(mh);
-        nopen += __popcll(__ballot(op));
-    }
-    if (lane == 0) {
-        st->scored[t] = cnt;
-        st->opened[t] = static_cast<int32_t>(nopen);
-        if (!forced) st->unforced += cnt;
-        st->sel_n = static_cast<int32_t>(sel0 + pre1);
-        st->steps = t + 1;
-        a.u_next[w] = static_cast<int32_t>(preh);
-    }
+    const unsigned long long hit = __ballot(lane < n && incl >= need);
+    const int first = hit ? (__ffsll(static_cast<long long>(hit)) - 1) : (n - 1);
+    return __shfl(key, first, 64);
 }
 
 // An open mask: set by atomics, so read past L1 (a kernel that cuts and
@@ -767,11 +600,9 @@ __device__ __forceinline__ int expand_slices(int n_u) {
 // next step's open masks at those positions (the masks alternate between
 // two buffers, as the list lengths do, so no slice reads what another
 // clears).  The last slice sees the whole list: it records the next length
-// and finishes the walks after the last step.  Without emit_flat no flat
-// entries are written (the next step is not scored from the flat list).
+// and finishes the walks after the last step.
 template <int R>
-__device__ __forceinline__ void expand_slice(const SearchArgs &a, int t, int p, int s, ExpandShared &sh,
-                                             bool emit_flat = true) {
+__device__ __forceinline__ void expand_slice(const SearchArgs &a, int t, int p, int s, ExpandShared &sh) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cap = a.cand_cap, c = a.chunk, log2c = a.log2c;
     const int cur = t & 1, nxt = cur ^ 1;
@@ -855,7 +686,7 @@ __device__ __forceinline__ void expand_slice(const SearchArgs &a, int t, int p, 
     const int cnt = x1 > x0 ? static_cast<int>(x1 - x0) : 0;
     if (tid == 0) {
         bool need = false;
-        for (int hh = 0; hh < a.group && emit_flat && !final_step && cnt > 0; ++hh) {
+        for (int hh = 0; hh < a.group && !final_step && cnt > 0; ++hh) {
             const int64_t nh = static_cast<int64_t>(a.u_next[head_walk(a, p, hh)]) * c;
             if (nh > 0 && !step_forced(a, t + 1, static_cast<int>(nh < cap ? nh : cap))) need = true;
         }
@@ -921,8 +752,8 @@ __global__ __launch_bounds__(kThreads) void k_un_expand(SearchArgs a, int t) {
 // a depth-s descendant of a root (D_s), and D_0 .. D_{steps-1} are few.  The
 // workgroup enumerates them, scores them all for every head in one pass of
 // record loads (matrix tiles, as the grid-wide scorer), then runs each step's
-// cut per head on one wavefront (cut_wave's rules: the candidates are the
-// children of the entries the head opened, in order; wave_tau's cut key)
+// cut per head on one wavefront (the candidates are the children of the
+// entries the head opened, in order; lane_tau's cut key)
 // from LDS, and builds no list in memory until the last step: there it
 // writes what the grid-wide kernels take over -- the next union list (the
 // children of the entries any head opened, in order), its cleared open masks
@@ -953,7 +784,6 @@ __global__ __launch_bounds__(kThreads) void k_un_small(SearchArgs a, int steps) 
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     __shared__ LevelTables tb;
     __shared__ TopShared T;
-    __shared__ WaveCutShared wc[kWaves];
     load_tables(a, tb);
     const int n0 = a.u_n[2 * p];                   // the roots (k_un_init)
     if (n0 <= 0) return;                           // empty tree: k_un_init finished the walks (uniform)
@@ -1033,7 +863,6 @@ __global__ __launch_bounds__(kThreads) void k_un_small(SearchArgs a, int steps) 
         __syncthreads();
         for (int h = wave; h < G; h += kWaves) {
             if (!T.active[h]) continue;            // opened nothing at an earlier step
-            WaveCutShared &L = wc[wave];
             const int w = head_walk(a, p, h);
             const int cnt = (s == 0) ? n0 : T.nopen[h] * c;
             // candidate x: entry `pos` of D_s
@@ -1043,19 +872,13 @@ __global__ __launch_bounds__(kThreads) void k_un_small(SearchArgs a, int steps) 
             const bool in = lane < cnt;
             const uint32_t id = in ? T.id[b + pos] : 0u;
             const float v = in ? T.sc[b + pos][h] : -INFINITY;
-            if (in) {
-                L.sc[lane] = v;
-                L.id[lane] = id;
-                L.pos[lane] = pos;
-            }
             if (a.visited && T.need && in) {
                 const int64_t bitn = a.node_off[id >> kLevelShift] + (id & kIndexMask);
                 atomicOr(a.visited + static_cast<int64_t>(p) * a.vis_words + (bitn >> 5), 1u << (bitn & 31));
             }
-            __builtin_amdgcn_wave_barrier();
             const bool forced = step_forced(a, s, cnt);
             unsigned long long tau = 0;
-            if (!forced) tau = wave_tau(a, cnt, L.id, L.sc, wave_max(in ? v : -INFINITY, 1, 64), a.k[s], L);
+            if (!forced) tau = lane_tau(a, in, v, id, wave_max(in ? v : -INFINITY, 1, 64), cnt, a.k[s]);
             // open, in candidate order
             const bool op = in && (forced || rank_key(v, id, log2c) >= tau);
             const bool l1 = op && (id >> kLevelShift) == 1u;
@@ -1071,7 +894,6 @@ __global__ __launch_bounds__(kThreads) void k_un_small(SearchArgs a, int steps) 
                 atomicOr(&T.mask[pos], 1u << h);
             }
             const int nopen = __popcll(__ballot(op));
-            __builtin_amdgcn_wave_barrier();
             if (lane == 0) {
                 T.scored[h][s] = cnt;
                 T.opened[h][s] = nopen;
