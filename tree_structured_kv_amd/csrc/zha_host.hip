@@ -400,7 +400,7 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
                 bound += static_cast<double>(roots) * cs;
             }
             all += bound;
-            if (bound > kSmallList || all > kTopNodes) break;
+            if (bound > kSmallList || all > kTopNodes || all > a.cand_cap) break;
             a.small_steps = s + 1;
         }
     }

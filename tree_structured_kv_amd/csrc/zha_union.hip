@@ -725,9 +725,11 @@ __device__ __forceinline__ void expand_slice(const SearchArgs &a, int t, int p, 
     }
 }
 
-// Step t, one workgroup per walk: the head's cut (cut_head).
+// Step t, one workgroup per walk: the head's cut (cut_head), and, when the
+// level-synchronous engine takes the next step, the hand-over (to_ls_walk:
+// it needs only what this walk's cut wrote).
 template <int R>
-__global__ __launch_bounds__(kThreads) void k_un_cut(SearchArgs a, int t) {
+__global__ __launch_bounds__(kThreads) void k_un_cut(SearchArgs a, int t, int handover) {
     __shared__ SelectShared sh;
     __shared__ uint32_t s_one[kWaves], s_high[kWaves];
     __shared__ float s_sc[kLdsCand];
@@ -735,6 +737,10 @@ __global__ __launch_bounds__(kThreads) void k_un_cut(SearchArgs a, int t) {
     const int w = blockIdx.x;
     if (a.u_n[2 * (w / a.group) + (t & 1)] <= 0) return;   // the pair has finished (all its heads)
     cut_head<R>(a, t, w, sh, s_one, s_high, s_sc, s_par);
+    if (handover) {
+        __syncthreads();                           // this walk's opened positions and count are written
+        to_ls_walk<R>(a, t, w);
+    }
 }
 
 // Step t, kExpSlices workgroups per pair, after every head's cut (a kernel
@@ -987,16 +993,15 @@ __global__ __launch_bounds__(kThreads) void k_un_small(SearchArgs a, int steps) 
     }
 }
 
-// Hand-over to the level-synchronous engine after the union cut of step t:
-// one workgroup per walk writes its candidates of step t+1 -- the children
-// of the list entries it opened, in order, exactly the list that engine's
-// own cut would have written -- as that engine's candidate list, sets its
-// walk state, finishes it if nothing remains, and registers its scoring
-// tiles.
+// Hand-over to the level-synchronous engine after the union cut of step t,
+// run by walk w's cut workgroup once its cut is done: the walk's candidates
+// of step t+1 -- the children of the list entries it opened, in order,
+// exactly the list that engine's own cut would have written -- become that
+// engine's candidate list; the walk state is set (finished if nothing
+// remains) and the scoring tiles registered.
 template <int R>
-__global__ __launch_bounds__(kThreads) void k_un_to_ls(SearchArgs a, int t) {
+__device__ __forceinline__ void to_ls_walk(const SearchArgs &a, int t, int w) {
     const int tid = threadIdx.x;
-    const int w = blockIdx.x;
     const int p = w / a.group;
     const int cap = a.cand_cap, c = a.chunk, log2c = a.log2c;
     if (a.u_n[2 * p + (t & 1)] <= 0) return;      // the pair finished earlier; so did its walks
@@ -1074,14 +1079,13 @@ static hipError_t launch_union_t(const SearchArgs &a, int n0, hipStream_t st) {
                                n0);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        hipLaunchKernelGGL((k_un_cut<R>), dim3(a.pairs * a.group), dim3(kThreads), 0, st, a, t);
+        const int handover = (t + 1 == a.ls_from) ? 1 : 0;
+        hipLaunchKernelGGL((k_un_cut<R>), dim3(a.pairs * a.group), dim3(kThreads), 0, st, a, t, handover);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (t + 1 == a.ls_from) {
-            hipLaunchKernelGGL((k_un_to_ls<R>), dim3(a.walks), dim3(kThreads), 0, st, a, t);
-        } else {
+        if (!handover) {
             hipLaunchKernelGGL((k_un_expand<R>), dim3(a.pairs * kExpSlices), dim3(kThreads), 0, st, a, t);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (a.ls_from > 0)
         return launch_ls_from(a, D, R, sizeof(QT) == 2 ? ZHA_BF16 : ZHA_F32, sizeof(ST) == 2 ? ZHA_BF16 : ZHA_F32,
