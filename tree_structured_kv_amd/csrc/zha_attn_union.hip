@@ -283,7 +283,9 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
     const int64_t p = ua_pair(a, g);
     const int nchunks = static_cast<int>((a.n1 + kUaBlocks - 1) / kUaBlocks);
     const int j0 = r * a.ua_cpw, j1 = min(nchunks, j0 + a.ua_cpw);
-    const float s = a.sharpness;
+    // logits in base-2 units (s * log2(e) * <q, k>), so each weight is one
+    // hardware exp2; the partials leave in natural units
+    const float s = a.sharpness * 1.4426950408889634f;
     const int64_t tail0 = static_cast<int64_t>(c) * a.n1;
     const int tail_keys = static_cast<int>(a.n_tokens - tail0);
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -378,31 +380,35 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
             const float mn = fmaxf(m_run, tmax);
-            const float corr = (m_run > -INFINITY) ? expf(m_run - mn) : 0.f;
+            const float corr = (m_run > -INFINITY) ? __builtin_amdgcn_exp2f(m_run - mn) : 0.f;
             float pe[4], psum = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                pe[e] = (x[e] > -INFINITY) ? expf(x[e] - mn) : 0.f;
+                pe[e] = (x[e] > -INFINITY) ? __builtin_amdgcn_exp2f(x[e] - mn) : 0.f;
                 psum += pe[e];
             }
             psum += __shfl_xor(psum, 16, 64);
             psum += __shfl_xor(psum, 32, 64);
             l_run = l_run * corr + psum;
             m_run = mn;
+            // the running sums are rescaled only when some column's maximum moved
+            if (__ballot(corr != 1.f) != 0ull) {
 #pragma unroll
-            for (int q = 0; q < DT; ++q)
+                for (int q = 0; q < DT; ++q)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[q][e] *= corr;
+                    for (int e = 0; e < 4; ++e) acc[q][e] *= corr;
+            }
             // O^T += V^T P^T as bf16 16x16x16 products: the probabilities of
             // keys 4*grp .. 4*grp+3 are already this lane's B operand; each is
-            // split into two bf16 parts (hi + lo, within 2^-17 of p relative),
-            // so the fp32 sums keep fp32 accuracy while V stays exact
+            // split into two bf16 parts, hi (p truncated) and lo (the exact
+            // remainder, rounded: within 2^-16 of p relative), so the fp32
+            // sums keep fp32 accuracy while V stays exact
             short4_t ph, pl;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const bf16_t hb = f32_to_bf16(pe[e]);
-                ph[e] = static_cast<short>(hb);
-                pl[e] = static_cast<short>(f32_to_bf16(pe[e] - bf16_to_f32(hb)));
+                const uint32_t u = __float_as_uint(pe[e]);
+                ph[e] = static_cast<short>(u >> 16);
+                pl[e] = __builtin_bit_cast(short, static_cast<__bf16>(pe[e] - __uint_as_float(u & 0xffff0000u)));
             }
 #pragma unroll
             for (int q = 0; q < DT; ++q) {
@@ -474,7 +480,7 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
     }
     // merge the wavefronts' states per column
     if (grp == 0) {
-        s_m[wave][col] = m_run;
+        s_m[wave][col] = m_run * 0.6931471805599453f;   // natural units from here on
         s_l[wave][col] = l_run;
     }
 #pragma unroll
