@@ -238,8 +238,9 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
 // S^T = K Q^T (rows = keys, columns = queries), so the probabilities already
 // sit in the B-operand layout of the products O^T += V^T P^T: lane group g
 // holds keys 4g .. 4g+3 of a 16-key slice.  Those are bf16 16x16x16 products
-// too, with each probability split into two bf16 parts (hi + lo, within
-// 2^-17 relative), so the fp32 sums keep fp32 accuracy while V stays exact
+// too, with each probability split into two bf16 parts (hi: p truncated, lo:
+// the exact remainder rounded; within 2^-16 relative), so the fp32 sums keep
+// fp32 accuracy while V stays exact
 // (fp32 16x16x4 products would take 16 times the matrix-core time).  Row i of
 // output tile q is element d = DT*i + q, so a lane reads the DT consecutive
 // elements DT*col .. of each of its keys' V rows once for all tiles.
@@ -273,7 +274,9 @@ __global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
 #pragma unroll
         for (int k = 0; k < DS; ++k) qb[k] = *reinterpret_cast<const short4_t *>(qp + 16 * k);
     }
-    const float s = a.sharpness;
+    // logits in base-2 units (one hardware exp2 per weight); the partial
+    // leaves in natural units
+    const float s = a.sharpness * 1.4426950408889634f;
     float m = -INFINITY, l = 0.f;
     float4_t acc[DT];
 #pragma unroll
@@ -318,13 +321,13 @@ __global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         const float mn = fmaxf(m, tmax);
-        const float corr = (m > -INFINITY) ? expf(m - mn) : 0.f;
+        const float corr = (m > -INFINITY) ? __builtin_amdgcn_exp2f(m - mn) : 0.f;
         float psum = 0.f;
 #pragma unroll
         for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float pe = (p[sub][e] > -INFINITY) ? expf(p[sub][e] - mn) : 0.f;
+                const float pe = (p[sub][e] > -INFINITY) ? __builtin_amdgcn_exp2f(p[sub][e] - mn) : 0.f;
                 p[sub][e] = pe;
                 psum += pe;
             }
@@ -332,19 +335,22 @@ __global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
         psum += __shfl_xor(psum, 32, 64);
         l = l * corr + psum;
         m = mn;
+        // the running sums are rescaled only when some query's maximum moved
+        if (__ballot(corr != 1.f) != 0ull) {
 #pragma unroll
-        for (int i = 0; i < DT; ++i)
+            for (int i = 0; i < DT; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][e] *= corr;
+                for (int e = 0; e < 4; ++e) acc[i][e] *= corr;
+        }
         // O^T += V^T P^T
 #pragma unroll
         for (int sub = 0; sub < 4; ++sub) {
             short4_t ph, pl;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const bf16_t hb = f32_to_bf16(p[sub][e]);
-                ph[e] = static_cast<short>(hb);
-                pl[e] = static_cast<short>(f32_to_bf16(p[sub][e] - bf16_to_f32(hb)));
+                const uint32_t u = __float_as_uint(p[sub][e]);
+                ph[e] = static_cast<short>(u >> 16);
+                pl[e] = __builtin_bit_cast(short, static_cast<__bf16>(p[sub][e] - __uint_as_float(u & 0xffff0000u)));
             }
             uint32_t vw[4][VW];
 #pragma unroll
@@ -373,7 +379,7 @@ __global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) part[2 + DT * (4 * grp + e) + q] = acc[q][e];
     if (grp == 0) {
-        part[0] = m;
+        part[0] = m * 0.6931471805599453f;         // natural units
         part[1] = l;
     }
 }
