@@ -28,6 +28,14 @@ namespace {
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
+// Elements q of four 32-bit words w0..w3 (each two bf16: q = 0 low half, 1
+// high half) packed in order as a 16x16x16 operand (two v_perm_b32).
+__device__ __forceinline__ short4_t pick4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, int q) {
+    const uint32_t sel = q ? 0x07060302u : 0x05040100u;
+    const uint32_t lo = __builtin_amdgcn_perm(w1, w0, sel), hi = __builtin_amdgcn_perm(w3, w2, sel);
+    return __builtin_bit_cast(short4_t, make_uint2(lo, hi));
+}
+
 constexpr int kWaves = kBlock / 64;
 
 __device__ __forceinline__ void merge_state(float &m, float &l, float *acc, float m2, float l2,
@@ -361,10 +369,7 @@ __global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
             }
 #pragma unroll
             for (int q = 0; q < DT; ++q) {
-                short4_t va;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    va[e] = static_cast<short>((q & 1) ? (vw[e][q >> 1] >> 16) : (vw[e][q >> 1] & 0xffffu));
+                const short4_t va = pick4(vw[0][q >> 1], vw[1][q >> 1], vw[2][q >> 1], vw[3][q >> 1], q & 1);
                 acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, acc[q], 0, 0, 0);
                 acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc[q], 0, 0, 0);
             }

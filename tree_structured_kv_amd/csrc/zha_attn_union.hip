@@ -53,6 +53,14 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 constexpr int kUaWaves = 4;
 constexpr int kUaBatch = 1024;         // selected blocks gathered in LDS before their tiles run
 
+// Elements q of four 32-bit words w0..w3 (each two bf16: q = 0 low half, 1
+// high half) packed in order as a 16x16x16 operand (two v_perm_b32).
+__device__ __forceinline__ short4_t pick4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, int q) {
+    const uint32_t sel = q ? 0x07060302u : 0x05040100u;
+    const uint32_t lo = __builtin_amdgcn_perm(w1, w0, sel), hi = __builtin_amdgcn_perm(w3, w2, sel);
+    return __builtin_bit_cast(short4_t, make_uint2(lo, hi));
+}
+
 __device__ __forceinline__ short4_t pk4(uint32_t lo, uint32_t hi) {
     short4_t r;
     r[0] = static_cast<short>(lo & 0xffffu);
@@ -423,12 +431,7 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
 #pragma unroll
             for (int q = 0; q < DT; ++q) {
                 // A operand: element DT*col + q of keys 4*grp + e
-                short4_t va;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t wd = T.vw[e][q >> 1];
-                    va[e] = static_cast<short>((q & 1) ? (wd >> 16) : (wd & 0xffffu));
-                }
+                const short4_t va = pick4(T.vw[0][q >> 1], T.vw[1][q >> 1], T.vw[2][q >> 1], T.vw[3][q >> 1], q & 1);
                 acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, acc[q], 0, 0, 0);
                 acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc[q], 0, 0, 0);
             }
