@@ -103,14 +103,17 @@ enum {
  * each walk selected and give the same result up to the order of fp32 sums.
  *   ZHA_ATTN_PER_WALK: every walk reads its own selected blocks (split-K
  *     work items per walk).
- *   ZHA_ATTN_UNION: per (sequence, KV head) pair, every block any of its
- *     query heads selected is read once and attended by each head that
- *     selected it (bf16 matrix-core logits for all heads of the group, a
- *     head mask per block).  Decode (q_per_head = 1), bf16 caches,
- *     group_size <= 16.  A walk's list is taken as a set: a block listed
- *     twice counts once (zha_search never lists a block twice).
- *   ZHA_ATTN_AUTO: union for bf16 decode with 16 query heads per KV head,
- *     else per-walk. */
+ *   ZHA_ATTN_UNION: per group of walks that share a KV cache, every block
+ *     any of them selected is read once and attended by each walk that
+ *     selected it (bf16 matrix-core logits for the whole group, a walk mask
+ *     per block).  bf16 caches, chunk >= 4.  Decode (q_per_head = 1): the
+ *     group is a (sequence, KV head) pair's query heads, group_size <= 16.
+ *     Prefill blocks (q_per_head > 1): groups of 16 walks of a pair, taken
+ *     in the order of a sketch of their selections.  A walk's list is taken
+ *     as a set: a block listed twice counts once (zha_search never lists a
+ *     block twice).
+ *   ZHA_ATTN_AUTO: union for bf16 prefill blocks and for bf16 decode with 16
+ *     query heads per KV head (where it applies), else per-walk. */
 enum { ZHA_ATTN_AUTO = 0, ZHA_ATTN_PER_WALK = 1, ZHA_ATTN_UNION = 2 };
 
 /* Device status bits. */

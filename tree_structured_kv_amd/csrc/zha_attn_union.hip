@@ -357,17 +357,15 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
                 T.kb[2 * m] = pk4(v.x, v.y);
                 T.kb[2 * m + 1] = pk4(v.z, v.w);
             }
-            // the lane group's four keys kq .. kq+3: with blocks of at least
-            // four keys they are consecutive rows of one block (or of the
-            // tail), so one lookup serves all four (keys past the end reuse
-            // the first row; their weights are zero)
+            // the lane group's four keys kq .. kq+3 are consecutive rows of
+            // one block (blocks hold at least four keys) or of the tail, so
+            // one lookup serves all four (keys past the end reuse the first
+            // row; their weights are zero)
             const int kq = kbase + 4 * grp;
-            const int64_t tq = (c >= 4) ? token_of(kq < nkeys ? kq : kbase) : 0;
+            const bf16_t *vq = vc + token_of(kq < nkeys ? kq : kbase) * D + DT * col;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int kk = kq + e;
-                const int64_t tok = (c >= 4) ? tq + (kk < nkeys ? e : 0) : token_of(kk < nkeys ? kk : kbase);
-                const bf16_t *vr = vc + tok * D + DT * col;
+                const bf16_t *vr = vq + (kq + e < nkeys ? e * D : 0);
                 if constexpr (DT == 8) {
                     const gu4_t v = gload_u4(vr);
                     T.vw[e][0] = v.x; T.vw[e][1] = v.y; T.vw[e][2] = v.z; T.vw[e][3] = v.w;
@@ -385,14 +383,11 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
             // logits of column col for keys kbase + 4*grp + e; masked: -inf
             float x[4], tmax = -INFINITY;
             const int kq = kbase + 4 * grp;
-            // blocks of at least four keys: the four keys share one block's mask
-            const bool qok = hv && kq < nkeys && (tail_item || c < 4 || ((s_msk[kq >> log2c] >> col) & 1u));
+            // the four keys share one block, so one mask
+            const bool qok = hv && kq < nkeys && (tail_item || ((s_msk[kq >> log2c] >> col) & 1u));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int kk = kq + e;
-                bool ok = qok && kk < nkeys;
-                if (ok && !tail_item && c < 4) ok = (s_msk[kk >> log2c] >> col) & 1u;
-                x[e] = ok ? s * sa[e] : -INFINITY;
+                x[e] = (qok && kq + e < nkeys) ? s * sa[e] : -INFINITY;
                 tmax = fmaxf(tmax, x[e]);
             }
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));

@@ -179,6 +179,7 @@ UnionGeom union_geom(const zha_tree *t, int32_t qph) {
 
 bool union_attn_ok(const zha_tree *t, int32_t qph) {
     if (t->geom.dtype != ZHA_BF16) return false;
+    if (t->geom.chunk < 4) return false;           // a lane's four keys must share a block
     if (qph == 1 && t->geom.group_size > 16) return false;
     const UnionGeom u = union_geom(t, qph);
     return u.wpg_max <= kUaMaxItems && u.ugroups * u.wpg_max < (int64_t(1) << 31);
