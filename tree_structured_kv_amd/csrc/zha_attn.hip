@@ -38,12 +38,13 @@ __device__ __forceinline__ short4_t pick4(uint32_t w0, uint32_t w1, uint32_t w2,
 
 constexpr int kWaves = kBlock / 64;
 
+// Two online-softmax states with maxima in base-2 units.
 __device__ __forceinline__ void merge_state(float &m, float &l, float *acc, float m2, float l2,
                                             const float *acc2, int n) {
     const float mm = fmaxf(m, m2);
     if (!(mm > -INFINITY)) return;   // both empty
-    const float c1 = (m > -INFINITY) ? expf(m - mm) : 0.f;
-    const float c2 = (m2 > -INFINITY) ? expf(m2 - mm) : 0.f;
+    const float c1 = (m > -INFINITY) ? __builtin_amdgcn_exp2f(m - mm) : 0.f;
+    const float c2 = (m2 > -INFINITY) ? __builtin_amdgcn_exp2f(m2 - mm) : 0.f;
     l = l * c1 + l2 * c2;
     for (int e = 0; e < n; ++e) acc[e] = acc[e] * c1 + acc2[e] * c2;
     m = mm;
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int slot = lane / LPK, sub = lane % LPK;
     const int c = a.chunk;
-    const float s = a.sharpness;
+    const float s = a.sharpness * 1.4426950408889634f;   // base-2 logits: one hardware exp2 per weight
     const int32_t n_items = a.item_off[a.walks];
     const int ck = a.item_off[a.walks + 1];     // keys per item (at most kChunkMax)
     __shared__ float sm[kWaves], sl[kWaves], sacc[kWaves][D];
@@ -206,8 +207,8 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
                 if (!ok[u]) continue;
                 const float lg = s * d;
                 const float mn = fmaxf(m, lg);
-                const float corr = (m > -INFINITY) ? expf(m - mn) : 0.f;
-                const float pe = expf(lg - mn);
+                const float corr = (m > -INFINITY) ? __builtin_amdgcn_exp2f(m - mn) : 0.f;
+                const float pe = __builtin_amdgcn_exp2f(lg - mn);
                 l = l * corr + pe;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pe, vr[u][e], acc[e] * corr);
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
             for (int wv = 1; wv < kWaves; ++wv) merge_state(mm, ll, &av, sm[wv], sl[wv], &sacc[wv][tid], 1);
             float *part = a.part + static_cast<int64_t>(item) * (D + 2);
             part[2 + tid] = av;
-            if (tid == 0) { part[0] = mm; part[1] = ll; }
+            if (tid == 0) { part[0] = mm * 0.6931471805599453f; part[1] = ll; }   // natural units
         }
         __syncthreads();
     }
