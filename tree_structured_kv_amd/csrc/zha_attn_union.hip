@@ -171,16 +171,16 @@ __global__ __launch_bounds__(1024) void k_ua_order(AttnArgs a) {
     const int64_t base = p * wpp + l0;             // first walk of the segment
     for (int i = tid; i < N; i += 1024) s[i] = i < n ? a.ukey[base + i] : ~0ull;
     __syncthreads();
+    // each stage as N/2 compare-exchange pairs (i, i + j), i with bit j clear
     for (int k = 2; k <= N; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < N; i += 1024) {
-                const int ij = i ^ j;
-                if (ij > i) {
-                    const unsigned long long x = s[i], y = s[ij];
-                    if (((i & k) == 0) ? (x > y) : (x < y)) {
-                        s[i] = y;
-                        s[ij] = x;
-                    }
+            for (int q = tid; q < N / 2; q += 1024) {
+                const int i = ((q & ~(j - 1)) << 1) | (q & (j - 1));
+                const int ij = i + j;
+                const unsigned long long x = s[i], y = s[ij];
+                if (((i & k) == 0) ? (x > y) : (x < y)) {
+                    s[i] = y;
+                    s[ij] = x;
                 }
             }
             __syncthreads();
