@@ -59,6 +59,13 @@ __device__ __forceinline__ gu4_t gload_u4(const void *p) { return *(ZHA_GLOBAL(g
 __device__ __forceinline__ gu2_t gload_u2(const void *p) { return *(ZHA_GLOBAL(gu2_t))p; }
 __device__ __forceinline__ float gload_f(const float *p) { return *(ZHA_GLOBAL(float))p; }
 
+// Read-only data at a wavefront-uniform address, through the constant
+// address space (scalar loads into SGPRs).  Only for memory that no
+// workgroup writes while the kernel runs.
+#define ZHA_CONST(T) const __attribute__((address_space(4))) T *
+__device__ __forceinline__ float cload_f(const float *p) { return *(ZHA_CONST(float))p; }
+__device__ __forceinline__ uint32_t cload_u32(const uint32_t *p) { return *(ZHA_CONST(uint32_t))p; }
+
 // Vec4 through a global pointer.
 template <typename T> struct GVec4;
 template <> struct GVec4<float> {

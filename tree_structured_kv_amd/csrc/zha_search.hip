@@ -61,8 +61,12 @@ __device__ __forceinline__ void load_q(const SearchArgs &a, int w, float (&qv)[r
 }
 
 // One wavefront scores candidates first, first + stride, ... below `end`, kU
-// at a time, and writes sc[i]; returns the largest score it wrote.
-template <int D, int R, typename ST>
+// at a time, and writes sc[i]; returns the largest score it wrote.  The
+// candidate's R biases sit at a wavefront-uniform address and come in
+// through scalar loads (no search writes node records).  With kScalarList
+// the candidate ids do too: only where the list was written by an earlier
+// launch, since the scalar cache does not see this kernel's own stores.
+template <int D, int R, typename ST, bool kScalarList>
 __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair,
                                             const float (&qv)[row_epl<D, ST>()],
                                             const uint32_t *cur, float *sc, int first, int end,
@@ -77,22 +81,28 @@ __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair,
     float wmax = -INFINITY;
     if (first >= end) return wmax;
 
+    first = __builtin_amdgcn_readfirstlane(first);
+    end = __builtin_amdgcn_readfirstlane(end);
     uint32_t ids[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
         const int i = first + u;
-        ids[u] = cur[i < end ? i : end - 1];
+        ids[u] = kScalarList ? cload_u32(cur + (i < end ? i : end - 1)) : cur[i < end ? i : end - 1];
     }
     for (int base = first; base < end; base += stride) {
         float kv[kU][NL][EPL];
         float bv[kU][NL];
+        uint32_t cid[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const uint32_t id = ids[u];
+            const uint32_t id = __builtin_amdgcn_readfirstlane(ids[u]);   // the same for every lane
+            cid[u] = id;
             const int lvl = static_cast<int>(id >> kLevelShift);
             const int64_t node = pair * a.cap[lvl] + static_cast<int64_t>(id & kIndexMask);
             const ST *kp = reinterpret_cast<const ST *>(a.kap[lvl]) + node * (R * D);
-            const float *bp = a.bet[lvl] + node * R;
+            float bsr[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) bsr[r] = cload_f(a.bet[lvl] + node * R + r);
 #pragma unroll
             for (int l = 0; l < NL; ++l) {
                 const int r = l * RPL + rsub;
@@ -101,7 +111,12 @@ __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair,
                         Vec16<ST>::load(kp + r * D + EPL * sub, kv[u][l]);
                     else
                         Vec4<ST>::load(kp + r * D + EPL * sub, kv[u][l]);
-                    bv[u][l] = bp[r];
+                    // this lane's reference r = l*RPL + rsub, chosen among SGPRs
+                    float b = bsr[l * RPL];
+#pragma unroll
+                    for (int g = 1; g < RPL; ++g)
+                        if (rsub == g && l * RPL + g < R) b = bsr[l * RPL + g];
+                    bv[u][l] = b;
                 } else {
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) kv[u][l][e] = 0.f;
@@ -113,7 +128,7 @@ __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair,
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int i = base + stride + u;
-            ids[u] = cur[i < end ? i : end - 1];
+            ids[u] = kScalarList ? cload_u32(cur + (i < end ? i : end - 1)) : cur[i < end ? i : end - 1];
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
@@ -138,7 +153,7 @@ __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair,
                 if (lane == 0) {
                     sc[i] = m;
                     if (a.visited) {
-                        const uint32_t id = cur[i];
+                        const uint32_t id = cid[u];
                         const int64_t bit = a.node_off[id >> kLevelShift] + (id & kIndexMask);
                         atomicOr(a.visited + pair * a.vis_words + (bit >> 5), 1u << (bit & 31));
                     }
@@ -227,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void k_search_decode(SearchArgs a) {
         const bool forced = step_forced(a, t, n);
         unsigned long long tau = 0;
         if (!forced) {
-            float wmax = score_wave<D, R, ST>(a, pair, qv, cur, sc, wave * kU, n, kWaves * kU, flags);
+            float wmax = score_wave<D, R, ST, false>(a, pair, qv, cur, sc, wave * kU, n, kWaves * kU, flags);
             if (lane == 0) sh.red[wave] = wmax;
             __syncthreads();
             float mx = sh.red[0];
@@ -299,8 +314,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_ls_score(SearchArgs a, int t,
             start = (tile % tiles0) * kTile;
         } else {
             const int2 e = a.tile_map[tile];
-            w = e.x;
-            start = e.y;
+            w = __builtin_amdgcn_readfirstlane(e.x);
+            start = __builtin_amdgcn_readfirstlane(e.y);
         }
         const int n = a.state[w].n;
         const int buf = a.state[w].buf;
@@ -312,7 +327,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_ls_score(SearchArgs a, int t,
         float qv[row_epl<D, ST>()];
         load_q<D, QT, ST>(a, w, qv);
         uint32_t flags = 0;
-        (void)score_wave<D, R, ST>(a, pair, qv, cur, sc, start + wave * kU, end, kSW * kU, flags);
+        (void)score_wave<D, R, ST, true>(a, pair, qv, cur, sc, start + wave * kU, end, kSW * kU, flags);
         if (flags && lane == 0) atomicOr(a.status, flags);
     }
 }
