@@ -33,6 +33,9 @@ def _case(name):
         return replace(W[2].scaled(n=32768 + 77, batch=2), kv_heads=2, levels=5), None
     if name == "mixed-small":
         return replace(W[4].scaled(n=65536 + 3, batch=2), levels=4), None
+    if name.endswith("-b8"):    # the same shapes on eight sequences (each its own seeds)
+        w, v = _case(name[:-3] + "-small")
+        return replace(w, batch=8), v
     if name == "mha-small":     # one query head per KV head
         return replace(W[1].scaled(n=4096 + 7, batch=2), kv_heads=4, group=1, levels=3), None
     raise KeyError(name)
@@ -223,6 +226,18 @@ def test_search_and_attention(Z, name, sname, engine):
     sel, bufs, out = _run(Z, idx, Qt, Kt, Vt, select, engine=engine)
     min_stable = 0.15 if name.startswith("demo") and select["mode"] == "topp" else 0.3
     _compare(w, K, V, Q, trees, select, bufs, out, min_stable=min_stable)
+
+
+@pytest.mark.parametrize("engine", ["persistent", "level-sync", "union", "block"])
+@pytest.mark.parametrize("name", ["ar1-b8", "clustered-b8", "mixed-b8"])
+def test_search_and_attention_more_sequences(Z, name, engine):
+    """Top-p 0.9 on eight sequences per KV head: the keys, values and queries
+    of each (sequence, KV head) come from seeds of their own, so this is the
+    main parity check over four times as many independent inputs."""
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, name)
+    select = SELECTS["topp90"]
+    sel, bufs, out = _run(Z, idx, Qt, Kt, Vt, select, engine=engine)
+    _compare(w, K, V, Q, trees, select, bufs, out, min_stable=0.3)
 
 
 @pytest.mark.parametrize("sname", ["topp90", "topk4", "p0"])
