@@ -35,7 +35,7 @@
  *     Query head h uses KV head h / group.  One tree per (sequence, KV head);
  *     every query head of the group walks it separately.
  *   - Supported: head_dim 64 or 128; chunk a power of two in [2, 64];
- *     levels 1..8; num_refs in {1, 2, 4, 8, 16}; dtype float32 or bfloat16.
+ *     levels 1..12; num_refs in {1, 2, 4, 8, 16}; dtype float32 or bfloat16.
  *     Anything else returns ZHA_ERR_UNSUPPORTED.
  */
 #ifndef ZHA_H
@@ -228,7 +228,7 @@ zha_status zha_build(zha_tree *t, const void *k_cache, int64_t n_tokens, void *s
 /* The caller has written rows [n, n + n_new) of every (sequence, KV head) of
  * k_cache, n = t->n_tokens.  Summarise every chunk that these rows complete,
  * at every level, and set t->n_tokens = n + n_new ([ZHA lesson] "How is the
- * tree built?": a node is created each time a chunk fills).  The result is
+ * tree built?": a new node appears whenever a chunk has filled).  The result is
  * bit-identical to zha_build over n + n_new tokens.  ZHA_ERR_CAPACITY if
  * n + n_new > max_tokens. */
 zha_status zha_append(zha_tree *t, const void *k_cache, int64_t n_new, void *stream);

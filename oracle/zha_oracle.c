@@ -334,8 +334,8 @@ void ora_attend(int64_t n_sel, const int64_t *sel, int d, double s,
                 double *out, double *lse)
 {
     /* [ZHA lesson] "How is the tree built?" and "Common misunderstandings":
-     * ordinary softmax attention runs on exactly the original keys and
-     * values that the walk chose. */
+     * plain softmax attention over the original keys and values that the
+     * walk picked (the summaries are used for routing only). */
     for (int e = 0; e < d; ++e) out[e] = 0.0;
     if (n_sel <= 0) {
         *lse = -INFINITY;

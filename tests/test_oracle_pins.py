@@ -44,9 +44,9 @@ def _spans(tree, l):
     return [(j * span, (j + 1) * span) for j in range(tree.nodes_at(l))]
 
 
-# P1 -- "the estimate is exact at a reference" ([ZHA lesson], "What does a node
-# summarize?"): a node's score at reference rho_r equals the true log-sum-exp
-# of its subtree's keys under rho_r.
+# P1 -- [ZHA lesson] "What does a node summarize?": at one of its own
+# reference queries a node's estimate has no error, so its score at rho_r equals
+# the true log-sum-exp of its subtree's keys under rho_r.
 def test_exact_at_reference(oracle_mod):
     O = oracle_mod
     K, refs, tr = _tree(O)
@@ -59,8 +59,8 @@ def test_exact_at_reference(oracle_mod):
                 assert abs(est - true) <= 1e-12 * max(1.0, abs(true))
 
 
-# P2 -- "never exceeds the true value" (same section): tangents of a convex
-# function lie below it for every query.
+# P2 -- same section: the estimate is a lower bound of the true log-sum-exp
+# for every query (tangents of a convex function lie below it).
 def test_never_exceeds_true_value(oracle_mod):
     O = oracle_mod
     K, refs, tr = _tree(O, seed=1)
@@ -79,8 +79,8 @@ def test_never_exceeds_true_value(oracle_mod):
     assert worst < 0.5  # the bound is tight somewhere, loose nowhere absurd
 
 
-# P3 -- "merging child nodes gives the same result as summarizing the original
-# keys directly" (same section, the paper's footnote).
+# P3 -- same section (the paper's footnote): summarising the children's
+# summaries yields exactly the summary of the raw keys of the whole span.
 def test_merge_equals_direct_summary(oracle_mod):
     O = oracle_mod
     K, refs, tr = _tree(O, n=4 ** 3 * 2 + 9, seed=2)
@@ -220,9 +220,9 @@ def _direct_scores(K, refs, c, s, q, level=1):
     return np.array(out)
 
 
-# P7 -- "top-p opens the smallest group holding enough of the estimated
-# attention" ([ZHA lesson], "How does top-p differ from top-K?"): brute force
-# over all subsets of up to 12 candidates.
+# P7 -- [ZHA lesson] "How does top-p differ from top-K?": top-p takes the
+# fewest nodes whose estimated attention mass together reaches p; checked by
+# brute force over all subsets of up to 12 candidates.
 @pytest.mark.parametrize("seed", range(12))
 def test_topp_is_smallest_set(oracle_mod, seed):
     O = oracle_mod
@@ -412,3 +412,205 @@ def test_bf16_keys_tangent_exact_at_reference(oracle_mod):
     k1, _ = tr.level(1)
     e1, _ = exact.level(1)
     assert np.all(np.abs(k1 - e1) <= np.ldexp(1.0, np.floor(np.log2(np.abs(e1) + 1e-300)).astype(int) - 8))
+
+
+# ---- multi-level walks against a brute-force numpy walk --------------------
+#
+# The walk of [ZHA lesson] "Run a small tree yourself" (route) written again in
+# numpy, from scratch, over node scores taken from the direct one-level
+# summary of each node's span (pinned above to equal the recursive records):
+# at every step the whole candidate list -- the children of every node opened
+# at the step before, across all parents -- is normalised by one softmax, and
+# the cut is taken on that joint list ([ZHA lesson] "How does top-p differ
+# from top-K?": the smallest score-ordered group whose mass reaches p).
+
+def _np_roots(n, c, L):
+    nl = [n // c ** l for l in range(L + 2)]
+    roots = [(L, j) for j in range(nl[L])]
+    for l in range(L - 1, 0, -1):
+        roots += [(l, j) for j in range(c * nl[l + 1], nl[l])]
+    return sorted(roots, key=lambda x: x[1] * c ** x[0])
+
+
+def _np_walk(K, refs, c, L, s, q, p=None, k=None):
+    """Returns (selected tokens, per-step [scored, opened], per-step masses
+    in cut order with the cut m and the sorted scores) of one walk."""
+    n = K.shape[0]
+    memo = {}
+
+    def score(node):
+        if node not in memo:
+            l, j = node
+            kap, bet = _direct(K[j * c ** l:(j + 1) * c ** l], refs, s)
+            memo[node] = max(s * kap[r] @ q + bet[r] for r in range(refs.shape[0]))
+        return memo[node]
+
+    cand = _np_roots(n, c, L)
+    sel, trace, steps = [], [], []
+    t = 0
+    while cand:
+        S = np.array([score(x) for x in cand])
+        starts = np.array([j * c ** l for (l, j) in cand])
+        order = np.lexsort((starts, -S))             # score descending, then span start
+        P = np.exp(S - S.max())
+        P /= P.sum()
+        if k is not None:
+            m = min(k, len(cand))
+        elif p >= 1.0:
+            m = len(cand)
+        else:
+            cum = np.cumsum(P[order])
+            hit = np.nonzero(cum >= p)[0]
+            m = int(hit[0]) + 1 if hit.size else len(cand)
+        opened = [cand[i] for i in order[:m]]
+        trace.append([len(cand), m])
+        steps.append((S[order], P[order], m))
+        nxt = []
+        for (l, j) in opened:
+            if l == 1:
+                sel.extend(range(j * c, j * c + c))
+            else:
+                nxt.extend((l - 1, j * c + e) for e in range(c))
+        cand = sorted(nxt, key=lambda x: x[1] * c ** x[0])
+        t += 1
+    sel.extend(range(c * (n // c), n))
+    return np.array(sorted(sel), dtype=np.int64), trace, steps
+
+
+def _clustered(rng, n, d, seg, amp):
+    cent = rng.standard_normal((n // seg + 1, d))
+    cent /= np.linalg.norm(cent, axis=1, keepdims=True)
+    return amp * np.repeat(cent, seg, axis=0)[:n] + rng.standard_normal((n, d))
+
+
+# Top-p over three levels: the joint softmax across all opened parents.  A cut
+# made per parent, or a softmax over one parent's children, opens other nodes
+# at steps 2 and 3 on these walks.
+@pytest.mark.parametrize("p", [0.5, 0.9])
+@pytest.mark.parametrize("n", [4 ** 3 * 6, 4 ** 3 * 6 + 4 * 3 + 2])
+def test_multilevel_topp_walk_brute_force(oracle_mod, p, n):
+    O = oracle_mod
+    rng = np.random.default_rng(int(p * 10) + n)
+    d, c, R, L, s = 8, 4, 3, 3, 0.6
+    K = _clustered(rng, n, d, 11, 2.5)
+    refs = rng.standard_normal((R, d)) / 2
+    tr = O.build(K, refs, c, L, s)
+    multi = 0
+    for i in range(50):
+        q = 2.5 * K[rng.integers(0, n)] / max(np.linalg.norm(K[0]), 1e-9) + 0.5 * rng.standard_normal(d)
+        sel, st = O.walk(tr, q, O.TOPP, p=p)
+        want, trace, _ = _np_walk(K, refs, c, L, s, q, p=p)
+        assert np.array_equal(sel, want), i
+        assert [[a, b] for a, b in zip(st["scored"], st["opened"])] == trace, i
+        assert st["keys_read"] == len(want)
+        assert st["comparisons"] == R * sum(a for a, _ in trace) + len(want)
+        multi += sum(1 for a, b in trace[1:] if b > 1 and a > c)
+    assert multi > 20          # many steps cut a list spanning several parents
+
+
+@pytest.mark.parametrize("ks", [(3,), (2, 5, 7), (1, 4)])
+def test_multilevel_topk_walk_brute_force(oracle_mod, ks):
+    O = oracle_mod
+    rng = np.random.default_rng(sum(ks))
+    n, d, c, R, L, s = 4 ** 3 * 5 + 9, 8, 4, 3, 3, 0.6
+    K = _clustered(rng, n, d, 7, 2.0)
+    refs = rng.standard_normal((R, d)) / 2
+    tr = O.build(K, refs, c, L, s)
+    for i in range(20):
+        q = 2.0 * rng.standard_normal(d)
+        sel, st = O.walk(tr, q, O.TOPK, ksched=list(ks))
+        # K may change per step: the schedule's last entry repeats
+        want, trace = _np_walk_sched(K, refs, c, L, s, q, ks)
+        assert np.array_equal(sel, want), i
+        assert [[a, b] for a, b in zip(st["scored"], st["opened"])] == trace, i
+
+
+def _np_walk_sched(K, refs, c, L, s, q, ks):
+    """Top-K walk with a per-step K (brute force, as _np_walk)."""
+    n = K.shape[0]
+    cand = _np_roots(n, c, L)
+    sel, trace = [], []
+    t = 0
+    while cand:
+        S = np.array([max(s * kap[r] @ q + bet[r] for r in range(refs.shape[0]))
+                      for kap, bet in (_direct(K[j * c ** l:(j + 1) * c ** l], refs, s) for (l, j) in cand)])
+        starts = np.array([j * c ** l for (l, j) in cand])
+        order = np.lexsort((starts, -S))
+        m = min(ks[min(t, len(ks) - 1)], len(cand))
+        trace.append([len(cand), m])
+        nxt = []
+        for i in order[:m]:
+            l, j = cand[i]
+            if l == 1:
+                sel.extend(range(j * c, j * c + c))
+            else:
+                nxt.extend((l - 1, j * c + e) for e in range(c))
+        cand = sorted(nxt, key=lambda x: x[1] * c ** x[0])
+        t += 1
+    sel.extend(range(c * (n // c), n))
+    return np.array(sorted(sel), dtype=np.int64), trace
+
+
+# The top-p cut gap (the stability measure of the parity contract): over the
+# unforced steps, the smallest of the score drop at the cut, the overshoot
+# C_m - p and the room p - C_(m-1) before the last opened node, all from the
+# brute-force walk's independently sorted masses.
+@pytest.mark.parametrize("p", [0.3, 0.7, 0.9])
+def test_topp_gap_from_sorted_masses(oracle_mod, p):
+    O = oracle_mod
+    rng = np.random.default_rng(int(100 * p))
+    n, d, c, R, L, s = 4 ** 3 * 4 + 6, 8, 4, 3, 3, 0.6
+    K = _clustered(rng, n, d, 9, 2.0)
+    refs = rng.standard_normal((R, d)) / 2
+    tr = O.build(K, refs, c, L, s)
+    which = {"score": 0, "over": 0, "room": 0}
+    for i in range(50):
+        q = 2.0 * rng.standard_normal(d)
+        _, st = O.walk(tr, q, O.TOPP, p=p)
+        _, _, steps = _np_walk(K, refs, c, L, s, q, p=p)
+        want, arg = math.inf, None
+        for Ssorted, Psorted, m in steps:
+            if len(Ssorted) == 1:
+                continue                              # forced: one candidate
+            cum = np.cumsum(Psorted)
+            terms = {"room": p - (cum[m - 2] if m >= 2 else 0.0)}
+            if m < len(Ssorted):
+                terms["over"] = cum[m - 1] - p
+                terms["score"] = Ssorted[m - 1] - Ssorted[m]
+            k = min(terms, key=terms.get)
+            if terms[k] < want:
+                want, arg = terms[k], k
+        assert abs(st["gap"] - want) <= 1e-12, (i, st["gap"], want)
+        if arg:
+            which[arg] += 1
+    assert all(v > 0 for v in which.values()), which   # each term decides some walk
+
+
+# Attention over a strict subset of the keys ([ZHA lesson] "How is the tree
+# built?" and "Common misunderstandings": attention runs on the chosen
+# original keys only): a softmax over exactly K[sel] applied to V[sel], and
+# the dense mass those keys hold, from numpy, on random unsorted-in-memory
+# subsets far from the identity.
+def test_attend_and_mass_on_strict_subsets(oracle_mod):
+    O = oracle_mod
+    rng = np.random.default_rng(21)
+    n, d, s = 300, 10, 0.4
+    K = 2 * rng.standard_normal((n, d))
+    V = rng.standard_normal((n, d))
+    for i in range(30):
+        q = 2 * rng.standard_normal(d)
+        size = int(rng.integers(1, n // 2))
+        sel = np.sort(rng.choice(np.arange(n // 3, n), size=min(size, n - n // 3), replace=False))
+        out, lse = O.attend(sel, q, K, V, s)
+        z = s * K[sel] @ q
+        w = np.exp(z - z.max())
+        w /= w.sum()
+        assert np.max(np.abs(out - w @ V[sel])) <= 1e-12 * max(1.0, np.max(np.abs(out)))
+        assert abs(lse - logsumexp(z)) <= 1e-12 * max(1.0, abs(lse))
+        zall = s * K @ q
+        pall = np.exp(zall - zall.max())
+        pall /= pall.sum()
+        assert abs(O.mass_kept(sel, q, K, s) - pall[sel].sum()) <= 1e-12
+    assert O.mass_kept(np.array([], dtype=np.int64), q, K, s) == 0.0
+    out, lse = O.attend(np.array([], dtype=np.int64), q, K, V, s)
+    assert np.all(out == 0.0) and lse == -math.inf

@@ -2,9 +2,9 @@
 //
 // [ZHA lesson] = the page "How does a tree of summaries search a context? How
 // ZHA works".  Sections "How is the tree built?" and "Common
-// misunderstandings": the summaries only find the way; ordinary softmax
-// attention then runs on exactly the original keys and values chosen, with
-// the full cache kept.  A walk's key set is the c keys of every listed
+// misunderstandings": the summaries only steer the walk; plain softmax
+// attention is then computed over the original keys and values the walk
+// picked, and the cache itself is never reduced.  A walk's key set is the c keys of every listed
 // level-1 block plus the raw tail past the last whole chunk.
 //
 // GPU design.  Walks select very different numbers of keys under top-p, so
