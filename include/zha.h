@@ -194,8 +194,23 @@ typedef struct {
     int32_t unforced_scored;         /* candidates whose scores were computed */
     int64_t comparisons;             /* R * sum(scored) + keys_read           */
     uint32_t flags;                  /* ZHA_FLAG_* raised by this walk        */
-    uint32_t reserved;
+    uint32_t paths;                  /* ZHA_PATH_*: slower code paths taken   */
 } zha_walk_stats;
+
+/* zha_walk_stats.paths: code paths a walk's cuts took that are rare or
+ * slower, reported so that tests and profiles can tell which ran.  They
+ * never change a result.
+ *   ZHA_PATH_TIE_SELECT: a cut's value window could not be split (more than
+ *     64 candidates with equal scores around the cut, or every score -inf),
+ *     so the cut key was found by the tie-exact select over full rank keys
+ *     (score, then span start).
+ *   ZHA_PATH_LONG_LIST: a prefill-block cut (ZHA_ENGINE_BLOCK) read a list
+ *     longer than the 1,024 candidates it keeps in registers.
+ *   ZHA_PATH_LDS_SPILL: a decode cut had more candidates than it stages in
+ *     LDS and ran its passes over global memory. */
+#define ZHA_PATH_TIE_SELECT 1u
+#define ZHA_PATH_LONG_LIST 2u
+#define ZHA_PATH_LDS_SPILL 4u
 
 /* ---- sizing and set-up (host only, no device work) -------------------- */
 
@@ -205,6 +220,13 @@ typedef struct {
  * then biases float32 [batch][kv_heads][floor(max_tokens/chunk^l)][num_refs],
  * each array 256-byte aligned.  Returns 0 if `g` is invalid. */
 uint64_t zha_tree_bytes(const zha_geometry *g);
+
+/* Depth rule of the demo program ([ZHA lesson] "Run a small tree yourself":
+ * summary levels are added until the top level holds at most 64 nodes): the
+ * fewest levels L >= 1 with floor(n_tokens / chunk^L) <= max_top, at most
+ * ZHA_MAX_LEVELS.  Host only.  -1 if n_tokens < 0, chunk is not a power of
+ * two in [2, 64] or max_top < 1. */
+int32_t zha_depth_for(int64_t n_tokens, int32_t chunk, int64_t max_top);
 
 /* Fill `t` for tree memory `tree_mem` (device, >= zha_tree_bytes) and the
  * reference queries `refs` (device float32 [kv_heads][num_refs][head_dim],

@@ -279,3 +279,69 @@ def test_sweep_depth_policy_and_nested_inputs():
     seg = k1[:64]
     assert np.min(seg @ seg.mean(0)) > 0.9 * np.max(k1[64:128] @ seg.mean(0)) - 1.0
     assert S.nested_queries(5000, 64, 8).shape == (8, 64)
+
+
+def test_binding_checks_tensors_before_any_call(Z):
+    """The C ABI sees bare pointers only, so the binding checks every tensor
+    it passes (device, contiguity, dtype, element count of the layout in
+    zha.h) and raises ZhaError before the library is called.  No tensor here
+    is on a GPU, so each call must stop at the first check it reaches."""
+    import torch
+    g = _geom(Z)
+    t = Z.TreeHandle()
+    t.geom = g
+    sel = Z.make_select("topp", 0.9, max_blocks=64)
+    walks = 2 * 2 * 2
+    q = torch.zeros(2, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(Z.ZhaError) as e:
+        Z.zha_search(t, q, sel, None, None, None, None, None)
+    assert "not on the GPU" in str(e.value)
+    with pytest.raises(Z.ZhaError) as e:
+        Z.zha_build(t, torch.zeros(1, dtype=torch.bfloat16), 16)
+    assert e.value.code == 1
+    with pytest.raises(Z.ZhaError):
+        Z.zha_tree_init(g, torch.zeros(16, dtype=torch.uint8), torch.zeros(2, 4, 128))
+    # the checks themselves, on host tensors taken for device ones
+    Z_on_gpu = Z._on_gpu
+    Z._on_gpu = lambda x: True
+    try:
+        Z._need_cache(t, torch.zeros(2, 2, 4096, 128, dtype=torch.bfloat16), "k_cache")
+        for bad in (torch.zeros(2, 2, 4095, 128, dtype=torch.bfloat16),               # short cache
+                    torch.zeros(2, 2, 4096, 128, dtype=torch.float32),                # wrong dtype
+                    torch.zeros(2, 2, 128, 4096, dtype=torch.bfloat16).transpose(2, 3)):  # a view
+            with pytest.raises(Z.ZhaError) as e:
+                Z._need_cache(t, bad, "k_cache")
+            assert e.value.code == 2
+        Z._need_rows(t, torch.zeros(walks, 128, dtype=torch.bfloat16), "q", 1)
+        with pytest.raises(Z.ZhaError):
+            Z._need_rows(t, torch.zeros(walks, 128, dtype=torch.bfloat16), "q", 4)
+        with pytest.raises(Z.ZhaError):
+            Z._need_lists(t, sel, torch.zeros(walks * 63, dtype=torch.int32),
+                          torch.zeros(walks, dtype=torch.int32), 1)
+        with pytest.raises(Z.ZhaError):
+            Z._need_lists(t, sel, torch.zeros(walks * 64, dtype=torch.int64),
+                          torch.zeros(walks, dtype=torch.int32), 1)
+        Z._need_lists(t, sel, torch.zeros(walks * 64, dtype=torch.int32), torch.zeros(walks, dtype=torch.int32), 1)
+    finally:
+        Z._on_gpu = Z_on_gpu
+
+
+def test_depth_rule(Z):
+    """[ZHA lesson] "Run a small tree yourself": levels are added until at most
+    64 nodes remain on top (demo geometry: 4,096 keys, chunk 4, 3 levels, 64
+    top nodes)."""
+    assert Z.zha_depth_for(4096, 4, 64) == 3
+    assert Z.zha_depth_for(4097, 4, 64) == 3
+    assert Z.zha_depth_for(4096 * 4 + 3, 4, 64) == 4
+    assert Z.zha_depth_for(1 << 20, 4, 64) == 7
+    assert Z.zha_depth_for(1 << 22, 4, 64) == 8
+    assert Z.zha_depth_for(1 << 24, 4, 64) == 9
+    assert Z.zha_depth_for(65536, 16, 1) == 4
+    assert Z.zha_depth_for(10, 4, 64) == 1
+    assert Z.zha_depth_for(0, 4, 64) == 1
+    assert Z.zha_depth_for(1 << 30, 2, 1) == 12         # capped at ZHA_MAX_LEVELS
+    for bad in ((-1, 4, 64), (100, 3, 64), (100, 128, 64), (100, 4, 0)):
+        assert Z.zha_depth_for(*bad) == -1
+    for n in (1, 63, 64, 65, 4095, 300000, 5 << 20):
+        L = Z.zha_depth_for(n, 4, 64)
+        assert n // 4 ** L <= 64 and (L == 1 or n // 4 ** (L - 1) > 64)

@@ -151,12 +151,23 @@ def test_build_equals_appends(Z, name):
         done += m
     assert other.n_tokens == w.n
     torch.cuda.synchronize()
+    worst = 0.0
     for l in range(1, w.levels + 1):
         a_k, a_b = idx.level(l)
         b_k, b_b = other.level(l)
         live = w.n // w.chunk ** l
         assert torch.equal(a_k[:, :, :live], b_k[:, :, :live]), l
         assert torch.equal(a_b[:, :, :live], b_b[:, :, :live]), l
+        # the appended tree against the oracle directly, not only the build
+        nk, nb = b_k.cpu().numpy(), b_b.cpu().numpy()
+        for (b, g), tr in trees.items():
+            ok, ob = tr.level(l)
+            if ok.shape[0] == 0:
+                continue
+            ek = np.max(np.abs(nk[b, g, :ok.shape[0]] - ok), axis=(1, 2)) / np.maximum(1.0, np.max(np.abs(ok), axis=(1, 2)))
+            eb = np.max(np.abs(nb[b, g, :ok.shape[0]] - ob), axis=1) / np.maximum(1.0, np.max(np.abs(ob), axis=1))
+            worst = max(worst, float(ek.max()), float(eb.max()))
+    assert worst <= P.TOL_TREE, worst
 
 
 SELECTS = {
@@ -180,6 +191,25 @@ def _run(Z, idx, Qt, Kt, Vt, select, max_blocks=None, max_candidates=0, engine="
     return sel, bufs, out
 
 
+def _check_walk(tree, q, select, gpu_blocks, toks, st, sel_o, st_o, where, full_stats=True):
+    """Every walk is checked.  Where the oracle's cut gap exceeds GAP the
+    GPU's selection and counts must equal the oracle's bit-exactly (returns
+    1); otherwise the GPU's walk must be a sequence of valid cuts under the
+    fp64 scores within VALID_TOL (tests/parity.py, check_walk_valid;
+    returns 0)."""
+    if st_o["gap"] > P.GAP:
+        assert np.array_equal(toks, sel_o), where
+        assert st["scored"] == st_o["scored"] and st["opened"] == st_o["opened"], where
+        assert st["comparisons"] == st_o["comparisons"], where
+        assert st["keys_read"] == st_o["keys_read"], where
+        if full_stats:
+            assert st["unforced_scored"] == st_o["unforced_scored"], where
+        return 1
+    ok, why = P.check_walk_valid(tree, q, select, np.asarray(gpu_blocks), st)
+    assert ok, (where, why)
+    return 0
+
+
 def _compare(w, K, V, Q, trees, select, bufs, out, min_stable=0.3):
     blocks = bufs["sel_blocks"].cpu().numpy()
     count = bufs["sel_count"].cpu().numpy()
@@ -199,13 +229,8 @@ def _compare(w, K, V, Q, trees, select, bufs, out, min_stable=0.3):
             toks = P.gpu_tokens(blocks[wi], count[wi], w.chunk, w.n)
             st = stats[wi]
             walks += 1
-            if st_o["gap"] > P.GAP:
-                stable += 1
-                assert np.array_equal(toks, sel_o), (b, h)
-                assert st["scored"] == st_o["scored"] and st["opened"] == st_o["opened"], (b, h)
-                assert st["comparisons"] == st_o["comparisons"]
-                assert st["keys_read"] == st_o["keys_read"]
-                assert st["unforced_scored"] == st_o["unforced_scored"]
+            stable += _check_walk(trees[(b, g)], q, select, blocks[wi, :count[wi]], toks, st, sel_o, st_o,
+                                  (b, h))
             ref, _ = O.attend(toks, q.astype(np.float64), K[b, g].astype(np.float64),
                               V[b, g].astype(np.float64), w.sharpness)
             ok, e = P.out_ok(outs[b, h], ref, w.dtype)
@@ -541,11 +566,8 @@ def test_prefill_block(Z, sname, engine):
             sel_o, st_o = P.oracle_walk(trees[(0, g)], q, select)
             toks = P.gpu_tokens(blocks[wi], count[wi], w.chunk, T0)
             walks += 1
-            if st_o["gap"] > P.GAP:
-                stable += 1
-                assert np.array_equal(toks, sel_o), (h, t)
-                assert stats[wi]["scored"] == st_o["scored"], (h, t)
-                assert stats[wi]["comparisons"] == st_o["comparisons"]
+            stable += _check_walk(trees[(0, g)], q, select, blocks[wi, :count[wi]], toks, stats[wi], sel_o,
+                                  st_o, (h, t))
             keys = np.concatenate([toks, np.arange(T0, T0 + t + 1)])
             ref, _ = O.attend(keys, q.astype(np.float64), K[0, g].astype(np.float64),
                               V[0, g].astype(np.float64), w.sharpness)
@@ -707,10 +729,7 @@ def test_short_caches(Z, n_tok, engine):
             q = Q[0, h]
             sel_o, st_o = P.oracle_walk(tr, q, select)
             toks = P.gpu_tokens(blocks[h], count[h], w.chunk, n_tok)
-            if st_o["gap"] > P.GAP:
-                assert np.array_equal(toks, sel_o), (h, toks, sel_o)
-                assert stats[h]["comparisons"] == st_o["comparisons"]
-                assert stats[h]["keys_read"] == st_o["keys_read"] == len(sel_o)
+            _check_walk(tr, q, select, blocks[h, :count[h]], toks, stats[h], sel_o, st_o, (h, n_tok))
             ref, _ = O.attend(toks, q.astype(np.float64), K[0, g].astype(np.float64),
                               V[0, g].astype(np.float64), w.sharpness)
             if n_tok == 0:
@@ -720,11 +739,12 @@ def test_short_caches(Z, n_tok, engine):
 
 # ---- full sizes: the bench's geometries and launch configuration, sampled walks ----
 
-@pytest.mark.parametrize("wid,select", [(2, dict(mode="topp", p=0.9)), (2, dict(mode="topk", k=(64,))),
+@pytest.mark.parametrize("wid,select", [(1, dict(mode="topp", p=0.9)),
+                                        (2, dict(mode="topp", p=0.9)), (2, dict(mode="topk", k=(64,))),
                                         (4, dict(mode="topp", p=0.9))])
 def test_full_size_sampled(Z, wid, select):
-    """The decode workloads at full size (262,144 and 1,048,576 keys, every
-    sequence and KV head, AUTO engine as the bench runs it): the walks of two
+    """The decode workloads at full size (65,536, 262,144 and 1,048,576 keys,
+    every sequence and KV head, AUTO engine as the bench runs it): the walks of two
     sampled (sequence, KV head) pairs against the oracle walk on that pair's
     fp64 tree, and their outputs against oracle attention.  Other pairs hold
     copies of the sampled pairs' data, so the launch shapes are the real ones."""
@@ -775,13 +795,13 @@ def test_full_size_sampled(Z, wid, select):
             sel_o, st_o = P.oracle_walk(tr, q[hh], select)
             toks = P.gpu_tokens(blocks[wi], count[wi], w.chunk, w.n)
             walks += 1
-            if st_o["gap"] > P.GAP:
-                stable += 1
-                assert np.array_equal(toks, sel_o), (b, h)
-                assert stats[wi]["comparisons"] == st_o["comparisons"], (b, h)
+            stable += _check_walk(tr, q[hh], select, blocks[wi, :count[wi]], toks, stats[wi], sel_o, st_o,
+                                  (b, h))
             ref, _ = O.attend(toks, q[hh].astype(np.float64), k.astype(np.float64), v.astype(np.float64),
                               w.sharpness)
             assert P.out_ok(outs[b, h], ref, w.dtype)[0], (b, h)
     # at 1M a third of the heads target 1 segment; those targeting 8 or 64
-    # segments see near-flat scores whose cut gaps fall under 1e-4
-    assert stable >= (0.25 if wid == 4 else 0.5) * walks, (stable, walks)
+    # segments see near-flat scores whose cut gaps fall under 1e-4 (those
+    # walks are checked for validity instead); AR(1) keys are smooth, so
+    # neighbouring nodes score alike and many cuts are close too
+    assert stable >= (0.25 if wid in (1, 4) else 0.5) * walks, (stable, walks)

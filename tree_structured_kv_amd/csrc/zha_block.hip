@@ -375,6 +375,7 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
 
     const bool forced = step_forced(a, t, n);
     unsigned long long tau = 0;
+    uint32_t path = staged ? 0u : kPathLongList;
     if (!forced) {
         const bool by_mass = (a.mode == ZHA_TOPP) && (a.p > 0.f);
         float mx = -INFINITY;
@@ -512,6 +513,7 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
         if (!exact_done) {
             // every score -inf, or a window that cannot be split: sort-free
             // fallback over full keys, one candidate at a time (rare)
+            path |= kPathTieSelect;
             unsigned long long need = 1;
             const bool by_mass2 = (a.mode == ZHA_TOPP) && (a.p > 0.f) && (mx > -INFINITY);
             unsigned long long z = 0;
@@ -577,6 +579,7 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
     if (nn > cap) { st.flags |= ZHA_FLAG_CAND_OVERFLOW; nn = cap; }
     st.scored[t] = n;
     st.opened[t] = static_cast<int32_t>(nopen);
+    st.flags |= path;
     if (!forced) st.unforced += n;
     st.sel_n += static_cast<int32_t>(n1);
     st.steps = t + 1;

@@ -515,6 +515,13 @@ uint64_t zha_tree_bytes(const zha_geometry *g) {
     return off;
 }
 
+int32_t zha_depth_for(int64_t n_tokens, int32_t chunk, int64_t max_top) {
+    if (n_tokens < 0 || chunk < 2 || chunk > 64 || (chunk & (chunk - 1)) || max_top < 1) return -1;
+    int32_t L = 1;
+    while (L < ZHA_MAX_LEVELS && level_count(n_tokens, chunk, L) > max_top) ++L;
+    return L;
+}
+
 zha_status zha_tree_init(zha_tree *t, const zha_geometry *g, void *tree_mem, uint64_t tree_bytes,
                          const float *refs) {
     if (!t) return ZHA_ERR_ARG;

@@ -26,6 +26,15 @@ constexpr int kUaSlice = 16384;      // union attention: level-1 blocks per mask
 constexpr int kUaSortMax = 16384;    // union attention, prefill: walks sorted together (one workgroup)
 constexpr int kXcds = 8;             // MI355X: accelerator dies (XCDs), each with its own L2
 
+// Which slower or rarer code paths a walk took (bits 16.. of the flags a walk
+// carries through the engines; finish_walk moves them to zha_walk_stats.paths
+// as ZHA_PATH_*, and only the low bits reach the status word).
+constexpr uint32_t kPathShift = 16;
+constexpr uint32_t kPathTieSelect = 1u << kPathShift;   // ZHA_PATH_TIE_SELECT
+constexpr uint32_t kPathLongList = 2u << kPathShift;    // ZHA_PATH_LONG_LIST
+constexpr uint32_t kPathLdsSpill = 4u << kPathShift;    // ZHA_PATH_LDS_SPILL
+constexpr uint32_t kFlagBits = (1u << kPathShift) - 1u;
+
 // Workgroups go to the XCDs in turn (workgroup i to XCD i mod kXcds).  With
 // a grid of xcd_grid(n) workgroups, workgroup i takes item xcd_item(i, n)
 // (nothing when that is -1): runs of consecutive items share one XCD and its

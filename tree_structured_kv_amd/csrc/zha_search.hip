@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void k_search_decode(SearchArgs a) {
             float mx = sh.red[0];
 #pragma unroll
             for (int i = 1; i < kWaves; ++i) mx = fmaxf(mx, sh.red[i]);
-            tau = cut_tau_win(a, n, cur, sc, mx, a.k[t], sh);
+            tau = cut_tau_win(a, n, cur, sc, mx, a.k[t], sh, &flags);
             unforced += n;
         }
         uint32_t ta, tb;
@@ -388,9 +388,10 @@ __global__ __launch_bounds__(kThreads) void k_ls_cut(SearchArgs a, int t) {
     const uint32_t *cid = staged ? s_id : cur;
     const float *csc = staged ? s_sc : sc;
     unsigned long long tau = 0;
+    uint32_t path = (staged || forced) ? 0u : kPathLdsSpill;
     if (!forced) {
         const float mx = block_max(m, sh);        // also a barrier: the staged entries are complete
-        tau = cut_tau_win(a, n, cid, csc, mx, a.k[t], sh);
+        tau = cut_tau_win(a, n, cid, csc, mx, a.k[t], sh, &path);
     } else {
         __syncthreads();
     }
@@ -400,6 +401,7 @@ __global__ __launch_bounds__(kThreads) void k_ls_cut(SearchArgs a, int t) {
     if (tid == 0) {
         int64_t nn = static_cast<int64_t>(tb) * a.chunk;
         if (nn > cap) { st.flags |= ZHA_FLAG_CAND_OVERFLOW; nn = cap; }
+        st.flags |= path;
         st.scored[t] = n;
         st.opened[t] = static_cast<int32_t>(ta + tb);
         if (!forced) st.unforced += n;

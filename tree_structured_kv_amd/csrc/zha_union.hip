@@ -444,10 +444,11 @@ __device__ __forceinline__ void cut_head(const SearchArgs &a, int t, int w, Sele
     }
     __syncthreads();
     unsigned long long tau = 0;
+    uint32_t path = (sc_lds || forced) ? 0u : kPathLdsSpill;
     if (!forced) {
         const float mx = block_max(m, sh);
-        tau = sc_lds ? cut_tau_win(a, cnt, cid, lds_sc, mx, a.k[t], sh)
-                     : cut_tau_win(a, cnt, cid, csc, mx, a.k[t], sh);
+        tau = sc_lds ? cut_tau_win(a, cnt, cid, lds_sc, mx, a.k[t], sh, &path)
+                     : cut_tau_win(a, cnt, cid, csc, mx, a.k[t], sh, &path);
     }
 
     // open, in candidate order: wavefront v owns segment v (64*kScanU a round)
@@ -519,6 +520,7 @@ __device__ __forceinline__ void cut_head(const SearchArgs &a, int t, int w, Sele
     if (tid == 0) {
         st->scored[t] = cnt;
         st->opened[t] = static_cast<int32_t>(tot_open);
+        st->flags |= path;
         if (!forced) st->unforced += cnt;
         st->sel_n = static_cast<int32_t>(sel0 + tot1);
         st->steps = t + 1;

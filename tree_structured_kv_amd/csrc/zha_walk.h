@@ -53,7 +53,7 @@ __device__ __forceinline__ void finish_walk(const SearchArgs &a, int w, int step
                             const int32_t *opened, int64_t sel_n, int32_t unforced, uint32_t fl) {
     if (sel_n > a.sel_cap) fl |= ZHA_FLAG_SEL_OVERFLOW;
     a.sel_count[w] = static_cast<int32_t>(sel_n < a.sel_cap ? sel_n : a.sel_cap);
-    if (fl) atomicOr(a.status, fl);
+    if (fl & kFlagBits) atomicOr(a.status, fl & kFlagBits);
     if (a.stats) {
         zha_walk_stats st;
         int64_t tot_scored = 0;
@@ -68,8 +68,8 @@ __device__ __forceinline__ void finish_walk(const SearchArgs &a, int w, int step
         st.blocks = static_cast<int32_t>(sel_n);
         st.unforced_scored = unforced;
         st.comparisons = tot_scored * R + st.keys_read;
-        st.flags = fl;
-        st.reserved = 0;
+        st.flags = fl & kFlagBits;
+        st.paths = fl >> kPathShift;
         a.stats[w] = st;
     }
 }
@@ -278,12 +278,17 @@ __device__ __forceinline__ int win_bin(float v, float top, float scale) {
 // ranked by their full keys.  Weights are the integer masses of cut_tau (or
 // counts), so the crossing is the same candidate.  Scores spread over the
 // bins, so the shared-memory histogram sees little contention.  Falls back
-// to cut_tau when every score is -inf or a window cannot be split (ties).
+// to cut_tau when every score is -inf or a window cannot be split (ties);
+// that fallback ORs kPathTieSelect into *path (every thread's copy).
 __device__ __forceinline__ unsigned long long cut_tau_win(const SearchArgs &a, int n, const uint32_t *cur,
-                                                          const float *sc, float mx, int kt, SelectShared &sh) {
+                                                          const float *sc, float mx, int kt, SelectShared &sh,
+                                                          uint32_t *path = nullptr) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int log2c = a.log2c;
-    if (!(mx > -INFINITY)) return cut_tau(a, n, cur, sc, mx, kt, sh);
+    if (!(mx > -INFINITY)) {
+        if (path) *path |= kPathTieSelect;
+        return cut_tau(a, n, cur, sc, mx, kt, sh);
+    }
     const bool by_mass = (a.mode == ZHA_TOPP) && (a.p > 0.f);
     // total weight and the lowest finite score
     unsigned long long zpart = 0;
@@ -395,7 +400,10 @@ __device__ __forceinline__ unsigned long long cut_tau_win(const SearchArgs &a, i
         top = fminf(nt, top);
         bot = fmaxf(nb, bot);
     }
-    if (!done) return cut_tau(a, n, cur, sc, mx, kt, sh);
+    if (!done) {
+        if (path) *path |= kPathTieSelect;
+        return cut_tau(a, n, cur, sc, mx, kt, sh);
+    }
 
     // the final bin's candidates, ranked by key
     if (tid == 0) sh.nf = 0;

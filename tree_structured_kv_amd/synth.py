@@ -319,3 +319,42 @@ def nested_refs(r, d, seed=0):
     """float32 [r][d] reference queries N(0, 1)/sqrt(d) of the length sweep."""
     rng = np.random.default_rng(np.random.SeedSequence([ROOT_SEED, 100, seed, S_NEST_REFS]))
     return (rng.standard_normal((r, d)) / math.sqrt(d)).astype(np.float32)
+
+
+def nested_values(n, d, seed=0):
+    """float32 [n][d] values N(0, 1) for the length sweep's keys."""
+    rng = np.random.default_rng(np.random.SeedSequence([ROOT_SEED, 100, seed, 13]))
+    out = np.empty((n, d), np.float32)
+    sl = 1 << 20
+    for a in range(0, n, sl):
+        b = min(n, a + sl)
+        out[a:b] = rng.standard_normal((b - a, d), dtype=np.float32)
+    return out
+
+
+# ---- constructed caches for particular code paths -----------------------------
+#
+# Stream ids 20.. keep these draws apart from everything above.
+
+S_TIED, S_FLATQ = 20, 21
+
+
+def repeated_chunk_pair(w: Workload, g: int, seed: int = 0):
+    """One (sequence, KV head) pair whose cache is a single chunk of w.chunk
+    random keys repeated end to end (every node of a level then holds the
+    same summary, so every score of a step ties), random values, and G
+    random queries N(0, 4).  float32 arrays, bf16-exact for bf16 workloads:
+    K, V [n][d], Q [G][d]."""
+    rng = np.random.default_rng(np.random.SeedSequence([ROOT_SEED, 200, seed, g, S_TIED]))
+    pat = _cast(w, rng.standard_normal((w.chunk, w.d)).astype(np.float32))
+    K = np.tile(pat, (w.n // w.chunk + 1, 1))[: w.n]
+    V = _cast(w, rng.standard_normal((w.n, w.d)).astype(np.float32))
+    Q = _cast(w, (2.0 * rng.standard_normal((w.group, w.d))).astype(np.float32))
+    return np.ascontiguousarray(K), V, Q
+
+
+def small_queries(w: Workload, count: int, scale: float, seed: int = 0) -> np.ndarray:
+    """float32 [count][d] queries N(0, scale^2) (bf16-exact for bf16): with a
+    small scale every node scores about the same."""
+    rng = np.random.default_rng(np.random.SeedSequence([ROOT_SEED, 200, seed, S_FLATQ]))
+    return _cast(w, (scale * rng.standard_normal((count, w.d))).astype(np.float32))

@@ -21,6 +21,7 @@ MAX_STEPS = 12
 TOPP, TOPK = 0, 1
 F32, BF16 = 0, 1
 FLAG_CAND_OVERFLOW, FLAG_SEL_OVERFLOW, FLAG_NONFINITE = 1, 2, 4
+PATH_TIE_SELECT, PATH_LONG_LIST, PATH_LDS_SPILL = 1, 2, 4
 ENGINE_AUTO, ENGINE_PERSISTENT, ENGINE_LEVEL_SYNC, ENGINE_UNION, ENGINE_BLOCK = 0, 1, 2, 3, 4
 ENGINES = {"auto": ENGINE_AUTO, "persistent": ENGINE_PERSISTENT, "level-sync": ENGINE_LEVEL_SYNC,
            "union": ENGINE_UNION, "block": ENGINE_BLOCK}
@@ -62,12 +63,12 @@ class WalkStats(ctypes.Structure):
                 ("steps", ctypes.c_int32), ("keys_read", ctypes.c_int32),
                 ("blocks", ctypes.c_int32), ("unforced_scored", ctypes.c_int32),
                 ("comparisons", ctypes.c_int64), ("flags", ctypes.c_uint32),
-                ("reserved", ctypes.c_uint32)]
+                ("paths", ctypes.c_uint32)]
 
 
 STATS_WORDS = ctypes.sizeof(WalkStats) // 4   # int32 words per stats record
 
-EXPORTS = ["zha_tree_bytes", "zha_tree_init", "zha_build", "zha_append",
+EXPORTS = ["zha_tree_bytes", "zha_depth_for", "zha_tree_init", "zha_build", "zha_append",
            "zha_search_workspace_bytes", "zha_search_engine", "zha_search", "zha_visited_words", "zha_attn_workspace_bytes", "zha_attn_engine",
            "zha_sparse_attn", "zha_forward_workspace_bytes", "zha_forward",
            "zha_dense_workspace_bytes", "zha_dense_topk_attn", "zha_bw_probe",
@@ -83,6 +84,7 @@ def _load():
     gp, sp, tp = ctypes.POINTER(Geometry), ctypes.POINTER(Select), ctypes.POINTER(TreeHandle)
     sig = {
         "zha_tree_bytes": (u64, [gp]),
+        "zha_depth_for": (i32, [i64, i32, i64]),
         "zha_tree_init": (i32, [tp, gp, vp, u64, vp]),
         "zha_build": (i32, [tp, vp, i64, vp]),
         "zha_append": (i32, [tp, vp, i64, vp]),
@@ -129,6 +131,60 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
+# The C ABI takes bare pointers and cannot see how large a buffer is, so the
+# binding checks every tensor it passes: on the GPU, contiguous, of the dtype
+# and element count the layout in include/zha.h fixes (ZhaError otherwise,
+# before anything is enqueued).  Raw integer pointers are passed unchecked.
+_ERR_ARG, _ERR_SHAPE = 1, 2
+
+
+def _on_gpu(t) -> bool:
+    return t.device.type == "cuda"
+
+
+def _need(t, name, dtype=None, numel=None, min_numel=None, min_bytes=None):
+    if t is None or isinstance(t, int):
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ZhaError(_ERR_ARG, f"{name}: expected a torch tensor or a device pointer")
+    if not _on_gpu(t):
+        raise ZhaError(_ERR_ARG, f"{name}: tensor is on {t.device}, not on the GPU")
+    if not t.is_contiguous():
+        raise ZhaError(_ERR_SHAPE, f"{name}: tensor is not contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ZhaError(_ERR_SHAPE, f"{name}: dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ZhaError(_ERR_SHAPE, f"{name}: {t.numel()} elements, expected {numel}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ZhaError(_ERR_SHAPE, f"{name}: {t.numel()} elements, expected at least {min_numel}")
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ZhaError(_ERR_SHAPE, f"{name}: {t.numel() * t.element_size()} bytes, expected at least {min_bytes}")
+
+
+def _geom_of(t):
+    g = t.geom
+    dt = torch.bfloat16 if g.dtype == BF16 else torch.float32
+    walks = g.batch * g.num_kv_heads * g.group_size
+    return g, dt, walks
+
+
+def _need_cache(t, k_cache, name):
+    g, dt, _ = _geom_of(t)
+    _need(k_cache, name, dt, numel=g.batch * g.num_kv_heads * g.max_tokens * g.head_dim)
+
+
+def _need_rows(t, x, name, q_per_head):
+    g, dt, walks = _geom_of(t)
+    _need(x, name, dt, numel=walks * q_per_head * g.head_dim)
+
+
+def _need_lists(t, sel, sel_blocks, sel_count, q_per_head):
+    _, _, walks = _geom_of(t)
+    W = walks * q_per_head
+    _need(sel_blocks, "sel_blocks", torch.int32, min_numel=W * sel.max_blocks_per_walk)
+    _need(sel_count, "sel_count", torch.int32, min_numel=W)
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -167,7 +223,13 @@ def zha_tree_bytes(geom: Geometry) -> int:
     return int(lib.zha_tree_bytes(ctypes.byref(geom)))
 
 
+def zha_depth_for(n_tokens: int, chunk: int, max_top: int = 64) -> int:
+    return int(lib.zha_depth_for(int(n_tokens), int(chunk), int(max_top)))
+
+
 def zha_tree_init(geom: Geometry, tree_mem, refs) -> TreeHandle:
+    _need(tree_mem, "tree_mem", min_bytes=zha_tree_bytes(geom))
+    _need(refs, "refs", torch.float32, numel=geom.num_kv_heads * geom.num_refs * geom.head_dim)
     t = TreeHandle()
     nbytes = tree_mem.numel() * tree_mem.element_size()
     _check(lib.zha_tree_init(ctypes.byref(t), ctypes.byref(geom), _ptr(tree_mem), nbytes, _ptr(refs)),
@@ -176,10 +238,12 @@ def zha_tree_init(geom: Geometry, tree_mem, refs) -> TreeHandle:
 
 
 def zha_build(t: TreeHandle, k_cache, n_tokens: int, stream=None):
+    _need_cache(t, k_cache, "k_cache")
     _check(lib.zha_build(ctypes.byref(t), _ptr(k_cache), int(n_tokens), _stream(stream)), "zha_build")
 
 
 def zha_append(t: TreeHandle, k_cache, n_new: int, stream=None):
+    _need_cache(t, k_cache, "k_cache")
     _check(lib.zha_append(ctypes.byref(t), _ptr(k_cache), int(n_new), _stream(stream)), "zha_append")
 
 
@@ -201,6 +265,13 @@ def zha_attn_engine(t: TreeHandle, sel: Select, q_per_head: int = 1) -> str | No
 
 def zha_search(t: TreeHandle, q, sel: Select, sel_blocks, sel_count, stats, status, ws,
                q_per_head: int = 1, stream=None, visited=None):
+    _need_rows(t, q, "q", q_per_head)
+    _need_lists(t, sel, sel_blocks, sel_count, q_per_head)
+    W = _geom_of(t)[2] * q_per_head
+    _need(stats, "stats", min_bytes=W * ctypes.sizeof(WalkStats))
+    _need(status, "status", min_bytes=4)
+    _need(visited, "visited", min_bytes=4 * zha_visited_words(t))
+    _need(ws, "ws")
     wsb = ws.numel() * ws.element_size()
     _check(lib.zha_search(ctypes.byref(t), _ptr(q), q_per_head, ctypes.byref(sel), _ptr(sel_blocks),
                           _ptr(sel_count), _ptr(stats), _ptr(status), _ptr(visited), _ptr(ws), wsb,
@@ -218,6 +289,12 @@ def zha_attn_workspace_bytes(t: TreeHandle, sel: Select, q_per_head: int = 1) ->
 
 def zha_sparse_attn(t: TreeHandle, q, k_cache, v_cache, sel: Select, sel_blocks, sel_count, out, ws,
                     q_per_head: int = 1, stream=None):
+    _need_rows(t, q, "q", q_per_head)
+    _need_rows(t, out, "out", q_per_head)
+    _need_cache(t, k_cache, "k_cache")
+    _need_cache(t, v_cache, "v_cache")
+    _need_lists(t, sel, sel_blocks, sel_count, q_per_head)
+    _need(ws, "ws")
     wsb = ws.numel() * ws.element_size()
     _check(lib.zha_sparse_attn(ctypes.byref(t), _ptr(q), q_per_head, _ptr(k_cache), _ptr(v_cache),
                                ctypes.byref(sel), _ptr(sel_blocks), _ptr(sel_count), _ptr(out),
@@ -231,6 +308,13 @@ def zha_forward_workspace_bytes(t: TreeHandle, sel: Select, q_per_head: int = 1)
 
 def zha_forward(t: TreeHandle, n_new: int, q, k_cache, v_cache, sel: Select, out, stats, status, ws,
                 q_per_head: int = 1, stream=None):
+    _need_rows(t, q, "q", q_per_head)
+    _need_rows(t, out, "out", q_per_head)
+    _need_cache(t, k_cache, "k_cache")
+    _need_cache(t, v_cache, "v_cache")
+    _need(stats, "stats", min_bytes=_geom_of(t)[2] * q_per_head * ctypes.sizeof(WalkStats))
+    _need(status, "status", min_bytes=4)
+    _need(ws, "ws")
     wsb = ws.numel() * ws.element_size()
     _check(lib.zha_forward(ctypes.byref(t), int(n_new), _ptr(q), q_per_head, _ptr(k_cache),
                            _ptr(v_cache), ctypes.byref(sel), _ptr(out), _ptr(stats), _ptr(status),
@@ -244,6 +328,14 @@ def zha_dense_workspace_bytes(t: TreeHandle, max_budget: int) -> int:
 
 def zha_dense_topk_attn(t: TreeHandle, q, k_cache, v_cache, budget, max_budget: int, out, ws,
                         sel_tokens=None, stream=None):
+    walks = _geom_of(t)[2]
+    _need_rows(t, q, "q", 1)
+    _need_rows(t, out, "out", 1)
+    _need_cache(t, k_cache, "k_cache")
+    _need_cache(t, v_cache, "v_cache")
+    _need(budget, "budget", torch.int32, min_numel=walks)
+    _need(sel_tokens, "sel_tokens", torch.int32, min_numel=walks * int(max_budget))
+    _need(ws, "ws")
     wsb = ws.numel() * ws.element_size()
     _check(lib.zha_dense_topk_attn(ctypes.byref(t), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                    _ptr(budget), int(max_budget), _ptr(out), _ptr(sel_tokens),
@@ -252,6 +344,8 @@ def zha_dense_topk_attn(t: TreeHandle, q, k_cache, v_cache, budget, max_budget: 
 
 
 def zha_bw_probe(buf, sink, stream=None):
+    _need(buf, "buf")
+    _need(sink, "sink", torch.float32, min_numel=1)
     nbytes = buf.numel() * buf.element_size()
     _check(lib.zha_bw_probe(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "zha_bw_probe")
 
@@ -272,7 +366,7 @@ def stats_to_dicts(stats_words: torch.Tensor):
         out.append(dict(steps=steps, scored=list(st.scored)[:steps], opened=list(st.opened)[:steps],
                         keys_read=st.keys_read, blocks=st.blocks,
                         unforced_scored=st.unforced_scored, comparisons=st.comparisons,
-                        flags=st.flags))
+                        flags=st.flags, paths=st.paths))
     return out
 
 
