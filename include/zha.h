@@ -328,6 +328,37 @@ zha_status zha_sparse_attn(const zha_tree *t, const void *q, int32_t q_per_head,
                            const int32_t *sel_count, void *out,
                            void *ws, uint64_t ws_bytes, void *stream);
 
+/* ---- attention without any allocation ---------------------------------------- */
+
+/* Bytes of the fixed device scratch of zha_sparse_attn_noalloc (64 MiB per
+ * GPU, part of the library's code object: each GPU the library runs on holds
+ * it from the library's first use there until the process ends). */
+#define ZHA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * zha_sparse_attn with the per-walk attention path (ZHA_ATTN_PER_WALK; the
+ * same kernels, so the same result bit for bit) and no workspace argument.
+ * Its work items and partial states live in the fixed scratch instead.  The
+ * call allocates and frees nothing, on the device or the host.
+ *   Arguments, layouts and errors as zha_sparse_attn, plus:
+ *   ZHA_ERR_WORKSPACE   the call needs more than ZHA_NOALLOC_SCRATCH_BYTES
+ *                       (it needs zha_attn_workspace_bytes of the same
+ *                       arguments with attn_engine = ZHA_ATTN_PER_WALK; a
+ *                       smaller max_blocks_per_walk lowers it);
+ *   ZHA_ERR_UNSUPPORTED sel->attn_engine is ZHA_ATTN_UNION (AUTO runs the
+ *                       per-walk path here);
+ *   ZHA_ERR_HIP         the scratch's device address could not be found.
+ * Every call on a GPU uses that GPU's one scratch, whose contents after a
+ * call are that call's: calls that overlap on one GPU (other streams, other
+ * host threads) race and must be serialised by the caller.  Nothing in the
+ * scratch needs clearing between calls (every word a call reads it has
+ * written first). */
+zha_status zha_sparse_attn_noalloc(const zha_tree *t, const void *q, int32_t q_per_head,
+                                   const void *k_cache, const void *v_cache,
+                                   const zha_select *sel, const int32_t *sel_blocks,
+                                   const int32_t *sel_count, void *out, void *stream);
+
 /* ---- one decode step ------------------------------------------------------- */
 
 /* Workspace bytes of zha_forward (search + attention + selection lists). */

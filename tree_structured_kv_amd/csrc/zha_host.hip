@@ -9,8 +9,16 @@
 #include "zha_internal.h"
 
 #include <algorithm>
+#include <mutex>
 
 using namespace zha;
+
+// Scratch of zha_sparse_attn_noalloc: one fixed array per GPU, allocated
+// with the code object when the library loads on a device and held until
+// the process ends.  Host code never passes this name to a kernel (on the
+// host it is only a stand-in); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[ZHA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -499,6 +507,23 @@ DenseWs dense_ws_layout(const zha_tree *t, int32_t max_budget) {
     return l;
 }
 
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (with that device current) and kept; nullptr on a HIP error.
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];
+
+void *scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -641,6 +666,31 @@ zha_status zha_sparse_attn(const zha_tree *t, const void *q, int32_t q_per_head,
     return do_attn(t, q, q_per_head, k_cache, v_cache, sel_blocks, nullptr, sel_count,
                    sel->max_blocks_per_walk, tree_keys_bound(t, sel, q_per_head), out, ws,
                    static_cast<hipStream_t>(stream), ae);
+}
+
+zha_status zha_sparse_attn_noalloc(const zha_tree *t, const void *q, int32_t q_per_head,
+                                   const void *k_cache, const void *v_cache, const zha_select *sel,
+                                   const int32_t *sel_blocks, const int32_t *sel_count, void *out,
+                                   void *stream) {
+    zha_status s = check_tree(t);
+    if (s != ZHA_OK) return s;
+    if ((s = check_select(sel)) != ZHA_OK) return s;
+    if (q_per_head < 1) return ZHA_ERR_ARG;
+    if (walks_of(&t->geom, q_per_head) > (int64_t(1) << 24)) return ZHA_ERR_UNSUPPORTED;
+    if (q_per_head > 1 && t->n_tokens + q_per_head > t->geom.max_tokens) return ZHA_ERR_CAPACITY;
+    if (!q || !k_cache || !v_cache || !sel_blocks || !sel_count || !out) return ZHA_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        !aligned_n(sel_blocks, 4) || !aligned_n(sel_count, 4))
+        return ZHA_ERR_ALIGN;
+    if (sel->attn_engine == ZHA_ATTN_UNION) return ZHA_ERR_UNSUPPORTED;
+    const int64_t keys_bound = tree_keys_bound(t, sel, q_per_head);
+    const uint64_t need = attn_ws_layout(t->geom.head_dim, keys_bound, walks_of(&t->geom, q_per_head)).total;
+    if (need > ZHA_NOALLOC_SCRATCH_BYTES) return ZHA_ERR_WORKSPACE;
+    void *ws = scratch_ptr();
+    if (!ws) return ZHA_ERR_HIP;
+    return do_attn(t, q, q_per_head, k_cache, v_cache, sel_blocks, nullptr, sel_count,
+                   sel->max_blocks_per_walk, keys_bound, out, ws, static_cast<hipStream_t>(stream),
+                   ZHA_ATTN_PER_WALK);
 }
 
 uint64_t zha_forward_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head) {

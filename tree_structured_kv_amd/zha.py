@@ -70,7 +70,7 @@ STATS_WORDS = ctypes.sizeof(WalkStats) // 4   # int32 words per stats record
 
 EXPORTS = ["zha_tree_bytes", "zha_depth_for", "zha_tree_init", "zha_build", "zha_append",
            "zha_search_workspace_bytes", "zha_search_engine", "zha_search", "zha_visited_words", "zha_attn_workspace_bytes", "zha_attn_engine",
-           "zha_sparse_attn", "zha_forward_workspace_bytes", "zha_forward",
+           "zha_sparse_attn", "zha_sparse_attn_noalloc", "zha_forward_workspace_bytes", "zha_forward",
            "zha_dense_workspace_bytes", "zha_dense_topk_attn", "zha_bw_probe",
            "zha_status_string"]
 
@@ -95,6 +95,7 @@ def _load():
         "zha_visited_words": (u64, [tp]),
         "zha_attn_workspace_bytes": (u64, [tp, sp, i32]),
         "zha_sparse_attn": (i32, [tp, vp, i32, vp, vp, sp, vp, vp, vp, vp, u64, vp]),
+        "zha_sparse_attn_noalloc": (i32, [tp, vp, i32, vp, vp, sp, vp, vp, vp, vp]),
         "zha_forward_workspace_bytes": (u64, [tp, sp, i32]),
         "zha_forward": (i32, [tp, i64, vp, i32, vp, vp, sp, vp, vp, vp, vp, u64, vp]),
         "zha_dense_workspace_bytes": (u64, [tp, i32]),
@@ -300,6 +301,19 @@ def zha_sparse_attn(t: TreeHandle, q, k_cache, v_cache, sel: Select, sel_blocks,
                                ctypes.byref(sel), _ptr(sel_blocks), _ptr(sel_count), _ptr(out),
                                _ptr(ws), wsb, _stream(stream)),
            "zha_sparse_attn")
+
+
+def zha_sparse_attn_noalloc(t: TreeHandle, q, k_cache, v_cache, sel: Select, sel_blocks, sel_count, out,
+                            q_per_head: int = 1, stream=None):
+    _need_rows(t, q, "q", q_per_head)
+    _need_rows(t, out, "out", q_per_head)
+    _need_cache(t, k_cache, "k_cache")
+    _need_cache(t, v_cache, "v_cache")
+    _need_lists(t, sel, sel_blocks, sel_count, q_per_head)
+    _check(lib.zha_sparse_attn_noalloc(ctypes.byref(t), _ptr(q), q_per_head, _ptr(k_cache), _ptr(v_cache),
+                                       ctypes.byref(sel), _ptr(sel_blocks), _ptr(sel_count), _ptr(out),
+                                       _stream(stream)),
+           "zha_sparse_attn_noalloc")
 
 
 def zha_forward_workspace_bytes(t: TreeHandle, sel: Select, q_per_head: int = 1) -> int:
