@@ -7,10 +7,12 @@ in HBM.  Prints one JSON line:
 
   value         queries/s = batch / step time (a query = one sequence's token,
                 all its query heads)
-  roofline      the search kernel (the dominant launch): algorithmic bytes per
-                launch / its mean HIP-event duration, against 8 TB/s
+  roofline      the step (search + attention): algorithmic bytes per step /
+                its mean HIP-event duration, against 8 TB/s; the search and
+                attention calls each on their own, and the dominant kernel's
+                figure from the committed kernel trace
   cpu_baseline  the fp64 oracle (search + attention) on a bounded sample of
-                the same workload, on this host's cores
+                the same workload, on all of this host's cores and on one
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -389,12 +391,13 @@ def run_stream(w, select, threads, max_blocks=8192, max_candidates=0):
     )
 
 
-def cpu_baseline(w, select, Q_host, seconds_budget=15.0):
-    """The fp64 oracle (walk + attention) over the query heads of sampled
-    sequences, threads over walks (ctypes drops the GIL)."""
+def cpu_baseline(w, select, Q_host, seconds_budget=12.0):
+    """The fp64 oracle (walk + attention) over the query heads of sequence 0,
+    threads over walks (ctypes drops the GIL): once on every core of this
+    process's affinity set, once on a single thread."""
     from oracle import oracle as O
     from tree_structured_kv_amd import synth as S
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    cores = len(os.sched_getaffinity(0))
     t_build = time.time()
     b = 0
     trees, KV = {}, {}
@@ -419,20 +422,32 @@ def cpu_baseline(w, select, Q_host, seconds_budget=15.0):
         O.attend(sel, q, KV[g][0], KV[g][1], w.sharpness)
         return st["comparisons"]
 
-    # time whole queries (all heads of sequence 0) until the budget is spent
-    reps = 0
-    t0 = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=cores) as ex:
-        while True:
-            list(ex.map(one, range(w.heads)))
-            reps += 1
-            if time.perf_counter() - t0 > seconds_budget:
-                break
-    dt = time.perf_counter() - t0
+    def timed(threads, budget):
+        # whole queries (all heads of sequence 0) until the budget is spent
+        reps = 0
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            while True:
+                list(ex.map(one, range(w.heads)))
+                reps += 1
+                if time.perf_counter() - t0 > budget:
+                    break
+        return reps, time.perf_counter() - t0
+
+    reps, dt = timed(cores, seconds_budget)
+    reps1, dt1 = timed(1, seconds_budget / 2)
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return dict(value=reps / dt, unit="queries/s", cores=cores, kind="oracle",
                 sample=f"sequence 0 ({w.kv_heads} KV heads, {w.heads} query heads, rotation 0) "
-                       f"of {w.name}, repeated {reps}x; oracle trees built untimed in {build_s:.1f}s",
-                seconds=dt)
+                       f"of {w.name}, repeated {reps}x on {cores} threads; oracle trees built untimed "
+                       f"in {build_s:.1f}s",
+                single_thread=dict(value=reps1 / dt1, unit="queries/s", cores=1, seconds=dt1, reps=reps1),
+                cpu_model=cpu, seconds=dt)
 
 
 ENGINE_KERNELS = {
@@ -475,19 +490,11 @@ def measured_traffic(workload, engine):
 SWEEP_NS = [4096, 16384, 65536, 262144, 1 << 20, 1 << 22, 1 << 24]
 
 
-def sweep_levels(n, c=4, top=64):
-    """Depth policy of the length sweep: the fewest levels that leave at
-    most `top` nodes at the top level."""
-    L = 1
-    while n // c ** L > top:
-        L += 1
-    return L
-
-
 def run_sweep(Zm, ns=SWEEP_NS, queries=64, sample=16, reps=10):
     """Length sweep on nested keys (synth.nested_*): for each context length,
-    one tree (chunk 4, 4 references, depth by sweep_levels) and `queries`
-    one-place queries walked with top-p 0.9; reports comparisons and keys
+    one tree (chunk 4, 4 references) and `queries`
+    one-place queries walked with top-p 0.9 (depth from zha_depth_for: the
+    fewest levels leaving at most 64 top nodes); reports comparisons and keys
     read per walk, the dense attention mass the selection keeps (fp64 on the
     host, `sample` walks) and the search time."""
     import torch
@@ -495,7 +502,7 @@ def run_sweep(Zm, ns=SWEEP_NS, queries=64, sample=16, reps=10):
     d, c, R, s = 64, 4, 4, 20.0
     out = []
     for n in ns:
-        L = sweep_levels(n, c)
+        L = Zm.zha_depth_for(n, c, 64)
         t0 = time.time()
         K = S.nested_keys(n, d)
         Q = S.nested_queries(n, d, queries)
@@ -574,14 +581,40 @@ def summary(res, bw_ach):
     )
 
 
+def arithmetic_dtype(w, res):
+    """The type the step computes in: fp32 everywhere (bf16 or fp32 inputs
+    widened) except the union attention path, whose logits and weighted sums
+    are bf16 matrix products accumulated in fp32."""
+    if w.dtype == "bf16" and res.get("attn_engine") == "union":
+        return "bf16 x bf16 -> f32"
+    return "f32"
+
+
+def dominant_kernel(workload, res):
+    """The kernel with the largest share of the step in the committed kernel
+    trace of this workload (profiles/*_trace.md, `dominant:` JSON line), with
+    its algorithmic bytes per launch and mean duration from that trace.  None
+    when the trace was taken on other kernel sources."""
+    digest = kernel_digest()
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(f) as fh:
+            for line in fh:
+                if line.startswith("dominant: "):
+                    d = json.loads(line[len("dominant: "):])
+                    if d.get("workload") == workload and d.get("source") == digest:
+                        d["profile"] = os.path.relpath(f, ROOT)
+                        return d
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode-256K-topp", choices=sorted(WORKLOADS))
-    ap.add_argument("--also", default="decode-1M-topp,decode-256K-topk64,decode-256K-topp-bf16keys,"
-                                      "decode-1M-topp-bf16keys",
+    ap.add_argument("--also", default="decode-1M-topp,decode-64K-topp,decode-256K-topk64,"
+                                      "decode-256K-topp-bf16keys,decode-1M-topp-bf16keys",
                     help="comma-separated extra workloads reported under 'also'")
     ap.add_argument("--engine", default="auto", choices=["auto", "persistent", "level-sync", "union"])
     ap.add_argument("--no-cpu", action="store_true")
@@ -648,8 +681,10 @@ def main():
         cpu = cpu_baseline(w, select, Q0)
         log(f"cpu baseline {cpu}")
 
-    ach = main_sum["search_gbs"]
     traffic = measured_traffic(args.workload, main_sum["engine"])
+    step_bytes = main_sum["search_bytes"] + main_sum["attn_bytes"]
+    ach = main_sum["step_gbs"]
+    dom = dominant_kernel(args.workload, main_sum)
     out = {
         "metric": METRIC,
         "value": main_sum["qps"],
@@ -661,7 +696,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": arithmetic_dtype(w, main_sum),
         "data": "synthetic",
         "config": {
             "workload": f"{w.name} {args.workload}",
@@ -672,13 +707,23 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": ach / HBM_PEAK_GBS,
-            "traffic": None if traffic is None else traffic["bytes_per_call"],
-            "kernel": f"zha_search ({main_sum['engine']} engine: {ENGINE_KERNELS[main_sum['engine']]})",
-            "bytes_per_launch": main_sum["search_bytes"], "launch_ms": main_sum["search_ms"],
+            "traffic": None if traffic is None else traffic.get("step_bytes"),
+            "kernel": (f"one decode step: zha_search ({main_sum['engine']} engine: "
+                       f"{ENGINE_KERNELS[main_sum['engine']]}) then zha_sparse_attn "
+                       f"({main_sum['attn_engine']} path)"),
+            "bytes_per_launch": step_bytes, "launch_ms": main_sum["ms_per_step"],
             "achievable_gbs": bw_ach, "frac_of_achievable": ach / bw_ach,
+            "search": {"bytes": main_sum["search_bytes"], "ms": main_sum["search_ms"],
+                       "gbs": main_sum["search_gbs"], "frac": main_sum["search_gbs"] / HBM_PEAK_GBS,
+                       "traffic": None if traffic is None else traffic.get("bytes_per_call")},
+            "attention": {"bytes": main_sum["attn_bytes"], "ms": main_sum["attn_ms"],
+                          "gbs": main_sum["attn_gbs"], "frac": main_sum["attn_gbs"] / HBM_PEAK_GBS,
+                          "traffic": None if traffic is None else traffic.get("attn_bytes_per_call")},
+            "dominant_kernel": dom,
             "traffic_source": None if traffic is None else traffic["profile"],
         },
-        "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
+        "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample",
+                                                                       "single_thread", "cpu_model")},
         "step": {k: v for k, v in main_sum.items() if k not in ("workload", "select", "qps")},
         "also": also,
     }
