@@ -262,16 +262,16 @@ def test_search_engine_resolution(Z):
     assert Z.zha_search_engine(four, topp) == "level-sync"
 
 
-def test_sweep_depth_policy_and_nested_inputs():
-    # the length sweep's depth rule: fewest levels leaving <= 64 top nodes (chunk 4)
+def test_sweep_depth_policy_and_nested_inputs(Z):
+    # the length sweep's depth rule (zha_depth_for): fewest levels leaving <= 64 top nodes (chunk 4)
     import sys
     sys.path.insert(0, ROOT)
     import bench
     import numpy as np
     from tree_structured_kv_amd import synth as S
-    assert [bench.sweep_levels(n) for n in bench.SWEEP_NS] == [3, 4, 5, 6, 7, 8, 9]
-    assert all(n // 4 ** bench.sweep_levels(n) <= 64 < n // 4 ** (bench.sweep_levels(n) - 1)
-               for n in bench.SWEEP_NS)
+    depth = [Z.zha_depth_for(n, 4, 64) for n in bench.SWEEP_NS]
+    assert depth == [3, 4, 5, 6, 7, 8, 9]
+    assert all(n // 4 ** L <= 64 < n // 4 ** (L - 1) for n, L in zip(bench.SWEEP_NS, depth))
     k1 = S.nested_keys(5000, 64)
     k2 = S.nested_keys(5000, 64)
     assert k1.dtype == np.float32 and k1.shape == (5000, 64) and np.array_equal(k1, k2)
