@@ -211,6 +211,62 @@ def run_dense(idx, w, Q, K, V, per_rot, steps, warmup):
 
 
 ENGINE = "auto"
+FORWARD = True
+
+
+def run_forward(idx, w, Q, K, V, select, steps, warmup):
+    """zha_forward (n_new = 0: search + attention of one step) through the
+    multi-launch path (AUTO engine) and through the one-launch path
+    (ZHA_ENGINE_FUSED), timed with the same flush protocol; mean ms each."""
+    import torch
+    from tree_structured_kv_amd import zha as Zm
+    out = torch.empty(w.batch, w.heads, w.d, dtype=K.dtype, device="cuda")
+    stats = torch.zeros(idx.walks, Zm.STATS_WORDS, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    res = {}
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    # batch 1: the first sequence alone, where launch latency weighs most
+    g1 = Zm.make_geometry(1, w.kv_heads, w.group, w.d, w.chunk, w.refs, w.levels, w.dtype, w.n, w.sharpness)
+    idx1 = Zm.Index(g1, idx.refs)
+    idx1.build(K[:1], w.n)
+    out1 = torch.empty(1, w.heads, w.d, dtype=K.dtype, device="cuda")
+    for name, eng in (("multi_launch", "auto"), ("one_launch", "fused")):
+        sel = Zm.make_select(select["mode"], select.get("p", 0.9), select.get("k", (1,)),
+                             max_blocks=w.n // w.chunk, engine=eng)
+        ws = idx1.forward_workspace(sel)
+        q1 = [Q[r % ROTATIONS][:1].contiguous() for r in range(ROTATIONS)]
+        for r in range(warmup):
+            idx1.forward(0, q1[r % ROTATIONS], K[:1], V[:1], sel, out1, stats[:idx1.walks], status, ws)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i in range(steps):
+            flush.fill_(i & 0xFF)
+            evs[i][0].record()
+            idx1.forward(0, q1[i % ROTATIONS], K[:1], V[:1], sel, out1, stats[:idx1.walks], status, ws)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        res["batch1_" + name + "_ms"] = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        del ws
+    del idx1
+    for name, eng in (("multi_launch", "auto"), ("one_launch", "fused")):
+        sel = Zm.make_select(select["mode"], select.get("p", 0.9), select.get("k", (1,)),
+                             max_blocks=w.n // w.chunk, engine=eng)
+        ws = idx.forward_workspace(sel)
+        for r in range(warmup):
+            idx.forward(0, Q[r % ROTATIONS], K, V, sel, out, stats, status, ws)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i in range(steps):
+            flush.fill_(i & 0xFF)
+            evs[i][0].record()
+            idx.forward(0, Q[i % ROTATIONS], K, V, sel, out, stats, status, ws)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        res[name + "_ms"] = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        res[name + "_status"] = int(status.cpu()[0])
+        del ws
+    del flush
+    return res
 
 
 def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True, summary="f32"):
@@ -295,8 +351,9 @@ def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True, summary="
         dist[k] = dict(mean=float(v.mean()), p50=float(np.percentile(v, 50)),
                        p90=float(np.percentile(v, 90)), max=float(v.max()))
     dense = run_dense(idx, w, Q, K, V, per_rot, steps, warmup) if dense_baseline else None
+    fwd = run_forward(idx, w, Q, K, V, select, steps, warmup) if FORWARD else None
     res = dict(
-        dense=dense,
+        dense=dense, forward=fwd,
         workload=w, select=select, wall_s=wall, steps=steps, engine=idx.engine(sel),
         attn_engine=idx.attn_engine(sel), node_keys=summary,
         ms_per_step=float(step_ms.mean()),
@@ -576,7 +633,7 @@ def summary(res, bw_ach):
         keys_per_step=by["keys"], keys_union_per_step=by["union_keys"],
         status=res["status"], per_walk=res["dist"],
         nodes_scored_union_per_level=res["union_scored_per_level"],
-        dense=res["dense"],
+        dense=res["dense"], zha_forward=res["forward"],
         speedup_vs_dense=(res["dense"]["ms_per_step"] / res["ms_per_step"]) if res["dense"] else None,
     )
 
@@ -621,6 +678,8 @@ def main():
     ap.add_argument("--stream", type=int, default=1,
                     help="also run the streaming build + prefill workload (1/0)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense full-scan baseline")
+    ap.add_argument("--no-forward", action="store_true",
+                    help="skip timing zha_forward through the multi-launch and one-launch paths")
     ap.add_argument("--calibrate", action="store_true",
                     help="also copy 1 GiB three times (the known-size kernel that scales HBM counters)")
     ap.add_argument("--threads", type=int, default=min(16, len(os.sched_getaffinity(0))))
@@ -637,8 +696,9 @@ def main():
     from tree_structured_kv_amd import synth as S
     from tree_structured_kv_amd import zha as Zm
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    global ENGINE
+    global ENGINE, FORWARD
     ENGINE = args.engine
+    FORWARD = not args.no_forward
 
     if args.sweep:
         rows = run_sweep(Zm)

@@ -87,6 +87,14 @@ enum { ZHA_TOPP = 0, ZHA_TOPK = 1 };
  *     scored for all of its walks at once (fp32 matrix-core tiles); the root
  *     list is scored against every walk the same way.  One wavefront cuts
  *     each walk.
+ *   ZHA_ENGINE_FUSED: zha_forward only, decode (q_per_head = 1) with
+ *     n_new <= 1: the append, the walk and the attention of a decode step
+ *     in one launch, one workgroup per walk (the walk is the persistent
+ *     engine's, so selections and stats equal it bit for bit; attention is
+ *     summed in another order than zha_sparse_attn's).  Nodes the append
+ *     makes are computed by each of the pair's workgroups for itself and
+ *     written to the tree by the pair's first query head; no workgroup waits
+ *     on another.  AUTO never picks it.
  *   ZHA_ENGINE_AUTO: block for prefill (q_per_head > 1), else union for
  *     decode with at least 64 walks and 16 query heads per KV head, or 8 to
  *     16 under top-p, else level-synchronous for top-p with at least 64
@@ -96,7 +104,8 @@ enum {
     ZHA_ENGINE_PERSISTENT = 1,
     ZHA_ENGINE_LEVEL_SYNC = 2,
     ZHA_ENGINE_UNION = 3,
-    ZHA_ENGINE_BLOCK = 4
+    ZHA_ENGINE_BLOCK = 4,
+    ZHA_ENGINE_FUSED = 5
 };
 
 /* Attention paths (zha_select.attn_engine).  Both attend exactly the keys

@@ -246,3 +246,140 @@ def test_sweep_geometry_deep_trees(Z, n, levels):
             ref, _ = O.attend(toks, q.astype(np.float64), Kd, Vd, s)
             assert P.out_ok(outs[0, h], ref, "f32")[0], (h, engine)
         assert stable >= 4, stable
+
+
+# ---- the decode step in one launch (zha_forward, ZHA_ENGINE_FUSED) ----------------
+
+def _fwd_lists(Z, idx, sel, ws):
+    """The selection lists zha_forward keeps at the start of its workspace:
+    sel_blocks [walks][max_blocks] int32, then sel_count [walks] at the next
+    256-byte boundary."""
+    W = idx.walks
+    nb = W * sel.max_blocks_per_walk * 4
+    blocks = ws[:nb].view(torch.int32).view(W, sel.max_blocks_per_walk)
+    off = (nb + 255) // 256 * 256
+    count = ws[off:off + 4 * W].view(torch.int32)
+    return blocks.cpu().numpy(), count.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,n0", [("ar1-small", 8192 - 3), ("demo", 4096 - 70), ("clustered-small", 32768 - 2)])
+def test_fused_decode_steps(Z, name, n0):
+    """Decode steps of one token each through the one-launch path: after
+    every step the selections and stats equal the persistent engine's on a
+    tree built over the same tokens (bit for bit), every walk is checked
+    against the oracle walk (bit-exact where its cut is unique, else valid),
+    the output against oracle attention over the selection, and after the
+    last step the appended tree equals a full build bit for bit (the steps
+    cross whole level-1 chunks and, at n = 8,192 / 4,096 / 32,768, complete
+    a node on every level at once)."""
+    from tests.test_gpu_parity import _case
+    w, _ = _case(name)
+    K, V, Q, R = P.make_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    Kt, Vt, Qt, idx = _device(Z, w, K, V, Q, R, n0)
+    steps = min(w.n - n0, 12)
+    select = dict(mode="topp", p=0.9)
+    sel_f = P.select_struct(Z, select, w.n // w.chunk, engine="fused")
+    sel_p = P.select_struct(Z, select, w.n // w.chunk, engine="persistent", attn="per-walk")
+    ws = idx.forward_workspace(sel_f)
+    out = torch.empty_like(Qt)
+    stats = torch.zeros(idx.walks, Z.STATS_WORDS, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    from tree_structured_kv_amd.zha import stats_to_dicts
+    for k in range(steps):
+        idx.forward(1, Qt, Kt, Vt, sel_f, out, stats, status, ws)
+        n = n0 + k + 1
+        assert idx.n_tokens == n
+        ref = Z.Index(idx.geom, torch.from_numpy(R))
+        ref.build(Kt, n)
+        bufs = ref.search(Qt, sel_p)
+        torch.cuda.synchronize()
+        assert int(status.cpu()[0]) == 0
+        fb, fc = _fwd_lists(Z, idx, sel_f, ws)
+        pb, pc = bufs["sel_blocks"].cpu().numpy(), bufs["sel_count"].cpu().numpy()
+        assert np.array_equal(fc, pc), (k, n)
+        for wi in range(idx.walks):
+            assert np.array_equal(fb[wi, :fc[wi]], pb[wi, :pc[wi]]), (k, wi)
+        assert torch.equal(stats, bufs["stats"]), k
+        if k in (0, steps - 1) or n % w.chunk == 0:
+            st = stats_to_dicts(stats.cpu())
+            outs = out.float().cpu().numpy()
+            trees = {(b, g): P.oracle_tree(w, K, R, b, g, n) for b in range(w.batch) for g in range(w.kv_heads)}
+            for b in range(w.batch):
+                for h in range(w.heads):
+                    g = h // w.group
+                    wi = b * w.heads + h
+                    sel_o, st_o = P.oracle_walk(trees[(b, g)], Q[b, h], select)
+                    toks = P.gpu_tokens(fb[wi], fc[wi], w.chunk, n)
+                    _check_walk(trees[(b, g)], Q[b, h], select, fb[wi, :fc[wi]], toks, st[wi], sel_o, st_o, (k, b, h))
+                    o, _ = O.attend(toks, Q[b, h].astype(np.float64), K[b, g, :n].astype(np.float64),
+                                    V[b, g, :n].astype(np.float64), w.sharpness)
+                    assert P.out_ok(outs[b, h], o, w.dtype)[0], (k, b, h)
+    full = Z.Index(idx.geom, torch.from_numpy(R))
+    full.build(Kt, idx.n_tokens)
+    torch.cuda.synchronize()
+    for l in range(1, w.levels + 1):
+        live = idx.n_tokens // w.chunk ** l
+        assert torch.equal(idx.level(l)[0][:, :, :live], full.level(l)[0][:, :, :live]), l
+        assert torch.equal(idx.level(l)[1][:, :, :live], full.level(l)[1][:, :, :live]), l
+
+
+def test_fused_rejects_what_it_does_not_run(Z):
+    w, _ = (replace(S.WORKLOADS[1].scaled(n=8197, batch=2), kv_heads=2, levels=4), None)
+    K, V, Q, R = P.make_inputs(w)
+    Kt, Vt, Qt, idx = _device(Z, w, K, V, Q, R, 4000)
+    sel = P.select_struct(Z, dict(mode="topp", p=0.9), w.n // w.chunk, engine="fused")
+    ws = idx.forward_workspace(sel)
+    out = torch.empty_like(Qt)
+    stats = torch.zeros(idx.walks, Z.STATS_WORDS, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(Z.ZhaError) as e:
+        idx.forward(2, Qt, Kt, Vt, sel, out, stats, status, ws)           # more than one token
+    assert e.value.code == 6
+    with pytest.raises(Z.ZhaError) as e:
+        idx.search(Qt, sel)                                                # zha_forward only
+    assert e.value.code == 6
+    assert idx.n_tokens == 4000 and idx.engine(sel) is None
+
+
+# ---- the dense baseline's select on heavy ties ------------------------------------
+
+@pytest.mark.parametrize("chunk", [4, 2])
+def test_dense_select_heavy_ties(Z, chunk):
+    """The dense indexer's exact top-budget select when the cache repeats a
+    pattern of `chunk` keys: every head's logits take `chunk` values, each
+    about n/chunk times, so the crossing bin holds thousands of equal keys --
+    gathered into LDS (chunk 4: ~4,100 per value) or too many for it (chunk
+    2: ~8,200, narrowed over the logits instead).  Ties go to the lower
+    index; the set must equal the fp64 order exactly."""
+    w = replace(S.WORKLOADS[1], n=16384 + 16 + 4 + 3, batch=1, kv_heads=2, group=8, chunk=chunk, refs=4,
+                levels=3)
+    K = np.empty((1, 2, w.n, w.d), np.float32)
+    V = np.empty_like(K)
+    Q = np.empty((1, w.heads, w.d), np.float32)
+    for g in range(2):
+        K[0, g], V[0, g], Q[0, g * w.group:(g + 1) * w.group] = S.repeated_chunk_pair(w, g, seed=chunk)
+    R = np.stack([S.refs(w, g) for g in range(2)])
+    Kt, Vt, Qt, idx = _device(Z, w, K, V, Q, R, w.n)
+    walks = w.heads
+    budget = np.array([1, 3, w.n // chunk - 1, w.n // chunk, w.n // chunk + 5, 2 * (w.n // chunk) + 1,
+                       w.n - 1, w.n, 100, 4000, 8191, 8193, 12000, 5, 17, 9000], np.int32)[:walks]
+    maxb = int(budget.max())
+    sel_t = torch.full((walks, maxb), -1, dtype=torch.int32, device="cuda")
+    out = idx.dense_topk_attn(Qt, Kt, Vt, torch.from_numpy(budget).cuda(), maxb, sel_tokens=sel_t)
+    torch.cuda.synchronize()
+    got_all = sel_t.cpu().numpy()
+    outs = out.float().cpu().numpy()
+    for h in range(walks):
+        g = h // w.group
+        k = int(budget[h])
+        lg = w.sharpness * (K[0, g].astype(np.float64) @ Q[0, h].astype(np.float64))
+        vals = np.unique(lg)
+        assert len(vals) == chunk and np.min(np.diff(vals)) > 1e-3      # well separated values
+        order = np.lexsort((np.arange(w.n), -lg))
+        want = np.sort(order[:k])
+        got = got_all[h, :k].astype(np.int64)
+        assert np.array_equal(got, want), (h, k)
+        ref, _ = O.attend(got, Q[0, h].astype(np.float64), K[0, g].astype(np.float64), V[0, g].astype(np.float64),
+                          w.sharpness)
+        assert P.out_ok(outs[0, h], ref, w.dtype)[0], h

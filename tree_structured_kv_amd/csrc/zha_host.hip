@@ -97,7 +97,7 @@ zha_status check_select(const zha_select *sel) {
     }
     if (sel->max_blocks_per_walk < 1) return ZHA_ERR_ARG;
     if (sel->max_candidates < 0) return ZHA_ERR_ARG;
-    if (sel->engine < ZHA_ENGINE_AUTO || sel->engine > ZHA_ENGINE_BLOCK) return ZHA_ERR_ARG;
+    if (sel->engine < ZHA_ENGINE_AUTO || sel->engine > ZHA_ENGINE_FUSED) return ZHA_ERR_ARG;
     if (sel->attn_engine < ZHA_ATTN_AUTO || sel->attn_engine > ZHA_ATTN_UNION) return ZHA_ERR_ARG;
     return ZHA_OK;
 }
@@ -249,6 +249,13 @@ ForwardWs forward_ws_layout(const zha_tree *t, const zha_select *sel, int32_t qp
 
 zha_status hip_status(hipError_t e) { return e == hipSuccess ? ZHA_OK : ZHA_ERR_HIP; }
 
+// The one-launch decode step keeps the records of the nodes an append makes
+// (at most one per level) in LDS next to the leaf scratch: 64 KB at most.
+bool fused_fits(const zha_tree *t) {
+    const zha_geometry &g = t->geom;
+    return fused_lds_bytes(g.head_dim, g.num_refs, g.chunk, static_cast<int>(summary_bytes(&g)), g.levels) <= 65536;
+}
+
 zha_status run_levels(zha_tree *t, const void *k_cache, int64_t n_old, int64_t n_new, hipStream_t st) {
     const zha_geometry &g = t->geom;
     char *mem = static_cast<char *>(t->tree_mem);
@@ -303,22 +310,23 @@ int resolve_engine(const zha_tree *t, const zha_select *sel, int32_t qph) {
     return ZHA_ENGINE_PERSISTENT;
 }
 
-zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_select *sel,
-                     int32_t *sel_blocks, int32_t *sel_count, zha_walk_stats *stats, uint32_t *status,
-                     uint32_t *visited, void *ws, hipStream_t st) {
+// Search arguments for the tree as it stands with n_tok tokens summarised;
+// returns the number of roots (clamped to the candidate capacity).
+int64_t fill_search(const zha_tree *t, int64_t n_tok, const void *q, int32_t qph, const zha_select *sel,
+                    int32_t *sel_blocks, int32_t *sel_count, zha_walk_stats *stats, uint32_t *status,
+                    uint32_t *visited, void *ws, int engine, SearchArgs &a) {
     const zha_geometry &g = t->geom;
     const int64_t walks = walks_of(&g, qph);
     SearchWs lay = search_ws_layout(t, sel, qph);
     const char *mem = static_cast<const char *>(t->tree_mem);
-    SearchArgs a;
     memset(&a, 0, sizeof(a));
     for (int l = 1; l <= g.levels; ++l) {
         a.kap[l] = reinterpret_cast<const float *>(mem + t->key_off[l]);
         a.bet[l] = reinterpret_cast<const float *>(mem + t->bias_off[l]);
         a.cap[l] = t->level_cap[l];
-        a.nl[l] = level_count(t->n_tokens, g.chunk, l);
+        a.nl[l] = level_count(n_tok, g.chunk, l);
     }
-    a.nl[0] = t->n_tokens;
+    a.nl[0] = n_tok;
     a.nl[g.levels + 1] = 0;
     a.q = q;
     a.sel_blocks = sel_blocks;
@@ -369,7 +377,7 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
     }
     a.pairs = g.batch * g.num_kv_heads;
     a.score_grid = 1024;
-    a.n_tokens = t->n_tokens;
+    a.n_tokens = n_tok;
     a.walks = static_cast<int32_t>(walks);
     a.qph = qph;
     a.heads = g.num_kv_heads * g.group_size;
@@ -394,7 +402,6 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
     for (int l = 1; l < g.levels; ++l) n0 += a.nl[l] - int64_t(g.chunk) * a.nl[l + 1];
     a.n_roots = n0;
     if (n0 > a.cand_cap) n0 = a.cand_cap;
-    const int engine = resolve_engine(t, sel, qph);
     // union engine: the first steps whose pair lists cannot exceed
     // kSmallList nodes run in one launch; a root at level l adds at most
     // c^s nodes to the list of step s < l
@@ -421,6 +428,17 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
         const int from = std::max(a.small_steps + 1, g.levels - 2);
         if (from < g.levels && from < ZHA_MAX_STEPS) a.ls_from = from;
     }
+    return n0;
+}
+
+zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_select *sel,
+                     int32_t *sel_blocks, int32_t *sel_count, zha_walk_stats *stats, uint32_t *status,
+                     uint32_t *visited, void *ws, hipStream_t st) {
+    const zha_geometry &g = t->geom;
+    const int engine = resolve_engine(t, sel, qph);
+    SearchArgs a;
+    const int64_t n0 = fill_search(t, t->n_tokens, q, qph, sel, sel_blocks, sel_count, stats, status, visited,
+                                   ws, engine, a);
     if (engine == ZHA_ENGINE_BLOCK)
         return hip_status(launch_block(a, g.head_dim, g.num_refs, g.dtype, g.summary_dtype, static_cast<int>(n0), st));
     if (engine == ZHA_ENGINE_UNION)
@@ -492,6 +510,10 @@ zha_status do_attn(const zha_tree *t, const void *q, int32_t qph, const void *k_
     return hip_status(launch_attn(a, g.head_dim, g.dtype, st));
 }
 
+// Logits row stride of the dense baseline: a multiple of 4 floats, so a lane
+// stores 4 consecutive logits as one 16-byte write.
+uint64_t dense_row_pad(const zha_geometry &g) { return (uint64_t(g.max_tokens) + 3) / 4 * 4; }
+
 struct DenseWs {
     uint64_t logits, sel, sel_n, attn, total;
 };
@@ -500,7 +522,7 @@ DenseWs dense_ws_layout(const zha_tree *t, int32_t max_budget) {
     const uint64_t walks = static_cast<uint64_t>(walks_of(&g, 1));
     DenseWs l;
     l.logits = 0;
-    l.sel = align_up(walks * uint64_t(g.max_tokens) * sizeof(float));
+    l.sel = align_up(walks * dense_row_pad(g) * sizeof(float));
     l.sel_n = l.sel + align_up(walks * uint64_t(max_budget) * sizeof(int32_t));
     l.attn = l.sel_n + align_up(walks * sizeof(int32_t));
     l.total = l.attn + attn_ws_layout(g.head_dim, max_budget, walks).total;
@@ -607,6 +629,7 @@ int32_t zha_search_engine(const zha_tree *t, const zha_select *sel, int32_t q_pe
     if (check_tree(t) != ZHA_OK || check_select(sel) != ZHA_OK || q_per_head < 1) return -1;
     const int e = resolve_engine(t, sel, q_per_head);
     if (e == ZHA_ENGINE_UNION && (q_per_head != 1 || t->geom.group_size > 16)) return -1;
+    if (e == ZHA_ENGINE_FUSED) return -1;             // zha_forward only: zha_search never runs it
     return e;
 }
 
@@ -636,6 +659,7 @@ zha_status zha_search(const zha_tree *t, const void *q, int32_t q_per_head, cons
         return ZHA_ERR_ALIGN;
     if (sel->engine == ZHA_ENGINE_UNION && (q_per_head != 1 || t->geom.group_size > 16))
         return ZHA_ERR_UNSUPPORTED;
+    if (sel->engine == ZHA_ENGINE_FUSED) return ZHA_ERR_UNSUPPORTED;     // zha_forward only
     if (ws_bytes < zha_search_workspace_bytes(t, sel, q_per_head)) return ZHA_ERR_WORKSPACE;
     return do_search(t, q, q_per_head, sel, sel_blocks, sel_count, stats, status, visited, ws,
                      static_cast<hipStream_t>(stream));
@@ -715,10 +739,39 @@ zha_status zha_forward(zha_tree *t, int64_t n_new, const void *q, int32_t q_per_
     if (q_per_head > 1 && t->n_tokens + q_per_head > t->geom.max_tokens) return ZHA_ERR_CAPACITY;
     if (sel->engine == ZHA_ENGINE_UNION && (q_per_head != 1 || t->geom.group_size > 16))
         return ZHA_ERR_UNSUPPORTED;
+    if (sel->engine == ZHA_ENGINE_FUSED && (q_per_head != 1 || n_new > 1 || !fused_fits(t)))
+        return ZHA_ERR_UNSUPPORTED;
     const int ae = resolve_attn(t, sel, q_per_head);
-    if (ae == ZHA_ATTN_UNION && !union_attn_ok(t, q_per_head)) return ZHA_ERR_UNSUPPORTED;
+    if (ae == ZHA_ATTN_UNION && !union_attn_ok(t, q_per_head) && sel->engine != ZHA_ENGINE_FUSED)
+        return ZHA_ERR_UNSUPPORTED;
     if (ws_bytes < zha_forward_workspace_bytes(t, sel, q_per_head)) return ZHA_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (sel->engine == ZHA_ENGINE_FUSED) {
+        // the append, the walk and the attention in one launch
+        const zha_geometry &g = t->geom;
+        const int64_t n_tok = t->n_tokens + n_new;
+        ForwardWs lay = forward_ws_layout(t, sel, q_per_head);
+        char *wsb = static_cast<char *>(ws);
+        FusedArgs f;
+        memset(&f, 0, sizeof(f));
+        (void)fill_search(t, n_tok, q, 1, sel, reinterpret_cast<int32_t *>(wsb + lay.sel_blocks),
+                          reinterpret_cast<int32_t *>(wsb + lay.sel_count), stats, status, nullptr,
+                          wsb + lay.search, ZHA_ENGINE_PERSISTENT, f.s);
+        f.k = k_cache;
+        f.v = v_cache;
+        f.out = out;
+        f.refs = t->refs;
+        f.max_tokens = g.max_tokens;
+        f.fresh_m = 0;
+        for (int l = 1; l <= g.levels; ++l) {
+            if (level_count(n_tok, g.chunk, l) > level_count(t->n_tokens, g.chunk, l)) f.fresh_m = l;
+            f.tree_k[l] = static_cast<char *>(t->tree_mem) + t->key_off[l];
+            f.tree_b[l] = reinterpret_cast<float *>(static_cast<char *>(t->tree_mem) + t->bias_off[l]);
+        }
+        s = hip_status(launch_fused(f, g.head_dim, g.num_refs, g.dtype, g.summary_dtype, st));
+        if (s == ZHA_OK) t->n_tokens = n_tok;
+        return s;
+    }
     // decode: the new rows join the tree first, so the query sees them
     if (q_per_head == 1 && n_new > 0) {
         s = run_levels(t, k_cache, t->n_tokens, t->n_tokens + n_new, st);
@@ -774,7 +827,7 @@ zha_status zha_dense_topk_attn(const zha_tree *t, const void *q, const void *k_c
     a.sel_n = reinterpret_cast<int32_t *>(wb + lay.sel_n);
     a.max_tokens = g.max_tokens;
     a.n_tokens = t->n_tokens;
-    a.row_pad = g.max_tokens;
+    a.row_pad = static_cast<int64_t>(dense_row_pad(g));
     a.walks = static_cast<int32_t>(walks_of(&g, 1));
     a.heads = g.num_kv_heads * g.group_size;
     a.group = g.group_size;

@@ -206,6 +206,20 @@ struct DenseArgs {
     float sharpness;
 };
 
+// One decode step in one launch (zha_forward with ZHA_ENGINE_FUSED): the
+// search arguments describe the tree after the append.
+struct FusedArgs {
+    SearchArgs s;
+    const void *k;                          // K cache
+    const void *v;                          // V cache
+    void *out;                              // [walks][D]
+    const float *refs;                      // [kv_heads][R][D]
+    int64_t max_tokens;
+    int32_t fresh_m;                        // levels 1..fresh_m gain their last node in this append
+    void *tree_k[ZHA_MAX_LEVELS + 1];       // level-l keys, pair 0 (written by the pairs' first walks)
+    float *tree_b[ZHA_MAX_LEVELS + 1];      // level-l biases, pair 0
+};
+
 hipError_t launch_level(const LevelArgs &a, int D, int dtype, int sdtype, bool leaf, hipStream_t st);
 hipError_t launch_search(const SearchArgs &a, int D, int R, int dtype, int sdtype, int engine, int n0,
                          hipStream_t st);
@@ -216,6 +230,8 @@ hipError_t launch_attn(const AttnArgs &a, int D, int dtype, hipStream_t st);
 hipError_t launch_attn_union(const AttnArgs &a, int D, hipStream_t st);
 hipError_t launch_attn_block(const AttnArgs &a, int D, hipStream_t st);
 hipError_t launch_dense(const DenseArgs &a, int D, int dtype, hipStream_t st);
+hipError_t launch_fused(const FusedArgs &f, int D, int R, int dtype, int sdtype, hipStream_t st);
+size_t fused_lds_bytes(int D, int R, int c, int sbytes, int m);
 hipError_t launch_probe(const void *buf, uint64_t bytes, float *sink, hipStream_t st);
 
 }  // namespace zha

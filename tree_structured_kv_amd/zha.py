@@ -22,9 +22,9 @@ TOPP, TOPK = 0, 1
 F32, BF16 = 0, 1
 FLAG_CAND_OVERFLOW, FLAG_SEL_OVERFLOW, FLAG_NONFINITE = 1, 2, 4
 PATH_TIE_SELECT, PATH_LONG_LIST, PATH_LDS_SPILL = 1, 2, 4
-ENGINE_AUTO, ENGINE_PERSISTENT, ENGINE_LEVEL_SYNC, ENGINE_UNION, ENGINE_BLOCK = 0, 1, 2, 3, 4
+ENGINE_AUTO, ENGINE_PERSISTENT, ENGINE_LEVEL_SYNC, ENGINE_UNION, ENGINE_BLOCK, ENGINE_FUSED = 0, 1, 2, 3, 4, 5
 ENGINES = {"auto": ENGINE_AUTO, "persistent": ENGINE_PERSISTENT, "level-sync": ENGINE_LEVEL_SYNC,
-           "union": ENGINE_UNION, "block": ENGINE_BLOCK}
+           "union": ENGINE_UNION, "block": ENGINE_BLOCK, "fused": ENGINE_FUSED}
 ATTN_AUTO, ATTN_PER_WALK, ATTN_UNION = 0, 1, 2
 ATTN_ENGINES = {"auto": ATTN_AUTO, "per-walk": ATTN_PER_WALK, "union": ATTN_UNION}
 
