@@ -201,13 +201,22 @@ def run_dense(idx, w, Q, K, V, per_rot, steps, warmup):
     e = 2 if w.dtype == "bf16" else 4
     walks = w.batch * w.heads
     k_bytes = w.batch * w.kv_heads * w.n * w.d * e
-    logit_bytes = walks * w.n * 4 * (1 + 4)      # written once, read by 3 histogram passes + 1 compaction
+    # written once by the K pass, read by the histogram pass, the gathering
+    # pass and the compaction (two more when a crossing bin overflows LDS)
+    logit_bytes = walks * w.n * 4 * (1 + 3)
     keys = float(np.mean([sum(s["keys_read"] for s in rows) for rows in per_rot]))
     attn_bytes = 2 * w.d * e * keys + 2 * walks * w.d * e
     return dict(ms_per_step=ms, qps=w.batch / (ms * 1e-3), k_pass_bytes=k_bytes,
                 logit_bytes=logit_bytes, attn_bytes=attn_bytes,
                 gbs=(k_bytes + logit_bytes + attn_bytes) / (ms * 1e-3) / 1e9,
                 max_budget=maxb)
+
+
+def dense_floor(dense, bw_ach):
+    """The least time any full-scan indexer needs on this GPU: one read of
+    every key of every (sequence, KV head) at the achievable HBM read rate,
+    before any selection or attention."""
+    return dense["k_pass_bytes"] / (bw_ach * 1e9) * 1e3
 
 
 ENGINE = "auto"
@@ -635,6 +644,8 @@ def summary(res, bw_ach):
         nodes_scored_union_per_level=res["union_scored_per_level"],
         dense=res["dense"], zha_forward=res["forward"],
         speedup_vs_dense=(res["dense"]["ms_per_step"] / res["ms_per_step"]) if res["dense"] else None,
+        dense_k_floor_ms=dense_floor(res["dense"], bw_ach) if res["dense"] else None,
+        speedup_vs_dense_k_floor=(dense_floor(res["dense"], bw_ach) / res["ms_per_step"]) if res["dense"] else None,
     )
 
 

@@ -6,15 +6,15 @@
 // Introduces ZHA, a Path to True Subquadratic Attention" on indexers that
 // scan the whole context), written from its plain definition.
 //
-// GPU design.  k_dense_logits reads every K row once per (sequence, KV head)
+// GPU design.  k_dense_kpass reads every K row once per (sequence, KV head)
 // and scores it for all query heads of the group: for bf16 caches that is a
-// [heads x D] x [D x keys] contraction done with 16x16x16 bf16 MFMA tiles
-// (heads padded to 16), so the pass stays bound by HBM, not by VALU.
-// k_dense_select then finds each walk's budget-th largest logit exactly with
-// an 11 + 11 + 10-bit radix select over order-preserving keys (one read of
-// the walk's logits per level; eight copies of the LDS histogram so that
-// lanes whose logits share a bin rarely collide on one address) and compacts
-// the selected indices in ascending order; among equal logits the lower
+// [keys x D] x [D x heads] contraction done with gfx950's 16x16x32 bf16
+// matrix products (heads padded to 16), so the pass stays bound by HBM, not
+// by VALU, and each head's fp32 logits leave in 64-byte runs.
+// k_dense_select then finds each walk's budget-th largest logit exactly (a
+// 12-bit histogram pass, the crossing bin gathered into LDS and narrowed
+// there by two 10-bit levels) and compacts the selected indices in ascending
+// order: three reads of the walk's logits; among equal logits the lower
 // index wins.  Attention reuses the planned split-K kernels with token lists.
 #include "zha_device.h"
 #include "zha_internal.h"
@@ -23,8 +23,8 @@ namespace zha {
 
 namespace {
 
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
@@ -37,75 +37,66 @@ __device__ __forceinline__ uint32_t logit_key(float f) {
 
 }  // namespace
 
-// bf16 logits: one wavefront per 16-key group, all heads of the pair (16 per
-// MFMA tile).  The D dimension is split as lane group g = lane/16 owning
-// elements [D/4 * g, D/4 * (g+1)) in both operands, so every lane reads one
-// contiguous piece of its key row and of each query row.
+// bf16 logits, keys as the rows of S^T = K Q^T: one wavefront per 64-key
+// run (four 16-key tiles in flight), every head of the pair as a column
+// (16 per tile), gfx950's 16x16x32 bf16 matrix product.  Lane group kb =
+// lane/16 owns the D/4 contiguous dims [kb*D/4, (kb+1)*D/4) of both operands
+// (a dot product may take its terms in any order, so the k index need only
+// agree between the operands), which it reads as 16-byte pieces of its key
+// row.  The product's lane holds 4 consecutive keys of one head, stored as
+// one float4: each head's logits are written in 64-byte runs.
 template <int D>
-__global__ __launch_bounds__(kBlock) void k_dense_logits_mfma(DenseArgs a) {
-    constexpr int KS = D / 16;            // MFMA steps (16 elements each)
-    constexpr int PER = D / 4;            // elements per lane group
+__global__ __launch_bounds__(kBlock) void k_dense_kpass(DenseArgs a) {
+    constexpr int PER = D / 4;            // dims per lane group
+    constexpr int KS = PER / 8;           // 16x16x32 steps (8 dims a lane each)
+    constexpr int UT = 4;                 // 16-key tiles in flight
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int pair = blockIdx.y;
-    const int grp = lane >> 4, col = lane & 15;
+    const int kb = lane >> 4, col = lane & 15;
     const int g_kv = pair % a.kv_heads;
     const int b = pair / a.kv_heads;
     const int64_t n = a.n_tokens;
-    const bf16_t *kb = static_cast<const bf16_t *>(a.k) + static_cast<int64_t>(pair) * a.max_tokens * D;
-    const int n_groups = static_cast<int>((n + 15) / 16);
+    const bf16_t *kbase = static_cast<const bf16_t *>(a.k) + static_cast<int64_t>(pair) * a.max_tokens * D + kb * PER;
+    const int64_t runs = (n + 63) / 64;
+    const int64_t rstride = static_cast<int64_t>(gridDim.x) * (kBlock / 64);
 
     for (int hb = 0; hb < a.group; hb += 16) {
-        // query operand: row = head hb + col of this pair's group
-        short4_t qa[KS];
+        // query operand: column = head hb + col
+        bf16x8_t qb[KS];
+        const int h = hb + col;
+        const bool hok = h < a.group;
+        const int64_t w = static_cast<int64_t>(b) * a.heads + g_kv * a.group + (hok ? h : 0);
         {
-            const int h = hb + col;
-            const bool ok = h < a.group;
-            const int w = b * a.heads + g_kv * a.group + (ok ? h : 0);
-            const bf16_t *qp = static_cast<const bf16_t *>(a.q) + static_cast<int64_t>(w) * D + grp * PER;
+            const bf16_t *qp = static_cast<const bf16_t *>(a.q) + w * D + kb * PER;
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                short4_t v;
-                v.x = ok ? static_cast<short>(qp[4 * kk + 0]) : 0;
-                v.y = ok ? static_cast<short>(qp[4 * kk + 1]) : 0;
-                v.z = ok ? static_cast<short>(qp[4 * kk + 2]) : 0;
-                v.w = ok ? static_cast<short>(qp[4 * kk + 3]) : 0;
-                qa[kk] = v;
-            }
+            for (int s = 0; s < KS; ++s) qb[s] = hok ? *reinterpret_cast<const bf16x8_t *>(qp + 8 * s) : bf16x8_t{};
         }
-        constexpr int UG = 4;                 // 16-key groups in flight per wavefront
-        const int gstride = gridDim.x * (kBlock / 64);
-        for (int kg0 = blockIdx.x * (kBlock / 64) + wave; kg0 < n_groups; kg0 += gstride * UG) {
-            short4_t kbv[UG][KS];
+        float *lrow = a.logits + w * a.row_pad;
+        for (int64_t run = static_cast<int64_t>(blockIdx.x) * (kBlock / 64) + wave; run < runs; run += rstride) {
+            const int64_t key0 = run * 64;
+            bf16x8_t kv[UT][KS];
 #pragma unroll
-            for (int u = 0; u < UG; ++u) {
-                const int64_t key = static_cast<int64_t>(kg0 + u * gstride) * 16 + col;
-                const int64_t row = key < n ? key : n - 1;
-                const bf16_t *kp = kb + row * D + grp * PER;
+            for (int u = 0; u < UT; ++u) {
+                int64_t row = key0 + 16 * u + col;
+                row = row < n ? row : n - 1;
 #pragma unroll
-                for (int kk = 0; kk < KS; kk += 2) {
-                    const uint4 v = *reinterpret_cast<const uint4 *>(kp + 4 * kk);
-                    kbv[u][kk] = short4_t{static_cast<short>(v.x & 0xffff), static_cast<short>(v.x >> 16),
-                                          static_cast<short>(v.y & 0xffff), static_cast<short>(v.y >> 16)};
-                    kbv[u][kk + 1] = short4_t{static_cast<short>(v.z & 0xffff), static_cast<short>(v.z >> 16),
-                                              static_cast<short>(v.w & 0xffff), static_cast<short>(v.w >> 16)};
-                }
+                for (int s = 0; s < KS; ++s) kv[u][s] = *reinterpret_cast<const bf16x8_t *>(kbase + row * D + 8 * s);
             }
 #pragma unroll
-            for (int u = 0; u < UG; ++u) {
-                const int64_t key = static_cast<int64_t>(kg0 + u * gstride) * 16 + col;
-                float4_t acc = {0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < UT; ++u) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < KS; ++kk)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qa[kk], kbv[u][kk], acc, 0, 0, 0);
-                if (key < n) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int h = hb + 4 * grp + i;
-                        if (h < a.group) {
-                            const int64_t w = static_cast<int64_t>(b) * a.heads + g_kv * a.group + h;
-                            a.logits[w * a.row_pad + key] = a.sharpness * acc[i];
-                        }
-                    }
+                for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[u][s], qb[s], acc, 0, 0, 0);
+                if (!hok) continue;
+                const int64_t k4 = key0 + 16 * u + 4 * kb;     // this lane's 4 keys
+                const float4 v = make_float4(a.sharpness * acc[0], a.sharpness * acc[1], a.sharpness * acc[2],
+                                             a.sharpness * acc[3]);
+                if (k4 + 3 < n) {
+                    *reinterpret_cast<float4 *>(lrow + k4) = v;
+                } else {
+                    if (k4 < n) lrow[k4] = v.x;
+                    if (k4 + 1 < n) lrow[k4 + 1] = v.y;
+                    if (k4 + 2 < n) lrow[k4 + 2] = v.z;
                 }
             }
         }
@@ -137,17 +128,70 @@ __global__ __launch_bounds__(kBlock) void k_dense_logits_f32(DenseArgs a) {
     }
 }
 
-// One workgroup per walk: exact top-budget selection over the walk's logits.
+// Workgroup (kSelThreads): the bin, among nb bins counted in `copies`
+// interleaved copies of a histogram (bin x of copy c at h[c * nb + x]), where
+// the count from the top reaches `need`; *above = the count in the bins
+// above it.  Bins are scanned from the highest.
+__device__ __forceinline__ void top_bin(const uint32_t *h, int copies, int nb, uint32_t need, uint32_t *s_wsum,
+                                        uint32_t *s_bin, uint32_t *s_above) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int per = nb / kSelThreads;     // bins per thread (1 or 4), highest first
+    uint32_t cnt[4] = {0, 0, 0, 0}, tsum = 0;
+    for (int e = 0; e < per; ++e) {
+        const int bin = nb - 1 - per * tid - e;
+        uint32_t c = 0;
+        for (int cp = 0; cp < copies; ++cp) c += h[cp * nb + bin];
+        cnt[e] = c;
+        tsum += c;
+    }
+    uint32_t incl = tsum;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int i = 0; i < wave; ++i) before += s_wsum[i];
+    const uint32_t excl = before + incl - tsum;
+    if (excl < need && excl + tsum >= need) {
+        uint32_t run = excl;
+        for (int e = 0; e < per; ++e) {
+            if (run + cnt[e] >= need) {
+                *s_bin = static_cast<uint32_t>(nb - 1 - per * tid - e);
+                *s_above = run;
+                break;
+            }
+            run += cnt[e];
+        }
+    }
+    __syncthreads();
+}
+
+// One workgroup per walk: exact top-budget selection over the walk's logits
+// (order-preserving 32-bit keys; among equal logits the lower index wins).
+//   pass 1: histogram of the top 12 key bits -> the bin holding the
+//           budget-th largest key;
+//   pass 2: that bin's keys and indices gathered into LDS (at most kSelBuf
+//           of them; a larger bin is narrowed by two more passes over the
+//           logits and one counting pass instead), where two 10-bit radix
+//           levels give the exact key tau, while every wavefront segment of
+//           the compaction counts its keys above the bin;
+//   pass 3: ordered compaction of the keys above tau and of the first ties,
+//           each segment starting at the prefix of those counts.
+constexpr int kSelBuf = 8192;
 __global__ __launch_bounds__(kSelThreads) void k_dense_select(DenseArgs a) {
     const int w = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t n = a.n_tokens;
     const float *lg = a.logits + static_cast<int64_t>(w) * a.row_pad;
     int32_t *out = a.sel + static_cast<int64_t>(w) * a.max_budget;
-    constexpr int kCopies = 8;            // histogram copies: lanes l and l+8 share one
-    __shared__ uint32_t hist[kCopies][2048];
+    constexpr int kCopies = 4;            // histogram copies: lanes l and l+4 share one
+    __shared__ uint32_t buf[2 * kSelBuf]; // pass 1: kCopies x 4096 bins; pass 2: the bin's keys, then indices
+    __shared__ uint32_t h2[1024];
+    __shared__ uint32_t s_above_seg[kSelWaves], s_tie_seg[kSelWaves];
     __shared__ uint32_t wsum[kSelWaves];
-    __shared__ uint32_t s_bin, s_above;
+    __shared__ uint32_t s_bin, s_above, s_n;
     __shared__ unsigned long long scan[kSelWaves];
 
     int64_t k = a.budget[w];
@@ -157,19 +201,42 @@ __global__ __launch_bounds__(kSelThreads) void k_dense_select(DenseArgs a) {
         if (tid == 0) a.sel_n[w] = 0;
         return;
     }
-
-    // three radix levels over the 32-bit key: bits [31:21], [20:10], [9:0]
-    uint32_t prefix = 0;     // decided high bits of the threshold key
-    uint32_t need = static_cast<uint32_t>(k);
     const int copy = lane & (kCopies - 1);
+    uint32_t need = static_cast<uint32_t>(k);
+
+    // pass 1: bits [31:20]
+    for (int i = tid; i < kCopies * 4096; i += kSelThreads) buf[i] = 0;
+    __syncthreads();
+    for (int64_t i0 = tid; i0 < n; i0 += 4 * kSelThreads) {
+        float v[4];
 #pragma unroll
-    for (int lev = 0; lev < 3; ++lev) {
-        const int sh = (lev == 0) ? 21 : (lev == 1) ? 10 : 0;
-        const int wd = (lev == 2) ? 10 : 11;
-        const int nb = 1 << wd;
-        for (int i = tid; i < kCopies * 2048; i += kSelThreads) (&hist[0][0])[i] = 0;
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = i0 + u * kSelThreads;
+            v[u] = (i < n) ? lg[i] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i0 + u * kSelThreads < n) atomicAdd(&buf[copy * 4096 + (logit_key(v[u]) >> 20)], 1u);
+    }
+    __syncthreads();
+    top_bin(buf, kCopies, 4096, need, wsum, &s_bin, &s_above);
+    const uint32_t b1 = s_bin;
+    need -= s_above;
+    uint32_t in_bin = 0;
+    for (int cp = 0; cp < kCopies; ++cp) in_bin += buf[cp * 4096 + b1];
+    __syncthreads();
+
+    // compaction segments: wavefront v owns [v*seg, (v+1)*seg), seg a multiple of 64
+    const int64_t seg = (((n + kSelWaves - 1) / kSelWaves) + 63) / 64 * 64;
+    uint32_t prefix = b1 << 20;
+    const bool gathered = in_bin <= static_cast<uint32_t>(kSelBuf);
+    uint32_t *bkey = buf, *bidx = buf + kSelBuf;
+    if (gathered) {
+        // pass 2: gather the bin's keys and indices, count each segment's
+        // keys above the bin, then two 10-bit levels in LDS
+        if (tid == 0) s_n = 0;
+        if (tid < kSelWaves) { s_above_seg[tid] = 0; s_tie_seg[tid] = 0; }
         __syncthreads();
-        const uint32_t want = (lev == 0) ? 0u : (prefix >> (sh + wd));
         for (int64_t i0 = tid; i0 < n; i0 += 4 * kSelThreads) {
             float v[4];
 #pragma unroll
@@ -181,58 +248,85 @@ __global__ __launch_bounds__(kSelThreads) void k_dense_select(DenseArgs a) {
             for (int u = 0; u < 4; ++u) {
                 const int64_t i = i0 + u * kSelThreads;
                 const uint32_t key = logit_key(v[u]);
-                const bool match = (i < n) && ((lev == 0) || ((key >> (sh + wd)) == want));
-                if (match) atomicAdd(&hist[copy][(key >> sh) & (nb - 1)], 1u);
-            }
-        }
-        __syncthreads();
-        // scan bins from the top: thread t holds bins nb-1-2t, nb-2-2t
-        uint32_t c2[2], tsum = 0;
-        for (int e = 0; e < 2; ++e) {
-            const int bin = nb - 1 - 2 * tid - e;
-            uint32_t cnt = 0;
-            if (bin >= 0)
-                for (int cp = 0; cp < kCopies; ++cp) cnt += hist[cp][bin];
-            c2[e] = cnt;
-            tsum += cnt;
-        }
-        uint32_t incl = tsum;
-        for (int off = 1; off < 64; off <<= 1) {
-            uint32_t o = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += o;
-        }
-        if (lane == 63) wsum[wave] = incl;
-        __syncthreads();
-        uint32_t before = 0;
-        for (int i = 0; i < wave; ++i) before += wsum[i];
-        const uint32_t excl = before + incl - tsum;
-        if (excl < need && excl + tsum >= need) {
-            uint32_t run = excl;
-            for (int e = 0; e < 2; ++e) {
-                if (run + c2[e] >= need) {
-                    s_bin = static_cast<uint32_t>(nb - 1 - 2 * tid - e);
-                    s_above = run;
-                    break;
+                const bool live = i < n;
+                if (live && (key >> 20) == b1) {
+                    const uint32_t slot = atomicAdd(&s_n, 1u);
+                    bkey[slot] = key;
+                    bidx[slot] = static_cast<uint32_t>(i);
                 }
-                run += c2[e];
+                // the wavefront's 64 indices lie in one segment
+                const uint32_t up = static_cast<uint32_t>(__popcll(__ballot(live && (key >> 20) > b1)));
+                if (lane == 0 && up) atomicAdd(&s_above_seg[(i - lane) / seg], up);
             }
         }
         __syncthreads();
-        prefix |= s_bin << sh;
-        need -= s_above;
+        const int nb = static_cast<int>(s_n);
+#pragma unroll
+        for (int lev = 0; lev < 2; ++lev) {
+            const int sh = lev == 0 ? 10 : 0;
+            for (int i = tid; i < 1024; i += kSelThreads) h2[i] = 0;
+            __syncthreads();
+            for (int i = tid; i < nb; i += kSelThreads) {
+                const uint32_t key = buf[i];
+                if (lev == 0 || (key >> 10) == (prefix >> 10)) atomicAdd(&h2[(key >> sh) & 1023u], 1u);
+            }
+            __syncthreads();
+            top_bin(h2, 1, 1024, need, wsum, &s_bin, &s_above);
+            prefix |= s_bin << sh;
+            need -= s_above;
+            __syncthreads();
+        }
+        // the gathered keys above tau and equal to it, per segment
+        for (int i = tid; i < nb; i += kSelThreads) {
+            const uint32_t key = bkey[i];
+            const int sg = static_cast<int>(bidx[i] / seg);
+            if (key > prefix) atomicAdd(&s_above_seg[sg], 1u);
+            else if (key == prefix) atomicAdd(&s_tie_seg[sg], 1u);
+        }
         __syncthreads();
+    } else {
+        // the bin is too large for LDS: two more passes over the logits
+        uint32_t *hist = buf;
+#pragma unroll
+        for (int lev = 0; lev < 2; ++lev) {
+            const int sh = lev == 0 ? 10 : 0;
+            for (int i = tid; i < 4 * 1024; i += kSelThreads) hist[i] = 0;
+            __syncthreads();
+            for (int64_t i0 = tid; i0 < n; i0 += 4 * kSelThreads) {
+                float v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int64_t i = i0 + u * kSelThreads;
+                    v[u] = (i < n) ? lg[i] : -INFINITY;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t key = logit_key(v[u]);
+                    if (i0 + u * kSelThreads < n && (key >> (sh + 10)) == (prefix >> (sh + 10)))
+                        atomicAdd(&hist[copy * 1024 + ((key >> sh) & 1023u)], 1u);
+                }
+            }
+            __syncthreads();
+            top_bin(hist, kCopies, 1024, need, wsum, &s_bin, &s_above);
+            prefix |= s_bin << sh;
+            need -= s_above;
+            __syncthreads();
+        }
     }
     const uint32_t tau = prefix;   // keys > tau open; `need` of the keys == tau open, lowest index first
 
     // ordered compaction: wavefront v owns the contiguous segment
     // [v*seg, (v+1)*seg) and walks it 64 consecutive logits at a time
     // (coalesced); ballots give each lane its rank inside the step.
-    const int64_t seg = (((n + kSelWaves - 1) / kSelWaves) + 63) / 64 * 64;
     const int64_t s0 = wave * seg;
     const int64_t s1 = (s0 + seg < n) ? s0 + seg : n;
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     constexpr int UC = 8;                 // 64-logit steps in flight per wavefront
     uint32_t ca = 0, ct = 0;
+    if (gathered) {
+        ca = s_above_seg[wave];
+        ct = s_tie_seg[wave];
+    } else
     for (int64_t base0 = s0; base0 < s1; base0 += 64 * UC) {
         uint32_t kv[UC];
 #pragma unroll
@@ -289,10 +383,16 @@ hipError_t launch_dense(const DenseArgs &a, int D, int dtype, hipStream_t st) {
     if (gx < 1) gx = 1;
     dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(pairs));
     if (dtype == ZHA_BF16) {
+        // 64-key runs, about 2048 workgroups of 4 wavefronts in all
+        const int64_t runs = (a.n_tokens + 63) / 64;
+        int rx = static_cast<int>((runs + 3) / 4);
+        if (rx > per_pair) rx = per_pair;
+        if (rx < 1) rx = 1;
+        dim3 rgrid(static_cast<unsigned>(rx), static_cast<unsigned>(pairs));
         if (D == 64)
-            hipLaunchKernelGGL(k_dense_logits_mfma<64>, grid, dim3(kBlock), 0, st, a);
+            hipLaunchKernelGGL(k_dense_kpass<64>, rgrid, dim3(kBlock), 0, st, a);
         else
-            hipLaunchKernelGGL(k_dense_logits_mfma<128>, grid, dim3(kBlock), 0, st, a);
+            hipLaunchKernelGGL(k_dense_kpass<128>, rgrid, dim3(kBlock), 0, st, a);
     } else {
         if (D == 64)
             hipLaunchKernelGGL(k_dense_logits_f32<64>, grid, dim3(kBlock), 0, st, a);
