@@ -519,7 +519,8 @@ def cpu_baseline(w, select, Q_host, seconds_budget=12.0):
 ENGINE_KERNELS = {
     "union": "k_un_init, k_un_small (first steps), then per level k_un_score + k_un_cut + k_un_expand; "
              "below 16 heads per KV head the hand-over in k_un_cut and k_ls_score + k_ls_cut for the last two levels",
-    "level-sync": "k_ls_init, then per level k_ls_score + k_ls_cut",
+    "level-sync": "k_ls_init, then per level k_ls_score + k_ls_cut; for decode with at most 16 heads "
+                  "per KV head the first levels from one dense table (k_top_score + k_top_cut)",
     "persistent": "one k_search_decode launch",
 }
 

@@ -256,7 +256,7 @@ def test_search_engine_resolution(Z):
     big = _handle(Z, batch=4, kv_heads=1, group=32)
     assert Z.zha_search_engine(big, Z.make_select("topp", 0.9, max_blocks=64, engine="union")) is None
     eight = _handle(Z, batch=4, kv_heads=2, group=8)     # 64 decode walks, 8 heads per KV head
-    assert Z.zha_search_engine(eight, topp) == "union"
+    assert Z.zha_search_engine(eight, topp) == "level-sync"          # with its dense top table
     assert Z.zha_search_engine(eight, topk) == "persistent"
     four = _handle(Z, batch=8, kv_heads=2, group=4)      # 64 walks, 4 heads per KV head
     assert Z.zha_search_engine(four, topp) == "level-sync"

@@ -297,15 +297,13 @@ int64_t visited_words_per_pair(const zha_tree *t) {
 
 // The engine a search runs on: the caller's choice, or for AUTO the one
 // that measured fastest for the shape (block for prefill blocks, union when
-// 16 query heads share a KV head in decode, level-synchronous for wide top-p
-// batches, else persistent).
+// 16 query heads share a KV head in decode, level-synchronous -- with its
+// dense top table -- for other wide top-p batches, else persistent).
 int resolve_engine(const zha_tree *t, const zha_select *sel, int32_t qph) {
     if (sel->engine != ZHA_ENGINE_AUTO) return sel->engine;
     const int64_t walks = walks_of(&t->geom, qph);
     if (qph > 1) return ZHA_ENGINE_BLOCK;
     if (qph == 1 && t->geom.group_size == 16 && walks >= 64) return ZHA_ENGINE_UNION;
-    if (qph == 1 && t->geom.group_size >= 8 && t->geom.group_size <= 16 && sel->mode == ZHA_TOPP && walks >= 64)
-        return ZHA_ENGINE_UNION;
     if (sel->mode == ZHA_TOPP && walks >= 64) return ZHA_ENGINE_LEVEL_SYNC;
     return ZHA_ENGINE_PERSISTENT;
 }
@@ -420,6 +418,51 @@ int64_t fill_search(const zha_tree *t, int64_t n_tok, const void *q, int32_t qph
             a.small_steps = s + 1;
         }
     }
+    // level-synchronous decode engine: its first steps run from one dense
+    // score table of the top levels (all their nodes, every head of the
+    // pair) when those levels are small -- at most kTopRowsMax nodes per pair
+    // -- and a step's candidates cover most of its level (always under
+    // top-p; under top-K when K_t * c reaches half the level below)
+    a.top_steps = 0;
+    a.top_lo = g.levels + 1;
+    a.top_rows = 0;
+    a.top_lds = 0;
+    if (engine == ZHA_ENGINE_LEVEL_SYNC && qph == 1 && g.group_size <= 16) {
+        int64_t rows = 0;
+        for (int s = 0; s < g.levels && s < ZHA_MAX_STEPS; ++s) {
+            const int l = g.levels - s;
+            if (rows + t->level_cap[l] > kTopRowsMax || rows + t->level_cap[l] > a.cand_cap) break;
+            if (sel->mode == ZHA_TOPK && s > 0 && 2 * int64_t(a.k[s - 1]) * g.chunk < t->level_cap[l]) break;
+            rows += t->level_cap[l];
+            a.top_steps = s + 1;
+            a.top_lo = l;
+        }
+        if (a.top_steps > 0) {
+            int64_t off = 0;
+            for (int l = 0; l <= ZHA_MAX_LEVELS + 1; ++l) a.top_off[l] = 0;
+            for (int l = a.top_lo; l <= g.levels; ++l) {
+                a.top_off[l] = off;
+                off += t->level_cap[l];
+            }
+            a.top_rows = off;
+            // the top steps' lists (and the one they hand over) fit in LDS
+            // when none can exceed kTopList candidates: step s meets at most
+            // the level L - s of the top chain plus, for the parentless roots
+            // of each lower level l, their level-(l - s) descendants
+            a.top_lds = 1;
+            for (int st = 0; st <= a.top_steps; ++st) {
+                int64_t cs = 1;
+                for (int i = 0; i < st; ++i) cs *= g.chunk;
+                int64_t bound = g.levels - st >= 1 ? a.nl[g.levels - st] : 0;
+                for (int l = 1; l < g.levels; ++l) {
+                    if (l - st < 1) continue;
+                    const int64_t par = a.nl[l] - int64_t(g.chunk) * a.nl[l + 1];
+                    bound += std::min(a.nl[l - st], par * cs);
+                }
+                if (bound > kTopList) a.top_lds = 0;
+            }
+        }
+    }
     // union engine with fewer than 16 heads per KV head: the heads' lists
     // overlap less, and on the last two steps (the widest) the
     // level-synchronous engine's per-walk scoring is faster; hand over there
@@ -441,6 +484,8 @@ zha_status do_search(const zha_tree *t, const void *q, int32_t qph, const zha_se
                                    ws, engine, a);
     if (engine == ZHA_ENGINE_BLOCK)
         return hip_status(launch_block(a, g.head_dim, g.num_refs, g.dtype, g.summary_dtype, static_cast<int>(n0), st));
+    if (engine == ZHA_ENGINE_LEVEL_SYNC && a.top_steps > 0)
+        return hip_status(launch_top(a, g.head_dim, g.num_refs, g.dtype, g.summary_dtype, st));
     if (engine == ZHA_ENGINE_UNION)
         return hip_status(launch_union(a, g.head_dim, g.num_refs, g.dtype, g.summary_dtype, static_cast<int>(n0), st));
     return hip_status(launch_search(a, g.head_dim, g.num_refs, g.dtype, g.summary_dtype, engine, static_cast<int>(n0), st));

@@ -26,6 +26,9 @@ constexpr int kUaSlice = 16384;      // union attention: level-1 blocks per mask
 constexpr int kUaSortMax = 16384;    // union attention, prefill: walks sorted together (one workgroup)
 constexpr int kXcds = 8;             // MI355X: accelerator dies (XCDs), each with its own L2
 
+constexpr int kTopRowsMax = 2048;   // level-synchronous engine: nodes per pair of the dense top table
+constexpr int kTopList = 4096;      // candidates a top step keeps in LDS
+
 // Which slower or rarer code paths a walk took (bits 16.. of the flags a walk
 // carries through the engines; finish_walk moves them to zha_walk_stats.paths
 // as ZHA_PATH_*, and only the low bits reach the status word).
@@ -120,6 +123,12 @@ struct SearchArgs {
     int64_t bin_lvl[ZHA_MAX_LEVELS + 2];   // first bin of level l within a pair
     int32_t pcap;                          // parents a walk keeps per step
     int64_t n_roots;                       // roots before clamping to cand_cap
+    int32_t top_steps;                     // level-synchronous engine: first steps cut from a dense
+                                           // score table of the top levels (0: none)
+    int32_t top_lo;                        // lowest level of that table (levels top_lo .. L)
+    int64_t top_off[ZHA_MAX_LEVELS + 2];   // row of node (l, 0) in a pair's table
+    int64_t top_rows;                      // table rows per pair (scores at [pair][row][gp], in u_score)
+    int32_t top_lds;                       // 1: the top steps' lists fit in LDS (kTopList entries)
     int32_t small_steps;                   // union engine: first steps done by one workgroup per pair
     int32_t ls_from;                       // union engine: steps from here run level-synchronously (0: none)
     int32_t pairs;
@@ -225,6 +234,7 @@ hipError_t launch_search(const SearchArgs &a, int D, int R, int dtype, int sdtyp
                          hipStream_t st);
 hipError_t launch_union(const SearchArgs &a, int D, int R, int dtype, int sdtype, int n0, hipStream_t st);
 hipError_t launch_ls_from(const SearchArgs &a, int D, int R, int dtype, int sdtype, int t0, hipStream_t st);
+hipError_t launch_top(const SearchArgs &a, int D, int R, int dtype, int sdtype, hipStream_t st);
 hipError_t launch_block(const SearchArgs &a, int D, int R, int dtype, int sdtype, int n0, hipStream_t st);
 hipError_t launch_attn(const AttnArgs &a, int D, int dtype, hipStream_t st);
 hipError_t launch_attn_union(const AttnArgs &a, int D, hipStream_t st);

@@ -162,9 +162,9 @@ __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair,
 // level-1 and of higher nodes opened.
 __device__ inline void open_cut(const SearchArgs &a, int n, const uint32_t *cur, const float *sc,
                          bool forced, unsigned long long tau, uint32_t *nxt, int32_t *selw,
-                         int64_t sel_n, uint32_t &ta, uint32_t &tb, SelectShared &sh) {
+                         int64_t sel_n, uint32_t &ta, uint32_t &tb, SelectShared &sh, int nxt_cap = -1) {
     const int tid = threadIdx.x;
-    const int c = a.chunk, log2c = a.log2c, cap = a.cand_cap;
+    const int c = a.chunk, log2c = a.log2c, cap = nxt_cap >= 0 ? nxt_cap : a.cand_cap;
     const int per = (n + kThreads - 1) / kThreads;
     const int i0 = tid * per;
     const int i1 = min(n, i0 + per);

@@ -528,57 +528,6 @@ __device__ __forceinline__ void cut_head(const SearchArgs &a, int t, int w, Sele
     }
 }
 
-// Wavefront, at most 64 candidates, one per lane (key 0 and weight 0 on the
-// other lanes): the cut key of cut_tau -- the rank key of the candidate at
-// which the weight summed in decreasing key order first reaches what the
-// step needs (weights and need exactly as there) -- by a bitonic sort of the
-// (key, weight) pairs across the lanes (keys are distinct: they hold the
-// span start), an inclusive scan of the weights and a ballot.
-__device__ unsigned long long lane_tau(const SearchArgs &a, bool in, float v, uint32_t id, float mx, int n, int kt) {
-    const int lane = threadIdx.x & 63;
-    const bool by_mass = (a.mode == ZHA_TOPP) && (a.p > 0.f);
-    const bool flat = !(mx > -INFINITY);   // every score -inf: equal masses
-    uint32_t wt = 0u;
-    if (in) wt = by_mass ? __float2uint_rn((flat ? 1.f : expf(v - mx)) * kMassScale) : 1u;
-    unsigned long long key = in ? rank_key(v, id, a.log2c) : 0ull;
-    unsigned long long need;
-    if (by_mass) {
-        unsigned long long z = wt;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
-        const double tq = ceil(static_cast<double>(a.p) * static_cast<double>(z));
-        need = static_cast<unsigned long long>(tq);
-        if (need < 1) need = 1;
-        if (need > z) need = z;
-    } else {
-        const int m = (a.mode == ZHA_TOPK) ? (kt < n ? kt : n) : 1;
-        need = static_cast<unsigned long long>(m < 1 ? 1 : m);
-    }
-    // descending bitonic sort over the 64 lanes
-#pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const unsigned long long ok = __shfl_xor(key, j, 64);
-            const uint32_t ow = static_cast<uint32_t>(__shfl_xor(static_cast<int>(wt), j, 64));
-            const bool lower = (lane & j) == 0, desc = (lane & k) == 0;
-            const bool take = (lower == desc) ? (ok > key) : (ok < key);
-            if (take) {
-                key = ok;
-                wt = ow;
-            }
-        }
-    }
-    unsigned long long incl = wt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const unsigned long long o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-    }
-    const unsigned long long hit = __ballot(lane < n && incl >= need);
-    const int first = hit ? (__ffsll(static_cast<long long>(hit)) - 1) : (n - 1);
-    return __shfl(key, first, 64);
-}
 
 // An open mask: set by atomics, so read past L1 (a kernel that cuts and
 // expands in one workgroup may hold a stale line of it there).
