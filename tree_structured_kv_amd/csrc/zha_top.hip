@@ -78,10 +78,63 @@ __device__ __forceinline__ float score_one(const SearchArgs &a, int64_t pair, co
 
 }  // namespace
 
+// Lane exchange with lane ^ O inside 32-lane groups.
+template <int O>
+__device__ __forceinline__ float xchg(float v) {
+    if constexpr (O == 1)
+        return dpp<kDppXor1>(v);
+    else if constexpr (O == 2)
+        return dpp<kDppXor2>(v);
+    else
+        return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (O << 10) | 0x1F));
+}
+
+// One level of a transposed sum: slots [0, M/2) keep their value plus the
+// partner's slot j + M/2 (which holds the same head there); a single slot
+// is summed plainly.
+template <int O, int M, int GP>
+__device__ __forceinline__ void sum_level(float (&v)[GP]) {
+    if constexpr (M >= 2) {
+#pragma unroll
+        for (int j = 0; j < M / 2; ++j) v[j] += xchg<O>(v[j + M / 2]);
+    } else {
+        v[0] += xchg<O>(v[0]);
+    }
+}
+
+// GP per-head partial dot products per lane summed over aligned groups of
+// LPR lanes, the groups paired as in group_sum (1, 2, 4, 8, 16 lanes apart,
+// so every head's sum is the same tree of additions, bit for bit), but
+// with each level moving only half the slots still held: slot j of lane l
+// holds head j ^ lane_head(l), and at the end slot 0 holds head lane_head(l).
+template <int LPR, int GP>
+__device__ __forceinline__ float transposed_sum(float (&v)[GP]) {
+    static_assert(GP <= LPR && LPR <= 32, "the heads fit the lanes of a row");
+    sum_level<1, GP>(v);
+    sum_level<2, (GP >= 2 ? GP / 2 : 1)>(v);
+    if constexpr (LPR >= 8) sum_level<4, (GP >= 4 ? GP / 4 : 1)>(v);
+    if constexpr (LPR >= 16) sum_level<8, (GP >= 8 ? GP / 8 : 1)>(v);
+    if constexpr (LPR >= 32) sum_level<16, (GP >= 16 ? GP / 16 : 1)>(v);
+    return v[0];
+}
+
+// The head whose sum a lane ends with: lane bit k selects the upper half at
+// level k.
+template <int GP>
+__device__ __forceinline__ int lane_head(int lane) {
+    int h = 0;
+#pragma unroll
+    for (int k = 0, m = GP / 2; m >= 1; ++k, m >>= 1)
+        if (lane & (1 << k)) h += m;
+    return h;
+}
+
 // Every live node of levels top_lo .. L, every query head of its pair:
 // grid (workgroups per pair, pairs); a wavefront takes kTopU nodes at a
 // time, reads each record once (16-byte loads) and scores it for the GP
-// query heads held in registers.  Lane h writes head h's score.
+// query heads held in registers (slot j of a lane holds the query of head
+// j ^ lane_head, as transposed_sum expects).  The lanes ending with head h
+// in the first reference group write its score.
 template <int D, int R, typename QT, typename ST, int GP>
 __global__ __launch_bounds__(kTopThreads) void k_top_score(SearchArgs a) {
     constexpr int EPL = row_epl<D, ST>();
@@ -94,14 +147,16 @@ __global__ __launch_bounds__(kTopThreads) void k_top_score(SearchArgs a) {
     const int64_t pair = blockIdx.y;
     const int G = a.group;
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x <= ZHA_MAX_STEPS) a.tile_count[threadIdx.x] = 0;
+    const int my_head = lane_head<GP>(sub);
     // the pair's query heads: walks pair*G .. pair*G + G - 1 (decode)
     float qv[GP][EPL];
 #pragma unroll
-    for (int h = 0; h < GP; ++h) {
+    for (int j = 0; j < GP; ++j) {
+        const int h = j ^ my_head;
         const int hh = h < G ? h : 0;
         const QT *qp = static_cast<const QT *>(a.q) + (pair * G + hh) * D + EPL * sub;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) qv[h][e] = Elem<QT>::load(qp, e);
+        for (int e = 0; e < EPL; ++e) qv[j][e] = Elem<QT>::load(qp, e);
     }
     // live nodes of the table, level by level from the top
     int64_t live = 0;
@@ -109,6 +164,7 @@ __global__ __launch_bounds__(kTopThreads) void k_top_score(SearchArgs a) {
     const int gp = (G + 3) & ~3;
     float *tab = a.u_score + pair * a.top_rows * gp;
     const float s = a.sharpness;
+    const bool writer = rsub == 0 && sub < GP && my_head < G;
     for (int64_t x0 = (static_cast<int64_t>(blockIdx.x) * kW + wave) * kTopU; x0 < live;
          x0 += static_cast<int64_t>(gridDim.x) * kW * kTopU) {
         float kv[kTopU][NL][EPL];
@@ -143,25 +199,28 @@ __global__ __launch_bounds__(kTopThreads) void k_top_score(SearchArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < kTopU; ++u) {
-            float mine = -INFINITY;
+            float best = -INFINITY;
 #pragma unroll
-            for (int h = 0; h < GP; ++h) {
-                float best = -INFINITY;
+            for (int i = 0; i < NL; ++i) {
+                float pd[GP];
 #pragma unroll
-                for (int i = 0; i < NL; ++i) {
-                    float d = kv[u][i][0] * qv[h][0];
+                for (int j = 0; j < GP; ++j) {
+                    float d = kv[u][i][0] * qv[j][0];
 #pragma unroll
-                    for (int e = 1; e < EPL; ++e) d = fmaf(kv[u][i][e], qv[h][e], d);
-                    d = group_sum<LPR>(d);
-                    best = fmaxf(best, fmaf(s, d, bv[u][i]));
+                    for (int e = 1; e < EPL; ++e) d = fmaf(kv[u][i][e], qv[j][e], d);
+                    pd[j] = d;
                 }
-                float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(best), 0));
-#pragma unroll
-                for (int gq = 1; gq < RPL; ++gq)
-                    m = fmaxf(m, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(best), gq * LPR)));
-                if (lane == h) mine = m;
+                const float d = transposed_sum<LPR, GP>(pd);
+                best = fmaxf(best, fmaf(s, d, bv[u][i]));
             }
-            if (row[u] >= 0 && lane < G) tab[row[u] * gp + lane] = mine;
+            // max over the RPL reference groups (lanes LPR apart)
+            if constexpr (RPL >= 4)
+                best = fmaxf(best, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(best), 0x401F)));
+            if constexpr (RPL >= 2) best = fmaxf(best, __shfl_xor(best, 32, 64));
+            float m = best;
+            if (m != m) m = -INFINITY;
+            if (m == 0.f) m = 0.f;
+            if (row[u] >= 0 && writer) tab[row[u] * gp + my_head] = m;
         }
     }
 }
