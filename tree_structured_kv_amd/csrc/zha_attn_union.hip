@@ -26,7 +26,7 @@
 //                last workgroup also the raw tail, which every walk attends);
 //                a marked chunk's blocks are compacted in LDS; each wavefront
 //                takes 16-key tiles, computes the logits of all columns at
-//                once with bf16 16x16x16 matrix products S^T = K Q^T (rows =
+//                once with bf16 16x16x32 matrix products S^T = K Q^T (rows =
 //                keys, columns = walks), masks the columns that did not
 //                select a key's block, keeps an online softmax per column in
 //                fp32 and accumulates O^T += V^T P^T with bf16 products (V
@@ -47,8 +47,9 @@ namespace zha {
 
 namespace {
 
-typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kUaWaves = 4;
 constexpr int kUaBatch = 1024;         // selected blocks gathered in LDS before their tiles run
@@ -61,14 +62,14 @@ __device__ __forceinline__ short4_t pick4(uint32_t w0, uint32_t w1, uint32_t w2,
     return __builtin_bit_cast(short4_t, make_uint2(lo, hi));
 }
 
-__device__ __forceinline__ short4_t pk4(uint32_t lo, uint32_t hi) {
-    short4_t r;
-    r[0] = static_cast<short>(lo & 0xffffu);
-    r[1] = static_cast<short>(lo >> 16);
-    r[2] = static_cast<short>(hi & 0xffffu);
-    r[3] = static_cast<short>(hi >> 16);
-    return r;
-}
+__device__ __forceinline__ bf16x8_t as_bf8(gu4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// The running maximum of a column moves only when the column's logits rise
+// more than this far above it (base-2 units): weights stay below 2^kLazy and
+// the running sums are rescaled rarely (exact: every sum and the final
+// normalisation use the same reference).
+constexpr float kLazy = 8.f;
+
 
 // The walks of a pair are consecutive: its G query heads, each with its
 // q_per_head query rows.
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(T) void k_ua_build(AttnArgs a) {
 
 template <int D>
 __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
-    constexpr int DS = D / 16;            // bf16 16x16x16 steps of a logit
+    constexpr int DS = D / 32;            // bf16 16x16x32 steps of a logit
     constexpr int DT = D / 16;            // row tiles of O^T: row i of tile q is d = DT*i + q
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
@@ -307,19 +308,20 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
     const bf16_t *kc = static_cast<const bf16_t *>(a.k) + p * a.max_tokens * D;
     const bf16_t *vc = static_cast<const bf16_t *>(a.v) + p * a.max_tokens * D;
     // B operand of S^T: lane (column col, group grp) holds the query of
-    // column col at elements 32*(st/2) + 8*grp + 4*(st%2) .. +3 (zero past
-    // the group's walks)
+    // column col at elements 32*st + 8*grp .. +7 (zero past the group's
+    // walks); the key rows of the A operand take the same elements (a dot
+    // product may sum its terms in any order, so lane group grp may own any
+    // slice of the head dimension as long as both operands agree)
     const int64_t qw = ua_walk(a, g, col);
     const bool hv = qw >= 0;
-    short4_t qb[DS];
+    bf16x8_t qb[DS];
     {
         const bf16_t *qr = static_cast<const bf16_t *>(a.q) + (hv ? qw : 0) * D + 8 * grp;
 #pragma unroll
-        for (int m = 0; m < DS / 2; ++m) {
-            gu4_t v = gload_u4(qr + 32 * m);
+        for (int st = 0; st < DS; ++st) {
+            gu4_t v = gload_u4(qr + 32 * st);
             if (!hv) v = gu4_t{0u, 0u, 0u, 0u};
-            qb[2 * m] = pk4(v.x, v.y);
-            qb[2 * m + 1] = pk4(v.z, v.w);
+            qb[st] = as_bf8(v);
         }
     }
     // online softmax state of column col, kept across the workgroup's chunks
@@ -341,22 +343,18 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
         };
         const int ntiles = (nkeys + 15) / 16;
         struct Tile {
-            short4_t kb[DS];                  // A operand of S^T
+            bf16x8_t kb[DS];                  // A operand of S^T
             uint32_t vw[4][DT / 2];           // V rows for O^T += V^T P^T
         };
-        // key rows of tile t: for S^T, key kbase + col (same element order
-        // as qb); for the second product at step e, key kbase + 4*grp + e,
+        // key rows of tile t: for S^T, key kbase + col (same elements as
+        // qb); for the second product at step e, key kbase + 4*grp + e,
         // elements DT*col .. DT*col + DT - 1
         auto load_tile = [&](int t, Tile &T) {
             const int kbase = t * 16;
             const int ka = kbase + col;
             const bf16_t *kr = kc + token_of(ka < nkeys ? ka : kbase) * D + 8 * grp;
 #pragma unroll
-            for (int m = 0; m < DS / 2; ++m) {
-                const gu4_t v = gload_u4(kr + 32 * m);
-                T.kb[2 * m] = pk4(v.x, v.y);
-                T.kb[2 * m + 1] = pk4(v.z, v.w);
-            }
+            for (int st = 0; st < DS; ++st) T.kb[st] = as_bf8(gload_u4(kr + 32 * st));
             // the lane group's four keys kq .. kq+3 are consecutive rows of
             // one block (blocks hold at least four keys) or of the tail, so
             // one lookup serves all four (keys past the end reuse the first
@@ -379,7 +377,7 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
             const int kbase = t * 16;
             float4_t sa = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int st = 0; st < DS; ++st) sa = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(T.kb[st], qb[st], sa, 0, 0, 0);
+            for (int st = 0; st < DS; ++st) sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T.kb[st], qb[st], sa, 0, 0, 0);
             // logits of column col for keys kbase + 4*grp + e; masked: -inf
             float x[4], tmax = -INFINITY;
             const int kq = kbase + 4 * grp;
@@ -392,25 +390,26 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
             }
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            const float mn = fmaxf(m_run, tmax);
-            const float corr = (m_run > -INFINITY) ? __builtin_amdgcn_exp2f(m_run - mn) : 0.f;
-            float pe[4], psum = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pe[e] = (x[e] > -INFINITY) ? __builtin_amdgcn_exp2f(x[e] - mn) : 0.f;
-                psum += pe[e];
-            }
-            psum += __shfl_xor(psum, 16, 64);
-            psum += __shfl_xor(psum, 32, 64);
-            l_run = l_run * corr + psum;
-            m_run = mn;
-            // the running sums are rescaled only when some column's maximum moved
-            if (__ballot(corr != 1.f) != 0ull) {
+            const float mt = fmaxf(m_run, tmax);
+            const bool move = mt > m_run + kLazy;
+            if (__ballot(move) != 0ull) {
+                const float corr = move ? ((m_run > -INFINITY) ? __builtin_amdgcn_exp2f(m_run - mt) : 0.f) : 1.f;
+                if (move) m_run = mt;
+                l_run *= corr;
 #pragma unroll
                 for (int q = 0; q < DT; ++q)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc[q][e] *= corr;
             }
+            float pe[4], psum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pe[e] = (x[e] > -INFINITY) ? __builtin_amdgcn_exp2f(x[e] - m_run) : 0.f;
+                psum += pe[e];
+            }
+            psum += __shfl_xor(psum, 16, 64);
+            psum += __shfl_xor(psum, 32, 64);
+            l_run += psum;
             // O^T += V^T P^T as bf16 16x16x16 products: the probabilities of
             // keys 4*grp .. 4*grp+3 are already this lane's B operand; each is
             // split into two bf16 parts, hi (p truncated) and lo (the exact
