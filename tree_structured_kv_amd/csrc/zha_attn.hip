@@ -36,6 +36,26 @@ __device__ __forceinline__ short4_t pick4(uint32_t w0, uint32_t w1, uint32_t w2,
     return __builtin_bit_cast(short4_t, make_uint2(lo, hi));
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// Elements q of eight 32-bit words w[0..7] (each two bf16: q = 0 low half,
+// 1 high half) packed in order as a 16x16x32 operand (four v_perm_b32).
+__device__ __forceinline__ bf16x8_t pick8(const uint32_t (&w)[8], int q) {
+    const uint32_t sel = q ? 0x07060302u : 0x05040100u;
+    uint4 r;
+    r.x = __builtin_amdgcn_perm(w[1], w[0], sel);
+    r.y = __builtin_amdgcn_perm(w[3], w[2], sel);
+    r.z = __builtin_amdgcn_perm(w[5], w[4], sel);
+    r.w = __builtin_amdgcn_perm(w[7], w[6], sel);
+    return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// A query's running maximum moves only when its logits rise more than this
+// far above it (base-2 units): weights stay below 2^kLazy and the running
+// sums are rescaled rarely (exact: every sum and the final normalisation use
+// the same reference).
+constexpr float kLazy = 8.f;
+
 constexpr int kWaves = kBlock / 64;
 
 // Two online-softmax states with maxima in base-2 units.
@@ -255,10 +275,10 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
 // elements DT*col .. of each of its keys' V rows once for all tiles.
 // Online softmax in fp32.
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
+__global__ __launch_bounds__(256, 3) void k_attn_block(AttnArgs a) {
     constexpr int KT = 64;                 // keys per tile
     constexpr int KP = D + 8;              // sK / sV row pitch (elements)
-    constexpr int DS = D / 16;             // bf16 product steps (16 elements each)
+    constexpr int DS = D / 32;             // bf16 16x16x32 steps of a logit
     constexpr int DT = D / 16;             // output row tiles of O^T
     constexpr int VW = DT / 2;             // 32-bit words of a lane's V slice
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -276,12 +296,14 @@ __global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
     const int q0 = qt * 64 + wave * 16;                    // this wavefront's first query
     const int myq = q0 + col;                              // this lane's query (column)
     const int64_t walk = static_cast<int64_t>(hq) * T + (myq < T ? myq : T - 1);
-    // B operand of S^T: Q^T, lane (query col, group grp) holds d = 16*k + 4*grp .. +3
-    short4_t qb[DS];
+    // B operand of S^T: Q^T, lane (query col, group grp) holds d = 32*k +
+    // 8*grp .. +7 (the key rows of the A operand take the same elements: a
+    // dot product may sum its terms in any order)
+    bf16x8_t qb[DS];
     {
-        const bf16_t *qp = static_cast<const bf16_t *>(a.q) + walk * D + 4 * grp;
+        const bf16_t *qp = static_cast<const bf16_t *>(a.q) + walk * D + 8 * grp;
 #pragma unroll
-        for (int k = 0; k < DS; ++k) qb[k] = *reinterpret_cast<const short4_t *>(qp + 16 * k);
+        for (int k = 0; k < DS; ++k) qb[k] = *reinterpret_cast<const bf16x8_t *>(qp + 32 * k);
     }
     // logits in base-2 units (one hardware exp2 per weight); the partial
     // leaves in natural units
@@ -312,11 +334,11 @@ __global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
 #pragma unroll
         for (int sub = 0; sub < 4; ++sub) {
             float4_t st = {0.f, 0.f, 0.f, 0.f};
-            const bf16_t *kr = sK + (16 * sub + col) * KP + 4 * grp;
+            const bf16_t *kr = sK + (16 * sub + col) * KP + 8 * grp;
 #pragma unroll
             for (int k = 0; k < DS; ++k) {
-                const short4_t ka = *reinterpret_cast<const short4_t *>(kr + 16 * k);
-                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, qb[k], st, 0, 0, 0);
+                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t *>(kr + 32 * k);
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[k], st, 0, 0, 0);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -329,50 +351,58 @@ __global__ __launch_bounds__(256) void k_attn_block(AttnArgs a) {
         // row (query) max over the 4 lane groups holding this column
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float mn = fmaxf(m, tmax);
-        const float corr = (m > -INFINITY) ? __builtin_amdgcn_exp2f(m - mn) : 0.f;
-        float psum = 0.f;
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float pe = (p[sub][e] > -INFINITY) ? __builtin_amdgcn_exp2f(p[sub][e] - mn) : 0.f;
-                p[sub][e] = pe;
-                psum += pe;
-            }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
-        l = l * corr + psum;
-        m = mn;
-        // the running sums are rescaled only when some query's maximum moved
-        if (__ballot(corr != 1.f) != 0ull) {
+        const float mt = fmaxf(m, tmax);
+        const bool move = mt > m + kLazy;
+        if (__ballot(move) != 0ull) {
+            const float corr = move ? ((m > -INFINITY) ? __builtin_amdgcn_exp2f(m - mt) : 0.f) : 1.f;
+            if (move) m = mt;
+            l *= corr;
 #pragma unroll
             for (int i = 0; i < DT; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[i][e] *= corr;
         }
-        // O^T += V^T P^T
+        float psum = 0.f;
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub) {
-            short4_t ph, pl;
+        for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t u = __float_as_uint(p[sub][e]);
-                ph[e] = static_cast<short>(u >> 16);
-                pl[e] = __builtin_bit_cast(short, static_cast<__bf16>(p[sub][e] - __uint_as_float(u & 0xffff0000u)));
+                const float pe = (p[sub][e] > -INFINITY) ? __builtin_amdgcn_exp2f(p[sub][e] - m) : 0.f;
+                p[sub][e] = pe;
+                psum += pe;
             }
-            uint32_t vw[4][VW];
+        psum += __shfl_xor(psum, 16, 64);
+        psum += __shfl_xor(psum, 32, 64);
+        l += psum;
+        // O^T += V^T P^T as bf16 16x16x32 products over 32 keys at a time:
+        // the lane's eight K slots are its own keys 16*sub + 4*grp + e of
+        // slices sub = 2h, 2h + 1 (any assignment of keys to slots sums the
+        // same terms), so its probabilities are already its B operand; each
+        // is split into two bf16 parts, hi (p truncated) and lo (the exact
+        // remainder, rounded), so the fp32 sums keep fp32 accuracy
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t *vr = reinterpret_cast<const uint32_t *>(sV + (16 * sub + 4 * grp + e) * KP + DT * col);
+        for (int h = 0; h < 2; ++h) {
+            bf16x8_t ph, pl;
 #pragma unroll
-                for (int j = 0; j < VW; ++j) vw[e][j] = vr[j];
+            for (int e = 0; e < 8; ++e) {
+                const float pv = p[2 * h + (e >> 2)][e & 3];
+                const uint32_t u = __float_as_uint(pv);
+                ph[e] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(u >> 16));
+                pl[e] = static_cast<__bf16>(pv - __uint_as_float(u & 0xffff0000u));
+            }
+            uint32_t vw[VW][8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int key = 16 * (2 * h + (e >> 2)) + 4 * grp + (e & 3);
+                const uint32_t *vr = reinterpret_cast<const uint32_t *>(sV + key * KP + DT * col);
+#pragma unroll
+                for (int j = 0; j < VW; ++j) vw[j][e] = vr[j];
             }
 #pragma unroll
             for (int q = 0; q < DT; ++q) {
-                const short4_t va = pick4(vw[0][q >> 1], vw[1][q >> 1], vw[2][q >> 1], vw[3][q >> 1], q & 1);
-                acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, acc[q], 0, 0, 0);
-                acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc[q], 0, 0, 0);
+                const bf16x8_t va = pick8(vw[q >> 1], q & 1);
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, acc[q], 0, 0, 0);
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, acc[q], 0, 0, 0);
             }
         }
     }

@@ -40,6 +40,8 @@ namespace {
 
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
 
 // An fp32 value as the exact sum of three bf16 values: hi and mid keep the
 // top 8 significant bits of x and of x - hi (truncation leaves an exact
@@ -134,12 +136,10 @@ __global__ __launch_bounds__(kBkThreads) void k_bk_init(SearchArgs a, int n0) {
 // (NPG = 16/R nodes x R references each); it loads a column tile's records
 // once and runs every row tile of the unit against them.  bf16 queries: each
 // fp32 key element is split into three bf16 parts whose sum is exact
-// (split3; one part when the keys are stored in bf16) and every 16-element
-// slice of the dot product is three bf16 16x16x16 products (exact bf16
-// products summed in fp32, as with fp32 products, at a fifth of their
-// matrix-core time); fp32 queries take fp32 16x16x4 products.  Lane group q
-// = lane/16 holds elements 16*j + 4*q .. 16*j + 4*q + 3 of slice j of the
-// query and of the reference row.
+// (split3; one part when the keys are stored in bf16) and every 32-element
+// slice of the dot product is three bf16 16x16x32 products (exact bf16
+// products summed in fp32, as with fp32 products, in far fewer matrix-core
+// cycles); fp32 queries take fp32 16x16x4 products.
 template <int D, int R, typename QT, typename ST>
 __global__ __launch_bounds__(kBkThreads) void k_bk_score(SearchArgs a, int t, int n0) {
     constexpr int NPG = 16 / R;
@@ -225,32 +225,40 @@ __global__ __launch_bounds__(kBkThreads) void k_bk_score(SearchArgs a, int t, in
             const uint32_t id = (t == 0) ? a.b_roots[ci] : child_id(parent, ci, c);
             const int lvl = static_cast<int>(id >> kLevelShift);
             const int64_t node = static_cast<int64_t>(pair) * s_cap[lvl] + (id & kIndexMask);
-            const ST *kp = reinterpret_cast<const ST *>(s_kap[lvl]) + node * (R * D) + (col % R) * D + 4 * grp;
-            float kb[KS];
-#pragma unroll
-            for (int k = 0; k < KS; k += 4) {
-                GVec4<ST>::load(kp + 4 * k, &kb[k]);
-            }
-            const float bias = gload_f(s_bet[lvl] + node * R + (col % R));
-            // bf16 queries: the key slices as three bf16 operands (B: rows =
-            // elements 4*grp .. of slice j, column col)
-            constexpr int NS = D / 16;
+            // bf16 queries: each 32-element slice j of the dot product is
+            // NP bf16 16x16x32 products (the key as three exact bf16 parts;
+            // one when the keys are stored in bf16), lane group grp taking
+            // elements 32*j + 8*grp .. +7 of the query row and of the
+            // reference row; fp32 queries: fp32 16x16x4 products, lane group
+            // grp taking elements 16*j + 4*grp .. +3
+            constexpr int NJ = D / 32;
             constexpr int NP = (sizeof(ST) == 2) ? 1 : 3;     // bf16 keys are their own hi part
-            short4_t kbf[NP][NS];
+            const ST *krow = reinterpret_cast<const ST *>(s_kap[lvl]) + node * (R * D) + (col % R) * D;
+            float kb[KS];
+            short8_t kbf[NP][NJ];
             if constexpr (sizeof(QT) == 2) {
 #pragma unroll
-                for (int j = 0; j < NS; ++j)
+                for (int j = 0; j < NJ; ++j) {
+                    GVec4<ST>::load(krow + 32 * j + 8 * grp, &kb[8 * j]);
+                    GVec4<ST>::load(krow + 32 * j + 8 * grp + 4, &kb[8 * j + 4]);
+                }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
                         short hi, mid, lo;
-                        split3(kb[4 * j + i], hi, mid, lo);
+                        split3(kb[8 * j + i], hi, mid, lo);
                         kbf[0][j][i] = hi;
                         if constexpr (NP == 3) {
                             kbf[1][j][i] = mid;
                             kbf[2][j][i] = lo;
                         }
                     }
+            } else {
+#pragma unroll
+                for (int k = 0; k < KS; k += 4) GVec4<ST>::load(krow + 4 * grp + 4 * k, &kb[k]);
             }
+            const float bias = gload_f(s_bet[lvl] + node * R + (col % R));
             if (mark && (col % R) == 0 && grp == 0 && ct * NPG + col / R < nchild) {
                 const int64_t bitn = a.node_off[lvl] + (id & kIndexMask);
                 atomicOr(a.visited + static_cast<int64_t>(pair) * a.vis_words + (bitn >> 5), 1u << (bitn & 31));
@@ -260,14 +268,16 @@ __global__ __launch_bounds__(kBkThreads) void k_bk_score(SearchArgs a, int t, in
                 const QT *qr = s_q + (rt * 16 + col) * QP + 4 * grp;
                 float4_t acc = {0.f, 0.f, 0.f, 0.f};
                 if constexpr (sizeof(QT) == 2) {
-                    short4_t qa[NS];
+                    const QT *qr8 = s_q + (rt * 16 + col) * QP + 8 * grp;
+                    bf16x8_t qa[NJ];
 #pragma unroll
-                    for (int j = 0; j < NS; ++j) qa[j] = *reinterpret_cast<const short4_t *>(qr + 16 * j);
+                    for (int j = 0; j < NJ; ++j) qa[j] = *reinterpret_cast<const bf16x8_t *>(qr8 + 32 * j);
 #pragma unroll
                     for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
-                        for (int j = 0; j < NS; ++j)
-                            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qa[j], kbf[pp][j], acc, 0, 0, 0);
+                        for (int j = 0; j < NJ; ++j)
+                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                qa[j], __builtin_bit_cast(bf16x8_t, kbf[pp][j]), acc, 0, 0, 0);
                 } else {
 #pragma unroll
                     for (int j = 0; j < KS / 4; ++j) {
@@ -305,13 +315,18 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
     const int lane = threadIdx.x;
     const int w = blockIdx.x;
     __shared__ WaveCut sh;
-    WalkState st = a.state[w];
-    const int n = st.n;
+    // the walk state's scalar fields only: a copy of the whole record (with
+    // its per-step arrays written at a runtime step) would live in scratch
+    WalkState *gst = a.state + w;
+    const int n = gst->n;
     if (n <= 0) return;                                   // finished earlier
+    const int buf = gst->buf;
+    const int32_t sel_n0 = gst->sel_n, unforced0 = gst->unforced;
+    uint32_t st_flags = gst->flags;
     const int cap = a.cand_cap, c = a.chunk, log2c = a.log2c;
     uint32_t *parents = a.cand + static_cast<int64_t>(w) * 2 * cap;
-    const uint32_t *par_cur = parents + static_cast<int64_t>(st.buf) * cap;
-    uint32_t *par_nxt = parents + static_cast<int64_t>(st.buf ^ 1) * cap;
+    const uint32_t *par_cur = parents + static_cast<int64_t>(buf) * cap;
+    uint32_t *par_nxt = parents + static_cast<int64_t>(buf ^ 1) * cap;
     const float *sc = a.score + static_cast<int64_t>(w) * cap;
     int32_t *selw = a.sel_blocks + static_cast<int64_t>(w) * a.sel_cap;
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -376,7 +391,11 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
     const bool forced = step_forced(a, t, n);
     unsigned long long tau = 0;
     uint32_t path = staged ? 0u : kPathLongList;
-    if (!forced) {
+    if (!forced && n <= 64) {
+        // one candidate per lane (staged: vr[0], ir[0]): the sort-based cut
+        const bool in = lane < n;
+        tau = lane_tau(a, in, vr[0], ir[0], wave_max(vr[0], 1, 64), n, a.k[t]);
+    } else if (!forced) {
         const bool by_mass = (a.mode == ZHA_TOPP) && (a.p > 0.f);
         float mx = -INFINITY;
         rounds(false, [&](float v, int, uint32_t, bool in) {
@@ -410,18 +429,33 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
             int w_bin[kWinPasses];
             int depth = 0;
             bool found = false;
+            // the windows live in registers: every index below is a
+            // compile-time constant (a runtime index would put the arrays in
+            // scratch memory)
+#pragma unroll
+            for (int q = 0; q < kWinPasses; ++q) { w_top[q] = 0.f; w_scale[q] = 0.f; w_bin[q] = 0; }
+            auto in_window = [&](float v) -> bool {
+                bool inw = true;
+#pragma unroll
+                for (int q = 0; q < kWinPasses; ++q)
+                    if (q < depth) inw = inw && win_bin(v, w_top[q], w_scale[q]) == w_bin[q];
+                return inw;
+            };
             for (; depth < kWinPasses; ++depth) {
                 if (!(top > bot)) break;
                 const float scale = 256.f / (top - bot);
-                w_top[depth] = top;
-                w_scale[depth] = scale;
+#pragma unroll
+                for (int q = 0; q < kWinPasses; ++q) {
+                    if (q == depth) {
+                        w_top[q] = top;
+                        w_scale[q] = scale;
+                    }
+                }
                 for (int i = lane; i < 256; i += 64) { sh.hcnt[i] = 0; sh.hw[i] = 0; }
                 __syncthreads();
                 rounds(false, [&](float v, int, uint32_t, bool in) {
                     if (!in) return;
-                    bool inw = true;
-                    for (int q = 0; q < depth; ++q) inw = inw && win_bin(v, w_top[q], w_scale[q]) == w_bin[q];
-                    if (!inw) return;
+                    if (!in_window(v)) return;
                     const int b = win_bin(v, top, scale);
                     unsigned long long wgt = 1;
                     if (by_mass) wgt = static_cast<unsigned long long>(__float2uint_rn(expf(v - mx) * kMassScale));
@@ -461,7 +495,9 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
                 __syncthreads();
                 const int b = static_cast<int>(sh.dig);
                 need -= sh.above;
-                w_bin[depth] = b;
+#pragma unroll
+                for (int q = 0; q < kWinPasses; ++q)
+                    if (q == depth) w_bin[q] = b;
                 const uint32_t cb = sh.cnt;
                 __syncthreads();
                 if (cb <= static_cast<uint32_t>(kWinFinal)) { ++depth; found = true; break; }
@@ -475,9 +511,7 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
                 __syncthreads();
                 rounds(true, [&](float v, int, uint32_t id, bool in) {
                     if (!in) return;
-                    bool inw = true;
-                    for (int q = 0; q < depth; ++q) inw = inw && win_bin(v, w_top[q], w_scale[q]) == w_bin[q];
-                    if (!inw) return;
+                    if (!in_window(v)) return;
                     const uint32_t slot = atomicAdd(&sh.nf, 1u);
                     if (slot < static_cast<uint32_t>(kWinFinal)) {
                         sh.fkey[slot] = rank_key(v, id, log2c);
@@ -564,7 +598,7 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
         const bool hi = open && (id >> kLevelShift) > 1u;
         const unsigned long long m1 = __ballot(l1), mh = __ballot(hi);
         if (l1) {
-            const int64_t pos = static_cast<int64_t>(st.sel_n) + n1 + __popcll(m1 & below);
+            const int64_t pos = static_cast<int64_t>(sel_n0) + n1 + __popcll(m1 & below);
             if (pos < a.sel_cap) selw[pos] = static_cast<int32_t>(id & kIndexMask);
         }
         if (hi) {
@@ -576,20 +610,22 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
         nopen += __popcll(__ballot(open));
     });
     int64_t nn = static_cast<int64_t>(nh) * c;
-    if (nn > cap) { st.flags |= ZHA_FLAG_CAND_OVERFLOW; nn = cap; }
-    st.scored[t] = n;
-    st.opened[t] = static_cast<int32_t>(nopen);
-    st.flags |= path;
-    if (!forced) st.unforced += n;
-    st.sel_n += static_cast<int32_t>(n1);
-    st.steps = t + 1;
-    st.buf ^= 1;
-    st.n = static_cast<int32_t>(nn);
-    if (st.n == 0 || t + 1 >= a.levels || t + 1 >= ZHA_MAX_STEPS) {
-        st.n = 0;
-        if (lane == 0) finish_walk<R>(a, w, t + 1, st.scored, st.opened, st.sel_n, st.unforced, st.flags);
+    if (nn > cap) { st_flags |= ZHA_FLAG_CAND_OVERFLOW; nn = cap; }
+    st_flags |= path;
+    const int32_t unforced = forced ? unforced0 : unforced0 + n;
+    const int32_t sel_n = sel_n0 + static_cast<int32_t>(n1);
+    const bool done = nn == 0 || t + 1 >= a.levels || t + 1 >= ZHA_MAX_STEPS;
+    if (lane == 0) {
+        gst->scored[t] = n;
+        gst->opened[t] = static_cast<int32_t>(nopen);
+        gst->flags = st_flags;
+        gst->unforced = unforced;
+        gst->sel_n = sel_n;
+        gst->steps = t + 1;
+        gst->buf = buf ^ 1;
+        gst->n = done ? 0 : static_cast<int32_t>(nn);
+        if (done) finish_walk<R>(a, w, t + 1, gst->scored, gst->opened, sel_n, unforced, st_flags);
     }
-    if (lane == 0) a.state[w] = st;
 }
 
 // Offsets of every parent's walk list (exclusive scan of the counts, pair
