@@ -36,7 +36,37 @@ sys.path.insert(0, ROOT)
 METRIC = "decode queries/sec (search+sparse attn) at 256K/1M keys; % HBM roofline"
 HBM_PEAK_GBS = 8000.0
 ROTATIONS = 8
-FLUSH_BYTES = 1 << 30               # written between timed steps: evicts L2 and the 256 MB MALL
+FLUSH_BYTES = 1 << 30               # touched between timed steps: evicts L2 and the 256 MB MALL
+FLUSH_MODE = "read"                 # "read": sum the buffer (evicts with clean lines); "write": fill it
+
+
+def new_flush_buffer():
+    import torch
+    buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    buf.fill_(0)
+    torch.cuda.synchronize()
+    return buf
+
+
+def evict_caches(buf, i):
+    """Move FLUSH_BYTES through the caches between timed steps, so that the
+    step reads its inputs from HBM.  A write leaves up to the MALL's size of
+    dirty lines, which the next kernels write back while they read; a read
+    evicts with clean lines."""
+    if FLUSH_MODE == "read":
+        buf.view(torch_int64()).sum()
+    else:
+        buf.fill_(i & 0xFF)
+
+
+def set_flush_mode(mode):
+    global FLUSH_MODE
+    FLUSH_MODE = mode
+
+
+def torch_int64():
+    import torch
+    return torch.int64
 
 STREAM = "prefill-256K-stream"      # streaming build + prefill blocks (reported under `also`)
 
@@ -188,10 +218,10 @@ def run_dense(idx, w, Q, K, V, per_rot, steps, warmup):
     for r in range(warmup):
         idx.dense_topk_attn(Q[r % ROTATIONS], K, V, budgets[r % ROTATIONS], maxb, out, ws)
     torch.cuda.synchronize()
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    flush = new_flush_buffer()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for i in range(steps):
-        flush.fill_(i & 0xFF)
+        evict_caches(flush, i)
         evs[i][0].record()
         idx.dense_topk_attn(Q[i % ROTATIONS], K, V, budgets[i % ROTATIONS], maxb, out, ws)
         evs[i][1].record()
@@ -233,7 +263,7 @@ def run_forward(idx, w, Q, K, V, select, steps, warmup):
     stats = torch.zeros(idx.walks, Zm.STATS_WORDS, dtype=torch.int32, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     res = {}
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    flush = new_flush_buffer()
     # batch 1: the first sequence alone, where launch latency weighs most
     g1 = Zm.make_geometry(1, w.kv_heads, w.group, w.d, w.chunk, w.refs, w.levels, w.dtype, w.n, w.sharpness)
     idx1 = Zm.Index(g1, idx.refs)
@@ -249,7 +279,7 @@ def run_forward(idx, w, Q, K, V, select, steps, warmup):
         torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         for i in range(steps):
-            flush.fill_(i & 0xFF)
+            evict_caches(flush, i)
             evs[i][0].record()
             idx1.forward(0, q1[i % ROTATIONS], K[:1], V[:1], sel, out1, stats[:idx1.walks], status, ws)
             evs[i][1].record()
@@ -266,7 +296,7 @@ def run_forward(idx, w, Q, K, V, select, steps, warmup):
         torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         for i in range(steps):
-            flush.fill_(i & 0xFF)
+            evict_caches(flush, i)
             evs[i][0].record()
             idx.forward(0, Q[i % ROTATIONS], K, V, sel, out, stats, status, ws)
             evs[i][1].record()
@@ -325,21 +355,33 @@ def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True, summary="
         step(r)
     torch.cuda.synchronize()
     # timed steps: each step's search and attention bracketed by HIP events
-    # on the launch stream, with 1 GiB written between steps so that every
-    # step reads its tree records and keys from HBM, not from L2 or the MALL
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(steps):
-        flush.fill_(i & 0xFF)
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
+    # on the launch stream, with 1 GiB moved through the caches between steps
+    # so that every step reads its tree records and keys from HBM, not from
+    # L2 or the MALL (FLUSH_MODE; the other mode is timed too and reported)
+    flush = new_flush_buffer()
+
+    def timed(mode):
+        prev = FLUSH_MODE
+        set_flush_mode(mode)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(steps):
+            evict_caches(flush, i)
+            step(i, evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        set_flush_mode(prev)
+        return evs, wall
+
+    other = "write" if FLUSH_MODE == "read" else "read"
+    evs_o, _ = timed(other)
+    evs, wall = timed(FLUSH_MODE)
     del flush
     search_ms = [e[0].elapsed_time(e[1]) for e in evs]
     attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
     step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    other_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs_o]))
     # the same steps back to back (caches warm from the previous step)
     t0 = time.perf_counter()
     for i in range(steps):
@@ -371,6 +413,7 @@ def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True, summary="
         qps=w.batch / (float(step_ms.mean()) * 1e-3),
         walks_per_s=walks / (float(step_ms.mean()) * 1e-3),
         back_to_back_ms=b2b_ms, back_to_back_qps=w.batch / (b2b_ms * 1e-3),
+        flush=FLUSH_MODE, ms_per_step_other_flush={other: other_ms},
         search_ms=float(np.mean(search_ms)), attn_ms=float(np.mean(attn_ms)),
         search_bytes=mean["search"], attn_bytes=mean["attn"], bytes=mean,
         build_ms=build_ms,
@@ -631,6 +674,7 @@ def summary(res, bw_ach):
         qps=res["qps"], walks_per_s=res["walks_per_s"], ms_per_step=res["ms_per_step"],
         ms_p10=res["ms_p10"], ms_p50=res["ms_p50"], ms_p90=res["ms_p90"],
         back_to_back_qps=res["back_to_back_qps"], back_to_back_ms=res["back_to_back_ms"],
+        flush=res["flush"], ms_per_step_other_flush=res["ms_per_step_other_flush"],
         search_ms=res["search_ms"], attn_ms=res["attn_ms"], build_ms=res["build_ms"],
         search_bytes=by["search"], attn_bytes=by["attn"],
         search_bytes_per_head=by["search_per_head"], attn_bytes_per_head=by["attn_per_head"],
@@ -695,9 +739,12 @@ def main():
     ap.add_argument("--calibrate", action="store_true",
                     help="also copy 1 GiB three times (the known-size kernel that scales HBM counters)")
     ap.add_argument("--threads", type=int, default=min(16, len(os.sched_getaffinity(0))))
+    ap.add_argument("--flush", default=FLUSH_MODE, choices=["write", "read"],
+                    help="how the 1 GiB between timed steps evicts the caches")
     ap.add_argument("--sweep", action="store_true",
                     help="only the length sweep on nested keys (4K .. 16M tokens); prints one JSON line")
     args = ap.parse_args()
+    set_flush_mode(args.flush)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(each (sequence, KV head) pair is independent; see the design notes on sharding)",

@@ -142,7 +142,11 @@ __global__ __launch_bounds__(kTopThreads) void k_top_score(SearchArgs a) {
     constexpr int RPL = 64 / LPR;
     constexpr int NL = (R + RPL - 1) / RPL;
     constexpr int kW = kTopThreads / 64;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wavefront index as a uniform value: the node loop below and its
+    // per-level table lookups then run on scalar registers and scalar loads
+    // (with a per-lane index they would be vector loads of the argument
+    // buffer, one dependent round trip per lookup)
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane % LPR, rsub = lane / LPR;
     const int64_t pair = blockIdx.y;
     const int G = a.group;
@@ -243,9 +247,11 @@ __global__ __launch_bounds__(kThreads) void k_top_cut(SearchArgs a) {
     __shared__ int s_rest, s_base;
     __shared__ int32_t s_scored[ZHA_MAX_STEPS], s_opened[ZHA_MAX_STEPS];
     __shared__ float s_tab[kTopRowsMax];             // this head's column of the table
+    __shared__ int32_t s_toff[ZHA_MAX_LEVELS + 2];   // first table row of each level (looked up per lane)
     __shared__ uint32_t s_list[2 * kTopList];        // two candidate lists (when a.top_lds)
     __shared__ float s_sc[kTopList];
     if (tid == 0) sh.flags = 0;
+    if (tid < ZHA_MAX_LEVELS + 2) s_toff[tid] = static_cast<int32_t>(a.top_off[tid]);
     {
         const float *tab = a.u_score + pair * a.top_rows * gp + h;
         for (int64_t r = tid; r < a.top_rows; r += kThreads) s_tab[r] = tab[r * gp];
@@ -283,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void k_top_cut(SearchArgs a) {
                 const uint32_t id = cur[i];
                 const int lvl = static_cast<int>(id >> kLevelShift);
                 if (lvl >= a.top_lo) {
-                    const float v = s_tab[a.top_off[lvl] + (id & kIndexMask)];
+                    const float v = s_tab[s_toff[lvl] + (id & kIndexMask)];
                     sc[i] = v;
                     m = fmaxf(m, v);
                 } else {
