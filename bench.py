@@ -308,6 +308,50 @@ def run_forward(idx, w, Q, K, V, select, steps, warmup):
     return res
 
 
+CONC_WALKS = 8          # walks sampled for the attention-concentration statistics
+
+
+def concentration(w, K, Q0, sel_blocks, sel_count, chunk=16):
+    """Workload statistics of dense attention on sampled walks (query
+    rotation 0), in fp64 on the host: the fraction of the context's 16-key
+    chunks needed to hold 90% of a walk's dense attention mass (the one
+    workload statistic the pages print, for their long-context evaluations),
+    and the dense mass the tree's selection keeps."""
+    n, c = w.n, w.chunk
+    walks = w.batch * w.heads
+    pick = sorted({(i * walks) // CONC_WALKS for i in range(CONC_WALKS)})
+    s = float(np.float32(1.0 / math.sqrt(w.d)))
+    fr, kept = [], []
+    cache = {}
+    for wi in pick:
+        b, h = divmod(wi, w.heads)
+        g = h // w.group
+        if (b, g) not in cache:
+            cache.clear()
+            cache[(b, g)] = K[b, g, :n].float().cpu().numpy()
+        Kp = cache[(b, g)]
+        q = Q0[b, h].float().cpu().numpy().astype(np.float64)
+        lg = np.empty(n, np.float64)
+        for a0 in range(0, n, 1 << 18):
+            lg[a0:a0 + (1 << 18)] = s * (Kp[a0:a0 + (1 << 18)].astype(np.float64) @ q)
+        p = np.exp(lg - lg.max())
+        p /= p.sum()
+        nc = (n + chunk - 1) // chunk
+        pc = np.zeros(nc * chunk)
+        pc[:n] = p
+        cm = np.sort(pc.reshape(nc, chunk).sum(axis=1))[::-1]
+        k90 = int(np.searchsorted(np.cumsum(cm), 0.9)) + 1
+        fr.append(min(k90, nc) / nc)
+        blk = sel_blocks[wi, :min(int(sel_count[wi]), sel_blocks.shape[1])].astype(np.int64)
+        toks = (blk[:, None] * c + np.arange(c)[None, :]).reshape(-1)
+        tail = np.arange(c * (n // c), n)
+        kept.append(float(p[np.concatenate([toks, tail])].sum()))
+    return dict(walks=len(pick), chunk_keys=chunk,
+                chunks_for_90pct=float(np.mean(fr)), chunks_for_90pct_min=float(np.min(fr)),
+                chunks_for_90pct_max=float(np.max(fr)),
+                mass_kept=float(np.mean(kept)), mass_kept_min=float(np.min(kept)))
+
+
 def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True, summary="f32"):
     import torch
     from tree_structured_kv_amd import zha as Zm
@@ -351,6 +395,8 @@ def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True, summary="
         u_k = union_keys(w, bufs["sel_blocks"].cpu().numpy(), bufs["sel_count"].cpu().numpy())
         acct.append(walk_bytes(w, rows, u_sc, u_k, summary))
         per_level.append(lvl_counts)
+        if r == 0:
+            conc = concentration(w, K, Q[0], bufs["sel_blocks"].cpu().numpy(), bufs["sel_count"].cpu().numpy())
     for r in range(warmup):
         step(r)
     torch.cuda.synchronize()
@@ -421,6 +467,7 @@ def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True, summary="
         keys_read_per_walk=float(np.mean(keys)),
         status=status, dist=dist,
         union_scored_per_level=[float(x) for x in np.mean(np.array(per_level), axis=0)],
+        concentration=conc,
         idx=idx, K=K, V=V, Q=Q, R=R, per_rot=per_rot,
     )
     return res
@@ -687,6 +734,7 @@ def summary(res, bw_ach):
         keys_per_step=by["keys"], keys_union_per_step=by["union_keys"],
         status=res["status"], per_walk=res["dist"],
         nodes_scored_union_per_level=res["union_scored_per_level"],
+        concentration=res["concentration"],
         dense=res["dense"], zha_forward=res["forward"],
         speedup_vs_dense=(res["dense"]["ms_per_step"] / res["ms_per_step"]) if res["dense"] else None,
         dense_k_floor_ms=dense_floor(res["dense"], bw_ach) if res["dense"] else None,

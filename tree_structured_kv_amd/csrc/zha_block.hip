@@ -409,7 +409,7 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
             rounds(false, [&](float v, int, uint32_t, bool in) {
                 if (!in) return;
                 if (v > -INFINITY) mn = fminf(mn, v);
-                if (by_mass) z += static_cast<unsigned long long>(__float2uint_rn(expf(v - mx) * kMassScale));
+                if (by_mass) z += static_cast<unsigned long long>(__float2uint_rn(mass_exp(v - mx) * kMassScale));
             });
             mn = -wave_max(-mn, 1, 64);
             z = wave_sum_u64(z);
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
                     if (!in_window(v)) return;
                     const int b = win_bin(v, top, scale);
                     unsigned long long wgt = 1;
-                    if (by_mass) wgt = static_cast<unsigned long long>(__float2uint_rn(expf(v - mx) * kMassScale));
+                    if (by_mass) wgt = static_cast<unsigned long long>(__float2uint_rn(mass_exp(v - mx) * kMassScale));
                     atomicAdd(&sh.hcnt[b], 1u);
                     if (wgt) atomicAdd(&sh.hw[b], wgt);
                 });
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
                     if (slot < static_cast<uint32_t>(kWinFinal)) {
                         sh.fkey[slot] = rank_key(v, id, log2c);
                         sh.fw[slot] = by_mass ? static_cast<unsigned long long>(
-                                                    __float2uint_rn(expf(v - mx) * kMassScale))
+                                                    __float2uint_rn(mass_exp(v - mx) * kMassScale))
                                               : 1ull;
                     }
                 });
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
             const bool by_mass2 = (a.mode == ZHA_TOPP) && (a.p > 0.f) && (mx > -INFINITY);
             unsigned long long z = 0;
             for (int x = lane; x < n; x += 64)
-                z += by_mass2 ? static_cast<unsigned long long>(__float2uint_rn(expf(sc[x] - mx) * kMassScale)) : 1ull;
+                z += by_mass2 ? static_cast<unsigned long long>(__float2uint_rn(mass_exp(sc[x] - mx) * kMassScale)) : 1ull;
             z = wave_sum_u64(z);
             if (a.mode == ZHA_TOPK) {
                 need = static_cast<unsigned long long>(a.k[t] < n ? a.k[t] : n);
@@ -570,7 +570,7 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
                 for (int y = 0; y < n; ++y) {
                     const unsigned long long ky = rank_key(sc[y], cand_id(y), log2c);
                     if (ky >= kx)
-                        above += by_mass2 ? static_cast<unsigned long long>(__float2uint_rn(expf(sc[y] - mx) * kMassScale))
+                        above += by_mass2 ? static_cast<unsigned long long>(__float2uint_rn(mass_exp(sc[y] - mx) * kMassScale))
                                           : 1ull;
                 }
                 if (above >= need && kx > best) best = kx;

@@ -236,8 +236,9 @@ __global__ __launch_bounds__(kTopThreads) void k_top_score(SearchArgs a) {
 template <int D, int R, typename QT, typename ST>
 __global__ __launch_bounds__(kThreads) void k_top_cut(SearchArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int w = blockIdx.x;
-    if (w >= a.walks) return;
+    // a pair's heads on one XCD: they read the same rows of the pair's table
+    const int w = static_cast<int>(xcd_item(blockIdx.x, a.walks));
+    if (w < 0) return;
     const int64_t pair = walk_pair(w, 1, a.heads, a.group, a.kv_heads);
     const int h = w % a.group;
     const int cap = a.cand_cap, gp = (a.group + 3) & ~3;
@@ -396,7 +397,8 @@ static hipError_t launch_top_t(const SearchArgs &a, hipStream_t st) {
         hipLaunchKernelGGL((k_top_score<D, R, QT, ST, 16>), grid, dim3(kTopThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_top_cut<D, R, QT, ST>), dim3(a.walks), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((k_top_cut<D, R, QT, ST>), dim3(static_cast<unsigned>(xcd_grid(a.walks))), dim3(kThreads), 0,
+                       st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.top_steps < a.levels)
         return launch_ls_from(a, D, R, sizeof(QT) == 2 ? ZHA_BF16 : ZHA_F32, sizeof(ST) == 2 ? ZHA_BF16 : ZHA_F32,

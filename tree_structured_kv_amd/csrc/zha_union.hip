@@ -51,8 +51,8 @@ __device__ __forceinline__ short4_t pack4(uint32_t lo, uint32_t hi) {
 
 constexpr int kScoreThreads = 256;
 constexpr int kUG = 2;                // matrix tiles in flight per wavefront
-constexpr int kLdsCand = 14336;       // candidate scores a cut stages in LDS (56 KB)
-constexpr int kLdsPar = 2048;         // parent ranks a cut stages in LDS (8 KB)
+constexpr int kLdsCand = 14848;       // candidate scores a cut stages in LDS (58 KB)
+constexpr int kLdsPar = 2048;         // parents whose ranks and node ids a cut stages in LDS (16 KB)
 constexpr int kExpMin = 256;          // list entries per expand workgroup (at least)
 static_assert(kSmallList <= 64, "a fused step's candidates fit one wavefront, one per lane");
 
@@ -62,6 +62,23 @@ __device__ __forceinline__ int head_walk(const SearchArgs &a, int pair, int h) {
 }
 
 __device__ __forceinline__ int round_flat(int n) { return (n + kFlatPad - 1) / kFlatPad * kFlatPad; }
+
+// A head's candidate ids by index: child x & (c - 1) of its opened parent
+// x >> log2c when the parents' node ids are staged in LDS, else the pair's
+// list entry at the candidate's list position.
+template <typename Pos>
+struct CandIds {
+    const uint32_t *ids;
+    Pos pos;
+    const uint32_t *pid;              // parents' node ids in LDS, or null
+    int log2c;
+    __device__ __forceinline__ uint32_t operator[](int x) const {
+        if (!pid) return ids[pos(x)];
+        const uint32_t p = pid[x >> log2c];
+        const uint32_t c = 1u << log2c;
+        return (((p >> kLevelShift) - 1u) << kLevelShift) | ((p & kIndexMask) * c + (static_cast<uint32_t>(x) & (c - 1u)));
+    }
+};
 
 struct ExpandShared {
     uint32_t seg_cnt[kWaves];
@@ -347,7 +364,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_un_score(SearchArgs a, int t,
 // step and get head bit h in the pair's open masks.
 template <int R>
 __device__ __forceinline__ void cut_head(const SearchArgs &a, int t, int w, SelectShared &sh, uint32_t *s_one,
-                                         uint32_t *s_high, float *lds_sc, int32_t *lds_par) {
+                                         uint32_t *s_high, float *lds_sc, int32_t *lds_par, uint32_t *lds_pid) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int p = w / a.group, h = w % a.group;
     const uint32_t bit = 1u << h;
@@ -358,13 +375,15 @@ __device__ __forceinline__ void cut_head(const SearchArgs &a, int t, int w, Sele
     if (t > 0 && n_open_prev == 0) return;         // this head opened nothing more
     WalkState *st = a.state + w;
     const uint32_t *ids = a.u_ids + (static_cast<int64_t>(p) * 2 + buf) * cap;
+    const uint32_t *prev_ids = a.u_ids + (static_cast<int64_t>(p) * 2 + (buf ^ 1)) * cap;   // step t-1's list
     const int gp = (a.group + 3) & ~3;
     const float *sc = a.u_score + static_cast<int64_t>(p) * cap * gp + h;   // score of position i: sc[i * gp]
     const int32_t *rank = a.u_rank + static_cast<int64_t>(p) * cap;
     uint32_t *om = a.u_omask + (static_cast<int64_t>(p) * 2 + buf) * cap;
     int32_t *opened_pos = a.u_open + static_cast<int64_t>(w) * cap;
-    uint32_t *cid = a.cand + static_cast<int64_t>(w) * 2 * cap;     // this head's candidate ids
-    uint32_t *cux = cid + cap;                                       // their list positions (fallback)
+    // the head's candidates' list positions when the parents' ranks do not
+    // fit in LDS (the second of the walk's two candidate buffers)
+    uint32_t *cux = a.cand + static_cast<int64_t>(w) * 2 * cap + cap;
     float *csc = a.h_score + static_cast<int64_t>(w) * cap;         // their scores (fallback)
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
@@ -383,7 +402,10 @@ __device__ __forceinline__ void cut_head(const SearchArgs &a, int t, int w, Sele
 #pragma unroll
                 for (int u = 0; u < kScanU; ++u) {
                     const int j = j0 + u * kThreads;
-                    if (j < n_open_prev) lds_par[j] = rank[i[u]];
+                    if (j < n_open_prev) {
+                        lds_par[j] = rank[i[u]];
+                        if (t > a.small_steps) lds_pid[j] = prev_ids[i[u]];
+                    }
                 }
             }
         } else {
@@ -419,23 +441,22 @@ __device__ __forceinline__ void cut_head(const SearchArgs &a, int t, int w, Sele
     const bool forced = step_forced(a, t, cnt);
     const bool sc_lds = cnt <= kLdsCand;
     float *vs = sc_lds ? lds_sc : csc;
+    // the candidates' scores only: a node id is fetched where it is needed
+    // (the few candidates tied at the cut's score, and the opened ones)
     float m = -INFINITY;
-    for (int x0 = tid; x0 < cnt; x0 += kScanU * kThreads) {
-        uint32_t id[kScanU];
-        float v[kScanU];
+    if (!forced) {
+        constexpr int GU = 2 * kScanU;             // score loads in flight per thread
+        for (int x0 = tid; x0 < cnt; x0 += GU * kThreads) {
+            float v[GU];
 #pragma unroll
-        for (int u = 0; u < kScanU; ++u) {
-            const int x = x0 + u * kThreads;
-            const int pos = x < cnt ? position(x) : 0;
-            id[u] = x < cnt ? ids[pos] : 0u;
-            v[u] = (x < cnt && !forced) ? sc[static_cast<int64_t>(pos) * gp] : 0.f;
-        }
+            for (int u = 0; u < GU; ++u) {
+                const int x = x0 + u * kThreads;
+                v[u] = x < cnt ? sc[static_cast<int64_t>(position(x)) * gp] : 0.f;
+            }
 #pragma unroll
-        for (int u = 0; u < kScanU; ++u) {
-            const int x = x0 + u * kThreads;
-            if (x < cnt) {
-                cid[x] = id[u];
-                if (!forced) {
+            for (int u = 0; u < GU; ++u) {
+                const int x = x0 + u * kThreads;
+                if (x < cnt) {
                     vs[x] = v[u];
                     m = fmaxf(m, v[u]);
                 }
@@ -443,20 +464,35 @@ __device__ __forceinline__ void cut_head(const SearchArgs &a, int t, int w, Sele
         }
     }
     __syncthreads();
+    // the parents' node ids come from step t-1's list, which is in memory
+    // only when a grid-wide step built it (not k_un_small's last step)
+    const bool pid_lds = t > a.small_steps && par_lds;
+    const CandIds<decltype(position)> cand{ids, position, pid_lds ? lds_pid : nullptr, log2c};
     unsigned long long tau = 0;
     uint32_t path = (sc_lds || forced) ? 0u : kPathLdsSpill;
     if (!forced) {
         const float mx = block_max(m, sh);
-        tau = sc_lds ? cut_tau_win(a, cnt, cid, lds_sc, mx, a.k[t], sh, &path)
-                     : cut_tau_win(a, cnt, cid, csc, mx, a.k[t], sh, &path);
+        // a list too long for LDS is cut from global memory: twice the
+        // loads in flight per thread
+        tau = sc_lds ? cut_tau_win(a, cnt, cand, lds_sc, mx, a.k[t], sh, &path)
+                     : cut_tau_win<2 * kScanU>(a, cnt, cand, csc, mx, a.k[t], sh, &path);
     }
 
     // open, in candidate order: wavefront v owns segment v (64*kScanU a round)
     const int seg = ((cnt + kWaves - 1) / kWaves + 63) / 64 * 64;
     const int c0 = wave * seg, c1 = min(cnt, c0 + seg);
+    // the score decides unless it equals the cut's: then the span start does
+    const uint32_t tau_hi = static_cast<uint32_t>(tau >> 32);
     auto opens = [&](int k, uint32_t &id) -> bool {
-        id = cid[k];
-        return forced || rank_key(vs[k], id, log2c) >= tau;
+        if (!forced) {
+            const float v = vs[k];
+            const uint32_t hi = ordered_bits(v);
+            if (hi < tau_hi) { id = 0; return false; }
+            id = cand[k];
+            return hi > tau_hi || rank_key(v, id, log2c) >= tau;
+        }
+        id = cand[k];
+        return true;
     };
     uint32_t n1 = 0, nopen = 0, nhigh = 0;
     for (int b0 = c0; b0 < c1; b0 += 64 * kScanU) {
@@ -685,9 +721,13 @@ __global__ __launch_bounds__(kThreads) void k_un_cut(SearchArgs a, int t, int ha
     __shared__ uint32_t s_one[kWaves], s_high[kWaves];
     __shared__ float s_sc[kLdsCand];
     __shared__ int32_t s_par[kLdsPar];
-    const int w = blockIdx.x;
+    __shared__ uint32_t s_pid[kLdsPar];
+    // a pair's heads on one XCD: they read the same rows of the pair's score
+    // table, which that XCD's L2 then fetches once
+    const int w = static_cast<int>(xcd_item(blockIdx.x, static_cast<int64_t>(a.pairs) * a.group));
+    if (w < 0) return;
     if (a.u_n[2 * (w / a.group) + (t & 1)] <= 0) return;   // the pair has finished (all its heads)
-    cut_head<R>(a, t, w, sh, s_one, s_high, s_sc, s_par);
+    cut_head<R>(a, t, w, sh, s_one, s_high, s_sc, s_par, s_pid);
     if (handover) {
         __syncthreads();                           // this walk's opened positions and count are written
         to_ls_walk<R>(a, t, w);
@@ -1031,7 +1071,8 @@ static hipError_t launch_union_t(const SearchArgs &a, int n0, hipStream_t st) {
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         const int handover = (t + 1 == a.ls_from) ? 1 : 0;
-        hipLaunchKernelGGL((k_un_cut<R>), dim3(a.pairs * a.group), dim3(kThreads), 0, st, a, t, handover);
+        hipLaunchKernelGGL((k_un_cut<R>), dim3(static_cast<unsigned>(xcd_grid(int64_t(a.pairs) * a.group))),
+                           dim3(kThreads), 0, st, a, t, handover);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (!handover) {
             hipLaunchKernelGGL((k_un_expand<R>), dim3(a.pairs * kExpSlices), dim3(kThreads), 0, st, a, t);

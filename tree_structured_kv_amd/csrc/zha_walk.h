@@ -12,6 +12,11 @@ namespace zha {
 
 constexpr float kMassScale = 2147483648.0f;  // 2^31: integer softmax masses
 
+// e^x for the integer masses of a cut (x = score - max <= 0): one hardware
+// exp2 of x*log2(e).  Every cut takes its masses from this one function, so
+// equal scores give equal masses everywhere; it is not the libm expf.
+__device__ __forceinline__ float mass_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
 // 64-bit rank key of a candidate: ordered score bits, then the complement of
 // its span start, so that equal scores rank in span order.
 __device__ __forceinline__ uint64_t rank_key(float score, uint32_t id, int log2c) {
@@ -129,8 +134,11 @@ __device__ __forceinline__ unsigned long long block_exscan64(unsigned long long 
 // that is not forced; every candidate with a key >= it opens.
 // With `mask` non-null only entries i with (mask[i] & bit) are candidates
 // (the union engine's per-head view of a pair's list); `n` is then the
-// length of the list and `cnt` the number of candidates.
-__device__ __forceinline__ unsigned long long cut_tau(const SearchArgs &a, int n, const uint32_t *cur,
+// length of the list and `cnt` the number of candidates.  `cur` gives the
+// candidates' node ids by index: an array, or an accessor that finds them
+// (cur[i]).
+template <int U = kScanU, typename Ids>
+__device__ __forceinline__ unsigned long long cut_tau(const SearchArgs &a, int n, Ids cur,
                                                       const float *sc, float mx, int kt, SelectShared &sh,
                                                       const uint32_t *mask = nullptr, uint32_t bit = 0,
                                                       int cnt = -1) {
@@ -142,20 +150,20 @@ __device__ __forceinline__ unsigned long long cut_tau(const SearchArgs &a, int n
     unsigned long long target;
     if (by_mass) {
         unsigned long long zpart = 0;
-        for (int i0 = tid; i0 < n; i0 += kScanU * kThreads) {
-            bool in[kScanU];
-            float v[kScanU];
+        for (int i0 = tid; i0 < n; i0 += U * kThreads) {
+            bool in[U];
+            float v[U];
 #pragma unroll
-            for (int u = 0; u < kScanU; ++u) {
+            for (int u = 0; u < U; ++u) {
                 const int i = i0 + u * kThreads;
                 in[u] = i < n && (!mask || (mask[i] & bit));
             }
 #pragma unroll
-            for (int u = 0; u < kScanU; ++u) v[u] = in[u] ? sc[i0 + u * kThreads] : 0.f;
+            for (int u = 0; u < U; ++u) v[u] = in[u] ? sc[i0 + u * kThreads] : 0.f;
 #pragma unroll
-            for (int u = 0; u < kScanU; ++u) {
+            for (int u = 0; u < U; ++u) {
                 if (!in[u]) continue;
-                const float e = flat ? 1.f : expf(v[u] - mx);
+                const float e = flat ? 1.f : mass_exp(v[u] - mx);
                 zpart += static_cast<unsigned long long>(__float2uint_rn(e * kMassScale));
             }
         }
@@ -175,30 +183,30 @@ __device__ __forceinline__ unsigned long long cut_tau(const SearchArgs &a, int n
         const int shift = 56 - 8 * pass;
         for (int i = tid; i < 256; i += kThreads) { sh.hcnt[i] = 0; sh.hw[i] = 0; }
         __syncthreads();
-        for (int i0 = tid; i0 < n; i0 += kScanU * kThreads) {
-            bool in[kScanU];
-            float v[kScanU];
-            uint32_t idv[kScanU];
+        for (int i0 = tid; i0 < n; i0 += U * kThreads) {
+            bool in[U];
+            float v[U];
+            uint32_t idv[U];
 #pragma unroll
-            for (int u = 0; u < kScanU; ++u) {
+            for (int u = 0; u < U; ++u) {
                 const int i = i0 + u * kThreads;
                 in[u] = i < n && (!mask || (mask[i] & bit));
             }
 #pragma unroll
-            for (int u = 0; u < kScanU; ++u) {
+            for (int u = 0; u < U; ++u) {
                 const int i = i0 + u * kThreads;
                 v[u] = in[u] ? sc[i] : 0.f;
                 idv[u] = in[u] ? cur[i] : 0u;
             }
 #pragma unroll
-            for (int u = 0; u < kScanU; ++u) {
+            for (int u = 0; u < U; ++u) {
                 if (!in[u]) continue;
                 const unsigned long long key = rank_key(v[u], idv[u], log2c);
                 if (pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8))) {
                     const uint32_t dg = static_cast<uint32_t>(key >> shift) & 255u;
                     unsigned long long wgt = 1;
                     if (by_mass) {
-                        const float e = flat ? 1.f : expf(v[u] - mx);
+                        const float e = flat ? 1.f : mass_exp(v[u] - mx);
                         wgt = static_cast<unsigned long long>(__float2uint_rn(e * kMassScale));
                     }
                     atomicAdd(&sh.hcnt[dg], 1u);
@@ -280,31 +288,32 @@ __device__ __forceinline__ int win_bin(float v, float top, float scale) {
 // bins, so the shared-memory histogram sees little contention.  Falls back
 // to cut_tau when every score is -inf or a window cannot be split (ties);
 // that fallback ORs kPathTieSelect into *path (every thread's copy).
-__device__ __forceinline__ unsigned long long cut_tau_win(const SearchArgs &a, int n, const uint32_t *cur,
+template <int U = kScanU, typename Ids>
+__device__ __forceinline__ unsigned long long cut_tau_win(const SearchArgs &a, int n, Ids cur,
                                                           const float *sc, float mx, int kt, SelectShared &sh,
                                                           uint32_t *path = nullptr) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int log2c = a.log2c;
     if (!(mx > -INFINITY)) {
         if (path) *path |= kPathTieSelect;
-        return cut_tau(a, n, cur, sc, mx, kt, sh);
+        return cut_tau<U>(a, n, cur, sc, mx, kt, sh);
     }
     const bool by_mass = (a.mode == ZHA_TOPP) && (a.p > 0.f);
     // total weight and the lowest finite score
     unsigned long long zpart = 0;
     float mn = mx;
-    for (int i0 = tid; i0 < n; i0 += kScanU * kThreads) {
-        float v[kScanU];
+    for (int i0 = tid; i0 < n; i0 += U * kThreads) {
+        float v[U];
 #pragma unroll
-        for (int u = 0; u < kScanU; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int i = i0 + u * kThreads;
             v[u] = i < n ? sc[i] : mx;
         }
 #pragma unroll
-        for (int u = 0; u < kScanU; ++u) {
+        for (int u = 0; u < U; ++u) {
             if (v[u] > -INFINITY) mn = fminf(mn, v[u]);
             if (by_mass && i0 + u * kThreads < n)
-                zpart += static_cast<unsigned long long>(__float2uint_rn(expf(v[u] - mx) * kMassScale));
+                zpart += static_cast<unsigned long long>(__float2uint_rn(mass_exp(v[u] - mx) * kMassScale));
         }
     }
     mn = -wave_max(-mn, 1, 64);
@@ -338,22 +347,22 @@ __device__ __forceinline__ unsigned long long cut_tau_win(const SearchArgs &a, i
         w_scale[depth] = scale;
         for (int i = tid; i < 256; i += kThreads) { sh.hcnt[i] = 0; sh.hw[i] = 0; }
         __syncthreads();
-        for (int i0 = tid; i0 < n; i0 += kScanU * kThreads) {
-            float v[kScanU];
+        for (int i0 = tid; i0 < n; i0 += U * kThreads) {
+            float v[U];
 #pragma unroll
-            for (int u = 0; u < kScanU; ++u) {
+            for (int u = 0; u < U; ++u) {
                 const int i = i0 + u * kThreads;
                 v[u] = i < n ? sc[i] : -INFINITY;
             }
 #pragma unroll
-            for (int u = 0; u < kScanU; ++u) {
+            for (int u = 0; u < U; ++u) {
                 if (i0 + u * kThreads >= n) continue;
                 bool in = true;
                 for (int q = 0; q < depth; ++q) in = in && win_bin(v[u], w_top[q], w_scale[q]) == w_bin[q];
                 if (!in) continue;
                 const int b = win_bin(v[u], top, scale);
                 unsigned long long wgt = 1;
-                if (by_mass) wgt = static_cast<unsigned long long>(__float2uint_rn(expf(v[u] - mx) * kMassScale));
+                if (by_mass) wgt = static_cast<unsigned long long>(__float2uint_rn(mass_exp(v[u] - mx) * kMassScale));
                 atomicAdd(&sh.hcnt[b], 1u);
                 if (wgt) atomicAdd(&sh.hw[b], wgt);
             }
@@ -402,7 +411,7 @@ __device__ __forceinline__ unsigned long long cut_tau_win(const SearchArgs &a, i
     }
     if (!done) {
         if (path) *path |= kPathTieSelect;
-        return cut_tau(a, n, cur, sc, mx, kt, sh);
+        return cut_tau<U>(a, n, cur, sc, mx, kt, sh);
     }
 
     // the final bin's candidates, ranked by key
@@ -416,7 +425,7 @@ __device__ __forceinline__ unsigned long long cut_tau_win(const SearchArgs &a, i
         const uint32_t slot = atomicAdd(&sh.nf, 1u);
         if (slot < static_cast<uint32_t>(kWinFinal)) {
             sh.fkey[slot] = rank_key(v, cur[i], log2c);
-            sh.fw[slot] = by_mass ? static_cast<unsigned long long>(__float2uint_rn(expf(v - mx) * kMassScale)) : 1ull;
+            sh.fw[slot] = by_mass ? static_cast<unsigned long long>(__float2uint_rn(mass_exp(v - mx) * kMassScale)) : 1ull;
         }
     }
     __syncthreads();
@@ -454,7 +463,7 @@ __device__ __forceinline__ unsigned long long lane_tau(const SearchArgs &a, bool
     const bool by_mass = (a.mode == ZHA_TOPP) && (a.p > 0.f);
     const bool flat = !(mx > -INFINITY);   // every score -inf: equal masses
     uint32_t wt = 0u;
-    if (in) wt = by_mass ? __float2uint_rn((flat ? 1.f : expf(v - mx)) * kMassScale) : 1u;
+    if (in) wt = by_mass ? __float2uint_rn((flat ? 1.f : mass_exp(v - mx)) * kMassScale) : 1u;
     unsigned long long key = in ? rank_key(v, id, a.log2c) : 0ull;
     unsigned long long need;
     if (by_mass) {
