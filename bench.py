@@ -206,7 +206,7 @@ def prepare(w, threads, summary="f32"):
     return _PREPARED[(w.wid, summary)]
 
 
-def run_dense(idx, w, Q, K, V, per_rot, steps, warmup):
+def run_dense(idx, w, Q, K, V, per_rot, steps, warmup, select=None):
     """The same-GPU dense full-scan indexer on the same queries, with each
     walk's key budget equal to the keys the tree walk read."""
     import torch
@@ -236,10 +236,44 @@ def run_dense(idx, w, Q, K, V, per_rot, steps, warmup):
     logit_bytes = walks * w.n * 4 * (1 + 3)
     keys = float(np.mean([sum(s["keys_read"] for s in rows) for rows in per_rot]))
     attn_bytes = 2 * w.d * e * keys + 2 * walks * w.d * e
-    return dict(ms_per_step=ms, qps=w.batch / (ms * 1e-3), k_pass_bytes=k_bytes,
-                logit_bytes=logit_bytes, attn_bytes=attn_bytes,
-                gbs=(k_bytes + logit_bytes + attn_bytes) / (ms * 1e-3) / 1e9,
-                max_budget=maxb)
+    res = dict(ms_per_step=ms, qps=w.batch / (ms * 1e-3), k_pass_bytes=k_bytes,
+               logit_bytes=logit_bytes, attn_bytes=attn_bytes,
+               gbs=(k_bytes + logit_bytes + attn_bytes) / (ms * 1e-3) / 1e9,
+               max_budget=maxb)
+    if select is not None and select.get("mode") == "topp":
+        res["topp_over_keys"] = run_dense_topp(idx, w, Q, K, V, float(select.get("p", 0.9)), steps, warmup)
+    return res
+
+
+def run_dense_topp(idx, w, Q, K, V, p, steps, warmup):
+    """The dense indexer with top-p over keys instead of an equal budget: each
+    walk attends the smallest prefix of its keys by logit whose softmax mass
+    over all keys reaches p (zha_dense_topp_attn), same protocol."""
+    import torch
+    walks = w.batch * w.heads
+    ws = idx.dense_workspace(w.n)
+    out = torch.empty(w.batch, w.heads, w.d, dtype=K.dtype, device="cuda")
+    cnt = torch.zeros(walks, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    keys = []
+    for r in range(max(warmup, ROTATIONS)):
+        idx.dense_topp_attn(Q[r % ROTATIONS], K, V, p, w.n, out, ws, sel_count=cnt, status=status)
+        if r < ROTATIONS:
+            torch.cuda.synchronize()
+            keys.append(float(cnt.double().mean()))
+    torch.cuda.synchronize()
+    flush = new_flush_buffer()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        evict_caches(flush, i)
+        evs[i][0].record()
+        idx.dense_topp_attn(Q[i % ROTATIONS], K, V, p, w.n, out, ws, sel_count=cnt, status=status)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    del flush
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    return dict(p=p, ms_per_step=ms, qps=w.batch / (ms * 1e-3), keys_per_walk=float(np.mean(keys)),
+                keys_frac=float(np.mean(keys)) / w.n, status=int(status.cpu()[0]))
 
 
 def dense_floor(dense, bw_ach):
@@ -447,7 +481,7 @@ def run_gpu(Z, w, select, steps, warmup, threads, dense_baseline=True, summary="
         v = np.array([s[k] for s in allw], dtype=np.float64)
         dist[k] = dict(mean=float(v.mean()), p50=float(np.percentile(v, 50)),
                        p90=float(np.percentile(v, 90)), max=float(v.max()))
-    dense = run_dense(idx, w, Q, K, V, per_rot, steps, warmup) if dense_baseline else None
+    dense = run_dense(idx, w, Q, K, V, per_rot, steps, warmup, select) if dense_baseline else None
     fwd = run_forward(idx, w, Q, K, V, select, steps, warmup) if FORWARD else None
     res = dict(
         dense=dense, forward=fwd,
@@ -739,6 +773,8 @@ def summary(res, bw_ach):
         speedup_vs_dense=(res["dense"]["ms_per_step"] / res["ms_per_step"]) if res["dense"] else None,
         dense_k_floor_ms=dense_floor(res["dense"], bw_ach) if res["dense"] else None,
         speedup_vs_dense_k_floor=(dense_floor(res["dense"], bw_ach) / res["ms_per_step"]) if res["dense"] else None,
+        speedup_vs_dense_topp=(res["dense"]["topp_over_keys"]["ms_per_step"] / res["ms_per_step"])
+        if res["dense"] and res["dense"].get("topp_over_keys") else None,
     )
 
 

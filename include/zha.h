@@ -406,6 +406,26 @@ zha_status zha_dense_topk_attn(const zha_tree *t, const void *q, const void *k_c
                                void *out, int32_t *sel_tokens, void *ws, uint64_t ws_bytes,
                                void *stream);
 
+/* Dense top-p over keys, the baseline's other selection rule: the same
+ * exact logits, then for each walk the smallest prefix of its keys ordered
+ * by (logit descending, index ascending) whose softmax mass over all keys
+ * reaches p (masses are exp(logit - max) * 2^31 rounded to integers, as in
+ * the tree's cuts, so the sums are exact), then attention over exactly
+ * those keys.  p >= 1 takes every key, p <= 0 the first one ([ZHA lesson]
+ * "How does top-p differ from top-K?" for the prefix rule, applied here to
+ * keys instead of nodes).  Workspace: zha_dense_workspace_bytes(t,
+ * max_budget).
+ *   sel_tokens  device int32 [walks][max_budget] or NULL (as above)
+ *   sel_count   device int32 [walks] or NULL: the prefix length of each walk
+ *               (clamped to max_budget)
+ *   status      device uint32 or NULL: ZHA_FLAG_SEL_OVERFLOW is ORed in
+ *               when a prefix is longer than max_budget
+ * Returns ZHA_ERR_ARG for a non-finite p. */
+zha_status zha_dense_topp_attn(const zha_tree *t, const void *q, const void *k_cache,
+                               const void *v_cache, float p, int32_t max_budget, void *out,
+                               int32_t *sel_tokens, int32_t *sel_count, uint32_t *status, void *ws,
+                               uint64_t ws_bytes, void *stream);
+
 /* Streaming read of `bytes` from device buffer `buf` (sum into *sink, a
  * device float); gives the achievable HBM read bandwidth on this GPU. */
 zha_status zha_bw_probe(const void *buf, uint64_t bytes, float *sink, void *stream);

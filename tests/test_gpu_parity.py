@@ -508,6 +508,76 @@ def test_dense_topk_baseline(Z, name):
     assert stable >= 0.5 * walks
 
 
+@pytest.mark.parametrize("name", ["demo", "clustered-small", "mixed-small"])
+@pytest.mark.parametrize("p", [0.5, 0.9, 1.0, 0.0])
+def test_dense_topp_baseline(Z, name, p):
+    """The dense baseline with top-p over keys: the smallest prefix of the
+    keys by (logit descending, index ascending) whose softmax mass over all
+    keys reaches p, against fp64 logits and masses.  Where the prefix is
+    decided with room to spare (its mass without the last key at least 2e-5
+    below p, with it at least 2e-5 above, and the boundary logits more than
+    1e-4 apart) the key set must be the fp64 one; elsewhere it must be a
+    valid top-p prefix within 1e-4.  p = 1 takes every key, p = 0 one."""
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, name)
+    walks = w.batch * w.heads
+    maxb = w.n
+    sel_t = torch.full((walks, maxb), -1, dtype=torch.int32, device="cuda")
+    cnt_t = torch.zeros(walks, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = idx.dense_topp_attn(Qt, Kt, Vt, p, maxb, sel_tokens=sel_t, sel_count=cnt_t, status=status)
+    torch.cuda.synchronize()
+    assert int(status.cpu()[0]) == 0
+    sel_np, cnt = sel_t.cpu().numpy(), cnt_t.cpu().numpy()
+    outs = out.float().cpu().numpy()
+    stable = 0
+    for b in range(w.batch):
+        for h in range(w.heads):
+            wi = b * w.heads + h
+            g = h // w.group
+            k = int(cnt[wi])
+            got = sel_np[wi, :k].astype(np.int64)
+            assert k >= 1 and np.all(np.diff(got) > 0), (b, h)
+            lg = w.sharpness * (K[b, g].astype(np.float64) @ Q[b, h].astype(np.float64))
+            pm = np.exp(lg - lg.max())
+            pm /= pm.sum()
+            order = np.lexsort((np.arange(w.n), -lg))
+            cum = np.cumsum(pm[order])
+            if p >= 1.0:
+                assert k == w.n, (b, h)
+            elif p <= 0.0:
+                assert k == 1 and got[0] == order[0], (b, h)
+            else:
+                kw = int(np.searchsorted(cum, p)) + 1          # first prefix with mass >= p
+                kw = min(kw, w.n)
+                lo = cum[kw - 2] if kw >= 2 else 0.0
+                gap_mass = min(p - lo, cum[kw - 1] - p)
+                gap_lg = np.inf if kw >= w.n else lg[order[kw - 1]] - lg[order[kw]]
+                # the GPU's logits are fp32 sums (about 1e-5 off), which
+                # moves a prefix mass by about as much: a margin of 2e-5 in
+                # mass decides the prefix
+                if gap_mass > 2e-5 and gap_lg > P.GAP:
+                    stable += 1
+                    assert np.array_equal(got, np.sort(order[:kw])), (b, h)
+                else:
+                    # a valid prefix: nothing outside outranks a member by more
+                    # than the tolerance, and its mass crosses p within it
+                    inside = np.zeros(w.n, bool)
+                    inside[got] = True
+                    lo_in = lg[inside].min()
+                    assert (~inside).sum() == 0 or lg[~inside].max() <= lo_in + P.VALID_TOL, (b, h)
+                    mass = pm[inside].sum()
+                    least = got[np.argmin(lg[got])]
+                    assert mass >= p - P.VALID_TOL and mass - pm[least] < p + P.VALID_TOL, (b, h)
+            ref, _ = O.attend(got, Q[b, h].astype(np.float64), K[b, g].astype(np.float64),
+                              V[b, g].astype(np.float64), w.sharpness)
+            assert P.out_ok(outs[b, h], ref, w.dtype)[0], (b, h)
+    if 0.0 < p < 1.0:
+        # every walk was checked above; with thousands of keys the key at the
+        # crossing often carries less than 2e-4 of the mass, so a prefix
+        # decided with 1e-4 to spare on both sides is the minority
+        assert stable >= max(1, 0.05 * walks), stable
+
+
 # ---- prefill blocks ------------------------------------------------------------
 
 _pcache = {}

@@ -18,6 +18,7 @@
 // index wins.  Attention reuses the planned split-K kernels with token lists.
 #include "zha_device.h"
 #include "zha_internal.h"
+#include "zha_walk.h"
 
 namespace zha {
 
@@ -373,6 +374,177 @@ __global__ __launch_bounds__(kSelThreads) void k_dense_select(DenseArgs a) {
     if (tid == 0) a.sel_n[w] = static_cast<int32_t>(k);
 }
 
+// The bin, among nb bins (counts hc, integer masses hm), where the mass
+// summed from the highest bin down first reaches `need`; *s_mab / *s_cab =
+// the mass and the count in the bins above it.
+__device__ __forceinline__ void top_bin_mass(const uint32_t *hc, const unsigned long long *hm, int nb,
+                                             unsigned long long need, unsigned long long *s_wsum, uint32_t *s_bin,
+                                             unsigned long long *s_mab, uint32_t *s_cab) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int per = nb / kSelThreads;     // bins per thread (1 or 4), highest first
+    unsigned long long ms[4] = {0, 0, 0, 0}, tsum = 0;
+    uint32_t cs[4] = {0, 0, 0, 0}, csum = 0;
+    for (int e = 0; e < per; ++e) {
+        const int bin = nb - 1 - per * tid - e;
+        ms[e] = hm[bin];
+        cs[e] = hc[bin];
+        tsum += ms[e];
+        csum += cs[e];
+    }
+    // inclusive scans of mass and count over the threads (highest bins first)
+    unsigned long long im = tsum, ic = csum;
+    for (int off = 1; off < 64; off <<= 1) {
+        const unsigned long long om = __shfl_up(im, off, 64), oc = __shfl_up(ic, off, 64);
+        if (lane >= off) { im += om; ic += oc; }
+    }
+    if (lane == 63) { s_wsum[wave] = im; s_wsum[kSelWaves + wave] = ic; }
+    __syncthreads();
+    unsigned long long bm = 0, bc = 0;
+    for (int i = 0; i < wave; ++i) { bm += s_wsum[i]; bc += s_wsum[kSelWaves + i]; }
+    const unsigned long long em = bm + im - tsum, ec = bc + ic - csum;
+    if (em < need && em + tsum >= need) {
+        unsigned long long run = em, rc = ec;
+        for (int e = 0; e < per; ++e) {
+            if (run + ms[e] >= need) {
+                *s_bin = static_cast<uint32_t>(nb - 1 - per * tid - e);
+                *s_mab = run;
+                *s_cab = static_cast<uint32_t>(rc);
+                break;
+            }
+            run += ms[e];
+            rc += cs[e];
+        }
+    }
+    __syncthreads();
+}
+
+// Top-p over keys, one workgroup per walk: the length of the smallest prefix
+// of the keys ordered by (logit descending, index ascending) whose softmax
+// mass reaches p -- the integer masses of the tree's cuts, exp(l - max)*2^31
+// rounded, so the sums are exact -- written as the walk's budget for
+// k_dense_select, which then selects exactly that prefix.  Four reads of the
+// walk's logits: the maximum; a 12-bit histogram of the order-preserving key
+// bits with counts and masses (and the total mass); two 10-bit levels on the
+// keys of the crossing bin.  The keys equal to the crossing key all carry
+// the same mass, so the number of them to take is a division.  p >= 1
+// takes every key, p <= 0 the first one.
+__global__ __launch_bounds__(kSelThreads) void k_dense_topp_budget(DenseArgs a) {
+    const int w = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n = a.n_tokens;
+    const float *lg = a.logits + static_cast<int64_t>(w) * a.row_pad;
+    __shared__ uint32_t hc[4096];
+    __shared__ unsigned long long hm[4096];
+    __shared__ unsigned long long s_wsum[2 * kSelWaves];
+    __shared__ float s_red[kSelWaves];
+    __shared__ uint32_t s_bin, s_cab;
+    __shared__ unsigned long long s_mab;
+    int64_t k;
+    if (n < 1) {
+        k = 0;
+    } else if (a.p >= 1.f) {
+        k = n;
+    } else if (!(a.p > 0.f)) {
+        k = 1;
+    } else {
+        // pass 1: the largest logit
+        float m = -INFINITY;
+        for (int64_t i = tid; i < n; i += kSelThreads) m = fmaxf(m, lg[i]);
+        m = wave_max(m, 1, 64);
+        if (lane == 0) s_red[wave] = m;
+        __syncthreads();
+        float M = s_red[0];
+        for (int i = 1; i < kSelWaves; ++i) M = fmaxf(M, s_red[i]);
+        auto mass = [&](float v) -> unsigned long long {
+            return static_cast<unsigned long long>(__float2uint_rn(mass_exp(v - M) * kMassScale));
+        };
+        // pass 2: top 12 key bits, counts and masses; the total mass
+        for (int i = tid; i < 4096; i += kSelThreads) { hc[i] = 0; hm[i] = 0; }
+        __syncthreads();
+        unsigned long long z = 0;
+        for (int64_t i0 = tid; i0 < n; i0 += 4 * kSelThreads) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t i = i0 + u * kSelThreads;
+                v[u] = (i < n) ? lg[i] : -INFINITY;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (i0 + u * kSelThreads >= n) continue;
+                const uint32_t b = logit_key(v[u]) >> 20;
+                const unsigned long long wt = mass(v[u]);
+                atomicAdd(&hc[b], 1u);
+                if (wt) atomicAdd(&hm[b], wt);
+                z += wt;
+            }
+        }
+        for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+        if (lane == 0) s_wsum[wave] = z;
+        __syncthreads();
+        unsigned long long Z = 0;
+        for (int i = 0; i < kSelWaves; ++i) Z += s_wsum[i];
+        __syncthreads();
+        unsigned long long need = static_cast<unsigned long long>(ceil(static_cast<double>(a.p) * static_cast<double>(Z)));
+        if (need < 1) need = 1;
+        if (need > Z) need = Z;
+        top_bin_mass(hc, hm, 4096, need, s_wsum, &s_bin, &s_mab, &s_cab);
+        uint32_t prefix = s_bin << 20;
+        need -= s_mab;
+        int64_t above = s_cab;
+        // passes 3 and 4: the next 10 bits, then the last 10, of the keys
+        // that share the prefix so far
+        uint32_t tie_cnt = 0;
+        unsigned long long tie_mass = 0;
+        for (int lev = 0; lev < 2; ++lev) {
+            const int sh = lev == 0 ? 10 : 0;
+            __syncthreads();
+            for (int i = tid; i < 1024; i += kSelThreads) { hc[i] = 0; hm[i] = 0; }
+            __syncthreads();
+            for (int64_t i0 = tid; i0 < n; i0 += 4 * kSelThreads) {
+                float v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int64_t i = i0 + u * kSelThreads;
+                    v[u] = (i < n) ? lg[i] : -INFINITY;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (i0 + u * kSelThreads >= n) continue;
+                    const uint32_t key = logit_key(v[u]);
+                    if ((key >> (sh + 10)) != (prefix >> (sh + 10))) continue;
+                    const uint32_t b = (key >> sh) & 1023u;
+                    const unsigned long long wt = mass(v[u]);
+                    atomicAdd(&hc[b], 1u);
+                    if (wt) atomicAdd(&hm[b], wt);
+                }
+            }
+            __syncthreads();
+            top_bin_mass(hc, hm, 1024, need, s_wsum, &s_bin, &s_mab, &s_cab);
+            prefix |= s_bin << sh;
+            need -= s_mab;
+            above += s_cab;
+            tie_cnt = hc[s_bin];
+            tie_mass = hm[s_bin];
+        }
+        // keys equal to the crossing key: equal masses; take as many as the
+        // remaining need asks for, lowest index first (k_dense_select)
+        const unsigned long long wt = tie_cnt ? tie_mass / tie_cnt : 0ull;
+        int64_t take = wt ? static_cast<int64_t>((need + wt - 1) / wt) : static_cast<int64_t>(tie_cnt);
+        if (take > tie_cnt) take = tie_cnt;
+        if (take < 1) take = 1;
+        k = above + take;
+    }
+    if (tid == 0) {
+        int64_t kk = k;
+        if (kk > a.max_budget) {
+            kk = a.max_budget;
+            if (a.status) atomicOr(a.status, ZHA_FLAG_SEL_OVERFLOW);
+        }
+        a.budget_out[w] = static_cast<int32_t>(kk);
+    }
+}
+
 hipError_t launch_dense(const DenseArgs &a, int D, int dtype, hipStream_t st) {
     if (a.walks <= 0 || a.n_tokens <= 0) return hipSuccess;
     const int pairs = a.walks / a.heads * a.kv_heads;
@@ -401,6 +573,12 @@ hipError_t launch_dense(const DenseArgs &a, int D, int dtype, hipStream_t st) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.budget_out) {
+        // top-p over keys: each walk's prefix length first
+        hipLaunchKernelGGL(k_dense_topp_budget, dim3(a.walks), dim3(kSelThreads), 0, st, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(k_dense_select, dim3(a.walks), dim3(kSelThreads), 0, st, a);
     return hipGetLastError();
 }

@@ -560,7 +560,7 @@ zha_status do_attn(const zha_tree *t, const void *q, int32_t qph, const void *k_
 uint64_t dense_row_pad(const zha_geometry &g) { return (uint64_t(g.max_tokens) + 3) / 4 * 4; }
 
 struct DenseWs {
-    uint64_t logits, sel, sel_n, attn, total;
+    uint64_t logits, sel, sel_n, budget, attn, total;
 };
 DenseWs dense_ws_layout(const zha_tree *t, int32_t max_budget) {
     const zha_geometry &g = t->geom;
@@ -569,7 +569,8 @@ DenseWs dense_ws_layout(const zha_tree *t, int32_t max_budget) {
     l.logits = 0;
     l.sel = align_up(walks * dense_row_pad(g) * sizeof(float));
     l.sel_n = l.sel + align_up(walks * uint64_t(max_budget) * sizeof(int32_t));
-    l.attn = l.sel_n + align_up(walks * sizeof(int32_t));
+    l.budget = l.sel_n + align_up(walks * sizeof(int32_t));
+    l.attn = l.budget + align_up(walks * sizeof(int32_t));
     l.total = l.attn + attn_ws_layout(g.head_dim, max_budget, walks).total;
     return l;
 }
@@ -846,16 +847,19 @@ uint64_t zha_dense_workspace_bytes(const zha_tree *t, int32_t max_budget) {
     return dense_ws_layout(t, max_budget).total;
 }
 
-zha_status zha_dense_topk_attn(const zha_tree *t, const void *q, const void *k_cache,
-                               const void *v_cache, const int32_t *budget, int32_t max_budget,
-                               void *out, int32_t *sel_tokens, void *ws, uint64_t ws_bytes,
-                               void *stream) {
+// Both dense baselines: logits, the selection (budget per walk given, or
+// from top-p over keys when budget is null), then attention.
+zha_status dense_attn(const zha_tree *t, const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *budget, float p, int32_t max_budget, void *out, int32_t *sel_tokens,
+                      int32_t *sel_count, uint32_t *status, void *ws, uint64_t ws_bytes, void *stream) {
     zha_status s = check_tree(t);
     if (s != ZHA_OK) return s;
     if (max_budget < 1) return ZHA_ERR_ARG;
-    if (!q || !k_cache || !v_cache || !budget || !out || !ws) return ZHA_ERR_ARG;
+    if (!q || !k_cache || !v_cache || !out || !ws) return ZHA_ERR_ARG;
+    if (!budget && !isfinite(p)) return ZHA_ERR_ARG;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-        !aligned16(ws) || !aligned_n(budget, 4) || (sel_tokens && !aligned_n(sel_tokens, 4)))
+        !aligned16(ws) || (budget && !aligned_n(budget, 4)) || (sel_tokens && !aligned_n(sel_tokens, 4)) ||
+        (sel_count && !aligned_n(sel_count, 4)) || (status && !aligned_n(status, 4)))
         return ZHA_ERR_ALIGN;
     if (ws_bytes < zha_dense_workspace_bytes(t, max_budget)) return ZHA_ERR_WORKSPACE;
     const zha_geometry &g = t->geom;
@@ -866,10 +870,13 @@ zha_status zha_dense_topk_attn(const zha_tree *t, const void *q, const void *k_c
     memset(&a, 0, sizeof(a));
     a.q = q;
     a.k = k_cache;
-    a.budget = budget;
+    a.budget_out = budget ? nullptr : reinterpret_cast<int32_t *>(wb + lay.budget);
+    a.budget = budget ? budget : a.budget_out;
+    a.status = status;
+    a.p = p;
     a.logits = reinterpret_cast<float *>(wb + lay.logits);
     a.sel = sel_tokens ? sel_tokens : reinterpret_cast<int32_t *>(wb + lay.sel);
-    a.sel_n = reinterpret_cast<int32_t *>(wb + lay.sel_n);
+    a.sel_n = sel_count ? sel_count : reinterpret_cast<int32_t *>(wb + lay.sel_n);
     a.max_tokens = g.max_tokens;
     a.n_tokens = t->n_tokens;
     a.row_pad = static_cast<int64_t>(dense_row_pad(g));
@@ -883,6 +890,23 @@ zha_status zha_dense_topk_attn(const zha_tree *t, const void *q, const void *k_c
     if (s != ZHA_OK) return s;
     return do_attn(t, q, 1, k_cache, v_cache, nullptr, a.sel, a.sel_n, max_budget, max_budget, out,
                    wb + lay.attn, st);
+}
+
+zha_status zha_dense_topk_attn(const zha_tree *t, const void *q, const void *k_cache,
+                               const void *v_cache, const int32_t *budget, int32_t max_budget,
+                               void *out, int32_t *sel_tokens, void *ws, uint64_t ws_bytes,
+                               void *stream) {
+    if (!budget) return ZHA_ERR_ARG;
+    return dense_attn(t, q, k_cache, v_cache, budget, 0.f, max_budget, out, sel_tokens, nullptr, nullptr, ws,
+                      ws_bytes, stream);
+}
+
+zha_status zha_dense_topp_attn(const zha_tree *t, const void *q, const void *k_cache,
+                               const void *v_cache, float p, int32_t max_budget, void *out,
+                               int32_t *sel_tokens, int32_t *sel_count, uint32_t *status, void *ws,
+                               uint64_t ws_bytes, void *stream) {
+    return dense_attn(t, q, k_cache, v_cache, nullptr, p, max_budget, out, sel_tokens, sel_count, status, ws,
+                      ws_bytes, stream);
 }
 
 zha_status zha_bw_probe(const void *buf, uint64_t bytes, float *sink, void *stream) {

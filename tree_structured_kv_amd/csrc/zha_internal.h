@@ -201,6 +201,9 @@ struct DenseArgs {
     const void *q;                 // [walks][D]
     const void *k;                 // cache
     const int32_t *budget;         // [walks]
+    int32_t *budget_out;           // top-p over keys: ws [walks], written by k_dense_topp_budget
+    uint32_t *status;              // top-p over keys: flags (nullable)
+    float p;                       // top-p over keys: the mass to reach
     float *logits;                 // ws [walks][row_pad]
     int32_t *sel;                  // [walks][max_budget] selected token ids, ascending
     int32_t *sel_n;                // [walks]

@@ -71,7 +71,7 @@ STATS_WORDS = ctypes.sizeof(WalkStats) // 4   # int32 words per stats record
 EXPORTS = ["zha_tree_bytes", "zha_depth_for", "zha_tree_init", "zha_build", "zha_append",
            "zha_search_workspace_bytes", "zha_search_engine", "zha_search", "zha_visited_words", "zha_attn_workspace_bytes", "zha_attn_engine",
            "zha_sparse_attn", "zha_sparse_attn_noalloc", "zha_forward_workspace_bytes", "zha_forward",
-           "zha_dense_workspace_bytes", "zha_dense_topk_attn", "zha_bw_probe",
+           "zha_dense_workspace_bytes", "zha_dense_topk_attn", "zha_dense_topp_attn", "zha_bw_probe",
            "zha_status_string"]
 
 
@@ -100,6 +100,7 @@ def _load():
         "zha_forward": (i32, [tp, i64, vp, i32, vp, vp, sp, vp, vp, vp, vp, u64, vp]),
         "zha_dense_workspace_bytes": (u64, [tp, i32]),
         "zha_dense_topk_attn": (i32, [tp, vp, vp, vp, vp, i32, vp, vp, vp, u64, vp]),
+        "zha_dense_topp_attn": (i32, [tp, vp, vp, vp, ctypes.c_float, i32, vp, vp, vp, vp, vp, u64, vp]),
         "zha_bw_probe": (i32, [vp, u64, vp, vp]),
         "zha_status_string": (ctypes.c_char_p, [i32]),
     }
@@ -357,6 +358,24 @@ def zha_dense_topk_attn(t: TreeHandle, q, k_cache, v_cache, budget, max_budget: 
            "zha_dense_topk_attn")
 
 
+def zha_dense_topp_attn(t: TreeHandle, q, k_cache, v_cache, p: float, max_budget: int, out, ws,
+                        sel_tokens=None, sel_count=None, status=None, stream=None):
+    walks = _geom_of(t)[2]
+    _need_rows(t, q, "q", 1)
+    _need_rows(t, out, "out", 1)
+    _need_cache(t, k_cache, "k_cache")
+    _need_cache(t, v_cache, "v_cache")
+    _need(sel_tokens, "sel_tokens", torch.int32, min_numel=walks * int(max_budget))
+    _need(sel_count, "sel_count", torch.int32, min_numel=walks)
+    _need(status, "status", min_bytes=4)
+    _need(ws, "ws")
+    wsb = ws.numel() * ws.element_size()
+    _check(lib.zha_dense_topp_attn(ctypes.byref(t), _ptr(q), _ptr(k_cache), _ptr(v_cache), float(p),
+                                   int(max_budget), _ptr(out), _ptr(sel_tokens), _ptr(sel_count),
+                                   _ptr(status), _ptr(ws), wsb, _stream(stream)),
+           "zha_dense_topp_attn")
+
+
 def zha_bw_probe(buf, sink, stream=None):
     _need(buf, "buf")
     _need(sink, "sink", torch.float32, min_numel=1)
@@ -480,6 +499,16 @@ class Index:
             ws = self.dense_workspace(max_budget)
         zha_dense_topk_attn(self.handle, q, k_cache, v_cache, budget, max_budget, out, ws,
                             sel_tokens, stream)
+        return out
+
+    def dense_topp_attn(self, q, k_cache, v_cache, p, max_budget, out=None, ws=None, sel_tokens=None,
+                        sel_count=None, status=None, stream=None):
+        if out is None:
+            out = torch.empty_like(q)
+        if ws is None:
+            ws = self.dense_workspace(max_budget)
+        zha_dense_topp_attn(self.handle, q, k_cache, v_cache, p, max_budget, out, ws, sel_tokens, sel_count,
+                            status, stream)
         return out
 
     def forward_workspace(self, sel: Select, qph: int = 1):
