@@ -807,8 +807,8 @@ def dominant_kernel(workload, res):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode-256K-topp", choices=sorted(WORKLOADS))
     ap.add_argument("--also", default="decode-1M-topp,decode-64K-topp,decode-256K-topk64,"
                                       "decode-256K-topp-bf16keys,decode-1M-topp-bf16keys",

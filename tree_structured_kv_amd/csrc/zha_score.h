@@ -84,15 +84,23 @@ __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair,
             const int lvl = static_cast<int>(id >> kLevelShift);
             const int64_t node = pair * a.cap[lvl] + static_cast<int64_t>(id & kIndexMask);
             const ST *kp = reinterpret_cast<const ST *>(a.kap[lvl]) + node * (R * D);
-            float bsr[R];
+            // the R biases: up to 8 come in through scalar loads (one set
+            // per candidate in flight); with more, each lane loads its own
+            // reference's (kU x 16 scalar values would not fit the SGPRs)
+            constexpr bool kScalarBias = R <= 8;
+            float bsr[kScalarBias ? R : 1];
+            const float *bp = a.bet[lvl] + node * R;
             if (kFresh && lvl <= fresh->m && static_cast<int64_t>(id & kIndexMask) == fresh->j[lvl]) {
                 // made by this launch: the workgroup's own copy in LDS
                 kp = reinterpret_cast<const ST *>(fresh->k[lvl]);
+                bp = fresh->b[lvl];
+                if constexpr (kScalarBias) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) bsr[r] = fresh->b[lvl][r];
-            } else {
+                    for (int r = 0; r < R; ++r) bsr[r] = bp[r];
+                }
+            } else if constexpr (kScalarBias) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) bsr[r] = cload_f(a.bet[lvl] + node * R + r);
+                for (int r = 0; r < R; ++r) bsr[r] = cload_f(bp + r);
             }
 #pragma unroll
             for (int l = 0; l < NL; ++l) {
@@ -102,12 +110,16 @@ __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair,
                         Vec16<ST>::load(kp + r * D + EPL * sub, kv[u][l]);
                     else
                         Vec4<ST>::load(kp + r * D + EPL * sub, kv[u][l]);
-                    // this lane's reference r = l*RPL + rsub, chosen among SGPRs
-                    float b = bsr[l * RPL];
+                    if constexpr (kScalarBias) {
+                        // this lane's reference r = l*RPL + rsub, chosen among SGPRs
+                        float b = bsr[l * RPL];
 #pragma unroll
-                    for (int g = 1; g < RPL; ++g)
-                        if (rsub == g && l * RPL + g < R) b = bsr[l * RPL + g];
-                    bv[u][l] = b;
+                        for (int g = 1; g < RPL; ++g)
+                            if (rsub == g && l * RPL + g < R) b = bsr[l * RPL + g];
+                        bv[u][l] = b;
+                    } else {
+                        bv[u][l] = bp[r];
+                    }
                 } else {
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) kv[u][l][e] = 0.f;
