@@ -583,13 +583,13 @@ def test_dense_topp_baseline(Z, name, p):
 _pcache = {}
 
 
-def _prefill_setup(Z):
+def _prefill_setup(Z, T=128):
     """A streamed cache (chunk 16, R 8, 3 levels) with a ragged prefix of
-    T0 = 2*4096 + 300 tokens already in the tree and a block of T = 128
-    queries per head at positions T0 .. T0+127 whose K/V rows are written."""
-    if "p" in _pcache:
-        return _pcache["p"]
-    T0, T = 2 * 4096 + 300, 128
+    T0 = 2*4096 + 300 tokens already in the tree and a block of T (128)
+    queries per head at positions T0 .. T0+T-1 whose K/V rows are written."""
+    if ("p", T) in _pcache:
+        return _pcache[("p", T)]
+    T0 = 2 * 4096 + 300
     w = replace(S.WORKLOADS[3].scaled(n=T0 + T, batch=1), kv_heads=2)
     K, V, _, R = P.make_inputs(w)
     Q = np.zeros((w.batch, w.heads, T, w.d), np.float32)
@@ -605,16 +605,20 @@ def _prefill_setup(Z):
     idx = Z.Index(geom, torch.from_numpy(R))
     idx.build(Kt, T0)
     trees = {(0, g): P.oracle_tree(w, K, R, 0, g, T0) for g in range(w.kv_heads)}
-    _pcache["p"] = (w, T0, T, K, V, Q, R, Kt, Vt, Qt, idx, trees)
-    return _pcache["p"]
+    _pcache[("p", T)] = (w, T0, T, K, V, Q, R, Kt, Vt, Qt, idx, trees)
+    return _pcache[("p", T)]
 
 
-@pytest.mark.parametrize("engine", ["persistent", "level-sync", "block"])
+@pytest.mark.parametrize("engine,T", [("persistent", 128), ("level-sync", 128), ("block", 128),
+                                      ("level-sync", 160)])
 @pytest.mark.parametrize("sname", ["topp90", "topk4", "open-all"])
-def test_prefill_block(Z, sname, engine):
+def test_prefill_block(Z, sname, engine, T):
     """Prefill: every query of the block walks the tree of the tokens before
-    the block, then attends its selection plus the block's keys up to itself."""
-    w, T0, T, K, V, Q, R, Kt, Vt, Qt, idx, trees = _prefill_setup(Z)
+    the block, then attends its selection plus the block's keys up to itself.
+    The level-synchronous scorer orders its tiles itself up to 4,096 walks
+    (32 heads x 128 queries) and takes the tiles the cut kernels register
+    beyond (x 160)."""
+    w, T0, T, K, V, Q, R, Kt, Vt, Qt, idx, trees = _prefill_setup(Z, T)
     select = dict(mode="topp", p=1.0) if sname == "open-all" else SELECTS[sname]
     sel = P.select_struct(Z, select, T0 // w.chunk, engine=engine)
     bufs = idx.search(Qt, sel, qph=T)

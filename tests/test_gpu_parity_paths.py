@@ -206,6 +206,45 @@ def test_full_size_late_prefill_block(Z):
     assert stable >= 0.3 * len(rows), (stable, len(rows))
 
 
+# ---- a pair that finishes inside the union engine before the hand-over ----------
+
+@pytest.mark.parametrize("n", [256 * 80 + 14, 256 * 20 + 14])
+@pytest.mark.parametrize("select", [dict(mode="topk", k=(1,)), dict(mode="topp", p=0.9)])
+def test_union_pair_done_before_handover(Z, n, select):
+    """Chunk 4, 4 levels, 8 heads per KV head: the union engine runs the
+    first steps and the level-synchronous engine the last two.  On pair 0 one
+    parentless level-1 chunk points along the heads' mean query, so every
+    head opens only that root at the first step and the pair's walks end
+    there: with 83 roots inside the grid-wide union cut, with 23 inside the
+    fused first step.  The level-synchronous steps must leave those walks as
+    they are; pair 1 (plain keys) walks to the bottom.  Every walk against
+    the oracle."""
+    w = replace(S.WORKLOADS[1], n=n, batch=1, kv_heads=2, group=8, chunk=4, refs=4, levels=4)
+    K, V, Q, R = P.make_inputs(w)
+    hot = (n // 4 - 2) * 4                     # the middle one of the three parentless chunks
+    u = Q[0, :8].astype(np.float64).mean(0)
+    u *= 8.0 * np.linalg.norm(K[0, 0], axis=1).mean() / np.linalg.norm(u)
+    K[0, 0, hot:hot + 4] = S.round_bf16(np.repeat(u[None, :].astype(np.float32), 4, 0))
+    Kt, Vt, Qt, idx = _device(Z, w, K, V, Q, R, n)
+    trees = [P.oracle_tree(w, K, R, 0, g, n) for g in range(2)]
+    blocks, count, stats, outs, status = _run(Z, idx, Qt, Kt, Vt, select, "union")
+    assert status == 0
+    done_early = 0
+    for h in range(w.heads):
+        g = h // w.group
+        q = Q[0, h]
+        sel_o, st_o = P.oracle_walk(trees[g], q, select)
+        if g == 0:
+            assert st_o["steps"] == 1 and st_o["gap"] > P.GAP, (h, st_o["steps"])   # the case holds
+            done_early += 1
+        toks = P.gpu_tokens(blocks[h], count[h], w.chunk, n)
+        _check_walk(trees[g], q, select, blocks[h, :count[h]], toks, stats[h], sel_o, st_o, (h, n))
+        ref, _ = O.attend(toks, q.astype(np.float64), K[0, g].astype(np.float64),
+                          V[0, g].astype(np.float64), w.sharpness)
+        assert P.out_ok(outs[0, h], ref, w.dtype)[0], h
+    assert done_early == 8
+
+
 # ---- the length sweep's deep trees --------------------------------------------------
 
 @pytest.mark.parametrize("n,levels", [(1 << 20, None), (1 << 20, 9), (1 << 22, None)])

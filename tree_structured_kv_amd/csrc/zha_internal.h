@@ -16,6 +16,7 @@ constexpr int kBlock = 256;          // threads per workgroup of most kernels
 constexpr int kChunkMin = 512;       // keys per attention work item: the planner picks 512 .. 2048
 constexpr int kChunkMax = 2048;      // (more, smaller items when a call reads few keys)
 constexpr int kTile = 32;            // candidates per tile of the level-synchronous scorer
+constexpr int kPlanWalks = 4096;     // walks up to which that scorer orders its tiles itself (in LDS)
 constexpr int kFlatPad = 32;         // union engine: each run of scoring entries is padded to this
 constexpr int kExpSlices = 8;        // union engine: workgroups (runs) per pair building the next list
 constexpr int kSmallList = 64;       // union engine: list bound of the steps fused into one launch

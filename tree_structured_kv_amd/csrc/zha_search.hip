@@ -137,19 +137,85 @@ __global__ __launch_bounds__(kThreads) void k_ls_init(SearchArgs a) {
     }
 }
 
-// Step t scoring over a flat tile list: at step 0 every walk has the same
-// roots, so its tiles are laid out arithmetically; later steps use the tiles
-// the cut kernel of the step before registered.
+// Step t scoring over tiles of kTile candidates of one walk.  The tiles are
+// taken in walk order -- a pair's heads are consecutive walks whose lists,
+// all in span order, overlap -- and XCD x takes the x-th eighth of that
+// order with its workgroups side by side, so the heads of a pair read the
+// node records they share through one L2 at about the same time.  Step 0's
+// tiles are arithmetic (every walk has the same roots).  Later steps count
+// each walk's tiles from its state (the walks whose cut at step t needs
+// scores) in LDS when there are at most kPlanWalks walks, else take the
+// tiles the cut kernels registered.
 template <int D, int R, typename QT, typename ST>
 __global__ __launch_bounds__(kScoreThreads) void k_ls_score(SearchArgs a, int t, int tiles0) {
     constexpr int kSW = kScoreThreads / 64;
+    __shared__ int s_first[kPlanWalks + 1];    // each walk's first tile, then the total
+    __shared__ int s_part[kSW];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n_tiles = (t == 0) ? a.walks * tiles0 : a.tile_count[t];
-    for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const bool plan = t > 0 && ls_tile_plan(a);
+    int n_tiles;
+    if (t == 0) {
+        n_tiles = a.walks * tiles0;
+    } else if (!plan) {
+        n_tiles = a.tile_count[t];
+    } else {
+        for (int w = threadIdx.x; w < a.walks; w += kScoreThreads) {
+            const int n = a.state[w].n;
+            s_first[w] = (n > 0 && !step_forced(a, t, n)) ? (n + kTile - 1) / kTile : 0;
+        }
+        __syncthreads();
+        // exclusive scan: each thread a run of consecutive walks
+        const int per = (a.walks + kScoreThreads - 1) / kScoreThreads;
+        const int w0 = min(a.walks, static_cast<int>(threadIdx.x) * per);
+        const int w1 = min(a.walks, w0 + per);
+        int sum = 0;
+        for (int w = w0; w < w1; ++w) sum += s_first[w];
+        int incl = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
+        }
+        if (lane == 63) s_part[wave] = incl;
+        __syncthreads();
+        int run = incl - sum, total = 0;
+#pragma unroll
+        for (int k = 0; k < kSW; ++k) {
+            const int v = s_part[k];
+            if (k < wave) run += v;
+            total += v;
+        }
+        for (int w = w0; w < w1; ++w) {
+            const int v = s_first[w];
+            s_first[w] = run;
+            run += v;
+        }
+        if (threadIdx.x == 0) s_first[a.walks] = total;
+        __syncthreads();
+        n_tiles = total;
+    }
+    // workgroups go to the XCDs in turn; the host makes the grid a multiple
+    // of kXcds
+    const int x = blockIdx.x % kXcds, per_x = max(1, static_cast<int>(gridDim.x) / kXcds);
+    const int first = static_cast<int>(static_cast<int64_t>(n_tiles) * x / kXcds) + static_cast<int>(blockIdx.x) / kXcds;
+    const int end = static_cast<int>(static_cast<int64_t>(n_tiles) * (x + 1) / kXcds);
+    int pw = 0;                                // walk of the current tile (plan)
+    if (plan && first < end) {
+        int hi = a.walks;                      // s_first[pw] <= first < s_first[hi]
+        while (hi - pw > 1) {
+            const int mid = (pw + hi) >> 1;
+            if (s_first[mid] <= first) pw = mid; else hi = mid;
+        }
+    }
+    for (int tile = first; tile < end; tile += per_x) {
         int w, start;
         if (t == 0) {
             w = tile / tiles0;
             start = (tile % tiles0) * kTile;
+        } else if (plan) {
+            while (s_first[pw + 1] <= tile) ++pw;
+            w = __builtin_amdgcn_readfirstlane(pw);
+            start = __builtin_amdgcn_readfirstlane((tile - s_first[pw]) * kTile);
         } else {
             const int2 e = a.tile_map[tile];
             w = __builtin_amdgcn_readfirstlane(e.x);
@@ -157,7 +223,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_ls_score(SearchArgs a, int t,
         }
         const int n = a.state[w].n;
         const int buf = a.state[w].buf;
-        const int end = min(n, start + kTile);
+        const int end_w = min(n, start + kTile);
         const int64_t pair = walk_pair(w, a.qph, a.heads, a.group, a.kv_heads);
         const uint32_t *cur = a.cand + static_cast<int64_t>(w) * 2 * a.cand_cap +
                               static_cast<int64_t>(buf) * a.cand_cap;
@@ -165,7 +231,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_ls_score(SearchArgs a, int t,
         float qv[row_epl<D, ST>()];
         load_q<D, QT, ST>(a, w, qv);
         uint32_t flags = 0;
-        (void)score_wave<D, R, ST, true>(a, pair, qv, cur, sc, start + wave * kU, end, kSW * kU, flags);
+        (void)score_wave<D, R, ST, true>(a, pair, qv, cur, sc, start + wave * kU, end_w, kSW * kU, flags);
         if (flags && lane == 0) atomicOr(a.status, flags);
     }
 }
@@ -253,12 +319,13 @@ __global__ __launch_bounds__(kThreads) void k_ls_cut(SearchArgs a, int t) {
         }
         a.state[w] = st;
         s_base = 0;
-        if (st.n > 0 && !step_forced(a, t + 1, st.n))
+        if (!ls_tile_plan(a) && st.n > 0 && !step_forced(a, t + 1, st.n))
             s_base = atomicAdd(&a.tile_count[t + 1], (st.n + kTile - 1) / kTile);
     }
     __syncthreads();
-    // register the next step's tiles unless its cut needs no scores
-    if (st.n > 0 && !step_forced(a, t + 1, st.n)) {
+    // register the next step's tiles unless its cut needs no scores (or the
+    // scorer counts them itself)
+    if (!ls_tile_plan(a) && st.n > 0 && !step_forced(a, t + 1, st.n)) {
         const int ntile = (st.n + kTile - 1) / kTile;
         for (int k = tid; k < ntile; k += kThreads) a.tile_map[s_base + k] = make_int2(w, k * kTile);
     }

@@ -369,11 +369,11 @@ __global__ __launch_bounds__(kThreads) void k_top_cut(SearchArgs a) {
         }
         a.state[w] = st;
         s_base = 0;
-        if (st.n > 0 && !step_forced(a, t, st.n))
+        if (!ls_tile_plan(a) && st.n > 0 && !step_forced(a, t, st.n))
             s_base = atomicAdd(&a.tile_count[t], (st.n + kTile - 1) / kTile);
     }
     __syncthreads();
-    if (st.n > 0 && !step_forced(a, t, st.n)) {
+    if (!ls_tile_plan(a) && st.n > 0 && !step_forced(a, t, st.n)) {
         const int ntile = (st.n + kTile - 1) / kTile;
         for (int k = tid; k < ntile; k += kThreads) a.tile_map[s_base + k] = make_int2(w, k * kTile);
     }

@@ -708,7 +708,10 @@ __device__ __forceinline__ void expand_slice(const SearchArgs &a, int t, int p, 
         const int w = head_walk(a, p, tid);
         WalkState *st = a.state + w;
         if (overflow) st->flags |= ZHA_FLAG_CAND_OVERFLOW;
-        if (last) finish_walk<R>(a, w, st->steps, st->scored, st->opened, st->sel_n, st->unforced, st->flags);
+        if (last) {
+            st->n = 0;                             // finished: later level-synchronous steps skip it
+            finish_walk<R>(a, w, st->steps, st->scored, st->opened, st->sel_n, st->unforced, st->flags);
+        }
     }
 }
 
@@ -972,7 +975,10 @@ __global__ __launch_bounds__(kThreads) void k_un_small(SearchArgs a, int steps) 
             st->steps = T.steps[h];
             st->flags = fl;
             a.u_next[w] = T.nopen[h];
-            if (last) finish_walk<R>(a, w, T.steps[h], T.scored[h], T.opened[h], T.sel_n[h], T.unforced[h], fl);
+            if (last) {
+                st->n = 0;
+                finish_walk<R>(a, w, T.steps[h], T.scored[h], T.opened[h], T.sel_n[h], T.unforced[h], fl);
+            }
         }
         // each head's opened entries of D_s, as list positions for the next cut
         for (int i = tid; i < G * kSmallList; i += kThreads) {
@@ -1021,11 +1027,11 @@ __device__ __forceinline__ void to_ls_walk(const SearchArgs &a, int t, int w) {
         }
         a.state[w] = st;
         s_base = 0;
-        if (st.n > 0 && !step_forced(a, t + 1, st.n))
+        if (!ls_tile_plan(a) && st.n > 0 && !step_forced(a, t + 1, st.n))
             s_base = atomicAdd(&a.tile_count[t + 1], (st.n + kTile - 1) / kTile);
     }
     __syncthreads();
-    if (st.n > 0 && !step_forced(a, t + 1, st.n)) {
+    if (!ls_tile_plan(a) && st.n > 0 && !step_forced(a, t + 1, st.n)) {
         const int ntile = (st.n + kTile - 1) / kTile;
         for (int k = tid; k < ntile; k += kThreads) a.tile_map[s_base + k] = make_int2(w, k * kTile);
     }

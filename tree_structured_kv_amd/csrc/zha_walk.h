@@ -33,6 +33,11 @@ __device__ __forceinline__ bool step_forced(const SearchArgs &a, int t, int n) {
     return (n <= 1) || (a.mode == ZHA_TOPK && a.k[t] >= n) || (a.mode == ZHA_TOPP && a.p >= 1.0f);
 }
 
+// Whether the level-synchronous scorer counts each walk's tiles itself from
+// the walk states (else the kernel that sets a walk's next list registers
+// its tiles in tile_map).
+__device__ __forceinline__ bool ls_tile_plan(const SearchArgs &a) { return a.walks <= kPlanWalks; }
+
 // Workgroup: the roots -- every level-L node, then the nodes of lower levels
 // whose parent chunk is not full yet, in span order.  Returns their number
 // (clamped to the candidate capacity).
