@@ -273,6 +273,58 @@ __device__ __forceinline__ unsigned long long cut_tau(const SearchArgs &a, int n
     return tau;
 }
 
+// Wavefront, at most 64 candidates, one per lane (key 0 and weight 0 on the
+// other lanes): the cut key of cut_tau -- the rank key of the candidate at
+// which the weight summed in decreasing key order first reaches what the
+// step needs (weights and need exactly as there) -- by a bitonic sort of the
+// (key, weight) pairs across the lanes (keys are distinct: they hold the
+// span start), an inclusive scan of the weights and a ballot.
+__device__ __forceinline__ unsigned long long lane_tau(const SearchArgs &a, bool in, float v, uint32_t id, float mx, int n, int kt) {
+    const int lane = threadIdx.x & 63;
+    const bool by_mass = (a.mode == ZHA_TOPP) && (a.p > 0.f);
+    const bool flat = !(mx > -INFINITY);   // every score -inf: equal masses
+    uint32_t wt = 0u;
+    if (in) wt = by_mass ? __float2uint_rn((flat ? 1.f : mass_exp(v - mx)) * kMassScale) : 1u;
+    unsigned long long key = in ? rank_key(v, id, a.log2c) : 0ull;
+    unsigned long long need;
+    if (by_mass) {
+        unsigned long long z = wt;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+        const double tq = ceil(static_cast<double>(a.p) * static_cast<double>(z));
+        need = static_cast<unsigned long long>(tq);
+        if (need < 1) need = 1;
+        if (need > z) need = z;
+    } else {
+        const int m = (a.mode == ZHA_TOPK) ? (kt < n ? kt : n) : 1;
+        need = static_cast<unsigned long long>(m < 1 ? 1 : m);
+    }
+    // descending bitonic sort over the 64 lanes
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const unsigned long long ok = __shfl_xor(key, j, 64);
+            const uint32_t ow = static_cast<uint32_t>(__shfl_xor(static_cast<int>(wt), j, 64));
+            const bool lower = (lane & j) == 0, desc = (lane & k) == 0;
+            const bool take = (lower == desc) ? (ok > key) : (ok < key);
+            if (take) {
+                key = ok;
+                wt = ow;
+            }
+        }
+    }
+    unsigned long long incl = wt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const unsigned long long o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    const unsigned long long hit = __ballot(lane < n && incl >= need);
+    const int first = hit ? (__ffsll(static_cast<long long>(hit)) - 1) : (n - 1);
+    return __shfl(key, first, 64);
+}
+
 // Bin of score v in a window of 256 bins counted down from `top` (bin 0
 // holds the highest scores; values below the window fall in bin 255).
 // Monotone: a higher score never lands in a higher bin.
@@ -302,6 +354,20 @@ __device__ __forceinline__ unsigned long long cut_tau_win(const SearchArgs &a, i
     if (!(mx > -INFINITY)) {
         if (path) *path |= kPathTieSelect;
         return cut_tau<U>(a, n, cur, sc, mx, kt, sh);
+    }
+    if (n <= 64) {
+        // one candidate per lane of wavefront 0: the sort-based cut
+        if (wave == 0) {
+            const bool in = lane < n;
+            const float v = in ? sc[lane] : -INFINITY;
+            const uint32_t id = in ? cur[lane] : 0u;
+            const unsigned long long k = lane_tau(a, in, v, id, mx, n, kt);
+            if (lane == 0) sh.tau = k;
+        }
+        __syncthreads();
+        const unsigned long long tau = sh.tau;
+        __syncthreads();
+        return tau;
     }
     const bool by_mass = (a.mode == ZHA_TOPP) && (a.p > 0.f);
     // total weight and the lowest finite score
@@ -443,70 +509,24 @@ __device__ __forceinline__ unsigned long long cut_tau_win(const SearchArgs &a, i
         sh.sw[r] = sh.fw[tid];
     }
     __syncthreads();
-    if (tid == 0) {
-        unsigned long long run = 0, tau = nf > 0 ? sh.skey[nf - 1] : 0ull;
-        for (int r = 0; r < nf; ++r) {
-            run += sh.sw[r];
-            if (run >= need) { tau = sh.skey[r]; break; }
+    if (wave == 0) {
+        // the first rank whose running weight reaches what is still needed
+        // (kWinFinal = one per lane): a scan and a ballot
+        const unsigned long long wv = lane < nf ? sh.sw[lane] : 0ull;
+        unsigned long long incl = wv;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const unsigned long long o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
         }
-        sh.tau = tau;
+        const unsigned long long hit = __ballot(lane < nf && incl >= need);
+        const int r = hit ? (__ffsll(static_cast<long long>(hit)) - 1) : nf - 1;
+        if (lane == 0) sh.tau = nf > 0 ? sh.skey[r] : 0ull;
     }
     __syncthreads();
     const unsigned long long tau = sh.tau;
     __syncthreads();
     return tau;
-}
-
-// Wavefront, at most 64 candidates, one per lane (key 0 and weight 0 on the
-// other lanes): the cut key of cut_tau -- the rank key of the candidate at
-// which the weight summed in decreasing key order first reaches what the
-// step needs (weights and need exactly as there) -- by a bitonic sort of the
-// (key, weight) pairs across the lanes (keys are distinct: they hold the
-// span start), an inclusive scan of the weights and a ballot.
-__device__ __forceinline__ unsigned long long lane_tau(const SearchArgs &a, bool in, float v, uint32_t id, float mx, int n, int kt) {
-    const int lane = threadIdx.x & 63;
-    const bool by_mass = (a.mode == ZHA_TOPP) && (a.p > 0.f);
-    const bool flat = !(mx > -INFINITY);   // every score -inf: equal masses
-    uint32_t wt = 0u;
-    if (in) wt = by_mass ? __float2uint_rn((flat ? 1.f : mass_exp(v - mx)) * kMassScale) : 1u;
-    unsigned long long key = in ? rank_key(v, id, a.log2c) : 0ull;
-    unsigned long long need;
-    if (by_mass) {
-        unsigned long long z = wt;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
-        const double tq = ceil(static_cast<double>(a.p) * static_cast<double>(z));
-        need = static_cast<unsigned long long>(tq);
-        if (need < 1) need = 1;
-        if (need > z) need = z;
-    } else {
-        const int m = (a.mode == ZHA_TOPK) ? (kt < n ? kt : n) : 1;
-        need = static_cast<unsigned long long>(m < 1 ? 1 : m);
-    }
-    // descending bitonic sort over the 64 lanes
-#pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const unsigned long long ok = __shfl_xor(key, j, 64);
-            const uint32_t ow = static_cast<uint32_t>(__shfl_xor(static_cast<int>(wt), j, 64));
-            const bool lower = (lane & j) == 0, desc = (lane & k) == 0;
-            const bool take = (lower == desc) ? (ok > key) : (ok < key);
-            if (take) {
-                key = ok;
-                wt = ow;
-            }
-        }
-    }
-    unsigned long long incl = wt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const unsigned long long o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-    }
-    const unsigned long long hit = __ballot(lane < n && incl >= need);
-    const int first = hit ? (__ffsll(static_cast<long long>(hit)) - 1) : (n - 1);
-    return __shfl(key, first, 64);
 }
 
 __device__ __forceinline__ float block_max(float v, SelectShared &sh) {
