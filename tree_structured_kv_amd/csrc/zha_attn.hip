@@ -100,8 +100,7 @@ __global__ __launch_bounds__(1024) void k_attn_plan(AttnArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     unsigned long long mine = 0;
     for (int w = tid; w < a.walks; w += 1024) mine += static_cast<unsigned long long>(walk_keys(a, w));
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mine += __shfl_xor(mine, off, 64);
+    mine = wave_total_u64(mine);
     if (lane == 0) ksum[wave] = mine;
     if (tid == 0) carry = 0;
     __syncthreads();
@@ -122,11 +121,7 @@ __global__ __launch_bounds__(1024) void k_attn_plan(AttnArgs a) {
             if (a.block_mfma) ++cnt;                 // the last item: the block's own keys
             if (cnt < 1) cnt = 1;
         }
-        int32_t incl = cnt;
-        for (int off = 1; off < 64; off <<= 1) {
-            int32_t o = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += o;
-        }
+        const int32_t incl = static_cast<int32_t>(wave_scan_u32(static_cast<uint32_t>(cnt)));
         if (lane == 63) wsum[wave] = incl;
         __syncthreads();
         int32_t before = carry;
@@ -237,9 +232,11 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
         }
 
         // merge key slots inside the wavefront (lanes with equal `sub`)
+#pragma unroll
         for (int off = LPK; off < 64; off <<= 1) {
-            float m2 = __shfl_xor(m, off, 64), l2 = __shfl_xor(l, off, 64), acc2[EPL];
-            for (int e = 0; e < EPL; ++e) acc2[e] = __shfl_xor(acc[e], off, 64);
+            float m2 = xor_lane_f(m, off), l2 = xor_lane_f(l, off), acc2[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc2[e] = xor_lane_f(acc[e], off);
             merge_state(m, l, acc, m2, l2, acc2, EPL);
         }
         if (slot == 0) {
@@ -349,8 +346,8 @@ __global__ __launch_bounds__(256, 3) void k_attn_block(AttnArgs a) {
             }
         }
         // row (query) max over the 4 lane groups holding this column
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        tmax = fmaxf(tmax, xor_lane_f(tmax, 16));
+        tmax = fmaxf(tmax, xor_lane_f(tmax, 32));
         const float mt = fmaxf(m, tmax);
         const bool move = mt > m + kLazy;
         if (__ballot(move) != 0ull) {
@@ -371,8 +368,8 @@ __global__ __launch_bounds__(256, 3) void k_attn_block(AttnArgs a) {
                 p[sub][e] = pe;
                 psum += pe;
             }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
+        psum += xor_lane_f(psum, 16);
+        psum += xor_lane_f(psum, 32);
         l += psum;
         // O^T += V^T P^T as bf16 16x16x32 products over 32 keys at a time:
         // the lane's eight K slots are its own keys 16*sub + 4*grp + e of

@@ -144,8 +144,8 @@ __global__ __launch_bounds__(256) void k_ua_sig(AttnArgs a) {
     }
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) {
-        m1 = min(m1, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m1), off, 64)));
-        m2 = min(m2, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m2), off, 64)));
+        m1 = min(m1, xor_lane_n(m1, off));
+        m2 = min(m2, xor_lane_n(m2, off));
     }
     if (w < a.walks && sub == 0) {
         const uint64_t loc = static_cast<uint64_t>((w % ua_wpp(a)) % kUaSortMax);
@@ -388,8 +388,8 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
                 x[e] = (qok && kq + e < nkeys) ? s * sa[e] : -INFINITY;
                 tmax = fmaxf(tmax, x[e]);
             }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            tmax = fmaxf(tmax, xor_lane_f(tmax, 16));
+            tmax = fmaxf(tmax, xor_lane_f(tmax, 32));
             const float mt = fmaxf(m_run, tmax);
             const bool move = mt > m_run + kLazy;
             if (__ballot(move) != 0ull) {
@@ -407,8 +407,8 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
                 pe[e] = (x[e] > -INFINITY) ? __builtin_amdgcn_exp2f(x[e] - m_run) : 0.f;
                 psum += pe[e];
             }
-            psum += __shfl_xor(psum, 16, 64);
-            psum += __shfl_xor(psum, 32, 64);
+            psum += xor_lane_f(psum, 16);
+            psum += xor_lane_f(psum, 32);
             l_run += psum;
             // O^T += V^T P^T as bf16 16x16x16 products: the probabilities of
             // keys 4*grp .. 4*grp+3 are already this lane's B operand; each is

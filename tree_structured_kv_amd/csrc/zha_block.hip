@@ -92,11 +92,7 @@ struct WaveCut {
     unsigned long long above;
 };
 
-__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) { return wave_total_u64(v); }
 
 }  // namespace
 
@@ -470,12 +466,7 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
                         lw[e] = by_mass ? sh.hw[4 * lane + e] : sh.hcnt[4 * lane + e];
                         lsum += lw[e];
                     }
-                    unsigned long long incl = lsum;
-#pragma unroll
-                    for (int off = 1; off < 64; off <<= 1) {
-                        const unsigned long long o = __shfl_up(incl, off, 64);
-                        if (lane >= off) incl += o;
-                    }
+                    unsigned long long incl = wave_scan_u64(lsum);
                     const unsigned long long excl = incl - lsum;
                     const unsigned long long mask = __ballot(incl >= need);
                     const int firstl = mask ? (__ffsll(static_cast<long long>(mask)) - 1) : 63;
@@ -531,12 +522,7 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
                 }
                 __syncthreads();
                 unsigned long long wv = lane < nf ? sh.sw[lane] : 0ull;
-                unsigned long long incl = wv;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const unsigned long long o = __shfl_up(incl, off, 64);
-                    if (lane >= off) incl += o;
-                }
+                unsigned long long incl = wave_scan_u64(wv);
                 const unsigned long long hit = __ballot(lane < nf && incl >= need);
                 const int r = hit ? (__ffsll(static_cast<long long>(hit)) - 1) : (nf - 1);
                 tau = (nf > 0) ? sh.skey[r] : 0ull;
@@ -577,7 +563,7 @@ __global__ __launch_bounds__(64) void k_bk_cut(SearchArgs a, int t) {
             }
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
-                const unsigned long long o = __shfl_xor(best, off, 64);
+                const unsigned long long o = xor_lane64_n(best, off);
                 best = o > best ? o : best;
             }
             tau = best;
@@ -648,12 +634,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_bk_group(SearchArgs a, int t)
         const unsigned long long units = static_cast<unsigned long long>((cnt + kBkRows - 1) / kBkRows);
         // entries in the low 40 bits, units in the high 24
         const unsigned long long v = static_cast<unsigned long long>(cnt) | (units << 40);
-        unsigned long long incl = v;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const unsigned long long o = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += o;
-        }
+        unsigned long long incl = wave_scan_u64(v);
         if (lane == 63) scan[wave] = incl;
         __syncthreads();
         unsigned long long before = carry;

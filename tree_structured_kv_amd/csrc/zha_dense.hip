@@ -145,11 +145,7 @@ __device__ __forceinline__ void top_bin(const uint32_t *h, int copies, int nb, u
         cnt[e] = c;
         tsum += c;
     }
-    uint32_t incl = tsum;
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-    }
+    const uint32_t incl = wave_scan_u32(tsum);
     if (lane == 63) s_wsum[wave] = incl;
     __syncthreads();
     uint32_t before = 0;
@@ -392,11 +388,7 @@ __device__ __forceinline__ void top_bin_mass(const uint32_t *hc, const unsigned 
         csum += cs[e];
     }
     // inclusive scans of mass and count over the threads (highest bins first)
-    unsigned long long im = tsum, ic = csum;
-    for (int off = 1; off < 64; off <<= 1) {
-        const unsigned long long om = __shfl_up(im, off, 64), oc = __shfl_up(ic, off, 64);
-        if (lane >= off) { im += om; ic += oc; }
-    }
+    const unsigned long long im = wave_scan_u64(tsum), ic = wave_scan_u64(csum);
     if (lane == 63) { s_wsum[wave] = im; s_wsum[kSelWaves + wave] = ic; }
     __syncthreads();
     unsigned long long bm = 0, bc = 0;
@@ -479,7 +471,7 @@ __global__ __launch_bounds__(kSelThreads) void k_dense_topp_budget(DenseArgs a) 
                 z += wt;
             }
         }
-        for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+        z = wave_total_u64(z);
         if (lane == 0) s_wsum[wave] = z;
         __syncthreads();
         unsigned long long Z = 0;

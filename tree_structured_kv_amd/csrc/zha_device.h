@@ -140,13 +140,125 @@ __device__ __forceinline__ float group_max(float v) {
     return v;
 }
 
+// Lane exchanges without the LDS permute unit.  xor_lane<J>: the value of
+// lane (lane ^ J) for J a power of two below 64: within a row of 16 lanes by
+// DPP (quad_perm for 1 and 2, row shifts for 4, row rotate for 8), across
+// rows by gfx950's row swaps (v_permlane16_swap / v_permlane32_swap, each
+// called with the value in both operands: the swapped halves are the
+// partner's).  wave_scan_u64: inclusive sum over the 64 lanes by DPP row
+// shifts and the row broadcasts of lanes 15 and 31.
+constexpr int kDppShl4 = 0x104;       // row_shl:4: lane i reads lane i+4 of its row
+constexpr int kDppShr = 0x110;        // row_shr:N (0x110 + N): lane i reads lane i-N of its row
+constexpr int kDppRor8 = 0x128;       // row_ror:8: lane i reads lane i^8 of its row
+constexpr int kDppBcast15 = 0x142;    // lane 15 of each row to the next row
+constexpr int kDppBcast31 = 0x143;    // lane 31 to rows 2 and 3
+
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROWS, 0xf, false));
+}
+
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+    const int lane = __lane_id();
+    if constexpr (J == 1) {
+        return dpp_u32<kDppXor1>(v);
+    } else if constexpr (J == 2) {
+        return dpp_u32<kDppXor2>(v);
+    } else if constexpr (J == 4) {
+        const uint32_t up = dpp_u32<kDppShl4>(v), dn = dpp_u32<kDppShr + 4>(v);
+        return (lane & 4) ? dn : up;
+    } else if constexpr (J == 8) {
+        return dpp_u32<kDppRor8>(v);
+    } else if constexpr (J == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? r[0] : r[1];
+    } else {
+        static_assert(J == 32, "xor_lane: J is a power of two below 64");
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? r[0] : r[1];
+    }
+}
+
+template <int J>
+__device__ __forceinline__ unsigned long long xor_lane64(unsigned long long v) {
+    const uint32_t lo = xor_lane<J>(static_cast<uint32_t>(v));
+    const uint32_t hi = xor_lane<J>(static_cast<uint32_t>(v >> 32));
+    return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+    const uint32_t lo = dpp_u32<CTRL, ROWS>(static_cast<uint32_t>(v));
+    const uint32_t hi = dpp_u32<CTRL, ROWS>(static_cast<uint32_t>(v >> 32));
+    return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ unsigned long long wave_scan_u64(unsigned long long x) {
+    x += dpp_u64<kDppShr + 1>(x);
+    x += dpp_u64<kDppShr + 2>(x);
+    x += dpp_u64<kDppShr + 4>(x);
+    x += dpp_u64<kDppShr + 8>(x);
+    x += dpp_u64<kDppBcast15, 0xa>(x);
+    x += dpp_u64<kDppBcast31, 0xc>(x);
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t x) {
+    x += dpp_u32<kDppShr + 1>(x);
+    x += dpp_u32<kDppShr + 2>(x);
+    x += dpp_u32<kDppShr + 4>(x);
+    x += dpp_u32<kDppShr + 8>(x);
+    x += dpp_u32<kDppBcast15, 0xa>(x);
+    x += dpp_u32<kDppBcast31, 0xc>(x);
+    return x;
+}
+
+// Lane l's 64-bit value for every lane (l wavefront-uniform).
+__device__ __forceinline__ unsigned long long read_lane64(unsigned long long v, int l) {
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), l));
+    return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+// The sum over all 64 lanes, in every lane.
+__device__ __forceinline__ unsigned long long wave_total_u64(unsigned long long v) {
+    return read_lane64(wave_scan_u64(v), 63);
+}
+
+__device__ __forceinline__ uint32_t wave_total_u32(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_scan_u32(v)), 63));
+}
+
+// xor_lane with the distance a (power-of-two) value that unrolled loops fold.
+__device__ __forceinline__ uint32_t xor_lane_n(uint32_t v, int j) {
+    switch (j) {
+        case 1: return xor_lane<1>(v);
+        case 2: return xor_lane<2>(v);
+        case 4: return xor_lane<4>(v);
+        case 8: return xor_lane<8>(v);
+        case 16: return xor_lane<16>(v);
+        default: return xor_lane<32>(v);
+    }
+}
+__device__ __forceinline__ float xor_lane_f(float v, int j) { return __uint_as_float(xor_lane_n(__float_as_uint(v), j)); }
+__device__ __forceinline__ unsigned long long xor_lane64_n(unsigned long long v, int j) {
+    const uint32_t lo = xor_lane_n(static_cast<uint32_t>(v), j);
+    const uint32_t hi = xor_lane_n(static_cast<uint32_t>(v >> 32), j);
+    return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+// Butterfly sum / max over aligned groups of `width` lanes (every lane of a
+// group gets the result; partners exactly as a lane-xor shuffle gives them).
 __device__ __forceinline__ float wave_sum(float v, int width) {
-    for (int off = 1; off < width; off <<= 1) v += __shfl_xor(v, off, 64);
+#pragma unroll
+    for (int off = 1; off < width; off <<= 1) v += xor_lane_f(v, off);
     return v;
 }
 
 __device__ __forceinline__ float wave_max(float v, int from, int to) {
-    for (int off = from; off < to; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+#pragma unroll
+    for (int off = from; off < to; off <<= 1) v = fmaxf(v, xor_lane_f(v, off));
     return v;
 }
 

@@ -37,21 +37,22 @@ namespace {
 constexpr int kFU = 2;   // key rows in flight per lane group (attention)
 
 __device__ __forceinline__ float lane_group_sum(float v, int width) {
-    for (int off = 1; off < width; off <<= 1) v += __shfl_xor(v, off, 64);
+#pragma unroll
+    for (int off = 1; off < width; off <<= 1) v += xor_lane_f(v, off);
     return v;
 }
 
 // Merge the online-softmax state (m, l, acc) with the one `off` lanes away.
 template <int EPL>
 __device__ __forceinline__ void merge_shfl(float &m, float &l, float (&acc)[EPL], int off) {
-    const float m2 = __shfl_xor(m, off, 64);
-    const float l2 = __shfl_xor(l, off, 64);
+    const float m2 = xor_lane_f(m, off);
+    const float l2 = xor_lane_f(l, off);
     const float mm = fmaxf(m, m2);
     const float c1 = (m > -INFINITY) ? expf(m - mm) : 0.f;
     const float c2 = (m2 > -INFINITY) ? expf(m2 - mm) : 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-        const float a2 = __shfl_xor(acc[e], off, 64);
+        const float a2 = xor_lane_f(acc[e], off);
         acc[e] = acc[e] * c1 + a2 * c2;
     }
     l = l * c1 + l2 * c2;

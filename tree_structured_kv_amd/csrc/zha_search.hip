@@ -170,12 +170,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_ls_score(SearchArgs a, int t,
         const int w1 = min(a.walks, w0 + per);
         int sum = 0;
         for (int w = w0; w < w1; ++w) sum += s_first[w];
-        int incl = sum;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int o = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += o;
-        }
+        const int incl = static_cast<int>(wave_scan_u32(static_cast<uint32_t>(sum)));
         if (lane == 63) s_part[wave] = incl;
         __syncthreads();
         int run = incl - sum, total = 0;

@@ -66,10 +66,10 @@ __device__ __forceinline__ void leaf_node(const float *rho, float *kk, float *wt
         }
         const float sg = live ? s * d : -INFINITY;
         float m = sg;
-        for (int off = 1; off < c; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        for (int off = 1; off < c; off <<= 1) m = fmaxf(m, xor_lane_f(m, off));
         const float ex = live ? expf(sg - m) : 0.f;
         float z = ex;
-        for (int off = 1; off < c; off <<= 1) z += __shfl_xor(z, off, 64);
+        for (int off = 1; off < c; off <<= 1) z += xor_lane_f(z, off);
         if (live) {
             wt[r * c + i] = ex / z;
             if (i == 0) { mx_s[r] = m; z_s[r] = z; }
@@ -105,7 +105,7 @@ __device__ __forceinline__ void leaf_node(const float *rho, float *kk, float *wt
         const float *qr = rho + r * P + d0;
 #pragma unroll
         for (int e = 0; e < 16; ++e) part = fmaf(acc[e], qr[e], part);
-        for (int off = 1; off < NS; off <<= 1) part += __shfl_xor(part, off, 64);
+        for (int off = 1; off < NS; off <<= 1) part += xor_lane_f(part, off);
         if (live) {
             if constexpr (sizeof(ST) == 2) {
                 uint32_t wv[8];

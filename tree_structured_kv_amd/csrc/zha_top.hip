@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kTopThreads) void k_top_score(SearchArgs a) {
             // max over the RPL reference groups (lanes LPR apart)
             if constexpr (RPL >= 4)
                 best = fmaxf(best, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(best), 0x401F)));
-            if constexpr (RPL >= 2) best = fmaxf(best, __shfl_xor(best, 32, 64));
+            if constexpr (RPL >= 2) best = fmaxf(best, xor_lane_f(best, 32));
             float m = best;
             if (m != m) m = -INFINITY;
             if (m == 0.f) m = 0.f;

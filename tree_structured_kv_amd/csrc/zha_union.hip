@@ -641,8 +641,7 @@ __device__ __forceinline__ void expand_slice(const SearchArgs &a, int t, int p, 
 #pragma unroll
         for (int u = 0; u < kScanU; ++u) mine += __popcll(__ballot(mv[u] != 0u));
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) cb += __shfl_xor(cb, off, 64);
+    cb = wave_total_u32(cb);
     if (lane == 0) {
         sh.seg_cnt[wave] = mine;
         sh.pre_cnt[wave] = cb;

@@ -115,12 +115,7 @@ __device__ __forceinline__ unsigned long long block_exscan64(unsigned long long 
                                                              unsigned long long *scratch,
                                                              unsigned long long *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    unsigned long long incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        unsigned long long o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-    }
+    unsigned long long incl = wave_scan_u64(v);
     if (lane == 63) scratch[wave] = incl;
     __syncthreads();
     unsigned long long base = 0, tot = 0;
@@ -225,12 +220,7 @@ __device__ __forceinline__ unsigned long long cut_tau(const SearchArgs &a, int n
             unsigned long long lw[4], lsum = 0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) { lw[e] = sh.hw[255 - 4 * lane - e]; lsum += lw[e]; }
-            unsigned long long incl = lsum;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                unsigned long long o = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += o;
-            }
+            unsigned long long incl = wave_scan_u64(lsum);
             const unsigned long long excl = incl - lsum;
             const unsigned long long mask = __ballot(incl >= need);
             const int first = mask ? (__ffsll(static_cast<long long>(mask)) - 1) : 63;
@@ -288,9 +278,7 @@ __device__ __forceinline__ unsigned long long lane_tau(const SearchArgs &a, bool
     unsigned long long key = in ? rank_key(v, id, a.log2c) : 0ull;
     unsigned long long need;
     if (by_mass) {
-        unsigned long long z = wt;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+        const unsigned long long z = wave_total_u64(wt);
         const double tq = ceil(static_cast<double>(a.p) * static_cast<double>(z));
         need = static_cast<unsigned long long>(tq);
         if (need < 1) need = 1;
@@ -304,8 +292,8 @@ __device__ __forceinline__ unsigned long long lane_tau(const SearchArgs &a, bool
     for (int k = 2; k <= 64; k <<= 1) {
 #pragma unroll
         for (int j = k >> 1; j > 0; j >>= 1) {
-            const unsigned long long ok = __shfl_xor(key, j, 64);
-            const uint32_t ow = static_cast<uint32_t>(__shfl_xor(static_cast<int>(wt), j, 64));
+            const unsigned long long ok = xor_lane64_n(key, j);
+            const uint32_t ow = xor_lane_n(wt, j);
             const bool lower = (lane & j) == 0, desc = (lane & k) == 0;
             const bool take = (lower == desc) ? (ok > key) : (ok < key);
             if (take) {
@@ -314,15 +302,10 @@ __device__ __forceinline__ unsigned long long lane_tau(const SearchArgs &a, bool
             }
         }
     }
-    unsigned long long incl = wt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const unsigned long long o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-    }
+    unsigned long long incl = wave_scan_u64(wt);
     const unsigned long long hit = __ballot(lane < n && incl >= need);
     const int first = hit ? (__ffsll(static_cast<long long>(hit)) - 1) : (n - 1);
-    return __shfl(key, first, 64);
+    return read_lane64(key, first);
 }
 
 // Bin of score v in a window of 256 bins counted down from `top` (bin 0
@@ -444,12 +427,7 @@ __device__ __forceinline__ unsigned long long cut_tau_win(const SearchArgs &a, i
             unsigned long long lw[4], lsum = 0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) { lw[e] = by_mass ? sh.hw[4 * lane + e] : sh.hcnt[4 * lane + e]; lsum += lw[e]; }
-            unsigned long long incl = lsum;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                unsigned long long o = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += o;
-            }
+            unsigned long long incl = wave_scan_u64(lsum);
             const unsigned long long excl = incl - lsum;
             const unsigned long long mask = __ballot(incl >= need);
             const int first = mask ? (__ffsll(static_cast<long long>(mask)) - 1) : 63;
@@ -513,12 +491,7 @@ __device__ __forceinline__ unsigned long long cut_tau_win(const SearchArgs &a, i
         // the first rank whose running weight reaches what is still needed
         // (kWinFinal = one per lane): a scan and a ballot
         const unsigned long long wv = lane < nf ? sh.sw[lane] : 0ull;
-        unsigned long long incl = wv;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const unsigned long long o = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += o;
-        }
+        unsigned long long incl = wave_scan_u64(wv);
         const unsigned long long hit = __ballot(lane < nf && incl >= need);
         const int r = hit ? (__ffsll(static_cast<long long>(hit)) - 1) : nf - 1;
         if (lane == 0) sh.tau = nf > 0 ? sh.skey[r] : 0ull;
