@@ -15,6 +15,12 @@
 // better, else 1024);
 // k_attn_partial is a grid-stride loop over the items, so every workgroup
 // streams about the same number of bytes whatever the spread between walks.
+// When the walks together select fewer keys than half of all the pairs'
+// cache keys, the heads of a pair rarely share a key and the key and value
+// rows come in through streaming (nontemporal) loads; otherwise ordinary
+// loads leave the shared rows in L2 for the next head (measured: 256K
+// clustered keys, 5% of the keys selected over a pair's heads, 100 -> 92 us;
+// 64K AR(1) keys, 80%, 3% slower streamed).  The plan decides it.
 // A key row is D*e bytes read as 16-byte pieces by D*e/16 lanes.  The online
 // softmax state (max, sum, weighted V) lives per key slot and is merged
 // across slots, wavefronts and finally items (k_attn_combine), all in fp32.
@@ -108,7 +114,9 @@ __global__ __launch_bounds__(1024) void k_attn_plan(AttnArgs a) {
         unsigned long long tot = 0;
         for (int i = 0; i < 16; ++i) tot += ksum[i];
         s_ck = tot < (2ull << 20) ? kChunkMin : (tot < (8ull << 20) ? 1024 : kChunkMax);
-        a.item_off[a.walks + 1] = s_ck;
+        const unsigned long long pairs = static_cast<unsigned long long>(a.walks) / (a.group * a.qph);
+        const bool stream = 2 * tot < pairs * static_cast<unsigned long long>(a.n_tokens);
+        a.item_off[a.walks + 1] = s_ck | (stream ? kStreamBit : 0);
     }
     __syncthreads();
     const int ck = s_ck;
@@ -150,10 +158,13 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
     const int c = a.chunk;
     const float s = a.sharpness * 1.4426950408889634f;   // base-2 logits: one hardware exp2 per weight
     const int32_t n_items = a.item_off[a.walks];
-    const int ck = a.item_off[a.walks + 1];     // keys per item (at most kChunkMax)
+    const int32_t plan = a.item_off[a.walks + 1];
+    const int ck = plan & ~kStreamBit;          // keys per item (at most kChunkMax)
     __shared__ float sm[kWaves], sl[kWaves], sacc[kWaves][D];
     __shared__ int32_t s_ids[kChunkMax + 1];    // the item's block (or token) ids
 
+    auto items = [&](auto kstream) {
+    constexpr bool kStream = decltype(kstream)::value;
     for (int32_t item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int w = a.item_walk[item];
         const int64_t chunk = item - a.item_off[w];
@@ -210,8 +221,13 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
                         tok = tail0 + (ki - body);
                     }
                 }
-                Vec16<KT>::load(kb + tok * D + sub * EPL, kr[u]);
-                Vec16<KT>::load(vb + tok * D + sub * EPL, vr[u]);
+                if constexpr (kStream) {
+                    Vec16<KT>::load_nt(kb + tok * D + sub * EPL, kr[u]);
+                    Vec16<KT>::load_nt(vb + tok * D + sub * EPL, vr[u]);
+                } else {
+                    Vec16<KT>::load(kb + tok * D + sub * EPL, kr[u]);
+                    Vec16<KT>::load(vb + tok * D + sub * EPL, vr[u]);
+                }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -253,6 +269,11 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(AttnArgs a) {
         }
         __syncthreads();
     }
+    };
+    if (plan & kStreamBit)
+        items(std::true_type{});
+    else
+        items(std::false_type{});
 }
 
 // Prefill: attention of every query of the block over the block's own keys

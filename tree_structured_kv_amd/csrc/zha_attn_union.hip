@@ -276,7 +276,8 @@ __global__ __launch_bounds__(T) void k_ua_build(AttnArgs a) {
     }
 }
 
-template <int D>
+// NT: key and value rows through streaming (nontemporal) loads.
+template <int D, bool NT>
 __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
     constexpr int DS = D / 32;            // bf16 16x16x32 steps of a logit
     constexpr int DT = D / 16;            // row tiles of O^T: row i of tile q is d = DT*i + q
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
             const int ka = kbase + col;
             const bf16_t *kr = kc + token_of(ka < nkeys ? ka : kbase) * D + 8 * grp;
 #pragma unroll
-            for (int st = 0; st < DS; ++st) T.kb[st] = as_bf8(gload_u4(kr + 32 * st));
+            for (int st = 0; st < DS; ++st) T.kb[st] = as_bf8(NT ? gload_u4_nt(kr + 32 * st) : gload_u4(kr + 32 * st));
             // the lane group's four keys kq .. kq+3 are consecutive rows of
             // one block (blocks hold at least four keys) or of the tail, so
             // one lookup serves all four (keys past the end reuse the first
@@ -365,10 +366,10 @@ __global__ __launch_bounds__(256) void k_ua_attn(AttnArgs a) {
             for (int e = 0; e < 4; ++e) {
                 const bf16_t *vr = vq + (kq + e < nkeys ? e * D : 0);
                 if constexpr (DT == 8) {
-                    const gu4_t v = gload_u4(vr);
+                    const gu4_t v = NT ? gload_u4_nt(vr) : gload_u4(vr);
                     T.vw[e][0] = v.x; T.vw[e][1] = v.y; T.vw[e][2] = v.z; T.vw[e][3] = v.w;
                 } else {
-                    const gu2_t v = gload_u2(vr);
+                    const gu2_t v = NT ? gload_u2_nt(vr) : gload_u2(vr);
                     T.vw[e][0] = v.x; T.vw[e][1] = v.y;
                 }
             }
@@ -643,8 +644,12 @@ static hipError_t launch_ua_t(const AttnArgs &a, hipStream_t st) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const int64_t items = a.ugroups * a.items_pp;
-    hipLaunchKernelGGL((k_ua_attn<D>), dim3(static_cast<unsigned>(a.qph == 1 ? items : xcd_grid(items))), dim3(256), 0,
-                       st, a);
+    // decode reads each selected block once per pair: streaming loads;
+    // prefill groups on one XCD share blocks through its L2: ordinary loads
+    if (a.qph == 1)
+        hipLaunchKernelGGL((k_ua_attn<D, true>), dim3(static_cast<unsigned>(items)), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_ua_attn<D, false>), dim3(static_cast<unsigned>(xcd_grid(items))), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.qph == 1) {
         hipLaunchKernelGGL((k_ua_combine<D>), dim3(a.walks), dim3(256), 0, st, a);

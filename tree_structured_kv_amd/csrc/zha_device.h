@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace zha {
 
 typedef uint16_t bf16_t;  // raw bfloat16 bits
@@ -31,10 +33,20 @@ template <> struct Elem<bf16_t> {
 };
 
 // Four consecutive elements as floats (one 16- or 8-byte load).
+typedef float gf4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t gu4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t gu2_t __attribute__((ext_vector_type(2)));
+#define ZHA_GLOBAL(T) const __attribute__((address_space(1))) T *
+
 template <typename T> struct Vec4;
 template <> struct Vec4<float> {
     static __device__ __forceinline__ void load(const float *p, float *o) {
         const float4 v = *reinterpret_cast<const float4 *>(p);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+    // streaming read (nontemporal): data read once and not again soon
+    static __device__ __forceinline__ void load_nt(const float *p, float *o) {
+        const gf4_t v = __builtin_nontemporal_load((ZHA_GLOBAL(gf4_t))p);
         o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
     }
 };
@@ -44,20 +56,23 @@ template <> struct Vec4<bf16_t> {
         o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
         o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
     }
+    static __device__ __forceinline__ void load_nt(const bf16_t *p, float *o) {
+        const gu2_t v = __builtin_nontemporal_load((ZHA_GLOBAL(gu2_t))p);
+        o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+        o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
 };
 
 // Loads through pointers known to address device (global) memory.  When a
 // pointer is read from a table in LDS the compiler cannot tell its address
 // space and emits flat loads, which also count on the LDS counter: a later
 // wait for an LDS read then waits for every flat load still in flight.
-typedef float gf4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t gu4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t gu2_t __attribute__((ext_vector_type(2)));
-#define ZHA_GLOBAL(T) const __attribute__((address_space(1))) T *
 __device__ __forceinline__ gf4_t gload_f4(const void *p) { return *(ZHA_GLOBAL(gf4_t))p; }
 __device__ __forceinline__ gu4_t gload_u4(const void *p) { return *(ZHA_GLOBAL(gu4_t))p; }
 __device__ __forceinline__ gu2_t gload_u2(const void *p) { return *(ZHA_GLOBAL(gu2_t))p; }
 __device__ __forceinline__ float gload_f(const float *p) { return *(ZHA_GLOBAL(float))p; }
+__device__ __forceinline__ gu4_t gload_u4_nt(const void *p) { return __builtin_nontemporal_load((ZHA_GLOBAL(gu4_t))p); }
+__device__ __forceinline__ gu2_t gload_u2_nt(const void *p) { return __builtin_nontemporal_load((ZHA_GLOBAL(gu2_t))p); }
 
 // Read-only data at a wavefront-uniform address, through the constant
 // address space (scalar loads into SGPRs).  Only for memory that no
@@ -90,6 +105,10 @@ template <> struct Vec16<float> {
         float4 v = *reinterpret_cast<const float4 *>(p);
         o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
     }
+    static __device__ __forceinline__ void load_nt(const float *p, float (&o)[4]) {
+        const gf4_t v = __builtin_nontemporal_load((ZHA_GLOBAL(gf4_t))p);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
 };
 template <> struct Vec16<bf16_t> {
     static constexpr int N = 8;
@@ -100,6 +119,14 @@ template <> struct Vec16<bf16_t> {
         for (int i = 0; i < 4; ++i) {
             o[2 * i] = __uint_as_float(w[i] << 16);
             o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void load_nt(const bf16_t *p, float (&o)[8]) {
+        const gu4_t v = __builtin_nontemporal_load((ZHA_GLOBAL(gu4_t))p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __uint_as_float(v[i] << 16);
+            o[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
         }
     }
 };

@@ -15,6 +15,7 @@ constexpr uint32_t kIndexMask = (1u << kLevelShift) - 1u;
 constexpr int kBlock = 256;          // threads per workgroup of most kernels
 constexpr int kChunkMin = 512;       // keys per attention work item: the planner picks 512 .. 2048
 constexpr int kChunkMax = 2048;      // (more, smaller items when a call reads few keys)
+constexpr int32_t kStreamBit = 1 << 30;  // in the attention plan's keys-per-item word: streaming loads
 constexpr int kTile = 32;            // candidates per tile of the level-synchronous scorer
 constexpr int kPlanWalks = 4096;     // walks up to which that scorer orders its tiles itself (in LDS)
 constexpr int kFlatPad = 32;         // union engine: each run of scoring entries is padded to this

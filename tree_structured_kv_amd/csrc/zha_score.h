@@ -49,7 +49,9 @@ __device__ __forceinline__ void load_q(const SearchArgs &a, int w, float (&qv)[r
 // through scalar loads (no search writes node records).  With kScalarList
 // the candidate ids do too: only where the list was written by an earlier
 // launch, since the scalar cache does not see this kernel's own stores.
-template <int D, int R, typename ST, bool kScalarList, bool kFresh = false>
+// With kStream the records come in through nontemporal (streaming) loads:
+// for steps whose records the group's other heads are unlikely to read too.
+template <int D, int R, typename ST, bool kScalarList, bool kFresh = false, bool kStream = false>
 __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair,
                                             const float (&qv)[row_epl<D, ST>()],
                                             const uint32_t *cur, float *sc, int first, int end,
@@ -106,8 +108,12 @@ __device__ __forceinline__ float score_wave(const SearchArgs &a, int64_t pair,
             for (int l = 0; l < NL; ++l) {
                 const int r = l * RPL + rsub;
                 if (r < R) {
-                    if constexpr (EPL == 8)
+                    if constexpr (EPL == 8 && kStream)
+                        Vec16<ST>::load_nt(kp + r * D + EPL * sub, kv[u][l]);
+                    else if constexpr (EPL == 8)
                         Vec16<ST>::load(kp + r * D + EPL * sub, kv[u][l]);
+                    else if constexpr (kStream)
+                        Vec4<ST>::load_nt(kp + r * D + EPL * sub, kv[u][l]);
                     else
                         Vec4<ST>::load(kp + r * D + EPL * sub, kv[u][l]);
                     if constexpr (kScalarBias) {

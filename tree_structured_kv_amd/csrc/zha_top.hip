@@ -189,10 +189,12 @@ __global__ __launch_bounds__(kTopThreads) void k_top_score(SearchArgs a) {
             for (int i = 0; i < NL; ++i) {
                 const int r = i * RPL + rsub;
                 if (r < R) {
+                    // each record is read once for all heads of the pair:
+                    // streaming loads
                     if constexpr (EPL == 8)
-                        Vec16<ST>::load(kp + r * D + EPL * sub, kv[u][i]);
+                        Vec16<ST>::load_nt(kp + r * D + EPL * sub, kv[u][i]);
                     else
-                        Vec4<ST>::load(kp + r * D + EPL * sub, kv[u][i]);
+                        Vec4<ST>::load_nt(kp + r * D + EPL * sub, kv[u][i]);
                     bv[u][i] = a.bet[l][node * R + r];
                 } else {
 #pragma unroll
