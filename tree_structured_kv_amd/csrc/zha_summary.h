@@ -20,8 +20,10 @@ namespace zha {
 // references staged in LDS at row pitch D + 4 floats; kk [c][D + 4], wt
 // [R][c], mx_s [R], z_s [R]: this wavefront's LDS scratch; keys: the chunk's
 // c rows; ok [R][D], ob [R]: the node's record (global or LDS).
-//   1. lane pair p = r*c + i: sigma = s <K_i, rho_r>; max and sum of
-//      exp(sigma - max) over the c lanes of reference r; w = softmax;
+//   1. sigma = s <K_i, rho_r> for every key i and reference r as 16x16x4
+//      fp32 matrix products (keys as rows, references as columns), into
+//      wt; then lane pair p = r*c + i: max and sum of exp(sigma - max) over
+//      the c lanes of reference r; w = softmax;
 //   2. lane item (r, 16 elements): key_r = sum_i w_i K_i, written as
 //      coalesced 16-float runs; bias_r = max + log(sum) - s <key_r, rho_r>
 //      summed over the D/16 lanes of r.
@@ -47,24 +49,43 @@ __device__ __forceinline__ void leaf_node(const float *rho, float *kk, float *wt
             *reinterpret_cast<float4 *>(kk + i * P + d0 + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
     }
     __builtin_amdgcn_wave_barrier();
-    // 1. scores and softmax weights, one (r, i) pair per lane and round
+    // 1a. the scores on the matrix cores: in product step m, lane group
+    //     q = lane/16 multiplies element q*D/4 + m of key row i (the tile's
+    //     row lane%16) and of reference r (column lane%16): one order of the
+    //     dot product's terms for every (i, r).  The product's lane holds
+    //     keys 4q .. 4q+3 of the tile for reference lane%16.
+    {
+        constexpr int QD = D / 4;
+        const int col = lane & 15, q = lane >> 4;
+        const bool rok = col < R;
+        const float *qr = rho + (rok ? col : 0) * P + q * QD;
+        for (int i0 = 0; i0 < c; i0 += 16) {
+            const bool kok = i0 + col < c;
+            const float *kr = kk + (kok ? i0 + col : 0) * P + q * QD;
+            gf4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < QD; m += 4) {
+                const float4 x = *reinterpret_cast<const float4 *>(kr + m);
+                const float4 y = *reinterpret_cast<const float4 *>(qr + m);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kok ? x.x : 0.f, rok ? y.x : 0.f, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kok ? x.y : 0.f, rok ? y.y : 0.f, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kok ? x.z : 0.f, rok ? y.z : 0.f, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kok ? x.w : 0.f, rok ? y.w : 0.f, acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = i0 + 4 * q + e;
+                if (i < c && rok) wt[col * c + i] = s * acc[e];
+            }
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // 1b. softmax weights, one (r, i) pair per lane and round
     for (int p0 = 0; p0 < c * R; p0 += 64) {
         const int pi = p0 + lane;
         const bool live = pi < c * R;
         const int r = live ? pi / c : 0, i = live ? pi % c : 0;
-        const float *kr = kk + i * P;
-        const float *qr = rho + r * P;
-        float d = 0.f;
-#pragma unroll 8
-        for (int e = 0; e < D; e += 4) {
-            const float4 x = *reinterpret_cast<const float4 *>(kr + e);
-            const float4 y = *reinterpret_cast<const float4 *>(qr + e);
-            d = fmaf(x.x, y.x, d);
-            d = fmaf(x.y, y.y, d);
-            d = fmaf(x.z, y.z, d);
-            d = fmaf(x.w, y.w, d);
-        }
-        const float sg = live ? s * d : -INFINITY;
+        const float sg = live ? wt[r * c + i] : -INFINITY;
         float m = sg;
         for (int off = 1; off < c; off <<= 1) m = fmaxf(m, xor_lane_f(m, off));
         const float ex = live ? expf(sg - m) : 0.f;
@@ -135,43 +156,68 @@ template <int D, typename ST, typename CK, typename CB>
 __device__ __forceinline__ void upper_node(const float *refs, float *sig, CK child_k, CB child_b, ST *ok,
                                            float *ob, int R, int c, float s) {
     constexpr int EPL = D / 64;                 // elements per lane
+    constexpr int CBT = 16;                     // children whose rows are loaded together
     const int lane = threadIdx.x & 63;
     for (int r = 0; r < R; ++r) {
         float rho[EPL];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) rho[e] = refs[r * D + lane * EPL + e];
-
-        // scores of the c children under rho_r
+        // scores of the c children under rho_r; the rows of up to CBT
+        // children (and their biases) are loaded before any is used, so
+        // their loads are in flight together
+        float xs[CBT][EPL];
+        float bs[CBT];
         float mx = -INFINITY;
-        for (int i = 0; i < c; ++i) {
-            const ST *ck = child_k(i);
-            float part = 0.f;
+        for (int i0 = 0; i0 < c; i0 += CBT) {
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                float x = Elem<ST>::load(ck, r * D + lane * EPL + e);
-                part = fmaf(x, rho[e], part);
+            for (int u = 0; u < CBT; ++u) {
+                if (i0 + u < c) {
+                    const ST *ck = child_k(i0 + u);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) xs[u][e] = Elem<ST>::load(ck, r * D + lane * EPL + e);
+                    bs[u] = child_b(i0 + u)[r];
+                }
             }
-            float dotv = wave_sum(part, 64);
-            float sg = s * dotv + child_b(i)[r];
-            if (lane == 0) sig[i] = sg;
-            mx = fmaxf(mx, sg);
+#pragma unroll
+            for (int u = 0; u < CBT; ++u) {
+                if (i0 + u < c) {
+                    float part = 0.f;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) part = fmaf(xs[u][e], rho[e], part);
+                    float dotv = wave_sum(part, 64);
+                    float sg = s * dotv + bs[u];
+                    if (lane == 0) sig[i0 + u] = sg;
+                    mx = fmaxf(mx, sg);
+                }
+            }
         }
         __builtin_amdgcn_wave_barrier();
         float z = 0.f;
         for (int i = 0; i < c; ++i) z += expf(sig[i] - mx);
         const float inv_z = 1.f / z;
-
-        // weighted sum of the child keys
+        // weighted sum of the child keys (rows still in registers when
+        // c <= CBT)
         float acc[EPL];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-        for (int i = 0; i < c; ++i) {
-            const ST *ck = child_k(i);
-            const float w = expf(sig[i] - mx) * inv_z;
+        if (c <= CBT) {
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                float x = Elem<ST>::load(ck, r * D + lane * EPL + e);
-                acc[e] = fmaf(w, x, acc[e]);
+            for (int u = 0; u < CBT; ++u) {
+                if (u < c) {
+                    const float w = expf(sig[u] - mx) * inv_z;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, xs[u][e], acc[e]);
+                }
+            }
+        } else {
+            for (int i = 0; i < c; ++i) {
+                const ST *ck = child_k(i);
+                const float w = expf(sig[i] - mx) * inv_z;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    float x = Elem<ST>::load(ck, r * D + lane * EPL + e);
+                    acc[e] = fmaf(w, x, acc[e]);
+                }
             }
         }
         float part = 0.f;
@@ -187,5 +233,4 @@ __device__ __forceinline__ void upper_node(const float *refs, float *sig, CK chi
         __builtin_amdgcn_wave_barrier();   // sig[] is rewritten for the next r
     }
 }
-
 }  // namespace zha
