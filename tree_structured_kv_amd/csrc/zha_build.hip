@@ -21,8 +21,10 @@
 
 namespace zha {
 
-// Level >= 2: one wavefront per node (upper_node).
-template <int D, typename ST>
+// Level >= 2: one wavefront per node (upper_node), the rows of up to CBT
+// children in flight together (8 for chunks of up to 8: fewer registers,
+// more wavefronts; 16 above).
+template <int D, typename ST, int CBT>
 __global__ __launch_bounds__(kBlock) void k_summarize(LevelArgs a) {
     const int wave = threadIdx.x >> 6;
     const int64_t jn = static_cast<int64_t>(blockIdx.x) * (kBlock / 64) + wave;
@@ -40,9 +42,10 @@ __global__ __launch_bounds__(kBlock) void k_summarize(LevelArgs a) {
     ST *ok = static_cast<ST *>(a.out_k) + (static_cast<int64_t>(pair) * a.out_cap + j) * R * D;
     float *ob = a.out_b + (static_cast<int64_t>(pair) * a.out_cap + j) * R;
     const float *refs = a.refs + static_cast<int64_t>(g) * R * D;
-    upper_node<D, ST>(
-        refs, sig_lds[wave], [&](int i) { return ck + (j * c + i) * R * D; },
-        [&](int i) { return cb + (j * c + i) * R; }, ok, ob, R, c, a.sharpness);
+    auto child_k = [&](int i) { return ck + (j * c + i) * R * D; };
+    auto child_b = [&](int i) { return cb + (j * c + i) * R; };
+    upper_node<D, ST, decltype(child_k), decltype(child_b), CBT>(refs, sig_lds[wave], child_k, child_b, ok, ob, R, c,
+                                                                 a.sharpness);
 }
 
 // Level 1, one wavefront per node (leaf_node), the chunk's c keys staged once
@@ -102,7 +105,10 @@ static hipError_t launch_level_t(const LevelArgs &a, bool leaf, hipStream_t st) 
     }
     dim3 grid(static_cast<unsigned>((a.count + (kBlock / 64) - 1) / (kBlock / 64)),
               static_cast<unsigned>(a.pairs));
-    hipLaunchKernelGGL((k_summarize<D, ST>), grid, dim3(kBlock), 0, st, a);
+    if (a.chunk <= 8)
+        hipLaunchKernelGGL((k_summarize<D, ST, 8>), grid, dim3(kBlock), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_summarize<D, ST, 16>), grid, dim3(kBlock), 0, st, a);
     return hipGetLastError();
 }
 

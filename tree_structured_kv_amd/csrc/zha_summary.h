@@ -97,20 +97,27 @@ __device__ __forceinline__ void leaf_node(const float *rho, float *kk, float *wt
         }
     }
     __builtin_amdgcn_wave_barrier();
-    // 2. keys and biases, one (r, 16-element slice) per lane and round
+    // 2. keys and biases, one (r, 16 elements) per lane and round.  A lane's
+    //    16 elements are 16/G groups of G = 16 bytes / sizeof(ST) consecutive
+    //    elements, group e at G*s + NS*G*e for slice s = lane's index among
+    //    the NS lanes of reference r: one 16-byte store per group, and the NS
+    //    lanes of a reference write NS*G consecutive elements (a 128-byte
+    //    line at D = 128) per store instruction.
+    constexpr int G = 16 / static_cast<int>(sizeof(ST));
     for (int t0 = 0; t0 < R * NS; t0 += 64) {
         const int ti = t0 + lane;
         const bool live = ti < R * NS;
-        const int r = live ? ti / NS : 0, d0 = live ? (ti % NS) * 16 : 0;
+        const int r = live ? ti / NS : 0, sl = live ? ti % NS : 0;
+        auto dim = [&](int k) { return G * sl + NS * G * (k / G) + (k % G); };   // element k's dimension
         float acc[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[e] = 0.f;
         for (int i = 0; i < c; ++i) {
             const float w = wt[r * c + i];
-            const float *kr = kk + i * P + d0;
+            const float *kr = kk + i * P;
 #pragma unroll
             for (int e = 0; e < 16; e += 4) {
-                const float4 x = *reinterpret_cast<const float4 *>(kr + e);
+                const float4 x = *reinterpret_cast<const float4 *>(kr + dim(e));
                 acc[e] = fmaf(w, x.x, acc[e]);
                 acc[e + 1] = fmaf(w, x.y, acc[e + 1]);
                 acc[e + 2] = fmaf(w, x.z, acc[e + 2]);
@@ -123,26 +130,28 @@ __device__ __forceinline__ void leaf_node(const float *rho, float *kk, float *wt
             for (int e = 0; e < 16; ++e) acc[e] = bf16_to_f32(f32_to_bf16(acc[e]));
         }
         float part = 0.f;
-        const float *qr = rho + r * P + d0;
+        const float *qr = rho + r * P;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) part = fmaf(acc[e], qr[e], part);
+        for (int e = 0; e < 16; ++e) part = fmaf(acc[e], qr[dim(e)], part);
         for (int off = 1; off < NS; off <<= 1) part += xor_lane_f(part, off);
         if (live) {
             if constexpr (sizeof(ST) == 2) {
-                uint32_t wv[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    wv[e] = static_cast<uint32_t>(f32_to_bf16(acc[2 * e])) |
-                            (static_cast<uint32_t>(f32_to_bf16(acc[2 * e + 1])) << 16);
-                *reinterpret_cast<uint4 *>(ok + r * D + d0) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-                *reinterpret_cast<uint4 *>(ok + r * D + d0 + 8) = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+                for (int g = 0; g < 2; ++g) {
+                    uint32_t wv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        wv[e] = static_cast<uint32_t>(f32_to_bf16(acc[8 * g + 2 * e])) |
+                                (static_cast<uint32_t>(f32_to_bf16(acc[8 * g + 2 * e + 1])) << 16);
+                    *reinterpret_cast<uint4 *>(ok + r * D + dim(8 * g)) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                }
             } else {
 #pragma unroll
                 for (int e = 0; e < 16; e += 4)
-                    *reinterpret_cast<float4 *>(ok + r * D + d0 + e) =
+                    *reinterpret_cast<float4 *>(ok + r * D + dim(e)) =
                         make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
             }
-            if (d0 == 0) ob[r] = (mx_s[r] + logf(z_s[r])) - s * part;
+            if (sl == 0) ob[r] = (mx_s[r] + logf(z_s[r])) - s * part;
         }
     }
 }
@@ -152,11 +161,10 @@ __device__ __forceinline__ void leaf_node(const float *rho, float *kk, float *wt
 // memory or LDS); refs [R][D] the references; sig: 64 floats of LDS for this
 // wavefront; ok [R][D], ob [R]: the node's record.  A lane holds D/64
 // consecutive elements of every row.
-template <int D, typename ST, typename CK, typename CB>
+template <int D, typename ST, typename CK, typename CB, int CBT = 16>
 __device__ __forceinline__ void upper_node(const float *refs, float *sig, CK child_k, CB child_b, ST *ok,
                                            float *ob, int R, int c, float s) {
     constexpr int EPL = D / 64;                 // elements per lane
-    constexpr int CBT = 16;                     // children whose rows are loaded together
     const int lane = threadIdx.x & 63;
     for (int r = 0; r < R; ++r) {
         float rho[EPL];
