@@ -36,6 +36,10 @@ def _case(name):
     if name.endswith("-b8"):    # the same shapes on eight sequences (each its own seeds)
         w, v = _case(name[:-3] + "-small")
         return replace(w, batch=8), v
+    if name == "wide32":        # chunk 32: two 16-key score tiles per level-1 node, 32 children per parent
+        return replace(W[2].scaled(n=32 * 32 * 4 + 45, batch=1), kv_heads=2, chunk=32, levels=2), None
+    if name == "wide64":        # chunk 64, the largest the library takes
+        return replace(W[2].scaled(n=64 * 64 * 2 + 99, batch=1), kv_heads=2, chunk=64, levels=2), None
     if name == "mha-small":     # one query head per KV head
         return replace(W[1].scaled(n=4096 + 7, batch=2), kv_heads=4, group=1, levels=3), None
     raise KeyError(name)
@@ -168,6 +172,20 @@ def test_build_equals_appends(Z, name):
             eb = np.max(np.abs(nb[b, g, :ok.shape[0]] - ob), axis=1) / np.maximum(1.0, np.max(np.abs(ob), axis=1))
             worst = max(worst, float(ek.max()), float(eb.max()))
     assert worst <= P.TOL_TREE, worst
+
+
+@pytest.mark.parametrize("name", ["wide32", "wide64"])
+def test_wide_chunks(Z, name):
+    """Chunks above 16 keys: the level-1 summary takes its scores over
+    several 16-key matrix tiles and an upper node reloads its children's rows
+    for the weighted sum.  Records against the oracle, appends bit-identical
+    to the build, and AUTO's search and attention against the oracle."""
+    test_tree_records(Z, name)
+    test_build_equals_appends(Z, name)
+    w, K, V, Q, R, Kt, Vt, Qt, idx, trees = _setup(Z, name)
+    for select in (dict(mode="topp", p=0.9), dict(mode="topk", k=(2,))):
+        sel, bufs, out = _run(Z, idx, Qt, Kt, Vt, select)
+        _compare(w, K, V, Q, trees, select, bufs, out, min_stable=0.0)
 
 
 SELECTS = {
