@@ -373,12 +373,26 @@ zha_status zha_sparse_attn_noalloc(const zha_tree *t, const void *q, int32_t q_p
 /* Workspace bytes of zha_forward (search + attention + selection lists). */
 uint64_t zha_forward_workspace_bytes(const zha_tree *t, const zha_select *sel, int32_t q_per_head);
 
-/* One step of a layer with the selection lists kept in the workspace.
+/* One step of a layer with the selection lists kept in the workspace: the
+ * upkeep of the tree as the cache grows ([ZHA lesson] "How is the tree
+ * built?": a node is summarised once its chunk of children is complete), the
+ * top-down walk of every query head ("Run a small tree yourself") and
+ * ordinary attention over the original keys the walk chose ("Common
+ * misunderstandings": summaries only steer the search).
  * Decode (q_per_head = 1): zha_append(n_new) first (the new token's key is
- * then visible to its own query), then zha_search and zha_sparse_attn.
+ * then visible to its own query), then zha_search and zha_sparse_attn; with
+ * sel->engine = ZHA_ENGINE_FUSED (n_new = 1) the three run in one launch.
  * Prefill block (q_per_head > 1): zha_search and zha_sparse_attn for the
  * block at positions [n_tokens, n_tokens + q_per_head), then
- * zha_append(n_new) (normally n_new = q_per_head). */
+ * zha_append(n_new) (normally n_new = q_per_head).
+ * Arguments: q, k_cache, v_cache, out, stats and status as for zha_search
+ * and zha_sparse_attn (device pointers, caller-owned, stats may be null);
+ * ws: caller-owned device workspace of at least
+ * zha_forward_workspace_bytes(t, sel, q_per_head) bytes, ws_bytes its size;
+ * stream: the hipStream_t every launch goes to (null: the default stream).
+ * Errors: the argument checks of the three calls (ZHA_ERR_ARG, _ALIGN,
+ * _CAPACITY, _UNSUPPORTED) and ZHA_ERR_WORKSPACE for a short workspace
+ * return before anything is enqueued; a failed launch returns ZHA_ERR_HIP. */
 zha_status zha_forward(zha_tree *t, int64_t n_new, const void *q, int32_t q_per_head,
                        const void *k_cache, const void *v_cache, const zha_select *sel,
                        void *out, zha_walk_stats *stats, uint32_t *status,
