@@ -181,7 +181,7 @@ UnionGeom union_geom(const zha_tree *t, int32_t qph) {
     u.n1cap = (g.max_tokens / g.chunk + 1) / 2 * 2;
     u.nchunks = (u.n1cap + kUaBlocks - 1) / kUaBlocks;
     u.cwords = (u.nchunks + 31) / 32;
-    u.wpg_max = qph > 1 ? 1 : std::max<int64_t>(1, std::min<int64_t>(4096 / pairs, u.nchunks));
+    u.wpg_max = qph > 1 ? 1 : std::max<int64_t>(1, std::min<int64_t>(2048 / pairs, u.nchunks));
     return u;
 }
 
@@ -542,7 +542,7 @@ zha_status do_attn(const zha_tree *t, const void *q, int32_t qph, const void *k_
         a.ugroups = lay.u.ugroups;
         a.cwords = static_cast<int32_t>(lay.u.cwords);
         a.gpp = static_cast<int32_t>(lay.u.gpp);
-        // decode: about 4096 workgroups in all, each over a contiguous range
+        // decode: about 2048 workgroups in all, each over a contiguous range
         // of chunks; prefill: one workgroup per group, over all chunks
         const int64_t nchunks = (a.n1 + kUaBlocks - 1) / kUaBlocks;
         int64_t wpg = std::min<int64_t>(lay.u.wpg_max, std::max<int64_t>(1, nchunks));

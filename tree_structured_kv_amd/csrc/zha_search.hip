@@ -49,8 +49,10 @@ constexpr int kScoreThreads = 256;     // workgroup of the level-synchronous sco
 
 // ---- persistent engine --------------------------------------------------------
 
+// At most 128 VGPRs (four wavefronts per SIMD: two workgroups per CU); the
+// two scoring variants together would take 136 and leave one.
 template <int D, int R, typename QT, typename ST>
-__global__ __launch_bounds__(kThreads) void k_search_decode(SearchArgs a) {
+__global__ __launch_bounds__(kThreads, 4) void k_search_decode(SearchArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int w = xcd_remap(blockIdx.x, gridDim.x);
     if (w >= a.walks) return;
@@ -80,7 +82,14 @@ __global__ __launch_bounds__(kThreads) void k_search_decode(SearchArgs a) {
         const bool forced = step_forced(a, t, n);
         unsigned long long tau = 0;
         if (!forced) {
-            float wmax = score_wave<D, R, ST, false>(a, pair, qv, cur, sc, wave * kU, n, kWaves * kU, flags);
+            // streaming record loads when the group's heads, each with a list
+            // as long as this one, cover less than half of the step's level
+            // (the rule of the level-synchronous scorer, from this walk's
+            // count: under top-K every head's list has the same length)
+            const bool stream = static_cast<int64_t>(n) * a.group * 2 < a.nl[max(1, a.levels - t)];
+            const float wmax =
+                stream ? score_wave<D, R, ST, false, false, true>(a, pair, qv, cur, sc, wave * kU, n, kWaves * kU, flags)
+                       : score_wave<D, R, ST, false>(a, pair, qv, cur, sc, wave * kU, n, kWaves * kU, flags);
             if (lane == 0) sh.red[wave] = wmax;
             __syncthreads();
             float mx = sh.red[0];
