@@ -19,6 +19,8 @@
 #include "zha_internal.h"
 #include "zha_summary.h"
 
+#include <algorithm>
+
 namespace zha {
 
 // Level >= 2: one wavefront per node (upper_node), the rows of up to CBT
@@ -48,8 +50,9 @@ __global__ __launch_bounds__(kBlock) void k_summarize(LevelArgs a) {
                                                                  a.sharpness);
 }
 
-// Level 1, one wavefront per node (leaf_node), the chunk's c keys staged once
-// in LDS (fp32) next to the group's R references (one copy per workgroup).
+// Level 1, one wavefront per node at a time (leaf_node), the chunk's c keys
+// staged once in LDS (fp32) next to the group's R references (one copy per
+// workgroup, which loops over nodes).
 // Every key is read from HBM once; the passes over it run from LDS.
 template <int D, typename KT, typename ST>
 __global__ __launch_bounds__(kBlock) void k_leaf(LevelArgs a, int waves) {
@@ -72,14 +75,17 @@ __global__ __launch_bounds__(kBlock) void k_leaf(LevelArgs a, int waves) {
         *reinterpret_cast<float4 *>(rho + r * P + d4) = *reinterpret_cast<const float4 *>(refs + r * D + d4);
     }
     __syncthreads();
-    const int64_t jn = static_cast<int64_t>(blockIdx.x) * waves + wave;
-    if (wave >= waves || jn >= a.count) return;  // no workgroup barrier below
-    const int64_t j = a.j0 + jn;
-    const KT *keys = static_cast<const KT *>(a.keys) + (static_cast<int64_t>(pair) * a.max_tokens + j * c) * D;
-    ST *ok = static_cast<ST *>(a.out_k) + (static_cast<int64_t>(pair) * a.out_cap + j) * R * D;
-    float *ob = a.out_b + (static_cast<int64_t>(pair) * a.out_cap + j) * R;
-
-    leaf_node<D, KT, ST>(rho, kk, wt, mx_s, z_s, keys, ok, ob, R, c, s);
+    if (wave >= waves) return;                   // no workgroup barrier below
+    // each node wavefront takes nodes gridDim.x * waves apart
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * waves;
+    for (int64_t jn = static_cast<int64_t>(blockIdx.x) * waves + wave; jn < a.count; jn += stride) {
+        const int64_t j = a.j0 + jn;
+        const KT *keys = static_cast<const KT *>(a.keys) + (static_cast<int64_t>(pair) * a.max_tokens + j * c) * D;
+        ST *ok = static_cast<ST *>(a.out_k) + (static_cast<int64_t>(pair) * a.out_cap + j) * R * D;
+        float *ob = a.out_b + (static_cast<int64_t>(pair) * a.out_cap + j) * R;
+        __builtin_amdgcn_wave_barrier();         // the previous node's LDS reads come first
+        leaf_node<D, KT, ST>(rho, kk, wt, mx_s, z_s, keys, ok, ob, R, c, s);
+    }
 }
 
 // Workgroup shape of k_leaf: as many node wavefronts as fit in 64 KB of LDS.
@@ -99,7 +105,12 @@ static hipError_t launch_level_t(const LevelArgs &a, bool leaf, hipStream_t st) 
     if (leaf) {
         size_t lds = 0;
         const int waves = leaf_waves(a, D, lds);
-        dim3 grid(static_cast<unsigned>((a.count + waves - 1) / waves), static_cast<unsigned>(a.pairs));
+        int64_t gx = (a.count + waves - 1) / waves;
+        // about 8192 workgroups in all, each node wavefront looping over nodes
+        // (one reference staging per workgroup; 4-5% faster than a
+        // workgroup per node group at 256K and 1M)
+        gx = std::min<int64_t>(gx, std::max<int64_t>(1, 8192 / a.pairs));
+        dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(a.pairs));
         hipLaunchKernelGGL((k_leaf<D, KT, ST>), grid, dim3(kBlock), lds, st, a, waves);
         return hipGetLastError();
     }
